@@ -1,0 +1,157 @@
+/*
+ * Seeded synthetic inputs for one routed-MoE layer (host side).
+ *
+ * What lives here: counter-based random draws, an approximately normal
+ * variate built from them, uniform variates, and the offline step that turns
+ * float expert weights into packed low-bit codes with one fp32 scale per row
+ * (the pages' engine gets its expert container from an offline converter;
+ * "colibrì … Show HN" page, implemented-features list, converter item).
+ * What does not live here: any arithmetic of the layer itself (router,
+ * Q8_0, integer dots, SwiGLU, combine).  Both the CPU oracle and the HIP
+ * library consume the bytes written here; a GPU copy of the same generator
+ * (synth_gpu.hip) writes identical bytes for the large weight sets.
+ *
+ * Generator definitions (all exact integer or correctly rounded fp32 steps,
+ * so a GPU implementation reproduces them bit for bit):
+ *   mix64        SplitMix64 output function (Steele, Lea, Flood, OOPSLA 2014)
+ *   draw(key,i)  = mix64(key + (i+1)*0x9E3779B97F4A7C15)   (i-th stream value)
+ *   normal(key,i) = (S - 393210) / 65536, S = sum of the twelve 16-bit fields of
+ *                  draw(key,3i), draw(key,3i+1), draw(key,3i+2)
+ *                  (Irwin–Hall sum of 12 uniforms: mean 0, variance ~1, |z| <= 6)
+ *   uniform(key,i) = (draw(key,i) >> 40) * 2^-24  in [0,1)
+ *
+ * Packed weight record of one expert (wbits = 4 or 2), rows of the three
+ * matrices followed by their fp32 per-row scales:
+ *   gate codes [I][H*wbits/8] | up codes [I][H*wbits/8] | down codes [H][I*wbits/8]
+ *   | gate scale [I] | up scale [I] | down scale [H]
+ * int4: element 2j in the low nibble of byte j, 2j+1 in the high nibble,
+ *       two's complement; int2: element 4j+i in bits 2i..2i+1, two's complement.
+ * Row quantiser: amax = max|w|, s = amax / qdiv (qdiv 7 for int4, 2 for int2),
+ *   code = clamp(roundf(w / s), qlo, qhi) (int4: [-8,7], int2: [-2,1]); s = 0 -> codes 0.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define SYN_GOLDEN 0x9E3779B97F4A7C15ULL
+
+static inline uint64_t mix64(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+static inline uint64_t draw(uint64_t key, uint64_t i) {
+  return mix64(key + (i + 1) * SYN_GOLDEN);
+}
+
+static inline int32_t sum16(uint64_t v) {
+  return (int32_t)(v & 0xFFFF) + (int32_t)((v >> 16) & 0xFFFF) +
+         (int32_t)((v >> 32) & 0xFFFF) + (int32_t)(v >> 48);
+}
+
+static inline float normal_at(uint64_t key, uint64_t i) {
+  int32_t s = sum16(draw(key, 3 * i)) + sum16(draw(key, 3 * i + 1)) +
+              sum16(draw(key, 3 * i + 2));
+  return (float)(s - 393210) * (1.0f / 65536.0f);
+}
+
+uint64_t synth_draw(uint64_t key, uint64_t i) { return draw(key, i); }
+
+uint64_t synth_key(uint64_t seed, uint32_t layer, uint32_t tensor,
+                   uint32_t expert, uint32_t matrix) {
+  uint64_t k = mix64(seed + SYN_GOLDEN);
+  k = mix64(k ^ (((uint64_t)layer << 32) | tensor));
+  k = mix64(k ^ (((uint64_t)expert << 32) | matrix));
+  return k;
+}
+
+/* out[i] = sigma * normal(key, start + i) */
+void synth_normal_fill(uint64_t key, uint64_t start, int64_t n, float sigma,
+                       float *out) {
+#pragma omp parallel for schedule(static) if (n > 65536)
+  for (int64_t i = 0; i < n; i++) out[i] = normal_at(key, start + (uint64_t)i) * sigma;
+}
+
+/* out[i] = lo + (hi - lo) * uniform(key, start + i) */
+void synth_uniform_fill(uint64_t key, uint64_t start, int64_t n, float lo,
+                        float hi, float *out) {
+  for (int64_t i = 0; i < n; i++) {
+    float u = (float)(draw(key, start + (uint64_t)i) >> 40) * 0x1p-24f;
+    out[i] = lo + (hi - lo) * u;
+  }
+}
+
+size_t synth_blob_bytes(int H, int I, int wbits) {
+  size_t codes = ((size_t)2 * I * H + (size_t)H * I) * (size_t)wbits / 8;
+  return codes + sizeof(float) * ((size_t)2 * I + H);
+}
+
+/* One weight row: n float draws (sigma * normal), quantised and packed. */
+static void quant_row(uint64_t key, uint64_t row, int n, int wbits, float sigma,
+                      uint8_t *dst, float *scale, float *wbuf) {
+  float amax = 0.0f;
+  for (int c = 0; c < n; c++) {
+    float w = normal_at(key, row * (uint64_t)n + (uint64_t)c) * sigma;
+    wbuf[c] = w;
+    amax = fmaxf(amax, fabsf(w));
+  }
+  const float qdiv = (wbits == 4) ? 7.0f : 2.0f;
+  const int qlo = (wbits == 4) ? -8 : -2, qhi = (wbits == 4) ? 7 : 1;
+  float s = amax / qdiv;
+  *scale = s;
+  const int per = 8 / wbits;
+  const unsigned mask = (1u << wbits) - 1u;
+  for (int j = 0; j < n / per; j++) {
+    unsigned byte = 0;
+    for (int i = 0; i < per; i++) {
+      int q = 0;
+      if (s != 0.0f) {
+        float r = roundf(wbuf[j * per + i] / s);
+        q = (int)r;
+        if (q < qlo) q = qlo;
+        if (q > qhi) q = qhi;
+      }
+      byte |= ((unsigned)q & mask) << (wbits * i);
+    }
+    dst[j] = (uint8_t)byte;
+  }
+}
+
+/* Float weights of one matrix row before quantisation (for tests of the record). */
+void synth_weight_row(uint64_t seed, uint32_t layer, uint32_t expert,
+                      uint32_t matrix, int n, int row, float sigma, float *out) {
+  uint64_t key = synth_key(seed, layer, 4u + matrix, expert, matrix);
+  for (int c = 0; c < n; c++)
+    out[c] = normal_at(key, (uint64_t)row * (uint64_t)n + (uint64_t)c) * sigma;
+}
+
+/* Expert record for (seed, layer, expert); matrix m = 0 gate, 1 up, 2 down. */
+int synth_expert_blob(uint64_t seed, uint32_t layer, uint32_t expert, int H,
+                      int I, int wbits, float sigma, uint8_t *blob) {
+  if ((wbits != 4 && wbits != 2) || H <= 0 || I <= 0 || H % 8 || I % 8) return -1;
+  const size_t gate_b = (size_t)I * H * wbits / 8;
+  const size_t down_b = (size_t)H * I * wbits / 8;
+  uint8_t *codes[3] = {blob, blob + gate_b, blob + 2 * gate_b};
+  float *scales = (float *)(blob + 2 * gate_b + down_b);
+  float *sc[3] = {scales, scales + I, scales + 2 * I};
+  const int rows[3] = {I, I, H}, cols[3] = {H, H, I};
+  for (int m = 0; m < 3; m++) {
+    const uint64_t key = synth_key(seed, layer, 4u + (uint32_t)m, expert, (uint32_t)m);
+    const int n = cols[m];
+    const size_t row_b = (size_t)n * wbits / 8;
+#pragma omp parallel
+    {
+      float *wbuf = (float *)malloc(sizeof(float) * (size_t)n);
+#pragma omp for schedule(static)
+      for (int r = 0; r < rows[m]; r++)
+        quant_row(key, (uint64_t)r, n, wbits, sigma, codes[m] + (size_t)r * row_b,
+                  sc[m] + r, wbuf);
+      free(wbuf);
+    }
+  }
+  return 0;
+}

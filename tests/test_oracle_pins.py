@@ -1,0 +1,464 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle step to a hand-worked fixture (tests/golden/), a
+library routine (numpy, math, scipy), a closed form, an invariant, or brute
+force on tiny inputs, so that a dropped term, a wrong sign or index, or a
+transposed operand in the oracle fails here.  CPU only.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _half_away(v):
+    v = np.asarray(v, np.float64)
+    return np.sign(v) * np.floor(np.abs(v) + 0.5)
+
+
+# ------------------------------------------------------------------ packed codes
+
+@pytest.mark.parametrize("wbits", [4, 2])
+def test_codes_match_hand_table(wbits):
+    for case in _load("packed_codes.json")[f"int{wbits}"]:
+        row = np.array([case["byte"]], np.uint8)
+        got = oracle.unpack(row, wbits, 8 // wbits).tolist()
+        assert got == case["codes"], case["derivation"]
+
+
+@pytest.mark.parametrize("wbits", [4, 2])
+def test_pack_unpack_round_trip_exhaustive(wbits):
+    per = 8 // wbits
+    allbytes = np.arange(256, dtype=np.uint8)
+    codes = oracle.unpack(allbytes, wbits, 256 * per)
+    assert np.array_equal(oracle.pack(codes, wbits), allbytes)
+    lo, hi = (-8, 7) if wbits == 4 else (-2, 1)
+    tuples = np.array(list(itertools.product(range(lo, hi + 1), repeat=per)), np.int8).ravel()
+    packed = oracle.pack(tuples, wbits)
+    assert np.array_equal(oracle.unpack(packed, wbits, tuples.size), tuples)
+    # every byte value appears exactly once: the code map is a bijection
+    assert sorted(packed.tolist()) == list(range(256))
+
+
+@pytest.mark.parametrize("wbits", [4, 2])
+def test_generated_record_decodes_to_rounded_weights(wbits):
+    """The generator's packed rows, read back by the oracle, equal a numpy
+    re-quantisation of the generator's float rows (two independent codes)."""
+    shape = synth.TINY.with_bits(wbits)
+    H, I = shape.hidden, shape.inter
+    blob = synth.expert_blob(shape, 7, 3, 5)
+    gate, up, down, sg, su, sd = oracle.blob_view(blob, H, I, wbits)
+    qdiv, lo, hi = (7.0, -8, 7) if wbits == 4 else (2.0, -2, 1)
+    for m, (rows, sc, n) in enumerate([(gate, sg, H), (up, su, H), (down, sd, I)]):
+        for r in (0, 1, rows.shape[0] - 1):
+            w = synth.weight_row(7, 3, 5, m, n, r)
+            s = np.float32(np.max(np.abs(w)) / np.float32(qdiv))
+            assert sc[r] == s
+            want = np.clip(_half_away(w / s), lo, hi).astype(np.int8)
+            assert np.array_equal(oracle.unpack(rows[r], wbits, n), want)
+
+
+def test_record_size_matches_nineteen_megabytes():
+    """~19 MB per int4 expert at hidden 6144 / intermediate 2048 (pages'
+    streaming section) -> 3*6144*2048/2 code bytes + fp32 row scales."""
+    assert oracle.blob_bytes(6144, 2048, 4) == 18_915_328
+    assert oracle.blob_bytes(6144, 2048, 2) == 9_478_144
+    assert synth.blob_bytes(synth.REAL) == 18_915_328
+
+
+# ------------------------------------------------------------------ integer dots
+
+def test_block_dot_single_product_table():
+    """All 16 x 255 products code*q as one-element blocks."""
+    for c in range(-8, 8):
+        codes = np.zeros(32, np.int8)
+        codes[5] = c
+        row = oracle.pack(codes, 4)
+        for v in range(-127, 128):
+            q = np.zeros(32, np.int8)
+            q[5] = v
+            assert oracle.block_dots(row, 4, q)[0] == c * v
+
+
+@pytest.mark.parametrize("wbits", [4, 2])
+def test_block_dots_vs_numpy_int64(wbits):
+    rng = np.random.default_rng(1)
+    lo, hi = (-8, 7) if wbits == 4 else (-2, 1)
+    n = 32 * 40
+    codes = rng.integers(lo, hi + 1, n).astype(np.int8)
+    q = rng.integers(-127, 128, n).astype(np.int8)
+    got = oracle.block_dots(oracle.pack(codes, wbits), wbits, q)
+    want = (codes.astype(np.int64) * q.astype(np.int64)).reshape(-1, 32).sum(1)
+    assert np.array_equal(got, want)
+
+
+def test_block_dot_extremes():
+    row = oracle.pack(np.full(32, -8, np.int8), 4)
+    assert oracle.block_dots(row, 4, np.full(32, -127, np.int8))[0] == 32512
+    assert oracle.block_dots(row, 4, np.full(32, 127, np.int8))[0] == -32512
+
+
+# ------------------------------------------------------------------ Q8_0
+
+def test_q8_0_hand_blocks():
+    for blk in _load("q8_0_blocks.json")["blocks"]:
+        x = np.zeros(32, np.float32)
+        for k, v in blk["x"].items():
+            x[int(k)] = v
+        want = np.zeros(32, np.int8)
+        for k, v in blk["q"].items():
+            want[int(k)] = v
+        q, d = oracle.q8_0(x)
+        assert d[0] == np.float32(blk["d"]), blk["name"]
+        assert np.array_equal(q, want), blk["name"]
+
+
+def test_q8_0_invariants_random():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal((16, 32 * 24)) * rng.uniform(1e-3, 1e3, (16, 1))).astype(np.float32)
+    x[3, 64:96] = 0.0
+    q, d = oracle.q8_0(x)
+    qb = q.reshape(16, -1, 32).astype(np.int64)
+    xb = x.reshape(16, -1, 32).astype(np.float64)
+    assert np.all(np.abs(qb) <= 127)
+    nz = d > 0
+    assert np.all(np.abs(qb).max(-1)[nz] == 127)
+    assert not nz[3, 2] and np.all(qb[3, 2] == 0)
+    err = np.abs(xb - qb * d[..., None].astype(np.float64))
+    assert np.all(err <= d[..., None] * (0.5 + 2e-5))
+    # d is the correctly rounded amax/127
+    amax = np.abs(x.reshape(16, -1, 32)).max(-1)
+    assert np.array_equal(d, (amax / np.float32(127)).astype(np.float32))
+
+
+def test_q8_0_integer_grid_is_exact():
+    rng = np.random.default_rng(3)
+    xi = rng.integers(-127, 128, (5, 32 * 8))
+    xi.reshape(5, -1, 32)[:, :, 7] = 127
+    q, d = oracle.q8_0(xi.astype(np.float32))
+    assert np.all(d == 1.0)
+    assert np.array_equal(q.astype(np.int64), xi)
+
+
+# ------------------------------------------------------------------ router arithmetic
+
+def _ulp(v):
+    return np.spacing(np.abs(np.float32(v))).astype(np.float64)
+
+
+def test_exp_canon_within_two_ulp():
+    ys = np.linspace(-87.0, 87.0, 20001, dtype=np.float32)
+    got = oracle.exp_canon(ys).astype(np.float64)
+    want = np.exp(ys.astype(np.float64))
+    ulps = np.abs(got - want) / _ulp(want.astype(np.float32))
+    assert ulps.max() <= 2.0
+    assert oracle.exp_canon([0.0])[0] == 1.0
+
+
+def test_sigmoid_canon_closed_forms():
+    ls = np.linspace(-20, 20, 4001, dtype=np.float32)
+    got = oracle.sigmoid_canon(ls).astype(np.float64)
+    want = expit(ls.astype(np.float64))
+    assert np.max(np.abs(got - want) / _ulp(want.astype(np.float32))) <= 3.0
+    assert oracle.sigmoid_canon([0.0])[0] == 0.5
+    sym = got + oracle.sigmoid_canon(-ls).astype(np.float64)
+    assert np.max(np.abs(sym - 1.0)) <= 2.5e-7
+
+
+def test_dot_canon_error_bound():
+    rng = np.random.default_rng(4)
+    for n in (64, 256, 6144):
+        a = rng.standard_normal(n).astype(np.float32)
+        b = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        exact = math.fsum((a.astype(np.float64) * b.astype(np.float64)).tolist())
+        bound = n * 2.0 ** -24 * float(np.sum(np.abs(a.astype(np.float64) * b)))
+        assert abs(float(oracle.dot_canon(a, b)) - exact) <= bound
+
+
+def test_router_scores_match_definition():
+    """s = sigmoid(x . W_r[e]) to fp32 accuracy and sb = s + bias, against fp64 numpy."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 256)).astype(np.float32)
+    wr = (rng.standard_normal((8, 256)) * 0.02).astype(np.float32)
+    bias = rng.uniform(-0.1, 0.1, 8).astype(np.float32)
+    s, sb = oracle.router_scores(x, wr, bias)
+    ref = expit(x.astype(np.float64) @ wr.astype(np.float64).T)
+    assert np.max(np.abs(s - ref)) < 1e-6
+    assert np.array_equal(sb, (s + bias).astype(np.float32))
+
+
+# ------------------------------------------------------------------ selection
+
+def test_select_hand_cases():
+    for c in _load("router_cases.json")["cases"]:
+        s = np.array([c["s"]], np.float32)
+        sb = np.array([c["sb"]], np.float32)
+        idx, w, _ = oracle.select(s, sb, c["G"], c["TG"], c["K"], c["scale"])
+        assert idx[0].tolist() == c["idx"], c["name"]
+        assert np.allclose(w[0], np.array(c["w"], np.float32), rtol=0, atol=1e-7), c["name"]
+
+
+@pytest.mark.parametrize("E,G,TG,K", [(8, 2, 1, 2), (8, 4, 2, 3), (16, 4, 2, 3), (12, 3, 2, 4)])
+def test_select_vs_subset_enumeration(E, G, TG, K):
+    """With distinct scores, the kept groups are the TG-subset of largest total
+    group score and the picks are the K-subset of largest total biased score."""
+    rng = np.random.default_rng(E * 100 + K)
+    gs = E // G
+    for _ in range(200):
+        s = rng.uniform(0.01, 1.0, (1, E)).astype(np.float32)
+        sb = (s + rng.uniform(-0.1, 0.1, (1, E)).astype(np.float32)).astype(np.float32)
+        idx, w, _ = oracle.select(s, sb, G, TG, K, 2.5)
+        v = sb[0].astype(np.float64)
+        gscore = [sum(sorted(v[g * gs:(g + 1) * gs])[-2:]) for g in range(G)]
+        best_groups = max(itertools.combinations(range(G), TG),
+                          key=lambda c: sum(gscore[g] for g in c))
+        cands = [e for e in range(E) if e // gs in best_groups]
+        best = max(itertools.combinations(cands, K), key=lambda c: sum(v[e] for e in c))
+        assert set(idx[0].tolist()) == set(best)
+        assert idx[0].tolist() == sorted(best, key=lambda e: (-v[e], e))
+        # weights use the unbiased score, normalised, times the scale
+        sel = s[0, idx[0]].astype(np.float64)
+        assert np.allclose(w[0], sel / sel.sum() * 2.5, rtol=3e-7, atol=0)
+
+
+def test_select_single_group_is_plain_top_k():
+    rng = np.random.default_rng(6)
+    for _ in range(100):
+        s = rng.uniform(0, 1, (1, 16)).astype(np.float32)
+        s[0, 3] = s[0, 9]  # a tie
+        idx, _, _ = oracle.select(s, s, 1, 1, 5, 1.0)
+        want = np.argsort(-s[0].astype(np.float64), kind="stable")[:5]
+        assert idx[0].tolist() == want.tolist()
+
+
+def test_zero_bias_single_group_is_top_k_of_logits():
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((4, 128)).astype(np.float32)
+    wr = (rng.standard_normal((16, 128)) * 0.1).astype(np.float32)
+    idx, _, _ = oracle.route(x, wr, np.zeros(16, np.float32), 1, 1, 4, 1.0)
+    logits = x.astype(np.float64) @ wr.astype(np.float64).T
+    for t in range(4):
+        assert idx[t].tolist() == np.argsort(-logits[t], kind="stable")[:4].tolist()
+
+
+def test_normalisation_identity():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    wr = (rng.standard_normal((32, 256)) * 0.02).astype(np.float32)
+    bias = rng.uniform(-0.1, 0.1, 32).astype(np.float32)
+    _, w, _ = oracle.route(x, wr, bias, 4, 2, 8, 2.5)
+    # each w_k carries <= 2 roundings, S carries K-1: |sum w - 2.5| <= 2.5 * (K+2) * 2^-24
+    assert np.max(np.abs(w.astype(np.float64).sum(1) - 2.5)) <= 2.5 * 10 * 2.0 ** -24
+    assert np.all(w > 0)
+
+
+def test_uniform_bias_shift_keeps_selection_and_weights():
+    rng = np.random.default_rng(9)
+    for _ in range(50):
+        # grid values so that adding 0.125 is exact in fp32
+        s = (rng.integers(256, 768, (1, 32)) / 1024.0).astype(np.float32)
+        b = (rng.integers(-64, 64, (1, 32)) / 1024.0).astype(np.float32)
+        sb = s + b
+        idx1, w1, _ = oracle.select(s, sb, 4, 2, 6, 2.5)
+        idx2, w2, _ = oracle.select(s, (sb + np.float32(0.125)).astype(np.float32), 4, 2, 6, 2.5)
+        assert np.array_equal(idx1, idx2) and np.array_equal(w1, w2)
+
+
+def test_crafted_tie_rows_pick_lower_index():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((2, 128)).astype(np.float32)
+    wr = (rng.standard_normal((8, 128)) * 0.02).astype(np.float32)
+    wr[5] = wr[1]  # identical router rows, identical biases
+    wr[1] *= 40.0  # make them the winners
+    wr[5] = wr[1]
+    bias = np.zeros(8, np.float32)
+    x[0] = np.abs(x[0]) * np.sign(wr[1])  # positive logit for experts 1 and 5
+    idx, _, _ = oracle.route(x[:1], wr, bias, 1, 1, 1, 1.0)
+    assert idx[0, 0] == 1
+
+
+# ------------------------------------------------------------------ grouping
+
+def test_group_vs_stable_argsort():
+    rng = np.random.default_rng(11)
+    for T, K, E in [(1, 8, 256), (4, 2, 8), (16, 8, 256), (2048, 8, 256), (37, 3, 10)]:
+        idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+        if T >= 4:
+            idx[T // 2] = idx[0]  # a duplicated token
+        g = oracle.group(idx, E)
+        flat = idx.ravel()
+        assert np.array_equal(g["perm"], np.argsort(flat, kind="stable"))
+        assert np.array_equal(g["counts"], np.bincount(flat, minlength=E))
+        assert np.array_equal(g["offsets"], np.concatenate([[0], np.cumsum(g["counts"])]))
+        assert np.array_equal(g["inv"][g["perm"]], np.arange(T * K))
+        act = np.nonzero(g["counts"])[0]
+        assert g["n_active"] == act.size and np.array_equal(g["active"][:act.size], act)
+        assert np.all(g["active"][act.size:] == -1)
+
+
+def test_group_rejects_out_of_range_expert():
+    with pytest.raises(ValueError):
+        oracle.group(np.array([[0, 9]], np.int32), 8)
+
+
+# ------------------------------------------------------------------ expert FFN
+
+def _tiny_inputs(seed=12, T=3, wbits=4):
+    shape = synth.TINY.with_bits(wbits)
+    blob = synth.expert_blob(shape, seed, 0, 1)
+    x = synth.tokens(shape, seed, T)
+    q, d = oracle.q8_0(x)
+    return shape, blob, x, q, d
+
+
+@pytest.mark.parametrize("wbits", [4, 2])
+def test_gate_up_equals_dequantised_matmul(wbits):
+    """Integer block dots rescaled == fp64 matmul of dequantised weights and
+    dequantised activations (algebraic identity), and h = silu(g) * u."""
+    shape, blob, x, q, d = _tiny_inputs(wbits=wbits)
+    H, I = shape.hidden, shape.inter
+    gate, up, _, sg, su, _ = oracle.blob_view(blob, H, I, wbits)
+    Wg = np.stack([oracle.unpack(gate[r], wbits, H) for r in range(I)]).astype(np.float64)
+    Wu = np.stack([oracle.unpack(up[r], wbits, H) for r in range(I)]).astype(np.float64)
+    Wg *= sg[:, None]
+    Wu *= su[:, None]
+    for t in range(q.shape[0]):
+        a = q[t].astype(np.float64) * np.repeat(d[t].astype(np.float64), 32)
+        out = oracle.gate_up(blob, H, I, wbits, q[t], d[t], want_dots=True)
+        g_ref, u_ref = Wg @ a, Wu @ a
+        assert np.allclose(out["g"], g_ref, rtol=1e-12, atol=1e-15)
+        assert np.allclose(out["u"], u_ref, rtol=1e-12, atol=1e-15)
+        h_ref = (g_ref * expit(g_ref) * u_ref).astype(np.float32)
+        assert np.max(np.abs(out["h"] - h_ref)) <= np.max(np.abs(h_ref)) * 1e-6
+        # dots: integer GEMV of the codes against q, blockwise
+        codes = np.stack([oracle.unpack(gate[r], wbits, H) for r in range(I)]).astype(np.int64)
+        want = (codes * q[t].astype(np.int64)).reshape(I, -1, 32).sum(-1)
+        assert np.array_equal(out["gate_dots"], want)
+
+
+@pytest.mark.parametrize("wbits", [4, 2])
+def test_down_equals_dequantised_matmul(wbits):
+    shape, blob, x, q, d = _tiny_inputs(wbits=wbits)
+    H, I = shape.hidden, shape.inter
+    _, _, down, _, _, sd = oracle.blob_view(blob, H, I, wbits)
+    Wd = np.stack([oracle.unpack(down[j], wbits, I) for j in range(H)]).astype(np.float64)
+    Wd *= sd[:, None]
+    h = oracle.gate_up(blob, H, I, wbits, q[0], d[0])["h"]
+    qh, dh = oracle.q8_0(h)
+    y, dots = oracle.down(blob, H, I, wbits, qh, dh, want_dots=True)
+    ref = Wd @ (qh.astype(np.float64) * np.repeat(dh.astype(np.float64), 32))
+    assert np.allclose(y, ref.astype(np.float32), rtol=1e-6, atol=1e-9)
+    assert dots.shape == (H, I // 32)
+
+
+def test_expert_chain_quantises_h():
+    shape, blob, x, q, d = _tiny_inputs()
+    out = oracle.expert(blob, shape.hidden, shape.inter, 4, q[1], d[1])
+    qh, dh = oracle.q8_0(out["h"])
+    assert np.array_equal(out["qh"], qh) and np.array_equal(out["dh"], dh)
+    y, _ = oracle.down(blob, shape.hidden, shape.inter, 4, qh, dh)
+    assert np.array_equal(out["y"], y)
+
+
+def test_grid_exact_ffn_dots_are_textbook_gemv():
+    """Integer-valued activations with block amax 127 (d = 1) and unit row
+    scales: g equals the plain integer GEMV of the codes."""
+    H, I = 256, 64
+    rng = np.random.default_rng(13)
+    codes = rng.integers(-8, 8, (3, I if True else 0, H)).astype(np.int8)
+    gate = np.concatenate([oracle.pack(codes[0, r], 4) for r in range(I)])
+    up = np.concatenate([oracle.pack(codes[1, r], 4) for r in range(I)])
+    dcodes = rng.integers(-8, 8, (H, I)).astype(np.int8)
+    down = np.concatenate([oracle.pack(dcodes[j], 4) for j in range(H)])
+    scales = np.ones(2 * I + H, np.float32)
+    blob = np.concatenate([gate, up, down, scales.view(np.uint8)])
+    xi = rng.integers(-127, 128, H)
+    xi.reshape(-1, 32)[:, 0] = 127
+    q, d = oracle.q8_0(xi.astype(np.float32))
+    out = oracle.gate_up(blob, H, I, 4, q, d)
+    assert np.array_equal(out["g"], (codes[0].astype(np.int64) @ xi).astype(np.float64))
+    assert np.array_equal(out["u"], (codes[1].astype(np.int64) @ xi).astype(np.float64))
+
+
+# ------------------------------------------------------------------ combine and layer
+
+def test_combine_vs_numpy():
+    rng = np.random.default_rng(14)
+    T, K, H = 3, 4, 64
+    eo = rng.standard_normal((T, K, H)).astype(np.float32)
+    w = rng.uniform(0, 1, (T, K)).astype(np.float32)
+    sh = rng.standard_normal((T, H)).astype(np.float32)
+    res = rng.standard_normal((T, H)).astype(np.float32)
+    y = oracle.combine(eo, w, sh)
+    ref = sh.astype(np.float64) + np.einsum("tk,tkh->th", w.astype(np.float64), eo)
+    assert np.allclose(y, ref.astype(np.float32), rtol=1e-6, atol=1e-7)
+    y2, yn = oracle.combine(eo, w, sh, res, want_norm=True)
+    ref2 = ref + res
+    assert np.allclose(y2, ref2.astype(np.float32), rtol=1e-6, atol=1e-7)
+    ms = np.mean(ref2 ** 2, axis=1, keepdims=True)
+    assert np.allclose(yn, ref2 / np.sqrt(ms + 1e-5), rtol=1e-6, atol=1e-7)
+    # scale invariance of the norm (eps negligible at this scale)
+    assert np.allclose(oracle.rmsnorm(8 * y2), oracle.rmsnorm(y2), rtol=1e-5, atol=1e-6)
+
+
+def _tiny_layer(blob_of, shared, T=4, seed=100):
+    shape = synth.TINY
+    x = synth.tokens(shape, seed, T)
+    wr = synth.router_weights(shape, seed)
+    bias = synth.router_bias_uniform(shape, seed)
+    return oracle.layer(x, wr, bias, blob_of, shared, H=shape.hidden, I=shape.inter,
+                        n_experts=shape.n_experts, n_group=shape.n_group,
+                        topk_group=shape.topk_group, top_k=shape.top_k,
+                        scale=shape.routed_scaling)
+
+
+def test_layer_identical_experts_closed_form():
+    """All routed experts identical -> y = shared(x) + 2.5 * expert(x)."""
+    blob = synth.expert_blob(synth.TINY, 100, 0, 0)
+    shared = synth.expert_blob(synth.TINY, 100, 0, synth.SHARED_ID)
+    out = _tiny_layer(lambda e: blob, shared)
+    for t in range(4):
+        e_y = oracle.expert(blob, 256, 128, 4, out["q"][t], out["d"][t])["y"].astype(np.float64)
+        ref = out["shared_out"][t].astype(np.float64) + 2.5 * e_y
+        assert np.max(np.abs(out["y"][t] - ref)) <= 1e-6 * np.sqrt(np.mean(ref ** 2)) + 1e-7
+
+
+def test_layer_zero_routed_experts_gives_shared_only():
+    zero = synth.expert_blob(synth.TINY, 100, 0, 0)
+    nb = 3 * 256 * 128 // 2
+    zero[:nb] = 0  # all codes 0, scales kept
+    shared = synth.expert_blob(synth.TINY, 100, 0, synth.SHARED_ID)
+    out = _tiny_layer(lambda e: zero, shared)
+    assert np.all(out["expert_out"] == 0)
+    assert np.array_equal(out["y"], out["shared_out"])
+
+
+def test_layer_groups_cover_every_slot_once():
+    shape = synth.TINY
+    blobs = {}
+
+    def blob_of(e):
+        blobs[e] = blobs.get(e) or 0
+        blobs[e] += 1
+        return synth.expert_blob(shape, 100, 0, e)
+
+    out = _tiny_layer(blob_of, None)
+    g = out["groups"]
+    # batch union: every distinct expert is fetched exactly once
+    assert sorted(blobs) == sorted(set(out["idx"].ravel().tolist()))
+    assert all(v == 1 for v in blobs.values())
+    assert g["counts"].sum() == out["idx"].size
