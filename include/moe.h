@@ -1,0 +1,224 @@
+/*
+ * libmoe — one routed Mixture-of-Experts layer step on an AMD MI355X (gfx950).
+ *
+ * The step, as the pages describe it ("Show HN: 遅いコンピュータで GLM 5.2 を
+ * 実行する", ja.news.hada.io, section 実装済みの主な機能; "Comment exécuter un
+ * réseau de neurones de 744 milliards de paramètres sur un ordinateur
+ * ordinaire", devtrends.cc, section "Comment fonctionne le moteur"):
+ *   1. a DeepSeek-V3-style sigmoid router with noaux_tc group-limited top-k,
+ *      routed_scaling_factor, and a shared expert;
+ *   2. Q8_0-style int8 activations;
+ *   3. batch union: each distinct expert selected by a batch is read once and
+ *      applied to every token routed to it;
+ *   4. expert FFNs whose three matrices are packed int4 (or int2) codes with
+ *      one scale per row, dequantised on use, multiplied against the int8
+ *      activations with exact integer accumulation;
+ *   5. the weighted sum of the routed experts plus the shared expert.
+ *
+ * Conventions for every call:
+ *   - cfg (and any moe_ffn_debug) is a host pointer; every other pointer is a
+ *     DEVICE pointer to caller-owned memory, at least 16-byte aligned.
+ *   - The library never allocates or frees device memory and never copies
+ *     between host and device.  Scratch memory comes from a caller-provided
+ *     workspace whose size is given by the matching *_workspace() query.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream), in order, without host synchronisation.  Returning 0 means
+ *     the work was enqueued; device-side faults surface at the caller's next
+ *     synchronisation, as for any HIP call.
+ *   - On a non-zero return nothing has been enqueued.  moe_strerror() names
+ *     the code; moe_last_error() gives a per-thread message with details.
+ *   - T = 0 tokens is a valid no-op.
+ *   - Results are bit-identical from run to run for fixed inputs and device
+ *     (no floating-point atomics).
+ *   - Calls are reentrant; they keep no state beyond the per-thread message.
+ *
+ * Data layouts (row-major):
+ *   x        fp32 [T][H]        token hidden states
+ *   w_router fp32 [E][H]        router matrix, one row per routed expert
+ *   bias     fp32 [E]           noaux_tc correction bias (selection only)
+ *   idx      int32 [T][K]       selected experts, rank order
+ *   w        fp32 [T][K]        routing weights, rank order
+ *   q, d     int8 [T][n], fp32 [T][n/32]   Q8_0 codes and block scales
+ *   expert records: moe_expert_blob_bytes(cfg) bytes per expert, routed
+ *     expert e at experts + e * blob_bytes; layout of one record:
+ *       gate codes [I][H*wbits/8] | up codes [I][H*wbits/8] |
+ *       down codes [H][I*wbits/8] | gate scale fp32 [I] | up scale fp32 [I] |
+ *       down scale fp32 [H]
+ *     int4: element 2j in the low nibble of byte j, 2j+1 in the high nibble;
+ *     int2: element 4j+i in bits 2i..2i+1; codes are two's complement and
+ *     every bit pattern is a valid code.  Weight value = scale[row] * code.
+ *     The blob base pointer must be 256-byte aligned (so is every record,
+ *     since blob_bytes is a multiple of 256 for supported shapes).
+ */
+#ifndef LIBMOE_H
+#define LIBMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)     /* bad shape, count or null required pointer */
+#define MOE_EALIGN (-2)     /* pointer not aligned as documented */
+#define MOE_EWORKSPACE (-3) /* workspace missing or smaller than required */
+#define MOE_EHIP (-4)       /* a HIP launch failed; see moe_last_error() */
+
+/* Layer shape.  Supported: hidden % 256 == 0, inter % 128 == 0,
+ * 2 <= n_experts <= 1024, n_experts % n_group == 0 with at least 2 experts
+ * per group, n_group <= 64, 1 <= topk_group <= n_group,
+ * 1 <= top_k <= min(16, topk_group * n_experts / n_group), n_shared in {0,1},
+ * wbits in {4, 2}. */
+typedef struct moe_cfg {
+  int32_t hidden;       /* H */
+  int32_t inter;        /* I, intermediate width of every expert (shared too) */
+  int32_t n_experts;    /* E, routed experts */
+  int32_t n_group;      /* G, expert groups for group-limited routing */
+  int32_t topk_group;   /* TG, groups kept per token */
+  int32_t top_k;        /* K, routed experts per token */
+  int32_t n_shared;     /* 0 or 1 shared expert */
+  int32_t wbits;        /* 4 (packed int4) or 2 (packed int2) */
+  float routed_scaling; /* routed_scaling_factor applied to routed weights */
+} moe_cfg;
+
+/* Bytes of one packed expert record for cfg (0 if cfg is unsupported). */
+size_t moe_expert_blob_bytes(const moe_cfg *cfg);
+
+/* ---------------------------------------------------------------------------
+ * moe_route — router ("Show HN…", 実装済みの主な機能, router item: sigmoid
+ * scores, noaux_tc, routed_scaling_factor).
+ *   s[t,e]  = sigmoid(x[t] . w_router[e]), computed in fp32 in one fixed order:
+ *             the dot product runs over consecutive chunks of 64 elements,
+ *             each an fma chain in increasing index from 0, chunk partials added
+ *             left to right; e^y uses Cody–Waite reduction by ln 2 and a
+ *             degree-7 Taylor polynomial (fma Horner), then scaling by 2^n;
+ *             sigmoid(l) = 1 / (1 + e^-l).
+ *   sb[t,e] = s[t,e] + bias[e]                    (bias used for selection only)
+ *   group score = sum of the two largest sb in each of the G contiguous groups;
+ *   the TG best groups are kept (ties: lower group index); the K best experts
+ *   of the kept groups by sb (ties: lower expert index) are written to idx in
+ *   rank order; w[t,k] = (s[t,idx] / S) * routed_scaling with
+ *   S = sum_k s[t,idx[t,k]] added in rank order (fp32).
+ * idx and w are bit-identical to a CPU implementation of the same steps.
+ * workspace: >= moe_route_workspace(cfg, T) bytes (may be NULL if that is 0).
+ * Errors: MOE_EINVAL (cfg, T < 0, null pointer), MOE_EALIGN, MOE_EWORKSPACE.
+ * ------------------------------------------------------------------------- */
+size_t moe_route_workspace(const moe_cfg *cfg, int32_t T);
+int moe_route(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
+              const float *bias, int32_t *idx, float *w, void *workspace, size_t ws_bytes,
+              void *stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_quant_act — Q8_0-style int8 activations ("Show HN…", 実装済みの主な機能,
+ * integer-dot item).  For each of `rows` rows of n floats and each block of 32:
+ *   d = amax / 127 (fp32, correctly rounded), id = d != 0 ? 1/d : 0,
+ *   q = clamp(roundf(x * id), -127, 127)  (round half away from zero).
+ * Bit-identical to the same steps on a CPU.  n % 32 == 0.
+ * Errors: MOE_EINVAL (rows < 0, n <= 0 or n % 32, null pointer), MOE_EALIGN.
+ * ------------------------------------------------------------------------- */
+int moe_quant_act(int32_t rows, int32_t n, const float *x, int8_t *q, float *d, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_group — batch-union grouping ("Show HN…", 実装済みの主な機能, batch-union
+ * MoE item; devtrends, "Comment fonctionne le moteur": duplicate requests
+ * for one expert are merged).  Slots s = t*K + k of idx [T][K]:
+ *   counts[e]   number of slots routed to e                       int32 [E]
+ *   offsets[e]  exclusive prefix sum of counts, offsets[E] = T*K  int32 [E+1]
+ *   perm        slots grouped by expert, increasing slot (= token) order
+ *               inside each expert                                int32 [T*K]
+ *   inv[s]      position of slot s in perm                        int32 [T*K]
+ *   active      experts with counts > 0, ascending, then -1       int32 [E]
+ *   n_active    number of such experts                            int32 [1]
+ * idx entries outside [0, E) are skipped (they get no position; perm and inv
+ * entries for them are left unwritten).  Bit-identical to a stable counting
+ * sort on the CPU.
+ * Errors: MOE_EINVAL (cfg, T < 0, null pointer), MOE_EALIGN.
+ * ------------------------------------------------------------------------- */
+int moe_group(const moe_cfg *cfg, int32_t T, const int32_t *idx, int32_t *counts,
+              int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
+              int32_t *n_active, void *stream);
+
+/* Optional device buffers a test can pass to moe_expert_ffn to receive the
+ * intermediate results (any member may be NULL; pass NULL for the struct in
+ * production).  Pair p < T*K is slot p (token p / K, rank p % K); pair
+ * T*K + t is the shared expert applied to token t.  P = T*K + T*n_shared.
+ *   gate_dots, up_dots  int32 [P][I][H/32]  exact block dots of code . q
+ *   h                   fp32  [P][I]        silu(gate) * up
+ *   q_h, d_h            int8 [P][I], fp32 [P][I/32]   Q8_0 of h
+ *   down_dots           int32 [P][H][I/32]  exact block dots of code . q_h   */
+typedef struct moe_ffn_debug {
+  int32_t *gate_dots;
+  int32_t *up_dots;
+  float *h;
+  int8_t *q_h;
+  float *d_h;
+  int32_t *down_dots;
+} moe_ffn_debug;
+
+/* ---------------------------------------------------------------------------
+ * moe_expert_ffn — the routed and shared expert FFNs ("Show HN…",
+ * 実装済みの主な機能: quantisation-kernel item, packed int4/int2 with per-row
+ * scales, dequantised on use; integer-dot item; batch-union item).
+ * For each selected (token t, expert e) and for the shared expert on every
+ * token, with q, d the Q8_0 activations of x (moe_quant_act):
+ *   g[r] = sg[r] * sum_b d[t,b] * P_gate[r,b],  P = exact int32 block dots
+ *   u[r] = su[r] * sum_b d[t,b] * P_up[r,b]
+ *   h[r] = silu(g[r]) * u[r],  silu(z) = z / (1 + e^-z)
+ *   (q_h, d_h) = Q8_0(h)
+ *   y[j] = sd[j] * sum_b d_h[b] * P_down[j,b]
+ * expert_out [T][K][H] receives y of slot (t, k) (unweighted);
+ * shared_out [T][H] receives the shared expert's y (required iff n_shared).
+ * Grouping (moe_group) runs inside this call on idx, so every distinct
+ * expert's weights are streamed once for all its tokens.
+ * experts: E records (see layout above); shared: one record or NULL.
+ * Errors: MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP.
+ * ------------------------------------------------------------------------- */
+size_t moe_expert_ffn_workspace(const moe_cfg *cfg, int32_t T);
+int moe_expert_ffn(const moe_cfg *cfg, int32_t T, const int8_t *q, const float *d,
+                   const int32_t *idx, const void *experts, const void *shared,
+                   float *expert_out, float *shared_out, void *workspace, size_t ws_bytes,
+                   const moe_ffn_debug *dbg, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_combine — weighted sum of the routed experts plus the shared expert
+ * ("Show HN…", 実装済みの主な機能, router item: routed_scaling_factor and
+ * shared expert):
+ *   y[t] = residual[t] + shared_out[t] + sum_k w[t,k] * expert_out[t,k]
+ * residual and shared_out may be NULL (treated as 0).  If y_norm is not NULL
+ * it receives y[t] / sqrt(mean(y[t]^2) + eps) (unit-gain RMSNorm, the input
+ * of the next layer in a pre-norm stack).
+ * Errors: MOE_EINVAL, MOE_EALIGN.
+ * ------------------------------------------------------------------------- */
+int moe_combine(int32_t T, int32_t H, int32_t K, const float *expert_out, const float *w,
+                const float *shared_out, const float *residual, float *y, float *y_norm,
+                float eps, void *stream);
+
+/* Unit-gain RMSNorm of T rows of H floats: y = x / sqrt(mean(x^2) + eps). */
+int moe_rmsnorm(int32_t T, int32_t H, const float *x, float *y, float eps, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_layer — the whole step: moe_route, moe_quant_act, moe_expert_ffn and
+ * moe_combine on one stream, with all intermediates in the workspace.
+ * x [T][H] is the (already normalised) layer input; y [T][H] the output
+ * (plus residual when given); y_norm optional as in moe_combine.  idx_out and
+ * w_out ([T][K], nullable) receive the routing decision.
+ * Errors: as the calls it makes.
+ * ------------------------------------------------------------------------- */
+size_t moe_layer_workspace(const moe_cfg *cfg, int32_t T);
+int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
+              const float *bias, const void *experts, const void *shared,
+              const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
+              float *w_out, void *workspace, size_t ws_bytes, void *stream);
+
+/* Name of a return code, and the calling thread's last detailed message. */
+const char *moe_strerror(int code);
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBMOE_H */

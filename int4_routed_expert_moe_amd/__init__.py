@@ -1,0 +1,277 @@
+"""Python binding of libmoe (the routed-MoE layer step for MI355X / gfx950).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libmoe.so`` behind the C ABI declared in ``include/moe.h``.  PyTorch supplies
+device memory (tensors) and the HIP stream (``torch.cuda.current_stream()``,
+which is a HIP stream under PyTorch-ROCm).  There is no fallback: if the
+library is not built, or a tensor is not on the GPU, calls raise.
+
+Functions mirror the C entry points: ``route``, ``quant_act``, ``group``,
+``expert_ffn``, ``combine``, ``rmsnorm``, ``layer`` (+ workspace queries).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+
+EXPORTS = (
+    "moe_expert_blob_bytes", "moe_route_workspace", "moe_route", "moe_quant_act", "moe_group",
+    "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_combine", "moe_rmsnorm",
+    "moe_layer_workspace", "moe_layer", "moe_strerror", "moe_last_error",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libmoe error {code}: {msg}")
+        self.code = code
+
+
+class MoeCfg(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
+                ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32), ("wbits", ctypes.c_int32),
+                ("routed_scaling", ctypes.c_float)]
+
+
+class MoeFfnDebug(ctypes.Structure):
+    _fields_ = [("gate_dots", ctypes.c_void_p), ("up_dots", ctypes.c_void_p),
+                ("h", ctypes.c_void_p), ("q_h", ctypes.c_void_p), ("d_h", ctypes.c_void_p),
+                ("down_dots", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
+                           "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    v, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    pc = ctypes.POINTER(MoeCfg)
+    L.moe_expert_blob_bytes.argtypes = [pc]
+    L.moe_expert_blob_bytes.restype = sz
+    L.moe_route_workspace.argtypes = [pc, i32]
+    L.moe_route_workspace.restype = sz
+    L.moe_route.argtypes = [pc, i32, v, v, v, v, v, v, sz, v]
+    L.moe_route.restype = ctypes.c_int
+    L.moe_quant_act.argtypes = [i32, i32, v, v, v, v]
+    L.moe_quant_act.restype = ctypes.c_int
+    L.moe_group.argtypes = [pc, i32, v, v, v, v, v, v, v, v]
+    L.moe_group.restype = ctypes.c_int
+    L.moe_expert_ffn_workspace.argtypes = [pc, i32]
+    L.moe_expert_ffn_workspace.restype = sz
+    L.moe_expert_ffn.argtypes = [pc, i32, v, v, v, v, v, v, v, v, sz,
+                                 ctypes.POINTER(MoeFfnDebug), v]
+    L.moe_expert_ffn.restype = ctypes.c_int
+    L.moe_combine.argtypes = [i32, i32, i32, v, v, v, v, v, v, f32, v]
+    L.moe_combine.restype = ctypes.c_int
+    L.moe_rmsnorm.argtypes = [i32, i32, v, v, f32, v]
+    L.moe_rmsnorm.restype = ctypes.c_int
+    L.moe_layer_workspace.argtypes = [pc, i32]
+    L.moe_layer_workspace.restype = sz
+    L.moe_layer.argtypes = [pc, i32, v, v, v, v, v, v, v, v, f32, v, v, v, sz, v]
+    L.moe_layer.restype = ctypes.c_int
+    L.moe_strerror.argtypes = [ctypes.c_int]
+    L.moe_strerror.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != MOE_OK:
+        L = lib()
+        raise MoeError(rc, f"{L.moe_strerror(rc).decode()}: {L.moe_last_error().decode()}")
+
+
+@dataclass(frozen=True)
+class Config:
+    hidden: int
+    inter: int
+    n_experts: int
+    n_group: int
+    topk_group: int
+    top_k: int
+    n_shared: int = 1
+    wbits: int = 4
+    routed_scaling: float = 2.5
+
+    @classmethod
+    def of(cls, shape) -> "Config":
+        return cls(shape.hidden, shape.inter, shape.n_experts, shape.n_group, shape.topk_group,
+                   shape.top_k, shape.n_shared, shape.wbits, shape.routed_scaling)
+
+    def c(self) -> MoeCfg:
+        return MoeCfg(self.hidden, self.inter, self.n_experts, self.n_group, self.topk_group,
+                      self.top_k, self.n_shared, self.wbits, self.routed_scaling)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def blob_bytes(cfg: Config) -> int:
+    return int(lib().moe_expert_blob_bytes(ctypes.byref(cfg.c())))
+
+
+def route_workspace(cfg: Config, T: int) -> int:
+    return int(lib().moe_route_workspace(ctypes.byref(cfg.c()), T))
+
+
+def expert_ffn_workspace(cfg: Config, T: int) -> int:
+    return int(lib().moe_expert_ffn_workspace(ctypes.byref(cfg.c()), T))
+
+
+def layer_workspace(cfg: Config, T: int) -> int:
+    return int(lib().moe_layer_workspace(ctypes.byref(cfg.c()), T))
+
+
+def _workspace(nbytes, device, ws=None):
+    torch = _torch()
+    if ws is not None:
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def route(cfg: Config, x, w_router, bias, idx=None, w=None, workspace=None):
+    """moe_route: returns (idx int32 [T,K], w fp32 [T,K])."""
+    torch = _torch()
+    T = x.shape[0]
+    idx = idx if idx is not None else torch.empty((T, cfg.top_k), dtype=torch.int32,
+                                                  device=x.device)
+    w = w if w is not None else torch.empty((T, cfg.top_k), dtype=torch.float32, device=x.device)
+    ws = _workspace(route_workspace(cfg, T), x.device, workspace)
+    _check(lib().moe_route(ctypes.byref(cfg.c()), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                           _ptr(idx), _ptr(w), _ptr(ws), ws.numel(), _stream()))
+    return idx, w
+
+
+def quant_act(x, q=None, d=None):
+    """moe_quant_act on the rows of x: returns (q int8, d fp32 [..., n/32])."""
+    torch = _torch()
+    n = x.shape[-1]
+    rows = x.numel() // n if n else 0
+    q = q if q is not None else torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    d = d if d is not None else torch.empty(x.shape[:-1] + (n // 32,), dtype=torch.float32,
+                                            device=x.device)
+    _check(lib().moe_quant_act(rows, n, _ptr(x), _ptr(q), _ptr(d), _stream()))
+    return q, d
+
+
+def group(cfg: Config, idx):
+    """moe_group: dict of counts, offsets, perm, inv, active, n_active (device tensors)."""
+    torch = _torch()
+    T = idx.shape[0]
+    E, S = cfg.n_experts, T * cfg.top_k
+    dev = idx.device
+    out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               perm=torch.empty(max(S, 1), dtype=torch.int32, device=dev),
+               inv=torch.empty(max(S, 1), dtype=torch.int32, device=dev),
+               active=torch.empty(E, dtype=torch.int32, device=dev),
+               n_active=torch.empty(1, dtype=torch.int32, device=dev))
+    _check(lib().moe_group(ctypes.byref(cfg.c()), T, _ptr(idx), _ptr(out["counts"]),
+                           _ptr(out["offsets"]), _ptr(out["perm"]), _ptr(out["inv"]),
+                           _ptr(out["active"]), _ptr(out["n_active"]), _stream()))
+    return out
+
+
+def debug_buffers(cfg: Config, T: int, device):
+    """Device buffers for every intermediate moe_expert_ffn can report."""
+    torch = _torch()
+    P = T * cfg.top_k + T * cfg.n_shared
+    H, I = cfg.hidden, cfg.inter
+    return dict(gate_dots=torch.zeros((P, I, H // 32), dtype=torch.int32, device=device),
+                up_dots=torch.zeros((P, I, H // 32), dtype=torch.int32, device=device),
+                h=torch.zeros((P, I), dtype=torch.float32, device=device),
+                q_h=torch.zeros((P, I), dtype=torch.int8, device=device),
+                d_h=torch.zeros((P, I // 32), dtype=torch.float32, device=device),
+                down_dots=torch.zeros((P, H, I // 32), dtype=torch.int32, device=device))
+
+
+def expert_ffn(cfg: Config, q, d, idx, experts, shared=None, expert_out=None, shared_out=None,
+               workspace=None, debug=None):
+    """moe_expert_ffn: returns (expert_out [T,K,H], shared_out [T,H] or None)."""
+    torch = _torch()
+    T = q.shape[0]
+    dev = q.device
+    H = cfg.hidden
+    expert_out = expert_out if expert_out is not None else torch.empty(
+        (T, cfg.top_k, H), dtype=torch.float32, device=dev)
+    if cfg.n_shared and shared_out is None:
+        shared_out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = _workspace(expert_ffn_workspace(cfg, T), dev, workspace)
+    dbg = None
+    if debug is not None:
+        dbg = MoeFfnDebug(*[(_ptr(debug[k]) if debug.get(k) is not None else None)
+                            for k in ("gate_dots", "up_dots", "h", "q_h", "d_h", "down_dots")])
+    _check(lib().moe_expert_ffn(ctypes.byref(cfg.c()), T, _ptr(q), _ptr(d), _ptr(idx),
+                                _ptr(experts), _ptr(shared), _ptr(expert_out), _ptr(shared_out),
+                                _ptr(ws), ws.numel(), ctypes.byref(dbg) if dbg else None,
+                                _stream()))
+    return expert_out, shared_out
+
+
+def combine(expert_out, w, shared_out=None, residual=None, y=None, y_norm=None, eps=1e-5,
+            want_norm=False):
+    """moe_combine: returns y (and y_norm when want_norm)."""
+    torch = _torch()
+    T, K, H = expert_out.shape
+    y = y if y is not None else torch.empty((T, H), dtype=torch.float32, device=expert_out.device)
+    if want_norm and y_norm is None:
+        y_norm = torch.empty_like(y)
+    _check(lib().moe_combine(T, H, K, _ptr(expert_out), _ptr(w), _ptr(shared_out),
+                             _ptr(residual), _ptr(y), _ptr(y_norm), eps, _stream()))
+    return (y, y_norm) if want_norm else y
+
+
+def rmsnorm(x, y=None, eps=1e-5):
+    torch = _torch()
+    T, H = x.shape
+    y = y if y is not None else torch.empty_like(x)
+    _check(lib().moe_rmsnorm(T, H, _ptr(x), _ptr(y), eps, _stream()))
+    return y
+
+
+def layer(cfg: Config, x, w_router, bias, experts, shared=None, residual=None, y=None,
+          y_norm=None, eps=1e-5, want_norm=False, idx_out=None, w_out=None, workspace=None):
+    """moe_layer (whole step): returns y (and y_norm when want_norm)."""
+    torch = _torch()
+    T, H = x.shape
+    y = y if y is not None else torch.empty((T, H), dtype=torch.float32, device=x.device)
+    if want_norm and y_norm is None:
+        y_norm = torch.empty_like(y)
+    ws = _workspace(layer_workspace(cfg, T), x.device, workspace)
+    _check(lib().moe_layer(ctypes.byref(cfg.c()), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                           _ptr(experts), _ptr(shared), _ptr(residual), _ptr(y), _ptr(y_norm),
+                           eps, _ptr(idx_out), _ptr(w_out), _ptr(ws), ws.numel(), _stream()))
+    return (y, y_norm) if want_norm else y

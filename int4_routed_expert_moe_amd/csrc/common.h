@@ -1,0 +1,113 @@
+// Device helpers shared by the libmoe kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define QBLK 32
+#define WAVE 64
+
+namespace moe {
+
+// --- wave reductions (wave64; ds_swizzle/dpp chosen by the compiler) -------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    unsigned long long u = __shfl_xor(v, o, WAVE);
+    v = u > v ? u : v;
+  }
+  return v;
+}
+
+// --- order-preserving key of a float (no NaN); -0 is folded onto +0 -------
+__device__ __forceinline__ uint32_t float_key(float f) {
+  f = f + 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// --- packed int4 -> int8 lanes ---------------------------------------------
+// A 32-bit word holds 8 codes: byte i = (code 2i in bits 0..3, code 2i+1 in
+// bits 4..7).  lo16 returns the even codes times 16 as four int8, hi16 the
+// odd codes times 16; the sign of each nibble lands on the int8 sign bit.
+__device__ __forceinline__ int lo16(uint32_t v) { return (int)((v << 4) & 0xF0F0F0F0u); }
+__device__ __forceinline__ int hi16(uint32_t v) { return (int)(v & 0xF0F0F0F0u); }
+
+// Even / odd bytes of the 8 int8 activations (w0 = bytes 0..3, w1 = 4..7).
+__device__ __forceinline__ int even_bytes(uint32_t w0, uint32_t w1) {
+  return (int)__builtin_amdgcn_perm(w1, w0, 0x06040200u);
+}
+__device__ __forceinline__ int odd_bytes(uint32_t w0, uint32_t w1) {
+  return (int)__builtin_amdgcn_perm(w1, w0, 0x07050301u);
+}
+
+__device__ __forceinline__ int sdot4(int a, int b, int c) {
+  return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// Q8_0 activation block pre-split for the int4 dot: ev[j] = bytes
+// (8j, 8j+2, 8j+4, 8j+6), od[j] = (8j+1, 8j+3, 8j+5, 8j+7), j = 0..3.
+struct QBlock {
+  int ev[4];
+  int od[4];
+};
+
+__device__ __forceinline__ QBlock split_block(const uint4 a, const uint4 b) {
+  QBlock r;
+  r.ev[0] = even_bytes(a.x, a.y);
+  r.od[0] = odd_bytes(a.x, a.y);
+  r.ev[1] = even_bytes(a.z, a.w);
+  r.od[1] = odd_bytes(a.z, a.w);
+  r.ev[2] = even_bytes(b.x, b.y);
+  r.od[2] = odd_bytes(b.x, b.y);
+  r.ev[3] = even_bytes(b.z, b.w);
+  r.od[3] = odd_bytes(b.z, b.w);
+  return r;
+}
+
+// Exact dot of 32 int4 codes (16 bytes, w) with 32 int8 activations: returns
+// 16 * sum(code * q).  |result| <= 16 * 32 * 8 * 127 < 2^20.
+__device__ __forceinline__ int dot_int4_block16(const uint4 w, const QBlock &a) {
+  int acc = 0;
+  acc = sdot4(lo16(w.x), a.ev[0], acc);
+  acc = sdot4(hi16(w.x), a.od[0], acc);
+  acc = sdot4(lo16(w.y), a.ev[1], acc);
+  acc = sdot4(hi16(w.y), a.od[1], acc);
+  acc = sdot4(lo16(w.z), a.ev[2], acc);
+  acc = sdot4(hi16(w.z), a.od[2], acc);
+  acc = sdot4(lo16(w.w), a.ev[3], acc);
+  acc = sdot4(hi16(w.w), a.od[3], acc);
+  return acc;
+}
+
+// --- packed int2 -> int8 lanes ---------------------------------------------
+// A byte holds 4 codes (code i in bits 2i..2i+1).  For a 32-bit word (16
+// codes), field f in {0,1,2,3} of every byte shifted to bits 6..7 gives 64 *
+// code as int8; q needs bytes (4j+f) of the block, gathered per field.
+__device__ __forceinline__ int int2_field64(uint32_t v, int f) {
+  return (int)((v << (6 - 2 * f)) & 0xC0C0C0C0u);
+}
+
+// Activations of one 64-element int2 piece split by field: a[f][j] holds
+// bytes (16j + 4i + f), i = 0..3 ... see gather_int2.
+struct QBlock2 {
+  int f[4][4];  // [field][word j]: bytes q[16j + f], q[16j + 4 + f], q[16j+8+f], q[16j+12+f]
+};
+
+// Four int8 bytes selected from two words with byte selectors (v_perm).
+__device__ __forceinline__ int perm2(uint32_t lo, uint32_t hi, uint32_t sel) {
+  return (int)__builtin_amdgcn_perm(hi, lo, sel);
+}
+
+}  // namespace moe

@@ -1,0 +1,41 @@
+// Internal launch entry points of the libmoe kernels (host side).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+void launch_quant_act(const float *x, int8_t *q, float *d, int64_t n_elems, hipStream_t st);
+void launch_combine(int T, int H, int K, const float *eo, const float *w, const float *shared,
+                    const float *residual, float *y, float *yn, float eps, hipStream_t st);
+void launch_rmsnorm(int T, int H, const float *x, float *y, float eps, hipStream_t st);
+
+// Router: scores into s/sb [T][E] (workspace), then selection into idx/w.
+void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *wr,
+                          const float *bias, float *s, float *sb, hipStream_t st);
+void launch_router_select(const moe_cfg &c, int T, const float *s, const float *sb,
+                          int32_t *idx, float *w, hipStream_t st);
+
+void launch_group(int n_slots, int E, const int32_t *idx, int32_t *counts, int32_t *offsets,
+                  int32_t *perm, int32_t *inv, int32_t *active, int32_t *n_active,
+                  hipStream_t st);
+
+// Expert FFN over grouped tokens (dot-product GEMV path).
+struct FfnArgs {
+  int H, I, E, K, T, n_shared, wbits;
+  size_t blob_bytes;
+  const int8_t *q;
+  const float *d;
+  const uint8_t *experts;
+  const uint8_t *shared;
+  const int32_t *offsets, *perm, *active, *n_active;
+  float *h;        // [P][I] fp32 workspace
+  float *expert_out;
+  float *shared_out;
+  moe_ffn_debug dbg;
+};
+void launch_ffn_gemv(const FfnArgs &a, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,385 @@
+// libmoe C ABI: argument validation, workspace layout and kernel launches.
+// Every entry point either enqueues all of its work on the given stream and
+// returns MOE_OK, or returns an error code having enqueued nothing.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int check_cfg(const moe_cfg *c) {
+  if (!c) return fail(MOE_EINVAL, "cfg is NULL");
+  if (c->hidden <= 0 || c->hidden % 256)
+    return fail(MOE_EINVAL, "hidden=%d must be a positive multiple of 256", c->hidden);
+  if (c->inter <= 0 || c->inter % 128)
+    return fail(MOE_EINVAL, "inter=%d must be a positive multiple of 128", c->inter);
+  if (c->wbits != 4 && c->wbits != 2) return fail(MOE_EINVAL, "wbits=%d not in {4,2}", c->wbits);
+  const int per = c->wbits == 4 ? 32 : 64;
+  if (c->hidden / per > 256 || c->inter / per > 128)
+    return fail(MOE_EINVAL, "hidden=%d / inter=%d too large for wbits=%d", c->hidden, c->inter,
+                c->wbits);
+  if (c->n_experts < 2 || c->n_experts > 1024)
+    return fail(MOE_EINVAL, "n_experts=%d not in [2,1024]", c->n_experts);
+  if (c->n_group < 1 || c->n_group > 64 || c->n_experts % c->n_group ||
+      c->n_experts / c->n_group < 2)
+    return fail(MOE_EINVAL, "n_group=%d must divide n_experts=%d into groups of >= 2 (<= 64 groups)",
+                c->n_group, c->n_experts);
+  if (c->topk_group < 1 || c->topk_group > c->n_group)
+    return fail(MOE_EINVAL, "topk_group=%d not in [1, n_group]", c->topk_group);
+  const int cand = c->topk_group * (c->n_experts / c->n_group);
+  if (c->top_k < 1 || c->top_k > 16 || c->top_k > cand)
+    return fail(MOE_EINVAL, "top_k=%d not in [1, min(16, %d)]", c->top_k, cand);
+  if (c->n_shared != 0 && c->n_shared != 1)
+    return fail(MOE_EINVAL, "n_shared=%d not in {0,1}", c->n_shared);
+  if (!(c->routed_scaling > 0.0f) || c->routed_scaling > 1e30f)
+    return fail(MOE_EINVAL, "routed_scaling must be finite and > 0");
+  return MOE_OK;
+}
+
+#define REQUIRE(p, name)                                                       \
+  do {                                                                         \
+    if (!(p)) return fail(MOE_EINVAL, "%s is NULL", name);                     \
+    if (!aligned((p), 16)) return fail(MOE_EALIGN, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+#define OPTIONAL(p, name)                                                      \
+  do {                                                                         \
+    if ((p) && !aligned((p), 16)) return fail(MOE_EALIGN, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+int launched(const char *what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+size_t blob_bytes(const moe_cfg &c) {
+  return ((size_t)2 * c.inter * c.hidden + (size_t)c.hidden * c.inter) * (size_t)c.wbits / 8 +
+         sizeof(float) * ((size_t)2 * c.inter + c.hidden);
+}
+
+// workspace carving --------------------------------------------------------
+struct Carve {
+  uint8_t *base;
+  size_t off = 0;
+  template <class T>
+  T *take(size_t n) {
+    T *p = base ? reinterpret_cast<T *>(base + off) : nullptr;
+    off += up256(n * sizeof(T));
+    return p;
+  }
+};
+
+struct RouteWs {
+  float *s, *sb;
+};
+RouteWs carve_route(Carve &cv, const moe_cfg &c, int T) {
+  RouteWs r;
+  r.s = cv.take<float>((size_t)T * c.n_experts);
+  r.sb = cv.take<float>((size_t)T * c.n_experts);
+  return r;
+}
+
+struct FfnWs {
+  int32_t *counts, *offsets, *perm, *inv, *active, *n_active;
+  float *h;
+};
+FfnWs carve_ffn(Carve &cv, const moe_cfg &c, int T) {
+  FfnWs f;
+  const size_t slots = (size_t)T * c.top_k;
+  const size_t pairs = slots + (size_t)T * c.n_shared;
+  f.counts = cv.take<int32_t>(c.n_experts);
+  f.offsets = cv.take<int32_t>(c.n_experts + 1);
+  f.perm = cv.take<int32_t>(slots);
+  f.inv = cv.take<int32_t>(slots);
+  f.active = cv.take<int32_t>(c.n_experts);
+  f.n_active = cv.take<int32_t>(1);
+  f.h = cv.take<float>(pairs * c.inter);
+  return f;
+}
+
+struct LayerWs {
+  RouteWs route;
+  int32_t *idx;
+  float *w;
+  int8_t *q;
+  float *d;
+  float *expert_out, *shared_out;
+  FfnWs ffn;
+};
+LayerWs carve_layer(Carve &cv, const moe_cfg &c, int T) {
+  LayerWs l;
+  l.route = carve_route(cv, c, T);
+  l.idx = cv.take<int32_t>((size_t)T * c.top_k);
+  l.w = cv.take<float>((size_t)T * c.top_k);
+  l.q = cv.take<int8_t>((size_t)T * c.hidden);
+  l.d = cv.take<float>((size_t)T * c.hidden / 32);
+  l.expert_out = cv.take<float>((size_t)T * c.top_k * c.hidden);
+  l.shared_out = cv.take<float>((size_t)T * c.hidden * c.n_shared);
+  l.ffn = carve_ffn(cv, c, T);
+  return l;
+}
+
+// unchecked enqueue helpers (arguments validated by the callers) ------------
+int do_route(const moe_cfg &c, int T, const float *x, const float *wr, const float *bias,
+             int32_t *idx, float *w, const RouteWs &ws, hipStream_t st) {
+  moe::launch_router_scores(c, T, x, wr, bias, ws.s, ws.sb, st);
+  moe::launch_router_select(c, T, ws.s, ws.sb, idx, w, st);
+  return launched("moe_route");
+}
+
+int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32_t *idx,
+           const void *experts, const void *shared, float *expert_out, float *shared_out,
+           const FfnWs &ws, const moe_ffn_debug *dbg, hipStream_t st) {
+  moe::launch_group(T * c.top_k, c.n_experts, idx, ws.counts, ws.offsets, ws.perm, ws.inv,
+                    ws.active, ws.n_active, st);
+  moe::FfnArgs a;
+  a.H = c.hidden;
+  a.I = c.inter;
+  a.E = c.n_experts;
+  a.K = c.top_k;
+  a.T = T;
+  a.n_shared = c.n_shared;
+  a.wbits = c.wbits;
+  a.blob_bytes = blob_bytes(c);
+  a.q = q;
+  a.d = d;
+  a.experts = static_cast<const uint8_t *>(experts);
+  a.shared = static_cast<const uint8_t *>(shared);
+  a.offsets = ws.offsets;
+  a.perm = ws.perm;
+  a.active = ws.active;
+  a.n_active = ws.n_active;
+  a.h = ws.h;
+  a.expert_out = expert_out;
+  a.shared_out = shared_out;
+  if (dbg) a.dbg = *dbg;
+  else memset(&a.dbg, 0, sizeof(a.dbg));
+  moe::launch_ffn_gemv(a, st);
+  return launched("moe_expert_ffn");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_expert_blob_bytes(const moe_cfg *cfg) {
+  if (check_cfg(cfg) != MOE_OK) return 0;
+  return blob_bytes(*cfg);
+}
+
+size_t moe_route_workspace(const moe_cfg *cfg, int32_t T) {
+  if (check_cfg(cfg) != MOE_OK || T < 0) return 0;
+  Carve cv{nullptr};
+  carve_route(cv, *cfg, T);
+  return cv.off;
+}
+
+int moe_route(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
+              const float *bias, int32_t *idx, float *w, void *workspace, size_t ws_bytes,
+              void *stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
+  if (T == 0) return MOE_OK;
+  REQUIRE(x, "x");
+  REQUIRE(w_router, "w_router");
+  REQUIRE(bias, "bias");
+  REQUIRE(idx, "idx");
+  REQUIRE(w, "w");
+  const size_t need = moe_route_workspace(cfg, T);
+  if (!workspace || ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "route workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned(workspace, 256)) return fail(MOE_EALIGN, "workspace is not 256-byte aligned");
+  Carve cv{static_cast<uint8_t *>(workspace)};
+  RouteWs ws = carve_route(cv, *cfg, T);
+  return do_route(*cfg, T, x, w_router, bias, idx, w, ws, (hipStream_t)stream);
+}
+
+int moe_quant_act(int32_t rows, int32_t n, const float *x, int8_t *q, float *d, void *stream) {
+  if (rows < 0) return fail(MOE_EINVAL, "rows=%d < 0", rows);
+  if (n <= 0 || n % 32) return fail(MOE_EINVAL, "n=%d must be a positive multiple of 32", n);
+  if (rows == 0) return MOE_OK;
+  REQUIRE(x, "x");
+  REQUIRE(q, "q");
+  REQUIRE(d, "d");
+  moe::launch_quant_act(x, q, d, (int64_t)rows * n, (hipStream_t)stream);
+  return launched("moe_quant_act");
+}
+
+int moe_group(const moe_cfg *cfg, int32_t T, const int32_t *idx, int32_t *counts,
+              int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
+              int32_t *n_active, void *stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
+  if (T == 0) return MOE_OK;
+  REQUIRE(idx, "idx");
+  REQUIRE(counts, "counts");
+  REQUIRE(offsets, "offsets");
+  REQUIRE(perm, "perm");
+  REQUIRE(inv, "inv");
+  REQUIRE(active, "active");
+  REQUIRE(n_active, "n_active");
+  moe::launch_group(T * cfg->top_k, cfg->n_experts, idx, counts, offsets, perm, inv, active,
+                    n_active, (hipStream_t)stream);
+  return launched("moe_group");
+}
+
+size_t moe_expert_ffn_workspace(const moe_cfg *cfg, int32_t T) {
+  if (check_cfg(cfg) != MOE_OK || T < 0) return 0;
+  Carve cv{nullptr};
+  carve_ffn(cv, *cfg, T);
+  return cv.off;
+}
+
+int moe_expert_ffn(const moe_cfg *cfg, int32_t T, const int8_t *q, const float *d,
+                   const int32_t *idx, const void *experts, const void *shared,
+                   float *expert_out, float *shared_out, void *workspace, size_t ws_bytes,
+                   const moe_ffn_debug *dbg, void *stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
+  if (T == 0) return MOE_OK;
+  REQUIRE(q, "q");
+  REQUIRE(d, "d");
+  REQUIRE(idx, "idx");
+  REQUIRE(experts, "experts");
+  REQUIRE(expert_out, "expert_out");
+  if (!aligned(experts, 256)) return fail(MOE_EALIGN, "experts is not 256-byte aligned");
+  if (cfg->n_shared) {
+    REQUIRE(shared, "shared");
+    REQUIRE(shared_out, "shared_out");
+    if (!aligned(shared, 256)) return fail(MOE_EALIGN, "shared is not 256-byte aligned");
+  }
+  if (dbg) {
+    OPTIONAL(dbg->gate_dots, "dbg->gate_dots");
+    OPTIONAL(dbg->up_dots, "dbg->up_dots");
+    OPTIONAL(dbg->h, "dbg->h");
+    OPTIONAL(dbg->q_h, "dbg->q_h");
+    OPTIONAL(dbg->d_h, "dbg->d_h");
+    OPTIONAL(dbg->down_dots, "dbg->down_dots");
+  }
+  const size_t need = moe_expert_ffn_workspace(cfg, T);
+  if (!workspace || ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "ffn workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned(workspace, 256)) return fail(MOE_EALIGN, "workspace is not 256-byte aligned");
+  Carve cv{static_cast<uint8_t *>(workspace)};
+  FfnWs ws = carve_ffn(cv, *cfg, T);
+  return do_ffn(*cfg, T, q, d, idx, experts, cfg->n_shared ? shared : nullptr, expert_out,
+                cfg->n_shared ? shared_out : nullptr, ws, dbg, (hipStream_t)stream);
+}
+
+int moe_combine(int32_t T, int32_t H, int32_t K, const float *expert_out, const float *w,
+                const float *shared_out, const float *residual, float *y, float *y_norm,
+                float eps, void *stream) {
+  if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
+  if (H <= 0 || H % 4) return fail(MOE_EINVAL, "H=%d must be a positive multiple of 4", H);
+  if (K < 0 || K > 16) return fail(MOE_EINVAL, "K=%d not in [0,16]", K);
+  if (!(eps >= 0.0f)) return fail(MOE_EINVAL, "eps must be >= 0");
+  if (T == 0) return MOE_OK;
+  if (K > 0) {
+    REQUIRE(expert_out, "expert_out");
+    REQUIRE(w, "w");
+  }
+  OPTIONAL(shared_out, "shared_out");
+  OPTIONAL(residual, "residual");
+  REQUIRE(y, "y");
+  OPTIONAL(y_norm, "y_norm");
+  moe::launch_combine(T, H, K, expert_out, w, shared_out, residual, y, y_norm, eps,
+                      (hipStream_t)stream);
+  return launched("moe_combine");
+}
+
+int moe_rmsnorm(int32_t T, int32_t H, const float *x, float *y, float eps, void *stream) {
+  if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
+  if (H <= 0 || H % 4) return fail(MOE_EINVAL, "H=%d must be a positive multiple of 4", H);
+  if (!(eps >= 0.0f)) return fail(MOE_EINVAL, "eps must be >= 0");
+  if (T == 0) return MOE_OK;
+  REQUIRE(x, "x");
+  REQUIRE(y, "y");
+  moe::launch_rmsnorm(T, H, x, y, eps, (hipStream_t)stream);
+  return launched("moe_rmsnorm");
+}
+
+size_t moe_layer_workspace(const moe_cfg *cfg, int32_t T) {
+  if (check_cfg(cfg) != MOE_OK || T < 0) return 0;
+  Carve cv{nullptr};
+  carve_layer(cv, *cfg, T);
+  return cv.off;
+}
+
+int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
+              const float *bias, const void *experts, const void *shared,
+              const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
+              float *w_out, void *workspace, size_t ws_bytes, void *stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
+  if (!(eps >= 0.0f)) return fail(MOE_EINVAL, "eps must be >= 0");
+  if (T == 0) return MOE_OK;
+  REQUIRE(x, "x");
+  REQUIRE(w_router, "w_router");
+  REQUIRE(bias, "bias");
+  REQUIRE(experts, "experts");
+  REQUIRE(y, "y");
+  OPTIONAL(residual, "residual");
+  OPTIONAL(y_norm, "y_norm");
+  OPTIONAL(idx_out, "idx_out");
+  OPTIONAL(w_out, "w_out");
+  if (!aligned(experts, 256)) return fail(MOE_EALIGN, "experts is not 256-byte aligned");
+  if (cfg->n_shared) {
+    REQUIRE(shared, "shared");
+    if (!aligned(shared, 256)) return fail(MOE_EALIGN, "shared is not 256-byte aligned");
+  }
+  const size_t need = moe_layer_workspace(cfg, T);
+  if (!workspace || ws_bytes < need)
+    return fail(MOE_EWORKSPACE, "layer workspace %zu < %zu bytes", ws_bytes, need);
+  if (!aligned(workspace, 256)) return fail(MOE_EALIGN, "workspace is not 256-byte aligned");
+  const moe_cfg &c = *cfg;
+  hipStream_t st = (hipStream_t)stream;
+  Carve cv{static_cast<uint8_t *>(workspace)};
+  LayerWs ws = carve_layer(cv, c, T);
+  int32_t *idx = idx_out ? idx_out : ws.idx;
+  float *w = w_out ? w_out : ws.w;
+  if ((rc = do_route(c, T, x, w_router, bias, idx, w, ws.route, st))) return rc;
+  moe::launch_quant_act(x, ws.q, ws.d, (int64_t)T * c.hidden, st);
+  if ((rc = launched("moe_layer quant"))) return rc;
+  if ((rc = do_ffn(c, T, ws.q, ws.d, idx, experts, c.n_shared ? shared : nullptr, ws.expert_out,
+                   c.n_shared ? ws.shared_out : nullptr, ws.ffn, nullptr, st)))
+    return rc;
+  moe::launch_combine(T, c.hidden, c.top_k, ws.expert_out, w,
+                      c.n_shared ? ws.shared_out : nullptr, residual, y, y_norm, eps, st);
+  return launched("moe_layer combine");
+}
+
+const char *moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EALIGN: return "misaligned pointer";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch failure";
+    default: return "unknown error";
+  }
+}
+
+const char *moe_last_error(void) { return g_msg; }
+
+}  // extern "C"

@@ -1,0 +1,189 @@
+// Router: sigmoid scores and noaux_tc group-limited top-k.
+//
+// Follows the router item of "Show HN: 遅いコンピュータで GLM 5.2 を実行する"
+// (ja.news.hada.io, section 実装済みの主な機能): a DeepSeek-V3-style sigmoid
+// router with noaux_tc selection and routed_scaling_factor.  The correction
+// bias takes part in selection only; the routing weights are the unbiased
+// sigmoid scores of the chosen experts, normalised and scaled.
+//
+// The fp32 arithmetic of the scores is fixed so that the chosen indices are
+// a function of the inputs alone (the same steps on a CPU give the same
+// bits): the dot product runs over consecutive 64-element chunks, each an fma
+// chain in increasing index starting from 0, and the chunk partials are
+// added left to right; e^y is a Cody–Waite reduction by ln 2 (split in a
+// 16-bit high part and a low part) followed by the degree-7 Taylor polynomial
+// of e^r in Horner form with fma, scaled by 2^n.  This file is compiled with
+// -ffp-contract=off and correctly rounded fp32 division.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__device__ __forceinline__ float exp_fixed(float y) {
+  y = y > 87.0f ? 87.0f : y;
+  y = y < -87.0f ? -87.0f : y;
+  const float n = __builtin_rintf(y * 1.44269502f);
+  float r = __builtin_fmaf(-n, 0.693145751953125f, y);
+  r = __builtin_fmaf(-n, 1.42860677e-06f, r);
+  float p = 1.98412701e-04f;            // 1/7!
+  p = __builtin_fmaf(p, r, 1.38888892e-03f);  // 1/6!
+  p = __builtin_fmaf(p, r, 8.33333377e-03f);  // 1/5!
+  p = __builtin_fmaf(p, r, 4.16666679e-02f);  // 1/4!
+  p = __builtin_fmaf(p, r, 1.66666672e-01f);  // 1/3!
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return __builtin_ldexpf(p, (int)n);
+}
+
+__device__ __forceinline__ float sigmoid_fixed(float l) { return 1.0f / (1.0f + exp_fixed(-l)); }
+
+// One wave per (expert, chunk of TT tokens).  Lane l owns the 64-element
+// chunks l, l+64, ...; each chunk is an fma chain over its 64 elements; the
+// chunk partials go to LDS and one lane per token adds them left to right.
+template <int TT>
+__global__ void __launch_bounds__(64) k_router_scores(int T, int H, int E,
+                                                      const float *__restrict__ x,
+                                                      const float *__restrict__ wr,
+                                                      const float *__restrict__ bias,
+                                                      float *__restrict__ s,
+                                                      float *__restrict__ sb) {
+  extern __shared__ float part[];  // [TT][nchunk]
+  const int e = blockIdx.x, t0 = blockIdx.y * TT, lane = threadIdx.x;
+  const int nchunk = H / 64;
+  const float *wrow = wr + (size_t)e * H;
+  for (int c = lane; c < nchunk; c += 64) {
+    float acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; t++) acc[t] = 0.0f;
+    const float4 *w4 = reinterpret_cast<const float4 *>(wrow + c * 64);
+#pragma unroll 4
+    for (int k4 = 0; k4 < 16; k4++) {
+      const float4 wv = w4[k4];
+#pragma unroll
+      for (int t = 0; t < TT; t++) {
+        if (t0 + t < T) {
+          const float4 xv =
+              reinterpret_cast<const float4 *>(x + (size_t)(t0 + t) * H + c * 64)[k4];
+          acc[t] = __builtin_fmaf(xv.x, wv.x, acc[t]);
+          acc[t] = __builtin_fmaf(xv.y, wv.y, acc[t]);
+          acc[t] = __builtin_fmaf(xv.z, wv.z, acc[t]);
+          acc[t] = __builtin_fmaf(xv.w, wv.w, acc[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TT; t++) part[t * nchunk + c] = acc[t];
+  }
+  __syncthreads();
+  if (lane < TT && t0 + lane < T) {
+    const float *p = part + lane * nchunk;
+    float tot = p[0];
+    for (int c = 1; c < nchunk; c++) tot = tot + p[c];
+    const float sv = sigmoid_fixed(tot);
+    const size_t o = (size_t)(t0 + lane) * E + e;
+    s[o] = sv;
+    sb[o] = sv + bias[e];
+  }
+}
+
+void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *wr,
+                          const float *bias, float *s, float *sb, hipStream_t st) {
+  const int H = c.hidden, E = c.n_experts;
+  const size_t lds = sizeof(float) * (size_t)(H / 64);
+  if (T <= 1) {
+    hipLaunchKernelGGL(k_router_scores<1>, dim3(E, T), dim3(64), lds, st, T, H, E, x, wr, bias,
+                       s, sb);
+  } else if (T <= 4) {
+    hipLaunchKernelGGL(k_router_scores<4>, dim3(E, 1), dim3(64), 4 * lds, st, T, H, E, x, wr,
+                       bias, s, sb);
+  } else {
+    hipLaunchKernelGGL(k_router_scores<8>, dim3(E, (T + 7) / 8), dim3(64), 8 * lds, st, T, H, E,
+                       x, wr, bias, s, sb);
+  }
+}
+
+// One wave per token.  Lane l holds experts l, l+64, ... (at most 16).
+//  1. group score = sum of the two largest sb of each group (lane g < G);
+//  2. TG rounds of a wave-wide max over (score, -group) keep the groups;
+//  3. K rounds of a wave-wide max over (sb, -expert) among kept groups pick
+//     the experts in rank order;
+//  4. w_k = (s_k / S) * scale, S summed in rank order.
+__global__ void __launch_bounds__(64) k_router_select(int E, int G, int TG, int K, float scale,
+                                                      const float *__restrict__ s,
+                                                      const float *__restrict__ sb,
+                                                      int32_t *__restrict__ idx,
+                                                      float *__restrict__ w) {
+  __shared__ float lsb[1024];
+  __shared__ float gscore[64];
+  __shared__ float ssel[16];
+  __shared__ int isel[16];
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const int gs = E / G;
+  const float *srow = s + (size_t)t * E;
+  const float *sbrow = sb + (size_t)t * E;
+  for (int e = lane; e < E; e += 64) lsb[e] = sbrow[e];
+  __syncthreads();
+  if (lane < G) {
+    float m1 = -INFINITY, m2 = -INFINITY;
+    for (int e = lane * gs; e < (lane + 1) * gs; e++) {
+      const float v = lsb[e];
+      if (v > m1) {
+        m2 = m1;
+        m1 = v;
+      } else if (v > m2) {
+        m2 = v;
+      }
+    }
+    gscore[lane] = m1 + m2;
+  }
+  __syncthreads();
+  bool kept = false;  // lane g < G: is group g kept
+  for (int j = 0; j < TG; j++) {
+    unsigned long long key = 0;
+    if (lane < G && !kept)
+      key = ((unsigned long long)float_key(gscore[lane]) << 32) | (0xFFFFFFFFu - (uint32_t)lane);
+    key = wave_max_u64(key);
+    int g = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+    g = (g >= 0 && g < G) ? g : 0;  // key 0 (no candidate) cannot occur for a valid cfg
+    if (lane == g) kept = true;
+  }
+  const unsigned long long kept_mask = __ballot(kept);
+  uint32_t taken = 0;  // bit j: expert lane + 64 j taken
+  for (int k = 0; k < K; k++) {
+    unsigned long long best = 0;
+    for (int j = 0; j * 64 + lane < E; j++) {
+      const int e = j * 64 + lane;
+      if (((kept_mask >> (e / gs)) & 1ull) && !((taken >> j) & 1u)) {
+        const unsigned long long key =
+            ((unsigned long long)float_key(lsb[e]) << 32) | (0xFFFFFFFFu - (uint32_t)e);
+        best = key > best ? key : best;
+      }
+    }
+    best = wave_max_u64(best);
+    int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
+    e = (e >= 0 && e < E) ? e : 0;  // as above: K <= candidates is validated on the host
+    if ((e & 63) == lane) taken |= 1u << (e >> 6);
+    if (lane == 0) {
+      isel[k] = e;
+      ssel[k] = srow[e];
+    }
+  }
+  __syncthreads();
+  if (lane == 0) {
+    float S = ssel[0];
+    for (int k = 1; k < K; k++) S = S + ssel[k];
+    for (int k = 0; k < K; k++) {
+      idx[(size_t)t * K + k] = isel[k];
+      w[(size_t)t * K + k] = (ssel[k] / S) * scale;
+    }
+  }
+}
+
+void launch_router_select(const moe_cfg &c, int T, const float *s, const float *sb,
+                          int32_t *idx, float *w, hipStream_t st) {
+  hipLaunchKernelGGL(k_router_select, dim3(T), dim3(64), 0, st, c.n_experts, c.n_group,
+                     c.topk_group, c.top_k, c.routed_scaling, s, sb, idx, w);
+}
+
+}  // namespace moe

@@ -1,0 +1,314 @@
+"""GPU parity: every libmoe call against the CPU oracle on seeded inputs.
+
+Bar: integer results (Q8_0 codes and scales, selected experts, grouping,
+int32 block dots) bit-exact; the router weights bit-exact (same fp32 steps);
+float layer outputs within max|err| <= 2e-3 * RMS(oracle output).
+Where fp32 decides an integer from a value the two sides compute differently
+(the Q8_0 of the SwiGLU output h), the oracle re-takes that decision on the
+GPU's own h in the same precision and must agree bit for bit.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import int4_routed_expert_moe_amd as moe
+import oracle
+import synth
+from _inputs import DeviceLayer, assert_close_rms
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    moe.lib()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def tiny(dev):
+    return DeviceLayer(synth.TINY, synth.SEEDS["tiny"])
+
+
+@pytest.fixture(scope="module")
+def real(dev):
+    return DeviceLayer(synth.REAL, synth.SEEDS["decode"])
+
+
+def to_d(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def h(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ------------------------------------------------------------------ generator
+
+def test_gpu_generator_matches_host(dev):
+    for shape in (synth.TINY, synth.REAL, synth.REAL.with_bits(2)):
+        bb = synth.blob_bytes(shape)
+        ids = [0, 3, synth.SHARED_ID]
+        out = torch.empty(len(ids) * bb, dtype=torch.uint8, device=dev)
+        synth.expert_blobs_gpu(shape, 11, 2, ids, out.data_ptr(), bb,
+                               torch.cuda.current_stream().cuda_stream)
+        got = h(out).reshape(len(ids), bb)
+        for i, e in enumerate(ids):
+            assert np.array_equal(got[i], synth.expert_blob(shape, 11, 2, e)), (shape, e)
+
+
+# ------------------------------------------------------------------ Q8_0
+
+@pytest.mark.parametrize("rows,n", [(1, 6144), (4, 256), (37, 2048), (3, 32), (2048, 6144)])
+def test_quant_act_bit_exact(dev, rows, n):
+    x = synth.normal(synth.key(5, rows, n), rows * n).reshape(rows, n)
+    x *= np.exp2(synth.normal(synth.key(6, rows, n), rows).astype(np.float32) * 4)[:, None]
+    x[0, :32] = 0.0
+    q, d = moe.quant_act(to_d(x, dev))
+    qo, do = oracle.q8_0(x)
+    assert np.array_equal(h(q), qo)
+    assert np.array_equal(h(d), do)
+
+
+def test_quant_act_hand_blocks_and_extremes(dev):
+    blocks = json.load(open(os.path.join(GOLDEN, "q8_0_blocks.json")))["blocks"]
+    rows = []
+    for b in blocks:
+        x = np.zeros(32, np.float32)
+        for k, v in b["x"].items():
+            x[int(k)] = v
+        rows.append(x)
+    rng = np.random.default_rng(0)
+    rows.append((rng.integers(-127, 128, 32)).astype(np.float32))
+    rows.append(np.full(32, 3.0e38, np.float32) * rng.choice([-1, 1], 32).astype(np.float32))
+    rows.append((rng.standard_normal(32) * 1e-30).astype(np.float32))
+    rows.append(np.linspace(-1, 1, 32, dtype=np.float32))
+    x = np.stack(rows)
+    q, d = moe.quant_act(to_d(x, dev))
+    qo, do = oracle.q8_0(x)
+    assert np.array_equal(h(q), qo)
+    assert np.array_equal(h(d), do)
+    for i, b in enumerate(blocks):
+        assert h(d)[i, 0] == np.float32(b["d"])
+
+
+# ------------------------------------------------------------------ router
+
+def _route_check(layer, x, dev):
+    s = layer.shape
+    cfg = moe.Config.of(s)
+    idx, w = moe.route(cfg, to_d(x, dev), layer.wr_d, layer.bias_d)
+    ri, rw, margin = oracle.route(x, layer.wr, layer.bias, s.n_group, s.topk_group, s.top_k,
+                                  s.routed_scaling)
+    assert np.array_equal(h(idx), ri)
+    assert np.array_equal(h(w).view(np.uint32), rw.view(np.uint32))
+    return margin
+
+
+def test_route_tiny(dev, tiny):
+    _route_check(tiny, synth.tokens(synth.TINY, synth.SEEDS["tiny"], 4), dev)
+
+
+@pytest.mark.parametrize("T,start", [(1, 0), (1, 1), (1, 7), (8, 100)])
+def test_route_decode(dev, real, T, start):
+    _route_check(real, synth.tokens(synth.REAL, synth.SEEDS["decode"], T, start=start), dev)
+
+
+@pytest.mark.parametrize("T", [4, 16])
+def test_route_verify(dev, real, T):
+    _route_check(real, synth.tokens_perturbed(synth.REAL, synth.SEEDS["verify"], T), dev)
+
+
+def test_route_prefill_zipf(dev):
+    lay = DeviceLayer(synth.REAL, synth.SEEDS["prefill"], bias="zipf")
+    x = synth.tokens(synth.REAL, synth.SEEDS["prefill"], 2048)
+    _route_check(lay, x, dev)
+
+
+# ------------------------------------------------------------------ grouping
+
+def _idx_case(T, K, E, kind, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "one":
+        return np.tile(np.arange(K, dtype=np.int32), (T, 1))
+    if kind == "zipf":
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p /= p.sum()
+        rows = [rng.choice(E, K, replace=False, p=p) for _ in range(T)]
+    else:
+        rows = [rng.choice(E, K, replace=False) for _ in range(T)]
+    idx = np.stack(rows).astype(np.int32)
+    if kind == "dup":
+        idx[T // 2:] = idx[:T - T // 2]
+    return idx
+
+
+@pytest.mark.parametrize("T,K,E,kind", [
+    (1, 8, 256, "rand"), (4, 2, 8, "rand"), (16, 8, 256, "dup"), (2048, 8, 256, "zipf"),
+    (100, 8, 256, "one"), (3, 4, 1024, "rand"), (777, 5, 300, "rand"), (1, 1, 2, "rand"),
+    (4096, 16, 64, "rand"),
+])
+def test_group_bit_exact(dev, T, K, E, kind):
+    idx = _idx_case(T, K, E, kind, T * 31 + K)
+    cfg = moe.Config(hidden=256, inter=128, n_experts=E, n_group=1, topk_group=1, top_k=K)
+    g = moe.group(cfg, to_d(idx, dev))
+    ref = oracle.group(idx, E)
+    for k in ("counts", "offsets", "active"):
+        assert np.array_equal(h(g[k]), ref[k]), k
+    assert np.array_equal(h(g["perm"])[:T * K], ref["perm"])
+    assert np.array_equal(h(g["inv"])[:T * K], ref["inv"])
+    assert int(h(g["n_active"])[0]) == ref["n_active"]
+
+
+# ------------------------------------------------------------------ expert FFN
+
+def _ffn_check(layer, x, dev, check_chain=True):
+    s = layer.shape
+    cfg = moe.Config.of(s)
+    H, I, K, wb = s.hidden, s.inter, s.top_k, s.wbits
+    T = x.shape[0]
+    idx, _, _ = oracle.route(x, layer.wr, layer.bias, s.n_group, s.topk_group, K,
+                             s.routed_scaling)
+    q, d = oracle.q8_0(x)
+    dbg = moe.debug_buffers(cfg, T, dev)
+    eo, so = moe.expert_ffn(cfg, to_d(q, dev), to_d(d, dev), to_d(idx, dev), layer.experts_d,
+                            layer.shared_d, debug=dbg)
+    eo, so = h(eo), h(so)
+    dbg = {k: h(v) for k, v in dbg.items()}
+    pairs = [(t * K + k, int(idx[t, k]), t) for t in range(T) for k in range(K)]
+    pairs += [(T * K + t, synth.SHARED_ID, t) for t in range(T)]
+    worst = 0.0
+    for p, e, t in pairs:
+        blob = layer.blob(e)
+        ref = oracle.gate_up(blob, H, I, wb, q[t], d[t], want_dots=True)
+        assert np.array_equal(dbg["gate_dots"][p], ref["gate_dots"]), (p, e)
+        assert np.array_equal(dbg["up_dots"][p], ref["up_dots"]), (p, e)
+        assert_close_rms(dbg["h"][p], ref["h"], 1e-5, f"h pair {p}")
+        qh, dh = oracle.q8_0(dbg["h"][p])
+        assert np.array_equal(dbg["q_h"][p], qh), p
+        assert np.array_equal(dbg["d_h"][p], dh), p
+        y_ref, dd_ref = oracle.down(blob, H, I, wb, dbg["q_h"][p], dbg["d_h"][p], want_dots=True)
+        assert np.array_equal(dbg["down_dots"][p], dd_ref), p
+        y = eo[t, p % K] if p < T * K else so[t]
+        assert_close_rms(y, y_ref, 1e-5, f"y pair {p} (same q_h)")
+        if check_chain:
+            chain = oracle.expert(blob, H, I, wb, q[t], d[t])["y"]
+            worst = max(worst, assert_close_rms(y, chain, 2e-3, f"y pair {p}"))
+    return worst
+
+
+def test_ffn_tiny(dev, tiny):
+    _ffn_check(tiny, synth.tokens(synth.TINY, synth.SEEDS["tiny"], 4), dev)
+
+
+def test_ffn_tiny_int2(dev):
+    lay = DeviceLayer(synth.TINY.with_bits(2), synth.SEEDS["tiny"])
+    _ffn_check(lay, synth.tokens(synth.TINY, synth.SEEDS["tiny"], 4), dev)
+
+
+def test_ffn_decode(dev, real):
+    _ffn_check(real, synth.tokens(synth.REAL, synth.SEEDS["decode"], 1, start=3), dev)
+
+
+def test_ffn_verify4(dev, real):
+    _ffn_check(real, synth.tokens_perturbed(synth.REAL, synth.SEEDS["verify"], 4), dev,
+               check_chain=False)
+
+
+# ------------------------------------------------------------------ combine
+
+@pytest.mark.parametrize("T,K,H,res,norm", [(1, 8, 6144, False, False), (4, 2, 256, True, True),
+                                            (16, 8, 6144, True, False), (5, 1, 64, False, True)])
+def test_combine(dev, T, K, H, res, norm):
+    rng = np.random.default_rng(T + K + H)
+    eo = rng.standard_normal((T, K, H)).astype(np.float32)
+    w = rng.uniform(0, 1, (T, K)).astype(np.float32)
+    sh = rng.standard_normal((T, H)).astype(np.float32)
+    r = rng.standard_normal((T, H)).astype(np.float32) if res else None
+    out = moe.combine(to_d(eo, dev), to_d(w, dev), to_d(sh, dev),
+                      to_d(r, dev) if res else None, want_norm=norm)
+    ref = oracle.combine(eo, w, sh, r, want_norm=norm)
+    if norm:
+        assert_close_rms(h(out[0]), ref[0], 1e-5, "y")
+        assert_close_rms(h(out[1]), ref[1], 1e-5, "y_norm")
+    else:
+        assert_close_rms(h(out), ref, 1e-5, "y")
+
+
+def test_rmsnorm(dev):
+    x = synth.tokens(synth.REAL, 3, 5)
+    assert_close_rms(h(moe.rmsnorm(to_d(x, dev))), oracle.rmsnorm(x), 1e-5)
+
+
+# ------------------------------------------------------------------ whole layer
+
+def _layer_check(layer, x, dev, residual=None, want_norm=False):
+    s = layer.shape
+    cfg = moe.Config.of(s)
+    T = x.shape[0]
+    idx_d = torch.empty((T, s.top_k), dtype=torch.int32, device=dev)
+    w_d = torch.empty((T, s.top_k), dtype=torch.float32, device=dev)
+    out = moe.layer(cfg, to_d(x, dev), layer.wr_d, layer.bias_d, layer.experts_d, layer.shared_d,
+                    residual=None if residual is None else to_d(residual, dev),
+                    want_norm=want_norm, idx_out=idx_d, w_out=w_d)
+    ref = layer.oracle_layer(x, residual, want_norm)
+    assert np.array_equal(h(idx_d), ref["idx"])
+    assert np.array_equal(h(w_d), ref["w"])
+    if want_norm:
+        assert_close_rms(h(out[0]), ref["y"], 2e-3, "y")
+        assert_close_rms(h(out[1]), ref["y_norm"], 2e-3, "y_norm")
+        return h(out[0])
+    assert_close_rms(h(out), ref["y"], 2e-3, "y")
+    return h(out)
+
+
+def test_layer_tiny(dev, tiny):
+    _layer_check(tiny, synth.tokens(synth.TINY, synth.SEEDS["tiny"], 4), dev)
+
+
+def test_layer_tiny_ragged_batches(dev, tiny):
+    for T in (1, 3, 5, 9, 33):
+        _layer_check(tiny, synth.tokens(synth.TINY, 77, T), dev)
+
+
+@pytest.mark.parametrize("start", [0, 1, 2])
+def test_layer_decode(dev, real, start):
+    _layer_check(real, synth.tokens(synth.REAL, synth.SEEDS["decode"], 1, start=start), dev)
+
+
+@pytest.mark.parametrize("T", [4, 16])
+def test_layer_verify(dev, real, T):
+    _layer_check(real, synth.tokens_perturbed(synth.REAL, synth.SEEDS["verify"], T), dev)
+
+
+def test_layer_residual_norm(dev, real):
+    x = synth.tokens(synth.REAL, 9, 2)
+    res = synth.tokens(synth.REAL, 10, 2)
+    _layer_check(real, x, dev, residual=res, want_norm=True)
+
+
+def test_layer_int2_decode(dev):
+    lay = DeviceLayer(synth.REAL.with_bits(2), synth.SEEDS["stack"])
+    _layer_check(lay, synth.tokens(synth.REAL, synth.SEEDS["stack"], 1), dev)
+
+
+def test_layer_deterministic(dev, real):
+    x = to_d(synth.tokens_perturbed(synth.REAL, 5, 16), dev)
+    cfg = moe.Config.of(synth.REAL)
+    a = h(moe.layer(cfg, x, real.wr_d, real.bias_d, real.experts_d, real.shared_d))
+    b = h(moe.layer(cfg, x, real.wr_d, real.bias_d, real.experts_d, real.shared_d))
+    assert np.array_equal(a, b)
+
+
+def test_zero_tokens_is_noop(dev, tiny):
+    cfg = moe.Config.of(synth.TINY)
+    x = torch.empty((0, 256), dtype=torch.float32, device=dev)
+    y = moe.layer(cfg, x, tiny.wr_d, tiny.bias_d, tiny.experts_d, tiny.shared_d)
+    assert y.shape == (0, 256)
