@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Throughput of the routed-MoE layer step on one MI355X.
+
+A step is one full pass of the layer (router scores and group-limited top-k,
+Q8_0 of the hidden state, batch-union grouping, expert gate/up + SwiGLU,
+Q8_0 of h, down projection, weighted combine with the shared expert) over one
+batch of synthetic tokens, through ``moe_layer`` in libmoe.
+
+Default workload ("decode"): one token per step through one layer at the real
+shape (hidden 6144, expert intermediate 2048, 256 routed experts in 8 groups,
+top-4 groups, top-8 experts, 1 shared expert, int4 experts with fp32 row
+scales, Q8_0 activations).  Every step takes a fresh token, and consecutive
+steps cycle over a ring of independently seeded layer instances resident in
+HBM, so a step's ~177 MB of weights are not still in the 256 MB last-level
+cache from the previous step.
+
+Timing: W untimed warm-up steps, then exactly K steps between two device
+synchronisations.  With --graph (default) the K steps are replayed from HIP
+graphs captured over blocks of consecutive steps (launch-bound at ~30 us per
+step otherwise).  A second, eager pass over the same steps launches every
+kernel with HIP events stamped from its own dispatch (hipExtLaunchKernelGGL)
+to give per-kernel durations; the dominant kernel's duration gives the
+roofline figure.  The CPU baseline is the oracle (plain C, OpenMP) timed on a
+bounded sample of the same workload on this host.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / int8 MFMA % (prefill)"
+HBM_PEAK_GBPS = 8000.0
+
+WORKLOADS = {
+    "decode": dict(T=1, tokens="normal", bias="uniform", seed="decode", ring=8),
+    "verify4": dict(T=4, tokens="perturbed", bias="uniform", seed="verify", ring=8),
+    "verify16": dict(T=16, tokens="perturbed", bias="uniform", seed="verify", ring=4),
+    "prefill": dict(T=2048, tokens="normal", bias="zipf", seed="prefill", ring=2),
+}
+
+
+def describe(name, shape, T, ring):
+    return (f"{name}: {T} token(s) per step through one routed-MoE layer (hidden {shape.hidden}, "
+            f"expert intermediate {shape.inter}, {shape.n_experts} experts in {shape.n_group} "
+            f"groups, top-{shape.topk_group} groups, top-{shape.top_k}, {shape.n_shared} shared "
+            f"expert, int{shape.wbits} experts + fp32 row scales, Q8_0 activations); weights "
+            f"cycled over {ring} seeded layer instances in HBM")
+
+
+class Hip:
+    """The HIP runtime already loaded by PyTorch (event timing only)."""
+
+    def __init__(self):
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        L = ctypes.CDLL(path)
+        L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.L = L
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.L.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.L.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.L.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def layer_bytes(shape, T, U, bb):
+    """Algorithmic HBM bytes of one step: router matrix and bias, the records of
+    the U distinct routed experts and the shared expert, x in, y out."""
+    E, H = shape.n_experts, shape.hidden
+    return E * H * 4 + E * 4 + (U + shape.n_shared) * bb + 2 * T * H * 4
+
+
+def gate_up_bytes(shape, T, U):
+    """Algorithmic bytes of one gate/up launch: gate and up codes and row scales
+    of U + shared experts, Q8_0 activations in, fp32 h out."""
+    H, I, K = shape.hidden, shape.inter, shape.top_k
+    per_expert = 2 * I * H * shape.wbits // 8 + 2 * I * 4
+    pairs = T * K + T * shape.n_shared
+    return (U + shape.n_shared) * per_expert + T * H + T * (H // 32) * 4 + pairs * I * 4
+
+
+def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s):
+    """Oracle (plain C + OpenMP) on the first steps of the same workload."""
+    import oracle
+    import synth
+    cache = {}
+
+    def blob_of(e):
+        if e not in cache:
+            cache[e] = synth.expert_blob(shape, seed, 0, e)
+        return cache[e]
+
+    shared = synth.expert_blob(shape, seed, 0, synth.SHARED_ID)
+    kw = dict(H=shape.hidden, I=shape.inter, n_experts=shape.n_experts, n_group=shape.n_group,
+              topk_group=shape.topk_group, top_k=shape.top_k, scale=shape.routed_scaling,
+              wbits=shape.wbits)
+    done_tok, spent, steps = 0, 0.0, 0
+    while spent < budget_s and steps < 64:
+        x = tokens_fn(steps)
+        idx, _, _ = oracle.route(x, wr, bias, shape.n_group, shape.topk_group, shape.top_k,
+                                 shape.routed_scaling)
+        for e in np.unique(idx):
+            blob_of(int(e))  # drawn outside the timed region
+        t0 = time.perf_counter()
+        oracle.layer(x, wr, bias, blob_of, shared, **kw)
+        spent += time.perf_counter() - t0
+        done_tok += x.shape[0]
+        steps += 1
+    return dict(value=done_tok / spent, unit="tokens/s", cores=oracle.threads(), kind="oracle",
+                sample=f"first {steps} step(s) ({done_tok} tokens) of the same workload on layer "
+                       f"instance 0, {spent:.1f} s of oracle time (plain C, OpenMP over output "
+                       f"rows; expert records drawn outside the timed region)")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--wbits", type=int, default=4, choices=(4, 2))
+    ap.add_argument("--ring", type=int, default=0, help="layer instances to cycle (0 = default)")
+    ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly")
+    ap.add_argument("--graph-block", type=int, default=64, help="steps per captured graph")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the multi-GPU sharding is a design, see DESIGN.md)"}))
+        sys.exit(2)
+
+    import torch
+
+    import int4_routed_expert_moe_amd as moe
+    import synth
+
+    wl = WORKLOADS[args.workload]
+    shape = synth.REAL.with_bits(args.wbits)
+    T = wl["T"]
+    R = args.ring or wl["ring"]
+    seed = synth.SEEDS[wl["seed"]]
+    K, W = args.steps, args.warmup
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.lib()
+    hip = Hip()
+    cfg = moe.Config.of(shape)
+    bb = moe.blob_bytes(cfg)
+    stream = torch.cuda.Stream(device=dev)  # default priority; graphs cannot capture stream 0
+    torch.cuda.set_stream(stream)
+
+    # --- resident inputs: R layer instances, tokens for every step ----------
+    ring = []
+    for l in range(R):
+        wr = synth.router_weights(shape, seed, l)
+        bias = (synth.router_bias_zipf(shape, seed, l) if wl["bias"] == "zipf"
+                else synth.router_bias_uniform(shape, seed, l))
+        ex = torch.empty(shape.n_experts * bb, dtype=torch.uint8, device=dev)
+        sh = torch.empty(bb, dtype=torch.uint8, device=dev)
+        synth.expert_blobs_gpu(shape, seed, l, list(range(shape.n_experts)), ex.data_ptr(), bb,
+                               stream.cuda_stream)
+        synth.expert_blobs_gpu(shape, seed, l, [synth.SHARED_ID], sh.data_ptr(), bb,
+                               stream.cuda_stream)
+        ring.append(dict(wr=torch.from_numpy(wr).to(dev), bias=torch.from_numpy(bias).to(dev),
+                         wr_h=wr, bias_h=bias, ex=ex, sh=sh))
+
+    def tokens_for(step):
+        if wl["tokens"] == "perturbed":
+            return synth.tokens_perturbed(shape, seed, T, start=step * (T // 2))
+        return synth.tokens(shape, seed, T, start=step * T)
+
+    n_tok_steps = W + K
+    if wl["tokens"] == "perturbed":
+        xs = np.stack([tokens_for(i) for i in range(n_tok_steps)])
+    else:
+        xs = synth.tokens(shape, seed, n_tok_steps * T).reshape(n_tok_steps, T, shape.hidden)
+    x_all = torch.from_numpy(xs).to(dev)
+    idx_all = torch.zeros((n_tok_steps, T, shape.top_k), dtype=torch.int32, device=dev)
+    y = torch.empty((T, shape.hidden), dtype=torch.float32, device=dev)
+    ws = torch.empty(moe.layer_workspace(cfg, T), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    L = moe.lib()
+    c_cfg = moe.Config.c(cfg)
+
+    def step_args(i, events=None):
+        r = ring[i % R]
+        return (ctypes.byref(c_cfg), T, x_all[i].data_ptr(), r["wr"].data_ptr(),
+                r["bias"].data_ptr(), r["ex"].data_ptr(), r["sh"].data_ptr(), None,
+                y.data_ptr(), None, 1e-5, idx_all[i].data_ptr(), None, ws.data_ptr(),
+                ws.numel(), events, stream.cuda_stream)
+
+    def run_step(i, events=None):
+        rc = L.moe_layer(*step_args(i, events))
+        if rc != 0:
+            raise RuntimeError(f"moe_layer failed: {L.moe_last_error().decode()}")
+
+    # --- warm-up ------------------------------------------------------------
+    for i in range(W):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    # --- timed region ---------------------------------------------------------
+    use_graph = not args.no_graph
+    graphs = []
+    if use_graph:
+        B = max(1, min(args.graph_block, K))
+        for b0 in range(W, W + K, B):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(b0, min(b0 + B, W + K)):
+                    run_step(i)
+            graphs.append(g)
+        for g in graphs:  # one untimed replay of every graph
+            g.replay()
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if use_graph:
+        for g in graphs:
+            g.replay()
+    else:
+        for i in range(W, W + K):
+            run_step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec = t1 - t0
+
+    # --- per-kernel durations (eager pass, events stamped by the dispatch) ----
+    n_ev = min(K, 256)
+    stage_names = list(moe.STAGES)
+    evs = []
+    for i in range(n_ev):
+        me = moe.MoeEvents()
+        for s in range(len(stage_names)):
+            me.start[s] = hip.event()
+            me.stop[s] = hip.event()
+        evs.append(me)
+    torch.cuda.synchronize()
+    for j in range(n_ev):
+        run_step(W + j, ctypes.byref(evs[j]))
+    torch.cuda.synchronize()
+    stage_ms = {}
+    for s, name in enumerate(stage_names):
+        v = [hip.elapsed_ms(evs[j].start[s], evs[j].stop[s]) for j in range(n_ev)]
+        stage_ms[name] = float(np.mean(v))
+    for me in evs:
+        for s in range(len(stage_names)):
+            hip.destroy(me.start[s])
+            hip.destroy(me.stop[s])
+
+    # --- work accounting ------------------------------------------------------
+    idx_h = idx_all.cpu().numpy()
+    U = float(np.mean([np.unique(idx_h[i]).size for i in range(W, W + K)]))
+    step_bytes = layer_bytes(shape, T, U, bb)
+    gu_bytes = gate_up_bytes(shape, T, U)
+    gu_sec = stage_ms["gate_up"] * 1e-3
+    achieved = gu_bytes / gu_sec / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": K * T / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": sec / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"i{shape.wbits}xi8->i32",
+        "data": "synthetic",
+        "config": {"workload": describe(args.workload, shape, T, R), "tokens_per_step": T,
+                   "layer_instances": R, "hip_graph": use_graph,
+                   "distinct_routed_experts_per_step": U},
+        "hbm_gbps": step_bytes / (sec / K) / 1e9,
+        "hbm_frac": step_bytes / (sec / K) / 1e9 / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": step_bytes,
+        "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "roofline": {"bound": "hbm", "kernel": "gate_up (expert gate/up + SwiGLU)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": gu_bytes},
+    }
+    if not args.no_cpu:
+        r0 = ring[0]
+        out["cpu_baseline"] = cpu_baseline(shape, seed, r0["wr_h"], r0["bias_h"], tokens_for, T,
+                                           args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

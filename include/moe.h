@@ -199,19 +199,42 @@ int moe_combine(int32_t T, int32_t H, int32_t K, const float *expert_out, const 
 /* Unit-gain RMSNorm of T rows of H floats: y = x / sqrt(mean(x^2) + eps). */
 int moe_rmsnorm(int32_t T, int32_t H, const float *x, float *y, float eps, void *stream);
 
+/* Optional kernel timestamps for moe_layer (pass NULL in production).  For
+ * each stage whose start/stop are not NULL (hipEvent_t created by the
+ * caller on the device of `stream`), the stage's kernel is launched with
+ * hipExtLaunchKernelGGL so that the two events carry the kernel's own
+ * dispatch start and completion times; hipEventElapsedTime(start, stop)
+ * is then that kernel's duration.  No extra work is enqueued. */
+enum {
+  MOE_STAGE_ROUTER_SCORES = 0,
+  MOE_STAGE_ROUTER_SELECT = 1,
+  MOE_STAGE_QUANT = 2,
+  MOE_STAGE_GROUP = 3,
+  MOE_STAGE_GATE_UP = 4,
+  MOE_STAGE_DOWN = 5,
+  MOE_STAGE_COMBINE = 6,
+  MOE_N_STAGES = 8
+};
+typedef struct moe_events {
+  void *start[MOE_N_STAGES];
+  void *stop[MOE_N_STAGES];
+} moe_events;
+
 /* ---------------------------------------------------------------------------
  * moe_layer — the whole step: moe_route, moe_quant_act, moe_expert_ffn and
  * moe_combine on one stream, with all intermediates in the workspace.
  * x [T][H] is the (already normalised) layer input; y [T][H] the output
  * (plus residual when given); y_norm optional as in moe_combine.  idx_out and
- * w_out ([T][K], nullable) receive the routing decision.
+ * w_out ([T][K], nullable) receive the routing decision.  ev: optional
+ * kernel timestamps (see moe_events), NULL in production.
  * Errors: as the calls it makes.
  * ------------------------------------------------------------------------- */
 size_t moe_layer_workspace(const moe_cfg *cfg, int32_t T);
 int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
               const float *bias, const void *experts, const void *shared,
               const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
-              float *w_out, void *workspace, size_t ws_bytes, void *stream);
+              float *w_out, void *workspace, size_t ws_bytes, const moe_events *ev,
+              void *stream);
 
 /* Name of a return code, and the calling thread's last detailed message. */
 const char *moe_strerror(int code);

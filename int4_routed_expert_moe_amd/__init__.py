@@ -41,6 +41,14 @@ class MoeCfg(ctypes.Structure):
                 ("routed_scaling", ctypes.c_float)]
 
 
+MOE_N_STAGES = 8
+STAGES = dict(router_scores=0, router_select=1, quant=2, group=3, gate_up=4, down=5, combine=6)
+
+
+class MoeEvents(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_void_p * MOE_N_STAGES), ("stop", ctypes.c_void_p * MOE_N_STAGES)]
+
+
 class MoeFfnDebug(ctypes.Structure):
     _fields_ = [("gate_dots", ctypes.c_void_p), ("up_dots", ctypes.c_void_p),
                 ("h", ctypes.c_void_p), ("q_h", ctypes.c_void_p), ("d_h", ctypes.c_void_p),
@@ -58,6 +66,10 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
                            "(there is no fallback implementation)")
+    try:  # load PyTorch's HIP runtime first so that libmoe binds to the same one
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     v, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     pc = ctypes.POINTER(MoeCfg)
@@ -82,7 +94,8 @@ def lib():
     L.moe_rmsnorm.restype = ctypes.c_int
     L.moe_layer_workspace.argtypes = [pc, i32]
     L.moe_layer_workspace.restype = sz
-    L.moe_layer.argtypes = [pc, i32, v, v, v, v, v, v, v, v, f32, v, v, v, sz, v]
+    L.moe_layer.argtypes = [pc, i32, v, v, v, v, v, v, v, v, f32, v, v, v, sz,
+                            ctypes.POINTER(MoeEvents), v]
     L.moe_layer.restype = ctypes.c_int
     L.moe_strerror.argtypes = [ctypes.c_int]
     L.moe_strerror.restype = ctypes.c_char_p
@@ -263,8 +276,12 @@ def rmsnorm(x, y=None, eps=1e-5):
 
 
 def layer(cfg: Config, x, w_router, bias, experts, shared=None, residual=None, y=None,
-          y_norm=None, eps=1e-5, want_norm=False, idx_out=None, w_out=None, workspace=None):
-    """moe_layer (whole step): returns y (and y_norm when want_norm)."""
+          y_norm=None, eps=1e-5, want_norm=False, idx_out=None, w_out=None, workspace=None,
+          events=None):
+    """moe_layer (whole step): returns y (and y_norm when want_norm).
+
+    events: optional MoeEvents (hipEvent_t handles per stage) to receive the
+    kernels' own start/stop timestamps."""
     torch = _torch()
     T, H = x.shape
     y = y if y is not None else torch.empty((T, H), dtype=torch.float32, device=x.device)
@@ -273,5 +290,6 @@ def layer(cfg: Config, x, w_router, bias, experts, shared=None, residual=None, y
     ws = _workspace(layer_workspace(cfg, T), x.device, workspace)
     _check(lib().moe_layer(ctypes.byref(cfg.c()), T, _ptr(x), _ptr(w_router), _ptr(bias),
                            _ptr(experts), _ptr(shared), _ptr(residual), _ptr(y), _ptr(y_norm),
-                           eps, _ptr(idx_out), _ptr(w_out), _ptr(ws), ws.numel(), _stream()))
+                           eps, _ptr(idx_out), _ptr(w_out), _ptr(ws), ws.numel(),
+                           ctypes.byref(events) if events is not None else None, _stream()))
     return (y, y_norm) if want_norm else y

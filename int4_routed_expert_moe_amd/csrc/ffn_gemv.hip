@@ -548,47 +548,48 @@ __global__ void __launch_bounds__(256) k_down_i2(FfnArgs a) {
 // ------------------------------------------------------------------ launch
 
 template <int TT, int NG, int ND, bool DBG>
-static void launch_tt(const FfnArgs &a, int n_slots, hipStream_t st) {
+static void launch_tt(const FfnArgs &a, int n_slots, hipStream_t st, const moe_events *ev) {
+  const Ev eg = stage_ev(ev, MOE_STAGE_GATE_UP), ed = stage_ev(ev, MOE_STAGE_DOWN);
   const dim3 g_gu(a.I / (4 * GU_RPW), n_slots);
   const dim3 g_dn(a.H / (4 * DN_RPW), n_slots);
   const size_t lds = (size_t)TT * a.I + sizeof(float) * (size_t)TT * (a.I / 32);
   if (a.wbits == 4) {
-    hipLaunchKernelGGL((k_gate_up_i4<TT, NG, DBG>), g_gu, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((k_down_i4<TT, ND, DBG>), g_dn, dim3(256), lds, st, a);
+    launch_k(k_gate_up_i4<TT, NG, DBG>, g_gu, dim3(256), 0, st, eg, a);
+    launch_k(k_down_i4<TT, ND, DBG>, g_dn, dim3(256), (uint32_t)lds, st, ed, a);
   } else {
-    hipLaunchKernelGGL((k_gate_up_i2<TT, NG, DBG>), g_gu, dim3(256), 0, st, a);
-    hipLaunchKernelGGL((k_down_i2<TT, ND, DBG>), g_dn, dim3(256), lds, st, a);
+    launch_k(k_gate_up_i2<TT, NG, DBG>, g_gu, dim3(256), 0, st, eg, a);
+    launch_k(k_down_i2<TT, ND, DBG>, g_dn, dim3(256), (uint32_t)lds, st, ed, a);
   }
 }
 
 // pieces per lane: gate/up rows have H/32 (int4) or H/64 (int2) 16-byte
 // pieces, down rows I/32 or I/64; template instances cover up to 4 and 2.
 template <int TT, bool DBG>
-static void launch_shape(const FfnArgs &a, int n_slots, hipStream_t st) {
+static void launch_shape(const FfnArgs &a, int n_slots, hipStream_t st, const moe_events *ev) {
   const int per = a.wbits == 4 ? 32 : 64;
   const int ng = (a.H / per + 63) / 64, nd = (a.I / per + 63) / 64;
-  if (ng <= 1 && nd <= 1) launch_tt<TT, 1, 1, DBG>(a, n_slots, st);
-  else if (ng <= 2 && nd <= 1) launch_tt<TT, 2, 1, DBG>(a, n_slots, st);
-  else if (ng <= 3 && nd <= 1) launch_tt<TT, 3, 1, DBG>(a, n_slots, st);
-  else if (ng <= 4 && nd <= 1) launch_tt<TT, 4, 1, DBG>(a, n_slots, st);
-  else launch_tt<TT, 4, 2, DBG>(a, n_slots, st);
+  if (ng <= 1 && nd <= 1) launch_tt<TT, 1, 1, DBG>(a, n_slots, st, ev);
+  else if (ng <= 2 && nd <= 1) launch_tt<TT, 2, 1, DBG>(a, n_slots, st, ev);
+  else if (ng <= 3 && nd <= 1) launch_tt<TT, 3, 1, DBG>(a, n_slots, st, ev);
+  else if (ng <= 4 && nd <= 1) launch_tt<TT, 4, 1, DBG>(a, n_slots, st, ev);
+  else launch_tt<TT, 4, 2, DBG>(a, n_slots, st, ev);
 }
 
-void launch_ffn_gemv(const FfnArgs &a, hipStream_t st) {
+void launch_ffn_gemv(const FfnArgs &a, hipStream_t st, const moe_events *ev) {
   const int n_slots = a.n_shared + (a.T * a.K < a.E ? a.T * a.K : a.E);
   const bool dbg = a.dbg.gate_dots || a.dbg.up_dots || a.dbg.h || a.dbg.q_h || a.dbg.d_h ||
                    a.dbg.down_dots;
   const int tt = a.T <= 1 ? 1 : (a.T <= 2 ? 2 : (a.T <= 4 ? 4 : 8));
   if (dbg) {
-    if (tt == 1) launch_shape<1, true>(a, n_slots, st);
-    else if (tt == 2) launch_shape<2, true>(a, n_slots, st);
-    else if (tt == 4) launch_shape<4, true>(a, n_slots, st);
-    else launch_shape<8, true>(a, n_slots, st);
+    if (tt == 1) launch_shape<1, true>(a, n_slots, st, ev);
+    else if (tt == 2) launch_shape<2, true>(a, n_slots, st, ev);
+    else if (tt == 4) launch_shape<4, true>(a, n_slots, st, ev);
+    else launch_shape<8, true>(a, n_slots, st, ev);
   } else {
-    if (tt == 1) launch_shape<1, false>(a, n_slots, st);
-    else if (tt == 2) launch_shape<2, false>(a, n_slots, st);
-    else if (tt == 4) launch_shape<4, false>(a, n_slots, st);
-    else launch_shape<8, false>(a, n_slots, st);
+    if (tt == 1) launch_shape<1, false>(a, n_slots, st, ev);
+    else if (tt == 2) launch_shape<2, false>(a, n_slots, st, ev);
+    else if (tt == 4) launch_shape<4, false>(a, n_slots, st, ev);
+    else launch_shape<8, false>(a, n_slots, st, ev);
   }
 }
 

@@ -119,10 +119,10 @@ __global__ void __launch_bounds__(GW * 64) k_group(int n_slots, int E,
 
 void launch_group(int n_slots, int E, const int32_t *idx, int32_t *counts, int32_t *offsets,
                   int32_t *perm, int32_t *inv, int32_t *active, int32_t *n_active,
-                  hipStream_t st) {
+                  hipStream_t st, const moe_events *ev) {
   const size_t lds = sizeof(int32_t) * ((size_t)GW * E + E);
-  hipLaunchKernelGGL(k_group, dim3(1), dim3(GW * 64), lds, st, n_slots, E, idx, counts, offsets,
-                     perm, inv, active, n_active);
+  launch_k(k_group, dim3(1), dim3(GW * 64), (uint32_t)lds, st, stage_ev(ev, MOE_STAGE_GROUP),
+           n_slots, E, idx, counts, offsets, perm, inv, active, n_active);
 }
 
 }  // namespace moe

@@ -1,5 +1,6 @@
 // Internal launch entry points of the libmoe kernels (host side).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -7,20 +8,45 @@
 
 namespace moe {
 
-void launch_quant_act(const float *x, int8_t *q, float *d, int64_t n_elems, hipStream_t st);
+// Kernel timestamps: a stage launched with a non-null event pair goes through
+// hipExtLaunchKernelGGL, which stamps the events from the kernel's own
+// dispatch (no extra queue packets).
+struct Ev {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+inline Ev stage_ev(const moe_events *e, int stage) {
+  Ev r;
+  if (e) {
+    r.start = (hipEvent_t)e->start[stage];
+    r.stop = (hipEvent_t)e->stop[stage];
+  }
+  return r;
+}
+template <typename F, typename... Args>
+inline void launch_k(F kernel, dim3 g, dim3 b, uint32_t lds, hipStream_t st, Ev ev, Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, g, b, lds, st, ev.start, ev.stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, g, b, lds, st, args...);
+}
+
+void launch_quant_act(const float *x, int8_t *q, float *d, int64_t n_elems, hipStream_t st,
+                      const moe_events *ev = nullptr);
 void launch_combine(int T, int H, int K, const float *eo, const float *w, const float *shared,
-                    const float *residual, float *y, float *yn, float eps, hipStream_t st);
+                    const float *residual, float *y, float *yn, float eps, hipStream_t st,
+                    const moe_events *ev = nullptr);
 void launch_rmsnorm(int T, int H, const float *x, float *y, float eps, hipStream_t st);
 
 // Router: scores into s/sb [T][E] (workspace), then selection into idx/w.
 void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *wr,
-                          const float *bias, float *s, float *sb, hipStream_t st);
+                          const float *bias, float *s, float *sb, hipStream_t st,
+                          const moe_events *ev = nullptr);
 void launch_router_select(const moe_cfg &c, int T, const float *s, const float *sb,
-                          int32_t *idx, float *w, hipStream_t st);
+                          int32_t *idx, float *w, hipStream_t st, const moe_events *ev = nullptr);
 
 void launch_group(int n_slots, int E, const int32_t *idx, int32_t *counts, int32_t *offsets,
                   int32_t *perm, int32_t *inv, int32_t *active, int32_t *n_active,
-                  hipStream_t st);
+                  hipStream_t st, const moe_events *ev = nullptr);
 
 // Expert FFN over grouped tokens (dot-product GEMV path).
 struct FfnArgs {
@@ -36,6 +62,6 @@ struct FfnArgs {
   float *shared_out;
   moe_ffn_debug dbg;
 };
-void launch_ffn_gemv(const FfnArgs &a, hipStream_t st);
+void launch_ffn_gemv(const FfnArgs &a, hipStream_t st, const moe_events *ev = nullptr);
 
 }  // namespace moe

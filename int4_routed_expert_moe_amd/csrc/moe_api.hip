@@ -138,17 +138,19 @@ LayerWs carve_layer(Carve &cv, const moe_cfg &c, int T) {
 
 // unchecked enqueue helpers (arguments validated by the callers) ------------
 int do_route(const moe_cfg &c, int T, const float *x, const float *wr, const float *bias,
-             int32_t *idx, float *w, const RouteWs &ws, hipStream_t st) {
-  moe::launch_router_scores(c, T, x, wr, bias, ws.s, ws.sb, st);
-  moe::launch_router_select(c, T, ws.s, ws.sb, idx, w, st);
+             int32_t *idx, float *w, const RouteWs &ws, hipStream_t st,
+             const moe_events *ev = nullptr) {
+  moe::launch_router_scores(c, T, x, wr, bias, ws.s, ws.sb, st, ev);
+  moe::launch_router_select(c, T, ws.s, ws.sb, idx, w, st, ev);
   return launched("moe_route");
 }
 
 int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32_t *idx,
            const void *experts, const void *shared, float *expert_out, float *shared_out,
-           const FfnWs &ws, const moe_ffn_debug *dbg, hipStream_t st) {
+           const FfnWs &ws, const moe_ffn_debug *dbg, hipStream_t st,
+           const moe_events *ev = nullptr) {
   moe::launch_group(T * c.top_k, c.n_experts, idx, ws.counts, ws.offsets, ws.perm, ws.inv,
-                    ws.active, ws.n_active, st);
+                    ws.active, ws.n_active, st, ev);
   moe::FfnArgs a;
   a.H = c.hidden;
   a.I = c.inter;
@@ -171,7 +173,7 @@ int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32
   a.shared_out = shared_out;
   if (dbg) a.dbg = *dbg;
   else memset(&a.dbg, 0, sizeof(a.dbg));
-  moe::launch_ffn_gemv(a, st);
+  moe::launch_ffn_gemv(a, st, ev);
   return launched("moe_expert_ffn");
 }
 
@@ -328,7 +330,8 @@ size_t moe_layer_workspace(const moe_cfg *cfg, int32_t T) {
 int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
               const float *bias, const void *experts, const void *shared,
               const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
-              float *w_out, void *workspace, size_t ws_bytes, void *stream) {
+              float *w_out, void *workspace, size_t ws_bytes, const moe_events *ev,
+              void *stream) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
@@ -358,14 +361,14 @@ int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
   LayerWs ws = carve_layer(cv, c, T);
   int32_t *idx = idx_out ? idx_out : ws.idx;
   float *w = w_out ? w_out : ws.w;
-  if ((rc = do_route(c, T, x, w_router, bias, idx, w, ws.route, st))) return rc;
-  moe::launch_quant_act(x, ws.q, ws.d, (int64_t)T * c.hidden, st);
+  if ((rc = do_route(c, T, x, w_router, bias, idx, w, ws.route, st, ev))) return rc;
+  moe::launch_quant_act(x, ws.q, ws.d, (int64_t)T * c.hidden, st, ev);
   if ((rc = launched("moe_layer quant"))) return rc;
   if ((rc = do_ffn(c, T, ws.q, ws.d, idx, experts, c.n_shared ? shared : nullptr, ws.expert_out,
-                   c.n_shared ? ws.shared_out : nullptr, ws.ffn, nullptr, st)))
+                   c.n_shared ? ws.shared_out : nullptr, ws.ffn, nullptr, st, ev)))
     return rc;
   moe::launch_combine(T, c.hidden, c.top_k, ws.expert_out, w,
-                      c.n_shared ? ws.shared_out : nullptr, residual, y, y_norm, eps, st);
+                      c.n_shared ? ws.shared_out : nullptr, residual, y, y_norm, eps, st, ev);
   return launched("moe_layer combine");
 }
 

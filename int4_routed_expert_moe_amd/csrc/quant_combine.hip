@@ -35,10 +35,12 @@ __global__ void __launch_bounds__(256) k_quant_act(const float *__restrict__ x,
   if ((i & 7) == 0) d[i >> 3] = dd;
 }
 
-void launch_quant_act(const float *x, int8_t *q, float *d, int64_t n_elems, hipStream_t st) {
+void launch_quant_act(const float *x, int8_t *q, float *d, int64_t n_elems, hipStream_t st,
+                      const moe_events *ev) {
   const int64_t quads = n_elems / 4;
   const int64_t blocks = (quads + 255) / 256;
-  hipLaunchKernelGGL(k_quant_act, dim3((unsigned)blocks), dim3(256), 0, st, x, q, d, quads);
+  launch_k(k_quant_act, dim3((unsigned)blocks), dim3(256), 0, st, stage_ev(ev, MOE_STAGE_QUANT), x,
+           q, d, quads);
 }
 
 // One block per token row; 256 threads stride over H in float4.
@@ -90,9 +92,10 @@ __global__ void __launch_bounds__(256) k_combine(int H, int K, const float *__re
 }
 
 void launch_combine(int T, int H, int K, const float *eo, const float *w, const float *shared,
-                    const float *residual, float *y, float *yn, float eps, hipStream_t st) {
-  hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, st, H, K, eo, w, shared, residual, y, yn,
-                     eps);
+                    const float *residual, float *y, float *yn, float eps, hipStream_t st,
+                    const moe_events *ev) {
+  launch_k(k_combine, dim3(T), dim3(256), 0, st, stage_ev(ev, MOE_STAGE_COMBINE), H, K, eo, w,
+           shared, residual, y, yn, eps);
 }
 
 __global__ void __launch_bounds__(256) k_rmsnorm(int H, const float *__restrict__ x,

@@ -88,18 +88,19 @@ __global__ void __launch_bounds__(64) k_router_scores(int T, int H, int E,
 }
 
 void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *wr,
-                          const float *bias, float *s, float *sb, hipStream_t st) {
+                          const float *bias, float *s, float *sb, hipStream_t st,
+                          const moe_events *ev) {
   const int H = c.hidden, E = c.n_experts;
+  const Ev e0 = stage_ev(ev, MOE_STAGE_ROUTER_SCORES);
   const size_t lds = sizeof(float) * (size_t)(H / 64);
   if (T <= 1) {
-    hipLaunchKernelGGL(k_router_scores<1>, dim3(E, T), dim3(64), lds, st, T, H, E, x, wr, bias,
-                       s, sb);
+    launch_k(k_router_scores<1>, dim3(E, T), dim3(64), lds, st, e0, T, H, E, x, wr, bias, s, sb);
   } else if (T <= 4) {
-    hipLaunchKernelGGL(k_router_scores<4>, dim3(E, 1), dim3(64), 4 * lds, st, T, H, E, x, wr,
-                       bias, s, sb);
+    launch_k(k_router_scores<4>, dim3(E, 1), dim3(64), 4 * lds, st, e0, T, H, E, x, wr, bias, s,
+             sb);
   } else {
-    hipLaunchKernelGGL(k_router_scores<8>, dim3(E, (T + 7) / 8), dim3(64), 8 * lds, st, T, H, E,
-                       x, wr, bias, s, sb);
+    launch_k(k_router_scores<8>, dim3(E, (T + 7) / 8), dim3(64), 8 * lds, st, e0, T, H, E, x, wr,
+             bias, s, sb);
   }
 }
 
@@ -181,9 +182,9 @@ __global__ void __launch_bounds__(64) k_router_select(int E, int G, int TG, int 
 }
 
 void launch_router_select(const moe_cfg &c, int T, const float *s, const float *sb,
-                          int32_t *idx, float *w, hipStream_t st) {
-  hipLaunchKernelGGL(k_router_select, dim3(T), dim3(64), 0, st, c.n_experts, c.n_group,
-                     c.topk_group, c.top_k, c.routed_scaling, s, sb, idx, w);
+                          int32_t *idx, float *w, hipStream_t st, const moe_events *ev) {
+  launch_k(k_router_select, dim3(T), dim3(64), 0, st, stage_ev(ev, MOE_STAGE_ROUTER_SELECT),
+           c.n_experts, c.n_group, c.topk_group, c.top_k, c.routed_scaling, s, sb, idx, w);
 }
 
 }  // namespace moe

@@ -85,6 +85,8 @@ def lib():
     L.oracle_combine.restype = None
     L.oracle_rmsnorm.argtypes = [c_i, c_i, c_v, c_v, c_f]
     L.oracle_rmsnorm.restype = None
+    L.oracle_threads.argtypes = []
+    L.oracle_threads.restype = c_i
     _lib = L
     return L
 
@@ -100,6 +102,11 @@ def _c(a, dtype):
 def _check(rc, what):
     if rc != 0:
         raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def threads() -> int:
+    """OpenMP threads used by the oracle's parallel loops."""
+    return int(lib().oracle_threads())
 
 
 # ------------------------------------------------------------------ codes

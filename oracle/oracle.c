@@ -444,3 +444,11 @@ void oracle_rmsnorm(int T, int H, const float *x, float *y, float eps) {
     for (int j = 0; j < H; j++) y[(size_t)t * H + j] = (float)(x[(size_t)t * H + j] * inv);
   }
 }
+
+/* Number of OpenMP threads the oracle's parallel loops use (1 without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_threads(void) { return 1; }
+#endif

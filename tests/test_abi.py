@@ -143,11 +143,11 @@ def test_combine_and_layer_errors(L):
     ws = moe.layer_workspace(REAL, 1)
     lay = L.moe_layer
     assert lay(ctypes.byref(c), 1, A, A, A, A, A, None, A, None, 1e-5, None, None, A, ws - 1,
-               None) == moe.MOE_EWORKSPACE
+               None, None) == moe.MOE_EWORKSPACE
     assert lay(ctypes.byref(c), 1, A, A, A, A, None, None, A, None, 1e-5, None, None, A, ws,
-               None) == moe.MOE_EINVAL
+               None, None) == moe.MOE_EINVAL
     assert lay(ctypes.byref(c), 1, A, A, A, A + 64, A, None, A, None, 1e-5, None, None, A, ws,
-               None) == moe.MOE_EALIGN
+               None, None) == moe.MOE_EALIGN
 
 
 def test_strerror(L):

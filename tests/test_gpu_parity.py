@@ -312,3 +312,33 @@ def test_zero_tokens_is_noop(dev, tiny):
     x = torch.empty((0, 256), dtype=torch.float32, device=dev)
     y = moe.layer(cfg, x, tiny.wr_d, tiny.bias_d, tiny.experts_d, tiny.shared_d)
     assert y.shape == (0, 256)
+
+
+def test_layer_graph_replays_match_eager(dev, real):
+    """moe_layer captured in a HIP graph: every replay equals the eager result,
+    with unrelated eager work and synchronisations between replays."""
+    cfg = moe.Config.of(synth.REAL)
+    st = torch.cuda.Stream(device=dev)
+    xs = [to_d(synth.tokens_perturbed(synth.REAL, 21 + i, 4), dev) for i in range(3)]
+    ws = torch.empty(moe.layer_workspace(cfg, 4), dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(st):
+        eager = [h(moe.layer(cfg, x, real.wr_d, real.bias_d, real.experts_d, real.shared_d,
+                             workspace=ws)) for x in xs]
+        ys = [torch.empty((4, 6144), dtype=torch.float32, device=dev) for _ in xs]
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=st):
+            for x, y in zip(xs, ys):
+                moe.layer(cfg, x, real.wr_d, real.bias_d, real.experts_d, real.shared_d, y=y,
+                          workspace=ws)
+        for rep in range(4):
+            for y in ys:
+                y.fill_(float("nan"))
+            other = moe.layer(cfg, to_d(synth.tokens(synth.REAL, 99 + rep, 2), dev), real.wr_d,
+                              real.bias_d, real.experts_d, real.shared_d)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for y, e in zip(ys, eager):
+                assert np.array_equal(h(y), e), f"replay {rep}"
+            assert np.all(np.isfinite(h(other)))
