@@ -23,7 +23,8 @@ MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 EXPORTS = (
     "moe_expert_blob_bytes", "moe_route_workspace", "moe_route", "moe_quant_act", "moe_group",
     "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_combine", "moe_rmsnorm",
-    "moe_layer_workspace", "moe_layer", "moe_strerror", "moe_last_error",
+    "moe_layer_workspace", "moe_layer_sync_bytes", "moe_layer", "moe_strerror",
+    "moe_last_error",
 )
 
 
@@ -42,11 +43,13 @@ class MoeCfg(ctypes.Structure):
 
 
 MOE_N_STAGES = 8
-STAGES = dict(router_scores=0, router_select=1, quant=2, group=3, gate_up=4, down=5, combine=6)
+STAGES = dict(router_scores=0, router_select=1, quant=2, group=3, gate_up=4, down=5, combine=6,
+              fused=7)
 
 
 class MoeEvents(ctypes.Structure):
-    _fields_ = [("start", ctypes.c_void_p * MOE_N_STAGES), ("stop", ctypes.c_void_p * MOE_N_STAGES)]
+    _fields_ = [("start", ctypes.c_void_p * MOE_N_STAGES), ("stop", ctypes.c_void_p * MOE_N_STAGES),
+                ("wg_trace", ctypes.c_void_p), ("trace_words", ctypes.c_uint64)]
 
 
 class MoeFfnDebug(ctypes.Structure):
@@ -94,6 +97,8 @@ def lib():
     L.moe_rmsnorm.restype = ctypes.c_int
     L.moe_layer_workspace.argtypes = [pc, i32]
     L.moe_layer_workspace.restype = sz
+    L.moe_layer_sync_bytes.argtypes = []
+    L.moe_layer_sync_bytes.restype = sz
     L.moe_layer.argtypes = [pc, i32, v, v, v, v, v, v, v, v, f32, v, v, v, sz,
                             ctypes.POINTER(MoeEvents), v]
     L.moe_layer.restype = ctypes.c_int
@@ -168,11 +173,21 @@ def layer_workspace(cfg: Config, T: int) -> int:
     return int(lib().moe_layer_workspace(ctypes.byref(cfg.c()), T))
 
 
+def layer_sync_bytes() -> int:
+    """Leading bytes of a layer workspace holding its (zero-between-calls) counters."""
+    return int(lib().moe_layer_sync_bytes())
+
+
+# byte offset of the count of bounded waits that timed out (diagnostic)
+LAYER_ERR_OFFSET = 5 * 256
+
+
 def _workspace(nbytes, device, ws=None):
+    """Caller's workspace, or a new zero-filled one (moe_layer needs zeros)."""
     torch = _torch()
     if ws is not None:
         return ws
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def route(cfg: Config, x, w_router, bias, idx=None, w=None, workspace=None):

@@ -64,4 +64,32 @@ struct FfnArgs {
 };
 void launch_ffn_gemv(const FfnArgs &a, hipStream_t st, const moe_events *ev = nullptr);
 
+// Whole layer for 1..16 tokens in one launch (layer_fused.hip).
+struct LayerArgs {
+  int H, I, E, G, TG, K, T, n_shared, wbits;
+  float scale, eps;
+  size_t blob_bytes;
+  const float *x, *wr, *bias, *residual;
+  const uint8_t *experts, *shared;
+  float *y, *y_norm;
+  int32_t *idx;
+  float *w;
+  float *s, *sb;                 // [T][E] router scores
+  int8_t *q;                     // [T][H] Q8_0 of x
+  float *d;                      // [T][H/32]
+  int32_t *counts, *offsets, *perm, *active, *n_active;
+  int8_t *qh;                    // [P][I] Q8_0 of h
+  float *dh;                     // [P][I/32]
+  float *eo;                     // [T*K][H] routed expert outputs
+  float *so;                     // [T][H] shared expert output
+  float *ssq;                    // [T][H/32] partial sums of squares
+  uint32_t *sync;                // zero-initialised counters
+  uint64_t *trace;               // optional [blocks][4] wall-clock stamps
+  uint64_t trace_words;
+  int n_router, nw_gu, nw_dn, n_slots_ub, xq_rows;
+};
+size_t layer_fused_sync_bytes();
+bool layer_fused_supported(const moe_cfg &c, int T);
+void launch_layer_fused(LayerArgs a, hipStream_t st, const moe_events *ev);
+
 }  // namespace moe

@@ -115,16 +115,22 @@ FfnWs carve_ffn(Carve &cv, const moe_cfg &c, int T) {
 }
 
 struct LayerWs {
+  uint32_t *sync;  // first in the workspace: counters of the fused kernel
+  float *ssq;
   RouteWs route;
   int32_t *idx;
   float *w;
   int8_t *q;
   float *d;
   float *expert_out, *shared_out;
+  int8_t *qh;
+  float *dh;
   FfnWs ffn;
 };
 LayerWs carve_layer(Carve &cv, const moe_cfg &c, int T) {
   LayerWs l;
+  l.sync = cv.take<uint32_t>(moe::layer_fused_sync_bytes() / sizeof(uint32_t));
+  l.ssq = cv.take<float>((size_t)T * (c.hidden / 32));
   l.route = carve_route(cv, c, T);
   l.idx = cv.take<int32_t>((size_t)T * c.top_k);
   l.w = cv.take<float>((size_t)T * c.top_k);
@@ -132,6 +138,9 @@ LayerWs carve_layer(Carve &cv, const moe_cfg &c, int T) {
   l.d = cv.take<float>((size_t)T * c.hidden / 32);
   l.expert_out = cv.take<float>((size_t)T * c.top_k * c.hidden);
   l.shared_out = cv.take<float>((size_t)T * c.hidden * c.n_shared);
+  const size_t pairs = (size_t)T * c.top_k + (size_t)T * c.n_shared;
+  l.qh = cv.take<int8_t>(pairs * c.inter);
+  l.dh = cv.take<float>(pairs * (c.inter / 32));
   l.ffn = carve_ffn(cv, c, T);
   return l;
 }
@@ -327,6 +336,8 @@ size_t moe_layer_workspace(const moe_cfg *cfg, int32_t T) {
   return cv.off;
 }
 
+size_t moe_layer_sync_bytes(void) { return moe::layer_fused_sync_bytes(); }
+
 int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
               const float *bias, const void *experts, const void *shared,
               const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
@@ -361,6 +372,50 @@ int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
   LayerWs ws = carve_layer(cv, c, T);
   int32_t *idx = idx_out ? idx_out : ws.idx;
   float *w = w_out ? w_out : ws.w;
+  if (moe::layer_fused_supported(c, T)) {
+    moe::LayerArgs a;
+    a.H = c.hidden;
+    a.I = c.inter;
+    a.E = c.n_experts;
+    a.G = c.n_group;
+    a.TG = c.topk_group;
+    a.K = c.top_k;
+    a.T = T;
+    a.n_shared = c.n_shared;
+    a.wbits = c.wbits;
+    a.scale = c.routed_scaling;
+    a.eps = eps;
+    a.blob_bytes = blob_bytes(c);
+    a.x = x;
+    a.wr = w_router;
+    a.bias = bias;
+    a.residual = residual;
+    a.experts = static_cast<const uint8_t *>(experts);
+    a.shared = c.n_shared ? static_cast<const uint8_t *>(shared) : nullptr;
+    a.y = y;
+    a.y_norm = y_norm;
+    a.idx = idx;
+    a.w = w;
+    a.s = ws.route.s;
+    a.sb = ws.route.sb;
+    a.q = ws.q;
+    a.d = ws.d;
+    a.counts = ws.ffn.counts;
+    a.offsets = ws.ffn.offsets;
+    a.perm = ws.ffn.perm;
+    a.active = ws.ffn.active;
+    a.n_active = ws.ffn.n_active;
+    a.qh = ws.qh;
+    a.dh = ws.dh;
+    a.eo = ws.expert_out;
+    a.so = ws.shared_out;
+    a.ssq = ws.ssq;
+    a.sync = ws.sync;
+    a.trace = (ev && ev->wg_trace) ? ev->wg_trace : nullptr;
+    a.trace_words = (ev && ev->wg_trace) ? ev->trace_words : 0;
+    moe::launch_layer_fused(a, st, ev);
+    return launched("moe_layer (fused)");
+  }
   if ((rc = do_route(c, T, x, w_router, bias, idx, w, ws.route, st, ev))) return rc;
   moe::launch_quant_act(x, ws.q, ws.d, (int64_t)T * c.hidden, st, ev);
   if ((rc = launched("moe_layer quant"))) return rc;

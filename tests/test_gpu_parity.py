@@ -320,7 +320,7 @@ def test_layer_graph_replays_match_eager(dev, real):
     cfg = moe.Config.of(synth.REAL)
     st = torch.cuda.Stream(device=dev)
     xs = [to_d(synth.tokens_perturbed(synth.REAL, 21 + i, 4), dev) for i in range(3)]
-    ws = torch.empty(moe.layer_workspace(cfg, 4), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(moe.layer_workspace(cfg, 4), dtype=torch.uint8, device=dev)
     with torch.cuda.stream(st):
         eager = [h(moe.layer(cfg, x, real.wr_d, real.bias_d, real.experts_d, real.shared_d,
                              workspace=ws)) for x in xs]
@@ -342,3 +342,20 @@ def test_layer_graph_replays_match_eager(dev, real):
             for y, e in zip(ys, eager):
                 assert np.array_equal(h(y), e), f"replay {rep}"
             assert np.all(np.isfinite(h(other)))
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 16])
+def test_layer_counters_return_to_zero(dev, real, T):
+    """The single-launch path leaves its counter region zero and records no
+    timed-out wait, call after call (same workspace)."""
+    cfg = moe.Config.of(synth.REAL)
+    ws = torch.zeros(moe.layer_workspace(cfg, T), dtype=torch.uint8, device=dev)
+    nsync = moe.layer_sync_bytes()
+    outs = []
+    for rep in range(3):
+        x = to_d(synth.tokens(synth.REAL, 300 + rep, T), dev)
+        outs.append(h(moe.layer(cfg, x, real.wr_d, real.bias_d, real.experts_d, real.shared_d,
+                                workspace=ws, want_norm=True)[1]))
+        sync = h(ws[:nsync])
+        assert np.count_nonzero(sync) == 0, f"call {rep}: counters not cleared"
+    assert all(np.all(np.isfinite(o)) for o in outs)
