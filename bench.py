@@ -103,13 +103,15 @@ def layer_bytes(shape, T, U, bb):
     return E * H * 4 + E * 4 + (U + shape.n_shared) * bb + 2 * T * H * 4
 
 
-def gate_up_bytes(shape, T, U):
+def gate_up_bytes(shape, T, U, h_bytes_per_elem):
     """Algorithmic bytes of one gate/up launch: gate and up codes and row scales
-    of U + shared experts, Q8_0 activations in, fp32 h out."""
+    of U + shared experts, Q8_0 activations in, h out (int8 codes + fp32 block
+    scales on the small-batch path, fp32 otherwise)."""
     H, I, K = shape.hidden, shape.inter, shape.top_k
     per_expert = 2 * I * H * shape.wbits // 8 + 2 * I * 4
     pairs = T * K + T * shape.n_shared
-    return (U + shape.n_shared) * per_expert + T * H + T * (H // 32) * 4 + pairs * I * 4
+    return ((U + shape.n_shared) * per_expert + T * H + T * (H // 32) * 4
+            + pairs * I * h_bytes_per_elem)
 
 
 def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s):
@@ -291,12 +293,10 @@ def main():
     idx_h = idx_all.cpu().numpy()
     U = float(np.mean([np.unique(idx_h[i]).size for i in range(W, W + K)]))
     step_bytes = layer_bytes(shape, T, U, bb)
-    if "fused" in stage_ms:  # the whole step is one kernel
-        dom, dom_bytes = "fused layer kernel (whole step)", step_bytes
-        dom_sec = stage_ms["fused"] * 1e-3
-    else:
-        dom, dom_bytes = "gate_up (expert gate/up + SwiGLU)", gate_up_bytes(shape, T, U)
-        dom_sec = stage_ms["gate_up"] * 1e-3
+    small = "router_select" not in stage_ms  # three-kernel small-batch path
+    dom = "gate_up (expert gate/up + SwiGLU" + (" + Q8_0 of h)" if small else ")")
+    dom_bytes = gate_up_bytes(shape, T, U, 1 + 4 / 32 if small else 4)
+    dom_sec = stage_ms["gate_up"] * 1e-3
     achieved = dom_bytes / dom_sec / 1e9
 
     out = {

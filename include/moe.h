@@ -213,27 +213,22 @@ enum {
   MOE_STAGE_GATE_UP = 4,
   MOE_STAGE_DOWN = 5,
   MOE_STAGE_COMBINE = 6,
-  MOE_STAGE_FUSED = 7, /* the single-launch layer kernel (1..16 tokens) */
   MOE_N_STAGES = 8
 };
 typedef struct moe_events {
   void *start[MOE_N_STAGES];
   void *stop[MOE_N_STAGES];
-  /* Optional device buffer (uint64 [n_workgroups][4]) for the single-launch
-   * layer kernel: per workgroup, the GPU wall clock (100 MHz) at start, when
-   * its first dependency was met, when its work ended, and at exit.  Word 3
-   * of workgroup 0's record is overwritten with the number of workgroups
-   * only if the buffer is large enough: trace_words >= 4 * n_workgroups. */
-  uint64_t *wg_trace;
-  uint64_t trace_words;
 } moe_events;
 
 /* ---------------------------------------------------------------------------
  * moe_layer — the whole step: routing, Q8_0 of x, grouping, expert FFNs and
  * combine on one stream, with all intermediates in the workspace.  For 1..16
- * tokens (and T*n_experts <= 4096) it runs as ONE kernel launch whose stages
- * overlap (the same arithmetic as the separate calls); otherwise it chains
- * the kernels of moe_route, moe_quant_act, moe_expert_ffn and moe_combine.
+ * tokens (and T*n_experts <= 4096) it runs as three kernels (router with
+ * selection and grouping; gate/up with the Q8_0 of h; down with the combine
+ * and optional RMSNorm) whose stage timestamps are MOE_STAGE_ROUTER_SCORES,
+ * MOE_STAGE_GATE_UP and MOE_STAGE_DOWN; otherwise it chains the kernels of
+ * moe_route, moe_quant_act, moe_expert_ffn and moe_combine.  Both give the
+ * same arithmetic as the separate calls.
  * Workspace precondition: the workspace must be zero-filled before its first
  * use by moe_layer (it begins with counters that every call leaves at zero);
  * between moe_layer calls it must not be handed to other calls.  Calls that
@@ -246,8 +241,8 @@ typedef struct moe_events {
  * ------------------------------------------------------------------------- */
 size_t moe_layer_workspace(const moe_cfg *cfg, int32_t T);
 /* Bytes at the start of a moe_layer workspace that hold its counters (the
- * part that must be zero before first use; moe_layer leaves it zero, except
- * for a diagnostic count of bounded waits that timed out, at byte 1280). */
+ * part that must be zero before first use; every moe_layer call leaves it
+ * zero). */
 size_t moe_layer_sync_bytes(void);
 int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
               const float *bias, const void *experts, const void *shared,

@@ -43,13 +43,11 @@ class MoeCfg(ctypes.Structure):
 
 
 MOE_N_STAGES = 8
-STAGES = dict(router_scores=0, router_select=1, quant=2, group=3, gate_up=4, down=5, combine=6,
-              fused=7)
+STAGES = dict(router_scores=0, router_select=1, quant=2, group=3, gate_up=4, down=5, combine=6)
 
 
 class MoeEvents(ctypes.Structure):
-    _fields_ = [("start", ctypes.c_void_p * MOE_N_STAGES), ("stop", ctypes.c_void_p * MOE_N_STAGES),
-                ("wg_trace", ctypes.c_void_p), ("trace_words", ctypes.c_uint64)]
+    _fields_ = [("start", ctypes.c_void_p * MOE_N_STAGES), ("stop", ctypes.c_void_p * MOE_N_STAGES)]
 
 
 class MoeFfnDebug(ctypes.Structure):
@@ -177,9 +175,6 @@ def layer_sync_bytes() -> int:
     """Leading bytes of a layer workspace holding its (zero-between-calls) counters."""
     return int(lib().moe_layer_sync_bytes())
 
-
-# byte offset of the count of bounded waits that timed out (diagnostic)
-LAYER_ERR_OFFSET = 5 * 256
 
 
 def _workspace(nbytes, device, ws=None):

@@ -8,11 +8,27 @@
 
 namespace moe {
 
-// --- wave reductions (wave64; ds_swizzle/dpp chosen by the compiler) -------
+// --- wave reductions (wave64) ----------------------------------------------
+// DPP moves stay in the VALU (no LDS round trip per step, unlike the
+// ds_bpermute that __shfl_xor lowers to).  Lanes a DPP move does not write
+// receive `old` (0 here, the identity of the sum).
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, BANK_MASK, true));
+}
+
+// Sum over the 64 lanes, returned to every lane: pairs and quads by
+// quad_perm, rows of 16 by two rotations, then rows 0+1 and 2+3 by the row
+// broadcasts of lanes 15 and 31; lane 63 ends with the total.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
-  return v;
+  v += dpp_f<0xB1>(v);        // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);        // quad_perm [2,3,0,1]
+  v += dpp_f<0x124>(v);       // row_ror:4
+  v += dpp_f<0x128>(v);       // row_ror:8
+  v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 -> rows 1 and 3
+  v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 -> rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

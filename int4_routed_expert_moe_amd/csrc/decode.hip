@@ -1,0 +1,797 @@
+// The routed-MoE layer step for small batches (decode and multi-token
+// verify, 1..16 tokens) in three kernels.
+//
+// Same method and arithmetic as the separate calls ("Show HN: 遅いコンピュータ
+// で GLM 5.2 を実行する", section 実装済みの主な機能: sigmoid router with
+// noaux_tc and routed_scaling_factor, shared expert, Q8_0 int8 activations,
+// packed int4/int2 weights with per-row scales, batch-union MoE).
+//
+//  K1 k_route_small   (E/2 workgroups) Q8_0 of a slice of x; fixed-order fp32
+//                     logits of two experts; the last workgroup to finish
+//                     (two-level count) selects every token's experts and
+//                     groups the T*K slots by expert (batch union).
+//  K2 k_gate_up_small (I/32 x slots) 32 rows of h = silu(gate x) * (up x)
+//                     for one expert slot and its tokens, written directly as
+//                     its Q8_0 block (no fp32 h round trip).
+//  K3 k_down_small    (H/8 workgroups) 8 output rows for every expert slot and
+//                     token, combined in LDS in rank order into y (+ residual);
+//                     with y_norm, the last workgroup applies the unit-gain
+//                     RMSNorm to whole rows.
+// Only the "last workgroup" steps communicate between workgroups; each costs
+// one agent-scope release per workgroup and one acquire by the last one.
+// Their counters sit in a zero-initialised workspace region that each call
+// leaves at zero.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// expert slots whose down rows a K3 wave loads together (rows in flight)
+#ifndef MOE_K3_SLOTS
+#define MOE_K3_SLOTS 4
+#endif
+
+namespace sbk {
+constexpr int TMAX = 16;
+constexpr int LINE = 64;  // uint32 words between counters (256 B)
+constexpr int C_RSUB = 0;   // 16 router sub-counters
+constexpr int C_ROUTE = 16;
+constexpr int C_NORM = 17;
+constexpr int C_END = 18;
+constexpr int RT = 8;       // output rows per K3 workgroup (2 per wave)
+constexpr int MAXP = TMAX * 17;  // pairs: T*K routed + T shared, K <= 16
+}  // namespace sbk
+
+size_t small_batch_sync_bytes() { return (size_t)sbk::C_END * sbk::LINE * sizeof(uint32_t); }
+
+__device__ __forceinline__ uint32_t *sctr(const LayerArgs &a, int c) {
+  return a.sync + (size_t)c * sbk::LINE;
+}
+
+__device__ __forceinline__ void release_fence() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void acquire_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+__device__ __forceinline__ void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The block's global writes become visible device-wide (stores drained, one
+// L2 write-back by thread 0), then thread 0 counts; old value broadcast.
+__device__ uint32_t block_count(uint32_t *p, uint32_t *lds_word) {
+  drain_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    release_fence();
+    *lds_word = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  const uint32_t old = *lds_word;
+  __syncthreads();
+  return old;
+}
+
+// The last block acquires what the others wrote (one L2 invalidate).
+__device__ void block_acquire() {
+  if (threadIdx.x == 0) acquire_fence();
+  __syncthreads();
+}
+
+__device__ __forceinline__ float exp_fixed_sb(float y) {
+  y = y > 87.0f ? 87.0f : y;
+  y = y < -87.0f ? -87.0f : y;
+  const float n = __builtin_rintf(y * 1.44269502f);
+  float r = __builtin_fmaf(-n, 0.693145751953125f, y);
+  r = __builtin_fmaf(-n, 1.42860677e-06f, r);
+  float p = 1.98412701e-04f;
+  p = __builtin_fmaf(p, r, 1.38888892e-03f);
+  p = __builtin_fmaf(p, r, 8.33333377e-03f);
+  p = __builtin_fmaf(p, r, 4.16666679e-02f);
+  p = __builtin_fmaf(p, r, 1.66666672e-01f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return __builtin_ldexpf(p, (int)n);
+}
+
+// Q8_0 of one 32-block held by 8 consecutive lanes (4 values each).
+__device__ __forceinline__ uint32_t q8_quad(float4 v, float *dd_out) {
+  float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+  m = fmaxf(m, __shfl_xor(m, 1, 8));
+  m = fmaxf(m, __shfl_xor(m, 2, 8));
+  m = fmaxf(m, __shfl_xor(m, 4, 8));
+  const float dd = m / 127.0f;
+  const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
+  auto cv = [&](float f) -> uint32_t {
+    float r = roundf(f * id);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (uint32_t)(uint8_t)(int8_t)(int)r;
+  };
+  *dd_out = dd;
+  return cv(v.x) | (cv(v.y) << 8) | (cv(v.z) << 16) | (cv(v.w) << 24);
+}
+
+// ============================================================ K1: routing
+
+struct RouteLds {
+  uint32_t word;
+  union {
+    float part[2][sbk::TMAX][128];  // chunk partials of the block's two experts
+    struct {
+      float sb[1024];               // biased scores of the token being selected
+      float s[1024];                // its unbiased scores
+      unsigned long long key[1024];  // (biased score, -index) of every expert
+      unsigned long long gkey[64];
+      unsigned long long kmask;
+      unsigned long long fkey[1024]; // finalists: K per kept group (0 = empty)
+      int fe[1024];
+      int sel[16];
+      float ssel[16];                // unbiased scores of the picks, rank order
+      int32_t idx[256];             // every token's selection, slot order
+      int32_t cnt[1024];
+      int32_t off[1025];
+      int32_t wt[8];
+    } fin;
+  } u;
+};
+
+// running top-2 of a sequence of values (the two largest, multiset)
+__device__ __forceinline__ void top2(float v, float &m1, float &m2) {
+  const float hi = fmaxf(m1, v), lo = fminf(m1, v);
+  m1 = hi;
+  m2 = fmaxf(m2, lo);
+}
+
+__device__ __forceinline__ unsigned long long rank_key(float v, int i) {
+  return ((unsigned long long)float_key(v) << 32) | (0xFFFFFFFFu - (uint32_t)i);
+}
+
+// Selection for token t by the whole block, by ranks instead of repeated
+// argmax: with key = (score, -index) (all distinct), an item is among the
+// best n exactly when fewer than n items have a larger key, and its rank is
+// its position in the descending order; this is the same set and order as
+// picking the maximum n times with ties to the lower index.
+__device__ void select_token(const LayerArgs &a, RouteLds &sm, int t) {
+  const int E = a.E, G = a.G, gs = E / G, K = a.K;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    const float v = a.sb[(size_t)t * E + e];
+    sm.u.fin.sb[e] = v;
+    sm.u.fin.s[e] = a.s[(size_t)t * E + e];
+    sm.u.fin.key[e] = rank_key(v, e);
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {  // group score: sum of the two largest biased scores
+    const int g = threadIdx.x;
+    float m1 = -INFINITY, m2 = -INFINITY;
+    const float *p = sm.u.fin.sb + g * gs;
+    if ((gs & 15) == 0) {  // 4 independent 16-byte LDS reads per step
+      for (int e = 0; e < gs; e += 16) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) v[u] = *reinterpret_cast<const float4 *>(p + e + 4 * u);
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          top2(v[u].x, m1, m2);
+          top2(v[u].y, m1, m2);
+          top2(v[u].z, m1, m2);
+          top2(v[u].w, m1, m2);
+        }
+      }
+    } else {
+      for (int e = 0; e < gs; e++) top2(p[e], m1, m2);
+    }
+    sm.u.fin.gkey[g] = rank_key(m1 + m2, g);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {  // kept groups as a bitmask (G <= 64)
+    bool kept = false;
+    if (threadIdx.x < G) {
+      const unsigned long long mine = sm.u.fin.gkey[threadIdx.x];
+      int r = 0;
+      for (int g = 0; g < G; g++) r += sm.u.fin.gkey[g] > mine;
+      kept = r < a.TG;
+    }
+    const unsigned long long m = __ballot(kept);
+    if (threadIdx.x == 0) sm.u.fin.kmask = m;
+  }
+  const int F = a.TG * K;  // finalist slots: K per kept group
+  for (int f = threadIdx.x; f < F; f += 256) sm.u.fin.fkey[f] = 0ull;
+  __syncthreads();
+  // stage A: rank within the group; a global top-K item is in its group's
+  // top-K, so each kept group hands its best K to slots j*K .. j*K+K-1
+  const unsigned long long kmask = sm.u.fin.kmask;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    const int g = e / gs;
+    if (!((kmask >> g) & 1ull)) continue;
+    const unsigned long long mine = sm.u.fin.key[e];
+    const unsigned long long *kk = sm.u.fin.key + g * gs;
+    int r = 0;
+    if ((gs & 15) == 0) {  // 8 independent 16-byte LDS reads per step
+      for (int i = 0; i < gs; i += 16) {
+        ulonglong2 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = *reinterpret_cast<const ulonglong2 *>(kk + i + 2 * u);
+#pragma unroll
+        for (int u = 0; u < 8; u++) r += (v[u].x > mine) + (v[u].y > mine);
+      }
+    } else {
+      for (int i = 0; i < gs; i++) r += kk[i] > mine;
+    }
+    if (r < K) {
+      const int j = __popcll(kmask & ((1ull << g) - 1ull));
+      sm.u.fin.fkey[j * K + r] = mine;
+      sm.u.fin.fe[j * K + r] = e;
+    }
+  }
+  __syncthreads();
+  // stage B: rank among the finalists = rank among all candidates
+  for (int f = threadIdx.x; f < F; f += 256) {
+    const unsigned long long mine = sm.u.fin.fkey[f];
+    if (mine == 0ull) continue;
+    int r = 0;
+    int i = 0;
+    for (; i + 16 <= F; i += 16) {
+      ulonglong2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; u++) v[u] = *reinterpret_cast<const ulonglong2 *>(sm.u.fin.fkey + i + 2 * u);
+#pragma unroll
+      for (int u = 0; u < 8; u++) r += (v[u].x > mine) + (v[u].y > mine);
+    }
+    for (; i < F; i++) r += sm.u.fin.fkey[i] > mine;
+    if (r < K) {
+      sm.u.fin.sel[r] = sm.u.fin.fe[f];
+      sm.u.fin.ssel[r] = sm.u.fin.s[sm.u.fin.fe[f]];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < K) {  // weights: unbiased scores over their sum in rank order
+    float sv[16];
+#pragma unroll
+    for (int k = 0; k < 16; k += 4) {  // four 16-byte reads, one round trip
+      const float4 v4 = *reinterpret_cast<const float4 *>(sm.u.fin.ssel + k);
+      sv[k] = v4.x;
+      sv[k + 1] = v4.y;
+      sv[k + 2] = v4.z;
+      sv[k + 3] = v4.w;
+    }
+    float S = sv[0];
+#pragma unroll
+    for (int k = 1; k < 16; k++) S = (k < K) ? S + sv[k] : S;
+    const int e = sm.u.fin.sel[threadIdx.x];
+    a.idx[t * K + threadIdx.x] = e;
+    a.w[t * K + threadIdx.x] = (sm.u.fin.ssel[threadIdx.x] / S) * a.scale;
+    sm.u.fin.idx[t * K + threadIdx.x] = e;
+  }
+  __syncthreads();
+}
+
+__device__ int exscan256(int v, int *wt, int *total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wt[wv] = x;
+  __syncthreads();
+  int pre = 0, all = 0;
+  for (int w = 0; w < 4; w++) {
+    pre += (w < wv) ? wt[w] : 0;
+    all += wt[w];
+  }
+  __syncthreads();
+  *total = all;
+  return pre + x - v;
+}
+
+// Select every token, then group the T*K slots (stable, by expert): counts
+// by LDS atomics, one prefix scan of (count, active) packed in one int.
+__device__ void select_and_group(const LayerArgs &a, RouteLds &sm) {
+  const int E = a.E, T = a.T, K = a.K, n = T * K;
+  for (int t = 0; t < T; t++) select_token(a, sm, t);
+  for (int e = threadIdx.x; e < E; e += 256) sm.u.fin.cnt[e] = 0;
+  __syncthreads();
+  if (threadIdx.x < n) atomicAdd(&sm.u.fin.cnt[sm.u.fin.idx[threadIdx.x]], 1);
+  __syncthreads();
+  int c[4], loc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int e = threadIdx.x * 4 + j;
+    c[j] = e < E ? sm.u.fin.cnt[e] : 0;
+    loc += c[j] + ((c[j] > 0) << 16);  // counts <= 256, active experts <= 1024
+  }
+  int total;
+  const int pk = exscan256(loc, sm.u.fin.wt, &total);
+  int pre = pk & 0xFFFF, apre = pk >> 16;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int e = threadIdx.x * 4 + j;
+    if (e < E) {
+      sm.u.fin.off[e] = pre;
+      a.offsets[e] = pre;
+      a.counts[e] = c[j];
+      a.active[e] = -1;
+    }
+    pre += c[j];
+  }
+  if (threadIdx.x == 0) {
+    a.offsets[E] = total & 0xFFFF;
+    a.n_active[0] = total >> 16;
+  }
+  __syncthreads();  // active[] = -1 before the compaction
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int e = threadIdx.x * 4 + j;
+    if (e < E && c[j] > 0) a.active[apre++] = e;
+  }
+  if (threadIdx.x < n) {
+    const int sl = threadIdx.x, e = sm.u.fin.idx[sl];
+    int rank = 0;
+    for (int j = 0; j < sl; j++) rank += sm.u.fin.idx[j] == e;
+    a.perm[sm.u.fin.off[e] + rank] = sl;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_route_small(LayerArgs a) {
+  __shared__ RouteLds sm;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int H = a.H, E = a.E, T = a.T;
+  // 1. Q8_0 of a slice of x, 8 lanes per block of 32
+  {
+    const int nbx = T * (H / 32);
+    const int per = (nbx + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int b0 = r * per, b1 = min(nbx, b0 + per);
+    for (int base = b0; base < b1; base += 32) {
+      const int blk = base + (tid >> 3), sub = tid & 7;
+      const bool ok = blk < b1;
+      const float4 v = ok ? reinterpret_cast<const float4 *>(a.x)[(size_t)blk * 8 + sub]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      float dd;
+      const uint32_t packed = q8_quad(v, &dd);
+      if (ok) {
+        reinterpret_cast<uint32_t *>(a.q)[(size_t)blk * 8 + sub] = packed;
+        if (sub == 0) a.d[blk] = dd;
+      }
+    }
+  }
+  // 2. logits of experts 2r and 2r+1; thread l < H/64 of each half owns the
+  //    chunk l (an fma chain over its 64 elements in index order)
+  const int half = tid >> 7, l = tid & 127;
+  const int e = 2 * r + half;
+  const int nch = H / 64;
+  if (e < E && l < nch) {
+    const float4 *w4 = reinterpret_cast<const float4 *>(a.wr + (size_t)e * H + l * 64);
+    float4 wv[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) wv[k] = w4[k];
+    for (int t = 0; t < T; t++) {
+      const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * H + l * 64);
+      float4 xv[16];
+#pragma unroll
+      for (int k = 0; k < 16; k++) xv[k] = x4[k];
+      // keep every load of W and x ahead of the chain (one memory latency,
+      // not sixteen): nothing is scheduled across this point
+      __builtin_amdgcn_sched_barrier(0);
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; k++) {
+        acc = __builtin_fmaf(xv[k].x, wv[k].x, acc);
+        acc = __builtin_fmaf(xv[k].y, wv[k].y, acc);
+        acc = __builtin_fmaf(xv[k].z, wv[k].z, acc);
+        acc = __builtin_fmaf(xv[k].w, wv[k].w, acc);
+      }
+      sm.u.part[half][t][l] = acc;
+    }
+  }
+  __syncthreads();
+  if (e < E && l < T) {  // chunk partials added left to right
+    float tot = sm.u.part[half][l][0];
+    for (int c = 1; c < nch; c++) tot = tot + sm.u.part[half][l][c];
+    const float sv = 1.0f / (1.0f + exp_fixed_sb(-tot));
+    a.s[(size_t)l * E + e] = sv;
+    a.sb[(size_t)l * E + e] = sv + a.bias[e];
+  }
+  // 3. two-level count (same-address atomics serialise); the last block
+  //    selects and groups, then clears the counters it alone still uses
+  const int nblk = gridDim.x;
+  const int sub = r % 16;
+  const uint32_t in_sub = (uint32_t)((nblk - 1 - sub) / 16 + 1);
+  uint32_t old = block_count(sctr(a, sbk::C_RSUB + sub), &sm.word);
+  if (old != in_sub - 1) return;
+  const uint32_t subs = (uint32_t)(nblk < 16 ? nblk : 16);
+  old = block_count(sctr(a, sbk::C_ROUTE), &sm.word);
+  if (old != subs - 1) return;
+  block_acquire();
+  select_and_group(a, sm);
+  if (tid < 16) *sctr(a, sbk::C_RSUB + tid) = 0u;
+  if (tid == 0) *sctr(a, sbk::C_ROUTE) = 0u;
+}
+
+// ============================================================ operands
+
+template <int WB>
+struct Act;
+template <>
+struct Act<4> {
+  QBlock q;
+  float d;  // block scale / 16 (the int4 dot returns 16 x the block dot)
+};
+template <>
+struct Act<2> {
+  int f[4][4];
+  float da, db;  // scales / 64 of the two blocks of a 64-code piece
+};
+
+template <int WB>
+__device__ __forceinline__ void load_act(const int8_t *q, const float *d, int p, bool ok,
+                                         Act<WB> &o);
+template <>
+__device__ __forceinline__ void load_act<4>(const int8_t *q, const float *d, int p, bool ok,
+                                            Act<4> &o) {
+  uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
+  float dd = 0.0f;
+  if (ok) {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(q + 32 * p);
+    x0 = qp[0];
+    x1 = qp[1];
+    dd = d[p] * (1.0f / 16.0f);
+  }
+  o.q = split_block(x0, x1);
+  o.d = dd;
+}
+template <>
+__device__ __forceinline__ void load_act<2>(const int8_t *q, const float *d, int p, bool ok,
+                                            Act<2> &o) {
+  uint4 z[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                make_uint4(0, 0, 0, 0)};
+  float d0 = 0.0f, d1 = 0.0f;
+  if (ok) {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(q + 64 * p);
+#pragma unroll
+    for (int j = 0; j < 4; j++) z[j] = qp[j];
+    d0 = d[2 * p] * (1.0f / 64.0f);
+    d1 = d[2 * p + 1] * (1.0f / 64.0f);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+#pragma unroll
+    for (int fi = 0; fi < 4; fi++) {
+      const uint32_t sel = (uint32_t)(fi | ((4 + fi) << 8)) | 0x0C0C0000u;
+      const uint32_t a01 = __builtin_amdgcn_perm(z[j].y, z[j].x, sel);
+      const uint32_t a23 = __builtin_amdgcn_perm(z[j].w, z[j].z, sel);
+      o.f[fi][j] = (int)__builtin_amdgcn_perm(a23, a01, 0x05040100u);
+    }
+  }
+  o.da = d0;
+  o.db = d1;
+}
+
+// sum_b d_b * P_b of one 16-byte weight piece against one token
+template <int WB>
+__device__ __forceinline__ float piece_dot(const uint4 w, const Act<WB> &a);
+template <>
+__device__ __forceinline__ float piece_dot<4>(const uint4 w, const Act<4> &a) {
+  return (float)dot_int4_block16(w, a.q) * a.d;
+}
+template <>
+__device__ __forceinline__ float piece_dot<2>(const uint4 w, const Act<2> &a) {
+  int x = 0, y = 0;
+#pragma unroll
+  for (int fi = 0; fi < 4; fi++) {
+    x = sdot4(int2_field64(w.x, fi), a.f[fi][0], x);
+    x = sdot4(int2_field64(w.y, fi), a.f[fi][1], x);
+    y = sdot4(int2_field64(w.z, fi), a.f[fi][2], y);
+    y = sdot4(int2_field64(w.w, fi), a.f[fi][3], y);
+  }
+  return fmaf((float)x, a.da, (float)y * a.db);
+}
+
+// Expert slot j: 0 .. n_shared-1 the shared expert, then the active routed
+// experts in ascending order.  Indices read from device memory are clamped.
+struct Slot {
+  const uint8_t *blob;
+  int n_tok;
+  bool shared;
+  const int32_t *list;
+};
+
+__device__ __forceinline__ Slot slot_of(const LayerArgs &a, int slot) {
+  Slot s;
+  if (slot < a.n_shared) {
+    s.blob = a.shared;
+    s.n_tok = a.T;
+    s.shared = true;
+    s.list = nullptr;
+  } else {
+    const int n_slots = a.T * a.K;
+    int e = a.active[slot - a.n_shared];
+    e = min(max(e, 0), a.E - 1);
+    const int lo = min(max(a.offsets[e], 0), n_slots);
+    const int hi = min(max(a.offsets[e + 1], lo), n_slots);
+    s.blob = a.experts + (size_t)e * a.blob_bytes;
+    s.n_tok = hi - lo;
+    s.shared = false;
+    s.list = a.perm + lo;
+  }
+  return s;
+}
+
+// token index and pair index (slot id t*K+k, or T*K + t for the shared expert)
+__device__ __forceinline__ void tok_pair(const LayerArgs &a, const Slot &s, int i, int &tok,
+                                         int &pair) {
+  if (s.shared) {
+    tok = i;
+    pair = a.T * a.K + i;
+  } else {
+    const int sl = min(max(s.list[i], 0), a.T * a.K - 1);
+    tok = sl / a.K;
+    pair = sl;
+  }
+}
+
+__device__ __forceinline__ int n_active_clamped(const LayerArgs &a) {
+  return min(max(a.n_active[0], 0), a.n_slots_ub - a.n_shared);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// ============================================================ K2: gate/up
+
+// Workgroup (blk, slot): rows 32 blk .. 32 blk + 31 of h for the slot's
+// tokens.  Wave wv streams rows 8wv .. 8wv+7 as four batches of two rows (a
+// gate and an up row each); registers stay low enough for every workgroup
+// of a decode step to be resident at once, which keeps ~27 MB in flight.  h goes to LDS; the 32 values of each token become one Q8_0 block.
+template <int WB, int TT, int NPL>
+__global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
+  __shared__ float hb[TT][32];
+  const int slot = blockIdx.y, blk = blockIdx.x;
+  if (slot >= a.n_shared && slot - a.n_shared >= n_active_clamped(a)) return;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int H = a.H, I = a.I;
+  const int npieces = H / (128 / WB);
+  const size_t row_b = (size_t)H * WB / 8;
+  const Slot s = slot_of(a, slot);
+  const uint8_t *gate = s.blob;
+  const uint8_t *up = s.blob + (size_t)I * row_b;
+  const float *scales = reinterpret_cast<const float *>(s.blob + 3 * (size_t)I * row_b);
+  const int rbase = blk * 32 + wv * 8;
+
+  for (int c0 = 0; c0 < s.n_tok; c0 += TT) {
+    uint4 wb[2][2][NPL];  // [row of batch][gate, up][piece]
+    auto load_batch = [&](int bt) {
+#pragma unroll
+      for (int rr = 0; rr < 2; rr++) {
+        const int r = rbase + bt * 2 + rr;
+#pragma unroll
+        for (int i = 0; i < NPL; i++) {
+          const int p = lane + 64 * i;
+          const bool ok = p < npieces;
+          wb[rr][0][i] = ok ? reinterpret_cast<const uint4 *>(gate + (size_t)r * row_b)[p]
+                            : make_uint4(0, 0, 0, 0);
+          wb[rr][1][i] = ok ? reinterpret_cast<const uint4 *>(up + (size_t)r * row_b)[p]
+                            : make_uint4(0, 0, 0, 0);
+        }
+      }
+    };
+    load_batch(0);
+    Act<WB> act[NPL][TT];
+    int pair[TT];
+#pragma unroll
+    for (int t = 0; t < TT; t++) {
+      int tok = 0;
+      pair[t] = -1;
+      if (c0 + t < s.n_tok) tok_pair(a, s, c0 + t, tok, pair[t]);
+#pragma unroll
+      for (int i = 0; i < NPL; i++) {
+        const int p = lane + 64 * i;
+        load_act<WB>(a.q + (size_t)tok * H, a.d + (size_t)tok * (H / 32), p,
+                     pair[t] >= 0 && p < npieces, act[i][t]);
+      }
+    }
+#pragma unroll
+    for (int bt = 0; bt < 4; bt++) {
+      if (bt > 0) load_batch(bt);
+#pragma unroll
+      for (int rr = 0; rr < 2; rr++) {
+        const int r = rbase + bt * 2 + rr;
+        float g[TT], u[TT];
+#pragma unroll
+        for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NPL; i++) {
+#pragma unroll
+          for (int t = 0; t < TT; t++) {
+            g[t] += piece_dot<WB>(wb[rr][0][i], act[i][t]);
+            u[t] += piece_dot<WB>(wb[rr][1][i], act[i][t]);
+          }
+        }
+        const float sg = scales[r], su = scales[I + r];
+#pragma unroll
+        for (int t = 0; t < TT; t++) {
+          const float gv = sg * wave_sum(g[t]);
+          const float uv = su * wave_sum(u[t]);
+          if (lane == 0) hb[t][wv * 8 + bt * 2 + rr] = silu(gv) * uv;
+        }
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < TT * 8) {  // Q8_0 of each token's 32 h values
+      const int t = threadIdx.x >> 3, j = threadIdx.x & 7;
+      const float4 v = make_float4(hb[t][4 * j], hb[t][4 * j + 1], hb[t][4 * j + 2],
+                                   hb[t][4 * j + 3]);
+      float dd;
+      const uint32_t packed = q8_quad(v, &dd);
+      if (pair[t] >= 0) {
+        reinterpret_cast<uint32_t *>(a.qh + (size_t)pair[t] * I + blk * 32)[j] = packed;
+        if (j == 0) a.dh[(size_t)pair[t] * (I / 32) + blk] = dd;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ============================================================ K3: down + combine
+
+// Workgroup `tile`: output rows 8 tile .. 8 tile + 7 of every expert slot for
+// every token (wave wv: rows 2wv, 2wv+1), slots taken SB at a time with all
+// their weight rows loaded up front; partial outputs go to LDS by pair, and
+// the tile is combined in rank order:
+//   y[t] = residual[t] + shared[t] + sum_k w[t,k] * expert_k[t]
+template <int WB, int TT, int NPL, int SB>
+__global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
+  __shared__ float part[sbk::MAXP][sbk::RT];
+  __shared__ float red[sbk::TMAX];
+  __shared__ uint32_t word;
+  const int tile = blockIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int H = a.H, I = a.I, T = a.T, K = a.K;
+  const int npieces = I / (128 / WB);
+  const size_t down_off = 2 * (size_t)I * ((size_t)H * WB / 8);
+  const size_t row_b = (size_t)I * WB / 8;
+  const int n_slots = a.n_shared + n_active_clamped(a);
+  const int j0 = tile * sbk::RT + wv * 2;
+
+  for (int s0 = 0; s0 < n_slots; s0 += SB) {
+    uint4 wd[SB][2][NPL];
+    float sd[SB][2];
+    Slot sl[SB];
+#pragma unroll
+    for (int b = 0; b < SB; b++) {
+      const bool ok_s = s0 + b < n_slots;
+      sl[b] = slot_of(a, ok_s ? s0 + b : 0);
+      if (!ok_s) sl[b].n_tok = 0;
+      const uint8_t *down = sl[b].blob + down_off;
+      const float *sdp =
+          reinterpret_cast<const float *>(sl[b].blob + 3 * (size_t)I * ((size_t)H * WB / 8)) +
+          2 * I;
+#pragma unroll
+      for (int rr = 0; rr < 2; rr++) {
+#pragma unroll
+        for (int i = 0; i < NPL; i++) {
+          const int p = lane + 64 * i;
+          wd[b][rr][i] = (ok_s && p < npieces)
+                             ? reinterpret_cast<const uint4 *>(down + (size_t)(j0 + rr) * row_b)[p]
+                             : make_uint4(0, 0, 0, 0);
+        }
+        sd[b][rr] = ok_s ? sdp[j0 + rr] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < SB; b++) {
+      for (int c0 = 0; c0 < sl[b].n_tok; c0 += TT) {
+        Act<WB> act[NPL][TT];
+        int pair[TT];
+#pragma unroll
+        for (int t = 0; t < TT; t++) {
+          int tok = 0;
+          pair[t] = -1;
+          if (c0 + t < sl[b].n_tok) tok_pair(a, sl[b], c0 + t, tok, pair[t]);
+          const int pp = pair[t] >= 0 ? pair[t] : 0;
+#pragma unroll
+          for (int i = 0; i < NPL; i++) {
+            const int p = lane + 64 * i;
+            load_act<WB>(a.qh + (size_t)pp * I, a.dh + (size_t)pp * (I / 32), p,
+                         pair[t] >= 0 && p < npieces, act[i][t]);
+          }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 2; rr++) {
+          float acc[TT];
+#pragma unroll
+          for (int t = 0; t < TT; t++) acc[t] = 0.0f;
+#pragma unroll
+          for (int i = 0; i < NPL; i++) {
+#pragma unroll
+            for (int t = 0; t < TT; t++) acc[t] += piece_dot<WB>(wd[b][rr][i], act[i][t]);
+          }
+#pragma unroll
+          for (int t = 0; t < TT; t++) {
+            const float yv = sd[b][rr] * wave_sum(acc[t]);
+            if (lane == 0 && pair[t] >= 0) part[pair[t]][wv * 2 + rr] = yv;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // combine in rank order, one thread per (token, row)
+  const bool norm = a.y_norm != nullptr;
+  float ss = 0.0f;
+  const int v = threadIdx.x;  // T * RT <= 128 threads active
+  if (v < T * sbk::RT) {
+    const int t = v / sbk::RT, r = v % sbk::RT, j = tile * sbk::RT + r;
+    float acc = a.residual ? a.residual[(size_t)t * H + j] : 0.0f;
+    if (a.n_shared) acc += part[T * K + t][r];
+    for (int k = 0; k < K; k++) acc = fmaf(a.w[t * K + k], part[t * K + k][r], acc);
+    a.y[(size_t)t * H + j] = acc;
+    ss = acc * acc;
+  }
+  if (!norm) return;
+  // per-token sum of squares of this tile's 8 rows (8 consecutive threads)
+  ss += __shfl_xor(ss, 1, 8);
+  ss += __shfl_xor(ss, 2, 8);
+  ss += __shfl_xor(ss, 4, 8);
+  const int n_tiles = gridDim.x;
+  if (v < T * sbk::RT && (v % sbk::RT) == 0) a.ssq[(size_t)(v / sbk::RT) * n_tiles + tile] = ss;
+  const uint32_t old = block_count(sctr(a, sbk::C_NORM), &word);
+  if (old != (uint32_t)n_tiles - 1) return;
+  block_acquire();
+  if (threadIdx.x < T) {  // tile sums added in tile order
+    float tot = 0.0f;
+    for (int i = 0; i < n_tiles; i++) tot += a.ssq[(size_t)threadIdx.x * n_tiles + i];
+    red[threadIdx.x] = 1.0f / sqrtf(tot / (float)H + a.eps);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * (H / 4); i += 256) {
+    const int t = i / (H / 4);
+    float4 y4 = reinterpret_cast<const float4 *>(a.y)[i];
+    const float inv = red[t];
+    y4.x *= inv;
+    y4.y *= inv;
+    y4.z *= inv;
+    y4.w *= inv;
+    reinterpret_cast<float4 *>(a.y_norm)[i] = y4;
+  }
+  if (threadIdx.x == 0) *sctr(a, sbk::C_NORM) = 0u;
+}
+
+// ============================================================ launch
+
+bool small_batch_supported(const moe_cfg &c, int T) {
+  if (T < 1 || T > sbk::TMAX) return false;
+  if (T * c.top_k > 256) return false;
+  if (c.hidden / 64 > 128 || c.hidden % sbk::RT) return false;
+  const int per = c.wbits == 4 ? 32 : 64;
+  return c.hidden / per <= 256 && c.inter / per <= 128;
+}
+
+template <int WB, int TT, int NPG, int NPD>
+static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
+  launch_k(k_route_small, dim3((a.E + 1) / 2), dim3(256), 0, st,
+           stage_ev(ev, MOE_STAGE_ROUTER_SCORES), a);
+  launch_k(k_gate_up_small<WB, TT, NPG>, dim3(a.I / 32, a.n_slots_ub), dim3(256), 0, st,
+           stage_ev(ev, MOE_STAGE_GATE_UP), a);
+  launch_k(k_down_small<WB, TT, NPD, MOE_K3_SLOTS>, dim3(a.H / sbk::RT), dim3(256), 0, st,
+           stage_ev(ev, MOE_STAGE_DOWN), a);
+}
+
+template <int WB, int TT>
+static void launch3_np(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
+  const int per = 128 / WB;
+  const int ng = (a.H / per + 63) / 64, nd = (a.I / per + 63) / 64;
+  if (ng <= 1 && nd <= 1) launch3<WB, TT, 1, 1>(a, st, ev);
+  else if (ng <= 2 && nd <= 1) launch3<WB, TT, 2, 1>(a, st, ev);
+  else if (ng <= 3 && nd <= 1) launch3<WB, TT, 3, 1>(a, st, ev);
+  else if (ng <= 4 && nd <= 1) launch3<WB, TT, 4, 1>(a, st, ev);
+  else launch3<WB, TT, 4, 2>(a, st, ev);
+}
+
+void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev) {
+  a.n_slots_ub = a.n_shared + (a.T * a.K < a.E ? a.T * a.K : a.E);
+  if (a.wbits == 4) {
+    if (a.T == 1) launch3_np<4, 1>(a, st, ev);
+    else launch3_np<4, 4>(a, st, ev);
+  } else {
+    if (a.T == 1) launch3_np<2, 1>(a, st, ev);
+    else launch3_np<2, 4>(a, st, ev);
+  }
+}
+
+}  // namespace moe

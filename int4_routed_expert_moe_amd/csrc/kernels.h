@@ -64,7 +64,7 @@ struct FfnArgs {
 };
 void launch_ffn_gemv(const FfnArgs &a, hipStream_t st, const moe_events *ev = nullptr);
 
-// Whole layer for 1..16 tokens in one launch (layer_fused.hip).
+// Whole layer for 1..16 tokens in three kernels (decode.hip).
 struct LayerArgs {
   int H, I, E, G, TG, K, T, n_shared, wbits;
   float scale, eps;
@@ -80,16 +80,12 @@ struct LayerArgs {
   int32_t *counts, *offsets, *perm, *active, *n_active;
   int8_t *qh;                    // [P][I] Q8_0 of h
   float *dh;                     // [P][I/32]
-  float *eo;                     // [T*K][H] routed expert outputs
-  float *so;                     // [T][H] shared expert output
-  float *ssq;                    // [T][H/32] partial sums of squares
+  float *ssq;                    // [T][H/8] partial sums of squares
   uint32_t *sync;                // zero-initialised counters
-  uint64_t *trace;               // optional [blocks][4] wall-clock stamps
-  uint64_t trace_words;
-  int n_router, nw_gu, nw_dn, n_slots_ub, xq_rows;
+  int n_slots_ub;
 };
-size_t layer_fused_sync_bytes();
-bool layer_fused_supported(const moe_cfg &c, int T);
-void launch_layer_fused(LayerArgs a, hipStream_t st, const moe_events *ev);
+size_t small_batch_sync_bytes();
+bool small_batch_supported(const moe_cfg &c, int T);
+void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev);
 
 }  // namespace moe

@@ -129,8 +129,8 @@ struct LayerWs {
 };
 LayerWs carve_layer(Carve &cv, const moe_cfg &c, int T) {
   LayerWs l;
-  l.sync = cv.take<uint32_t>(moe::layer_fused_sync_bytes() / sizeof(uint32_t));
-  l.ssq = cv.take<float>((size_t)T * (c.hidden / 32));
+  l.sync = cv.take<uint32_t>(moe::small_batch_sync_bytes() / sizeof(uint32_t));
+  l.ssq = cv.take<float>((size_t)T * (c.hidden / 8));
   l.route = carve_route(cv, c, T);
   l.idx = cv.take<int32_t>((size_t)T * c.top_k);
   l.w = cv.take<float>((size_t)T * c.top_k);
@@ -336,7 +336,7 @@ size_t moe_layer_workspace(const moe_cfg *cfg, int32_t T) {
   return cv.off;
 }
 
-size_t moe_layer_sync_bytes(void) { return moe::layer_fused_sync_bytes(); }
+size_t moe_layer_sync_bytes(void) { return moe::small_batch_sync_bytes(); }
 
 int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
               const float *bias, const void *experts, const void *shared,
@@ -372,7 +372,7 @@ int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
   LayerWs ws = carve_layer(cv, c, T);
   int32_t *idx = idx_out ? idx_out : ws.idx;
   float *w = w_out ? w_out : ws.w;
-  if (moe::layer_fused_supported(c, T)) {
+  if (moe::small_batch_supported(c, T)) {
     moe::LayerArgs a;
     a.H = c.hidden;
     a.I = c.inter;
@@ -407,14 +407,10 @@ int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
     a.n_active = ws.ffn.n_active;
     a.qh = ws.qh;
     a.dh = ws.dh;
-    a.eo = ws.expert_out;
-    a.so = ws.shared_out;
     a.ssq = ws.ssq;
     a.sync = ws.sync;
-    a.trace = (ev && ev->wg_trace) ? ev->wg_trace : nullptr;
-    a.trace_words = (ev && ev->wg_trace) ? ev->trace_words : 0;
-    moe::launch_layer_fused(a, st, ev);
-    return launched("moe_layer (fused)");
+    moe::launch_small_batch(a, st, ev);
+    return launched("moe_layer (small batch)");
   }
   if ((rc = do_route(c, T, x, w_router, bias, idx, w, ws.route, st, ev))) return rc;
   moe::launch_quant_act(x, ws.q, ws.d, (int64_t)T * c.hidden, st, ev);
