@@ -103,15 +103,21 @@ def layer_bytes(shape, T, U, bb):
     return E * H * 4 + E * 4 + (U + shape.n_shared) * bb + 2 * T * H * 4
 
 
-def gate_up_bytes(shape, T, U, h_bytes_per_elem):
-    """Algorithmic bytes of one gate/up launch: gate and up codes and row scales
-    of U + shared experts, Q8_0 activations in, h out (int8 codes + fp32 block
-    scales on the small-batch path, fp32 otherwise)."""
-    H, I, K = shape.hidden, shape.inter, shape.top_k
+def gate_up_bytes(shape, T, U, small):
+    """Algorithmic bytes of one gate/up launch.
+
+    Small-batch path (1..16 tokens): gate and up codes and row scales of the U
+    routed experts, Q8_0 of x in, Q8_0 of h out for the T*K routed pairs, and
+    the shared expert's fp32 h in / Q8_0 out (its gate/up runs beside the
+    selection).  Larger batches: the same for U + shared experts with fp32 h
+    out."""
+    H, I, K, S = shape.hidden, shape.inter, shape.top_k, shape.n_shared
     per_expert = 2 * I * H * shape.wbits // 8 + 2 * I * 4
-    pairs = T * K + T * shape.n_shared
-    return ((U + shape.n_shared) * per_expert + T * H + T * (H // 32) * 4
-            + pairs * I * h_bytes_per_elem)
+    q8 = 1 + 4 / 32  # bytes per element of a Q8_0 vector (codes + fp32 block scales)
+    x_in = T * H * q8
+    if small:
+        return U * per_expert + x_in + T * K * I * q8 + S * T * I * (4 + q8)
+    return (U + S) * per_expert + x_in + (T * K + T * S) * I * 4
 
 
 def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s):
@@ -130,7 +136,7 @@ def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s):
               topk_group=shape.topk_group, top_k=shape.top_k, scale=shape.routed_scaling,
               wbits=shape.wbits)
     done_tok, spent, steps = 0, 0.0, 0
-    while spent < budget_s and steps < 64:
+    while spent < budget_s and steps < 1024:
         x = tokens_fn(steps)
         idx, _, _ = oracle.route(x, wr, bias, shape.n_group, shape.topk_group, shape.top_k,
                                  shape.routed_scaling)
@@ -293,9 +299,9 @@ def main():
     idx_h = idx_all.cpu().numpy()
     U = float(np.mean([np.unique(idx_h[i]).size for i in range(W, W + K)]))
     step_bytes = layer_bytes(shape, T, U, bb)
-    small = "router_select" not in stage_ms  # three-kernel small-batch path
-    dom = "gate_up (expert gate/up + SwiGLU" + (" + Q8_0 of h)" if small else ")")
-    dom_bytes = gate_up_bytes(shape, T, U, 1 + 4 / 32 if small else 4)
+    small = T <= 16  # the layer's small-batch path (four kernels)
+    dom = "gate_up (routed expert gate/up + SwiGLU + Q8_0 of h)" if small else "gate_up"
+    dom_bytes = gate_up_bytes(shape, T, U, small)
     dom_sec = stage_ms["gate_up"] * 1e-3
     achieved = dom_bytes / dom_sec / 1e9
 

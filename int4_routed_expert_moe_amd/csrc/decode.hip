@@ -6,23 +6,29 @@
 // noaux_tc and routed_scaling_factor, shared expert, Q8_0 int8 activations,
 // packed int4/int2 weights with per-row scales, batch-union MoE).
 //
-//  K1 k_route_small   (E/2 workgroups) Q8_0 of a slice of x; fixed-order fp32
-//                     logits of two experts; the last workgroup to finish
-//                     (two-level count) selects every token's experts and
-//                     groups the T*K slots by expert (batch union).
-//  K2 k_gate_up_small (I/32 x slots) 32 rows of h = silu(gate x) * (up x)
-//                     for one expert slot and its tokens, written directly as
-//                     its Q8_0 block (no fp32 h round trip).
-//  K3 k_down_small    (H/8 workgroups) 8 output rows for every expert slot and
-//                     token, combined in LDS in rank order into y (+ residual);
-//                     with y_norm, the last workgroup applies the unit-gain
-//                     RMSNorm to whole rows.
-// Only the "last workgroup" steps communicate between workgroups; each costs
-// one agent-scope release per workgroup and one acquire by the last one.
-// Their counters sit in a zero-initialised workspace region that each call
-// leaves at zero.
+//  K1  k_route_small   (E workgroups) Q8_0 of a slice of x; the fixed-order
+//                      fp32 logit and sigmoid score of one expert per token.
+//  K1b k_select_small  (T + I/8 workgroups) group-limited top-k of one token
+//                      per workgroup; the rest run the shared expert's gate/up
+//                      (it needs no routing), 8 rows each, h in fp32.
+//  K2  k_gate_up_small (I/32 x routed slots) each workgroup finds its expert
+//                      slot of the batch union from the T*K selections, then
+//                      32 rows of h = silu(gate x) * (up x) for that expert and
+//                      its tokens, written directly as Q8_0 blocks; the first
+//                      slot's workgroups also quantise the shared expert's h.
+//  K3  k_down_small    (H/8 workgroups) 8 output rows for every expert slot
+//                      and token, combined in LDS in rank order into y
+//                      (+ residual); with y_norm, the last workgroup applies
+//                      the unit-gain RMSNorm to whole rows.
+// Every kernel spreads its weight bytes over all CUs: one CU streams only a
+// few tens of GB/s, so a phase confined to a few CUs is slow however small.
+// Kernel boundaries carry every dependency except the RMSNorm's "last
+// workgroup" step, whose counter sits in a zero-initialised workspace region
+// that each call leaves at zero.
 #include "common.h"
 #include "kernels.h"
+
+#include <algorithm>
 
 namespace moe {
 
@@ -30,17 +36,27 @@ namespace moe {
 #ifndef MOE_K3_SLOTS
 #define MOE_K3_SLOTS 4
 #endif
+// gate/up rows (each a gate and an up row) a K2 wave loads together: 1, 2, 4, 8
+#ifndef MOE_K2_ROWS
+#define MOE_K2_ROWS 2
+#endif
 
 namespace sbk {
 constexpr int TMAX = 16;
 constexpr int LINE = 64;  // uint32 words between counters (256 B)
-constexpr int C_RSUB = 0;   // 16 router sub-counters
-constexpr int C_ROUTE = 16;
-constexpr int C_NORM = 17;
-constexpr int C_END = 18;
+constexpr int C_NORM = 0;   // workgroups of the down kernel done (RMSNorm)
+constexpr int C_END = 1;
 constexpr int RT = 8;       // output rows per K3 workgroup (2 per wave)
 constexpr int MAXP = TMAX * 17;  // pairs: T*K routed + T shared, K <= 16
 }  // namespace sbk
+
+// Slot table (written by the last router workgroup): entry j describes
+// expert slot j -- the shared expert first, then the active routed experts
+// in ascending order -- as SLOT_W int32: expert (-1 = shared), token count,
+// TMAX pair ids (routed: slot id t*K+k; shared: T*K+t), TMAX token ids.
+// Entries past the last slot have a token count of 0.  A consumer reads its
+// entry in one round trip.
+constexpr int SLOT_W = 2 + 2 * sbk::TMAX;
 
 size_t small_batch_sync_bytes() { return (size_t)sbk::C_END * sbk::LINE * sizeof(uint32_t); }
 
@@ -107,28 +123,81 @@ __device__ __forceinline__ uint32_t q8_quad(float4 v, float *dd_out) {
   return cv(v.x) | (cv(v.y) << 8) | (cv(v.z) << 16) | (cv(v.w) << 24);
 }
 
-// ============================================================ K1: routing
+// ============================================================ K1: router
 
-struct RouteLds {
-  uint32_t word;
-  union {
-    float part[2][sbk::TMAX][128];  // chunk partials of the block's two experts
-    struct {
-      float sb[1024];               // biased scores of the token being selected
-      float s[1024];                // its unbiased scores
-      unsigned long long key[1024];  // (biased score, -index) of every expert
-      unsigned long long gkey[64];
-      unsigned long long kmask;
-      unsigned long long fkey[1024]; // finalists: K per kept group (0 = empty)
-      int fe[1024];
-      int sel[16];
-      float ssel[16];                // unbiased scores of the picks, rank order
-      int32_t idx[256];             // every token's selection, slot order
-      int32_t cnt[1024];
-      int32_t off[1025];
-      int32_t wt[8];
-    } fin;
-  } u;
+// Router workgroup e (one per expert): Q8_0 of a slice of x for the expert
+// kernels, then the fixed-order fp32 logit and the sigmoid score of expert e
+// for every token.  Thread l < H/64 of half h owns chunk l (an fma chain
+// over its 64 elements in index order) of the tokens t = h, h+2, ...
+__global__ void __launch_bounds__(256) k_route_small(LayerArgs a) {
+  __shared__ float part[sbk::TMAX][128];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int H = a.H, E = a.E, T = a.T;
+  {  // Q8_0 of a slice of x, 8 lanes per block of 32
+    const int nbx = T * (H / 32);
+    const int per = (nbx + E - 1) / E;
+    const int b0 = e * per, b1 = min(nbx, b0 + per);
+    for (int base = b0; base < b1; base += 32) {
+      const int blk = base + (tid >> 3), sub = tid & 7;
+      const bool ok = blk < b1;
+      const float4 v = ok ? reinterpret_cast<const float4 *>(a.x)[(size_t)blk * 8 + sub]
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      float dd;
+      const uint32_t packed = q8_quad(v, &dd);
+      if (ok) {
+        reinterpret_cast<uint32_t *>(a.q)[(size_t)blk * 8 + sub] = packed;
+        if (sub == 0) a.d[blk] = dd;
+      }
+    }
+  }
+  const int half = tid >> 7, l = tid & 127;
+  const int nch = H / 64;
+  if (half < T && l < nch) {
+    const float4 *w4 = reinterpret_cast<const float4 *>(a.wr + (size_t)e * H + l * 64);
+    float4 wv[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) wv[k] = w4[k];
+    for (int t = half; t < T; t += 2) {
+      const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * H + l * 64);
+      float4 xv[16];
+#pragma unroll
+      for (int k = 0; k < 16; k++) xv[k] = x4[k];
+      // keep every load of W and x ahead of the chain (one memory latency,
+      // not sixteen): nothing is scheduled across this point
+      __builtin_amdgcn_sched_barrier(0);
+      float acc = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 16; k++) {
+        acc = __builtin_fmaf(xv[k].x, wv[k].x, acc);
+        acc = __builtin_fmaf(xv[k].y, wv[k].y, acc);
+        acc = __builtin_fmaf(xv[k].z, wv[k].z, acc);
+        acc = __builtin_fmaf(xv[k].w, wv[k].w, acc);
+      }
+      part[t][l] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < T) {  // chunk partials added left to right
+    float tot = part[tid][0];
+    for (int c = 1; c < nch; c++) tot = tot + part[tid][c];
+    const float sv = 1.0f / (1.0f + exp_fixed_sb(-tot));
+    a.s[(size_t)tid * E + e] = sv;
+    a.sb[(size_t)tid * E + e] = sv + a.bias[e];
+  }
+}
+
+// ============================================================ selection of one token
+
+struct SelLds {
+  float sb[1024];                // biased scores of the token
+  float s[1024];                 // its unbiased scores
+  unsigned long long key[1024];  // (biased score, -index) of every expert
+  unsigned long long gkey[64];
+  unsigned long long kmask;
+  unsigned long long fkey[1024];  // finalists: K per kept group (0 = empty)
+  int fe[1024];
+  int sel[16];
+  float ssel[16];                 // unbiased scores of the picks, rank order
 };
 
 // running top-2 of a sequence of values (the two largest, multiset)
@@ -147,19 +216,19 @@ __device__ __forceinline__ unsigned long long rank_key(float v, int i) {
 // best n exactly when fewer than n items have a larger key, and its rank is
 // its position in the descending order; this is the same set and order as
 // picking the maximum n times with ties to the lower index.
-__device__ void select_token(const LayerArgs &a, RouteLds &sm, int t) {
+__device__ void select_token(const LayerArgs &a, SelLds &sm, int t) {
   const int E = a.E, G = a.G, gs = E / G, K = a.K;
   for (int e = threadIdx.x; e < E; e += 256) {
     const float v = a.sb[(size_t)t * E + e];
-    sm.u.fin.sb[e] = v;
-    sm.u.fin.s[e] = a.s[(size_t)t * E + e];
-    sm.u.fin.key[e] = rank_key(v, e);
+    sm.sb[e] = v;
+    sm.s[e] = a.s[(size_t)t * E + e];
+    sm.key[e] = rank_key(v, e);
   }
   __syncthreads();
   if (threadIdx.x < G) {  // group score: sum of the two largest biased scores
     const int g = threadIdx.x;
     float m1 = -INFINITY, m2 = -INFINITY;
-    const float *p = sm.u.fin.sb + g * gs;
+    const float *p = sm.sb + g * gs;
     if ((gs & 15) == 0) {  // 4 independent 16-byte LDS reads per step
       for (int e = 0; e < gs; e += 16) {
         float4 v[4];
@@ -176,31 +245,31 @@ __device__ void select_token(const LayerArgs &a, RouteLds &sm, int t) {
     } else {
       for (int e = 0; e < gs; e++) top2(p[e], m1, m2);
     }
-    sm.u.fin.gkey[g] = rank_key(m1 + m2, g);
+    sm.gkey[g] = rank_key(m1 + m2, g);
   }
   __syncthreads();
   if (threadIdx.x < 64) {  // kept groups as a bitmask (G <= 64)
     bool kept = false;
     if (threadIdx.x < G) {
-      const unsigned long long mine = sm.u.fin.gkey[threadIdx.x];
+      const unsigned long long mine = sm.gkey[threadIdx.x];
       int r = 0;
-      for (int g = 0; g < G; g++) r += sm.u.fin.gkey[g] > mine;
+      for (int g = 0; g < G; g++) r += sm.gkey[g] > mine;
       kept = r < a.TG;
     }
     const unsigned long long m = __ballot(kept);
-    if (threadIdx.x == 0) sm.u.fin.kmask = m;
+    if (threadIdx.x == 0) sm.kmask = m;
   }
   const int F = a.TG * K;  // finalist slots: K per kept group
-  for (int f = threadIdx.x; f < F; f += 256) sm.u.fin.fkey[f] = 0ull;
+  for (int f = threadIdx.x; f < F; f += 256) sm.fkey[f] = 0ull;
   __syncthreads();
   // stage A: rank within the group; a global top-K item is in its group's
   // top-K, so each kept group hands its best K to slots j*K .. j*K+K-1
-  const unsigned long long kmask = sm.u.fin.kmask;
+  const unsigned long long kmask = sm.kmask;
   for (int e = threadIdx.x; e < E; e += 256) {
     const int g = e / gs;
     if (!((kmask >> g) & 1ull)) continue;
-    const unsigned long long mine = sm.u.fin.key[e];
-    const unsigned long long *kk = sm.u.fin.key + g * gs;
+    const unsigned long long mine = sm.key[e];
+    const unsigned long long *kk = sm.key + g * gs;
     int r = 0;
     if ((gs & 15) == 0) {  // 8 independent 16-byte LDS reads per step
       for (int i = 0; i < gs; i += 16) {
@@ -215,28 +284,28 @@ __device__ void select_token(const LayerArgs &a, RouteLds &sm, int t) {
     }
     if (r < K) {
       const int j = __popcll(kmask & ((1ull << g) - 1ull));
-      sm.u.fin.fkey[j * K + r] = mine;
-      sm.u.fin.fe[j * K + r] = e;
+      sm.fkey[j * K + r] = mine;
+      sm.fe[j * K + r] = e;
     }
   }
   __syncthreads();
   // stage B: rank among the finalists = rank among all candidates
   for (int f = threadIdx.x; f < F; f += 256) {
-    const unsigned long long mine = sm.u.fin.fkey[f];
+    const unsigned long long mine = sm.fkey[f];
     if (mine == 0ull) continue;
     int r = 0;
     int i = 0;
     for (; i + 16 <= F; i += 16) {
       ulonglong2 v[8];
 #pragma unroll
-      for (int u = 0; u < 8; u++) v[u] = *reinterpret_cast<const ulonglong2 *>(sm.u.fin.fkey + i + 2 * u);
+      for (int u = 0; u < 8; u++) v[u] = *reinterpret_cast<const ulonglong2 *>(sm.fkey + i + 2 * u);
 #pragma unroll
       for (int u = 0; u < 8; u++) r += (v[u].x > mine) + (v[u].y > mine);
     }
-    for (; i < F; i++) r += sm.u.fin.fkey[i] > mine;
+    for (; i < F; i++) r += sm.fkey[i] > mine;
     if (r < K) {
-      sm.u.fin.sel[r] = sm.u.fin.fe[f];
-      sm.u.fin.ssel[r] = sm.u.fin.s[sm.u.fin.fe[f]];
+      sm.sel[r] = sm.fe[f];
+      sm.ssel[r] = sm.s[sm.fe[f]];
     }
   }
   __syncthreads();
@@ -244,7 +313,7 @@ __device__ void select_token(const LayerArgs &a, RouteLds &sm, int t) {
     float sv[16];
 #pragma unroll
     for (int k = 0; k < 16; k += 4) {  // four 16-byte reads, one round trip
-      const float4 v4 = *reinterpret_cast<const float4 *>(sm.u.fin.ssel + k);
+      const float4 v4 = *reinterpret_cast<const float4 *>(sm.ssel + k);
       sv[k] = v4.x;
       sv[k + 1] = v4.y;
       sv[k + 2] = v4.z;
@@ -253,156 +322,12 @@ __device__ void select_token(const LayerArgs &a, RouteLds &sm, int t) {
     float S = sv[0];
 #pragma unroll
     for (int k = 1; k < 16; k++) S = (k < K) ? S + sv[k] : S;
-    const int e = sm.u.fin.sel[threadIdx.x];
+    const int e = sm.sel[threadIdx.x];
     a.idx[t * K + threadIdx.x] = e;
-    a.w[t * K + threadIdx.x] = (sm.u.fin.ssel[threadIdx.x] / S) * a.scale;
-    sm.u.fin.idx[t * K + threadIdx.x] = e;
-  }
-  __syncthreads();
-}
-
-__device__ int exscan256(int v, int *wt, int *total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wt[wv] = x;
-  __syncthreads();
-  int pre = 0, all = 0;
-  for (int w = 0; w < 4; w++) {
-    pre += (w < wv) ? wt[w] : 0;
-    all += wt[w];
-  }
-  __syncthreads();
-  *total = all;
-  return pre + x - v;
-}
-
-// Select every token, then group the T*K slots (stable, by expert): counts
-// by LDS atomics, one prefix scan of (count, active) packed in one int.
-__device__ void select_and_group(const LayerArgs &a, RouteLds &sm) {
-  const int E = a.E, T = a.T, K = a.K, n = T * K;
-  for (int t = 0; t < T; t++) select_token(a, sm, t);
-  for (int e = threadIdx.x; e < E; e += 256) sm.u.fin.cnt[e] = 0;
-  __syncthreads();
-  if (threadIdx.x < n) atomicAdd(&sm.u.fin.cnt[sm.u.fin.idx[threadIdx.x]], 1);
-  __syncthreads();
-  int c[4], loc = 0;
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int e = threadIdx.x * 4 + j;
-    c[j] = e < E ? sm.u.fin.cnt[e] : 0;
-    loc += c[j] + ((c[j] > 0) << 16);  // counts <= 256, active experts <= 1024
-  }
-  int total;
-  const int pk = exscan256(loc, sm.u.fin.wt, &total);
-  int pre = pk & 0xFFFF, apre = pk >> 16;
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int e = threadIdx.x * 4 + j;
-    if (e < E) {
-      sm.u.fin.off[e] = pre;
-      a.offsets[e] = pre;
-      a.counts[e] = c[j];
-      a.active[e] = -1;
-    }
-    pre += c[j];
-  }
-  if (threadIdx.x == 0) {
-    a.offsets[E] = total & 0xFFFF;
-    a.n_active[0] = total >> 16;
-  }
-  __syncthreads();  // active[] = -1 before the compaction
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int e = threadIdx.x * 4 + j;
-    if (e < E && c[j] > 0) a.active[apre++] = e;
-  }
-  if (threadIdx.x < n) {
-    const int sl = threadIdx.x, e = sm.u.fin.idx[sl];
-    int rank = 0;
-    for (int j = 0; j < sl; j++) rank += sm.u.fin.idx[j] == e;
-    a.perm[sm.u.fin.off[e] + rank] = sl;
+    a.w[t * K + threadIdx.x] = (sm.ssel[threadIdx.x] / S) * a.scale;
   }
 }
 
-__global__ void __launch_bounds__(256) k_route_small(LayerArgs a) {
-  __shared__ RouteLds sm;
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const int H = a.H, E = a.E, T = a.T;
-  // 1. Q8_0 of a slice of x, 8 lanes per block of 32
-  {
-    const int nbx = T * (H / 32);
-    const int per = (nbx + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int b0 = r * per, b1 = min(nbx, b0 + per);
-    for (int base = b0; base < b1; base += 32) {
-      const int blk = base + (tid >> 3), sub = tid & 7;
-      const bool ok = blk < b1;
-      const float4 v = ok ? reinterpret_cast<const float4 *>(a.x)[(size_t)blk * 8 + sub]
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-      float dd;
-      const uint32_t packed = q8_quad(v, &dd);
-      if (ok) {
-        reinterpret_cast<uint32_t *>(a.q)[(size_t)blk * 8 + sub] = packed;
-        if (sub == 0) a.d[blk] = dd;
-      }
-    }
-  }
-  // 2. logits of experts 2r and 2r+1; thread l < H/64 of each half owns the
-  //    chunk l (an fma chain over its 64 elements in index order)
-  const int half = tid >> 7, l = tid & 127;
-  const int e = 2 * r + half;
-  const int nch = H / 64;
-  if (e < E && l < nch) {
-    const float4 *w4 = reinterpret_cast<const float4 *>(a.wr + (size_t)e * H + l * 64);
-    float4 wv[16];
-#pragma unroll
-    for (int k = 0; k < 16; k++) wv[k] = w4[k];
-    for (int t = 0; t < T; t++) {
-      const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * H + l * 64);
-      float4 xv[16];
-#pragma unroll
-      for (int k = 0; k < 16; k++) xv[k] = x4[k];
-      // keep every load of W and x ahead of the chain (one memory latency,
-      // not sixteen): nothing is scheduled across this point
-      __builtin_amdgcn_sched_barrier(0);
-      float acc = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 16; k++) {
-        acc = __builtin_fmaf(xv[k].x, wv[k].x, acc);
-        acc = __builtin_fmaf(xv[k].y, wv[k].y, acc);
-        acc = __builtin_fmaf(xv[k].z, wv[k].z, acc);
-        acc = __builtin_fmaf(xv[k].w, wv[k].w, acc);
-      }
-      sm.u.part[half][t][l] = acc;
-    }
-  }
-  __syncthreads();
-  if (e < E && l < T) {  // chunk partials added left to right
-    float tot = sm.u.part[half][l][0];
-    for (int c = 1; c < nch; c++) tot = tot + sm.u.part[half][l][c];
-    const float sv = 1.0f / (1.0f + exp_fixed_sb(-tot));
-    a.s[(size_t)l * E + e] = sv;
-    a.sb[(size_t)l * E + e] = sv + a.bias[e];
-  }
-  // 3. two-level count (same-address atomics serialise); the last block
-  //    selects and groups, then clears the counters it alone still uses
-  const int nblk = gridDim.x;
-  const int sub = r % 16;
-  const uint32_t in_sub = (uint32_t)((nblk - 1 - sub) / 16 + 1);
-  uint32_t old = block_count(sctr(a, sbk::C_RSUB + sub), &sm.word);
-  if (old != in_sub - 1) return;
-  const uint32_t subs = (uint32_t)(nblk < 16 ? nblk : 16);
-  old = block_count(sctr(a, sbk::C_ROUTE), &sm.word);
-  if (old != subs - 1) return;
-  block_acquire();
-  select_and_group(a, sm);
-  if (tid < 16) *sctr(a, sbk::C_RSUB + tid) = 0u;
-  if (tid == 0) *sctr(a, sbk::C_ROUTE) = 0u;
-}
 
 // ============================================================ operands
 
@@ -483,82 +408,29 @@ __device__ __forceinline__ float piece_dot<2>(const uint4 w, const Act<2> &a) {
   return fmaf((float)x, a.da, (float)y * a.db);
 }
 
-// Expert slot j: 0 .. n_shared-1 the shared expert, then the active routed
-// experts in ascending order.  Indices read from device memory are clamped.
-struct Slot {
-  const uint8_t *blob;
-  int n_tok;
-  bool shared;
-  const int32_t *list;
-};
-
-__device__ __forceinline__ Slot slot_of(const LayerArgs &a, int slot) {
-  Slot s;
-  if (slot < a.n_shared) {
-    s.blob = a.shared;
-    s.n_tok = a.T;
-    s.shared = true;
-    s.list = nullptr;
-  } else {
-    const int n_slots = a.T * a.K;
-    int e = a.active[slot - a.n_shared];
-    e = min(max(e, 0), a.E - 1);
-    const int lo = min(max(a.offsets[e], 0), n_slots);
-    const int hi = min(max(a.offsets[e + 1], lo), n_slots);
-    s.blob = a.experts + (size_t)e * a.blob_bytes;
-    s.n_tok = hi - lo;
-    s.shared = false;
-    s.list = a.perm + lo;
-  }
-  return s;
-}
-
-// token index and pair index (slot id t*K+k, or T*K + t for the shared expert)
-__device__ __forceinline__ void tok_pair(const LayerArgs &a, const Slot &s, int i, int &tok,
-                                         int &pair) {
-  if (s.shared) {
-    tok = i;
-    pair = a.T * a.K + i;
-  } else {
-    const int sl = min(max(s.list[i], 0), a.T * a.K - 1);
-    tok = sl / a.K;
-    pair = sl;
-  }
-}
-
-__device__ __forceinline__ int n_active_clamped(const LayerArgs &a) {
-  return min(max(a.n_active[0], 0), a.n_slots_ub - a.n_shared);
-}
-
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// ============================================================ K2: gate/up
-
-// Workgroup (blk, slot): rows 32 blk .. 32 blk + 31 of h for the slot's
-// tokens.  Wave wv streams rows 8wv .. 8wv+7 as four batches of two rows (a
-// gate and an up row each); registers stay low enough for every workgroup
-// of a decode step to be resident at once, which keeps ~27 MB in flight.  h goes to LDS; the 32 values of each token become one Q8_0 block.
-template <int WB, int TT, int NPL>
-__global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
-  __shared__ float hb[TT][32];
-  const int slot = blockIdx.y, blk = blockIdx.x;
-  if (slot >= a.n_shared && slot - a.n_shared >= n_active_clamped(a)) return;
+// 32 rows of h (rows 32 blk ..) for one expert and n_tok tokens.  Wave wv
+// streams rows 8wv .. 8wv+7 in batches of RB rows (a gate and an up row
+// each).  Activations of token i: Q8_0 codes/scales at qrow(i)/drow(i).
+// h goes to LDS; each token's 32 values become one Q8_0 block of q_h.
+template <int WB, int TT, int NPL, int RB, class QRow, class DRow>
+__device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t *blob, int blk,
+                             int n_tok, const int *pairs, QRow qrow, DRow drow) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, I = a.I;
   const int npieces = H / (128 / WB);
   const size_t row_b = (size_t)H * WB / 8;
-  const Slot s = slot_of(a, slot);
-  const uint8_t *gate = s.blob;
-  const uint8_t *up = s.blob + (size_t)I * row_b;
-  const float *scales = reinterpret_cast<const float *>(s.blob + 3 * (size_t)I * row_b);
+  const uint8_t *gate = blob;
+  const uint8_t *up = blob + (size_t)I * row_b;
+  const float *scales = reinterpret_cast<const float *>(blob + 3 * (size_t)I * row_b);
   const int rbase = blk * 32 + wv * 8;
-
-  for (int c0 = 0; c0 < s.n_tok; c0 += TT) {
-    uint4 wb[2][2][NPL];  // [row of batch][gate, up][piece]
+  for (int c0 = 0; c0 < n_tok; c0 += TT) {
+    uint4 wb[RB][2][NPL];  // [row of batch][gate, up][piece]
     auto load_batch = [&](int bt) {
 #pragma unroll
-      for (int rr = 0; rr < 2; rr++) {
-        const int r = rbase + bt * 2 + rr;
+      for (int rr = 0; rr < RB; rr++) {
+        const int r = rbase + bt * RB + rr;
 #pragma unroll
         for (int i = 0; i < NPL; i++) {
           const int p = lane + 64 * i;
@@ -572,25 +444,22 @@ __global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
     };
     load_batch(0);
     Act<WB> act[NPL][TT];
-    int pair[TT];
 #pragma unroll
     for (int t = 0; t < TT; t++) {
-      int tok = 0;
-      pair[t] = -1;
-      if (c0 + t < s.n_tok) tok_pair(a, s, c0 + t, tok, pair[t]);
+      const bool live = c0 + t < n_tok;
 #pragma unroll
       for (int i = 0; i < NPL; i++) {
         const int p = lane + 64 * i;
-        load_act<WB>(a.q + (size_t)tok * H, a.d + (size_t)tok * (H / 32), p,
-                     pair[t] >= 0 && p < npieces, act[i][t]);
+        load_act<WB>(qrow(live ? c0 + t : c0), drow(live ? c0 + t : c0), p, live && p < npieces,
+                     act[i][t]);
       }
     }
 #pragma unroll
-    for (int bt = 0; bt < 4; bt++) {
+    for (int bt = 0; bt < 8 / RB; bt++) {
       if (bt > 0) load_batch(bt);
 #pragma unroll
-      for (int rr = 0; rr < 2; rr++) {
-        const int r = rbase + bt * 2 + rr;
+      for (int rr = 0; rr < RB; rr++) {
+        const int r = rbase + bt * RB + rr;
         float g[TT], u[TT];
 #pragma unroll
         for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
@@ -607,7 +476,7 @@ __global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
         for (int t = 0; t < TT; t++) {
           const float gv = sg * wave_sum(g[t]);
           const float uv = su * wave_sum(u[t]);
-          if (lane == 0) hb[t][wv * 8 + bt * 2 + rr] = silu(gv) * uv;
+          if (lane == 0) hb[t][wv * 8 + bt * RB + rr] = silu(gv) * uv;
         }
       }
     }
@@ -618,18 +487,182 @@ __global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
                                    hb[t][4 * j + 3]);
       float dd;
       const uint32_t packed = q8_quad(v, &dd);
-      if (pair[t] >= 0) {
-        reinterpret_cast<uint32_t *>(a.qh + (size_t)pair[t] * I + blk * 32)[j] = packed;
-        if (j == 0) a.dh[(size_t)pair[t] * (I / 32) + blk] = dd;
+      if (c0 + t < n_tok) {
+        const int pair = min(max(pairs[c0 + t], 0), a.T * (a.K + a.n_shared) - 1);
+        reinterpret_cast<uint32_t *>(a.qh + (size_t)pair * I + blk * 32)[j] = packed;
+        if (j == 0) a.dh[(size_t)pair * (I / 32) + blk] = dd;
       }
     }
     __syncthreads();
   }
 }
 
+// ============================================================ K1b: selection + shared gate/up
+
+// The shared expert's gate/up (it needs no routing), in workgroups of 8
+// rows so that its bytes spread over every CU: wave wv holds rows 8 blk +
+// 2 wv, +1 (a gate and an up row each) and runs every token through them;
+// h goes out in fp32 (its Q8_0 blocks span four workgroups; the gate/up
+// kernel quantises them).
+template <int WB, int TT, int NPL>
+__device__ void shared_rows_block(const LayerArgs &a, int blk) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int H = a.H, I = a.I, T = a.T;
+  const int npieces = H / (128 / WB);
+  const size_t row_b = (size_t)H * WB / 8;
+  const uint8_t *gate = a.shared;
+  const uint8_t *up = a.shared + (size_t)I * row_b;
+  const float *scales = reinterpret_cast<const float *>(a.shared + 3 * (size_t)I * row_b);
+  const int r0 = blk * 8 + wv * 2;
+  uint4 wb[2][2][NPL];
+#pragma unroll
+  for (int rr = 0; rr < 2; rr++) {
+#pragma unroll
+    for (int i = 0; i < NPL; i++) {
+      const int p = lane + 64 * i;
+      const bool ok = p < npieces;
+      wb[rr][0][i] = ok ? reinterpret_cast<const uint4 *>(gate + (size_t)(r0 + rr) * row_b)[p]
+                        : make_uint4(0, 0, 0, 0);
+      wb[rr][1][i] = ok ? reinterpret_cast<const uint4 *>(up + (size_t)(r0 + rr) * row_b)[p]
+                        : make_uint4(0, 0, 0, 0);
+    }
+  }
+  const float sg0 = scales[r0], sg1 = scales[r0 + 1];
+  const float su0 = scales[I + r0], su1 = scales[I + r0 + 1];
+  for (int c0 = 0; c0 < T; c0 += TT) {
+    Act<WB> act[NPL][TT];
+#pragma unroll
+    for (int t = 0; t < TT; t++) {
+      const bool live = c0 + t < T;
+      const int tok = live ? c0 + t : c0;
+#pragma unroll
+      for (int i = 0; i < NPL; i++) {
+        const int p = lane + 64 * i;
+        load_act<WB>(a.q + (size_t)tok * H, a.d + (size_t)tok * (H / 32), p, live && p < npieces,
+                     act[i][t]);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 2; rr++) {
+      float g[TT], u[TT];
+#pragma unroll
+      for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NPL; i++) {
+#pragma unroll
+        for (int t = 0; t < TT; t++) {
+          g[t] += piece_dot<WB>(wb[rr][0][i], act[i][t]);
+          u[t] += piece_dot<WB>(wb[rr][1][i], act[i][t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TT; t++) {
+        const float gv = (rr ? sg1 : sg0) * wave_sum(g[t]);
+        const float uv = (rr ? su1 : su0) * wave_sum(u[t]);
+        if (lane == 0 && c0 + t < T) a.hs[(size_t)(c0 + t) * I + r0 + rr] = silu(gv) * uv;
+      }
+    }
+  }
+}
+
+// Workgroups [0, T): selection of token blockIdx.x; the rest: shared rows.
+template <int WB, int TT, int NPL>
+__global__ void __launch_bounds__(256) k_select_small(LayerArgs a) {
+  __shared__ SelLds sm;
+  if ((int)blockIdx.x >= a.T) {
+    shared_rows_block<WB, TT, NPL>(a, blockIdx.x - a.T);
+    return;
+  }
+  select_token(a, sm, blockIdx.x);
+}
+
+// ============================================================ K2: gate/up
+
+// Expert slot j of the batch union (the j-th smallest distinct expert in
+// idx) and its pairs in slot order, built in LDS by every K2 workgroup from
+// the T*K selections: bitmap of chosen experts, an expert's slot = chosen
+// experts below it, pairs ranked by ballots.  ent: expert (-1 = none), count,
+// TMAX pair ids, TMAX token ids.
+__device__ void union_slot(const LayerArgs &a, int j, int *ent) {
+  __shared__ int sel[256];
+  __shared__ uint32_t bits[32];
+  __shared__ int wcnt[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = a.T * a.K, E = a.E;
+  if (tid < 32) bits[tid] = 0u;
+  if (tid == 0) ent[0] = -1;
+  int e = -1;
+  if (tid < n) e = min(max(a.idx[tid], 0), E - 1);
+  __syncthreads();
+  if (tid < n) atomicOr(&bits[e >> 5], 1u << (e & 31));
+  __syncthreads();
+  if (tid < n) {
+    int r = __popc(bits[e >> 5] & ((1u << (e & 31)) - 1u));
+    for (int w = 0; w < (e >> 5); w++) r += __popc(bits[w]);
+    if (r == j) ent[0] = e;  // every holder of that expert writes the same value
+  }
+  __syncthreads();
+  const int ej = ent[0];
+  const bool m = tid < n && e == ej && ej >= 0;
+  const unsigned long long b = __ballot(m);
+  if (lane == 0) wcnt[wv] = __popcll(b);
+  __syncthreads();
+  int rank = __popcll(b & ((1ull << lane) - 1ull));
+  for (int w = 0; w < wv; w++) rank += wcnt[w];
+  if (m && rank < sbk::TMAX) {  // a token picks an expert at most once
+    ent[2 + rank] = tid;
+    ent[2 + sbk::TMAX + rank] = tid / a.K;
+  }
+  if (tid == 0) ent[1] = ej >= 0 ? wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3] : 0;
+  __syncthreads();
+}
+
+// Block (blk, j): rows 32 blk .. 32 blk + 31 of h for routed slot j.  The
+// workgroups with blk == 0 also publish their slot's table entry (and the
+// shared expert's) for the down kernel.
+template <int WB, int TT, int NPL>
+__global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
+  __shared__ float hb[TT][32];
+  __shared__ int ent[SLOT_W];
+  const int j = blockIdx.y, blk = blockIdx.x;
+  if (j == 0 && a.n_shared && (int)threadIdx.x < a.T * 8) {
+    // Q8_0 of the shared expert's h, block blk of every token
+    const int t = threadIdx.x >> 3, q = threadIdx.x & 7;
+    const float4 v = reinterpret_cast<const float4 *>(a.hs + (size_t)t * a.I + blk * 32)[q];
+    float dd;
+    const uint32_t packed = q8_quad(v, &dd);
+    const int pair = a.T * a.K + t;
+    reinterpret_cast<uint32_t *>(a.qh + (size_t)pair * a.I + blk * 32)[q] = packed;
+    if (q == 0) a.dh[(size_t)pair * (a.I / 32) + blk] = dd;
+  }
+  union_slot(a, j, ent);
+  const int n_tok = min(max(ent[1], 0), a.T);
+  if (blk == 0) {
+    int32_t *dst = a.slots + (size_t)(a.n_shared + j) * SLOT_W;
+    if (threadIdx.x < SLOT_W) dst[threadIdx.x] = ent[threadIdx.x];
+    if (j == 0 && a.n_shared && threadIdx.x < a.T) {  // the shared expert takes every token
+      if (threadIdx.x == 0) {
+        a.slots[0] = -1;
+        a.slots[1] = a.T;
+      }
+      a.slots[2 + threadIdx.x] = a.T * a.K + threadIdx.x;
+      a.slots[2 + sbk::TMAX + threadIdx.x] = threadIdx.x;
+    }
+  }
+  if (n_tok == 0) return;
+  const int e = min(max(ent[0], 0), a.E - 1);
+  const int *pairs = ent + 2, *toks = ent + 2 + sbk::TMAX;
+  gate_up_rows<WB, TT, NPL, MOE_K2_ROWS>(
+      a, hb, a.experts + (size_t)e * a.blob_bytes, blk, n_tok, pairs,
+      [&](int i) { return (const int8_t *)(a.q + (size_t)min(max(toks[i], 0), a.T - 1) * a.H); },
+      [&](int i) {
+        return (const float *)(a.d + (size_t)min(max(toks[i], 0), a.T - 1) * (a.H / 32));
+      });
+}
+
 // ============================================================ K3: down + combine
 
-// Workgroup `tile`: output rows 8 tile .. 8 tile + 7 of every expert slot for
+// Block `tile`: output rows 8 tile .. 8 tile + 7 of every expert slot for
 // every token (wave wv: rows 2wv, 2wv+1), slots taken SB at a time with all
 // their weight rows loaded up front; partial outputs go to LDS by pair, and
 // the tile is combined in rank order:
@@ -639,28 +672,31 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   __shared__ float part[sbk::MAXP][sbk::RT];
   __shared__ float red[sbk::TMAX];
   __shared__ uint32_t word;
+  extern __shared__ __align__(16) int tab[];  // [n_slots_ub][SLOT_W]
   const int tile = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, I = a.I, T = a.T, K = a.K;
   const int npieces = I / (128 / WB);
   const size_t down_off = 2 * (size_t)I * ((size_t)H * WB / 8);
   const size_t row_b = (size_t)I * WB / 8;
-  const int n_slots = a.n_shared + n_active_clamped(a);
   const int j0 = tile * sbk::RT + wv * 2;
+  for (int i = threadIdx.x; i < a.n_slots_ub * SLOT_W; i += 256) tab[i] = a.slots[i];
+  __syncthreads();
+  int n_slots = 0;
+  while (n_slots < a.n_slots_ub && tab[n_slots * SLOT_W + 1] > 0) n_slots++;
 
   for (int s0 = 0; s0 < n_slots; s0 += SB) {
     uint4 wd[SB][2][NPL];
     float sd[SB][2];
-    Slot sl[SB];
 #pragma unroll
     for (int b = 0; b < SB; b++) {
       const bool ok_s = s0 + b < n_slots;
-      sl[b] = slot_of(a, ok_s ? s0 + b : 0);
-      if (!ok_s) sl[b].n_tok = 0;
-      const uint8_t *down = sl[b].blob + down_off;
+      const int ex = ok_s ? tab[(s0 + b) * SLOT_W] : -1;
+      const uint8_t *blob =
+          ex < 0 ? a.shared : a.experts + (size_t)min(ex, a.E - 1) * a.blob_bytes;
+      const uint8_t *down = blob + down_off;
       const float *sdp =
-          reinterpret_cast<const float *>(sl[b].blob + 3 * (size_t)I * ((size_t)H * WB / 8)) +
-          2 * I;
+          reinterpret_cast<const float *>(blob + 3 * (size_t)I * ((size_t)H * WB / 8)) + 2 * I;
 #pragma unroll
       for (int rr = 0; rr < 2; rr++) {
 #pragma unroll
@@ -675,14 +711,14 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
     }
 #pragma unroll
     for (int b = 0; b < SB; b++) {
-      for (int c0 = 0; c0 < sl[b].n_tok; c0 += TT) {
+      const int n_tok = (s0 + b < n_slots) ? min(tab[(s0 + b) * SLOT_W + 1], T) : 0;
+      const int *prs = tab + (s0 + b) * SLOT_W + 2;
+      for (int c0 = 0; c0 < n_tok; c0 += TT) {
         Act<WB> act[NPL][TT];
         int pair[TT];
 #pragma unroll
         for (int t = 0; t < TT; t++) {
-          int tok = 0;
-          pair[t] = -1;
-          if (c0 + t < sl[b].n_tok) tok_pair(a, sl[b], c0 + t, tok, pair[t]);
+          pair[t] = (c0 + t < n_tok) ? min(max(prs[c0 + t], 0), T * (K + a.n_shared) - 1) : -1;
           const int pp = pair[t] >= 0 ? pair[t] : 0;
 #pragma unroll
           for (int i = 0; i < NPL; i++) {
@@ -754,6 +790,10 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
 
 // ============================================================ launch
 
+size_t small_batch_slot_ints(int T, int K, int n_shared) {
+  return (size_t)(n_shared + T * K) * SLOT_W;
+}
+
 bool small_batch_supported(const moe_cfg &c, int T) {
   if (T < 1 || T > sbk::TMAX) return false;
   if (T * c.top_k > 256) return false;
@@ -764,12 +804,14 @@ bool small_batch_supported(const moe_cfg &c, int T) {
 
 template <int WB, int TT, int NPG, int NPD>
 static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
-  launch_k(k_route_small, dim3((a.E + 1) / 2), dim3(256), 0, st,
-           stage_ev(ev, MOE_STAGE_ROUTER_SCORES), a);
-  launch_k(k_gate_up_small<WB, TT, NPG>, dim3(a.I / 32, a.n_slots_ub), dim3(256), 0, st,
-           stage_ev(ev, MOE_STAGE_GATE_UP), a);
-  launch_k(k_down_small<WB, TT, NPD, MOE_K3_SLOTS>, dim3(a.H / sbk::RT), dim3(256), 0, st,
-           stage_ev(ev, MOE_STAGE_DOWN), a);
+  const int n_sh = a.n_shared ? a.I / 8 : 0;
+  launch_k(k_route_small, dim3(a.E), dim3(256), 0, st, stage_ev(ev, MOE_STAGE_ROUTER_SCORES), a);
+  launch_k(k_select_small<WB, TT, NPG>, dim3(a.T + n_sh), dim3(256), 0, st,
+           stage_ev(ev, MOE_STAGE_ROUTER_SELECT), a);
+  launch_k(k_gate_up_small<WB, TT, NPG>, dim3(a.I / 32, a.n_slots_ub - a.n_shared), dim3(256), 0,
+           st, stage_ev(ev, MOE_STAGE_GATE_UP), a);
+  launch_k(k_down_small<WB, TT, NPD, MOE_K3_SLOTS>, dim3(a.H / sbk::RT), dim3(256),
+           (uint32_t)(a.n_slots_ub * SLOT_W * sizeof(int)), st, stage_ev(ev, MOE_STAGE_DOWN), a);
 }
 
 template <int WB, int TT>

@@ -77,7 +77,8 @@ struct LayerArgs {
   float *s, *sb;                 // [T][E] router scores
   int8_t *q;                     // [T][H] Q8_0 of x
   float *d;                      // [T][H/32]
-  int32_t *counts, *offsets, *perm, *active, *n_active;
+  int32_t *slots;                // [n_slots_ub][2 + 2*16] slot table
+  float *hs;                     // [T][I] shared expert's h (fp32)
   int8_t *qh;                    // [P][I] Q8_0 of h
   float *dh;                     // [P][I/32]
   float *ssq;                    // [T][H/8] partial sums of squares
@@ -85,6 +86,7 @@ struct LayerArgs {
   int n_slots_ub;
 };
 size_t small_batch_sync_bytes();
+size_t small_batch_slot_ints(int T, int K, int n_shared);
 bool small_batch_supported(const moe_cfg &c, int T);
 void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev);
 

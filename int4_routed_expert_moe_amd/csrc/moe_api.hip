@@ -117,6 +117,8 @@ FfnWs carve_ffn(Carve &cv, const moe_cfg &c, int T) {
 struct LayerWs {
   uint32_t *sync;  // first in the workspace: counters of the fused kernel
   float *ssq;
+  int32_t *slots;
+  float *hs;
   RouteWs route;
   int32_t *idx;
   float *w;
@@ -131,6 +133,8 @@ LayerWs carve_layer(Carve &cv, const moe_cfg &c, int T) {
   LayerWs l;
   l.sync = cv.take<uint32_t>(moe::small_batch_sync_bytes() / sizeof(uint32_t));
   l.ssq = cv.take<float>((size_t)T * (c.hidden / 8));
+  l.slots = cv.take<int32_t>(moe::small_batch_slot_ints(T, c.top_k, c.n_shared));
+  l.hs = cv.take<float>((size_t)T * c.inter * c.n_shared);
   l.route = carve_route(cv, c, T);
   l.idx = cv.take<int32_t>((size_t)T * c.top_k);
   l.w = cv.take<float>((size_t)T * c.top_k);
@@ -400,11 +404,8 @@ int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
     a.sb = ws.route.sb;
     a.q = ws.q;
     a.d = ws.d;
-    a.counts = ws.ffn.counts;
-    a.offsets = ws.ffn.offsets;
-    a.perm = ws.ffn.perm;
-    a.active = ws.ffn.active;
-    a.n_active = ws.ffn.n_active;
+    a.slots = ws.slots;
+    a.hs = ws.hs;
     a.qh = ws.qh;
     a.dh = ws.dh;
     a.ssq = ws.ssq;
