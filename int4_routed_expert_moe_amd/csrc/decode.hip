@@ -34,7 +34,7 @@ namespace moe {
 
 // expert slots whose down rows a K3 wave loads together (rows in flight)
 #ifndef MOE_K3_SLOTS
-#define MOE_K3_SLOTS 4
+#define MOE_K3_SLOTS 2
 #endif
 // gate/up rows (each a gate and an up row) a K2 wave loads together: 1, 2, 4, 8
 #ifndef MOE_K2_ROWS
@@ -412,8 +412,9 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 
 // 32 rows of h (rows 32 blk ..) for one expert and n_tok tokens.  Wave wv
 // streams rows 8wv .. 8wv+7 in batches of RB rows (a gate and an up row
-// each).  Activations of token i: Q8_0 codes/scales at qrow(i)/drow(i).
-// h goes to LDS; each token's 32 values become one Q8_0 block of q_h.
+// each), double-buffered.  Activations of token i: Q8_0 codes/scales at
+// qrow(i)/drow(i).  h goes to LDS; each token's 32 values become one Q8_0
+// block of q_h.
 template <int WB, int TT, int NPL, int RB, class QRow, class DRow>
 __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t *blob, int blk,
                              int n_tok, const int *pairs, QRow qrow, DRow drow) {
@@ -425,9 +426,13 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
   const uint8_t *up = blob + (size_t)I * row_b;
   const float *scales = reinterpret_cast<const float *>(blob + 3 * (size_t)I * row_b);
   const int rbase = blk * 32 + wv * 8;
+  // row scales of the wave's 8 rows: lane l < 8 gate row l, 8 <= l < 16 up row l-8
+  const float sc = lane < 16 ? scales[(lane < 8 ? 0 : I) + rbase + (lane & 7)] : 0.0f;
+  constexpr int NB = 8 / RB;
   for (int c0 = 0; c0 < n_tok; c0 += TT) {
-    uint4 wb[RB][2][NPL];  // [row of batch][gate, up][piece]
-    auto load_batch = [&](int bt) {
+    // two buffers: batch bt+1 is in flight while batch bt is computed
+    uint4 wb[2][RB][2][NPL];  // [buffer][row of batch][gate, up][piece]
+    auto load_batch = [&](uint4 (&dst)[RB][2][NPL], int bt) {
 #pragma unroll
       for (int rr = 0; rr < RB; rr++) {
         const int r = rbase + bt * RB + rr;
@@ -435,14 +440,14 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
         for (int i = 0; i < NPL; i++) {
           const int p = lane + 64 * i;
           const bool ok = p < npieces;
-          wb[rr][0][i] = ok ? reinterpret_cast<const uint4 *>(gate + (size_t)r * row_b)[p]
-                            : make_uint4(0, 0, 0, 0);
-          wb[rr][1][i] = ok ? reinterpret_cast<const uint4 *>(up + (size_t)r * row_b)[p]
-                            : make_uint4(0, 0, 0, 0);
+          dst[rr][0][i] = ok ? reinterpret_cast<const uint4 *>(gate + (size_t)r * row_b)[p]
+                             : make_uint4(0, 0, 0, 0);
+          dst[rr][1][i] = ok ? reinterpret_cast<const uint4 *>(up + (size_t)r * row_b)[p]
+                             : make_uint4(0, 0, 0, 0);
         }
       }
     };
-    load_batch(0);
+    load_batch(wb[0], 0);
     Act<WB> act[NPL][TT];
 #pragma unroll
     for (int t = 0; t < TT; t++) {
@@ -455,11 +460,11 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
       }
     }
 #pragma unroll
-    for (int bt = 0; bt < 8 / RB; bt++) {
-      if (bt > 0) load_batch(bt);
+    for (int bt = 0; bt < NB; bt++) {
+      if (bt + 1 < NB) load_batch(wb[(bt + 1) & 1], bt + 1);
 #pragma unroll
       for (int rr = 0; rr < RB; rr++) {
-        const int r = rbase + bt * RB + rr;
+        const int rl = bt * RB + rr;  // row within the wave's 8
         float g[TT], u[TT];
 #pragma unroll
         for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
@@ -467,16 +472,17 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
         for (int i = 0; i < NPL; i++) {
 #pragma unroll
           for (int t = 0; t < TT; t++) {
-            g[t] += piece_dot<WB>(wb[rr][0][i], act[i][t]);
-            u[t] += piece_dot<WB>(wb[rr][1][i], act[i][t]);
+            g[t] += piece_dot<WB>(wb[bt & 1][rr][0][i], act[i][t]);
+            u[t] += piece_dot<WB>(wb[bt & 1][rr][1][i], act[i][t]);
           }
         }
-        const float sg = scales[r], su = scales[I + r];
+        const float sg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), rl));
+        const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), 8 + rl));
 #pragma unroll
         for (int t = 0; t < TT; t++) {
           const float gv = sg * wave_sum(g[t]);
           const float uv = su * wave_sum(u[t]);
-          if (lane == 0) hb[t][wv * 8 + bt * RB + rr] = silu(gv) * uv;
+          if (lane == 0) hb[t][wv * 8 + rl] = silu(gv) * uv;
         }
       }
     }
@@ -652,7 +658,7 @@ __global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
   if (n_tok == 0) return;
   const int e = min(max(ent[0], 0), a.E - 1);
   const int *pairs = ent + 2, *toks = ent + 2 + sbk::TMAX;
-  gate_up_rows<WB, TT, NPL, MOE_K2_ROWS>(
+  gate_up_rows<WB, TT, NPL, (TT == 1 ? MOE_K2_ROWS : 1)>(
       a, hb, a.experts + (size_t)e * a.blob_bytes, blk, n_tok, pairs,
       [&](int i) { return (const int8_t *)(a.q + (size_t)min(max(toks[i], 0), a.T - 1) * a.H); },
       [&](int i) {
@@ -662,36 +668,105 @@ __global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
 
 // ============================================================ K3: down + combine
 
+// Sum over each row of 16 lanes (every lane of the row gets it).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x124>(v);  // row_ror:4
+  v += dpp_f<0x128>(v);  // row_ror:8
+  return v;
+}
+
+constexpr int TAB_W = 2 + sbk::TMAX;  // expert, count, pairs: what the down kernel reads
+
+// Activations of pairs prs[c0 .. c0+TT) (pair ids clamped, -1 past n_tok)
+// for the pieces qb + pl + 16 i of a quarter of nq pieces.
+template <int WB, int TT, int NPQ>
+__device__ __forceinline__ void down_act(const LayerArgs &a, const int *prs, int n_tok, int c0,
+                                         int P, int qb, int nq, int pl, Act<WB> (&act)[NPQ][TT],
+                                         int (&pair)[TT]) {
+  const int I = a.I;
+#pragma unroll
+  for (int t = 0; t < TT; t++) {
+    pair[t] = (c0 + t < n_tok) ? min(max(prs[c0 + t], 0), P - 1) : -1;
+    const int pp = pair[t] >= 0 ? pair[t] : 0;
+#pragma unroll
+    for (int i = 0; i < NPQ; i++) {
+      const int q = pl + 16 * i;
+      load_act<WB>(a.qh + (size_t)pp * I, a.dh + (size_t)pp * (I / 32), qb + q,
+                   pair[t] >= 0 && q < nq, act[i][t]);
+    }
+  }
+}
+
+// Two rows (l/16, l/16 + 4) of one slot for TT pairs: quarter partials into
+// part[wv][pair][row].
+template <int WB, int TT, int NPQ>
+__device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, int pl,
+                                          const uint4 (&w)[2][NPQ], const float (&sd)[2],
+                                          const Act<WB> (&act)[NPQ][TT], const int (&pair)[TT]) {
+#pragma unroll
+  for (int rr = 0; rr < 2; rr++) {
+    float acc[TT];
+#pragma unroll
+    for (int t = 0; t < TT; t++) acc[t] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NPQ; i++) {
+#pragma unroll
+      for (int t = 0; t < TT; t++) acc[t] += piece_dot<WB>(w[rr][i], act[i][t]);
+    }
+#pragma unroll
+    for (int t = 0; t < TT; t++) {
+      const float yv = sd[rr] * row16_sum(acc[t]);
+      if (pl == 0 && pair[t] >= 0) part[((size_t)wv * P + pair[t]) * sbk::RT + rl + 4 * rr] = yv;
+    }
+  }
+}
+
 // Block `tile`: output rows 8 tile .. 8 tile + 7 of every expert slot for
-// every token (wave wv: rows 2wv, 2wv+1), slots taken SB at a time with all
-// their weight rows loaded up front; partial outputs go to LDS by pair, and
-// the tile is combined in rank order:
+// every token.  Wave wv covers all 8 rows over quarter wv of the I
+// dimension (pieces [wv n/4, (wv+1) n/4) of the row's n): lane l takes rows
+// l/16 and l/16 + 4 and the pieces l%16 (+16 i) of the quarter, so the 4 lane rows of a wave share each activation
+// piece (one cache-line request for all four).  Rows are reduced over 16
+// lanes; the 4 quarters land in LDS and are added in quarter order in the
+// combine, which runs in rank order:
 //   y[t] = residual[t] + shared[t] + sum_k w[t,k] * expert_k[t]
-template <int WB, int TT, int NPL, int SB>
+template <int WB, int TT, int NPQ, int SB>
 __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
-  __shared__ float part[sbk::MAXP][sbk::RT];
+  extern __shared__ __align__(16) uint8_t dyn[];
   __shared__ float red[sbk::TMAX];
+  __shared__ float wsh[256];
   __shared__ uint32_t word;
-  extern __shared__ __align__(16) int tab[];  // [n_slots_ub][SLOT_W]
-  const int tile = blockIdx.x;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int tile = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I, T = a.T, K = a.K;
+  const int P = T * (K + a.n_shared);  // pairs
+  float *part = reinterpret_cast<float *>(dyn);                          // [4][P][RT]
+  int *tab = reinterpret_cast<int *>(dyn + (size_t)4 * P * sbk::RT * 4);  // [slots][TAB_W]
   const int npieces = I / (128 / WB);
-  const size_t down_off = 2 * (size_t)I * ((size_t)H * WB / 8);
+  const int qb = wv * npieces / 4, nq = (wv + 1) * npieces / 4 - qb;  // this wave's quarter
   const size_t row_b = (size_t)I * WB / 8;
-  const int j0 = tile * sbk::RT + wv * 2;
-  for (int i = threadIdx.x; i < a.n_slots_ub * SLOT_W; i += 256) tab[i] = a.slots[i];
+  const size_t down_off = 2 * (size_t)I * ((size_t)H * WB / 8);
+  const int rl = lane >> 4, pl = lane & 15;
+  const int j0 = tile * sbk::RT;
+  for (int i = tid; i < a.n_slots_ub * TAB_W; i += 256)
+    tab[i] = a.slots[(size_t)(i / TAB_W) * SLOT_W + i % TAB_W];
+  if (tid < T * K) wsh[tid] = a.w[tid];
+  const int v = tid;  // combine: one thread per (token, row), T * RT <= 128
+  const bool comb = v < T * sbk::RT;
+  const float resid =
+      (comb && a.residual) ? a.residual[(size_t)(v / sbk::RT) * H + j0 + v % sbk::RT] : 0.0f;
   __syncthreads();
   int n_slots = 0;
-  while (n_slots < a.n_slots_ub && tab[n_slots * SLOT_W + 1] > 0) n_slots++;
+  while (n_slots < a.n_slots_ub && tab[n_slots * TAB_W + 1] > 0) n_slots++;
 
   for (int s0 = 0; s0 < n_slots; s0 += SB) {
-    uint4 wd[SB][2][NPL];
+    uint4 wd[SB][2][NPQ];
     float sd[SB][2];
 #pragma unroll
     for (int b = 0; b < SB; b++) {
       const bool ok_s = s0 + b < n_slots;
-      const int ex = ok_s ? tab[(s0 + b) * SLOT_W] : -1;
+      const int ex = ok_s ? tab[(s0 + b) * TAB_W] : -1;
       const uint8_t *blob =
           ex < 0 ? a.shared : a.experts + (size_t)min(ex, a.E - 1) * a.blob_bytes;
       const uint8_t *down = blob + down_off;
@@ -699,63 +774,53 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
           reinterpret_cast<const float *>(blob + 3 * (size_t)I * ((size_t)H * WB / 8)) + 2 * I;
 #pragma unroll
       for (int rr = 0; rr < 2; rr++) {
+        const int row = j0 + rl + 4 * rr;
 #pragma unroll
-        for (int i = 0; i < NPL; i++) {
-          const int p = lane + 64 * i;
-          wd[b][rr][i] = (ok_s && p < npieces)
-                             ? reinterpret_cast<const uint4 *>(down + (size_t)(j0 + rr) * row_b)[p]
+        for (int i = 0; i < NPQ; i++) {
+          const int q = pl + 16 * i;
+          wd[b][rr][i] = (ok_s && q < nq)
+                             ? reinterpret_cast<const uint4 *>(down + (size_t)row * row_b)[qb + q]
                              : make_uint4(0, 0, 0, 0);
         }
-        sd[b][rr] = ok_s ? sdp[j0 + rr] : 0.0f;
+        sd[b][rr] = ok_s ? sdp[row] : 0.0f;
       }
+    }
+    // the first TT pairs of every slot of the batch: one round trip for all
+    Act<WB> act0[SB][NPQ][TT];
+    int pair0[SB][TT];
+#pragma unroll
+    for (int b = 0; b < SB; b++) {
+      const int n_tok = (s0 + b < n_slots) ? min(tab[(s0 + b) * TAB_W + 1], T) : 0;
+      down_act<WB, TT, NPQ>(a, tab + (s0 + b) * TAB_W + 2, n_tok, 0, P, qb, nq, pl, act0[b],
+                            pair0[b]);
     }
 #pragma unroll
     for (int b = 0; b < SB; b++) {
-      const int n_tok = (s0 + b < n_slots) ? min(tab[(s0 + b) * SLOT_W + 1], T) : 0;
-      const int *prs = tab + (s0 + b) * SLOT_W + 2;
-      for (int c0 = 0; c0 < n_tok; c0 += TT) {
-        Act<WB> act[NPL][TT];
+      const int n_tok = (s0 + b < n_slots) ? min(tab[(s0 + b) * TAB_W + 1], T) : 0;
+      down_rows<WB, TT, NPQ>(part, P, wv, rl, pl, wd[b], sd[b], act0[b], pair0[b]);
+      for (int c0 = TT; c0 < n_tok; c0 += TT) {
+        Act<WB> act[NPQ][TT];
         int pair[TT];
-#pragma unroll
-        for (int t = 0; t < TT; t++) {
-          pair[t] = (c0 + t < n_tok) ? min(max(prs[c0 + t], 0), T * (K + a.n_shared) - 1) : -1;
-          const int pp = pair[t] >= 0 ? pair[t] : 0;
-#pragma unroll
-          for (int i = 0; i < NPL; i++) {
-            const int p = lane + 64 * i;
-            load_act<WB>(a.qh + (size_t)pp * I, a.dh + (size_t)pp * (I / 32), p,
-                         pair[t] >= 0 && p < npieces, act[i][t]);
-          }
-        }
-#pragma unroll
-        for (int rr = 0; rr < 2; rr++) {
-          float acc[TT];
-#pragma unroll
-          for (int t = 0; t < TT; t++) acc[t] = 0.0f;
-#pragma unroll
-          for (int i = 0; i < NPL; i++) {
-#pragma unroll
-            for (int t = 0; t < TT; t++) acc[t] += piece_dot<WB>(wd[b][rr][i], act[i][t]);
-          }
-#pragma unroll
-          for (int t = 0; t < TT; t++) {
-            const float yv = sd[b][rr] * wave_sum(acc[t]);
-            if (lane == 0 && pair[t] >= 0) part[pair[t]][wv * 2 + rr] = yv;
-          }
-        }
+        down_act<WB, TT, NPQ>(a, tab + (s0 + b) * TAB_W + 2, n_tok, c0, P, qb, nq, pl, act,
+                              pair);
+        down_rows<WB, TT, NPQ>(part, P, wv, rl, pl, wd[b], sd[b], act, pair);
       }
     }
   }
   __syncthreads();
-  // combine in rank order, one thread per (token, row)
+  // combine in rank order, one thread per (token, row); quarters in order
   const bool norm = a.y_norm != nullptr;
   float ss = 0.0f;
-  const int v = threadIdx.x;  // T * RT <= 128 threads active
-  if (v < T * sbk::RT) {
-    const int t = v / sbk::RT, r = v % sbk::RT, j = tile * sbk::RT + r;
-    float acc = a.residual ? a.residual[(size_t)t * H + j] : 0.0f;
-    if (a.n_shared) acc += part[T * K + t][r];
-    for (int k = 0; k < K; k++) acc = fmaf(a.w[t * K + k], part[t * K + k][r], acc);
+  if (comb) {
+    const int t = v / sbk::RT, r = v % sbk::RT, j = j0 + r;
+    auto full = [&](int pr) {
+      const size_t q = (size_t)P * sbk::RT;
+      const float *pp = part + (size_t)pr * sbk::RT + r;
+      return ((pp[0] + pp[q]) + pp[2 * q]) + pp[3 * q];
+    };
+    float acc = resid;
+    if (a.n_shared) acc += full(T * K + t);
+    for (int k = 0; k < K; k++) acc = fmaf(wsh[t * K + k], full(t * K + k), acc);
     a.y[(size_t)t * H + j] = acc;
     ss = acc * acc;
   }
@@ -810,8 +875,10 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
            stage_ev(ev, MOE_STAGE_ROUTER_SELECT), a);
   launch_k(k_gate_up_small<WB, TT, NPG>, dim3(a.I / 32, a.n_slots_ub - a.n_shared), dim3(256), 0,
            st, stage_ev(ev, MOE_STAGE_GATE_UP), a);
-  launch_k(k_down_small<WB, TT, NPD, MOE_K3_SLOTS>, dim3(a.H / sbk::RT), dim3(256),
-           (uint32_t)(a.n_slots_ub * SLOT_W * sizeof(int)), st, stage_ev(ev, MOE_STAGE_DOWN), a);
+  const int P = a.T * (a.K + a.n_shared);
+  const size_t lds3 = (size_t)4 * P * sbk::RT * sizeof(float) + (size_t)a.n_slots_ub * TAB_W * 4;
+  launch_k(k_down_small<WB, TT, NPD, (TT == 1 ? MOE_K3_SLOTS : 2)>, dim3(a.H / sbk::RT),
+           dim3(256), (uint32_t)lds3, st, stage_ev(ev, MOE_STAGE_DOWN), a);
 }
 
 template <int WB, int TT>
