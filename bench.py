@@ -120,6 +120,27 @@ def gate_up_bytes(shape, T, U, small):
     return (U + S) * per_expert + x_in + (T * K + T * S) * I * 4
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, calibrated), or None when the
+    kernel sources changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"<!-- traffic kernel=gate_up workload=(\S+) src_sha256=([0-9a-f]+) "
+                  r"bytes_per_launch=(\d+) -->", open(path).read())
+    if not m or m.group(1) != workload:
+        return None
+    csrc = os.path.join(ROOT, "int4_routed_expert_moe_amd", "csrc")
+    src = b"".join(open(os.path.join(csrc, f), "rb").read()
+                   for f in ("decode.hip", "common.h", "kernels.h"))
+    if hashlib.sha256(src).hexdigest() != m.group(2):
+        return None
+    return float(m.group(3))
+
+
 def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s):
     """Oracle (plain C + OpenMP) on the first steps of the same workload."""
     import oracle
@@ -165,6 +186,8 @@ def main():
     ap.add_argument("--graph-block", type=int, default=64, help="steps per captured graph")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="also run a plain elementwise kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -237,6 +260,15 @@ def main():
         rc = L.moe_layer(*step_args(i, events))
         if rc != 0:
             raise RuntimeError(f"moe_layer failed: {L.moe_last_error().decode()}")
+
+    if args.copy_mb:  # a plain streaming kernel of known size, for hardware-counter calibration
+        n = args.copy_mb << 20  # reads n bytes, writes n bytes
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # --- warm-up ------------------------------------------------------------
     for i in range(W):
@@ -327,7 +359,8 @@ def main():
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "roofline": {"bound": "hbm", "kernel": dom,
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(args.workload) if small else None,
                      "bytes_per_launch": dom_bytes, "launch_us": dom_sec * 1e6},
     }
     if not args.no_cpu:
