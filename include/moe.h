@@ -223,12 +223,15 @@ typedef struct moe_events {
 /* ---------------------------------------------------------------------------
  * moe_layer — the whole step: routing, Q8_0 of x, grouping, expert FFNs and
  * combine on one stream, with all intermediates in the workspace.  For 1..16
- * tokens (and T*n_experts <= 4096) it runs as three kernels (router with
- * selection and grouping; gate/up with the Q8_0 of h; down with the combine
- * and optional RMSNorm) whose stage timestamps are MOE_STAGE_ROUTER_SCORES,
- * MOE_STAGE_GATE_UP and MOE_STAGE_DOWN; otherwise it chains the kernels of
- * moe_route, moe_quant_act, moe_expert_ffn and moe_combine.  Both give the
- * same arithmetic as the separate calls.
+ * tokens (with T*top_k <= 256, hidden <= 8192, and at most 256 / 128 packed
+ * 16-byte pieces per gate / down row) it runs as four kernels: router scores
+ * (MOE_STAGE_ROUTER_SCORES); per-token selection beside the shared expert's
+ * gate/up (MOE_STAGE_ROUTER_SELECT); batch union and routed gate/up with the
+ * Q8_0 of h (MOE_STAGE_GATE_UP); down with the combine and optional RMSNorm
+ * (MOE_STAGE_DOWN).  Otherwise it chains the kernels of moe_route,
+ * moe_quant_act, moe_expert_ffn and moe_combine.  Both give the same
+ * arithmetic as the separate calls (bit-identical idx and int32 block dots;
+ * float outputs within rounding of the summation order).
  * Workspace precondition: the workspace must be zero-filled before its first
  * use by moe_layer (it begins with counters that every call leaves at zero);
  * between moe_layer calls it must not be handed to other calls.  Calls that
