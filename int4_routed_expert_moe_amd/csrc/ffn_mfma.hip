@@ -1,0 +1,437 @@
+// Expert FFNs for large batches (prefill): grouped int4 x int8 GEMMs on the
+// matrix cores ("Show HN: 遅いコンピュータで GLM 5.2 を実行する", section
+// 実装済みの主な機能: packed int4 weights with per-row scales dequantised on
+// use, integer-dot kernels on Q8_0-style int8 activations, batch-union MoE).
+//
+// Same arithmetic as the GEMV path: for every (token, row) of an expert,
+//   acc = sum_b d[t,b] * P[t,r,b],  P = exact int32 dot of block b (32 codes)
+// then g = sg[r]*acc (and u), h = silu(g)*u, Q8_0(h), and the down projection
+// y = sd[j] * sum_b d_h[b] * P_down[j,b].
+//
+// One v_mfma_i32_16x16x32_i8 computes the 16x16 block dots of one Q8_0 block
+// exactly (K = 32 = the block), so the per-block scales are applied by a VALU
+// fix-up (convert, fused multiply-add) after every MFMA.  int4 codes enter
+// the MFMA as 16 x code (the low/high nibble split), with the 1/16 folded
+// into the activation scale; the split reorders k inside each group of 8,
+// and the activations staged in LDS are reordered the same way.
+//
+// Work items are (expert, 64-token tile) pairs from a tile list; a
+// workgroup computes 64 rows x 64 tokens of one work item (gate and up
+// together, so SwiGLU and the Q8_0 of h happen in its epilogue).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace mf {
+constexpr int NT = 64;              // tokens per tile
+constexpr int RT = 64;              // rows per workgroup
+constexpr int CB = 8;               // Q8_0 blocks per K chunk (256 k)
+constexpr int BSTR = CB * 32 + 16;  // LDS bytes per activation row (padded)
+constexpr int ASTR = CB * 16 + 4;   // LDS bytes per int4 weight row (padded)
+}  // namespace mf
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// --------------------------------------------------------------- tile list
+
+// tiles[i] = {expert (E = shared), first list position, token count}.  Routed
+// tokens of expert e are perm[offsets[e] ..]; the shared expert takes tokens
+// 0..T-1 in order.  One workgroup of 256 threads.
+__global__ void __launch_bounds__(256) k_mfma_tiles(int E, int T, int n_shared,
+                                                    const int32_t *offsets, int4 *tiles,
+                                                    int32_t *n_tiles) {
+  __shared__ int wt[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int c[4], loc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {  // 4 consecutive experts per thread (E <= 1024)
+    const int e = tid * 4 + j;
+    const int n = e < E ? offsets[e + 1] - offsets[e] : 0;
+    c[j] = (n + mf::NT - 1) / mf::NT;
+    loc += c[j];
+  }
+  int x = loc;  // inclusive scan over the block
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wt[wv] = x;
+  __syncthreads();
+  int pre = x - loc, total = 0;
+  for (int w = 0; w < 4; w++) {
+    pre += w < wv ? wt[w] : 0;
+    total += wt[w];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const int e = tid * 4 + j;
+    if (e < E) {
+      const int n = offsets[e + 1] - offsets[e];
+      for (int i = 0; i < c[j]; i++)
+        tiles[pre + i] = make_int4(e, offsets[e] + i * mf::NT, min(mf::NT, n - i * mf::NT), 0);
+    }
+    pre += c[j];
+  }
+  const int ns = n_shared ? (T + mf::NT - 1) / mf::NT : 0;
+  for (int i = tid; i < ns; i += 256)
+    tiles[total + i] = make_int4(E, i * mf::NT, min(mf::NT, T - i * mf::NT), 0);
+  if (tid == 0) *n_tiles = total + ns;
+}
+
+// ---------------------------------------------------------------- helpers
+
+struct TileInfo {
+  const uint8_t *blob;
+  int n;         // tokens in the tile
+  bool shared;
+};
+
+__device__ __forceinline__ TileInfo tile_info(const FfnArgs &a, int4 t) {
+  TileInfo r;
+  r.shared = t.x >= a.E;
+  r.blob = r.shared ? a.shared : a.experts + (size_t)min(max(t.x, 0), a.E - 1) * a.blob_bytes;
+  r.n = min(max(t.z, 0), mf::NT);
+  return r;
+}
+
+// token and pair of list position i of a tile
+__device__ __forceinline__ void tile_tok(const FfnArgs &a, int4 t, bool shared, int i, int &tok,
+                                         int &pair) {
+  if (shared) {
+    tok = min(max(t.y + i, 0), a.T - 1);
+    pair = a.T * a.K + tok;
+  } else {
+    const int sl = min(max(a.perm[min(max(t.y + i, 0), a.T * a.K - 1)], 0), a.T * a.K - 1);
+    tok = sl / a.K;
+    pair = sl;
+  }
+}
+
+// 8 activation bytes reordered (even positions, then odd) to match the
+// nibble split of the weights.
+__device__ __forceinline__ uint2 even_odd8(uint32_t w0, uint32_t w1) {
+  return make_uint2((uint32_t)even_bytes(w0, w1), (uint32_t)odd_bytes(w0, w1));
+}
+
+// A fragment of one 32-code block: lane (m, g) holds codes 8g..8g+7 of row m
+// as 16 x code, even codes first.
+__device__ __forceinline__ long a_frag(uint32_t w) {
+  return (long)(uint32_t)lo16(w) | ((long)(uint32_t)hi16(w) << 32);
+}
+
+// Stage one K chunk of activations: rows = tokens (64), CB blocks of 32
+// int8 (reordered per 8) and their scales / 16.
+struct ActChunk {
+  uint4 v[4];  // 4 x 16 bytes per thread (64 tokens x 16 pieces)
+  float d[2];  // 64 tokens x 8 block scales
+};
+
+__device__ __forceinline__ void load_act_chunk(const int8_t *q, const float *d, int row_len,
+                                               const int *tokl, int n, int c, int nblk,
+                                               ActChunk &r) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int i = tid + 256 * u, tok_i = i >> 4, piece = i & 15;  // 16-byte piece
+    const int blk = c * mf::CB + (piece >> 1);
+    const bool ok = tok_i < n && blk < nblk;
+    r.v[u] = ok ? *reinterpret_cast<const uint4 *>(q + (size_t)tokl[tok_i] * row_len +
+                                                    (size_t)blk * 32 + (piece & 1) * 16)
+                : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int i = tid + 256 * u, tok_i = i >> 3, b = i & 7;
+    const int blk = c * mf::CB + b;
+    r.d[u] = (tok_i < n && blk < nblk) ? d[(size_t)tokl[tok_i] * (row_len / 32) + blk] * 0.0625f
+                                       : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void store_act_chunk(const ActChunk &r, uint8_t *bs, float *ds) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int i = tid + 256 * u, tok_i = i >> 4, piece = i & 15;
+    uint2 *dst = reinterpret_cast<uint2 *>(bs + tok_i * mf::BSTR + piece * 16);
+    dst[0] = even_odd8(r.v[u].x, r.v[u].y);
+    dst[1] = even_odd8(r.v[u].z, r.v[u].w);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const int i = tid + 256 * u;
+    ds[(i >> 3) * mf::CB + (i & 7)] = r.d[u];
+  }
+}
+
+// Stage one K chunk of nm int4 weight matrices: 64 rows x CB blocks x 16 B.
+template <int NM>
+struct WChunk {
+  uint4 v[NM * 2];
+};
+
+template <int NM>
+__device__ __forceinline__ void load_w_chunk(const uint8_t *const *mat, size_t row_b, int r0,
+                                             int c, int nblk, WChunk<NM> &r) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int m = 0; m < NM; m++) {
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int i = tid + 256 * u, row = i >> 3, b = i & 7;  // 64 rows x 8 blocks
+      const int blk = c * mf::CB + b;
+      r.v[m * 2 + u] = blk < nblk ? *reinterpret_cast<const uint4 *>(
+                                         mat[m] + (size_t)(r0 + row) * row_b + (size_t)blk * 16)
+                                  : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+template <int NM>
+__device__ __forceinline__ void store_w_chunk(const WChunk<NM> &r, uint8_t *as) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int m = 0; m < NM; m++) {
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int i = tid + 256 * u, row = i >> 3, b = i & 7;
+      uint32_t *dst = reinterpret_cast<uint32_t *>(as + (size_t)m * mf::RT * mf::ASTR +
+                                                   row * mf::ASTR + b * 16);
+      dst[0] = r.v[m * 2 + u].x;
+      dst[1] = r.v[m * 2 + u].y;
+      dst[2] = r.v[m * 2 + u].z;
+      dst[3] = r.v[m * 2 + u].w;
+    }
+  }
+}
+
+// The K loop shared by both kernels: NM weight matrices (gate+up: 2, down:
+// 1) times the tile's activations; acc[m][s][i] = sum_b d*P for matrix m,
+// token sub-tile s (16 tokens), row 16 wv + 4 g + i.  DBG: raw block dots of
+// matrix m go to dots[m] at ((pair * R + row) * nblk + block).
+template <int NM, bool DBG>
+__device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, const int8_t *q,
+                           const float *d, int row_len, const int *tokl, const int *pairl, int n,
+                           int nblk, uint8_t *bs, float *ds, uint8_t *as, float (&acc)[NM][4][4],
+                           int32_t *const *dots, int R) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int m16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < NM; m++)
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc[m][s][i] = 0.0f;
+  const int nchunk = (nblk + mf::CB - 1) / mf::CB;
+  ActChunk ac;
+  WChunk<NM> wc;
+  load_act_chunk(q, d, row_len, tokl, n, 0, nblk, ac);
+  load_w_chunk<NM>(mat, row_b, r0, 0, nblk, wc);
+  for (int c = 0; c < nchunk; c++) {
+    __syncthreads();  // the previous chunk is consumed
+    store_act_chunk(ac, bs, ds);
+    store_w_chunk<NM>(wc, as);
+    __syncthreads();
+    if (c + 1 < nchunk) {  // next chunk in flight during this one's MFMAs
+      load_act_chunk(q, d, row_len, tokl, n, c + 1, nblk, ac);
+      load_w_chunk<NM>(mat, row_b, r0, c + 1, nblk, wc);
+    }
+    const int nb = min(mf::CB, nblk - c * mf::CB);
+    for (int b = 0; b < nb; b++) {
+      long af[NM];
+#pragma unroll
+      for (int m = 0; m < NM; m++) {
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(
+            as + (size_t)m * mf::RT * mf::ASTR + (wv * 16 + m16) * mf::ASTR + b * 16 + g * 4);
+        af[m] = a_frag(w);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; s++) {
+        const int col = s * 16 + m16;
+        const long bf = *reinterpret_cast<const long *>(bs + col * mf::BSTR + b * 32 + g * 8);
+        const float dd = ds[col * mf::CB + b];
+#pragma unroll
+        for (int m = 0; m < NM; m++) {
+          const v4i z = {0, 0, 0, 0};
+          const v4i p = __builtin_amdgcn_mfma_i32_16x16x32_i8(af[m], bf, z, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; i++) acc[m][s][i] = fmaf(dd, (float)p[i], acc[m][s][i]);
+          if (DBG && dots[m] && col < n) {
+            const int blk = c * mf::CB + b;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int row = r0 + wv * 16 + g * 4 + i;
+              dots[m][((size_t)pairl[col] * R + row) * nblk + blk] = p[i] >> 4;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+constexpr size_t MF_LDS_B = (size_t)mf::NT * mf::BSTR;
+constexpr size_t MF_LDS_D = (size_t)mf::NT * mf::CB * 4;
+
+// ---------------------------------------------------------------- gate/up
+
+// Workgroup (row tile, work item): rows 64 x .. 64 x + 63 of gate and up for
+// the work item's tokens; h = silu(g) * u to LDS, then the Q8_0 of h (two
+// 32-row blocks per token) to q_h / d_h of each pair.
+template <bool DBG>
+__global__ void __launch_bounds__(256) k_gate_up_mfma(FfnArgs a, const int4 *tiles,
+                                                      const int32_t *n_tiles, int8_t *q_h,
+                                                      float *d_h) {
+  __shared__ __align__(16) uint8_t bs[MF_LDS_B];
+  __shared__ float ds[mf::NT * mf::CB];
+  __shared__ __align__(16) uint8_t as[2 * mf::RT * mf::ASTR];
+  __shared__ int tokl[mf::NT], pairl[mf::NT];
+  if ((int)blockIdx.y >= *n_tiles) return;
+  const int4 t = tiles[blockIdx.y];
+  const TileInfo ti = tile_info(a, t);
+  const int H = a.H, I = a.I, r0 = blockIdx.x * mf::RT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid < mf::NT) {
+    int tok = 0, pair = 0;
+    if (tid < ti.n) tile_tok(a, t, ti.shared, tid, tok, pair);
+    tokl[tid] = tok;
+    pairl[tid] = pair;
+  }
+  __syncthreads();
+  const size_t row_b = (size_t)H / 2;
+  const uint8_t *mats[2] = {ti.blob, ti.blob + (size_t)I * row_b};
+  float acc[2][4][4];
+  int32_t *dots[2] = {a.dbg.gate_dots, a.dbg.up_dots};
+  mfma_kloop<2, DBG>(mats, row_b, r0, a.q, a.d, H, tokl, pairl, ti.n, H / 32, bs, ds, as, acc,
+                     dots, I);
+  // epilogue: h into LDS as [token][64 rows] fp32 (reuses the activation tile)
+  const float *scales = reinterpret_cast<const float *>(ti.blob + 3 * (size_t)I * row_b);
+  __syncthreads();
+  float *hs = reinterpret_cast<float *>(bs);  // 64 x 64 floats = 16 KB <= sizeof(bs)
+  const int m16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int rl = wv * 16 + g * 4 + i;
+    const float sg = scales[r0 + rl], su = scales[I + r0 + rl];
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      const float gv = sg * acc[0][s][i], uv = su * acc[1][s][i];
+      const float hv = gv / (1.0f + __expf(-gv)) * uv;
+      hs[(s * 16 + m16) * mf::RT + rl] = hv;
+      if (DBG && a.dbg.h && s * 16 + m16 < ti.n)
+        a.dbg.h[(size_t)pairl[s * 16 + m16] * I + r0 + rl] = hv;
+    }
+  }
+  __syncthreads();
+  // Q8_0: 64 tokens x 2 blocks x 8 lanes (4 values each) = 4 passes of 256
+#pragma unroll
+  for (int u = 0; u < 4; u++) {
+    const int i = tid + 256 * u, tok_i = i >> 4, blk = (i >> 3) & 1, j = i & 7;
+    const float4 v = *reinterpret_cast<const float4 *>(hs + tok_i * mf::RT + blk * 32 + j * 4);
+    float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    m = fmaxf(m, __shfl_xor(m, 1, 8));
+    m = fmaxf(m, __shfl_xor(m, 2, 8));
+    m = fmaxf(m, __shfl_xor(m, 4, 8));
+    const float dd = m / 127.0f;
+    const float id = dd != 0.0f ? 1.0f / dd : 0.0f;
+    auto cv = [&](float f) -> uint32_t {
+      const float r = fminf(fmaxf(roundf(f * id), -127.0f), 127.0f);
+      return (uint32_t)(uint8_t)(int8_t)(int)r;
+    };
+    const uint32_t packed = cv(v.x) | (cv(v.y) << 8) | (cv(v.z) << 16) | (cv(v.w) << 24);
+    if (tok_i < ti.n) {
+      const size_t pair = (size_t)pairl[tok_i];
+      reinterpret_cast<uint32_t *>(q_h + pair * I + r0 + blk * 32)[j] = packed;
+      if (j == 0) d_h[pair * (I / 32) + (r0 >> 5) + blk] = dd;
+      if (DBG && a.dbg.q_h) reinterpret_cast<uint32_t *>(a.dbg.q_h + pair * I + r0 + blk * 32)[j] = packed;
+      if (DBG && a.dbg.d_h && j == 0) a.dbg.d_h[pair * (I / 32) + (r0 >> 5) + blk] = dd;
+    }
+  }
+}
+
+// ------------------------------------------------------------------- down
+
+// Workgroup (row tile, work item): output rows 64 x .. of the down matrix
+// for the work item's pairs, from Q8_0(h); routed rows go to expert_out of
+// the slot, shared rows to shared_out of the token.
+template <bool DBG>
+__global__ void __launch_bounds__(256) k_down_mfma(FfnArgs a, const int4 *tiles,
+                                                   const int32_t *n_tiles, const int8_t *q_h,
+                                                   const float *d_h) {
+  __shared__ __align__(16) uint8_t bs[MF_LDS_B];
+  __shared__ float ds[mf::NT * mf::CB];
+  __shared__ __align__(16) uint8_t as[mf::RT * mf::ASTR];
+  __shared__ int tokl[mf::NT], pairl[mf::NT];
+  if ((int)blockIdx.y >= *n_tiles) return;
+  const int4 t = tiles[blockIdx.y];
+  const TileInfo ti = tile_info(a, t);
+  const int H = a.H, I = a.I, r0 = blockIdx.x * mf::RT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid < mf::NT) {
+    int tok = 0, pair = 0;
+    if (tid < ti.n) tile_tok(a, t, ti.shared, tid, tok, pair);
+    tokl[tid] = pair;  // activations of the down projection are indexed by pair
+    pairl[tid] = pair;
+  }
+  __syncthreads();
+  const size_t row_b = (size_t)I / 2;
+  const uint8_t *mats[1] = {ti.blob + 2 * (size_t)I * ((size_t)H / 2)};
+  float acc[1][4][4];
+  int32_t *dots[1] = {a.dbg.down_dots};
+  mfma_kloop<1, DBG>(mats, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs, ds, as, acc,
+                     dots, H);
+  const float *sd =
+      reinterpret_cast<const float *>(ti.blob + 3 * (size_t)I * ((size_t)H / 2)) + 2 * I;
+  const int m16 = lane & 15, g = lane >> 4;
+  const int row = r0 + wv * 16 + g * 4;  // 4 consecutive rows per lane
+  const float4 s4 = *reinterpret_cast<const float4 *>(sd + row);
+#pragma unroll
+  for (int s = 0; s < 4; s++) {
+    const int col = s * 16 + m16;
+    if (col >= ti.n) continue;
+    const float4 y = make_float4(s4.x * acc[0][s][0], s4.y * acc[0][s][1], s4.z * acc[0][s][2],
+                                 s4.w * acc[0][s][3]);
+    const int pair = pairl[col];
+    float *dst = ti.shared ? a.shared_out + (size_t)(pair - a.T * a.K) * H
+                           : a.expert_out + (size_t)pair * H;
+    *reinterpret_cast<float4 *>(dst + row) = y;
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+size_t mfma_tiles_max(int T, int K, int E, int n_shared) {
+  return (size_t)(T * K + mf::NT - 1) / mf::NT + E + (n_shared ? (T + mf::NT - 1) / mf::NT : 0);
+}
+
+bool mfma_supported(const FfnArgs &a) {
+  return a.wbits == 4 && a.H % 256 == 0 && a.I % mf::RT == 0 && a.H % mf::RT == 0 &&
+         a.E <= 1024 && a.T > 0;
+}
+
+void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_h, float *d_h,
+                     hipStream_t st, const moe_events *ev) {
+  const int max_tiles = (int)mfma_tiles_max(a.T, a.K, a.E, a.n_shared);
+  hipLaunchKernelGGL(k_mfma_tiles, dim3(1), dim3(256), 0, st, a.E, a.T, a.n_shared, a.offsets,
+                     tiles, n_tiles);
+  const bool dbg = a.dbg.gate_dots || a.dbg.up_dots || a.dbg.h || a.dbg.q_h || a.dbg.d_h ||
+                   a.dbg.down_dots;
+  const dim3 g1(a.I / mf::RT, max_tiles), g2(a.H / mf::RT, max_tiles);
+  if (dbg) {
+    launch_k(k_gate_up_mfma<true>, g1, dim3(256), 0, st, stage_ev(ev, MOE_STAGE_GATE_UP), a,
+             (const int4 *)tiles, (const int32_t *)n_tiles, q_h, d_h);
+    launch_k(k_down_mfma<true>, g2, dim3(256), 0, st, stage_ev(ev, MOE_STAGE_DOWN), a,
+             (const int4 *)tiles, (const int32_t *)n_tiles, (const int8_t *)q_h,
+             (const float *)d_h);
+  } else {
+    launch_k(k_gate_up_mfma<false>, g1, dim3(256), 0, st, stage_ev(ev, MOE_STAGE_GATE_UP), a,
+             (const int4 *)tiles, (const int32_t *)n_tiles, q_h, d_h);
+    launch_k(k_down_mfma<false>, g2, dim3(256), 0, st, stage_ev(ev, MOE_STAGE_DOWN), a,
+             (const int4 *)tiles, (const int32_t *)n_tiles, (const int8_t *)q_h,
+             (const float *)d_h);
+  }
+}
+
+}  // namespace moe

@@ -64,6 +64,14 @@ struct FfnArgs {
 };
 void launch_ffn_gemv(const FfnArgs &a, hipStream_t st, const moe_events *ev = nullptr);
 
+// Expert FFN over grouped tokens on the matrix cores (ffn_mfma.hip): tile list
+// from the grouping offsets, then grouped gate/up (Q8_0 of h into q_h/d_h,
+// [P][I] and [P][I/32]) and grouped down into expert_out / shared_out.
+size_t mfma_tiles_max(int T, int K, int E, int n_shared);
+bool mfma_supported(const FfnArgs &a);
+void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_h, float *d_h,
+                     hipStream_t st, const moe_events *ev = nullptr);
+
 // Whole layer for 1..16 tokens in three kernels (decode.hip).
 struct LayerArgs {
   int H, I, E, G, TG, K, T, n_shared, wbits;

@@ -98,7 +98,9 @@ RouteWs carve_route(Carve &cv, const moe_cfg &c, int T) {
 
 struct FfnWs {
   int32_t *counts, *offsets, *perm, *inv, *active, *n_active;
-  float *h;
+  int32_t *n_tiles;
+  int4 *tiles;
+  float *h;  // fp32 h [P][I] (GEMV path); the MFMA path keeps Q8_0(h) here
 };
 FfnWs carve_ffn(Carve &cv, const moe_cfg &c, int T) {
   FfnWs f;
@@ -110,6 +112,8 @@ FfnWs carve_ffn(Carve &cv, const moe_cfg &c, int T) {
   f.inv = cv.take<int32_t>(slots);
   f.active = cv.take<int32_t>(c.n_experts);
   f.n_active = cv.take<int32_t>(1);
+  f.n_tiles = cv.take<int32_t>(1);
+  f.tiles = cv.take<int4>(moe::mfma_tiles_max(T, c.top_k, c.n_experts, c.n_shared));
   f.h = cv.take<float>(pairs * c.inter);
   return f;
 }
@@ -186,7 +190,14 @@ int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32
   a.shared_out = shared_out;
   if (dbg) a.dbg = *dbg;
   else memset(&a.dbg, 0, sizeof(a.dbg));
-  moe::launch_ffn_gemv(a, st, ev);
+  if (T > 16 && moe::mfma_supported(a)) {  // batches: grouped GEMMs on the matrix cores
+    const size_t pairs = (size_t)T * c.top_k + (size_t)T * c.n_shared;
+    int8_t *q_h = reinterpret_cast<int8_t *>(ws.h);
+    float *d_h = reinterpret_cast<float *>(q_h + ((pairs * c.inter + 255) & ~(size_t)255));
+    moe::launch_ffn_mfma(a, ws.tiles, ws.n_tiles, q_h, d_h, st, ev);
+  } else {
+    moe::launch_ffn_gemv(a, st, ev);
+  }
   return launched("moe_expert_ffn");
 }
 
