@@ -249,6 +249,7 @@ __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, cons
       }
 #pragma unroll
       for (int s = 0; s < 4; s++) {
+        if (s * 16 >= n) break;  // sub-tiles past the work item's tokens (uniform)
         const int col = s * 16 + m16;
         const long bf = *reinterpret_cast<const long *>(bs + col * mf::BSTR + b * 32 + g * 8);
         const float dd = ds[col * mf::CB + b];
@@ -281,7 +282,7 @@ constexpr size_t MF_LDS_D = (size_t)mf::NT * mf::CB * 4;
 // the work item's tokens; h = silu(g) * u to LDS, then the Q8_0 of h (two
 // 32-row blocks per token) to q_h / d_h of each pair.
 template <bool DBG>
-__global__ void __launch_bounds__(256) k_gate_up_mfma(FfnArgs a, const int4 *tiles,
+__global__ void __launch_bounds__(256, 3) k_gate_up_mfma(FfnArgs a, const int4 *tiles,
                                                       const int32_t *n_tiles, int8_t *q_h,
                                                       float *d_h) {
   __shared__ __align__(16) uint8_t bs[MF_LDS_B];

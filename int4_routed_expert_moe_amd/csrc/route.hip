@@ -87,6 +87,112 @@ __global__ void __launch_bounds__(64) k_router_scores(int T, int H, int E,
   }
 }
 
+// Router scores for larger batches as a register-tiled fp32 GEMM with the
+// same fixed order: every (token, expert) output is an fma chain over each
+// 64-element chunk of k in increasing order, from 0, and the chunk partials
+// are added left to right.  Workgroup tile: (16 TM) tokens x (16 TN)
+// experts; thread (tx, ty) owns tokens tx + 16 a and experts ty + 16 b
+// (interleaved so that a wave's LDS reads fall in distinct banks).  One
+// chunk of x and W (64 k each) is staged in LDS per step, rows padded to
+// 68 floats, the next chunk in registers meanwhile; each thread walks k
+// four at a time with 16-byte LDS reads.
+namespace rg {
+constexpr int KC = 64, STR = KC + 4;
+}
+template <int TM, int TN>
+__global__ void __launch_bounds__(256) k_router_gemm(int T, int H, int E,
+                                                     const float *__restrict__ x,
+                                                     const float *__restrict__ wr,
+                                                     const float *__restrict__ bias,
+                                                     float *__restrict__ s,
+                                                     float *__restrict__ sb) {
+  constexpr int MT = 16 * TM, NTL = 16 * TN;
+  __shared__ __align__(16) float xs[MT * rg::STR];
+  __shared__ __align__(16) float ws[NTL * rg::STR];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int t0 = blockIdx.x * MT, e0 = blockIdx.y * NTL;
+  float tot[TM][TN], acc[TM][TN];
+  const int nch = H / rg::KC;
+  constexpr int NX = MT * 16 / 256, NW = NTL * 16 / 256;  // float4 per thread per chunk
+  float4 px[NX], pw[NW];  // the next chunk, in flight during this one's FMAs
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int u = 0; u < NX; u++) {
+      const int i = tid + 256 * u, r = i >> 4, q = i & 15, t = t0 + r;
+      px[u] = t < T ? reinterpret_cast<const float4 *>(x + (size_t)t * H + c * rg::KC)[q]
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < NW; u++) {
+      const int i = tid + 256 * u, r = i >> 4, q = i & 15, e = e0 + r;
+      pw[u] = e < E ? reinterpret_cast<const float4 *>(wr + (size_t)e * H + c * rg::KC)[q]
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  fetch(0);
+  for (int c = 0; c < nch; c++) {
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NX; u++) {
+      const int i = tid + 256 * u;
+      *reinterpret_cast<float4 *>(xs + (i >> 4) * rg::STR + (i & 15) * 4) = px[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NW; u++) {
+      const int i = tid + 256 * u;
+      *reinterpret_cast<float4 *>(ws + (i >> 4) * rg::STR + (i & 15) * 4) = pw[u];
+    }
+    __syncthreads();
+    if (c + 1 < nch) fetch(c + 1);
+#pragma unroll
+    for (int a = 0; a < TM; a++)
+#pragma unroll
+      for (int b = 0; b < TN; b++) acc[a][b] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < rg::KC; k += 4) {
+      float4 xv[TM], wv[TN];
+#pragma unroll
+      for (int a = 0; a < TM; a++)
+        xv[a] = *reinterpret_cast<const float4 *>(xs + (tx + 16 * a) * rg::STR + k);
+#pragma unroll
+      for (int b = 0; b < TN; b++)
+        wv[b] = *reinterpret_cast<const float4 *>(ws + (ty + 16 * b) * rg::STR + k);
+#pragma unroll
+      for (int a = 0; a < TM; a++)
+#pragma unroll
+        for (int b = 0; b < TN; b++) {
+          float v = acc[a][b];
+          v = __builtin_fmaf(xv[a].x, wv[b].x, v);
+          v = __builtin_fmaf(xv[a].y, wv[b].y, v);
+          v = __builtin_fmaf(xv[a].z, wv[b].z, v);
+          v = __builtin_fmaf(xv[a].w, wv[b].w, v);
+          acc[a][b] = v;
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < TM; a++)
+#pragma unroll
+      for (int b = 0; b < TN; b++) tot[a][b] = c == 0 ? acc[a][b] : tot[a][b] + acc[a][b];
+  }
+#pragma unroll
+  for (int a = 0; a < TM; a++) {
+    const int t = t0 + tx + 16 * a;
+#pragma unroll
+    for (int b = 0; b < TN; b++) {
+      const int e = e0 + ty + 16 * b;
+      if (t < T && e < E) {
+        const float sv = sigmoid_fixed(tot[a][b]);
+        s[(size_t)t * E + e] = sv;
+        sb[(size_t)t * E + e] = sv + bias[e];
+      }
+    }
+  }
+}
+
+#ifndef ROUTER_TM
+#define ROUTER_TM 2
+#endif
+
 void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *wr,
                           const float *bias, float *s, float *sb, hipStream_t st,
                           const moe_events *ev) {
@@ -98,9 +204,13 @@ void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *
   } else if (T <= 4) {
     launch_k(k_router_scores<4>, dim3(E, 1), dim3(64), 4 * lds, st, e0, T, H, E, x, wr, bias, s,
              sb);
-  } else {
+  } else if (T <= 64) {
     launch_k(k_router_scores<8>, dim3(E, (T + 7) / 8), dim3(64), 8 * lds, st, e0, T, H, E, x, wr,
              bias, s, sb);
+  } else {
+    launch_k(k_router_gemm<ROUTER_TM, 4>, dim3((T + 16 * ROUTER_TM - 1) / (16 * ROUTER_TM),
+                                               (E + 63) / 64),
+             dim3(256), 0, st, e0, T, H, E, x, wr, bias, s, sb);
   }
 }
 
