@@ -49,10 +49,20 @@ WORKLOADS = {
     "verify4": dict(T=4, tokens="perturbed", bias="uniform", seed="verify", ring=8),
     "verify16": dict(T=16, tokens="perturbed", bias="uniform", seed="verify", ring=4),
     "prefill": dict(T=2048, tokens="normal", bias="zipf", seed="prefill", ring=2),
+    # 16 consecutive layers per step (pre-norm residual between them), all resident
+    "stack1": dict(T=1, tokens="normal", bias="zipf", seed="stack", ring=16, layers=16),
+    "stack8": dict(T=8, tokens="normal", bias="zipf", seed="stack", ring=16, layers=16),
 }
 
 
-def describe(name, shape, T, ring):
+def describe(name, shape, T, ring, layers=1):
+    if layers > 1:
+        return (f"{name}: {T} token(s) per step through a stack of {layers} routed-MoE layers "
+                f"(independent seeds, Zipf-skewed bias, unit-gain RMSNorm + residual between "
+                f"layers; hidden {shape.hidden}, expert intermediate {shape.inter}, "
+                f"{shape.n_experts} experts in {shape.n_group} groups, top-{shape.topk_group} "
+                f"groups, top-{shape.top_k}, {shape.n_shared} shared expert, int{shape.wbits} "
+                f"experts + fp32 row scales, Q8_0 activations), all layers resident in HBM")
     return (f"{name}: {T} token(s) per step through one routed-MoE layer (hidden {shape.hidden}, "
             f"expert intermediate {shape.inter}, {shape.n_experts} experts in {shape.n_group} "
             f"groups, top-{shape.topk_group} groups, top-{shape.top_k}, {shape.n_shared} shared "
@@ -142,6 +152,39 @@ def measured_traffic(workload):
     return float(m.group(3))
 
 
+def cpu_baseline_stack(shape, seed, layers, tokens_fn, T, n_steps):
+    """Oracle on the first steps of the stack workload (all layers)."""
+    import oracle
+    import synth
+    kw = dict(H=shape.hidden, I=shape.inter, n_experts=shape.n_experts, n_group=shape.n_group,
+              topk_group=shape.topk_group, top_k=shape.top_k, scale=shape.routed_scaling,
+              wbits=shape.wbits)
+    caches = [dict() for _ in layers]
+    shared = [synth.expert_blob(shape, seed, l, synth.SHARED_ID) for l in range(len(layers))]
+    spent, done = 0.0, 0
+    for i in range(n_steps):
+        h = tokens_fn(i)
+        t0 = time.perf_counter()
+        xn = oracle.rmsnorm(h)
+        spent += time.perf_counter() - t0
+        for l, (wr, bias) in enumerate(layers):
+            idx, _, _ = oracle.route(xn, wr, bias, shape.n_group, shape.topk_group, shape.top_k,
+                                     shape.routed_scaling)
+            for e in np.unique(idx):  # drawn outside the timed region
+                if int(e) not in caches[l]:
+                    caches[l][int(e)] = synth.expert_blob(shape, seed, l, int(e))
+            t0 = time.perf_counter()
+            out = oracle.layer(xn, wr, bias, caches[l].__getitem__, shared[l], residual=h,
+                               want_norm=True, **kw)
+            spent += time.perf_counter() - t0
+            h, xn = out["y"], out["y_norm"]
+        done += T
+    return dict(value=done / spent, unit="tokens/s", cores=oracle.threads(), kind="oracle",
+                sample=f"first {n_steps} step(s) ({done} tokens through all {len(layers)} layers) "
+                       f"of the same workload, {spent:.1f} s of oracle time (plain C, OpenMP "
+                       f"over output rows; expert records drawn outside the timed region)")
+
+
 def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s):
     """Oracle (plain C + OpenMP) on the first steps of the same workload."""
     import oracle
@@ -204,7 +247,8 @@ def main():
     wl = WORKLOADS[args.workload]
     shape = synth.REAL.with_bits(args.wbits)
     T = wl["T"]
-    R = args.ring or wl["ring"]
+    NL = wl.get("layers", 1)
+    R = wl["ring"] if NL > 1 else (args.ring or wl["ring"])
     seed = synth.SEEDS[wl["seed"]]
     K, W = args.steps, args.warmup
     dev = torch.device("cuda:0")
@@ -242,25 +286,42 @@ def main():
     else:
         xs = synth.tokens(shape, seed, n_tok_steps * T).reshape(n_tok_steps, T, shape.hidden)
     x_all = torch.from_numpy(xs).to(dev)
-    idx_all = torch.zeros((n_tok_steps, T, shape.top_k), dtype=torch.int32, device=dev)
+    idx_all = torch.zeros((n_tok_steps, NL, T, shape.top_k), dtype=torch.int32, device=dev)
     y = torch.empty((T, shape.hidden), dtype=torch.float32, device=dev)
+    hbuf = [torch.empty((T, shape.hidden), dtype=torch.float32, device=dev) for _ in range(2)]
+    xnbuf = [torch.empty((T, shape.hidden), dtype=torch.float32, device=dev) for _ in range(2)]
     ws = torch.zeros(moe.layer_workspace(cfg, T), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     L = moe.lib()
     c_cfg = moe.Config.c(cfg)
 
-    def step_args(i, events=None):
-        r = ring[i % R]
-        return (ctypes.byref(c_cfg), T, x_all[i].data_ptr(), r["wr"].data_ptr(),
-                r["bias"].data_ptr(), r["ex"].data_ptr(), r["sh"].data_ptr(), None,
-                y.data_ptr(), None, 1e-5, idx_all[i].data_ptr(), None, ws.data_ptr(),
-                ws.numel(), events, stream.cuda_stream)
-
-    def run_step(i, events=None):
-        rc = L.moe_layer(*step_args(i, events))
+    def call_layer(r, x_ptr, res_ptr, y_ptr, yn_ptr, idx_ptr, events):
+        rc = L.moe_layer(ctypes.byref(c_cfg), T, x_ptr, r["wr"].data_ptr(), r["bias"].data_ptr(),
+                         r["ex"].data_ptr(), r["sh"].data_ptr(), res_ptr, y_ptr, yn_ptr, 1e-5,
+                         idx_ptr, None, ws.data_ptr(), ws.numel(), events, stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"moe_layer failed: {L.moe_last_error().decode()}")
+
+    def run_step(i, events=None):
+        """events: None, or one moe_events per layer."""
+        ev = (lambda l: None) if events is None else (lambda l: ctypes.byref(events[l]))
+        if NL == 1:
+            call_layer(ring[i % R], x_all[i].data_ptr(), None, y.data_ptr(), None,
+                       idx_all[i, 0].data_ptr(), ev(0))
+            return
+        # pre-norm stack: xn = RMSNorm(h); h <- h + MoE_l(xn), the layer also
+        # writes RMSNorm of the new h for the next layer
+        rc = L.moe_rmsnorm(T, shape.hidden, x_all[i].data_ptr(), xnbuf[0].data_ptr(), 1e-5,
+                           stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"moe_rmsnorm failed: {L.moe_last_error().decode()}")
+        h_ptr = x_all[i].data_ptr()
+        for l in range(NL):
+            a, b = l % 2, (l + 1) % 2
+            call_layer(ring[l], xnbuf[a].data_ptr(), h_ptr, hbuf[b].data_ptr(),
+                       xnbuf[b].data_ptr(), idx_all[i, l].data_ptr(), ev(l))
+            h_ptr = hbuf[b].data_ptr()
 
     if args.copy_mb:  # a plain streaming kernel of known size, for hardware-counter calibration
         n = args.copy_mb << 20  # reads n bytes, writes n bytes
@@ -303,40 +364,46 @@ def main():
     sec = t1 - t0
 
     # --- per-kernel durations (eager pass, events stamped by the dispatch) ----
-    n_ev = min(K, 256)
+    n_ev = max(1, min(K, 256 // NL))
     stage_names = list(moe.STAGES)
     evs = []
     for i in range(n_ev):
-        me = moe.MoeEvents()
-        for s in range(len(stage_names)):
-            me.start[s] = hip.event()
-            me.stop[s] = hip.event()
-        evs.append(me)
+        per_layer = []
+        for l in range(NL):
+            me = moe.MoeEvents()
+            for s in range(len(stage_names)):
+                me.start[s] = hip.event()
+                me.stop[s] = hip.event()
+            per_layer.append(me)
+        evs.append(per_layer)
     torch.cuda.synchronize()
     for j in range(n_ev):
-        run_step(W + j, ctypes.byref(evs[j]))
+        run_step(W + j, evs[j])
     torch.cuda.synchronize()
     stage_ms = {}
     for s, name in enumerate(stage_names):
         try:  # stages the chosen path did not launch have unrecorded events
-            v = [hip.elapsed_ms(evs[j].start[s], evs[j].stop[s]) for j in range(n_ev)]
+            v = [hip.elapsed_ms(me.start[s], me.stop[s]) for per_layer in evs for me in per_layer]
         except RuntimeError:
             continue
-        stage_ms[name] = float(np.mean(v))
-    for me in evs:
-        for s in range(len(stage_names)):
-            hip.destroy(me.start[s])
-            hip.destroy(me.stop[s])
+        stage_ms[name] = float(np.mean(v))  # per layer
+    for per_layer in evs:
+        for me in per_layer:
+            for s in range(len(stage_names)):
+                hip.destroy(me.start[s])
+                hip.destroy(me.stop[s])
 
     # --- work accounting ------------------------------------------------------
     idx_h = idx_all.cpu().numpy()
-    U = float(np.mean([np.unique(idx_h[i]).size for i in range(W, W + K)]))
-    step_bytes = layer_bytes(shape, T, U, bb)
+    U_l = [float(np.mean([np.unique(idx_h[i, l]).size for i in range(W, W + K)]))
+           for l in range(NL)]
+    U = float(np.mean(U_l))
+    step_bytes = sum(layer_bytes(shape, T, u, bb) for u in U_l)
     small = T <= 16  # the layer's small-batch path (four kernels)
     dom_sec = stage_ms["gate_up"] * 1e-3
     if small:  # HBM-bound GEMV: algorithmic bytes of the gate/up launch
         dom = "gate_up (routed expert gate/up + SwiGLU + Q8_0 of h)"
-        dom_bytes = gate_up_bytes(shape, T, U, small)
+        dom_bytes = float(np.mean([gate_up_bytes(shape, T, u, small) for u in U_l]))
         roof = {"bound": "hbm", "kernel": dom, "achieved": dom_bytes / dom_sec / 1e9,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] / HBM_PEAK_GBPS
@@ -354,7 +421,7 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": K * T / sec,
+        "value": K * T / sec,  # tokens through the whole step (all layers of a stack)
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
@@ -365,8 +432,8 @@ def main():
         "vs_baseline": None,
         "dtype": f"i{shape.wbits}xi8->i32",
         "data": "synthetic",
-        "config": {"workload": describe(args.workload, shape, T, R), "tokens_per_step": T,
-                   "layer_instances": R, "hip_graph": use_graph,
+        "config": {"workload": describe(args.workload, shape, T, R, NL), "tokens_per_step": T,
+                   "layers_per_step": NL, "layer_instances": R, "hip_graph": use_graph,
                    "distinct_routed_experts_per_step": U},
         "hbm_gbps": step_bytes / (sec / K) / 1e9,
         "hbm_frac": step_bytes / (sec / K) / 1e9 / HBM_PEAK_GBPS,
@@ -375,9 +442,14 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu:
-        r0 = ring[0]
-        out["cpu_baseline"] = cpu_baseline(shape, seed, r0["wr_h"], r0["bias_h"], tokens_for, T,
-                                           args.cpu_budget)
+        if NL > 1:
+            out["cpu_baseline"] = cpu_baseline_stack(shape, seed,
+                                                     [(r["wr_h"], r["bias_h"]) for r in ring],
+                                                     tokens_for, T, 2)
+        else:
+            r0 = ring[0]
+            out["cpu_baseline"] = cpu_baseline(shape, seed, r0["wr_h"], r0["bias_h"], tokens_for,
+                                               T, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 

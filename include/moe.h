@@ -227,15 +227,15 @@ typedef struct moe_events {
  * 16-byte pieces per gate / down row) it runs as four kernels: router scores
  * (MOE_STAGE_ROUTER_SCORES); per-token selection beside the shared expert's
  * gate/up (MOE_STAGE_ROUTER_SELECT); batch union and routed gate/up with the
- * Q8_0 of h (MOE_STAGE_GATE_UP); down with the combine and optional RMSNorm
- * (MOE_STAGE_DOWN).  Otherwise it chains the kernels of moe_route,
+ * Q8_0 of h (MOE_STAGE_GATE_UP); down with the combine (MOE_STAGE_DOWN); and,
+ * when y_norm is given, the RMSNorm (MOE_STAGE_COMBINE).  Otherwise it chains the kernels of moe_route,
  * moe_quant_act, moe_expert_ffn and moe_combine.  Both give the same
  * arithmetic as the separate calls (bit-identical idx and int32 block dots;
  * float outputs within rounding of the summation order).
  * Workspace precondition: the workspace must be zero-filled before its first
- * use by moe_layer (it begins with counters that every call leaves at zero);
- * between moe_layer calls it must not be handed to other calls.  Calls that
- * overlap on the same workspace race.
+ * use by moe_layer (it begins with a reserved line that every call leaves at
+ * zero); between moe_layer calls it must not be handed to other calls.  Calls
+ * that overlap on the same workspace race.
  * x [T][H] is the (already normalised) layer input; y [T][H] the output
  * (plus residual when given); y_norm optional as in moe_combine.  idx_out and
  * w_out ([T][K], nullable) receive the routing decision.  ev: optional
@@ -243,9 +243,8 @@ typedef struct moe_events {
  * Errors: as the calls it makes.
  * ------------------------------------------------------------------------- */
 size_t moe_layer_workspace(const moe_cfg *cfg, int32_t T);
-/* Bytes at the start of a moe_layer workspace that hold its counters (the
- * part that must be zero before first use; every moe_layer call leaves it
- * zero). */
+/* Bytes at the start of a moe_layer workspace that must be zero before its
+ * first use (every moe_layer call leaves them zero). */
 size_t moe_layer_sync_bytes(void);
 int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
               const float *bias, const void *experts, const void *shared,

@@ -43,51 +43,21 @@ namespace moe {
 
 namespace sbk {
 constexpr int TMAX = 16;
-constexpr int LINE = 64;  // uint32 words between counters (256 B)
-constexpr int C_NORM = 0;   // workgroups of the down kernel done (RMSNorm)
-constexpr int C_END = 1;
-constexpr int RT = 8;       // output rows per K3 workgroup (2 per wave)
+constexpr int RT = 8;            // output rows per K3 workgroup
 constexpr int MAXP = TMAX * 17;  // pairs: T*K routed + T shared, K <= 16
 }  // namespace sbk
 
-// Slot table (written by the last router workgroup): entry j describes
-// expert slot j -- the shared expert first, then the active routed experts
-// in ascending order -- as SLOT_W int32: expert (-1 = shared), token count,
-// TMAX pair ids (routed: slot id t*K+k; shared: T*K+t), TMAX token ids.
+// Slot table (written by the gate/up workgroups of column 0): entry j
+// describes expert slot j -- the shared expert first, then the active routed
+// experts in ascending order -- as SLOT_W int32: expert (-1 = shared), token
+// count, TMAX pair ids (routed: slot id t*K+k; shared: T*K+t), TMAX token ids.
 // Entries past the last slot have a token count of 0.  A consumer reads its
 // entry in one round trip.
 constexpr int SLOT_W = 2 + 2 * sbk::TMAX;
 
-size_t small_batch_sync_bytes() { return (size_t)sbk::C_END * sbk::LINE * sizeof(uint32_t); }
-
-__device__ __forceinline__ uint32_t *sctr(const LayerArgs &a, int c) {
-  return a.sync + (size_t)c * sbk::LINE;
-}
-
-__device__ __forceinline__ void release_fence() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void acquire_fence() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-__device__ __forceinline__ void drain_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// The block's global writes become visible device-wide (stores drained, one
-// L2 write-back by thread 0), then thread 0 counts; old value broadcast.
-__device__ uint32_t block_count(uint32_t *p, uint32_t *lds_word) {
-  drain_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    release_fence();
-    *lds_word = __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  const uint32_t old = *lds_word;
-  __syncthreads();
-  return old;
-}
-
-// The last block acquires what the others wrote (one L2 invalidate).
-__device__ void block_acquire() {
-  if (threadIdx.x == 0) acquire_fence();
-  __syncthreads();
-}
+// A reserved, zero-initialised line at the start of the layer workspace; no
+// kernel of this path communicates between workgroups, so it stays zero.
+size_t small_batch_sync_bytes() { return 256; }
 
 __device__ __forceinline__ float exp_fixed_sb(float y) {
   y = y > 87.0f ? 87.0f : y;
@@ -734,9 +704,7 @@ __device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, in
 template <int WB, int TT, int NPQ, int SB>
 __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   extern __shared__ __align__(16) uint8_t dyn[];
-  __shared__ float red[sbk::TMAX];
   __shared__ float wsh[256];
-  __shared__ uint32_t word;
   const int tile = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I, T = a.T, K = a.K;
@@ -825,32 +793,39 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
     ss = acc * acc;
   }
   if (!norm) return;
-  // per-token sum of squares of this tile's 8 rows (8 consecutive threads)
+  // per-token sum of squares of this tile's 8 rows (8 consecutive threads);
+  // the normalisation kernel adds the tiles
   ss += __shfl_xor(ss, 1, 8);
   ss += __shfl_xor(ss, 2, 8);
   ss += __shfl_xor(ss, 4, 8);
-  const int n_tiles = gridDim.x;
-  if (v < T * sbk::RT && (v % sbk::RT) == 0) a.ssq[(size_t)(v / sbk::RT) * n_tiles + tile] = ss;
-  const uint32_t old = block_count(sctr(a, sbk::C_NORM), &word);
-  if (old != (uint32_t)n_tiles - 1) return;
-  block_acquire();
-  if (threadIdx.x < T) {  // tile sums added in tile order
-    float tot = 0.0f;
-    for (int i = 0; i < n_tiles; i++) tot += a.ssq[(size_t)threadIdx.x * n_tiles + i];
-    red[threadIdx.x] = 1.0f / sqrtf(tot / (float)H + a.eps);
-  }
+  if (comb && (v % sbk::RT) == 0) a.ssq[(size_t)(v / sbk::RT) * gridDim.x + tile] = ss;
+}
+
+// ============================================================ K4: RMSNorm
+
+// y_norm[t] = y[t] / sqrt(sum(y[t]^2) / H + eps) for the next layer of a
+// pre-norm stack (unit gain).  Workgroup (t, c): every workgroup of token t
+// adds the n_tiles partial sums in the same fixed order (strided per thread,
+// then the DPP wave sum, then the 4 waves in order) and scales 1024 values.
+__global__ void __launch_bounds__(256) k_norm_small(LayerArgs a, int n_tiles) {
+  __shared__ float wsum[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  float p = 0.0f;
+  for (int i = tid; i < n_tiles; i += 256) p += a.ssq[(size_t)t * n_tiles + i];
+  p = wave_sum(p);
+  if ((tid & 63) == 0) wsum[tid >> 6] = p;
   __syncthreads();
-  for (int i = threadIdx.x; i < T * (H / 4); i += 256) {
-    const int t = i / (H / 4);
-    float4 y4 = reinterpret_cast<const float4 *>(a.y)[i];
-    const float inv = red[t];
+  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+  const float inv = 1.0f / sqrtf(tot / (float)a.H + a.eps);
+  const int j = blockIdx.y * 1024 + tid * 4;
+  if (j < a.H) {
+    float4 y4 = *reinterpret_cast<const float4 *>(a.y + (size_t)t * a.H + j);
     y4.x *= inv;
     y4.y *= inv;
     y4.z *= inv;
     y4.w *= inv;
-    reinterpret_cast<float4 *>(a.y_norm)[i] = y4;
+    *reinterpret_cast<float4 *>(a.y_norm + (size_t)t * a.H + j) = y4;
   }
-  if (threadIdx.x == 0) *sctr(a, sbk::C_NORM) = 0u;
 }
 
 // ============================================================ launch
@@ -879,6 +854,9 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
   const size_t lds3 = (size_t)4 * P * sbk::RT * sizeof(float) + (size_t)a.n_slots_ub * TAB_W * 4;
   launch_k(k_down_small<WB, TT, NPD, (TT == 1 ? MOE_K3_SLOTS : 2)>, dim3(a.H / sbk::RT),
            dim3(256), (uint32_t)lds3, st, stage_ev(ev, MOE_STAGE_DOWN), a);
+  if (a.y_norm)
+    launch_k(k_norm_small, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, st,
+             stage_ev(ev, MOE_STAGE_COMBINE), a, a.H / sbk::RT);
 }
 
 template <int WB, int TT>
