@@ -628,7 +628,7 @@ __global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
   if (n_tok == 0) return;
   const int e = min(max(ent[0], 0), a.E - 1);
   const int *pairs = ent + 2, *toks = ent + 2 + sbk::TMAX;
-  gate_up_rows<WB, TT, NPL, (TT == 1 ? MOE_K2_ROWS : 1)>(
+  gate_up_rows<WB, TT, NPL, (TT == 1 ? (WB == 2 ? 2 * MOE_K2_ROWS : MOE_K2_ROWS) : 1)>(
       a, hb, a.experts + (size_t)e * a.blob_bytes, blk, n_tok, pairs,
       [&](int i) { return (const int8_t *)(a.q + (size_t)min(max(toks[i], 0), a.T - 1) * a.H); },
       [&](int i) {
@@ -647,11 +647,24 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Sum over each group of 8 lanes (quads, then the half-row mirror).
+__device__ __forceinline__ float row8_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror: lane i + lane 7-i of each 8
+  return v;
+}
+
+template <int LPR>
+__device__ __forceinline__ float lane_row_sum(float v) {
+  return LPR == 16 ? row16_sum(v) : row8_sum(v);
+}
+
 constexpr int TAB_W = 2 + sbk::TMAX;  // expert, count, pairs: what the down kernel reads
 
 // Activations of pairs prs[c0 .. c0+TT) (pair ids clamped, -1 past n_tok)
-// for the pieces qb + pl + 16 i of a quarter of nq pieces.
-template <int WB, int TT, int NPQ>
+// for the pieces qb + pl + LPR i of a quarter of nq pieces.
+template <int WB, int TT, int NPQ, int LPR>
 __device__ __forceinline__ void down_act(const LayerArgs &a, const int *prs, int n_tok, int c0,
                                          int P, int qb, int nq, int pl, Act<WB> (&act)[NPQ][TT],
                                          int (&pair)[TT]) {
@@ -662,21 +675,22 @@ __device__ __forceinline__ void down_act(const LayerArgs &a, const int *prs, int
     const int pp = pair[t] >= 0 ? pair[t] : 0;
 #pragma unroll
     for (int i = 0; i < NPQ; i++) {
-      const int q = pl + 16 * i;
+      const int q = pl + LPR * i;
       load_act<WB>(a.qh + (size_t)pp * I, a.dh + (size_t)pp * (I / 32), qb + q,
                    pair[t] >= 0 && q < nq, act[i][t]);
     }
   }
 }
 
-// Two rows (l/16, l/16 + 4) of one slot for TT pairs: quarter partials into
-// part[wv][pair][row].
-template <int WB, int TT, int NPQ>
+// The RPL = LPR/8 rows of lane row rl (rl, rl + 64/LPR) of one slot for TT
+// pairs: quarter partials into part[wv][pair][row].
+template <int WB, int TT, int NPQ, int LPR>
 __device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, int pl,
-                                          const uint4 (&w)[2][NPQ], const float (&sd)[2],
+                                          const uint4 (&w)[LPR / 8][NPQ],
+                                          const float (&sd)[LPR / 8],
                                           const Act<WB> (&act)[NPQ][TT], const int (&pair)[TT]) {
 #pragma unroll
-  for (int rr = 0; rr < 2; rr++) {
+  for (int rr = 0; rr < LPR / 8; rr++) {
     float acc[TT];
 #pragma unroll
     for (int t = 0; t < TT; t++) acc[t] = 0.0f;
@@ -687,22 +701,26 @@ __device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, in
     }
 #pragma unroll
     for (int t = 0; t < TT; t++) {
-      const float yv = sd[rr] * row16_sum(acc[t]);
-      if (pl == 0 && pair[t] >= 0) part[((size_t)wv * P + pair[t]) * sbk::RT + rl + 4 * rr] = yv;
+      const float yv = sd[rr] * lane_row_sum<LPR>(acc[t]);
+      if (pl == 0 && pair[t] >= 0)
+        part[((size_t)wv * P + pair[t]) * sbk::RT + rl + (64 / LPR) * rr] = yv;
     }
   }
 }
 
 // Block `tile`: output rows 8 tile .. 8 tile + 7 of every expert slot for
 // every token.  Wave wv covers all 8 rows over quarter wv of the I
-// dimension (pieces [wv n/4, (wv+1) n/4) of the row's n): lane l takes rows
-// l/16 and l/16 + 4 and the pieces l%16 (+16 i) of the quarter, so the 4 lane rows of a wave share each activation
-// piece (one cache-line request for all four).  Rows are reduced over 16
-// lanes; the 4 quarters land in LDS and are added in quarter order in the
-// combine, which runs in rank order:
+// dimension (pieces [wv n/4, (wv+1) n/4) of the row's n) with LPR lanes per
+// row: lane l takes rows l/LPR (+ 64/LPR) and the pieces l%LPR (+LPR i) of
+// the quarter, so the lane rows of a wave share each activation piece (one
+// cache-line request for all).  LPR = 8 when a quarter has at most 8 pieces,
+// so that every lane loads.  Rows are reduced over their LPR lanes; the 4
+// quarters land in LDS and are added in quarter order in the combine, which
+// runs in rank order:
 //   y[t] = residual[t] + shared[t] + sum_k w[t,k] * expert_k[t]
-template <int WB, int TT, int NPQ, int SB>
+template <int WB, int TT, int NPQ, int SB, int LPR>
 __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
+  constexpr int RPL = LPR / 8;  // rows per lane
   extern __shared__ __align__(16) uint8_t dyn[];
   __shared__ float wsh[256];
   const int tile = blockIdx.x, tid = threadIdx.x;
@@ -715,7 +733,7 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   const int qb = wv * npieces / 4, nq = (wv + 1) * npieces / 4 - qb;  // this wave's quarter
   const size_t row_b = (size_t)I * WB / 8;
   const size_t down_off = 2 * (size_t)I * ((size_t)H * WB / 8);
-  const int rl = lane >> 4, pl = lane & 15;
+  const int rl = lane / LPR, pl = lane % LPR;
   const int j0 = tile * sbk::RT;
   for (int i = tid; i < a.n_slots_ub * TAB_W; i += 256)
     tab[i] = a.slots[(size_t)(i / TAB_W) * SLOT_W + i % TAB_W];
@@ -729,8 +747,8 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   while (n_slots < a.n_slots_ub && tab[n_slots * TAB_W + 1] > 0) n_slots++;
 
   for (int s0 = 0; s0 < n_slots; s0 += SB) {
-    uint4 wd[SB][2][NPQ];
-    float sd[SB][2];
+    uint4 wd[SB][RPL][NPQ];
+    float sd[SB][RPL];
 #pragma unroll
     for (int b = 0; b < SB; b++) {
       const bool ok_s = s0 + b < n_slots;
@@ -741,11 +759,11 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
       const float *sdp =
           reinterpret_cast<const float *>(blob + 3 * (size_t)I * ((size_t)H * WB / 8)) + 2 * I;
 #pragma unroll
-      for (int rr = 0; rr < 2; rr++) {
-        const int row = j0 + rl + 4 * rr;
+      for (int rr = 0; rr < RPL; rr++) {
+        const int row = j0 + rl + (64 / LPR) * rr;
 #pragma unroll
         for (int i = 0; i < NPQ; i++) {
-          const int q = pl + 16 * i;
+          const int q = pl + LPR * i;
           wd[b][rr][i] = (ok_s && q < nq)
                              ? reinterpret_cast<const uint4 *>(down + (size_t)row * row_b)[qb + q]
                              : make_uint4(0, 0, 0, 0);
@@ -759,19 +777,19 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
 #pragma unroll
     for (int b = 0; b < SB; b++) {
       const int n_tok = (s0 + b < n_slots) ? min(tab[(s0 + b) * TAB_W + 1], T) : 0;
-      down_act<WB, TT, NPQ>(a, tab + (s0 + b) * TAB_W + 2, n_tok, 0, P, qb, nq, pl, act0[b],
-                            pair0[b]);
+      down_act<WB, TT, NPQ, LPR>(a, tab + (s0 + b) * TAB_W + 2, n_tok, 0, P, qb, nq, pl,
+                                 act0[b], pair0[b]);
     }
 #pragma unroll
     for (int b = 0; b < SB; b++) {
       const int n_tok = (s0 + b < n_slots) ? min(tab[(s0 + b) * TAB_W + 1], T) : 0;
-      down_rows<WB, TT, NPQ>(part, P, wv, rl, pl, wd[b], sd[b], act0[b], pair0[b]);
+      down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, wd[b], sd[b], act0[b], pair0[b]);
       for (int c0 = TT; c0 < n_tok; c0 += TT) {
         Act<WB> act[NPQ][TT];
         int pair[TT];
-        down_act<WB, TT, NPQ>(a, tab + (s0 + b) * TAB_W + 2, n_tok, c0, P, qb, nq, pl, act,
-                              pair);
-        down_rows<WB, TT, NPQ>(part, P, wv, rl, pl, wd[b], sd[b], act, pair);
+        down_act<WB, TT, NPQ, LPR>(a, tab + (s0 + b) * TAB_W + 2, n_tok, c0, P, qb, nq, pl, act,
+                                   pair);
+        down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, wd[b], sd[b], act, pair);
       }
     }
   }
@@ -852,8 +870,14 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
            st, stage_ev(ev, MOE_STAGE_GATE_UP), a);
   const int P = a.T * (a.K + a.n_shared);
   const size_t lds3 = (size_t)4 * P * sbk::RT * sizeof(float) + (size_t)a.n_slots_ub * TAB_W * 4;
-  launch_k(k_down_small<WB, TT, NPD, (TT == 1 ? MOE_K3_SLOTS : 2)>, dim3(a.H / sbk::RT),
-           dim3(256), (uint32_t)lds3, st, stage_ev(ev, MOE_STAGE_DOWN), a);
+  constexpr int SB = TT == 1 ? (WB == 2 ? 2 * MOE_K3_SLOTS : MOE_K3_SLOTS) : 2;
+  const int quarter = (a.I / (128 / WB) + 3) / 4;
+  if (quarter <= 8)
+    launch_k(k_down_small<WB, TT, 1, SB, 8>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3, st,
+             stage_ev(ev, MOE_STAGE_DOWN), a);
+  else
+    launch_k(k_down_small<WB, TT, NPD, SB, 16>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
+             st, stage_ev(ev, MOE_STAGE_DOWN), a);
   if (a.y_norm)
     launch_k(k_norm_small, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, st,
              stage_ev(ev, MOE_STAGE_COMBINE), a, a.H / sbk::RT);
@@ -876,8 +900,10 @@ void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev) {
     if (a.T == 1) launch3_np<4, 1>(a, st, ev);
     else launch3_np<4, 4>(a, st, ev);
   } else {
+    // an int2 activation fragment covers 64 codes: two tokens per chunk keep
+    // the registers within two waves per SIMD
     if (a.T == 1) launch3_np<2, 1>(a, st, ev);
-    else launch3_np<2, 4>(a, st, ev);
+    else launch3_np<2, 2>(a, st, ev);
   }
 }
 
