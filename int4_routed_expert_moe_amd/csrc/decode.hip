@@ -36,6 +36,10 @@ namespace moe {
 #ifndef MOE_K3_SLOTS
 #define MOE_K3_SLOTS 2
 #endif
+// tokens per chunk of the down kernel for batches of more than one token
+#ifndef MOE_K3_TT
+#define MOE_K3_TT 2
+#endif
 // gate/up rows (each a gate and an up row) a K2 wave loads together: 1, 2, 4, 8
 #ifndef MOE_K2_ROWS
 #define MOE_K2_ROWS 2
@@ -871,12 +875,13 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
   const int P = a.T * (a.K + a.n_shared);
   const size_t lds3 = (size_t)4 * P * sbk::RT * sizeof(float) + (size_t)a.n_slots_ub * TAB_W * 4;
   constexpr int SB = TT == 1 ? (WB == 2 ? 2 * MOE_K3_SLOTS : MOE_K3_SLOTS) : 2;
+  constexpr int TT3 = TT == 1 ? 1 : MOE_K3_TT;  // tokens per chunk in the down kernel
   const int quarter = (a.I / (128 / WB) + 3) / 4;
   if (quarter <= 8)
-    launch_k(k_down_small<WB, TT, 1, SB, 8>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3, st,
-             stage_ev(ev, MOE_STAGE_DOWN), a);
+    launch_k(k_down_small<WB, TT3, 1, SB, 8>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
+             st, stage_ev(ev, MOE_STAGE_DOWN), a);
   else
-    launch_k(k_down_small<WB, TT, NPD, SB, 16>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
+    launch_k(k_down_small<WB, TT3, NPD, SB, 16>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
              st, stage_ev(ev, MOE_STAGE_DOWN), a);
   if (a.y_norm)
     launch_k(k_norm_small, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, st,
