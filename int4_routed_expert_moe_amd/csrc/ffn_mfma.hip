@@ -209,9 +209,10 @@ __device__ __forceinline__ void store_w_chunk(const WChunk<NM> &r, uint8_t *as) 
 
 // The K loop shared by both kernels: NM weight matrices (gate+up: 2, down:
 // 1) times the tile's activations; acc[m][s][i] = sum_b d*P for matrix m,
-// token sub-tile s (16 tokens), row 16 wv + 4 g + i.  DBG: raw block dots of
+// token sub-tile s (16 tokens, s < NS: the sub-tiles that hold tokens, fixed
+// per workgroup so the loop body has no branches), row 16 wv + 4 g + i.  DBG: raw block dots of
 // matrix m go to dots[m] at ((pair * R + row) * nblk + block).
-template <int NM, bool DBG>
+template <int NM, bool DBG, int NS>
 __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, const int8_t *q,
                            const float *d, int row_len, const int *tokl, const int *pairl, int n,
                            int nblk, uint8_t *bs, float *ds, uint8_t *as, float (&acc)[NM][4][4],
@@ -248,8 +249,7 @@ __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, cons
         af[m] = a_frag(w);
       }
 #pragma unroll
-      for (int s = 0; s < 4; s++) {
-        if (s * 16 >= n) break;  // sub-tiles past the work item's tokens (uniform)
+      for (int s = 0; s < NS; s++) {  // only the sub-tiles that hold tokens
         const int col = s * 16 + m16;
         const long bf = *reinterpret_cast<const long *>(bs + col * mf::BSTR + b * 32 + g * 8);
         const float dd = ds[col * mf::CB + b];
@@ -270,6 +270,31 @@ __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, cons
         }
       }
     }
+  }
+}
+
+// mfma_kloop with the sub-tile count of n tokens chosen once.
+template <int NM, bool DBG>
+__device__ void mfma_kloop_n(const uint8_t *const *mat, size_t row_b, int r0, const int8_t *q,
+                             const float *d, int row_len, const int *tokl, const int *pairl,
+                             int n, int nblk, uint8_t *bs, float *ds, uint8_t *as,
+                             float (&acc)[NM][4][4], int32_t *const *dots, int R) {
+  switch ((n + 15) / 16) {
+    case 1:
+      mfma_kloop<NM, DBG, 1>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds, as, acc,
+                             dots, R);
+      break;
+    case 2:
+      mfma_kloop<NM, DBG, 2>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds, as, acc,
+                             dots, R);
+      break;
+    case 3:
+      mfma_kloop<NM, DBG, 3>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds, as, acc,
+                             dots, R);
+      break;
+    default:
+      mfma_kloop<NM, DBG, 4>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds, as, acc,
+                             dots, R);
   }
 }
 
@@ -305,8 +330,8 @@ __global__ void __launch_bounds__(256, 3) k_gate_up_mfma(FfnArgs a, const int4 *
   const uint8_t *mats[2] = {ti.blob, ti.blob + (size_t)I * row_b};
   float acc[2][4][4];
   int32_t *dots[2] = {a.dbg.gate_dots, a.dbg.up_dots};
-  mfma_kloop<2, DBG>(mats, row_b, r0, a.q, a.d, H, tokl, pairl, ti.n, H / 32, bs, ds, as, acc,
-                     dots, I);
+  mfma_kloop_n<2, DBG>(mats, row_b, r0, a.q, a.d, H, tokl, pairl, ti.n, H / 32, bs, ds, as, acc,
+                       dots, I);
   // epilogue: h into LDS as [token][64 rows] fp32 (reuses the activation tile)
   const float *scales = reinterpret_cast<const float *>(ti.blob + 3 * (size_t)I * row_b);
   __syncthreads();
@@ -381,8 +406,8 @@ __global__ void __launch_bounds__(256) k_down_mfma(FfnArgs a, const int4 *tiles,
   const uint8_t *mats[1] = {ti.blob + 2 * (size_t)I * ((size_t)H / 2)};
   float acc[1][4][4];
   int32_t *dots[1] = {a.dbg.down_dots};
-  mfma_kloop<1, DBG>(mats, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs, ds, as, acc,
-                     dots, H);
+  mfma_kloop_n<1, DBG>(mats, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs, ds, as, acc,
+                       dots, H);
   const float *sd =
       reinterpret_cast<const float *>(ti.blob + 3 * (size_t)I * ((size_t)H / 2)) + 2 * I;
   const int m16 = lane & 15, g = lane >> 4;
