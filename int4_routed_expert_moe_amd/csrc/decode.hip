@@ -739,6 +739,33 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   const size_t down_off = 2 * (size_t)I * ((size_t)H * WB / 8);
   const int rl = lane / LPR, pl = lane % LPR;
   const int j0 = tile * sbk::RT;
+  // The shared expert (slot 0 when present) needs nothing from the slot
+  // table: its rows and its first TT pairs are requested before the table.
+  int shp[sbk::TMAX];  // its pair ids T*K + t
+#pragma unroll
+  for (int t = 0; t < sbk::TMAX; t++) shp[t] = T * K + t;
+  const int S0 = a.n_shared;
+  uint4 ws0[RPL][NPQ];
+  float sd0[RPL];
+  Act<WB> act_s[NPQ][TT];
+  int pair_s[TT];
+  if (S0) {
+    const uint8_t *down = a.shared + down_off;
+    const float *sdp =
+        reinterpret_cast<const float *>(a.shared + 3 * (size_t)I * ((size_t)H * WB / 8)) + 2 * I;
+#pragma unroll
+    for (int rr = 0; rr < RPL; rr++) {
+      const int row = j0 + rl + (64 / LPR) * rr;
+#pragma unroll
+      for (int i = 0; i < NPQ; i++) {
+        const int q = pl + LPR * i;
+        ws0[rr][i] = q < nq ? reinterpret_cast<const uint4 *>(down + (size_t)row * row_b)[qb + q]
+                            : make_uint4(0, 0, 0, 0);
+      }
+      sd0[rr] = sdp[row];
+    }
+    down_act<WB, TT, NPQ, LPR>(a, shp, T, 0, P, qb, nq, pl, act_s, pair_s);
+  }
   for (int i = tid; i < a.n_slots_ub * TAB_W; i += 256)
     tab[i] = a.slots[(size_t)(i / TAB_W) * SLOT_W + i % TAB_W];
   if (tid < T * K) wsh[tid] = a.w[tid];
@@ -750,7 +777,16 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   int n_slots = 0;
   while (n_slots < a.n_slots_ub && tab[n_slots * TAB_W + 1] > 0) n_slots++;
 
-  for (int s0 = 0; s0 < n_slots; s0 += SB) {
+  if (S0) {  // the shared slot, from the registers filled above
+    down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, ws0, sd0, act_s, pair_s);
+    for (int c0 = TT; c0 < T; c0 += TT) {
+      Act<WB> act[NPQ][TT];
+      int pair[TT];
+      down_act<WB, TT, NPQ, LPR>(a, shp, T, c0, P, qb, nq, pl, act, pair);
+      down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, ws0, sd0, act, pair);
+    }
+  }
+  for (int s0 = S0; s0 < n_slots; s0 += SB) {
     uint4 wd[SB][RPL][NPQ];
     float sd[SB][RPL];
 #pragma unroll
