@@ -78,6 +78,10 @@ void oracle_unpack(const uint8_t *row, int wbits, int n, int8_t *out) {
 
 /* Inverse of oracle_code over a row of n codes (used by the pins). */
 int oracle_pack(const int8_t *codes, int n, int wbits, uint8_t *out) {
+  if (wbits == 8) {  /* one two's-complement byte per code */
+    for (int k = 0; k < n; k++) out[k] = (uint8_t)codes[k];
+    return 0;
+  }
   if (wbits != 4 && wbits != 2) return -1;
   const int per = 8 / wbits;
   if (n % per) return -1;

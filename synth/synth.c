@@ -20,14 +20,16 @@
  *                  (Irwin–Hall sum of 12 uniforms: mean 0, variance ~1, |z| <= 6)
  *   uniform(key,i) = (draw(key,i) >> 40) * 2^-24  in [0,1)
  *
- * Packed weight record of one expert (wbits = 4 or 2), rows of the three
+ * Packed weight record of one expert (wbits = 8, 4 or 2), rows of the three
  * matrices followed by their fp32 per-row scales:
  *   gate codes [I][H*wbits/8] | up codes [I][H*wbits/8] | down codes [H][I*wbits/8]
  *   | gate scale [I] | up scale [I] | down scale [H]
  * int4: element 2j in the low nibble of byte j, 2j+1 in the high nibble,
- *       two's complement; int2: element 4j+i in bits 2i..2i+1, two's complement.
- * Row quantiser: amax = max|w|, s = amax / qdiv (qdiv 7 for int4, 2 for int2),
- *   code = clamp(roundf(w / s), qlo, qhi) (int4: [-8,7], int2: [-2,1]); s = 0 -> codes 0.
+ *       two's complement; int2: element 4j+i in bits 2i..2i+1, two's complement;
+ *       int8: one two's-complement byte per element.
+ * Row quantiser: amax = max|w|, s = amax / qdiv (qdiv 127 for int8, 7 for
+ *   int4, 2 for int2), code = clamp(roundf(w / s), qlo, qhi) (int8: [-127,127],
+ *   int4: [-8,7], int2: [-2,1]); s = 0 -> codes 0.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
  */
@@ -99,8 +101,9 @@ static void quant_row(uint64_t key, uint64_t row, int n, int wbits, float sigma,
     wbuf[c] = w;
     amax = fmaxf(amax, fabsf(w));
   }
-  const float qdiv = (wbits == 4) ? 7.0f : 2.0f;
-  const int qlo = (wbits == 4) ? -8 : -2, qhi = (wbits == 4) ? 7 : 1;
+  const float qdiv = (wbits == 8) ? 127.0f : (wbits == 4) ? 7.0f : 2.0f;
+  const int qlo = (wbits == 8) ? -127 : (wbits == 4) ? -8 : -2;
+  const int qhi = (wbits == 8) ? 127 : (wbits == 4) ? 7 : 1;
   float s = amax / qdiv;
   *scale = s;
   const int per = 8 / wbits;
@@ -132,7 +135,7 @@ void synth_weight_row(uint64_t seed, uint32_t layer, uint32_t expert,
 /* Expert record for (seed, layer, expert); matrix m = 0 gate, 1 up, 2 down. */
 int synth_expert_blob(uint64_t seed, uint32_t layer, uint32_t expert, int H,
                       int I, int wbits, float sigma, uint8_t *blob) {
-  if ((wbits != 4 && wbits != 2) || H <= 0 || I <= 0 || H % 8 || I % 8) return -1;
+  if ((wbits != 8 && wbits != 4 && wbits != 2) || H <= 0 || I <= 0 || H % 8 || I % 8) return -1;
   const size_t gate_b = (size_t)I * H * wbits / 8;
   const size_t down_b = (size_t)H * I * wbits / 8;
   uint8_t *codes[3] = {blob, blob + gate_b, blob + 2 * gate_b};

@@ -68,8 +68,9 @@ k_synth_rows(MatJob job, int n, int wbits, float sigma) {
     __syncthreads();
   }
   amax = red[0];
-  const float qdiv = (wbits == 4) ? 7.0f : 2.0f;
-  const int qlo = (wbits == 4) ? -8 : -2, qhi = (wbits == 4) ? 7 : 1;
+  const float qdiv = (wbits == 8) ? 127.0f : (wbits == 4) ? 7.0f : 2.0f;
+  const int qlo = (wbits == 8) ? -127 : (wbits == 4) ? -8 : -2;
+  const int qhi = (wbits == 8) ? 127 : (wbits == 4) ? 7 : 1;
   const float s = amax / qdiv;
   const int per = 8 / wbits;
   const unsigned mask = (1u << wbits) - 1u;
@@ -98,7 +99,7 @@ extern "C" {
 int synth_gpu_expert_blobs(uint64_t seed, uint32_t layer, const uint32_t *expert_ids,
                            int n_experts, int H, int I, int wbits, float sigma,
                            void *out, size_t stride, void *stream) {
-  if ((wbits != 4 && wbits != 2) || H <= 0 || I <= 0 || H % 8 || I % 8 ||
+  if ((wbits != 8 && wbits != 4 && wbits != 2) || H <= 0 || I <= 0 || H % 8 || I % 8 ||
       n_experts < 0 || !out || H > 16384 || I > 16384)
     return -1;
   hipStream_t st = (hipStream_t)stream;

@@ -32,7 +32,7 @@ def _half_away(v):
 
 # ------------------------------------------------------------------ packed codes
 
-@pytest.mark.parametrize("wbits", [4, 2])
+@pytest.mark.parametrize("wbits", [4, 2, 8])
 def test_codes_match_hand_table(wbits):
     for case in _load("packed_codes.json")[f"int{wbits}"]:
         row = np.array([case["byte"]], np.uint8)
@@ -40,13 +40,17 @@ def test_codes_match_hand_table(wbits):
         assert got == case["codes"], case["derivation"]
 
 
-@pytest.mark.parametrize("wbits", [4, 2])
+def _code_range(wbits):
+    return {8: (-128, 127), 4: (-8, 7), 2: (-2, 1)}[wbits]
+
+
+@pytest.mark.parametrize("wbits", [4, 2, 8])
 def test_pack_unpack_round_trip_exhaustive(wbits):
     per = 8 // wbits
     allbytes = np.arange(256, dtype=np.uint8)
     codes = oracle.unpack(allbytes, wbits, 256 * per)
     assert np.array_equal(oracle.pack(codes, wbits), allbytes)
-    lo, hi = (-8, 7) if wbits == 4 else (-2, 1)
+    lo, hi = _code_range(wbits)
     tuples = np.array(list(itertools.product(range(lo, hi + 1), repeat=per)), np.int8).ravel()
     packed = oracle.pack(tuples, wbits)
     assert np.array_equal(oracle.unpack(packed, wbits, tuples.size), tuples)
@@ -54,7 +58,7 @@ def test_pack_unpack_round_trip_exhaustive(wbits):
     assert sorted(packed.tolist()) == list(range(256))
 
 
-@pytest.mark.parametrize("wbits", [4, 2])
+@pytest.mark.parametrize("wbits", [4, 2, 8])
 def test_generated_record_decodes_to_rounded_weights(wbits):
     """The generator's packed rows, read back by the oracle, equal a numpy
     re-quantisation of the generator's float rows (two independent codes)."""
@@ -62,7 +66,7 @@ def test_generated_record_decodes_to_rounded_weights(wbits):
     H, I = shape.hidden, shape.inter
     blob = synth.expert_blob(shape, 7, 3, 5)
     gate, up, down, sg, su, sd = oracle.blob_view(blob, H, I, wbits)
-    qdiv, lo, hi = (7.0, -8, 7) if wbits == 4 else (2.0, -2, 1)
+    qdiv, lo, hi = {4: (7.0, -8, 7), 2: (2.0, -2, 1), 8: (127.0, -127, 127)}[wbits]
     for m, (rows, sc, n) in enumerate([(gate, sg, H), (up, su, H), (down, sd, I)]):
         for r in (0, 1, rows.shape[0] - 1):
             w = synth.weight_row(7, 3, 5, m, n, r)
@@ -77,7 +81,9 @@ def test_record_size_matches_nineteen_megabytes():
     streaming section) -> 3*6144*2048/2 code bytes + fp32 row scales."""
     assert oracle.blob_bytes(6144, 2048, 4) == 18_915_328
     assert oracle.blob_bytes(6144, 2048, 2) == 9_478_144
+    assert oracle.blob_bytes(6144, 2048, 8) == 37_789_696  # int8 experts: 3*6144*2048 + scales
     assert synth.blob_bytes(synth.REAL) == 18_915_328
+    assert synth.blob_bytes(synth.REAL.with_bits(8)) == 37_789_696
 
 
 # ------------------------------------------------------------------ integer dots
@@ -94,10 +100,10 @@ def test_block_dot_single_product_table():
             assert oracle.block_dots(row, 4, q)[0] == c * v
 
 
-@pytest.mark.parametrize("wbits", [4, 2])
+@pytest.mark.parametrize("wbits", [4, 2, 8])
 def test_block_dots_vs_numpy_int64(wbits):
     rng = np.random.default_rng(1)
-    lo, hi = (-8, 7) if wbits == 4 else (-2, 1)
+    lo, hi = _code_range(wbits)
     n = 32 * 40
     codes = rng.integers(lo, hi + 1, n).astype(np.int8)
     q = rng.integers(-127, 128, n).astype(np.int8)
@@ -325,7 +331,7 @@ def _tiny_inputs(seed=12, T=3, wbits=4):
     return shape, blob, x, q, d
 
 
-@pytest.mark.parametrize("wbits", [4, 2])
+@pytest.mark.parametrize("wbits", [4, 2, 8])
 def test_gate_up_equals_dequantised_matmul(wbits):
     """Integer block dots rescaled == fp64 matmul of dequantised weights and
     dequantised activations (algebraic identity), and h = silu(g) * u."""
@@ -350,7 +356,7 @@ def test_gate_up_equals_dequantised_matmul(wbits):
         assert np.array_equal(out["gate_dots"], want)
 
 
-@pytest.mark.parametrize("wbits", [4, 2])
+@pytest.mark.parametrize("wbits", [4, 2, 8])
 def test_down_equals_dequantised_matmul(wbits):
     shape, blob, x, q, d = _tiny_inputs(wbits=wbits)
     H, I = shape.hidden, shape.inter
