@@ -224,7 +224,7 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--wbits", type=int, default=4, choices=(4, 2))
+    ap.add_argument("--wbits", type=int, default=4, choices=(8, 4, 2))
     ap.add_argument("--ring", type=int, default=0, help="layer instances to cycle (0 = default)")
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly")
     ap.add_argument("--graph-block", type=int, default=64, help="steps per captured graph")

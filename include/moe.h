@@ -44,6 +44,8 @@
  *       gate codes [I][H*wbits/8] | up codes [I][H*wbits/8] |
  *       down codes [H][I*wbits/8] | gate scale fp32 [I] | up scale fp32 [I] |
  *       down scale fp32 [H]
+ *     int8: element j in byte j, codes in [-127, 127] (-128 is not
+ *     produced by the quantiser but is accepted);
  *     int4: element 2j in the low nibble of byte j, 2j+1 in the high nibble;
  *     int2: element 4j+i in bits 2i..2i+1; codes are two's complement and
  *     every bit pattern is a valid code.  Weight value = scale[row] * code.
@@ -71,7 +73,9 @@ extern "C" {
  * 2 <= n_experts <= 1024, n_experts % n_group == 0 with at least 2 experts
  * per group, n_group <= 64, 1 <= topk_group <= n_group,
  * 1 <= top_k <= min(16, topk_group * n_experts / n_group), n_shared in {0,1},
- * wbits in {4, 2}. */
+ * wbits in {8, 4, 2}; a weight row holds at most 256 16-byte pieces of codes
+ * (448 for int8) along hidden and 128 along inter, i.e. hidden <= 8192 and
+ * inter <= 4096 for int4 (16384 / 8192 for int2, 7168 / 2048 for int8). */
 typedef struct moe_cfg {
   int32_t hidden;       /* H */
   int32_t inter;        /* I, intermediate width of every expert (shared too) */
@@ -80,7 +84,7 @@ typedef struct moe_cfg {
   int32_t topk_group;   /* TG, groups kept per token */
   int32_t top_k;        /* K, routed experts per token */
   int32_t n_shared;     /* 0 or 1 shared expert */
-  int32_t wbits;        /* 4 (packed int4) or 2 (packed int2) */
+  int32_t wbits;        /* 8 (int8), 4 (packed int4) or 2 (packed int2) */
   float routed_scaling; /* routed_scaling_factor applied to routed weights */
 } moe_cfg;
 

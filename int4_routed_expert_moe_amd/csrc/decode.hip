@@ -318,9 +318,30 @@ struct Act<2> {
   float da, db;  // scales / 64 of the two blocks of a 64-code piece
 };
 
+template <>
+struct Act<8> {
+  int q[4];  // 16 activations (half a Q8_0 block), natural order
+  float d;   // the block's scale
+};
+
 template <int WB>
 __device__ __forceinline__ void load_act(const int8_t *q, const float *d, int p, bool ok,
                                          Act<WB> &o);
+template <>
+__device__ __forceinline__ void load_act<8>(const int8_t *q, const float *d, int p, bool ok,
+                                            Act<8> &o) {
+  uint4 x = make_uint4(0, 0, 0, 0);
+  float dd = 0.0f;
+  if (ok) {
+    x = reinterpret_cast<const uint4 *>(q)[p];
+    dd = d[p >> 1];
+  }
+  o.q[0] = (int)x.x;
+  o.q[1] = (int)x.y;
+  o.q[2] = (int)x.z;
+  o.q[3] = (int)x.w;
+  o.d = dd;
+}
 template <>
 __device__ __forceinline__ void load_act<4>(const int8_t *q, const float *d, int p, bool ok,
                                             Act<4> &o) {
@@ -366,6 +387,14 @@ __device__ __forceinline__ void load_act<2>(const int8_t *q, const float *d, int
 template <int WB>
 __device__ __forceinline__ float piece_dot(const uint4 w, const Act<WB> &a);
 template <>
+__device__ __forceinline__ float piece_dot<8>(const uint4 w, const Act<8> &a) {
+  int acc = sdot4((int)w.x, a.q[0], 0);  // 16 int8 codes: exact, |acc| < 2^19
+  acc = sdot4((int)w.y, a.q[1], acc);
+  acc = sdot4((int)w.z, a.q[2], acc);
+  acc = sdot4((int)w.w, a.q[3], acc);
+  return (float)acc * a.d;
+}
+template <>
 __device__ __forceinline__ float piece_dot<4>(const uint4 w, const Act<4> &a) {
   return (float)dot_int4_block16(w, a.q) * a.d;
 }
@@ -384,25 +413,32 @@ __device__ __forceinline__ float piece_dot<2>(const uint4 w, const Act<2> &a) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
-// 32 rows of h (rows 32 blk ..) for one expert and n_tok tokens.  Wave wv
-// streams rows 8wv .. 8wv+7 in batches of RB rows (a gate and an up row
-// each), double-buffered.  Activations of token i: Q8_0 codes/scales at
-// qrow(i)/drow(i).  h goes to LDS; each token's 32 values become one Q8_0
-// block of q_h.
-template <int WB, int TT, int NPL, int RB, class QRow, class DRow>
+// 32 rows of h (rows 32 blk ..) for one expert and n_tok tokens.  KS = 1:
+// wave wv streams rows 8wv .. 8wv+7 whole; KS = 2 (long int8 rows): waves
+// wv and wv+2 stream rows 16(wv&1) .. +15, each over one half of the hidden
+// dimension, and the halves are added in LDS.  Rows go in batches of RB (a
+// gate and an up row each), double-buffered.  Activations of token i: Q8_0
+// codes/scales at qrow(i)/drow(i).  h goes to LDS; each token's 32 values
+// become one Q8_0 block of q_h.
+template <int WB, int TT, int NPL, int RB, int KS, class QRow, class DRow>
 __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t *blob, int blk,
                              int n_tok, const int *pairs, QRow qrow, DRow drow) {
+  static_assert(KS == 1 || KS == 2, "K split");
+  __shared__ float part[KS][TT][32][2];  // KS = 2: scaled half sums (gate, up)
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, I = a.I;
-  const int npieces = H / (128 / WB);
+  constexpr int RW = 8 * KS;  // rows per wave
+  const int khalf = wv / (4 / KS), wr = wv % (4 / KS);
+  const int np_all = H / (128 / WB), np_half = (np_all + KS - 1) / KS;
+  const int p0 = khalf * np_half, npieces = min(np_all, p0 + np_half);
   const size_t row_b = (size_t)H * WB / 8;
   const uint8_t *gate = blob;
   const uint8_t *up = blob + (size_t)I * row_b;
   const float *scales = reinterpret_cast<const float *>(blob + 3 * (size_t)I * row_b);
-  const int rbase = blk * 32 + wv * 8;
-  // row scales of the wave's 8 rows: lane l < 8 gate row l, 8 <= l < 16 up row l-8
-  const float sc = lane < 16 ? scales[(lane < 8 ? 0 : I) + rbase + (lane & 7)] : 0.0f;
-  constexpr int NB = 8 / RB;
+  const int rbase = blk * 32 + wr * RW;
+  // row scales of the wave's rows: lane l < RW gate row l, RW <= l < 2 RW up row l - RW
+  const float sc = lane < 2 * RW ? scales[(lane < RW ? 0 : I) + rbase + lane % RW] : 0.0f;
+  constexpr int NB = RW / RB;
   for (int c0 = 0; c0 < n_tok; c0 += TT) {
     // two buffers: batch bt+1 is in flight while batch bt is computed
     uint4 wb[2][RB][2][NPL];  // [buffer][row of batch][gate, up][piece]
@@ -412,7 +448,7 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
         const int r = rbase + bt * RB + rr;
 #pragma unroll
         for (int i = 0; i < NPL; i++) {
-          const int p = lane + 64 * i;
+          const int p = p0 + lane + 64 * i;
           const bool ok = p < npieces;
           dst[rr][0][i] = ok ? reinterpret_cast<const uint4 *>(gate + (size_t)r * row_b)[p]
                              : make_uint4(0, 0, 0, 0);
@@ -428,7 +464,7 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
       const bool live = c0 + t < n_tok;
 #pragma unroll
       for (int i = 0; i < NPL; i++) {
-        const int p = lane + 64 * i;
+        const int p = p0 + lane + 64 * i;
         load_act<WB>(qrow(live ? c0 + t : c0), drow(live ? c0 + t : c0), p, live && p < npieces,
                      act[i][t]);
       }
@@ -438,7 +474,7 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
       if (bt + 1 < NB) load_batch(wb[(bt + 1) & 1], bt + 1);
 #pragma unroll
       for (int rr = 0; rr < RB; rr++) {
-        const int rl = bt * RB + rr;  // row within the wave's 8
+        const int rl = bt * RB + rr;  // row within the wave's RW
         float g[TT], u[TT];
 #pragma unroll
         for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
@@ -451,13 +487,28 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
           }
         }
         const float sg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), rl));
-        const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), 8 + rl));
+        const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), RW + rl));
 #pragma unroll
         for (int t = 0; t < TT; t++) {
           const float gv = sg * wave_sum(g[t]);
           const float uv = su * wave_sum(u[t]);
-          if (lane == 0) hb[t][wv * 8 + rl] = silu(gv) * uv;
+          if (lane == 0) {
+            if constexpr (KS == 1) {
+              hb[t][wv * 8 + rl] = silu(gv) * uv;
+            } else {
+              part[khalf][t][wr * RW + rl][0] = gv;
+              part[khalf][t][wr * RW + rl][1] = uv;
+            }
+          }
         }
+      }
+    }
+    if constexpr (KS == 2) {
+      __syncthreads();
+      if (threadIdx.x < TT * 32) {
+        const int t = threadIdx.x >> 5, r = threadIdx.x & 31;
+        hb[t][r] = silu(part[0][t][r][0] + part[1][t][r][0]) *
+                   (part[0][t][r][1] + part[1][t][r][1]);
       }
     }
     __syncthreads();
@@ -632,7 +683,10 @@ __global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
   if (n_tok == 0) return;
   const int e = min(max(ent[0], 0), a.E - 1);
   const int *pairs = ent + 2, *toks = ent + 2 + sbk::TMAX;
-  gate_up_rows<WB, TT, NPL, (TT == 1 ? (WB == 2 ? 2 * MOE_K2_ROWS : MOE_K2_ROWS) : 1)>(
+  // int8 rows longer than 4 pieces per lane are split over two waves
+  constexpr int KS = WB == 8 && NPL > 4 ? 2 : 1;
+  gate_up_rows<WB, TT, KS == 2 ? 4 : NPL,
+               (TT == 1 ? (WB == 2 ? 2 * MOE_K2_ROWS : WB == 8 ? 1 : MOE_K2_ROWS) : 1), KS>(
       a, hb, a.experts + (size_t)e * a.blob_bytes, blk, n_tok, pairs,
       [&](int i) { return (const int8_t *)(a.q + (size_t)min(max(toks[i], 0), a.T - 1) * a.H); },
       [&](int i) {
@@ -896,8 +950,8 @@ bool small_batch_supported(const moe_cfg &c, int T) {
   if (T < 1 || T > sbk::TMAX) return false;
   if (T * c.top_k > 256) return false;
   if (c.hidden / 64 > 128 || c.hidden % sbk::RT) return false;
-  const int per = c.wbits == 4 ? 32 : 64;
-  return c.hidden / per <= 256 && c.inter / per <= 128;
+  const int per = 128 / c.wbits;  // codes per 16-byte piece
+  return c.hidden / per <= (c.wbits == 8 ? 448 : 256) && c.inter / per <= 128;
 }
 
 template <int WB, int TT, int NPG, int NPD>
@@ -928,16 +982,25 @@ template <int WB, int TT>
 static void launch3_np(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
   const int per = 128 / WB;
   const int ng = (a.H / per + 63) / 64, nd = (a.I / per + 63) / 64;
-  if (ng <= 1 && nd <= 1) launch3<WB, TT, 1, 1>(a, st, ev);
-  else if (ng <= 2 && nd <= 1) launch3<WB, TT, 2, 1>(a, st, ev);
-  else if (ng <= 3 && nd <= 1) launch3<WB, TT, 3, 1>(a, st, ev);
-  else if (ng <= 4 && nd <= 1) launch3<WB, TT, 4, 1>(a, st, ev);
-  else launch3<WB, TT, 4, 2>(a, st, ev);
+  if constexpr (WB == 8) {  // 16 codes per piece: up to 7 pieces per lane
+    if (ng <= 2 && nd <= 1) launch3<WB, TT, 2, 1>(a, st, ev);
+    else if (ng <= 4 && nd <= 2) launch3<WB, TT, 4, 2>(a, st, ev);
+    else launch3<WB, TT, 7, 2>(a, st, ev);
+  } else {
+    if (ng <= 1 && nd <= 1) launch3<WB, TT, 1, 1>(a, st, ev);
+    else if (ng <= 2 && nd <= 1) launch3<WB, TT, 2, 1>(a, st, ev);
+    else if (ng <= 3 && nd <= 1) launch3<WB, TT, 3, 1>(a, st, ev);
+    else if (ng <= 4 && nd <= 1) launch3<WB, TT, 4, 1>(a, st, ev);
+    else launch3<WB, TT, 4, 2>(a, st, ev);
+  }
 }
 
 void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev) {
   a.n_slots_ub = a.n_shared + (a.T * a.K < a.E ? a.T * a.K : a.E);
-  if (a.wbits == 4) {
+  if (a.wbits == 8) {  // a piece carries 16 codes: two tokens per chunk
+    if (a.T == 1) launch3_np<8, 1>(a, st, ev);
+    else launch3_np<8, 2>(a, st, ev);
+  } else if (a.wbits == 4) {
     if (a.T == 1) launch3_np<4, 1>(a, st, ev);
     else launch3_np<4, 4>(a, st, ev);
   } else {

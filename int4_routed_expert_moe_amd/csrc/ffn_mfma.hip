@@ -13,7 +13,8 @@
 // fix-up (convert, fused multiply-add) after every MFMA.  int4 codes enter
 // the MFMA as 16 x code (the low/high nibble split), with the 1/16 folded
 // into the activation scale; the split reorders k inside each group of 8,
-// and the activations staged in LDS are reordered the same way.
+// and the activations staged in LDS are reordered the same way.  int8 codes
+// (the same format with 8-bit codes) enter as they are.
 //
 // Work items are (expert, 64-token tile) pairs from a tile list; a
 // workgroup computes 64 rows x 64 tokens of one work item (gate and up
@@ -28,7 +29,9 @@ constexpr int NT = 64;              // tokens per tile
 constexpr int RT = 64;              // rows per workgroup
 constexpr int CB = 8;               // Q8_0 blocks per K chunk (256 k)
 constexpr int BSTR = CB * 32 + 16;  // LDS bytes per activation row (padded)
-constexpr int ASTR = CB * 16 + 4;   // LDS bytes per int4 weight row (padded)
+// LDS bytes per weight row of a chunk (padded): int4 16 B per block, int8 32 B
+template <int WB>
+constexpr int astr() { return WB == 8 ? CB * 32 + 8 : CB * 16 + 4; }
 }  // namespace mf
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -116,18 +119,26 @@ __device__ __forceinline__ uint2 even_odd8(uint32_t w0, uint32_t w1) {
 }
 
 // A fragment of one 32-code block: lane (m, g) holds codes 8g..8g+7 of row m
-// as 16 x code, even codes first.
-__device__ __forceinline__ long a_frag(uint32_t w) {
-  return (long)(uint32_t)lo16(w) | ((long)(uint32_t)hi16(w) << 32);
+// -- int4: as 16 x code, even codes first (from 4 bytes); int8: the 8 bytes.
+template <int WB>
+__device__ __forceinline__ long a_frag(const uint8_t *row, int b, int g) {
+  if constexpr (WB == 8) {
+    return *reinterpret_cast<const long *>(row + b * 32 + g * 8);
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(row + b * 16 + g * 4);
+    return (long)(uint32_t)lo16(w) | ((long)(uint32_t)hi16(w) << 32);
+  }
 }
 
 // Stage one K chunk of activations: rows = tokens (64), CB blocks of 32
-// int8 (reordered per 8) and their scales / 16.
+// int8 and their scales (for int4 weights: reordered per 8 like the nibble
+// split, and the scales / 16).
 struct ActChunk {
   uint4 v[4];  // 4 x 16 bytes per thread (64 tokens x 16 pieces)
   float d[2];  // 64 tokens x 8 block scales
 };
 
+template <int WB>
 __device__ __forceinline__ void load_act_chunk(const int8_t *q, const float *d, int row_len,
                                                const int *tokl, int n, int c, int nblk,
                                                ActChunk &r) {
@@ -145,19 +156,25 @@ __device__ __forceinline__ void load_act_chunk(const int8_t *q, const float *d, 
   for (int u = 0; u < 2; u++) {
     const int i = tid + 256 * u, tok_i = i >> 3, b = i & 7;
     const int blk = c * mf::CB + b;
-    r.d[u] = (tok_i < n && blk < nblk) ? d[(size_t)tokl[tok_i] * (row_len / 32) + blk] * 0.0625f
-                                       : 0.0f;
+    r.d[u] = (tok_i < n && blk < nblk)
+                 ? d[(size_t)tokl[tok_i] * (row_len / 32) + blk] * (WB == 8 ? 1.0f : 0.0625f)
+                 : 0.0f;
   }
 }
 
+template <int WB>
 __device__ __forceinline__ void store_act_chunk(const ActChunk &r, uint8_t *bs, float *ds) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < 4; u++) {
     const int i = tid + 256 * u, tok_i = i >> 4, piece = i & 15;
-    uint2 *dst = reinterpret_cast<uint2 *>(bs + tok_i * mf::BSTR + piece * 16);
-    dst[0] = even_odd8(r.v[u].x, r.v[u].y);
-    dst[1] = even_odd8(r.v[u].z, r.v[u].w);
+    if constexpr (WB == 8) {
+      *reinterpret_cast<uint4 *>(bs + tok_i * mf::BSTR + piece * 16) = r.v[u];
+    } else {
+      uint2 *dst = reinterpret_cast<uint2 *>(bs + tok_i * mf::BSTR + piece * 16);
+      dst[0] = even_odd8(r.v[u].x, r.v[u].y);
+      dst[1] = even_odd8(r.v[u].z, r.v[u].w);
+    }
   }
 #pragma unroll
   for (int u = 0; u < 2; u++) {
@@ -166,43 +183,54 @@ __device__ __forceinline__ void store_act_chunk(const ActChunk &r, uint8_t *bs, 
   }
 }
 
-// Stage one K chunk of nm int4 weight matrices: 64 rows x CB blocks x 16 B.
-template <int NM>
+// Stage one K chunk of NM weight matrices: 64 rows x CB blocks x (4 WB)
+// bytes, as 16-byte pieces (PPR per row).
+template <int NM, int WB>
 struct WChunk {
-  uint4 v[NM * 2];
+  static constexpr int PPR = mf::CB * WB / 4;  // pieces per row: int4 8, int8 16
+  uint4 v[NM * PPR / 4];                       // 64 rows x PPR pieces / 256 threads
 };
 
-template <int NM>
+template <int NM, int WB>
 __device__ __forceinline__ void load_w_chunk(const uint8_t *const *mat, size_t row_b, int r0,
-                                             int c, int nblk, WChunk<NM> &r) {
+                                             int c, int nblk, WChunk<NM, WB> &r) {
+  constexpr int PPR = WChunk<NM, WB>::PPR, PER = PPR / 4;
   const int tid = threadIdx.x;
 #pragma unroll
   for (int m = 0; m < NM; m++) {
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int i = tid + 256 * u, row = i >> 3, b = i & 7;  // 64 rows x 8 blocks
-      const int blk = c * mf::CB + b;
-      r.v[m * 2 + u] = blk < nblk ? *reinterpret_cast<const uint4 *>(
-                                         mat[m] + (size_t)(r0 + row) * row_b + (size_t)blk * 16)
-                                  : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < PER; u++) {
+      const int i = tid + 256 * u, row = i / PPR, pc = i % PPR;
+      const int blk = c * mf::CB + pc * 16 / (4 * WB);
+      r.v[m * PER + u] =
+          blk < nblk ? *reinterpret_cast<const uint4 *>(mat[m] + (size_t)(r0 + row) * row_b +
+                                                        (size_t)c * mf::CB * 4 * WB + pc * 16)
+                     : make_uint4(0, 0, 0, 0);
     }
   }
 }
 
-template <int NM>
-__device__ __forceinline__ void store_w_chunk(const WChunk<NM> &r, uint8_t *as) {
+template <int NM, int WB>
+__device__ __forceinline__ void store_w_chunk(const WChunk<NM, WB> &r, uint8_t *as) {
+  constexpr int PPR = WChunk<NM, WB>::PPR, PER = PPR / 4, AS = mf::astr<WB>();
   const int tid = threadIdx.x;
 #pragma unroll
   for (int m = 0; m < NM; m++) {
 #pragma unroll
-    for (int u = 0; u < 2; u++) {
-      const int i = tid + 256 * u, row = i >> 3, b = i & 7;
-      uint32_t *dst = reinterpret_cast<uint32_t *>(as + (size_t)m * mf::RT * mf::ASTR +
-                                                   row * mf::ASTR + b * 16);
-      dst[0] = r.v[m * 2 + u].x;
-      dst[1] = r.v[m * 2 + u].y;
-      dst[2] = r.v[m * 2 + u].z;
-      dst[3] = r.v[m * 2 + u].w;
+    for (int u = 0; u < PER; u++) {
+      const int i = tid + 256 * u, row = i / PPR, pc = i % PPR;
+      uint8_t *dst = as + (size_t)m * mf::RT * AS + row * AS + pc * 16;
+      const uint4 v = r.v[m * PER + u];
+      if constexpr (WB == 8) {  // rows 8-byte aligned
+        reinterpret_cast<uint2 *>(dst)[0] = make_uint2(v.x, v.y);
+        reinterpret_cast<uint2 *>(dst)[1] = make_uint2(v.z, v.w);
+      } else {  // rows 4-byte aligned
+        uint32_t *d32 = reinterpret_cast<uint32_t *>(dst);
+        d32[0] = v.x;
+        d32[1] = v.y;
+        d32[2] = v.z;
+        d32[3] = v.w;
+      }
     }
   }
 }
@@ -212,7 +240,7 @@ __device__ __forceinline__ void store_w_chunk(const WChunk<NM> &r, uint8_t *as) 
 // token sub-tile s (16 tokens, s < NS: the sub-tiles that hold tokens, fixed
 // per workgroup so the loop body has no branches), row 16 wv + 4 g + i.  DBG: raw block dots of
 // matrix m go to dots[m] at ((pair * R + row) * nblk + block).
-template <int NM, bool DBG, int NS>
+template <int NM, bool DBG, int NS, int WB>
 __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, const int8_t *q,
                            const float *d, int row_len, const int *tokl, const int *pairl, int n,
                            int nblk, uint8_t *bs, float *ds, uint8_t *as, float (&acc)[NM][4][4],
@@ -226,28 +254,26 @@ __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, cons
 #pragma unroll
       for (int i = 0; i < 4; i++) acc[m][s][i] = 0.0f;
   const int nchunk = (nblk + mf::CB - 1) / mf::CB;
+  constexpr int AS = mf::astr<WB>();
   ActChunk ac;
-  WChunk<NM> wc;
-  load_act_chunk(q, d, row_len, tokl, n, 0, nblk, ac);
-  load_w_chunk<NM>(mat, row_b, r0, 0, nblk, wc);
+  WChunk<NM, WB> wc;
+  load_act_chunk<WB>(q, d, row_len, tokl, n, 0, nblk, ac);
+  load_w_chunk<NM, WB>(mat, row_b, r0, 0, nblk, wc);
   for (int c = 0; c < nchunk; c++) {
     __syncthreads();  // the previous chunk is consumed
-    store_act_chunk(ac, bs, ds);
-    store_w_chunk<NM>(wc, as);
+    store_act_chunk<WB>(ac, bs, ds);
+    store_w_chunk<NM, WB>(wc, as);
     __syncthreads();
     if (c + 1 < nchunk) {  // next chunk in flight during this one's MFMAs
-      load_act_chunk(q, d, row_len, tokl, n, c + 1, nblk, ac);
-      load_w_chunk<NM>(mat, row_b, r0, c + 1, nblk, wc);
+      load_act_chunk<WB>(q, d, row_len, tokl, n, c + 1, nblk, ac);
+      load_w_chunk<NM, WB>(mat, row_b, r0, c + 1, nblk, wc);
     }
     const int nb = min(mf::CB, nblk - c * mf::CB);
     for (int b = 0; b < nb; b++) {
       long af[NM];
 #pragma unroll
-      for (int m = 0; m < NM; m++) {
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(
-            as + (size_t)m * mf::RT * mf::ASTR + (wv * 16 + m16) * mf::ASTR + b * 16 + g * 4);
-        af[m] = a_frag(w);
-      }
+      for (int m = 0; m < NM; m++)
+        af[m] = a_frag<WB>(as + (size_t)m * mf::RT * AS + (wv * 16 + m16) * AS, b, g);
 #pragma unroll
       for (int s = 0; s < NS; s++) {  // only the sub-tiles that hold tokens
         const int col = s * 16 + m16;
@@ -264,7 +290,7 @@ __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, cons
 #pragma unroll
             for (int i = 0; i < 4; i++) {
               const int row = r0 + wv * 16 + g * 4 + i;
-              dots[m][((size_t)pairl[col] * R + row) * nblk + blk] = p[i] >> 4;
+              dots[m][((size_t)pairl[col] * R + row) * nblk + blk] = WB == 8 ? p[i] : p[i] >> 4;
             }
           }
         }
@@ -274,27 +300,27 @@ __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, cons
 }
 
 // mfma_kloop with the sub-tile count of n tokens chosen once.
-template <int NM, bool DBG>
+template <int NM, bool DBG, int WB>
 __device__ void mfma_kloop_n(const uint8_t *const *mat, size_t row_b, int r0, const int8_t *q,
                              const float *d, int row_len, const int *tokl, const int *pairl,
                              int n, int nblk, uint8_t *bs, float *ds, uint8_t *as,
                              float (&acc)[NM][4][4], int32_t *const *dots, int R) {
   switch ((n + 15) / 16) {
     case 1:
-      mfma_kloop<NM, DBG, 1>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds, as, acc,
-                             dots, R);
+      mfma_kloop<NM, DBG, 1, WB>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+                                 as, acc, dots, R);
       break;
     case 2:
-      mfma_kloop<NM, DBG, 2>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds, as, acc,
-                             dots, R);
+      mfma_kloop<NM, DBG, 2, WB>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+                                 as, acc, dots, R);
       break;
     case 3:
-      mfma_kloop<NM, DBG, 3>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds, as, acc,
-                             dots, R);
+      mfma_kloop<NM, DBG, 3, WB>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+                                 as, acc, dots, R);
       break;
     default:
-      mfma_kloop<NM, DBG, 4>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds, as, acc,
-                             dots, R);
+      mfma_kloop<NM, DBG, 4, WB>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+                                 as, acc, dots, R);
   }
 }
 
@@ -306,13 +332,13 @@ constexpr size_t MF_LDS_D = (size_t)mf::NT * mf::CB * 4;
 // Workgroup (row tile, work item): rows 64 x .. 64 x + 63 of gate and up for
 // the work item's tokens; h = silu(g) * u to LDS, then the Q8_0 of h (two
 // 32-row blocks per token) to q_h / d_h of each pair.
-template <bool DBG>
+template <bool DBG, int WB>
 __global__ void __launch_bounds__(256, 3) k_gate_up_mfma(FfnArgs a, const int4 *tiles,
                                                       const int32_t *n_tiles, int8_t *q_h,
                                                       float *d_h) {
   __shared__ __align__(16) uint8_t bs[MF_LDS_B];
   __shared__ float ds[mf::NT * mf::CB];
-  __shared__ __align__(16) uint8_t as[2 * mf::RT * mf::ASTR];
+  __shared__ __align__(16) uint8_t as[2 * mf::RT * mf::astr<WB>()];
   __shared__ int tokl[mf::NT], pairl[mf::NT];
   if ((int)blockIdx.y >= *n_tiles) return;
   const int4 t = tiles[blockIdx.y];
@@ -326,12 +352,12 @@ __global__ void __launch_bounds__(256, 3) k_gate_up_mfma(FfnArgs a, const int4 *
     pairl[tid] = pair;
   }
   __syncthreads();
-  const size_t row_b = (size_t)H / 2;
+  const size_t row_b = (size_t)H * WB / 8;
   const uint8_t *mats[2] = {ti.blob, ti.blob + (size_t)I * row_b};
   float acc[2][4][4];
   int32_t *dots[2] = {a.dbg.gate_dots, a.dbg.up_dots};
-  mfma_kloop_n<2, DBG>(mats, row_b, r0, a.q, a.d, H, tokl, pairl, ti.n, H / 32, bs, ds, as, acc,
-                       dots, I);
+  mfma_kloop_n<2, DBG, WB>(mats, row_b, r0, a.q, a.d, H, tokl, pairl, ti.n, H / 32, bs, ds, as,
+                           acc, dots, I);
   // epilogue: h into LDS as [token][64 rows] fp32 (reuses the activation tile)
   const float *scales = reinterpret_cast<const float *>(ti.blob + 3 * (size_t)I * row_b);
   __syncthreads();
@@ -382,13 +408,13 @@ __global__ void __launch_bounds__(256, 3) k_gate_up_mfma(FfnArgs a, const int4 *
 // Workgroup (row tile, work item): output rows 64 x .. of the down matrix
 // for the work item's pairs, from Q8_0(h); routed rows go to expert_out of
 // the slot, shared rows to shared_out of the token.
-template <bool DBG>
+template <bool DBG, int WB>
 __global__ void __launch_bounds__(256) k_down_mfma(FfnArgs a, const int4 *tiles,
                                                    const int32_t *n_tiles, const int8_t *q_h,
                                                    const float *d_h) {
   __shared__ __align__(16) uint8_t bs[MF_LDS_B];
   __shared__ float ds[mf::NT * mf::CB];
-  __shared__ __align__(16) uint8_t as[mf::RT * mf::ASTR];
+  __shared__ __align__(16) uint8_t as[mf::RT * mf::astr<WB>()];
   __shared__ int tokl[mf::NT], pairl[mf::NT];
   if ((int)blockIdx.y >= *n_tiles) return;
   const int4 t = tiles[blockIdx.y];
@@ -402,14 +428,14 @@ __global__ void __launch_bounds__(256) k_down_mfma(FfnArgs a, const int4 *tiles,
     pairl[tid] = pair;
   }
   __syncthreads();
-  const size_t row_b = (size_t)I / 2;
-  const uint8_t *mats[1] = {ti.blob + 2 * (size_t)I * ((size_t)H / 2)};
+  const size_t row_b = (size_t)I * WB / 8;
+  const size_t gate_b = (size_t)I * ((size_t)H * WB / 8);  // bytes of one gate/up matrix
+  const uint8_t *mats[1] = {ti.blob + 2 * gate_b};
   float acc[1][4][4];
   int32_t *dots[1] = {a.dbg.down_dots};
-  mfma_kloop_n<1, DBG>(mats, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs, ds, as, acc,
-                       dots, H);
-  const float *sd =
-      reinterpret_cast<const float *>(ti.blob + 3 * (size_t)I * ((size_t)H / 2)) + 2 * I;
+  mfma_kloop_n<1, DBG, WB>(mats, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs, ds, as,
+                           acc, dots, H);
+  const float *sd = reinterpret_cast<const float *>(ti.blob + 3 * gate_b) + 2 * I;
   const int m16 = lane & 15, g = lane >> 4;
   const int row = r0 + wv * 16 + g * 4;  // 4 consecutive rows per lane
   const float4 s4 = *reinterpret_cast<const float4 *>(sd + row);
@@ -433,8 +459,19 @@ size_t mfma_tiles_max(int T, int K, int E, int n_shared) {
 }
 
 bool mfma_supported(const FfnArgs &a) {
-  return a.wbits == 4 && a.H % 256 == 0 && a.I % mf::RT == 0 && a.H % mf::RT == 0 &&
-         a.E <= 1024 && a.T > 0;
+  return (a.wbits == 4 || a.wbits == 8) && a.H % 256 == 0 && a.I % mf::RT == 0 &&
+         a.H % mf::RT == 0 && a.E <= 1024 && a.T > 0;
+}
+
+template <bool DBG, int WB>
+static void launch_mfma_wb(const FfnArgs &a, int max_tiles, int4 *tiles, int32_t *n_tiles,
+                           int8_t *q_h, float *d_h, hipStream_t st, const moe_events *ev) {
+  const dim3 g1(a.I / mf::RT, max_tiles), g2(a.H / mf::RT, max_tiles);
+  launch_k(k_gate_up_mfma<DBG, WB>, g1, dim3(256), 0, st, stage_ev(ev, MOE_STAGE_GATE_UP), a,
+           (const int4 *)tiles, (const int32_t *)n_tiles, q_h, d_h);
+  launch_k(k_down_mfma<DBG, WB>, g2, dim3(256), 0, st, stage_ev(ev, MOE_STAGE_DOWN), a,
+           (const int4 *)tiles, (const int32_t *)n_tiles, (const int8_t *)q_h,
+           (const float *)d_h);
 }
 
 void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_h, float *d_h,
@@ -444,19 +481,12 @@ void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_
                      tiles, n_tiles);
   const bool dbg = a.dbg.gate_dots || a.dbg.up_dots || a.dbg.h || a.dbg.q_h || a.dbg.d_h ||
                    a.dbg.down_dots;
-  const dim3 g1(a.I / mf::RT, max_tiles), g2(a.H / mf::RT, max_tiles);
-  if (dbg) {
-    launch_k(k_gate_up_mfma<true>, g1, dim3(256), 0, st, stage_ev(ev, MOE_STAGE_GATE_UP), a,
-             (const int4 *)tiles, (const int32_t *)n_tiles, q_h, d_h);
-    launch_k(k_down_mfma<true>, g2, dim3(256), 0, st, stage_ev(ev, MOE_STAGE_DOWN), a,
-             (const int4 *)tiles, (const int32_t *)n_tiles, (const int8_t *)q_h,
-             (const float *)d_h);
+  if (a.wbits == 8) {
+    if (dbg) launch_mfma_wb<true, 8>(a, max_tiles, tiles, n_tiles, q_h, d_h, st, ev);
+    else launch_mfma_wb<false, 8>(a, max_tiles, tiles, n_tiles, q_h, d_h, st, ev);
   } else {
-    launch_k(k_gate_up_mfma<false>, g1, dim3(256), 0, st, stage_ev(ev, MOE_STAGE_GATE_UP), a,
-             (const int4 *)tiles, (const int32_t *)n_tiles, q_h, d_h);
-    launch_k(k_down_mfma<false>, g2, dim3(256), 0, st, stage_ev(ev, MOE_STAGE_DOWN), a,
-             (const int4 *)tiles, (const int32_t *)n_tiles, (const int8_t *)q_h,
-             (const float *)d_h);
+    if (dbg) launch_mfma_wb<true, 4>(a, max_tiles, tiles, n_tiles, q_h, d_h, st, ev);
+    else launch_mfma_wb<false, 4>(a, max_tiles, tiles, n_tiles, q_h, d_h, st, ev);
   }
 }
 

@@ -29,9 +29,10 @@ int check_cfg(const moe_cfg *c) {
     return fail(MOE_EINVAL, "hidden=%d must be a positive multiple of 256", c->hidden);
   if (c->inter <= 0 || c->inter % 128)
     return fail(MOE_EINVAL, "inter=%d must be a positive multiple of 128", c->inter);
-  if (c->wbits != 4 && c->wbits != 2) return fail(MOE_EINVAL, "wbits=%d not in {4,2}", c->wbits);
-  const int per = c->wbits == 4 ? 32 : 64;
-  if (c->hidden / per > 256 || c->inter / per > 128)
+  if (c->wbits != 8 && c->wbits != 4 && c->wbits != 2)
+    return fail(MOE_EINVAL, "wbits=%d not in {8,4,2}", c->wbits);
+  const int per = 128 / c->wbits;  // codes per 16-byte piece
+  if (c->hidden / per > (c->wbits == 8 ? 448 : 256) || c->inter / per > 128)
     return fail(MOE_EINVAL, "hidden=%d / inter=%d too large for wbits=%d", c->hidden, c->inter,
                 c->wbits);
   if (c->n_experts < 2 || c->n_experts > 1024)
@@ -190,7 +191,10 @@ int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32
   a.shared_out = shared_out;
   if (dbg) a.dbg = *dbg;
   else memset(&a.dbg, 0, sizeof(a.dbg));
-  if (T > 16 && moe::mfma_supported(a)) {  // batches: grouped GEMMs on the matrix cores
+  const bool mfma = moe::mfma_supported(a);
+  if (c.wbits == 8 && !mfma)  // the vector-dot kernels take packed int4 / int2 only
+    return fail(MOE_EINVAL, "int8 experts need the matrix-core path (H %% 256, I %% 64)");
+  if ((T > 16 || c.wbits == 8) && mfma) {  // grouped GEMMs, matrix cores
     const size_t pairs = (size_t)T * c.top_k + (size_t)T * c.n_shared;
     int8_t *q_h = reinterpret_cast<int8_t *>(ws.h);
     float *d_h = reinterpret_cast<float *>(q_h + ((pairs * c.inter + 255) & ~(size_t)255));

@@ -60,7 +60,7 @@ def test_workspace_queries(L):
 @pytest.mark.parametrize("field,value", [
     ("hidden", 100), ("hidden", 0), ("inter", 96), ("n_experts", 1), ("n_experts", 2048),
     ("n_group", 3), ("n_group", 0), ("topk_group", 0), ("topk_group", 9), ("top_k", 0),
-    ("top_k", 17), ("n_shared", 2), ("wbits", 3), ("wbits", 8), ("routed_scaling", 0.0),
+    ("top_k", 17), ("n_shared", 2), ("wbits", 3), ("wbits", 16), ("wbits", 1), ("routed_scaling", 0.0),
     ("routed_scaling", float("nan")),
 ])
 def test_bad_cfg_rejected(L, field, value):
@@ -72,6 +72,16 @@ def test_bad_cfg_rejected(L, field, value):
     rc = L.moe_route(ctypes.byref(c), 1, A, A, A, A, A, A, 1 << 30, None)
     assert rc == moe.MOE_EINVAL
     assert L.moe_last_error()
+
+
+@pytest.mark.parametrize("wbits,hidden,inter,ok", [
+    (8, 7168, 2048, True), (8, 7424, 2048, False), (8, 6144, 2176, False),
+    (4, 8192, 4096, True), (4, 8448, 2048, False), (2, 16384, 8192, True),
+])
+def test_row_length_limits(L, wbits, hidden, inter, ok):
+    import dataclasses
+    c = dataclasses.replace(REAL, wbits=wbits, hidden=hidden, inter=inter).c()
+    assert (L.moe_expert_blob_bytes(ctypes.byref(c)) > 0) == ok
 
 
 def test_top_k_above_candidates_rejected(L):

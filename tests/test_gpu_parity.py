@@ -53,7 +53,7 @@ def h(t):
 # ------------------------------------------------------------------ generator
 
 def test_gpu_generator_matches_host(dev):
-    for shape in (synth.TINY, synth.REAL, synth.REAL.with_bits(2)):
+    for shape in (synth.TINY, synth.REAL, synth.REAL.with_bits(2), synth.REAL.with_bits(8)):
         bb = synth.blob_bytes(shape)
         ids = [0, 3, synth.SHARED_ID]
         out = torch.empty(len(ids) * bb, dtype=torch.uint8, device=dev)
@@ -237,6 +237,34 @@ def test_ffn_real_mfma(dev, real):
     _ffn_check(real, synth.tokens(synth.REAL, synth.SEEDS["prefill"], 24), dev, check_chain=False)
 
 
+# int8-weight experts (the same record format with 8-bit codes) take the
+# matrix-core path at every batch size.
+
+@pytest.fixture(scope="module")
+def real8(dev):
+    return DeviceLayer(synth.REAL.with_bits(8), synth.SEEDS["decode"])
+
+
+@pytest.mark.parametrize("T", [1, 4, 40])
+def test_ffn_tiny_int8(dev, T):
+    lay = DeviceLayer(synth.TINY.with_bits(8), synth.SEEDS["tiny"])
+    _ffn_check(lay, synth.tokens(synth.TINY, synth.SEEDS["tiny"], T, start=2), dev)
+
+
+def test_ffn_decode_int8(dev, real8):
+    _ffn_check(real8, synth.tokens(synth.REAL, synth.SEEDS["decode"], 1, start=3), dev)
+
+
+def test_ffn_verify_int8(dev, real8):
+    _ffn_check(real8, synth.tokens_perturbed(synth.REAL, synth.SEEDS["verify"], 4), dev,
+               check_chain=False)
+
+
+def test_ffn_real_mfma_int8(dev, real8):
+    _ffn_check(real8, synth.tokens(synth.REAL, synth.SEEDS["prefill"], 24), dev,
+               check_chain=False)
+
+
 # ------------------------------------------------------------------ combine
 
 @pytest.mark.parametrize("T,K,H,res,norm", [(1, 8, 6144, False, False), (4, 2, 256, True, True),
@@ -312,6 +340,28 @@ def test_layer_residual_norm(dev, real):
 def test_layer_int2_decode(dev):
     lay = DeviceLayer(synth.REAL.with_bits(2), synth.SEEDS["stack"])
     _layer_check(lay, synth.tokens(synth.REAL, synth.SEEDS["stack"], 1), dev)
+
+
+def test_layer_tiny_int8(dev):
+    lay = DeviceLayer(synth.TINY.with_bits(8), synth.SEEDS["tiny"])
+    for T in (1, 4, 9, 33):
+        _layer_check(lay, synth.tokens(synth.TINY, 78, T), dev)
+
+
+@pytest.mark.parametrize("start", [0, 1])
+def test_layer_int8_decode(dev, real8, start):
+    _layer_check(real8, synth.tokens(synth.REAL, synth.SEEDS["decode"], 1, start=start), dev)
+
+
+@pytest.mark.parametrize("T", [4, 16])
+def test_layer_int8_verify(dev, real8, T):
+    _layer_check(real8, synth.tokens_perturbed(synth.REAL, synth.SEEDS["verify"], T), dev)
+
+
+def test_layer_int8_residual_norm(dev, real8):
+    x = synth.tokens(synth.REAL, 9, 2)
+    res = synth.tokens(synth.REAL, 10, 2)
+    _layer_check(real8, x, dev, residual=res, want_norm=True)
 
 
 def test_layer_deterministic(dev, real):
