@@ -69,6 +69,8 @@ def lib():
     L.oracle_select.restype = c_i
     L.oracle_route.argtypes = [c_i, c_i, c_i, c_i, c_i, c_i, c_f, c_v, c_v, c_v, c_v, c_v, c_v]
     L.oracle_route.restype = c_i
+    L.oracle_top_p.argtypes = [c_i, c_i, c_i, c_f, c_f, c_v, c_v, c_v, c_v]
+    L.oracle_top_p.restype = c_i
     L.oracle_group.argtypes = [c_i, c_i, c_i, c_v, c_v, c_v, c_v, c_v, c_v, c_v]
     L.oracle_group.restype = c_i
     L.oracle_block_dots.argtypes = [c_v, c_i, c_v, c_i, c_v]
@@ -184,14 +186,33 @@ def select(s, sb, n_group, topk_group, top_k, scale):
     return idx, w, margin
 
 
-def route(x, wr, bias, n_group, topk_group, top_k, scale):
-    """Router for T tokens: (idx [T,K] int32, w [T,K] fp32, margins [T,2] fp64)."""
+def top_p(s, idx, w, p, scale):
+    """Adaptive expert top-p (R15) on a rank-ordered selection: new (idx, w,
+    kept [T]); dropped ranks get idx -1 and w 0.  p = 0 or 1 changes nothing."""
+    s = _c(s, np.float32)
+    idx, w = np.array(idx, np.int32, order="C"), np.array(w, np.float32, order="C")
+    T, E = s.shape
+    K = idx.shape[1]
+    kept = np.empty(T, np.int32)
+    _check(lib().oracle_top_p(T, K, E, p, scale, _ptr(s), _ptr(idx), _ptr(w), _ptr(kept)),
+           "top_p")
+    return idx, w, kept
+
+
+def route(x, wr, bias, n_group, topk_group, top_k, scale, top_p_value=0.0):
+    """Router for T tokens: (idx [T,K] int32, w [T,K] fp32, margins [T,2] fp64);
+    with 0 < top_p_value < 1 the adaptive top-p cut (R15) follows."""
     x, wr, bias = _c(x, np.float32), _c(wr, np.float32), _c(bias, np.float32)
     T, H = x.shape
     E = wr.shape[0]
     idx = np.empty((T, top_k), np.int32)
     w = np.empty((T, top_k), np.float32)
     margin = np.empty((T, 2), np.float64)
+    if 0.0 < top_p_value < 1.0:
+        s, sb = router_scores(x, wr, bias)
+        idx, w, margin = select(s, sb, n_group, topk_group, top_k, scale)
+        idx, w, _ = top_p(s, idx, w, top_p_value, scale)
+        return idx, w, margin
     _check(lib().oracle_route(T, H, E, n_group, topk_group, top_k, scale, _ptr(x), _ptr(wr),
                               _ptr(bias), _ptr(idx), _ptr(w), _ptr(margin)), "route")
     return idx, w, margin
@@ -298,7 +319,7 @@ def rmsnorm(x, eps=1e-5):
 # ------------------------------------------------------------------ whole layer
 
 def layer(x, router_w, bias, blob_of, shared_blob, *, H, I, n_experts, n_group, topk_group,
-          top_k, scale, wbits=4, residual=None, want_norm=False, eps=1e-5):
+          top_k, scale, wbits=4, residual=None, want_norm=False, eps=1e-5, top_p_value=0.0):
     """One routed-MoE layer for T tokens, step by step.
 
     ``blob_of(e)`` returns the packed record of routed expert ``e`` (only the
@@ -308,7 +329,7 @@ def layer(x, router_w, bias, blob_of, shared_blob, *, H, I, n_experts, n_group, 
     """
     x = _c(x, np.float32)
     T = x.shape[0]
-    idx, w, margin = route(x, router_w, bias, n_group, topk_group, top_k, scale)
+    idx, w, margin = route(x, router_w, bias, n_group, topk_group, top_k, scale, top_p_value)
     q, d = q8_0(x)
     groups = group(idx, n_experts)
     expert_out = np.zeros((T, top_k, H), np.float32)

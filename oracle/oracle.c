@@ -18,6 +18,10 @@
  *        per batch and applying it to every position routed to it.
  *  [HN-S] same page, section ディスクストリーミングベースの MoE 実行方式:
  *        ~19 MB per int4 expert.
+ *  [HN-R] same page, section モデルのダウンロードと実行 (download and run),
+ *        its list of options: an adaptive expert top-p (value 0.7 given)
+ *        that cuts expert reads by 30-40%; [HN-B] section コミュニティ
+ *        ベンチマーク: that option gave 1.6x end to end.
  *  [DT]  "Comment exécuter un réseau de neurones de 744 milliards de
  *        paramètres sur un ordinateur ordinaire" (devtrends.cc), section
  *        "Comment fonctionne le moteur": requests for the same expert are
@@ -42,6 +46,12 @@
  *  R9 combine: y = shared + sum_k w_k * expert_k (shared expert weight 1).
  *  R10 packed codes: int4 element 2j in the low nibble of byte j, 2j+1 in the
  *     high nibble; int2 element 4j+i in bits 2i..2i+1; two's complement.
+ *  R15 adaptive expert top-p (p in (0,1); 0 or 1 = off): after the top-K
+ *     selection, keep the shortest prefix of the rank order whose unbiased
+ *     scores, summed left to right in fp32, reach p * S (fp32 product; S as
+ *     in R4); the kept weights are renormalised over that prefix,
+ *     w_k = (s_k / S_kept) * routed_scaling; a dropped rank has idx -1 and
+ *     w 0 and is read by no later step.
  *
  * Precision: router fp32 (R5); Q8_0 decisions fp32; block dots exact in
  * int64 (checked to fit int32); the float epilogues in fp64, rounded to fp32.
@@ -245,6 +255,51 @@ int oracle_select(int T, int E, int G, int TG, int K, float scale, const float *
   return 0;
 }
 
+/* [HN-R] adaptive expert top-p, reading R15, applied in place to one
+ * token's rank-ordered selection (idx, w) given its unbiased scores s[E].
+ * Returns the number of experts kept. */
+int oracle_top_p_one(int K, int E, float p, float scale, const float *s, int32_t *idx,
+                     float *w) {
+  if (!(p > 0.0f && p < 1.0f)) return K;  /* off: the plain top-K */
+  float S = 0.0f;
+  for (int k = 0; k < K; k++) {
+    if (idx[k] < 0 || idx[k] >= E) return -1;
+    S = S + s[idx[k]];
+  }
+  const float thr = p * S;
+  float cum = 0.0f;
+  int kept = K;
+  for (int k = 0; k < K; k++) {
+    cum = cum + s[idx[k]];
+    if (cum >= thr) {
+      kept = k + 1;
+      break;
+    }
+  }
+  float S_kept = 0.0f;
+  for (int k = 0; k < kept; k++) S_kept = S_kept + s[idx[k]];
+  for (int k = 0; k < K; k++) {
+    if (k < kept) {
+      w[k] = (s[idx[k]] / S_kept) * scale;
+    } else {
+      idx[k] = -1;
+      w[k] = 0.0f;
+    }
+  }
+  return kept;
+}
+
+int oracle_top_p(int T, int K, int E, float p, float scale, const float *s, int32_t *idx,
+                 float *w, int32_t *kept) {
+  for (int t = 0; t < T; t++) {
+    int r = oracle_top_p_one(K, E, p, scale, s + (size_t)t * E, idx + (size_t)t * K,
+                             w + (size_t)t * K);
+    if (r < 0) return -1;
+    if (kept) kept[t] = r;
+  }
+  return 0;
+}
+
 int oracle_route(int T, int H, int E, int G, int TG, int K, float scale, const float *x,
                  const float *wr, const float *bias, int32_t *idx, float *w,
                  double *margin) {
@@ -263,13 +318,15 @@ int oracle_route(int T, int H, int E, int G, int TG, int K, float scale, const f
 /* [HN] batch-union item, [DT] merged requests: token slots (slot = t*K + k)
  * grouped by expert with a counting sort in slot order, so each expert's list
  * is in increasing token order; active = experts with at least one slot,
- * ascending, padded with -1. */
+ * ascending, padded with -1.  A slot dropped by top-p (idx -1, R15) joins no
+ * list: inv = -1, and perm holds the offsets[E] kept slots followed by -1. */
 int oracle_group(int T, int K, int E, const int32_t *idx, int32_t *counts,
                  int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
                  int32_t *n_active) {
   const int n = T * K;
   for (int e = 0; e < E; e++) counts[e] = 0;
   for (int i = 0; i < n; i++) {
+    if (idx[i] == -1) continue;
     if (idx[i] < 0 || idx[i] >= E) return -1;
     counts[idx[i]]++;
   }
@@ -277,7 +334,12 @@ int oracle_group(int T, int K, int E, const int32_t *idx, int32_t *counts,
   for (int e = 0; e < E; e++) offsets[e + 1] = offsets[e] + counts[e];
   int32_t *cursor = (int32_t *)malloc(sizeof(int32_t) * (E > 0 ? E : 1));
   for (int e = 0; e < E; e++) cursor[e] = offsets[e];
+  for (int i = offsets[E]; i < n; i++) perm[i] = -1;
   for (int i = 0; i < n; i++) {
+    if (idx[i] == -1) {
+      inv[i] = -1;
+      continue;
+    }
     int p = cursor[idx[i]]++;
     perm[p] = i;
     inv[i] = p;

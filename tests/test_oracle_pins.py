@@ -297,6 +297,111 @@ def test_crafted_tie_rows_pick_lower_index():
     assert idx[0, 0] == 1
 
 
+# ------------------------------------------------------------------ adaptive top-p
+
+def _select_top_p(s, sb, G, TG, K, scale, p):
+    idx, w, _ = oracle.select(s, sb, G, TG, K, scale)
+    return oracle.top_p(s, idx, w, p, scale)
+
+
+def test_top_p_hand_cases():
+    for c in _load("top_p_cases.json")["cases"]:
+        s = np.array([c["s"]], np.float32)
+        sb = (s + np.array([c["bias"]], np.float32)).astype(np.float32)
+        idx, w, kept = _select_top_p(s, sb, 1, 1, c["K"], c["scale"], c["p"])
+        assert idx[0].tolist() == c["idx"], c["name"]
+        want = np.array([a / b for a, b in c["w_num"]])
+        assert np.max(np.abs(w[0] - want)) <= 1e-6, c["name"]
+        assert kept[0] == sum(i >= 0 for i in c["idx"]), c["name"]
+
+
+def test_top_p_vs_exact_prefix_definition():
+    """The kept prefix is the shortest one whose exact share of the selected
+    unbiased mass reaches p (cases within 1e-5 of the threshold skipped)."""
+    rng = np.random.default_rng(21)
+    checked = 0
+    for _ in range(400):
+        E, K = 16, int(rng.integers(1, 9))
+        s = rng.uniform(0.01, 1.0, (1, E)).astype(np.float32)
+        sb = (s + rng.uniform(-0.1, 0.1, (1, E)).astype(np.float32)).astype(np.float32)
+        p = float(np.float32(rng.uniform(0.05, 0.95)))
+        idx0, _, _ = oracle.select(s, sb, 4, 2, K, 2.5)
+        idx, w, kept = oracle.top_p(s, idx0, np.zeros_like(idx0, np.float32), p, 2.5)
+        sel = s[0, idx0[0]].astype(np.float64)
+        share = np.cumsum(sel) / sel.sum()
+        if np.min(np.abs(share - p)) < 1e-5:
+            continue
+        n = int(np.argmax(share >= p)) + 1
+        assert kept[0] == n
+        assert idx[0, :n].tolist() == idx0[0, :n].tolist()
+        assert np.all(idx[0, n:] == -1) and np.all(w[0, n:] == 0)
+        assert np.allclose(w[0, :n], sel[:n] / sel[:n].sum() * 2.5, rtol=3e-7, atol=0)
+        checked += 1
+    assert checked > 300
+
+
+def test_top_p_off_values_keep_plain_selection():
+    rng = np.random.default_rng(22)
+    s = rng.uniform(0.01, 1.0, (8, 32)).astype(np.float32)
+    sb = (s + rng.uniform(-0.1, 0.1, (8, 32)).astype(np.float32)).astype(np.float32)
+    idx0, w0, _ = oracle.select(s, sb, 4, 2, 8, 2.5)
+    for p in (0.0, 1.0):
+        idx, w, kept = oracle.top_p(s, idx0, w0, p, 2.5)
+        assert np.array_equal(idx, idx0) and np.array_equal(w, w0) and np.all(kept == 8)
+
+
+def test_top_p_renormalisation_and_monotone_count():
+    rng = np.random.default_rng(23)
+    s = rng.uniform(0.01, 1.0, (64, 32)).astype(np.float32)
+    sb = (s + rng.uniform(-0.1, 0.1, (64, 32)).astype(np.float32)).astype(np.float32)
+    idx0, w0, _ = oracle.select(s, sb, 4, 2, 8, 2.5)
+    last = np.ones(64, np.int32)
+    for p in (0.1, 0.3, 0.5, 0.7, 0.9, 0.99):
+        idx, w, kept = oracle.top_p(s, idx0, w0, p, 2.5)
+        assert np.all(kept >= last) and np.all(kept >= 1) and np.all(kept <= 8)
+        last = kept
+        # kept weights sum to the scale (each carries <= 2 roundings, S_kept K-1)
+        assert np.max(np.abs(w.astype(np.float64).sum(1) - 2.5)) <= 2.5 * 10 * 2.0 ** -24
+        assert np.array_equal((idx >= 0).sum(1), kept)
+
+
+def test_group_skips_dropped_slots():
+    rng = np.random.default_rng(24)
+    for T, K, E in [(1, 8, 256), (16, 8, 256), (37, 3, 10), (2048, 8, 256)]:
+        idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+        keep = rng.integers(1, K + 1, T)
+        for t in range(T):
+            idx[t, keep[t]:] = -1
+        g = oracle.group(idx, E)
+        flat = idx.ravel()
+        valid = np.nonzero(flat >= 0)[0]
+        n = valid.size
+        assert g["offsets"][E] == n
+        assert np.array_equal(g["perm"][:n], valid[np.argsort(flat[valid], kind="stable")])
+        assert np.all(g["perm"][n:] == -1)
+        assert np.all(g["inv"][flat < 0] == -1)
+        assert np.array_equal(g["inv"][g["perm"][:n]], np.arange(n))
+        assert np.array_equal(g["counts"], np.bincount(flat[valid], minlength=E))
+
+
+def test_layer_top_p_identical_experts_closed_form():
+    """Kept weights are renormalised, so with identical routed experts the
+    layer is still shared(x) + 2.5 * expert(x) whatever top-p drops."""
+    shape = synth.TINY
+    blob = synth.expert_blob(shape, 100, 0, 0)
+    shared = synth.expert_blob(shape, 100, 0, synth.SHARED_ID)
+    x = synth.tokens(shape, 100, 6)
+    wr = synth.router_weights(shape, 100)
+    bias = synth.router_bias_uniform(shape, 100)
+    out = oracle.layer(x, wr, bias, lambda e: blob, shared, H=256, I=128, n_experts=8,
+                       n_group=2, topk_group=1, top_k=2, scale=2.5, top_p_value=0.5)
+    assert np.any(out["idx"] < 0)  # the cut drops something here
+    for t in range(6):
+        e_y = oracle.expert(blob, 256, 128, 4, out["q"][t], out["d"][t])["y"].astype(np.float64)
+        ref = out["shared_out"][t].astype(np.float64) + 2.5 * e_y
+        assert np.max(np.abs(out["y"][t] - ref)) <= 1e-6 * np.sqrt(np.mean(ref ** 2)) + 1e-7
+
+
 # ------------------------------------------------------------------ grouping
 
 def test_group_vs_stable_argsort():
