@@ -55,18 +55,20 @@ WORKLOADS = {
 }
 
 
-def describe(name, shape, T, ring, layers=1):
+def describe(name, shape, T, ring, layers=1, top_p=0.0):
+    tp = (f", adaptive expert top-p {top_p:g} (shortest rank-order prefix holding that share of "
+          f"the selected scores, weights renormalised)" if 0 < top_p < 1 else "")
     if layers > 1:
         return (f"{name}: {T} token(s) per step through a stack of {layers} routed-MoE layers "
                 f"(independent seeds, Zipf-skewed bias, unit-gain RMSNorm + residual between "
                 f"layers; hidden {shape.hidden}, expert intermediate {shape.inter}, "
                 f"{shape.n_experts} experts in {shape.n_group} groups, top-{shape.topk_group} "
                 f"groups, top-{shape.top_k}, {shape.n_shared} shared expert, int{shape.wbits} "
-                f"experts + fp32 row scales, Q8_0 activations), all layers resident in HBM")
+                f"experts + fp32 row scales, Q8_0 activations{tp}), all layers resident in HBM")
     return (f"{name}: {T} token(s) per step through one routed-MoE layer (hidden {shape.hidden}, "
             f"expert intermediate {shape.inter}, {shape.n_experts} experts in {shape.n_group} "
             f"groups, top-{shape.topk_group} groups, top-{shape.top_k}, {shape.n_shared} shared "
-            f"expert, int{shape.wbits} experts + fp32 row scales, Q8_0 activations); weights "
+            f"expert, int{shape.wbits} experts + fp32 row scales, Q8_0 activations{tp}); weights "
             f"cycled over {ring} seeded layer instances in HBM")
 
 
@@ -152,13 +154,13 @@ def measured_traffic(workload):
     return float(m.group(3))
 
 
-def cpu_baseline_stack(shape, seed, layers, tokens_fn, T, n_steps):
+def cpu_baseline_stack(shape, seed, layers, tokens_fn, T, n_steps, top_p=0.0):
     """Oracle on the first steps of the stack workload (all layers)."""
     import oracle
     import synth
     kw = dict(H=shape.hidden, I=shape.inter, n_experts=shape.n_experts, n_group=shape.n_group,
               topk_group=shape.topk_group, top_k=shape.top_k, scale=shape.routed_scaling,
-              wbits=shape.wbits)
+              wbits=shape.wbits, top_p_value=top_p)
     caches = [dict() for _ in layers]
     shared = [synth.expert_blob(shape, seed, l, synth.SHARED_ID) for l in range(len(layers))]
     spent, done = 0.0, 0
@@ -169,8 +171,8 @@ def cpu_baseline_stack(shape, seed, layers, tokens_fn, T, n_steps):
         spent += time.perf_counter() - t0
         for l, (wr, bias) in enumerate(layers):
             idx, _, _ = oracle.route(xn, wr, bias, shape.n_group, shape.topk_group, shape.top_k,
-                                     shape.routed_scaling)
-            for e in np.unique(idx):  # drawn outside the timed region
+                                     shape.routed_scaling, top_p)
+            for e in np.unique(idx[idx >= 0]):  # drawn outside the timed region
                 if int(e) not in caches[l]:
                     caches[l][int(e)] = synth.expert_blob(shape, seed, l, int(e))
             t0 = time.perf_counter()
@@ -185,7 +187,7 @@ def cpu_baseline_stack(shape, seed, layers, tokens_fn, T, n_steps):
                        f"over output rows; expert records drawn outside the timed region)")
 
 
-def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s):
+def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s, top_p=0.0):
     """Oracle (plain C + OpenMP) on the first steps of the same workload."""
     import oracle
     import synth
@@ -199,13 +201,13 @@ def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s):
     shared = synth.expert_blob(shape, seed, 0, synth.SHARED_ID)
     kw = dict(H=shape.hidden, I=shape.inter, n_experts=shape.n_experts, n_group=shape.n_group,
               topk_group=shape.topk_group, top_k=shape.top_k, scale=shape.routed_scaling,
-              wbits=shape.wbits)
+              wbits=shape.wbits, top_p_value=top_p)
     done_tok, spent, steps = 0, 0.0, 0
     while spent < budget_s and steps < 1024:
         x = tokens_fn(steps)
         idx, _, _ = oracle.route(x, wr, bias, shape.n_group, shape.topk_group, shape.top_k,
-                                 shape.routed_scaling)
-        for e in np.unique(idx):
+                                 shape.routed_scaling, top_p)
+        for e in np.unique(idx[idx >= 0]):
             blob_of(int(e))  # drawn outside the timed region
         t0 = time.perf_counter()
         oracle.layer(x, wr, bias, blob_of, shared, **kw)
@@ -226,6 +228,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--wbits", type=int, default=4, choices=(8, 4, 2))
     ap.add_argument("--ring", type=int, default=0, help="layer instances to cycle (0 = default)")
+    ap.add_argument("--topp", type=float, default=0.0,
+                    help="adaptive expert top-p in (0, 1); 0 = off (plain top-k)")
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly")
     ap.add_argument("--graph-block", type=int, default=64, help="steps per captured graph")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
@@ -255,7 +259,7 @@ def main():
     torch.cuda.set_device(dev)
     moe.lib()
     hip = Hip()
-    cfg = moe.Config.of(shape)
+    cfg = moe.Config.of(shape, args.topp)
     bb = moe.blob_bytes(cfg)
     stream = torch.cuda.Stream(device=dev)  # default priority; graphs cannot capture stream 0
     torch.cuda.set_stream(stream)
@@ -395,8 +399,11 @@ def main():
 
     # --- work accounting ------------------------------------------------------
     idx_h = idx_all.cpu().numpy()
-    U_l = [float(np.mean([np.unique(idx_h[i, l]).size for i in range(W, W + K)]))
-           for l in range(NL)]
+    def distinct(v):  # routed experts of one step (-1: ranks dropped by top-p)
+        return np.unique(v[v >= 0]).size
+
+    U_l = [float(np.mean([distinct(idx_h[i, l]) for i in range(W, W + K)])) for l in range(NL)]
+    pairs = float(np.mean([(idx_h[i] >= 0).sum() for i in range(W, W + K)])) / NL
     U = float(np.mean(U_l))
     step_bytes = sum(layer_bytes(shape, T, u, bb) for u in U_l)
     small = T <= 16  # the layer's small-batch path (four kernels)
@@ -407,11 +414,13 @@ def main():
         roof = {"bound": "hbm", "kernel": dom, "achieved": dom_bytes / dom_sec / 1e9,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] / HBM_PEAK_GBPS
-        roof["traffic"] = measured_traffic(args.workload)
+        # counters were taken on the int4 workload without top-p
+        roof["traffic"] = (measured_traffic(args.workload)
+                           if args.wbits == 4 and not args.topp else None)
         roof.update(bytes_per_launch=dom_bytes, launch_us=dom_sec * 1e6)
     else:  # grouped GEMM on the matrix cores: int8 operations (2 per MAC) of the launch
         dom = "gate_up (grouped int4 x int8 MFMA GEMM + SwiGLU + Q8_0 of h)"
-        ops = 2.0 * T * (shape.top_k + shape.n_shared) * 2 * shape.inter * shape.hidden
+        ops = 2.0 * (pairs + T * shape.n_shared) * 2 * shape.inter * shape.hidden
         roof = {"bound": "mfma", "kernel": dom, "achieved": ops / dom_sec / 1e12,
                 "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "traffic": None,
                 "ops_per_launch": ops, "launch_us": dom_sec * 1e6,
@@ -432,9 +441,11 @@ def main():
         "vs_baseline": None,
         "dtype": f"i{shape.wbits}xi8->i32",
         "data": "synthetic",
-        "config": {"workload": describe(args.workload, shape, T, R, NL), "tokens_per_step": T,
-                   "layers_per_step": NL, "layer_instances": R, "hip_graph": use_graph,
-                   "distinct_routed_experts_per_step": U},
+        "config": {"workload": describe(args.workload, shape, T, R, NL, args.topp),
+                   "tokens_per_step": T, "layers_per_step": NL, "layer_instances": R,
+                   "hip_graph": use_graph, "top_p": args.topp or None,
+                   "distinct_routed_experts_per_step": U,
+                   "routed_pairs_per_layer": pairs},
         "hbm_gbps": step_bytes / (sec / K) / 1e9,
         "hbm_frac": step_bytes / (sec / K) / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
@@ -445,11 +456,11 @@ def main():
         if NL > 1:
             out["cpu_baseline"] = cpu_baseline_stack(shape, seed,
                                                      [(r["wr_h"], r["bias_h"]) for r in ring],
-                                                     tokens_for, T, 2)
+                                                     tokens_for, T, 2, args.topp)
         else:
             r0 = ring[0]
             out["cpu_baseline"] = cpu_baseline(shape, seed, r0["wr_h"], r0["bias_h"], tokens_for,
-                                               T, args.cpu_budget)
+                                               T, args.cpu_budget, args.topp)
     print(json.dumps(out), flush=True)
 
 

@@ -75,7 +75,8 @@ extern "C" {
  * 1 <= top_k <= min(16, topk_group * n_experts / n_group), n_shared in {0,1},
  * wbits in {8, 4, 2}; a weight row holds at most 256 16-byte pieces of codes
  * (448 for int8) along hidden and 128 along inter, i.e. hidden <= 8192 and
- * inter <= 4096 for int4 (16384 / 8192 for int2, 7168 / 2048 for int8). */
+ * inter <= 4096 for int4 (16384 / 8192 for int2, 7168 / 2048 for int8);
+ * top_p = 0 (off), or in (0, 1] (1 is off as well). */
 typedef struct moe_cfg {
   int32_t hidden;       /* H */
   int32_t inter;        /* I, intermediate width of every expert (shared too) */
@@ -86,6 +87,7 @@ typedef struct moe_cfg {
   int32_t n_shared;     /* 0 or 1 shared expert */
   int32_t wbits;        /* 8 (int8), 4 (packed int4) or 2 (packed int2) */
   float routed_scaling; /* routed_scaling_factor applied to routed weights */
+  float top_p;          /* adaptive expert top-p (see moe_route); 0 = off */
 } moe_cfg;
 
 /* Bytes of one packed expert record for cfg (0 if cfg is unsupported). */
@@ -106,6 +108,12 @@ size_t moe_expert_blob_bytes(const moe_cfg *cfg);
  *   of the kept groups by sb (ties: lower expert index) are written to idx in
  *   rank order; w[t,k] = (s[t,idx] / S) * routed_scaling with
  *   S = sum_k s[t,idx[t,k]] added in rank order (fp32).
+ * Adaptive expert top-p ("Show HN…", section モデルのダウンロードと実行,
+ * options list: an expert top-p that cuts expert reads), when 0 < top_p < 1:
+ * with c_j = s_0 + ... + s_j added in rank order (fp32) and thr = top_p * S
+ * (fp32), the first n ranks are kept, n = 1 + the first j with c_j >= thr;
+ * their weights become w = (s / c_{n-1}) * routed_scaling and the other
+ * ranks get idx = -1 and w = 0 (no later call reads an expert for them).
  * idx and w are bit-identical to a CPU implementation of the same steps.
  * workspace: >= moe_route_workspace(cfg, T) bytes (may be NULL if that is 0).
  * Errors: MOE_EINVAL (cfg, T < 0, null pointer), MOE_EALIGN, MOE_EWORKSPACE.
@@ -130,15 +138,15 @@ int moe_quant_act(int32_t rows, int32_t n, const float *x, int8_t *q, float *d, 
  * MoE item; devtrends, "Comment fonctionne le moteur": duplicate requests
  * for one expert are merged).  Slots s = t*K + k of idx [T][K]:
  *   counts[e]   number of slots routed to e                       int32 [E]
- *   offsets[e]  exclusive prefix sum of counts, offsets[E] = T*K  int32 [E+1]
+ *   offsets[e]  exclusive prefix sum of counts; offsets[E] = number
+ *               of routed slots (T*K unless top-p dropped some)   int32 [E+1]
  *   perm        slots grouped by expert, increasing slot (= token) order
- *               inside each expert                                int32 [T*K]
- *   inv[s]      position of slot s in perm                        int32 [T*K]
+ *               inside each expert, then -1 up to T*K             int32 [T*K]
+ *   inv[s]      position of slot s in perm, -1 if not routed      int32 [T*K]
  *   active      experts with counts > 0, ascending, then -1       int32 [E]
  *   n_active    number of such experts                            int32 [1]
- * idx entries outside [0, E) are skipped (they get no position; perm and inv
- * entries for them are left unwritten).  Bit-identical to a stable counting
- * sort on the CPU.
+ * idx entries outside [0, E) (-1: dropped by top-p) are not routed.
+ * Bit-identical to a stable counting sort on the CPU.
  * Errors: MOE_EINVAL (cfg, T < 0, null pointer), MOE_EALIGN.
  * ------------------------------------------------------------------------- */
 int moe_group(const moe_cfg *cfg, int32_t T, const int32_t *idx, int32_t *counts,
@@ -173,7 +181,8 @@ typedef struct moe_ffn_debug {
  *   h[r] = silu(g[r]) * u[r],  silu(z) = z / (1 + e^-z)
  *   (q_h, d_h) = Q8_0(h)
  *   y[j] = sd[j] * sum_b d_h[b] * P_down[j,b]
- * expert_out [T][K][H] receives y of slot (t, k) (unweighted);
+ * expert_out [T][K][H] receives y of slot (t, k) (unweighted; rows of
+ * slots with idx -1 are not written);
  * shared_out [T][H] receives the shared expert's y (required iff n_shared).
  * Grouping (moe_group) runs inside this call on idx, so every distinct
  * expert's weights are streamed once for all its tokens.
@@ -191,7 +200,8 @@ int moe_expert_ffn(const moe_cfg *cfg, int32_t T, const int8_t *q, const float *
  * ("Show HN…", 実装済みの主な機能, router item: routed_scaling_factor and
  * shared expert):
  *   y[t] = residual[t] + shared_out[t] + sum_k w[t,k] * expert_out[t,k]
- * residual and shared_out may be NULL (treated as 0).  If y_norm is not NULL
+ * residual and shared_out may be NULL (treated as 0).  A term with
+ * w[t,k] == 0 is skipped and its expert_out row not read (top-p drops).  If y_norm is not NULL
  * it receives y[t] / sqrt(mean(y[t]^2) + eps) (unit-gain RMSNorm, the input
  * of the next layer in a pre-norm stack).
  * Errors: MOE_EINVAL, MOE_EALIGN.
@@ -217,6 +227,7 @@ enum {
   MOE_STAGE_GATE_UP = 4,
   MOE_STAGE_DOWN = 5,
   MOE_STAGE_COMBINE = 6,
+  MOE_STAGE_NORM = 7,
   MOE_N_STAGES = 8
 };
 typedef struct moe_events {
@@ -227,13 +238,13 @@ typedef struct moe_events {
 /* ---------------------------------------------------------------------------
  * moe_layer — the whole step: routing, Q8_0 of x, grouping, expert FFNs and
  * combine on one stream, with all intermediates in the workspace.  For 1..16
- * tokens (with T*top_k <= 256, hidden <= 8192, and at most 256 / 128 packed
- * 16-byte pieces per gate / down row) it runs as four kernels: router scores
+ * tokens (with T*top_k <= 256) it runs as four kernels: router scores
  * (MOE_STAGE_ROUTER_SCORES); per-token selection beside the shared expert's
  * gate/up (MOE_STAGE_ROUTER_SELECT); batch union and routed gate/up with the
- * Q8_0 of h (MOE_STAGE_GATE_UP); down with the combine (MOE_STAGE_DOWN); and,
- * when y_norm is given, the RMSNorm (MOE_STAGE_COMBINE).  Otherwise it chains the kernels of moe_route,
- * moe_quant_act, moe_expert_ffn and moe_combine.  Both give the same
+ * Q8_0 of h (MOE_STAGE_GATE_UP); down with the combine (MOE_STAGE_DOWN);
+ * then, when y_norm is given, the RMSNorm (MOE_STAGE_NORM).  Otherwise it
+ * chains the kernels of moe_route, moe_quant_act, moe_expert_ffn and
+ * moe_combine (MOE_STAGE_COMBINE, which includes the RMSNorm).  Both give the same
  * arithmetic as the separate calls (bit-identical idx and int32 block dots;
  * float outputs within rounding of the summation order).
  * Workspace precondition: the workspace must be zero-filled before its first

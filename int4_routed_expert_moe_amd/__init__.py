@@ -39,11 +39,12 @@ class MoeCfg(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("wbits", ctypes.c_int32),
-                ("routed_scaling", ctypes.c_float)]
+                ("routed_scaling", ctypes.c_float), ("top_p", ctypes.c_float)]
 
 
 MOE_N_STAGES = 8
-STAGES = dict(router_scores=0, router_select=1, quant=2, group=3, gate_up=4, down=5, combine=6)
+STAGES = dict(router_scores=0, router_select=1, quant=2, group=3, gate_up=4, down=5, combine=6,
+              norm=7)
 
 
 class MoeEvents(ctypes.Structure):
@@ -125,15 +126,16 @@ class Config:
     n_shared: int = 1
     wbits: int = 4
     routed_scaling: float = 2.5
+    top_p: float = 0.0  # adaptive expert top-p; 0 = off
 
     @classmethod
-    def of(cls, shape) -> "Config":
+    def of(cls, shape, top_p: float = 0.0) -> "Config":
         return cls(shape.hidden, shape.inter, shape.n_experts, shape.n_group, shape.topk_group,
-                   shape.top_k, shape.n_shared, shape.wbits, shape.routed_scaling)
+                   shape.top_k, shape.n_shared, shape.wbits, shape.routed_scaling, top_p)
 
     def c(self) -> MoeCfg:
         return MoeCfg(self.hidden, self.inter, self.n_experts, self.n_group, self.topk_group,
-                      self.top_k, self.n_shared, self.wbits, self.routed_scaling)
+                      self.top_k, self.n_shared, self.wbits, self.routed_scaling, self.top_p)
 
 
 def _torch():

@@ -126,4 +126,29 @@ __device__ __forceinline__ int perm2(uint32_t lo, uint32_t hi, uint32_t sel) {
   return (int)__builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Adaptive expert top-p ("Show HN…", section モデルのダウンロードと実行,
+// options list) on one token's unbiased scores sv[0..K) in rank order, S
+// their fp32 left-to-right sum: the number n of ranks kept, the first n with
+// sv[0] + ... + sv[n-1] >= top_p * S (same order, fp32), and that sum in
+// *S_kept.  top_p outside (0, 1) keeps every rank (S_kept = S).
+__device__ __forceinline__ int top_p_keep(const float (&sv)[16], int K, float S, float top_p,
+                                          float *S_kept) {
+  *S_kept = S;
+  if (!(top_p > 0.0f && top_p < 1.0f)) return K;
+  const float thr = top_p * S;
+  float c = 0.0f;
+  int n = K;
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    if (k < K && n == K) {
+      c = c + sv[k];
+      if (c >= thr) {
+        n = k + 1;
+        *S_kept = c;
+      }
+    }
+  }
+  return n;
+}
+
 }  // namespace moe

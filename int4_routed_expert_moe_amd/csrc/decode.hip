@@ -44,6 +44,14 @@ namespace moe {
 #ifndef MOE_K2_ROWS
 #define MOE_K2_ROWS 2
 #endif
+// tokens per chunk of the int4 gate/up kernel for batches of more than one token
+#ifndef MOE_TT_INT4
+#define MOE_TT_INT4 2
+#endif
+// largest batch the four-kernel path takes (at most 16)
+#ifndef MOE_SMALL_T_MAX
+#define MOE_SMALL_T_MAX 16
+#endif
 
 namespace sbk {
 constexpr int TMAX = 16;
@@ -296,9 +304,11 @@ __device__ void select_token(const LayerArgs &a, SelLds &sm, int t) {
     float S = sv[0];
 #pragma unroll
     for (int k = 1; k < 16; k++) S = (k < K) ? S + sv[k] : S;
-    const int e = sm.sel[threadIdx.x];
-    a.idx[t * K + threadIdx.x] = e;
-    a.w[t * K + threadIdx.x] = (sm.ssel[threadIdx.x] / S) * a.scale;
+    float Sk;
+    const int n = top_p_keep(sv, K, S, a.top_p, &Sk);  // n = K unless top-p cuts
+    const bool keep = (int)threadIdx.x < n;
+    a.idx[t * K + threadIdx.x] = keep ? sm.sel[threadIdx.x] : -1;
+    a.w[t * K + threadIdx.x] = keep ? (sm.ssel[threadIdx.x] / Sk) * a.scale : 0.0f;
   }
 }
 
@@ -622,12 +632,15 @@ __device__ void union_slot(const LayerArgs &a, int j, int *ent) {
   const int n = a.T * a.K, E = a.E;
   if (tid < 32) bits[tid] = 0u;
   if (tid == 0) ent[0] = -1;
-  int e = -1;
-  if (tid < n) e = min(max(a.idx[tid], 0), E - 1);
-  __syncthreads();
-  if (tid < n) atomicOr(&bits[e >> 5], 1u << (e & 31));
-  __syncthreads();
+  int e = -1;  // -1: no pair, or a rank dropped by top-p
   if (tid < n) {
+    const int v = a.idx[tid];
+    e = (v >= 0 && v < E) ? v : -1;
+  }
+  __syncthreads();
+  if (e >= 0) atomicOr(&bits[e >> 5], 1u << (e & 31));
+  __syncthreads();
+  if (e >= 0) {
     int r = __popc(bits[e >> 5] & ((1u << (e & 31)) - 1u));
     for (int w = 0; w < (e >> 5); w++) r += __popc(bits[w]);
     if (r == j) ent[0] = e;  // every holder of that expert writes the same value
@@ -900,7 +913,10 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
     };
     float acc = resid;
     if (a.n_shared) acc += full(T * K + t);
-    for (int k = 0; k < K; k++) acc = fmaf(wsh[t * K + k], full(t * K + k), acc);
+    for (int k = 0; k < K; k++) {
+      const float wk = wsh[t * K + k];
+      if (wk != 0.0f) acc = fmaf(wk, full(t * K + k), acc);  // 0: dropped by top-p
+    }
     a.y[(size_t)t * H + j] = acc;
     ss = acc * acc;
   }
@@ -947,7 +963,7 @@ size_t small_batch_slot_ints(int T, int K, int n_shared) {
 }
 
 bool small_batch_supported(const moe_cfg &c, int T) {
-  if (T < 1 || T > sbk::TMAX) return false;
+  if (T < 1 || T > MOE_SMALL_T_MAX) return false;
   if (T * c.top_k > 256) return false;
   if (c.hidden / 64 > 128 || c.hidden % sbk::RT) return false;
   const int per = 128 / c.wbits;  // codes per 16-byte piece
@@ -975,7 +991,7 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
              st, stage_ev(ev, MOE_STAGE_DOWN), a);
   if (a.y_norm)
     launch_k(k_norm_small, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, st,
-             stage_ev(ev, MOE_STAGE_COMBINE), a, a.H / sbk::RT);
+             stage_ev(ev, MOE_STAGE_NORM), a, a.H / sbk::RT);
 }
 
 template <int WB, int TT>
@@ -1002,7 +1018,7 @@ void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev) {
     else launch3_np<8, 2>(a, st, ev);
   } else if (a.wbits == 4) {
     if (a.T == 1) launch3_np<4, 1>(a, st, ev);
-    else launch3_np<4, 4>(a, st, ev);
+    else launch3_np<4, MOE_TT_INT4>(a, st, ev);
   } else {
     // an int2 activation fragment covers 64 codes: two tokens per chunk keep
     // the registers within two waves per SIMD

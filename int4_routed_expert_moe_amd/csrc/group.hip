@@ -89,6 +89,7 @@ __global__ void __launch_bounds__(GW * 64) k_group(int n_slots, int E,
     offsets[E] = n_used;
     n_active[0] = n_act;
   }
+  for (int i = n_used + tid; i < n_slots; i += GW * 64) perm[i] = -1;  // unrouted tail
   __syncthreads();  // active[] = -1 is ordered before the compaction below
   if (tid < E && c > 0) active[ex_a] = tid;
 
@@ -98,7 +99,7 @@ __global__ void __launch_bounds__(GW * 64) k_group(int n_slots, int E,
   for (int base = s_lo; base < s_hi; base += 64) {
     const int s = base + lane;
     int e = (s < s_hi) ? idx[s] : -1;
-    if (e >= E) e = -1;
+    if (e >= E || e < 0) e = -1;
     int rank = 0, same = 0;
     for (int j = 0; j < 64; j++) {
       const int ej = __shfl(e, j, 64);
@@ -112,6 +113,8 @@ __global__ void __launch_bounds__(GW * 64) k_group(int n_slots, int E,
       perm[pos] = s;
       inv[s] = pos;
       if (rank == 0) hist[wv * E + e] += same;  // the first lane holding e advances
+    } else if (s < s_hi) {
+      inv[s] = -1;  // not routed (top-p drop)
     }
     __builtin_amdgcn_wave_barrier();
   }

@@ -76,6 +76,7 @@ void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_
 struct LayerArgs {
   int H, I, E, G, TG, K, T, n_shared, wbits;
   float scale, eps;
+  float top_p;  // adaptive expert top-p; 0 or 1 = off
   size_t blob_bytes;
   const float *x, *wr, *bias, *residual;
   const uint8_t *experts, *shared;

@@ -23,6 +23,11 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// smallest batch whose expert FFNs run as grouped MFMA GEMMs (int4 / int2)
+#ifndef MOE_MFMA_MIN_T
+#define MOE_MFMA_MIN_T 17
+#endif
+
 int check_cfg(const moe_cfg *c) {
   if (!c) return fail(MOE_EINVAL, "cfg is NULL");
   if (c->hidden <= 0 || c->hidden % 256)
@@ -50,6 +55,8 @@ int check_cfg(const moe_cfg *c) {
     return fail(MOE_EINVAL, "n_shared=%d not in {0,1}", c->n_shared);
   if (!(c->routed_scaling > 0.0f) || c->routed_scaling > 1e30f)
     return fail(MOE_EINVAL, "routed_scaling must be finite and > 0");
+  if (!(c->top_p >= 0.0f && c->top_p <= 1.0f))
+    return fail(MOE_EINVAL, "top_p must be 0 (off) or in (0, 1]");
   return MOE_OK;
 }
 
@@ -194,7 +201,7 @@ int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32
   const bool mfma = moe::mfma_supported(a);
   if (c.wbits == 8 && !mfma)  // the vector-dot kernels take packed int4 / int2 only
     return fail(MOE_EINVAL, "int8 experts need the matrix-core path (H %% 256, I %% 64)");
-  if ((T > 16 || c.wbits == 8) && mfma) {  // grouped GEMMs, matrix cores
+  if ((T >= MOE_MFMA_MIN_T || c.wbits == 8) && mfma) {  // grouped GEMMs, matrix cores
     const size_t pairs = (size_t)T * c.top_k + (size_t)T * c.n_shared;
     int8_t *q_h = reinterpret_cast<int8_t *>(ws.h);
     float *d_h = reinterpret_cast<float *>(q_h + ((pairs * c.inter + 255) & ~(size_t)255));
@@ -403,6 +410,7 @@ int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
     a.n_shared = c.n_shared;
     a.wbits = c.wbits;
     a.scale = c.routed_scaling;
+    a.top_p = c.top_p;
     a.eps = eps;
     a.blob_bytes = blob_bytes(c);
     a.x = x;

@@ -68,8 +68,9 @@ __global__ void __launch_bounds__(256) k_combine(int H, int K, const float *__re
       acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
     }
     for (int k = 0; k < K; k++) {
-      float4 e = eo4[(size_t)k * H4 + j];
       const float c = wk[k];
+      if (c == 0.0f) continue;  // a rank dropped by top-p: its row is not read
+      float4 e = eo4[(size_t)k * H4 + j];
       acc.x = fmaf(c, e.x, acc.x);
       acc.y = fmaf(c, e.y, acc.y);
       acc.z = fmaf(c, e.z, acc.z);

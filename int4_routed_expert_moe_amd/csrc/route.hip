@@ -219,8 +219,10 @@ void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *
 //  2. TG rounds of a wave-wide max over (score, -group) keep the groups;
 //  3. K rounds of a wave-wide max over (sb, -expert) among kept groups pick
 //     the experts in rank order;
-//  4. w_k = (s_k / S) * scale, S summed in rank order.
+//  4. w_k = (s_k / S) * scale, S summed in rank order; with top-p, only the
+//     kept ranks, renormalised over their own sum.
 __global__ void __launch_bounds__(64) k_router_select(int E, int G, int TG, int K, float scale,
+                                                      float top_p,
                                                       const float *__restrict__ s,
                                                       const float *__restrict__ sb,
                                                       int32_t *__restrict__ idx,
@@ -281,20 +283,26 @@ __global__ void __launch_bounds__(64) k_router_select(int E, int G, int TG, int 
     }
   }
   __syncthreads();
-  if (lane == 0) {
-    float S = ssel[0];
-    for (int k = 1; k < K; k++) S = S + ssel[k];
-    for (int k = 0; k < K; k++) {
-      idx[(size_t)t * K + k] = isel[k];
-      w[(size_t)t * K + k] = (ssel[k] / S) * scale;
-    }
+  if (lane < K) {
+    float sv[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) sv[k] = k < K ? ssel[k] : 0.0f;
+    float S = sv[0];
+#pragma unroll
+    for (int k = 1; k < 16; k++) S = (k < K) ? S + sv[k] : S;
+    float Sk;
+    const int n = top_p_keep(sv, K, S, top_p, &Sk);  // n = K unless top-p cuts
+    const bool keep = lane < n;
+    idx[(size_t)t * K + lane] = keep ? isel[lane] : -1;
+    w[(size_t)t * K + lane] = keep ? (ssel[lane] / Sk) * scale : 0.0f;
   }
 }
 
 void launch_router_select(const moe_cfg &c, int T, const float *s, const float *sb,
                           int32_t *idx, float *w, hipStream_t st, const moe_events *ev) {
   launch_k(k_router_select, dim3(T), dim3(64), 0, st, stage_ev(ev, MOE_STAGE_ROUTER_SELECT),
-           c.n_experts, c.n_group, c.topk_group, c.top_k, c.routed_scaling, s, sb, idx, w);
+           c.n_experts, c.n_group, c.topk_group, c.top_k, c.routed_scaling, c.top_p, s, sb, idx,
+           w);
 }
 
 }  // namespace moe

@@ -101,12 +101,12 @@ def test_quant_act_hand_blocks_and_extremes(dev):
 
 # ------------------------------------------------------------------ router
 
-def _route_check(layer, x, dev):
+def _route_check(layer, x, dev, top_p=0.0):
     s = layer.shape
-    cfg = moe.Config.of(s)
+    cfg = moe.Config.of(s, top_p)
     idx, w = moe.route(cfg, to_d(x, dev), layer.wr_d, layer.bias_d)
     ri, rw, margin = oracle.route(x, layer.wr, layer.bias, s.n_group, s.topk_group, s.top_k,
-                                  s.routed_scaling)
+                                  s.routed_scaling, top_p)
     assert np.array_equal(h(idx), ri)
     assert np.array_equal(h(w).view(np.uint32), rw.view(np.uint32))
     return margin
@@ -130,6 +130,17 @@ def test_route_prefill_zipf(dev):
     lay = DeviceLayer(synth.REAL, synth.SEEDS["prefill"], bias="zipf")
     x = synth.tokens(synth.REAL, synth.SEEDS["prefill"], 2048)
     _route_check(lay, x, dev)
+
+
+# Adaptive expert top-p (the cut runs in the wave-per-token selector here).
+
+@pytest.mark.parametrize("p", [0.3, 0.7, 0.9])
+def test_route_top_p(dev, real, p):
+    x = synth.tokens(synth.REAL, synth.SEEDS["decode"], 40, start=3)
+    _route_check(real, x, dev, top_p=p)
+    idx, _ = moe.route(moe.Config.of(synth.REAL, p), to_d(x, dev), real.wr_d, real.bias_d)
+    if p < 0.8:
+        assert (h(idx) < 0).any()  # the cut drops ranks on this workload
 
 
 # ------------------------------------------------------------------ grouping
@@ -156,7 +167,20 @@ def _idx_case(T, K, E, kind, seed):
     (4096, 16, 64, "rand"),
 ])
 def test_group_bit_exact(dev, T, K, E, kind):
-    idx = _idx_case(T, K, E, kind, T * 31 + K)
+    _group_check(dev, _idx_case(T, K, E, kind, T * 31 + K), E)
+
+
+@pytest.mark.parametrize("T,K,E", [(1, 8, 256), (16, 8, 256), (2048, 8, 256), (37, 3, 10)])
+def test_group_with_dropped_ranks(dev, T, K, E):
+    idx = _idx_case(T, K, E, "rand", T + K)
+    keep = np.random.default_rng(T).integers(1, K + 1, T)
+    for t in range(T):
+        idx[t, keep[t]:] = -1
+    _group_check(dev, idx, E)
+
+
+def _group_check(dev, idx, E):
+    T, K = idx.shape
     cfg = moe.Config(hidden=256, inter=128, n_experts=E, n_group=1, topk_group=1, top_k=K)
     g = moe.group(cfg, to_d(idx, dev))
     ref = oracle.group(idx, E)
@@ -292,16 +316,16 @@ def test_rmsnorm(dev):
 
 # ------------------------------------------------------------------ whole layer
 
-def _layer_check(layer, x, dev, residual=None, want_norm=False):
+def _layer_check(layer, x, dev, residual=None, want_norm=False, top_p=0.0):
     s = layer.shape
-    cfg = moe.Config.of(s)
+    cfg = moe.Config.of(s, top_p)
     T = x.shape[0]
     idx_d = torch.empty((T, s.top_k), dtype=torch.int32, device=dev)
     w_d = torch.empty((T, s.top_k), dtype=torch.float32, device=dev)
     out = moe.layer(cfg, to_d(x, dev), layer.wr_d, layer.bias_d, layer.experts_d, layer.shared_d,
                     residual=None if residual is None else to_d(residual, dev),
                     want_norm=want_norm, idx_out=idx_d, w_out=w_d)
-    ref = layer.oracle_layer(x, residual, want_norm)
+    ref = layer.oracle_layer(x, residual, want_norm, top_p)
     assert np.array_equal(h(idx_d), ref["idx"])
     assert np.array_equal(h(w_d), ref["w"])
     if want_norm:
@@ -340,6 +364,31 @@ def test_layer_residual_norm(dev, real):
 def test_layer_int2_decode(dev):
     lay = DeviceLayer(synth.REAL.with_bits(2), synth.SEEDS["stack"])
     _layer_check(lay, synth.tokens(synth.REAL, synth.SEEDS["stack"], 1), dev)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16, 40])
+def test_layer_top_p(dev, real, T):
+    """Decode, verify and the chained path (T > 16) with top-p 0.7."""
+    x = synth.tokens_perturbed(synth.REAL, synth.SEEDS["verify"], T) if T > 1 else \
+        synth.tokens(synth.REAL, synth.SEEDS["decode"], 1, start=4)
+    _layer_check(real, x, dev, top_p=0.7)
+
+
+def test_layer_top_p_tiny_ragged(dev, tiny):
+    for T, p in ((1, 0.5), (5, 0.6), (33, 0.55)):
+        _layer_check(tiny, synth.tokens(synth.TINY, 79, T), dev, top_p=p)
+
+
+def test_combine_skips_dropped_rows(dev):
+    rng = np.random.default_rng(3)
+    T, K, H = 3, 8, 256
+    eo = rng.standard_normal((T, K, H)).astype(np.float32)
+    w = rng.uniform(0.1, 1, (T, K)).astype(np.float32)
+    w[:, 5:] = 0.0
+    eo[:, 5:] = np.nan  # never read
+    out = h(moe.combine(to_d(eo, dev), to_d(w, dev), None, None))
+    eo[:, 5:] = 0.0
+    assert_close_rms(out, oracle.combine(eo, w), 1e-5, "y")
 
 
 def test_layer_tiny_int8(dev):
