@@ -267,6 +267,88 @@ int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
               float *w_out, void *workspace, size_t ws_bytes, const moe_events *ev,
               void *stream);
 
+/* ---------------------------------------------------------------------------
+ * moe_layer_ptrs — moe_layer with the routed expert records addressed one by
+ * one: expert_ptrs is a device array of E pointers, entry e the record of
+ * routed expert e (layout as above, 256-byte aligned), in any memory the
+ * device can read — HBM, or pinned host memory for experts not resident on
+ * the GPU (read over the host link as the kernels stream them).  This is
+ * the device side of an expert cache for models larger than HBM ("Show
+ * HN…", section ディスクストリーミングベースの MoE 実行方式: experts streamed
+ * on demand into a cache, the learning cache pinning frequent ones): a
+ * caller can move records between host and HBM and rewrite table entries
+ * between calls (see moe_cache_*).  Same results as moe_layer on the same
+ * record bytes; same arguments, workspace and errors otherwise.
+ * ------------------------------------------------------------------------- */
+int moe_layer_ptrs(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
+                   const float *bias, const void *const *expert_ptrs, const void *shared,
+                   const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
+                   float *w_out, void *workspace, size_t ws_bytes, const moe_events *ev,
+                   void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Expert cache (host runtime around moe_layer_ptrs) — "Show HN…", section
+ * ディスクストリーミングベースの MoE 実行方式 (per-layer LRU cache and pinned hot
+ * store for experts loaded on demand) and section Learning cache (usage of
+ * routed experts recorded, the hottest pinned at start-up).  One cache per
+ * layer.  The cold copy of every routed record is in pinned host memory
+ * (host_records[e]: device-readable addresses, see moe_host_device_ptr);
+ * `slots` holds n_slots records in HBM; `table` is the device array of E
+ * record pointers that moe_layer_ptrs reads.  Slots [0, n_pinned) take the
+ * experts with the largest counts in `usage` (nullable; ties to the lower
+ * id, zero counts not pinned), copied at creation; the other slots are LRU.
+ *
+ * moe_cache_step is called after each moe_layer_ptrs call on the same
+ * stream, with that call's idx (device, n = T*K entries, -1 allowed).  It
+ * enqueues a read-back of idx; for every earlier call whose idx has landed
+ * (all of them, in order, when wait != 0) it counts each distinct routed
+ * expert as a hit (the call read it from HBM) or a miss (from host memory),
+ * adds it to the usage counts, and promotes up to max_promote missed
+ * experts per call into LRU slots (an empty slot, else the least recently
+ * hit).  A victim's table entry is pointed back at host memory on `stream`
+ * first; the record copy then runs on the cache's own copy stream after an
+ * event on `stream` (so no earlier kernel still reads the slot), and the new
+ * entry is written on `stream` once the copy has landed (at a later call, or
+ * within this call when wait != 0).  `stream` never waits for a copy; with
+ * wait == 0 the host waits only when 32 read-backs are outstanding.
+ * Results of moe_layer_ptrs do not depend on the cache state (same bytes
+ * either way).  Not thread-safe; not capturable in a HIP graph.  create
+ * allocates host memory (the handle, a pinned read-back ring) and a stream;
+ * destroy waits for the copy stream and frees them.
+ * Errors: MOE_EINVAL, MOE_EALIGN (slots 256-byte, table 8-byte, every host
+ * record 256-byte aligned), MOE_EHIP.
+ * ------------------------------------------------------------------------- */
+typedef struct moe_cache moe_cache;
+typedef struct moe_cache_stats {
+  uint64_t steps;        /* calls accounted (idx landed) */
+  uint64_t routed;       /* distinct routed experts over those calls */
+  uint64_t hits;         /* of which read from HBM */
+  uint64_t misses;       /* of which read from host memory */
+  uint64_t promotions;   /* record copies started */
+  uint64_t completed;    /* record copies landed and published */
+  uint64_t bytes_copied; /* host -> HBM bytes of the promotions */
+  int32_t resident;      /* experts whose entry points at HBM now */
+} moe_cache_stats;
+
+/* Device-readable address of pinned host memory (hipHostGetDevicePointer). */
+int moe_host_device_ptr(const void *host, void **dev);
+int moe_cache_create(const moe_cfg *cfg, int32_t n_slots, int32_t n_pinned, int32_t max_promote,
+                     int32_t max_pairs, const void *const *host_records, void *slots,
+                     void *table, const uint64_t *usage, void *stream, moe_cache **out);
+int moe_cache_step(moe_cache *c, const int32_t *idx, int32_t n, int32_t wait, void *stream);
+int moe_cache_get_stats(const moe_cache *c, moe_cache_stats *s);
+/* usage [E]: the recorded counts (start-up counts included), for the next
+ * run's pinning; slot_of [E]: slot of each expert, -1 when read from host. */
+int moe_cache_usage(const moe_cache *c, uint64_t *usage);
+int moe_cache_slot_of(const moe_cache *c, int32_t *slot_of);
+int moe_cache_destroy(moe_cache *c);
+/* The cache policy alone on the host, for tests: n_steps calls of n idx
+ * entries each, copies landing before the next call (as with wait != 0);
+ * hits/misses per call [n_steps], final slot_of [n_experts]. */
+int moe_cache_simulate(int32_t n_experts, int32_t n_slots, int32_t n_pinned, int32_t max_promote,
+                       const uint64_t *usage, const int32_t *idx, int32_t n_steps, int32_t n,
+                       int32_t *hits, int32_t *misses, int32_t *slot_of);
+
 /* Name of a return code, and the calling thread's last detailed message. */
 const char *moe_strerror(int code);
 const char *moe_last_error(void);

@@ -23,8 +23,10 @@ MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 EXPORTS = (
     "moe_expert_blob_bytes", "moe_route_workspace", "moe_route", "moe_quant_act", "moe_group",
     "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_combine", "moe_rmsnorm",
-    "moe_layer_workspace", "moe_layer_sync_bytes", "moe_layer", "moe_strerror",
-    "moe_last_error",
+    "moe_layer_workspace", "moe_layer_sync_bytes", "moe_layer", "moe_layer_ptrs",
+    "moe_host_device_ptr", "moe_cache_create", "moe_cache_step", "moe_cache_get_stats",
+    "moe_cache_usage", "moe_cache_slot_of", "moe_cache_destroy", "moe_cache_simulate",
+    "moe_strerror", "moe_last_error",
 )
 
 
@@ -55,6 +57,13 @@ class MoeFfnDebug(ctypes.Structure):
     _fields_ = [("gate_dots", ctypes.c_void_p), ("up_dots", ctypes.c_void_p),
                 ("h", ctypes.c_void_p), ("q_h", ctypes.c_void_p), ("d_h", ctypes.c_void_p),
                 ("down_dots", ctypes.c_void_p)]
+
+
+class MoeCacheStats(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_uint64), ("routed", ctypes.c_uint64),
+                ("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64),
+                ("promotions", ctypes.c_uint64), ("completed", ctypes.c_uint64),
+                ("bytes_copied", ctypes.c_uint64), ("resident", ctypes.c_int32)]
 
 
 _lib = None
@@ -101,6 +110,26 @@ def lib():
     L.moe_layer.argtypes = [pc, i32, v, v, v, v, v, v, v, v, f32, v, v, v, sz,
                             ctypes.POINTER(MoeEvents), v]
     L.moe_layer.restype = ctypes.c_int
+    L.moe_layer_ptrs.argtypes = L.moe_layer.argtypes
+    L.moe_layer_ptrs.restype = ctypes.c_int
+    u64p, i32p = ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int32)
+    L.moe_host_device_ptr.argtypes = [v, ctypes.POINTER(v)]
+    L.moe_host_device_ptr.restype = ctypes.c_int
+    L.moe_cache_create.argtypes = [pc, i32, i32, i32, i32, ctypes.POINTER(v), v, v, u64p, v,
+                                   ctypes.POINTER(v)]
+    L.moe_cache_create.restype = ctypes.c_int
+    L.moe_cache_step.argtypes = [v, v, i32, i32, v]
+    L.moe_cache_step.restype = ctypes.c_int
+    L.moe_cache_get_stats.argtypes = [v, ctypes.POINTER(MoeCacheStats)]
+    L.moe_cache_get_stats.restype = ctypes.c_int
+    L.moe_cache_usage.argtypes = [v, u64p]
+    L.moe_cache_usage.restype = ctypes.c_int
+    L.moe_cache_slot_of.argtypes = [v, i32p]
+    L.moe_cache_slot_of.restype = ctypes.c_int
+    L.moe_cache_destroy.argtypes = [v]
+    L.moe_cache_destroy.restype = ctypes.c_int
+    L.moe_cache_simulate.argtypes = [i32, i32, i32, i32, u64p, i32p, i32, i32, i32p, i32p, i32p]
+    L.moe_cache_simulate.restype = ctypes.c_int
     L.moe_strerror.argtypes = [ctypes.c_int]
     L.moe_strerror.restype = ctypes.c_char_p
     L.moe_last_error.argtypes = []
@@ -305,3 +334,112 @@ def layer(cfg: Config, x, w_router, bias, experts, shared=None, residual=None, y
                            eps, _ptr(idx_out), _ptr(w_out), _ptr(ws), ws.numel(),
                            ctypes.byref(events) if events is not None else None, _stream()))
     return (y, y_norm) if want_norm else y
+
+
+def layer_ptrs(cfg: Config, x, w_router, bias, expert_ptrs, shared=None, residual=None, y=None,
+               y_norm=None, eps=1e-5, want_norm=False, idx_out=None, w_out=None,
+               workspace=None, events=None):
+    """moe_layer_ptrs: as layer(), the routed records given by a device int64
+    tensor of E record addresses (HBM or device-readable pinned host memory)."""
+    torch = _torch()
+    T, H = x.shape
+    y = y if y is not None else torch.empty((T, H), dtype=torch.float32, device=x.device)
+    if want_norm and y_norm is None:
+        y_norm = torch.empty_like(y)
+    ws = _workspace(layer_workspace(cfg, T), x.device, workspace)
+    _check(lib().moe_layer_ptrs(ctypes.byref(cfg.c()), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                                _ptr(expert_ptrs), _ptr(shared), _ptr(residual), _ptr(y),
+                                _ptr(y_norm), eps, _ptr(idx_out), _ptr(w_out), _ptr(ws),
+                                ws.numel(), ctypes.byref(events) if events is not None else None,
+                                _stream()))
+    return (y, y_norm) if want_norm else y
+
+
+def host_device_ptr(host_tensor) -> int:
+    """Device-readable address of a pinned host tensor's storage."""
+    out = ctypes.c_void_p()
+    _check(lib().moe_host_device_ptr(ctypes.c_void_p(host_tensor.data_ptr()), ctypes.byref(out)))
+    return int(out.value)
+
+
+class ExpertCache:
+    """One layer's expert cache (moe_cache_*): routed records in pinned host
+    memory (``host_records``: a pinned uint8 tensor of E records), ``n_slots``
+    of them cached in HBM, and the device table of record pointers that
+    ``layer_ptrs`` reads (``self.table``)."""
+
+    def __init__(self, cfg: Config, host_records, n_slots: int, n_pinned: int = 0,
+                 max_promote: int = 2, max_pairs: int = 256, usage=None, device="cuda:0"):
+        torch = _torch()
+        import numpy as np
+        self.cfg = cfg
+        bb = blob_bytes(cfg)
+        E = cfg.n_experts
+        assert host_records.is_pinned() and host_records.numel() >= E * bb
+        base = host_device_ptr(host_records)
+        recs = (ctypes.c_void_p * E)(*[base + e * bb for e in range(E)])
+        self.host_records = host_records
+        self.slots = torch.empty(max(n_slots, 1) * bb, dtype=torch.uint8, device=device)
+        self.table = torch.empty(E, dtype=torch.int64, device=device)
+        self.max_pairs = max_pairs
+        u = None
+        if usage is not None:
+            self._usage = np.ascontiguousarray(usage, dtype=np.uint64)
+            u = self._usage.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
+        h = ctypes.c_void_p()
+        _check(lib().moe_cache_create(ctypes.byref(cfg.c()), n_slots, n_pinned, max_promote,
+                                      max_pairs, recs, _ptr(self.slots), _ptr(self.table), u,
+                                      _stream(), ctypes.byref(h)))
+        self._h = h
+
+    def step(self, idx, wait=False):
+        _check(lib().moe_cache_step(self._h, _ptr(idx), idx.numel(), int(bool(wait)), _stream()))
+
+    def stats(self) -> dict:
+        s = MoeCacheStats()
+        _check(lib().moe_cache_get_stats(self._h, ctypes.byref(s)))
+        return {k: getattr(s, k) for k, _ in MoeCacheStats._fields_}
+
+    def usage(self):
+        import numpy as np
+        out = np.zeros(self.cfg.n_experts, np.uint64)
+        _check(lib().moe_cache_usage(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))))
+        return out
+
+    def slot_of(self):
+        import numpy as np
+        out = np.zeros(self.cfg.n_experts, np.int32)
+        _check(lib().moe_cache_slot_of(self._h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+        return out
+
+    def close(self):
+        if self._h:
+            lib().moe_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def cache_simulate(n_experts, n_slots, n_pinned, max_promote, idx, usage=None):
+    """The cache policy alone (host): per-step hits and misses, final slot_of."""
+    import numpy as np
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    n_steps = idx.shape[0]
+    n = idx[0].size if n_steps else 0
+    hits = np.zeros(n_steps, np.int32)
+    misses = np.zeros(n_steps, np.int32)
+    slot_of = np.zeros(n_experts, np.int32)
+    u = None
+    if usage is not None:
+        usage = np.ascontiguousarray(usage, dtype=np.uint64)
+        u = usage.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    _check(lib().moe_cache_simulate(n_experts, n_slots, n_pinned, max_promote, u,
+                                    idx.ctypes.data_as(i32p), n_steps, n,
+                                    hits.ctypes.data_as(i32p), misses.ctypes.data_as(i32p),
+                                    slot_of.ctypes.data_as(i32p)))
+    return hits, misses, slot_of

@@ -126,6 +126,15 @@ __device__ __forceinline__ int perm2(uint32_t lo, uint32_t hi, uint32_t sel) {
   return (int)__builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// Record of routed expert e (0 <= e < E): entry e of the caller's table of
+// record pointers when there is one (records may then sit anywhere the
+// device can read: HBM cache slots, pinned host memory), else
+// experts + e * blob_bytes.
+template <class Args>
+__device__ __forceinline__ const uint8_t *expert_record(const Args &a, int e) {
+  return a.expert_ptrs ? a.expert_ptrs[e] : a.experts + (size_t)e * a.blob_bytes;
+}
+
 // Adaptive expert top-p ("Show HN…", section モデルのダウンロードと実行,
 // options list) on one token's unbiased scores sv[0..K) in rank order, S
 // their fp32 left-to-right sum: the number n of ranks kept, the first n with

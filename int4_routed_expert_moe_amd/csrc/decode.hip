@@ -700,7 +700,7 @@ __global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
   constexpr int KS = WB == 8 && NPL > 4 ? 2 : 1;
   gate_up_rows<WB, TT, KS == 2 ? 4 : NPL,
                (TT == 1 ? (WB == 2 ? 2 * MOE_K2_ROWS : WB == 8 ? 1 : MOE_K2_ROWS) : 1), KS>(
-      a, hb, a.experts + (size_t)e * a.blob_bytes, blk, n_tok, pairs,
+      a, hb, expert_record(a, e), blk, n_tok, pairs,
       [&](int i) { return (const int8_t *)(a.q + (size_t)min(max(toks[i], 0), a.T - 1) * a.H); },
       [&](int i) {
         return (const float *)(a.d + (size_t)min(max(toks[i], 0), a.T - 1) * (a.H / 32));
@@ -861,7 +861,7 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
       const bool ok_s = s0 + b < n_slots;
       const int ex = ok_s ? tab[(s0 + b) * TAB_W] : -1;
       const uint8_t *blob =
-          ex < 0 ? a.shared : a.experts + (size_t)min(ex, a.E - 1) * a.blob_bytes;
+          ex < 0 ? a.shared : expert_record(a, min(ex, a.E - 1));
       const uint8_t *down = blob + down_off;
       const float *sdp =
           reinterpret_cast<const float *>(blob + 3 * (size_t)I * ((size_t)H * WB / 8)) + 2 * I;

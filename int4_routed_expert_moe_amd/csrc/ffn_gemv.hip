@@ -52,7 +52,7 @@ __device__ __forceinline__ bool slot_info(const FfnArgs &a, int j, SlotInfo &si)
   if (act >= *a.n_active) return false;
   const int e = a.active[act];
   const int lo = a.offsets[e], hi = a.offsets[e + 1];
-  si.blob = a.experts + (size_t)e * a.blob_bytes;
+  si.blob = expert_record(a, e);
   si.n_tok = hi - lo;
   si.shared = false;
   si.list = a.perm + lo;

@@ -94,7 +94,7 @@ struct TileInfo {
 __device__ __forceinline__ TileInfo tile_info(const FfnArgs &a, int4 t) {
   TileInfo r;
   r.shared = t.x >= a.E;
-  r.blob = r.shared ? a.shared : a.experts + (size_t)min(max(t.x, 0), a.E - 1) * a.blob_bytes;
+  r.blob = r.shared ? a.shared : expert_record(a, min(max(t.x, 0), a.E - 1));
   r.n = min(max(t.z, 0), mf::NT);
   return r;
 }

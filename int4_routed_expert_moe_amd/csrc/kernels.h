@@ -8,6 +8,9 @@
 
 namespace moe {
 
+// Sets the calling thread's message for moe_last_error and returns code.
+int set_error(int code, const char *msg);
+
 // Kernel timestamps: a stage launched with a non-null event pair goes through
 // hipExtLaunchKernelGGL, which stamps the events from the kernel's own
 // dispatch (no extra queue packets).
@@ -55,6 +58,7 @@ struct FfnArgs {
   const int8_t *q;
   const float *d;
   const uint8_t *experts;
+  const uint8_t *const *expert_ptrs;  // nullable: per-expert record pointers
   const uint8_t *shared;
   const int32_t *offsets, *perm, *active, *n_active;
   float *h;        // [P][I] fp32 workspace
@@ -80,6 +84,7 @@ struct LayerArgs {
   size_t blob_bytes;
   const float *x, *wr, *bias, *residual;
   const uint8_t *experts, *shared;
+  const uint8_t *const *expert_ptrs;  // nullable: per-expert record pointers
   float *y, *y_norm;
   int32_t *idx;
   float *w;

@@ -19,6 +19,17 @@ int fail(int code, const char *fmt, ...) {
   return code;
 }
 
+}  // namespace
+
+namespace moe {
+int set_error(int code, const char *msg) {
+  snprintf(g_msg, sizeof(g_msg), "%s", msg);
+  return code;
+}
+}  // namespace moe
+
+namespace {
+
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -173,7 +184,7 @@ int do_route(const moe_cfg &c, int T, const float *x, const float *wr, const flo
 int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32_t *idx,
            const void *experts, const void *shared, float *expert_out, float *shared_out,
            const FfnWs &ws, const moe_ffn_debug *dbg, hipStream_t st,
-           const moe_events *ev = nullptr) {
+           const moe_events *ev = nullptr, const void *const *expert_ptrs = nullptr) {
   moe::launch_group(T * c.top_k, c.n_experts, idx, ws.counts, ws.offsets, ws.perm, ws.inv,
                     ws.active, ws.n_active, st, ev);
   moe::FfnArgs a;
@@ -188,6 +199,7 @@ int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32
   a.q = q;
   a.d = d;
   a.experts = static_cast<const uint8_t *>(experts);
+  a.expert_ptrs = reinterpret_cast<const uint8_t *const *>(expert_ptrs);
   a.shared = static_cast<const uint8_t *>(shared);
   a.offsets = ws.offsets;
   a.perm = ws.perm;
@@ -364,11 +376,17 @@ size_t moe_layer_workspace(const moe_cfg *cfg, int32_t T) {
 
 size_t moe_layer_sync_bytes(void) { return moe::small_batch_sync_bytes(); }
 
-int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
-              const float *bias, const void *experts, const void *shared,
-              const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
-              float *w_out, void *workspace, size_t ws_bytes, const moe_events *ev,
-              void *stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_layer with the routed records either contiguous (experts) or given one
+// pointer each (expert_ptrs, a device array of E pointers); exactly one is set.
+int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
+               const float *bias, const void *experts, const void *const *expert_ptrs,
+               const void *shared, const float *residual, float *y, float *y_norm, float eps,
+               int32_t *idx_out, float *w_out, void *workspace, size_t ws_bytes,
+               const moe_events *ev, void *stream) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
@@ -377,13 +395,17 @@ int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
   REQUIRE(x, "x");
   REQUIRE(w_router, "w_router");
   REQUIRE(bias, "bias");
-  REQUIRE(experts, "experts");
   REQUIRE(y, "y");
   OPTIONAL(residual, "residual");
   OPTIONAL(y_norm, "y_norm");
   OPTIONAL(idx_out, "idx_out");
   OPTIONAL(w_out, "w_out");
-  if (!aligned(experts, 256)) return fail(MOE_EALIGN, "experts is not 256-byte aligned");
+  if (expert_ptrs) {
+    if (!aligned(expert_ptrs, 8)) return fail(MOE_EALIGN, "expert_ptrs is not 8-byte aligned");
+  } else {
+    REQUIRE(experts, "experts");
+    if (!aligned(experts, 256)) return fail(MOE_EALIGN, "experts is not 256-byte aligned");
+  }
   if (cfg->n_shared) {
     REQUIRE(shared, "shared");
     if (!aligned(shared, 256)) return fail(MOE_EALIGN, "shared is not 256-byte aligned");
@@ -418,6 +440,7 @@ int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
     a.bias = bias;
     a.residual = residual;
     a.experts = static_cast<const uint8_t *>(experts);
+    a.expert_ptrs = reinterpret_cast<const uint8_t *const *>(expert_ptrs);
     a.shared = c.n_shared ? static_cast<const uint8_t *>(shared) : nullptr;
     a.y = y;
     a.y_norm = y_norm;
@@ -440,11 +463,35 @@ int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
   moe::launch_quant_act(x, ws.q, ws.d, (int64_t)T * c.hidden, st, ev);
   if ((rc = launched("moe_layer quant"))) return rc;
   if ((rc = do_ffn(c, T, ws.q, ws.d, idx, experts, c.n_shared ? shared : nullptr, ws.expert_out,
-                   c.n_shared ? ws.shared_out : nullptr, ws.ffn, nullptr, st, ev)))
+                   c.n_shared ? ws.shared_out : nullptr, ws.ffn, nullptr, st, ev, expert_ptrs)))
     return rc;
   moe::launch_combine(T, c.hidden, c.top_k, ws.expert_out, w,
                       c.n_shared ? ws.shared_out : nullptr, residual, y, y_norm, eps, st, ev);
   return launched("moe_layer combine");
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
+              const float *bias, const void *experts, const void *shared,
+              const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
+              float *w_out, void *workspace, size_t ws_bytes, const moe_events *ev,
+              void *stream) {
+  if (!experts) return fail(MOE_EINVAL, "experts is NULL");
+  return layer_impl(cfg, T, x, w_router, bias, experts, nullptr, shared, residual, y, y_norm,
+                    eps, idx_out, w_out, workspace, ws_bytes, ev, stream);
+}
+
+int moe_layer_ptrs(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
+                   const float *bias, const void *const *expert_ptrs, const void *shared,
+                   const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
+                   float *w_out, void *workspace, size_t ws_bytes, const moe_events *ev,
+                   void *stream) {
+  if (!expert_ptrs) return fail(MOE_EINVAL, "expert_ptrs is NULL");
+  return layer_impl(cfg, T, x, w_router, bias, nullptr, expert_ptrs, shared, residual, y, y_norm,
+                    eps, idx_out, w_out, workspace, ws_bytes, ev, stream);
 }
 
 const char *moe_strerror(int code) {

@@ -170,3 +170,25 @@ def test_binding_refuses_host_tensors(L):
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError):
         moe.quant_act(torch.zeros(2, 64))
+
+
+def test_cache_create_rejects_bad_arguments(L):
+    c = REAL.c()
+    out = ctypes.c_void_p()
+    recs = (ctypes.c_void_p * 256)(*([A] * 256))
+    # pinned > slots
+    assert L.moe_cache_create(ctypes.byref(c), 4, 5, 1, 8, recs, ctypes.c_void_p(A),
+                              ctypes.c_void_p(A), None, None, ctypes.byref(out)) == moe.MOE_EINVAL
+    # misaligned host record
+    bad = (ctypes.c_void_p * 256)(*([A + 8] * 256))
+    assert L.moe_cache_create(ctypes.byref(c), 4, 1, 1, 8, bad, ctypes.c_void_p(A),
+                              ctypes.c_void_p(A), None, None, ctypes.byref(out)) == moe.MOE_EALIGN
+    assert not out.value
+    assert L.moe_cache_step(None, ctypes.c_void_p(A), 8, 0, None) == moe.MOE_EINVAL
+
+
+def test_layer_ptrs_rejects_null_table(L):
+    c = TINY.c()
+    rc = L.moe_layer_ptrs(ctypes.byref(c), 1, A, A, A, None, A, None, A, None, 1e-5, None, None,
+                          A, 1 << 30, None, None)
+    assert rc == moe.MOE_EINVAL
