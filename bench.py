@@ -43,6 +43,7 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / int8 MFMA % (prefill)"
 HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
+HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction (host to GPU)
 
 WORKLOADS = {
     "decode": dict(T=1, tokens="normal", bias="uniform", seed="decode", ring=8),
@@ -55,21 +56,26 @@ WORKLOADS = {
 }
 
 
-def describe(name, shape, T, ring, layers=1, top_p=0.0):
+def describe(name, shape, T, ring, layers=1, top_p=0.0, cache_slots=0):
     tp = (f", adaptive expert top-p {top_p:g} (shortest rank-order prefix holding that share of "
           f"the selected scores, weights renormalised)" if 0 < top_p < 1 else "")
+    if cache_slots:
+        tp += (f"; routed experts in pinned host memory, {cache_slots} of {shape.n_experts} per "
+               f"layer cached in HBM (LRU + hot store pinned from recorded usage), misses "
+               f"streamed over the host link")
     if layers > 1:
         return (f"{name}: {T} token(s) per step through a stack of {layers} routed-MoE layers "
                 f"(independent seeds, Zipf-skewed bias, unit-gain RMSNorm + residual between "
                 f"layers; hidden {shape.hidden}, expert intermediate {shape.inter}, "
                 f"{shape.n_experts} experts in {shape.n_group} groups, top-{shape.topk_group} "
                 f"groups, top-{shape.top_k}, {shape.n_shared} shared expert, int{shape.wbits} "
-                f"experts + fp32 row scales, Q8_0 activations{tp}), all layers resident in HBM")
+                f"experts + fp32 row scales, Q8_0 activations{tp})" +
+                ("" if cache_slots else ", all layers resident in HBM"))
     return (f"{name}: {T} token(s) per step through one routed-MoE layer (hidden {shape.hidden}, "
             f"expert intermediate {shape.inter}, {shape.n_experts} experts in {shape.n_group} "
             f"groups, top-{shape.topk_group} groups, top-{shape.top_k}, {shape.n_shared} shared "
             f"expert, int{shape.wbits} experts + fp32 row scales, Q8_0 activations{tp}); weights "
-            f"cycled over {ring} seeded layer instances in HBM")
+            f"cycled over {ring} seeded layer instances" + ("" if cache_slots else " in HBM"))
 
 
 class Hip:
@@ -230,6 +236,12 @@ def main():
     ap.add_argument("--ring", type=int, default=0, help="layer instances to cycle (0 = default)")
     ap.add_argument("--topp", type=float, default=0.0,
                     help="adaptive expert top-p in (0, 1); 0 = off (plain top-k)")
+    ap.add_argument("--cache-slots", type=int, default=0,
+                    help="routed experts in pinned host memory, this many per layer cached in "
+                         "HBM (0 = every expert resident in HBM)")
+    ap.add_argument("--cache-pinned", type=int, default=-1,
+                    help="slots pinned from the warm-up's recorded usage (-1 = half)")
+    ap.add_argument("--cache-promote", type=int, default=2, help="promotions per layer call")
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly")
     ap.add_argument("--graph-block", type=int, default=64, help="steps per captured graph")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
@@ -278,6 +290,13 @@ def main():
                                stream.cuda_stream)
         ring.append(dict(wr=torch.from_numpy(wr).to(dev), bias=torch.from_numpy(bias).to(dev),
                          wr_h=wr, bias_h=bias, ex=ex, sh=sh))
+        if args.cache_slots:  # the cold copy in pinned host memory; HBM keeps only the cache
+            torch.cuda.synchronize()
+            host = torch.empty(ex.numel(), dtype=torch.uint8, pin_memory=True)
+            host.copy_(ex)
+            ring[-1].update(host=host, ex=None)
+            del ex
+            torch.cuda.empty_cache()
 
     def tokens_for(step):
         if wl["tokens"] == "perturbed":
@@ -301,9 +320,19 @@ def main():
     c_cfg = moe.Config.c(cfg)
 
     def call_layer(r, x_ptr, res_ptr, y_ptr, yn_ptr, idx_ptr, events):
-        rc = L.moe_layer(ctypes.byref(c_cfg), T, x_ptr, r["wr"].data_ptr(), r["bias"].data_ptr(),
-                         r["ex"].data_ptr(), r["sh"].data_ptr(), res_ptr, y_ptr, yn_ptr, 1e-5,
-                         idx_ptr, None, ws.data_ptr(), ws.numel(), events, stream.cuda_stream)
+        if "cache" in r:  # records through the cache's table, then the cache's bookkeeping
+            rc = L.moe_layer_ptrs(ctypes.byref(c_cfg), T, x_ptr, r["wr"].data_ptr(),
+                                  r["bias"].data_ptr(), r["cache"].table.data_ptr(),
+                                  r["sh"].data_ptr(), res_ptr, y_ptr, yn_ptr, 1e-5, idx_ptr, None,
+                                  ws.data_ptr(), ws.numel(), events, stream.cuda_stream)
+            if rc == 0:
+                rc = L.moe_cache_step(r["cache"]._h, idx_ptr, T * shape.top_k, 0,
+                                      stream.cuda_stream)
+        else:
+            rc = L.moe_layer(ctypes.byref(c_cfg), T, x_ptr, r["wr"].data_ptr(),
+                             r["bias"].data_ptr(), r["ex"].data_ptr(), r["sh"].data_ptr(),
+                             res_ptr, y_ptr, yn_ptr, 1e-5, idx_ptr, None, ws.data_ptr(),
+                             ws.numel(), events, stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"moe_layer failed: {L.moe_last_error().decode()}")
 
@@ -337,12 +366,29 @@ def main():
         del src, dst
 
     # --- warm-up ------------------------------------------------------------
+    if args.cache_slots:
+        # the learning cache: an LRU-only pass records usage, then each layer's
+        # cache is rebuilt with its hottest experts pinned
+        S = min(args.cache_slots, shape.n_experts)
+        P = S // 2 if args.cache_pinned < 0 else min(args.cache_pinned, S)
+        for r in ring:
+            r["cache"] = moe.ExpertCache(cfg, r["host"], S, 0, args.cache_promote,
+                                         T * shape.top_k, device=dev)
+        for i in range(W):
+            run_step(i)
+        torch.cuda.synchronize()
+        for r in ring:
+            usage = r["cache"].usage()
+            r["cache"].close()
+            r["cache"] = moe.ExpertCache(cfg, r["host"], S, P, args.cache_promote,
+                                         T * shape.top_k, usage=usage, device=dev)
     for i in range(W):
         run_step(i)
     torch.cuda.synchronize()
+    cache0 = [r["cache"].stats() for r in ring] if args.cache_slots else None
 
     # --- timed region ---------------------------------------------------------
-    use_graph = not args.no_graph
+    use_graph = not args.no_graph and not args.cache_slots  # the cache steps on the host
     graphs = []
     if use_graph:
         B = max(1, min(args.graph_block, K))
@@ -366,6 +412,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec = t1 - t0
+    cache1 = [r["cache"].stats() for r in ring] if args.cache_slots else None
 
     # --- per-kernel durations (eager pass, events stamped by the dispatch) ----
     n_ev = max(1, min(K, 256 // NL))
@@ -408,7 +455,28 @@ def main():
     step_bytes = sum(layer_bytes(shape, T, u, bb) for u in U_l)
     small = T <= 16  # the layer's small-batch path (four kernels)
     dom_sec = stage_ms["gate_up"] * 1e-3
-    if small:  # HBM-bound GEMV: algorithmic bytes of the gate/up launch
+    cache_info = None
+    if args.cache_slots:
+        d = {k: sum(c1[k] - c0[k] for c0, c1 in zip(cache0, cache1))
+             for k in ("steps", "routed", "hits", "misses", "promotions", "bytes_copied")}
+        calls = max(d["steps"], 1)  # layer calls accounted in the timed region
+        miss_bytes = d["misses"] * bb  # a missed record is streamed once over the host link
+        link = (miss_bytes + d["bytes_copied"]) / calls * (K * NL) / sec / 1e9
+        cache_info = {"slots_per_layer": min(args.cache_slots, shape.n_experts),
+                      "pinned_per_layer": (min(args.cache_slots, shape.n_experts) // 2
+                                           if args.cache_pinned < 0 else args.cache_pinned),
+                      "hbm_resident_fraction": min(args.cache_slots, shape.n_experts)
+                      / shape.n_experts,
+                      "hit_rate": d["hits"] / max(d["routed"], 1),
+                      "misses_per_layer_call": d["misses"] / calls,
+                      "promotions_per_layer_call": d["promotions"] / calls,
+                      "host_link_gbps": link}
+    if args.cache_slots:  # bound by the host link: missed records + promotion copies
+        roof = {"bound": "host-link", "kernel": "whole step (misses stream over the host link)",
+                "achieved": cache_info["host_link_gbps"], "peak": HOST_LINK_PEAK_GBPS,
+                "unit": "GB/s", "frac": cache_info["host_link_gbps"] / HOST_LINK_PEAK_GBPS,
+                "traffic": None}
+    elif small:  # HBM-bound GEMV: algorithmic bytes of the gate/up launch
         dom = "gate_up (routed expert gate/up + SwiGLU + Q8_0 of h)"
         dom_bytes = float(np.mean([gate_up_bytes(shape, T, u, small) for u in U_l]))
         roof = {"bound": "hbm", "kernel": dom, "achieved": dom_bytes / dom_sec / 1e9,
@@ -441,7 +509,8 @@ def main():
         "vs_baseline": None,
         "dtype": f"i{shape.wbits}xi8->i32",
         "data": "synthetic",
-        "config": {"workload": describe(args.workload, shape, T, R, NL, args.topp),
+        "config": {"workload": describe(args.workload, shape, T, R, NL, args.topp,
+                                        min(args.cache_slots, shape.n_experts)),
                    "tokens_per_step": T, "layers_per_step": NL, "layer_instances": R,
                    "hip_graph": use_graph, "top_p": args.topp or None,
                    "distinct_routed_experts_per_step": U,
@@ -452,6 +521,8 @@ def main():
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "roofline": roof,
     }
+    if cache_info:
+        out["cache"] = cache_info
     if not args.no_cpu:
         if NL > 1:
             out["cpu_baseline"] = cpu_baseline_stack(shape, seed,
