@@ -62,10 +62,12 @@ constexpr int MAXP = TMAX * 17;  // pairs: T*K routed + T shared, K <= 16
 // Slot table (written by the gate/up workgroups of column 0): entry j
 // describes expert slot j -- the shared expert first, then the active routed
 // experts in ascending order -- as SLOT_W int32: expert (-1 = shared), token
-// count, TMAX pair ids (routed: slot id t*K+k; shared: T*K+t), TMAX token ids.
-// Entries past the last slot have a token count of 0.  A consumer reads its
-// entry in one round trip.
-constexpr int SLOT_W = 2 + 2 * sbk::TMAX;
+// count, TMAX pair ids (routed: slot id t*K+k; shared: T*K+t), TMAX token ids,
+// then the expert's record address (two int32 at SLOT_PTR).  Entries past the
+// last slot have a token count of 0.  A consumer reads its entry in one round
+// trip.
+constexpr int SLOT_PTR = 2 + 2 * sbk::TMAX;
+constexpr int SLOT_W = SLOT_PTR + 2;
 
 // A reserved, zero-initialised line at the start of the layer workspace; no
 // kernel of this path communicates between workgroups, so it stays zero.
@@ -623,27 +625,36 @@ __global__ void __launch_bounds__(256) k_select_small(LayerArgs a) {
 // idx) and its pairs in slot order, built in LDS by every K2 workgroup from
 // the T*K selections: bitmap of chosen experts, an expert's slot = chosen
 // experts below it, pairs ranked by ballots.  ent: expert (-1 = none), count,
-// TMAX pair ids, TMAX token ids.
-__device__ void union_slot(const LayerArgs &a, int j, int *ent) {
-  __shared__ int sel[256];
+// TMAX pair ids, TMAX token ids.  Returns the expert's record address; with a
+// table of record pointers, every thread holding a selection fetches its
+// entry at once, so that load overlaps the union's own work.
+__device__ const uint8_t *union_slot(const LayerArgs &a, int j, int *ent) {
   __shared__ uint32_t bits[32];
   __shared__ int wcnt[4];
+  __shared__ const uint8_t *rec;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n = a.T * a.K, E = a.E;
   if (tid < 32) bits[tid] = 0u;
-  if (tid == 0) ent[0] = -1;
+  if (tid == 0) {
+    ent[0] = -1;
+    rec = a.shared;  // any readable address for an empty slot
+  }
   int e = -1;  // -1: no pair, or a rank dropped by top-p
   if (tid < n) {
     const int v = a.idx[tid];
     e = (v >= 0 && v < E) ? v : -1;
   }
+  const uint8_t *my_rec = e >= 0 ? expert_record(a, e) : nullptr;
   __syncthreads();
   if (e >= 0) atomicOr(&bits[e >> 5], 1u << (e & 31));
   __syncthreads();
   if (e >= 0) {
     int r = __popc(bits[e >> 5] & ((1u << (e & 31)) - 1u));
     for (int w = 0; w < (e >> 5); w++) r += __popc(bits[w]);
-    if (r == j) ent[0] = e;  // every holder of that expert writes the same value
+    if (r == j) {  // every holder of that expert writes the same values
+      ent[0] = e;
+      rec = my_rec;
+    }
   }
   __syncthreads();
   const int ej = ent[0];
@@ -659,6 +670,7 @@ __device__ void union_slot(const LayerArgs &a, int j, int *ent) {
   }
   if (tid == 0) ent[1] = ej >= 0 ? wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3] : 0;
   __syncthreads();
+  return rec;
 }
 
 // Block (blk, j): rows 32 blk .. 32 blk + 31 of h for routed slot j.  The
@@ -679,28 +691,29 @@ __global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
     reinterpret_cast<uint32_t *>(a.qh + (size_t)pair * a.I + blk * 32)[q] = packed;
     if (q == 0) a.dh[(size_t)pair * (a.I / 32) + blk] = dd;
   }
-  union_slot(a, j, ent);
+  const uint8_t *rec = union_slot(a, j, ent);
   const int n_tok = min(max(ent[1], 0), a.T);
   if (blk == 0) {
     int32_t *dst = a.slots + (size_t)(a.n_shared + j) * SLOT_W;
-    if (threadIdx.x < SLOT_W) dst[threadIdx.x] = ent[threadIdx.x];
+    if (threadIdx.x < SLOT_PTR) dst[threadIdx.x] = ent[threadIdx.x];
+    if (threadIdx.x == 0) *reinterpret_cast<const uint8_t **>(dst + SLOT_PTR) = rec;
     if (j == 0 && a.n_shared && threadIdx.x < a.T) {  // the shared expert takes every token
       if (threadIdx.x == 0) {
         a.slots[0] = -1;
         a.slots[1] = a.T;
+        *reinterpret_cast<const uint8_t **>(a.slots + SLOT_PTR) = a.shared;
       }
       a.slots[2 + threadIdx.x] = a.T * a.K + threadIdx.x;
       a.slots[2 + sbk::TMAX + threadIdx.x] = threadIdx.x;
     }
   }
   if (n_tok == 0) return;
-  const int e = min(max(ent[0], 0), a.E - 1);
   const int *pairs = ent + 2, *toks = ent + 2 + sbk::TMAX;
   // int8 rows longer than 4 pieces per lane are split over two waves
   constexpr int KS = WB == 8 && NPL > 4 ? 2 : 1;
   gate_up_rows<WB, TT, KS == 2 ? 4 : NPL,
                (TT == 1 ? (WB == 2 ? 2 * MOE_K2_ROWS : WB == 8 ? 1 : MOE_K2_ROWS) : 1), KS>(
-      a, hb, expert_record(a, e), blk, n_tok, pairs,
+      a, hb, rec, blk, n_tok, pairs,
       [&](int i) { return (const int8_t *)(a.q + (size_t)min(max(toks[i], 0), a.T - 1) * a.H); },
       [&](int i) {
         return (const float *)(a.d + (size_t)min(max(toks[i], 0), a.T - 1) * (a.H / 32));
@@ -800,6 +813,8 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   const int P = T * (K + a.n_shared);  // pairs
   float *part = reinterpret_cast<float *>(dyn);                          // [4][P][RT]
   int *tab = reinterpret_cast<int *>(dyn + (size_t)4 * P * sbk::RT * 4);  // [slots][TAB_W]
+  const uint8_t **recs = reinterpret_cast<const uint8_t **>(
+      dyn + (size_t)4 * P * sbk::RT * 4 + (((size_t)a.n_slots_ub * TAB_W * 4 + 7) & ~(size_t)7));
   const int npieces = I / (128 / WB);
   const int qb = wv * npieces / 4, nq = (wv + 1) * npieces / 4 - qb;  // this wave's quarter
   const size_t row_b = (size_t)I * WB / 8;
@@ -835,6 +850,8 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   }
   for (int i = tid; i < a.n_slots_ub * TAB_W; i += 256)
     tab[i] = a.slots[(size_t)(i / TAB_W) * SLOT_W + i % TAB_W];
+  for (int i = tid; i < a.n_slots_ub; i += 256)
+    recs[i] = *reinterpret_cast<const uint8_t *const *>(a.slots + (size_t)i * SLOT_W + SLOT_PTR);
   if (tid < T * K) wsh[tid] = a.w[tid];
   const int v = tid;  // combine: one thread per (token, row), T * RT <= 128
   const bool comb = v < T * sbk::RT;
@@ -859,9 +876,7 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
 #pragma unroll
     for (int b = 0; b < SB; b++) {
       const bool ok_s = s0 + b < n_slots;
-      const int ex = ok_s ? tab[(s0 + b) * TAB_W] : -1;
-      const uint8_t *blob =
-          ex < 0 ? a.shared : expert_record(a, min(ex, a.E - 1));
+      const uint8_t *blob = ok_s ? recs[s0 + b] : a.shared;
       const uint8_t *down = blob + down_off;
       const float *sdp =
           reinterpret_cast<const float *>(blob + 3 * (size_t)I * ((size_t)H * WB / 8)) + 2 * I;
@@ -979,7 +994,9 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
   launch_k(k_gate_up_small<WB, TT, NPG>, dim3(a.I / 32, a.n_slots_ub - a.n_shared), dim3(256), 0,
            st, stage_ev(ev, MOE_STAGE_GATE_UP), a);
   const int P = a.T * (a.K + a.n_shared);
-  const size_t lds3 = (size_t)4 * P * sbk::RT * sizeof(float) + (size_t)a.n_slots_ub * TAB_W * 4;
+  const size_t lds3 = (size_t)4 * P * sbk::RT * sizeof(float) +
+                      (((size_t)a.n_slots_ub * TAB_W * 4 + 7) & ~(size_t)7) +
+                      (size_t)a.n_slots_ub * sizeof(void *);
   constexpr int SB = TT == 1 ? (WB == 2 ? 2 * MOE_K3_SLOTS : MOE_K3_SLOTS) : 2;
   constexpr int TT3 = TT == 1 ? 1 : MOE_K3_TT;  // tokens per chunk in the down kernel
   const int quarter = (a.I / (128 / WB) + 3) / 4;
