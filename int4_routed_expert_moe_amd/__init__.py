@@ -41,7 +41,8 @@ class MoeCfg(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("wbits", ctypes.c_int32),
-                ("routed_scaling", ctypes.c_float), ("top_p", ctypes.c_float)]
+                ("routed_scaling", ctypes.c_float), ("top_p", ctypes.c_float),
+                ("wfmt", ctypes.c_int32)]
 
 
 MOE_N_STAGES = 8
@@ -156,15 +157,19 @@ class Config:
     wbits: int = 4
     routed_scaling: float = 2.5
     top_p: float = 0.0  # adaptive expert top-p; 0 = off
+    wfmt: int = 0  # 0: integer codes with fp32 row scales; 1: MXFP4 (wbits 4)
 
     @classmethod
     def of(cls, shape, top_p: float = 0.0) -> "Config":
+        mx = shape.wbits == -4  # the synthetic shapes' code for MXFP4 experts
         return cls(shape.hidden, shape.inter, shape.n_experts, shape.n_group, shape.topk_group,
-                   shape.top_k, shape.n_shared, shape.wbits, shape.routed_scaling, top_p)
+                   shape.top_k, shape.n_shared, 4 if mx else shape.wbits, shape.routed_scaling,
+                   top_p, 1 if mx else 0)
 
     def c(self) -> MoeCfg:
         return MoeCfg(self.hidden, self.inter, self.n_experts, self.n_group, self.topk_group,
-                      self.top_k, self.n_shared, self.wbits, self.routed_scaling, self.top_p)
+                      self.top_k, self.n_shared, self.wbits, self.routed_scaling, self.top_p,
+                      self.wfmt)
 
 
 def _torch():

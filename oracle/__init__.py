@@ -26,6 +26,8 @@ QBLK = 32
 _lib = None
 
 
+MXFP4 = -4  # weight-format code of MXFP4 experts (reading R16)
+
 def build() -> str:
     """Compile oracle.c into liboracle.so (gcc, plain C11, no fp contraction)."""
     src = os.path.join(_HERE, "oracle.c")
@@ -69,6 +71,10 @@ def lib():
     L.oracle_select.restype = c_i
     L.oracle_route.argtypes = [c_i, c_i, c_i, c_i, c_i, c_i, c_f, c_v, c_v, c_v, c_v, c_v, c_v]
     L.oracle_route.restype = c_i
+    L.oracle_fp4_value.argtypes = [c_i]
+    L.oracle_fp4_value.restype = ctypes.c_double
+    L.oracle_e8m0_value.argtypes = [c_i]
+    L.oracle_e8m0_value.restype = ctypes.c_double
     L.oracle_top_p.argtypes = [c_i, c_i, c_i, c_f, c_f, c_v, c_v, c_v, c_v]
     L.oracle_top_p.restype = c_i
     L.oracle_group.argtypes = [c_i, c_i, c_i, c_v, c_v, c_v, c_v, c_v, c_v, c_v]
@@ -118,9 +124,13 @@ def code(row: np.ndarray, wbits: int, k: int) -> int:
     return lib().oracle_code(_ptr(row), wbits, k)
 
 
+def _bits(wbits: int) -> int:
+    return 4 if wbits == MXFP4 else wbits
+
+
 def unpack(row: np.ndarray, wbits: int, n: int) -> np.ndarray:
     row = _c(row, np.uint8)
-    assert row.size * (8 // wbits) >= n
+    assert row.size * (8 // _bits(wbits)) >= n
     out = np.empty(n, np.int8)
     lib().oracle_unpack(_ptr(row), wbits, n, _ptr(out))
     return out
@@ -128,7 +138,7 @@ def unpack(row: np.ndarray, wbits: int, n: int) -> np.ndarray:
 
 def pack(codes: np.ndarray, wbits: int) -> np.ndarray:
     codes = _c(codes, np.int8)
-    out = np.empty(codes.size * wbits // 8, np.uint8)
+    out = np.empty(codes.size * _bits(wbits) // 8, np.uint8)
     _check(lib().oracle_pack(_ptr(codes), codes.size, wbits, _ptr(out)), "pack")
     return out
 
@@ -238,12 +248,30 @@ def group(idx: np.ndarray, n_experts: int):
 
 # ------------------------------------------------------------------ experts
 
+def fp4_value(code: int) -> float:
+    return float(lib().oracle_fp4_value(code))
+
+
+def e8m0_value(s: int) -> float:
+    return float(lib().oracle_e8m0_value(s))
+
+
 def blob_bytes(H, I, wbits=4) -> int:
     return int(lib().oracle_blob_bytes(H, I, wbits))
 
 
 def blob_view(blob: np.ndarray, H: int, I: int, wbits: int = 4):
-    """Split a packed expert record into (gate, up, down code rows, scales)."""
+    """Split a packed expert record into (gate, up, down code rows, scales);
+    MXFP4: the scales are the per-block E8M0 bytes [rows][n/32]."""
+    if wbits == MXFP4:
+        gr, dr = H // 2, I // 2
+        gate = blob[: I * gr].reshape(I, gr)
+        up = blob[I * gr: 2 * I * gr].reshape(I, gr)
+        down = blob[2 * I * gr: 2 * I * gr + H * dr].reshape(H, dr)
+        t = blob[2 * I * gr + H * dr:]
+        nb, mb = H // QBLK, I // QBLK
+        return (gate, up, down, t[:I * nb].reshape(I, nb), t[I * nb:2 * I * nb].reshape(I, nb),
+                t[2 * I * nb:2 * I * nb + H * mb].reshape(H, mb))
     gr, dr = H * wbits // 8, I * wbits // 8
     gate = blob[: I * gr].reshape(I, gr)
     up = blob[I * gr: 2 * I * gr].reshape(I, gr)

@@ -22,6 +22,8 @@
  *        its list of options: an adaptive expert top-p (value 0.7 given)
  *        that cuts expert reads by 30-40%; [HN-B] section コミュニティ
  *        ベンチマーク: that option gave 1.6x end to end.
+ *  [DT-M] devtrends page below, section "Modèles supportés": one supported
+ *        model reads native MXFP4 weights directly from its shards.
  *  [DT]  "Comment exécuter un réseau de neurones de 744 milliards de
  *        paramètres sur un ordinateur ordinaire" (devtrends.cc), section
  *        "Comment fonctionne le moteur": requests for the same expert are
@@ -46,6 +48,16 @@
  *  R9 combine: y = shared + sum_k w_k * expert_k (shared expert weight 1).
  *  R10 packed codes: int4 element 2j in the low nibble of byte j, 2j+1 in the
  *     high nibble; int2 element 4j+i in bits 2i..2i+1; two's complement.
+ *  R16 MXFP4 experts (wbits code ORACLE_MXFP4 below): the OCP microscaling
+ *     format -- FP4 E2M1 elements (sign bit, 2-bit exponent with bias 1,
+ *     1-bit mantissa: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte
+ *     (element 2j in the low nibble), and one E8M0 scale byte s per 32
+ *     consecutive elements of a row, value 2^(s-127); no per-row scale.
+ *     Record: gate codes [I][H/2], up codes [I][H/2], down codes [H][I/2],
+ *     then the scale bytes gate [I][H/32], up [I][H/32], down [H][I/32].
+ *     Activations stay Q8_0 (the engine's integer kernels take them), so a
+ *     row is sum_b 2^(s_b-127) * d_b * sum_k fp4(c_k) q_k; the integer block
+ *     dot reported for it is P2 = sum_k (2 fp4(c_k)) q_k (2 fp4 is an integer).
  *  R15 adaptive expert top-p (p in (0,1); 0 or 1 = off): after the top-K
  *     selection, keep the shortest prefix of the rank order whose unbiased
  *     scores, summed left to right in fp32, reach p * S (fp32 product; S as
@@ -65,8 +77,22 @@
 
 /* ---------------------------------------------------------------- codes */
 
-/* Element k of a packed weight row (R10). */
+#define ORACLE_MXFP4 (-4)
+
+/* R16: value of an FP4 E2M1 code (0..15) and of an E8M0 scale byte. */
+double oracle_fp4_value(int code) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  const double v = mag[code & 7];
+  return (code & 8) ? -v : v;
+}
+double oracle_e8m0_value(int s) { return ldexp(1.0, s - 127); }
+
+/* Element k of a packed weight row (R10; MXFP4: the raw 4-bit code, R16). */
 int oracle_code(const uint8_t *row, int wbits, int k) {
+  if (wbits == ORACLE_MXFP4) {
+    int b = row[k / 2];
+    return (k % 2 == 0) ? (b & 0xF) : ((b >> 4) & 0xF);
+  }
   if (wbits == 4) {
     int b = row[k / 2];
     int v = (k % 2 == 0) ? (b & 0xF) : ((b >> 4) & 0xF);
@@ -88,6 +114,15 @@ void oracle_unpack(const uint8_t *row, int wbits, int n, int8_t *out) {
 
 /* Inverse of oracle_code over a row of n codes (used by the pins). */
 int oracle_pack(const int8_t *codes, int n, int wbits, uint8_t *out) {
+  if (wbits == ORACLE_MXFP4) {  /* raw 4-bit codes 0..15, element 2j low */
+    if (n % 2) return -1;
+    for (int j = 0; j < n / 2; j++) {
+      if (codes[2 * j] < 0 || codes[2 * j] > 15 || codes[2 * j + 1] < 0 || codes[2 * j + 1] > 15)
+        return -1;
+      out[j] = (uint8_t)(codes[2 * j] | (codes[2 * j + 1] << 4));
+    }
+    return 0;
+  }
   if (wbits == 8) {  /* one two's-complement byte per code */
     for (int k = 0; k < n; k++) out[k] = (uint8_t)codes[k];
     return 0;
@@ -360,8 +395,11 @@ int oracle_group(int T, int K, int E, const int32_t *idx, int32_t *counts,
 int oracle_block_dots(const uint8_t *row, int wbits, const int8_t *q, int n, int32_t *out) {
   for (int b = 0; b < n / QBLK; b++) {
     int64_t acc = 0;
-    for (int k = b * QBLK; k < (b + 1) * QBLK; k++)
-      acc += (int64_t)oracle_code(row, wbits, k) * (int64_t)q[k];
+    for (int k = b * QBLK; k < (b + 1) * QBLK; k++) {
+      const int c = oracle_code(row, wbits, k);
+      const int64_t wv = wbits == ORACLE_MXFP4 ? (int64_t)(2.0 * oracle_fp4_value(c)) : c;
+      acc += wv * (int64_t)q[k];
+    }
     if (acc > INT32_MAX || acc < INT32_MIN) return -1;
     out[b] = (int32_t)acc;
   }
@@ -369,33 +407,48 @@ int oracle_block_dots(const uint8_t *row, int wbits, const int8_t *q, int n, int
 }
 
 size_t oracle_blob_bytes(int H, int I, int wbits) {
+  if (wbits == ORACLE_MXFP4)  /* R16: 4-bit codes, one scale byte per 32 */
+    return ((size_t)2 * I * H + (size_t)H * I) / 2 + ((size_t)2 * I * H + (size_t)H * I) / QBLK;
   return ((size_t)2 * I * H + (size_t)H * I) * (size_t)wbits / 8 +
          sizeof(float) * ((size_t)2 * I + H);
 }
 
 typedef struct {
   const uint8_t *gate, *up, *down;
-  const float *sg, *su, *sd;
+  const float *sg, *su, *sd;        /* per-row scales (integer codes) */
+  const uint8_t *bg, *bu, *bd;      /* per-block E8M0 scales (MXFP4) */
   size_t gate_row, down_row;
 } blob_view;
 
 static blob_view view_of(const uint8_t *blob, int H, int I, int wbits) {
   blob_view v;
-  v.gate_row = (size_t)H * wbits / 8;
-  v.down_row = (size_t)I * wbits / 8;
+  const int bits = wbits == ORACLE_MXFP4 ? 4 : wbits;
+  v.gate_row = (size_t)H * bits / 8;
+  v.down_row = (size_t)I * bits / 8;
   v.gate = blob;
   v.up = blob + (size_t)I * v.gate_row;
   v.down = blob + 2 * (size_t)I * v.gate_row;
-  const float *sc = (const float *)(v.down + (size_t)H * v.down_row);
-  v.sg = sc;
-  v.su = sc + I;
-  v.sd = sc + 2 * I;
+  const uint8_t *tail = v.down + (size_t)H * v.down_row;
+  v.sg = v.su = v.sd = NULL;
+  v.bg = v.bu = v.bd = NULL;
+  if (wbits == ORACLE_MXFP4) {
+    v.bg = tail;
+    v.bu = tail + (size_t)I * (H / QBLK);
+    v.bd = tail + 2 * (size_t)I * (H / QBLK);
+  } else {
+    const float *sc = (const float *)tail;
+    v.sg = sc;
+    v.su = sc + I;
+    v.sd = sc + 2 * I;
+  }
   return v;
 }
 
-/* fp64 value of one output row: scale_r * sum_b d_b * P_b (dequantise on use). */
-static double row_value(const uint8_t *row, int wbits, float scale, const int8_t *q,
-                        const float *d, int n, int32_t *dots_out, int *err) {
+/* fp64 value of one output row (dequantise on use): integer codes
+ * scale_r * sum_b d_b * P_b; MXFP4 (bsc: the row's block scales)
+ * sum_b 2^(s_b-127) * d_b * P2_b / 2. */
+static double row_value(const uint8_t *row, int wbits, float scale, const uint8_t *bsc,
+                        const int8_t *q, const float *d, int n, int32_t *dots_out, int *err) {
   int32_t P[QBLK * 16];
   int32_t *dots = dots_out;
   int32_t *tmp = NULL;
@@ -405,6 +458,12 @@ static double row_value(const uint8_t *row, int wbits, float scale, const int8_t
   }
   if (oracle_block_dots(row, wbits, q, n, dots)) *err = 1;
   double acc = 0.0;
+  if (bsc) {
+    for (int b = 0; b < n / QBLK; b++)
+      acc += oracle_e8m0_value(bsc[b]) * (double)d[b] * (0.5 * (double)dots[b]);
+    free(tmp);
+    return acc;
+  }
   for (int b = 0; b < n / QBLK; b++) acc += (double)d[b] * (double)dots[b];
   free(tmp);
   return (double)scale * acc;
@@ -422,9 +481,12 @@ int oracle_gate_up(const uint8_t *blob, int H, int I, int wbits, const int8_t *q
 #pragma omp parallel for schedule(static) reduction(| : err)
   for (int r = 0; r < I; r++) {
     int e1 = 0;
-    double g = row_value(v.gate + r * v.gate_row, wbits, v.sg[r], q, d, H,
+    const int mx = wbits == ORACLE_MXFP4;
+    double g = row_value(v.gate + r * v.gate_row, wbits, mx ? 1.0f : v.sg[r],
+                         mx ? v.bg + (size_t)r * (H / QBLK) : NULL, q, d, H,
                          gate_dots ? gate_dots + (size_t)r * (H / QBLK) : NULL, &e1);
-    double u = row_value(v.up + r * v.gate_row, wbits, v.su[r], q, d, H,
+    double u = row_value(v.up + r * v.gate_row, wbits, mx ? 1.0f : v.su[r],
+                         mx ? v.bu + (size_t)r * (H / QBLK) : NULL, q, d, H,
                          up_dots ? up_dots + (size_t)r * (H / QBLK) : NULL, &e1);
     double silu = g / (1.0 + exp(-g));
     if (g_out) g_out[r] = g;
@@ -445,7 +507,9 @@ int oracle_down(const uint8_t *blob, int H, int I, int wbits, const int8_t *qh,
 #pragma omp parallel for schedule(static) reduction(| : err)
   for (int j = 0; j < H; j++) {
     int e1 = 0;
-    double val = row_value(v.down + j * v.down_row, wbits, v.sd[j], qh, dh, I,
+    const int mx = wbits == ORACLE_MXFP4;
+    double val = row_value(v.down + j * v.down_row, wbits, mx ? 1.0f : v.sd[j],
+                           mx ? v.bd + (size_t)j * (I / QBLK) : NULL, qh, dh, I,
                            down_dots ? down_dots + (size_t)j * (I / QBLK) : NULL, &e1);
     if (y) y[j] = (float)val;
     err |= e1;

@@ -19,8 +19,8 @@ Workloads (shapes and distributions of the method's real layer; all seeded):
   stack    16 such layers, independent seeds, Zipf-skewed bias, RMSNorm +
            residual between layers, 1 or 8 tokens, int4 or int2 experts
 Distributions: tokens ~N(0,1); router weights ~N(0, 0.02^2) fp32; expert
-gate/up/down weights ~N(0, 0.02^2) quantised per row to packed int4 (or int2)
-with fp32 absmax scales.
+gate/up/down weights ~N(0, 0.02^2) quantised per row to packed int4 (or int2,
+int8) with fp32 absmax scales, or per 32-block to MXFP4.
 """
 from __future__ import annotations
 
@@ -43,6 +43,9 @@ _lib = None
 _glib = None
 
 
+MXFP4 = -4  # weight-format code: MXFP4 experts (FP4 E2M1 codes, E8M0 scale per 32)
+
+
 @dataclass(frozen=True)
 class LayerShape:
     hidden: int
@@ -53,7 +56,11 @@ class LayerShape:
     top_k: int
     n_shared: int = 1
     routed_scaling: float = 2.5
-    wbits: int = 4
+    wbits: int = 4  # 8, 4, 2 (integer codes, fp32 row scales) or MXFP4
+
+    @property
+    def label(self) -> str:
+        return "mxfp4" if self.wbits == MXFP4 else f"int{self.wbits}"
 
     def with_bits(self, wbits: int) -> "LayerShape":
         return LayerShape(self.hidden, self.inter, self.n_experts, self.n_group,

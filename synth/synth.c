@@ -31,6 +31,17 @@
  *   int4, 2 for int2), code = clamp(roundf(w / s), qlo, qhi) (int8: [-127,127],
  *   int4: [-8,7], int2: [-2,1]); s = 0 -> codes 0.
  *
+ * MXFP4 record (wbits code -4; the OCP microscaling format that one of the
+ * pages' supported models ships its weights in): FP4 E2M1 codes two per byte
+ * (element 2j in the low nibble) for the three matrices in the same order,
+ * then one E8M0 scale byte per 32 consecutive elements of a row: gate
+ * [I][H/32], up [I][H/32], down [H][I/32].  Block quantiser: amax = max|w|
+ * over the block, X = floor(log2 amax) - 2 (frexpf, exact; the largest FP4
+ * magnitude is 6 = 1.5 * 2^2), scale byte X + 127 clamped to [1, 254]
+ * (127 when amax = 0); each element v = w * 2^-X (exact) goes to the nearest
+ * FP4 magnitude {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even mantissa,
+ * saturating at 6, sign in bit 3 (zero magnitude -> code 0).
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
  */
 #include <math.h>
@@ -87,9 +98,43 @@ void synth_uniform_fill(uint64_t key, uint64_t start, int64_t n, float lo,
   }
 }
 
+#define SYN_MXFP4 (-4)
+
 size_t synth_blob_bytes(int H, int I, int wbits) {
-  size_t codes = ((size_t)2 * I * H + (size_t)H * I) * (size_t)wbits / 8;
-  return codes + sizeof(float) * ((size_t)2 * I + H);
+  const size_t elems = (size_t)2 * I * H + (size_t)H * I;
+  if (wbits == SYN_MXFP4) return elems / 2 + elems / 32;
+  return elems * (size_t)wbits / 8 + sizeof(float) * ((size_t)2 * I + H);
+}
+
+/* FP4 E2M1 code of w at block exponent X (see the header). */
+static unsigned fp4_code(float w, int X) {
+  const float v = fabsf(ldexpf(w, -X));
+  unsigned m;
+  if (v <= 0.25f) m = 0;
+  else if (v < 0.75f) m = 1;
+  else if (v <= 1.25f) m = 2;
+  else if (v < 1.75f) m = 3;
+  else if (v <= 2.5f) m = 4;
+  else if (v < 3.5f) m = 5;
+  else if (v <= 5.0f) m = 6;
+  else m = 7;
+  return m == 0 ? 0u : (m | (w < 0.0f ? 8u : 0u));
+}
+
+/* One MXFP4 block: 32 floats -> 16 code bytes and the E8M0 scale byte. */
+static void mx_block(const float *w, uint8_t *codes, uint8_t *scale) {
+  float amax = 0.0f;
+  for (int k = 0; k < 32; k++) amax = fmaxf(amax, fabsf(w[k]));
+  int s = 127;
+  if (amax > 0.0f) {
+    int ex;
+    frexpf(amax, &ex);  /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+    s = ex - 1 - 2 + 127;
+    s = s < 1 ? 1 : (s > 254 ? 254 : s);
+  }
+  *scale = (uint8_t)s;
+  for (int j = 0; j < 16; j++)
+    codes[j] = (uint8_t)(fp4_code(w[2 * j], s - 127) | (fp4_code(w[2 * j + 1], s - 127) << 4));
 }
 
 /* One weight row: n float draws (sigma * normal), quantised and packed. */
@@ -133,8 +178,37 @@ void synth_weight_row(uint64_t seed, uint32_t layer, uint32_t expert,
 }
 
 /* Expert record for (seed, layer, expert); matrix m = 0 gate, 1 up, 2 down. */
+static int mx_expert_blob(uint64_t seed, uint32_t layer, uint32_t expert, int H, int I,
+                          float sigma, uint8_t *blob) {
+  if (H <= 0 || I <= 0 || H % 32 || I % 32) return -1;
+  const size_t gate_b = (size_t)I * H / 2, down_b = (size_t)H * I / 2;
+  uint8_t *codes[3] = {blob, blob + gate_b, blob + 2 * gate_b};
+  uint8_t *sb = blob + 2 * gate_b + down_b;
+  uint8_t *scl[3] = {sb, sb + (size_t)I * (H / 32), sb + 2 * (size_t)I * (H / 32)};
+  const int rows[3] = {I, I, H}, cols[3] = {H, H, I};
+  for (int m = 0; m < 3; m++) {
+    const uint64_t key = synth_key(seed, layer, 4u + (uint32_t)m, expert, (uint32_t)m);
+    const int n = cols[m];
+#pragma omp parallel
+    {
+      float *wbuf = (float *)malloc(sizeof(float) * (size_t)n);
+#pragma omp for schedule(static)
+      for (int r = 0; r < rows[m]; r++) {
+        for (int c = 0; c < n; c++)
+          wbuf[c] = normal_at(key, (uint64_t)r * (uint64_t)n + (uint64_t)c) * sigma;
+        for (int b = 0; b < n / 32; b++)
+          mx_block(wbuf + 32 * b, codes[m] + (size_t)r * (n / 2) + 16 * b,
+                   scl[m] + (size_t)r * (n / 32) + b);
+      }
+      free(wbuf);
+    }
+  }
+  return 0;
+}
+
 int synth_expert_blob(uint64_t seed, uint32_t layer, uint32_t expert, int H,
                       int I, int wbits, float sigma, uint8_t *blob) {
+  if (wbits == SYN_MXFP4) return mx_expert_blob(seed, layer, expert, H, I, sigma, blob);
   if ((wbits != 8 && wbits != 4 && wbits != 2) || H <= 0 || I <= 0 || H % 8 || I % 8) return -1;
   const size_t gate_b = (size_t)I * H * wbits / 8;
   const size_t down_b = (size_t)H * I * wbits / 8;

@@ -90,6 +90,78 @@ k_synth_rows(MatJob job, int n, int wbits, float sigma) {
   if (tid == 0) job.scales[ex][row] = s;
 }
 
+// MXFP4 records (wbits code -4): the block quantiser of synth.c, one
+// thread per block of 32 once the row is in LDS.
+__device__ static unsigned fp4_code(float w, int X) {
+  const float v = fabsf(ldexpf(w, -X));
+  unsigned m;
+  if (v <= 0.25f) m = 0;
+  else if (v < 0.75f) m = 1;
+  else if (v <= 1.25f) m = 2;
+  else if (v < 1.75f) m = 3;
+  else if (v <= 2.5f) m = 4;
+  else if (v < 3.5f) m = 5;
+  else if (v <= 5.0f) m = 6;
+  else m = 7;
+  return m == 0 ? 0u : (m | (w < 0.0f ? 8u : 0u));
+}
+
+struct MxJob {
+  uint64_t key[8];
+  uint8_t *codes[8];   // first code row of this matrix in each record
+  uint8_t *scales[8];  // first scale byte of this matrix in each record
+};
+
+__global__ void __launch_bounds__(256) k_synth_rows_mx(MxJob job, int n, float sigma) {
+  extern __shared__ float wrow[];
+  const int row = blockIdx.x, ex = blockIdx.y, tid = threadIdx.x;
+  const uint64_t key = job.key[ex];
+  for (int c = tid; c < n; c += 256)
+    wrow[c] = normal_at(key, (uint64_t)row * (uint64_t)n + (uint64_t)c) * sigma;
+  __syncthreads();
+  for (int b = tid; b < n / 32; b += 256) {
+    const float *w = wrow + 32 * b;
+    float amax = 0.0f;
+    for (int k = 0; k < 32; k++) amax = fmaxf(amax, fabsf(w[k]));
+    int s = 127;
+    if (amax > 0.0f) {
+      int e;
+      frexpf(amax, &e);
+      s = e - 1 - 2 + 127;
+      s = s < 1 ? 1 : (s > 254 ? 254 : s);
+    }
+    job.scales[ex][(size_t)row * (n / 32) + b] = (uint8_t)s;
+    uint8_t *dst = job.codes[ex] + (size_t)row * (n / 2) + 16 * b;
+    for (int j = 0; j < 16; j++)
+      dst[j] = (uint8_t)(fp4_code(w[2 * j], s - 127) | (fp4_code(w[2 * j + 1], s - 127) << 4));
+  }
+}
+
+static int mx_blobs(uint64_t seed, uint32_t layer, const uint32_t *expert_ids, int n_experts,
+                    int H, int I, float sigma, void *out, size_t stride, hipStream_t st) {
+  const size_t gate_b = (size_t)I * H / 2, down_b = (size_t)H * I / 2;
+  const int rows[3] = {I, I, H}, cols[3] = {H, H, I};
+  for (int e0 = 0; e0 < n_experts; e0 += 8) {
+    const int ne = (n_experts - e0) < 8 ? (n_experts - e0) : 8;
+    for (int m = 0; m < 3; m++) {
+      MxJob job;
+      for (int i = 0; i < 8; i++) {
+        const int ei = e0 + (i < ne ? i : 0);
+        uint8_t *base = (uint8_t *)out + (size_t)ei * stride;
+        uint8_t *sb = base + 2 * gate_b + down_b;
+        job.key[i] = host_key(seed, layer, 4u + (uint32_t)m, expert_ids[ei], (uint32_t)m);
+        job.codes[i] = base + (m == 0 ? 0 : (m == 1 ? gate_b : 2 * gate_b));
+        job.scales[i] = sb + (size_t)(m == 0 ? 0 : (m == 1 ? 1 : 2)) * I * (H / 32);
+      }
+      hipLaunchKernelGGL(k_synth_rows_mx, dim3(rows[m], ne), dim3(256), sizeof(float) * cols[m],
+                         st, job, cols[m], sigma);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return (int)err;
+    }
+  }
+  return 0;
+}
+
 extern "C" {
 
 // Fills the records of experts expert_ids[0..n_experts) of (seed, layer) at
@@ -99,10 +171,11 @@ extern "C" {
 int synth_gpu_expert_blobs(uint64_t seed, uint32_t layer, const uint32_t *expert_ids,
                            int n_experts, int H, int I, int wbits, float sigma,
                            void *out, size_t stride, void *stream) {
-  if ((wbits != 8 && wbits != 4 && wbits != 2) || H <= 0 || I <= 0 || H % 8 || I % 8 ||
-      n_experts < 0 || !out || H > 16384 || I > 16384)
+  if ((wbits != 8 && wbits != 4 && wbits != 2 && wbits != -4) || H <= 0 || I <= 0 || H % 32 ||
+      I % 32 || n_experts < 0 || !out || H > 16384 || I > 16384)
     return -1;
   hipStream_t st = (hipStream_t)stream;
+  if (wbits == -4) return mx_blobs(seed, layer, expert_ids, n_experts, H, I, sigma, out, stride, st);
   const size_t gate_b = (size_t)I * H * wbits / 8;
   const size_t down_b = (size_t)H * I * wbits / 8;
   const int rows[3] = {I, I, H}, cols[3] = {H, H, I};

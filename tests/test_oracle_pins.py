@@ -573,3 +573,104 @@ def test_layer_groups_cover_every_slot_once():
     assert sorted(blobs) == sorted(set(out["idx"].ravel().tolist()))
     assert all(v == 1 for v in blobs.values())
     assert g["counts"].sum() == out["idx"].size
+
+
+# ------------------------------------------------------------------ MXFP4 experts (R16)
+
+MX = oracle.MXFP4
+
+
+def test_fp4_and_e8m0_hand_values():
+    g = _load("mxfp4_codes.json")
+    for c in g["fp4"]:
+        assert oracle.fp4_value(c["code"]) == c["value"], c
+    for c in g["e8m0"]:
+        assert oracle.e8m0_value(c["s"]) == c["value"], c
+    p = g["packing"]
+    assert oracle.pack(np.array(p["codes"], np.int8), MX).tolist() == p["bytes"]
+    assert oracle.unpack(np.array(p["bytes"], np.uint8), MX, 4).tolist() == p["codes"]
+
+
+def test_mx_pack_unpack_exhaustive():
+    codes = np.array([(a, b) for a in range(16) for b in range(16)], np.int8).ravel()
+    packed = oracle.pack(codes, MX)
+    assert np.array_equal(oracle.unpack(packed, MX, codes.size), codes)
+    assert np.array_equal(np.sort(packed), np.arange(256))
+
+
+def _fp4_grid_nearest(v):
+    """Nearest FP4 magnitude by direct search; ties to the even mantissa."""
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    best = min(range(8), key=lambda m: (abs(abs(v) - mags[m]), m % 2))
+    return best
+
+
+def test_generated_mx_record_is_the_block_quantisation():
+    shape = synth.TINY.with_bits(MX)
+    blob = synth.expert_blob(shape, 41, 0, 3)
+    assert blob.size == oracle.blob_bytes(256, 128, MX) == synth.blob_bytes(shape)
+    gate, up, down, bg, bu, bd = oracle.blob_view(blob, 256, 128, MX)
+    for m, (codes, scl, n) in enumerate(((gate, bg, 256), (down, bd, 128))):
+        mat = 0 if m == 0 else 2
+        for r in (0, 5, codes.shape[0] - 1):
+            w = np.empty(n, np.float32)
+            synth.lib().synth_weight_row(41, 0, 3, mat, n, r, synth.WEIGHT_SIGMA,
+                                         w.ctypes.data)
+            c = oracle.unpack(codes[r], MX, n)
+            for b in range(n // 32):
+                wb = w[32 * b:32 * (b + 1)].astype(np.float64)
+                X = int(scl[r, b]) - 127
+                amax = np.max(np.abs(wb))
+                # the block maximum lands in [4, 8) before rounding (X = floor(log2 amax) - 2)
+                assert 4.0 <= amax / 2.0 ** X < 8.0
+                for k in range(32):
+                    v = wb[k] / 2.0 ** X
+                    mag = min(_fp4_grid_nearest(v), 7)
+                    want = 0 if mag == 0 else mag | (8 if v < 0 else 0)
+                    assert c[32 * b + k] == want, (m, r, b, k, v)
+
+
+def test_mx_block_dots_vs_numpy():
+    rng = np.random.default_rng(15)
+    for _ in range(20):
+        codes = rng.integers(0, 16, 64).astype(np.int8)
+        q = rng.integers(-127, 128, 64).astype(np.int8)
+        got = oracle.block_dots(oracle.pack(codes, MX), MX, q)
+        twice = np.array([2.0 * oracle.fp4_value(int(c)) for c in codes]).astype(np.int64)
+        want = (twice * q.astype(np.int64)).reshape(2, 32).sum(1)
+        assert np.array_equal(got, want)
+
+
+def test_mx_gate_up_equals_dequantised_matmul():
+    shape = synth.TINY.with_bits(MX)
+    blob = synth.expert_blob(shape, 42, 0, 1)
+    x = synth.tokens(shape, 42, 2)
+    q, d = oracle.q8_0(x)
+    gate, up, down, bg, bu, bd = oracle.blob_view(blob, 256, 128, MX)
+    fp4 = np.array([oracle.fp4_value(c) for c in range(16)])
+    for t in range(2):
+        xq = q[t].astype(np.float64) * np.repeat(d[t].astype(np.float64), 32)
+        ref = oracle.gate_up(blob, 256, 128, MX, q[t], d[t])
+        for codes, scl, got in ((gate, bg, ref["g"]), (up, bu, ref["u"])):
+            W = fp4[np.stack([oracle.unpack(codes[r], MX, 256) for r in range(128)])]
+            W = W * np.repeat(2.0 ** (scl.astype(np.float64) - 127), 32, axis=1)
+            assert np.max(np.abs(W @ xq - got)) <= 1e-12 * np.max(np.abs(got))
+
+
+def test_mx_grid_exact_dots():
+    """Codes 0..7 with scale 2^0 and integer activations (amax 127 -> d = 1):
+    the rows are the textbook dot of the FP4 values with the integers."""
+    H, I = 256, 128
+    rng = np.random.default_rng(16)
+    blob = np.zeros(oracle.blob_bytes(H, I, MX), np.uint8)
+    gate, up, down, bg, bu, bd = oracle.blob_view(blob, H, I, MX)
+    codes = rng.integers(0, 16, (I, H)).astype(np.int8)
+    gate[:] = np.stack([oracle.pack(r, MX) for r in codes])
+    bg[:] = 127
+    x = rng.integers(-126, 127, (1, H)).astype(np.float32)
+    x[0, ::32] = 127.0  # amax 127 in every block
+    q, d = oracle.q8_0(x)
+    assert np.all(d == 1.0) and np.array_equal(q[0], x[0].astype(np.int8))
+    ref = oracle.gate_up(blob, H, I, MX, q[0], d[0], want_dots=True)
+    fp4 = np.array([oracle.fp4_value(c) for c in range(16)])
+    assert np.array_equal(ref["g"], fp4[codes] @ x[0].astype(np.float64))
