@@ -59,6 +59,8 @@ WORKLOADS = {
 def describe(name, shape, T, ring, layers=1, top_p=0.0, cache_slots=0):
     tp = (f", adaptive expert top-p {top_p:g} (shortest rank-order prefix holding that share of "
           f"the selected scores, weights renormalised)" if 0 < top_p < 1 else "")
+    wfmt = ("MXFP4 (FP4 E2M1 codes + E8M0 scale per 32)" if shape.wbits == -4
+            else f"int{shape.wbits} codes + fp32 row scales")
     if cache_slots:
         tp += (f"; routed experts in pinned host memory, {cache_slots} of {shape.n_experts} per "
                f"layer cached in HBM (LRU + hot store pinned from recorded usage), misses "
@@ -68,13 +70,13 @@ def describe(name, shape, T, ring, layers=1, top_p=0.0, cache_slots=0):
                 f"(independent seeds, Zipf-skewed bias, unit-gain RMSNorm + residual between "
                 f"layers; hidden {shape.hidden}, expert intermediate {shape.inter}, "
                 f"{shape.n_experts} experts in {shape.n_group} groups, top-{shape.topk_group} "
-                f"groups, top-{shape.top_k}, {shape.n_shared} shared expert, int{shape.wbits} "
-                f"experts + fp32 row scales, Q8_0 activations{tp})" +
+                f"groups, top-{shape.top_k}, {shape.n_shared} shared expert, {wfmt} "
+                f"experts, Q8_0 activations{tp})" +
                 ("" if cache_slots else ", all layers resident in HBM"))
     return (f"{name}: {T} token(s) per step through one routed-MoE layer (hidden {shape.hidden}, "
             f"expert intermediate {shape.inter}, {shape.n_experts} experts in {shape.n_group} "
             f"groups, top-{shape.topk_group} groups, top-{shape.top_k}, {shape.n_shared} shared "
-            f"expert, int{shape.wbits} experts + fp32 row scales, Q8_0 activations{tp}); weights "
+            f"expert, {wfmt} experts, Q8_0 activations{tp}); weights "
             f"cycled over {ring} seeded layer instances" + ("" if cache_slots else " in HBM"))
 
 
@@ -131,7 +133,10 @@ def gate_up_bytes(shape, T, U, small):
     selection).  Larger batches: the same for U + shared experts with fp32 h
     out."""
     H, I, K, S = shape.hidden, shape.inter, shape.top_k, shape.n_shared
-    per_expert = 2 * I * H * shape.wbits // 8 + 2 * I * 4
+    if shape.wbits == -4:  # MXFP4: 4-bit codes and one scale byte per 32
+        per_expert = 2 * I * H // 2 + 2 * I * H // 32
+    else:
+        per_expert = 2 * I * H * shape.wbits // 8 + 2 * I * 4
     q8 = 1 + 4 / 32  # bytes per element of a Q8_0 vector (codes + fp32 block scales)
     x_in = T * H * q8
     if small:
@@ -232,7 +237,8 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--wbits", type=int, default=4, choices=(8, 4, 2))
+    ap.add_argument("--wbits", default="4", choices=("8", "4", "2", "mxfp4"),
+                    help="expert weights: int8/int4/int2 codes with row scales, or MXFP4")
     ap.add_argument("--ring", type=int, default=0, help="layer instances to cycle (0 = default)")
     ap.add_argument("--topp", type=float, default=0.0,
                     help="adaptive expert top-p in (0, 1); 0 = off (plain top-k)")
@@ -261,7 +267,7 @@ def main():
     import synth
 
     wl = WORKLOADS[args.workload]
-    shape = synth.REAL.with_bits(args.wbits)
+    shape = synth.REAL.with_bits(synth.MXFP4 if args.wbits == "mxfp4" else int(args.wbits))
     T = wl["T"]
     NL = wl.get("layers", 1)
     R = wl["ring"] if NL > 1 else (args.ring or wl["ring"])
@@ -484,10 +490,10 @@ def main():
         roof["frac"] = roof["achieved"] / HBM_PEAK_GBPS
         # counters were taken on the int4 workload without top-p
         roof["traffic"] = (measured_traffic(args.workload)
-                           if args.wbits == 4 and not args.topp else None)
+                           if args.wbits == "4" and not args.topp else None)
         roof.update(bytes_per_launch=dom_bytes, launch_us=dom_sec * 1e6)
     else:  # grouped GEMM on the matrix cores: int8 operations (2 per MAC) of the launch
-        dom = "gate_up (grouped int4 x int8 MFMA GEMM + SwiGLU + Q8_0 of h)"
+        dom = f"gate_up (grouped {shape.label} x int8 MFMA GEMM + SwiGLU + Q8_0 of h)"
         ops = 2.0 * (pairs + T * shape.n_shared) * 2 * shape.inter * shape.hidden
         roof = {"bound": "mfma", "kernel": dom, "achieved": ops / dom_sec / 1e12,
                 "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "traffic": None,
@@ -507,7 +513,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": f"i{shape.wbits}xi8->i32",
+        "dtype": "fp4e2m1xi8->i32" if shape.wbits == -4 else f"i{shape.wbits}xi8->i32",
         "data": "synthetic",
         "config": {"workload": describe(args.workload, shape, T, R, NL, args.topp,
                                         min(args.cache_slots, shape.n_experts)),

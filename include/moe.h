@@ -44,6 +44,13 @@
  *       gate codes [I][H*wbits/8] | up codes [I][H*wbits/8] |
  *       down codes [H][I*wbits/8] | gate scale fp32 [I] | up scale fp32 [I] |
  *       down scale fp32 [H]
+ *     MXFP4 records (wfmt = 1; "Comment exécuter…", section "Modèles
+ *     supportés": native MXFP4 weights): the codes as for int4 but FP4 E2M1
+ *     (sign bit 3, magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6), then one E8M0 byte
+ *     s per 32 consecutive codes of a row (value 2^(s-127)) instead of the
+ *     row scales: gate [I][H/32] | up [I][H/32] | down [H][I/32]; a row is
+ *     sum_b 2^(s_b-127) d_b sum_k fp4(c_k) q_k, and the int32 block dot
+ *     reported for it (moe_ffn_debug) is sum_k 2 fp4(c_k) q_k.
  *     int8: element j in byte j, codes in [-127, 127] (-128 is not
  *     produced by the quantiser but is accepted);
  *     int4: element 2j in the low nibble of byte j, 2j+1 in the high nibble;
@@ -76,7 +83,8 @@ extern "C" {
  * wbits in {8, 4, 2}; a weight row holds at most 256 16-byte pieces of codes
  * (448 for int8) along hidden and 128 along inter, i.e. hidden <= 8192 and
  * inter <= 4096 for int4 (16384 / 8192 for int2, 7168 / 2048 for int8);
- * top_p = 0 (off), or in (0, 1] (1 is off as well). */
+ * top_p = 0 (off), or in (0, 1] (1 is off as well); wfmt 0, or 1 with
+ * wbits 4 (MXFP4). */
 typedef struct moe_cfg {
   int32_t hidden;       /* H */
   int32_t inter;        /* I, intermediate width of every expert (shared too) */
@@ -88,6 +96,7 @@ typedef struct moe_cfg {
   int32_t wbits;        /* 8 (int8), 4 (packed int4) or 2 (packed int2) */
   float routed_scaling; /* routed_scaling_factor applied to routed weights */
   float top_p;          /* adaptive expert top-p (see moe_route); 0 = off */
+  int32_t wfmt;         /* 0: integer codes, fp32 row scales; 1: MXFP4 (wbits 4) */
 } moe_cfg;
 
 /* Bytes of one packed expert record for cfg (0 if cfg is unsupported). */

@@ -126,6 +126,73 @@ __device__ __forceinline__ int perm2(uint32_t lo, uint32_t hi, uint32_t sel) {
   return (int)__builtin_amdgcn_perm(hi, lo, sel);
 }
 
+// A load through the global address space.  Record addresses read from
+// memory (the caller's pointer table, the slot table) are generic to the
+// compiler, which would otherwise emit flat loads for every weight piece.
+#define MOE_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ T gload(const uint8_t *base, size_t off) {
+  const MOE_GLOBAL uint8_t *g = (const MOE_GLOBAL uint8_t *)base;
+  return *(const MOE_GLOBAL T *)(g + off);
+}
+typedef unsigned int moe_u32x4 __attribute__((ext_vector_type(4)));
+template <>
+__device__ __forceinline__ uint4 gload<uint4>(const uint8_t *base, size_t off) {
+  const MOE_GLOBAL uint8_t *g = (const MOE_GLOBAL uint8_t *)base;
+  const moe_u32x4 v = *(const MOE_GLOBAL moe_u32x4 *)(g + off);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Weight-format tags of the kernels: 8, 4, 2 = integer codes of that many
+// bits with one fp32 scale per row; WB_MX = MXFP4 ("Comment exécuter un
+// réseau de neurones de 744 milliards de paramètres…", section "Modèles
+// supportés": native MXFP4 weights) -- FP4 E2M1 codes packed like int4, one
+// E8M0 scale byte per 32 codes of a row, no row scale.
+constexpr int WB_MX = 5;
+template <int WB>
+__host__ __device__ constexpr int code_bits() {
+  return WB == WB_MX ? 4 : WB;
+}
+
+// E8M0 scale byte -> 2^(s-127) as fp32 (s = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_float(uint32_t s) {
+  return __uint_as_float(s ? s << 23 : 0x00400000u);
+}
+
+// FP4 E2M1 codes in the low (shift 0) or high (shift 4) nibbles of a word's
+// four bytes -> four int8 lanes of twice their value (0, 1, 2, 3, 4, 6, 8,
+// 12 with the code's sign): magnitudes by byte lookup (v_perm_b32 selectors
+// 0-7), the negative table picked where the sign bit is set.  The per-byte
+// mask comes from v_perm_b32's sign-replicating selectors 8-11 (the top bit
+// of bytes 1, 3, 5, 7 of the 8-byte input): with the codes shifted so that
+// each sign bit is the top bit of one of those bytes, one v_perm yields
+// 0xFF or 0x00 per lane.
+__device__ __forceinline__ int mx_lanes(uint32_t w, int shift) {
+  const uint32_t c = (w >> shift) & 0x0F0F0F0Fu;
+  const uint32_t sel = c & 0x07070707u;
+  const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, sel);
+  const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, sel);
+  // input bytes 1, 3 = (c << 12) bytes 1, 3 hold the signs of code bytes 0, 2;
+  // bytes 5, 7 = (c << 4) bytes 1, 3 hold those of code bytes 1, 3
+  const uint32_t m = __builtin_amdgcn_perm(c << 4, c << 12, 0x0B090A08u);
+  return (int)((neg & m) | (pos & ~m));
+}
+
+// Exact dot of 32 FP4 codes (16 bytes) with 32 int8 activations split like
+// the int4 ones: sum (2 fp4(c)) q, |result| <= 32 * 12 * 127.
+__device__ __forceinline__ int dot_mx_block(const uint4 w, const QBlock &a) {
+  int acc = 0;
+  acc = sdot4(mx_lanes(w.x, 0), a.ev[0], acc);
+  acc = sdot4(mx_lanes(w.x, 4), a.od[0], acc);
+  acc = sdot4(mx_lanes(w.y, 0), a.ev[1], acc);
+  acc = sdot4(mx_lanes(w.y, 4), a.od[1], acc);
+  acc = sdot4(mx_lanes(w.z, 0), a.ev[2], acc);
+  acc = sdot4(mx_lanes(w.z, 4), a.od[2], acc);
+  acc = sdot4(mx_lanes(w.w, 0), a.ev[3], acc);
+  acc = sdot4(mx_lanes(w.w, 4), a.od[3], acc);
+  return acc;
+}
+
 // Record of routed expert e (0 <= e < E): entry e of the caller's table of
 // record pointers when there is one (records may then sit anywhere the
 // device can read: HBM cache slots, pinned host memory), else

@@ -335,6 +335,33 @@ struct Act<8> {
   int q[4];  // 16 activations (half a Q8_0 block), natural order
   float d;   // the block's scale
 };
+template <>
+struct Act<WB_MX> {
+  QBlock q;
+  float d;  // block scale / 2 (the MXFP4 dot returns 2 x the block dot)
+};
+
+// One 16-byte weight piece; for MXFP4 also its block's scale.
+template <int WB>
+struct WP {
+  uint4 w;
+};
+template <>
+struct WP<WB_MX> {
+  uint4 w;
+  float s;
+};
+
+// Piece p of a weight row (scl: the row's E8M0 bytes, MXFP4 only; with
+// SCALE false the scale is filled in later).
+template <int WB, bool SCALE = true>
+__device__ __forceinline__ WP<WB> load_wp(const uint8_t *row, const uint8_t *scl, int p,
+                                          bool ok) {
+  WP<WB> r;
+  r.w = ok ? gload<uint4>(row, (size_t)p * 16) : make_uint4(0, 0, 0, 0);
+  if constexpr (WB == WB_MX) r.s = (SCALE && ok) ? e8m0_float(gload<uint8_t>(scl, p)) : 0.0f;
+  return r;
+}
 
 template <int WB>
 __device__ __forceinline__ void load_act(const int8_t *q, const float *d, int p, bool ok,
@@ -369,6 +396,20 @@ __device__ __forceinline__ void load_act<4>(const int8_t *q, const float *d, int
   o.d = dd;
 }
 template <>
+__device__ __forceinline__ void load_act<WB_MX>(const int8_t *q, const float *d, int p, bool ok,
+                                                Act<WB_MX> &o) {
+  uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
+  float dd = 0.0f;
+  if (ok) {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(q + 32 * p);
+    x0 = qp[0];
+    x1 = qp[1];
+    dd = d[p] * 0.5f;
+  }
+  o.q = split_block(x0, x1);
+  o.d = dd;
+}
+template <>
 __device__ __forceinline__ void load_act<2>(const int8_t *q, const float *d, int p, bool ok,
                                             Act<2> &o) {
   uint4 z[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
@@ -397,9 +438,14 @@ __device__ __forceinline__ void load_act<2>(const int8_t *q, const float *d, int
 
 // sum_b d_b * P_b of one 16-byte weight piece against one token
 template <int WB>
-__device__ __forceinline__ float piece_dot(const uint4 w, const Act<WB> &a);
+__device__ __forceinline__ float piece_dot(const WP<WB> &p, const Act<WB> &a);
 template <>
-__device__ __forceinline__ float piece_dot<8>(const uint4 w, const Act<8> &a) {
+__device__ __forceinline__ float piece_dot<WB_MX>(const WP<WB_MX> &p, const Act<WB_MX> &a) {
+  return (float)dot_mx_block(p.w, a.q) * (a.d * p.s);
+}
+template <>
+__device__ __forceinline__ float piece_dot<8>(const WP<8> &p, const Act<8> &a) {
+  const uint4 w = p.w;
   int acc = sdot4((int)w.x, a.q[0], 0);  // 16 int8 codes: exact, |acc| < 2^19
   acc = sdot4((int)w.y, a.q[1], acc);
   acc = sdot4((int)w.z, a.q[2], acc);
@@ -407,11 +453,12 @@ __device__ __forceinline__ float piece_dot<8>(const uint4 w, const Act<8> &a) {
   return (float)acc * a.d;
 }
 template <>
-__device__ __forceinline__ float piece_dot<4>(const uint4 w, const Act<4> &a) {
-  return (float)dot_int4_block16(w, a.q) * a.d;
+__device__ __forceinline__ float piece_dot<4>(const WP<4> &p, const Act<4> &a) {
+  return (float)dot_int4_block16(p.w, a.q) * a.d;
 }
 template <>
-__device__ __forceinline__ float piece_dot<2>(const uint4 w, const Act<2> &a) {
+__device__ __forceinline__ float piece_dot<2>(const WP<2> &p, const Act<2> &a) {
+  const uint4 w = p.w;
   int x = 0, y = 0;
 #pragma unroll
   for (int fi = 0; fi < 4; fi++) {
@@ -436,25 +483,36 @@ template <int WB, int TT, int NPL, int RB, int KS, class QRow, class DRow>
 __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t *blob, int blk,
                              int n_tok, const int *pairs, QRow qrow, DRow drow) {
   static_assert(KS == 1 || KS == 2, "K split");
+  static_assert(WB != WB_MX || KS == 1, "MXFP4 rows fit one wave");
   __shared__ float part[KS][TT][32][2];  // KS = 2: scaled half sums (gate, up)
+  // MXFP4: the block scales of the workgroup's 32 gate and 32 up rows, staged
+  // once with 16-byte loads (one byte load per piece would double the load
+  // instructions of the weight stream): [gate, up][32 rows][H/32 <= 256]
+  constexpr int MSC = 32 * 256;
+  __shared__ __align__(16) uint8_t msc[WB == WB_MX ? 2 * MSC : 16];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, I = a.I;
   constexpr int RW = 8 * KS;  // rows per wave
   const int khalf = wv / (4 / KS), wr = wv % (4 / KS);
-  const int np_all = H / (128 / WB), np_half = (np_all + KS - 1) / KS;
+  const int np_all = H / (128 / code_bits<WB>()), np_half = (np_all + KS - 1) / KS;
   const int p0 = khalf * np_half, npieces = min(np_all, p0 + np_half);
-  const size_t row_b = (size_t)H * WB / 8;
+  const size_t row_b = (size_t)H * code_bits<WB>() / 8;
   const uint8_t *gate = blob;
   const uint8_t *up = blob + (size_t)I * row_b;
-  const float *scales = reinterpret_cast<const float *>(blob + 3 * (size_t)I * row_b);
+  const uint8_t *tail = blob + 3 * (size_t)I * row_b;  // row scales, or MXFP4 block scales
+  const float *scales = reinterpret_cast<const float *>(tail);
+  const int nblk = H / 32;
+  const uint8_t *gsc = tail, *usc = tail + (size_t)I * nblk;  // MXFP4
   const int rbase = blk * 32 + wr * RW;
   // row scales of the wave's rows: lane l < RW gate row l, RW <= l < 2 RW up row l - RW
-  const float sc = lane < 2 * RW ? scales[(lane < RW ? 0 : I) + rbase + lane % RW] : 0.0f;
+  const float sc = lane >= 2 * RW ? 0.0f
+                   : WB == WB_MX ? 1.0f
+                                 : scales[(lane < RW ? 0 : I) + rbase + lane % RW];
   constexpr int NB = RW / RB;
   for (int c0 = 0; c0 < n_tok; c0 += TT) {
     // two buffers: batch bt+1 is in flight while batch bt is computed
-    uint4 wb[2][RB][2][NPL];  // [buffer][row of batch][gate, up][piece]
-    auto load_batch = [&](uint4 (&dst)[RB][2][NPL], int bt) {
+    WP<WB> wb[2][RB][2][NPL];  // [buffer][row of batch][gate, up][piece]
+    auto load_batch = [&](WP<WB> (&dst)[RB][2][NPL], int bt) {
 #pragma unroll
       for (int rr = 0; rr < RB; rr++) {
         const int r = rbase + bt * RB + rr;
@@ -462,10 +520,8 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
         for (int i = 0; i < NPL; i++) {
           const int p = p0 + lane + 64 * i;
           const bool ok = p < npieces;
-          dst[rr][0][i] = ok ? reinterpret_cast<const uint4 *>(gate + (size_t)r * row_b)[p]
-                             : make_uint4(0, 0, 0, 0);
-          dst[rr][1][i] = ok ? reinterpret_cast<const uint4 *>(up + (size_t)r * row_b)[p]
-                             : make_uint4(0, 0, 0, 0);
+          dst[rr][0][i] = load_wp<WB, false>(gate + (size_t)r * row_b, nullptr, p, ok);
+          dst[rr][1][i] = load_wp<WB, false>(up + (size_t)r * row_b, nullptr, p, ok);
         }
       }
     };
@@ -481,12 +537,32 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
                      act[i][t]);
       }
     }
+    if constexpr (WB == WB_MX) {
+      if (c0 == 0) {  // rows blk*32 .. +31 of each matrix: 32 * nblk contiguous bytes
+        const int n16 = 32 * nblk / 16;
+        for (int i = threadIdx.x; i < 2 * n16; i += 256) {
+          const int m = i / n16, o = (i % n16) * 16;
+          *reinterpret_cast<uint4 *>(msc + m * MSC + o) =
+              gload<uint4>(m ? usc : gsc, (size_t)blk * 32 * nblk + o);
+        }
+        __syncthreads();
+      }
+    }
 #pragma unroll
     for (int bt = 0; bt < NB; bt++) {
       if (bt + 1 < NB) load_batch(wb[(bt + 1) & 1], bt + 1);
 #pragma unroll
       for (int rr = 0; rr < RB; rr++) {
         const int rl = bt * RB + rr;  // row within the wave's RW
+        if constexpr (WB == WB_MX) {
+#pragma unroll
+          for (int i = 0; i < NPL; i++) {
+            const int p = lane + 64 * i;
+            const int o = (wr * RW + rl) * nblk + p;
+            wb[bt & 1][rr][0][i].s = p < npieces ? e8m0_float(msc[o]) : 0.0f;
+            wb[bt & 1][rr][1][i].s = p < npieces ? e8m0_float(msc[MSC + o]) : 0.0f;
+          }
+        }
         float g[TT], u[TT];
 #pragma unroll
         for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
@@ -551,27 +627,30 @@ template <int WB, int TT, int NPL>
 __device__ void shared_rows_block(const LayerArgs &a, int blk) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, I = a.I, T = a.T;
-  const int npieces = H / (128 / WB);
-  const size_t row_b = (size_t)H * WB / 8;
+  const int npieces = H / (128 / code_bits<WB>());
+  const size_t row_b = (size_t)H * code_bits<WB>() / 8;
   const uint8_t *gate = a.shared;
   const uint8_t *up = a.shared + (size_t)I * row_b;
-  const float *scales = reinterpret_cast<const float *>(a.shared + 3 * (size_t)I * row_b);
+  const uint8_t *tail = a.shared + 3 * (size_t)I * row_b;
+  const float *scales = reinterpret_cast<const float *>(tail);
+  const int nblk = H / 32;
+  const uint8_t *gsc = tail, *usc = tail + (size_t)I * nblk;  // MXFP4
   const int r0 = blk * 8 + wv * 2;
-  uint4 wb[2][2][NPL];
+  WP<WB> wb[2][2][NPL];
 #pragma unroll
   for (int rr = 0; rr < 2; rr++) {
 #pragma unroll
     for (int i = 0; i < NPL; i++) {
       const int p = lane + 64 * i;
       const bool ok = p < npieces;
-      wb[rr][0][i] = ok ? reinterpret_cast<const uint4 *>(gate + (size_t)(r0 + rr) * row_b)[p]
-                        : make_uint4(0, 0, 0, 0);
-      wb[rr][1][i] = ok ? reinterpret_cast<const uint4 *>(up + (size_t)(r0 + rr) * row_b)[p]
-                        : make_uint4(0, 0, 0, 0);
+      const size_t r = (size_t)(r0 + rr);
+      wb[rr][0][i] = load_wp<WB>(gate + r * row_b, gsc + r * nblk, p, ok);
+      wb[rr][1][i] = load_wp<WB>(up + r * row_b, usc + r * nblk, p, ok);
     }
   }
-  const float sg0 = scales[r0], sg1 = scales[r0 + 1];
-  const float su0 = scales[I + r0], su1 = scales[I + r0 + 1];
+  const bool mx = WB == WB_MX;  // no row scales
+  const float sg0 = mx ? 1.0f : scales[r0], sg1 = mx ? 1.0f : scales[r0 + 1];
+  const float su0 = mx ? 1.0f : scales[I + r0], su1 = mx ? 1.0f : scales[I + r0 + 1];
   for (int c0 = 0; c0 < T; c0 += TT) {
     Act<WB> act[NPL][TT];
 #pragma unroll
@@ -712,7 +791,8 @@ __global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
   // int8 rows longer than 4 pieces per lane are split over two waves
   constexpr int KS = WB == 8 && NPL > 4 ? 2 : 1;
   gate_up_rows<WB, TT, KS == 2 ? 4 : NPL,
-               (TT == 1 ? (WB == 2 ? 2 * MOE_K2_ROWS : WB == 8 ? 1 : MOE_K2_ROWS) : 1), KS>(
+               (TT == 1 ? (WB == 2 ? 2 * MOE_K2_ROWS : WB == 8 || WB == WB_MX ? 1 : MOE_K2_ROWS) : 1),
+               KS>(
       a, hb, rec, blk, n_tok, pairs,
       [&](int i) { return (const int8_t *)(a.q + (size_t)min(max(toks[i], 0), a.T - 1) * a.H); },
       [&](int i) {
@@ -770,7 +850,7 @@ __device__ __forceinline__ void down_act(const LayerArgs &a, const int *prs, int
 // pairs: quarter partials into part[wv][pair][row].
 template <int WB, int TT, int NPQ, int LPR>
 __device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, int pl,
-                                          const uint4 (&w)[LPR / 8][NPQ],
+                                          const WP<WB> (&w)[LPR / 8][NPQ],
                                           const float (&sd)[LPR / 8],
                                           const Act<WB> (&act)[NPQ][TT], const int (&pair)[TT]) {
 #pragma unroll
@@ -815,10 +895,14 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   int *tab = reinterpret_cast<int *>(dyn + (size_t)4 * P * sbk::RT * 4);  // [slots][TAB_W]
   const uint8_t **recs = reinterpret_cast<const uint8_t **>(
       dyn + (size_t)4 * P * sbk::RT * 4 + (((size_t)a.n_slots_ub * TAB_W * 4 + 7) & ~(size_t)7));
-  const int npieces = I / (128 / WB);
+  constexpr int CB = code_bits<WB>();
+  const int npieces = I / (128 / CB);
   const int qb = wv * npieces / 4, nq = (wv + 1) * npieces / 4 - qb;  // this wave's quarter
-  const size_t row_b = (size_t)I * WB / 8;
-  const size_t down_off = 2 * (size_t)I * ((size_t)H * WB / 8);
+  const size_t row_b = (size_t)I * CB / 8;
+  const size_t down_off = 2 * (size_t)I * ((size_t)H * CB / 8);
+  const size_t tail_off = 3 * (size_t)I * ((size_t)H * CB / 8);  // scales after the codes
+  const size_t dsc_off = tail_off + 2 * (size_t)I * (H / 32);    // MXFP4 down block scales
+  const int nblk = I / 32;
   const int rl = lane / LPR, pl = lane % LPR;
   const int j0 = tile * sbk::RT;
   // The shared expert (slot 0 when present) needs nothing from the slot
@@ -827,24 +911,23 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
 #pragma unroll
   for (int t = 0; t < sbk::TMAX; t++) shp[t] = T * K + t;
   const int S0 = a.n_shared;
-  uint4 ws0[RPL][NPQ];
+  WP<WB> ws0[RPL][NPQ];
   float sd0[RPL];
   Act<WB> act_s[NPQ][TT];
   int pair_s[TT];
   if (S0) {
     const uint8_t *down = a.shared + down_off;
-    const float *sdp =
-        reinterpret_cast<const float *>(a.shared + 3 * (size_t)I * ((size_t)H * WB / 8)) + 2 * I;
+    const float *sdp = reinterpret_cast<const float *>(a.shared + tail_off) + 2 * I;
 #pragma unroll
     for (int rr = 0; rr < RPL; rr++) {
       const int row = j0 + rl + (64 / LPR) * rr;
 #pragma unroll
       for (int i = 0; i < NPQ; i++) {
         const int q = pl + LPR * i;
-        ws0[rr][i] = q < nq ? reinterpret_cast<const uint4 *>(down + (size_t)row * row_b)[qb + q]
-                            : make_uint4(0, 0, 0, 0);
+        ws0[rr][i] = load_wp<WB>(down + (size_t)row * row_b,
+                                 a.shared + dsc_off + (size_t)row * nblk, qb + q, q < nq);
       }
-      sd0[rr] = sdp[row];
+      sd0[rr] = WB == WB_MX ? 1.0f : sdp[row];
     }
     down_act<WB, TT, NPQ, LPR>(a, shp, T, 0, P, qb, nq, pl, act_s, pair_s);
   }
@@ -871,26 +954,24 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
     }
   }
   for (int s0 = S0; s0 < n_slots; s0 += SB) {
-    uint4 wd[SB][RPL][NPQ];
+    WP<WB> wd[SB][RPL][NPQ];
     float sd[SB][RPL];
 #pragma unroll
     for (int b = 0; b < SB; b++) {
       const bool ok_s = s0 + b < n_slots;
       const uint8_t *blob = ok_s ? recs[s0 + b] : a.shared;
       const uint8_t *down = blob + down_off;
-      const float *sdp =
-          reinterpret_cast<const float *>(blob + 3 * (size_t)I * ((size_t)H * WB / 8)) + 2 * I;
+      const float *sdp = reinterpret_cast<const float *>(blob + tail_off) + 2 * I;
 #pragma unroll
       for (int rr = 0; rr < RPL; rr++) {
         const int row = j0 + rl + (64 / LPR) * rr;
 #pragma unroll
         for (int i = 0; i < NPQ; i++) {
           const int q = pl + LPR * i;
-          wd[b][rr][i] = (ok_s && q < nq)
-                             ? reinterpret_cast<const uint4 *>(down + (size_t)row * row_b)[qb + q]
-                             : make_uint4(0, 0, 0, 0);
+          wd[b][rr][i] = load_wp<WB>(down + (size_t)row * row_b,
+                                     blob + dsc_off + (size_t)row * nblk, qb + q, ok_s && q < nq);
         }
-        sd[b][rr] = ok_s ? sdp[row] : 0.0f;
+        sd[b][rr] = !ok_s ? 0.0f : WB == WB_MX ? 1.0f : sdp[row];
       }
     }
     // the first TT pairs of every slot of the batch: one round trip for all
@@ -999,7 +1080,7 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
                       (size_t)a.n_slots_ub * sizeof(void *);
   constexpr int SB = TT == 1 ? (WB == 2 ? 2 * MOE_K3_SLOTS : MOE_K3_SLOTS) : 2;
   constexpr int TT3 = TT == 1 ? 1 : MOE_K3_TT;  // tokens per chunk in the down kernel
-  const int quarter = (a.I / (128 / WB) + 3) / 4;
+  const int quarter = (a.I / (128 / code_bits<WB>()) + 3) / 4;
   if (quarter <= 8)
     launch_k(k_down_small<WB, TT3, 1, SB, 8>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
              st, stage_ev(ev, MOE_STAGE_DOWN), a);
@@ -1013,7 +1094,7 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
 
 template <int WB, int TT>
 static void launch3_np(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
-  const int per = 128 / WB;
+  const int per = 128 / code_bits<WB>();
   const int ng = (a.H / per + 63) / 64, nd = (a.I / per + 63) / 64;
   if constexpr (WB == 8) {  // 16 codes per piece: up to 7 pieces per lane
     if (ng <= 2 && nd <= 1) launch3<WB, TT, 2, 1>(a, st, ev);
@@ -1030,7 +1111,10 @@ static void launch3_np(const LayerArgs &a, hipStream_t st, const moe_events *ev)
 
 void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev) {
   a.n_slots_ub = a.n_shared + (a.T * a.K < a.E ? a.T * a.K : a.E);
-  if (a.wbits == 8) {  // a piece carries 16 codes: two tokens per chunk
+  if (a.wfmt == 1) {  // MXFP4: int4 layout of the codes, a scale per piece
+    if (a.T == 1) launch3_np<WB_MX, 1>(a, st, ev);
+    else launch3_np<WB_MX, MOE_TT_INT4>(a, st, ev);
+  } else if (a.wbits == 8) {  // a piece carries 16 codes: two tokens per chunk
     if (a.T == 1) launch3_np<8, 1>(a, st, ev);
     else launch3_np<8, 2>(a, st, ev);
   } else if (a.wbits == 4) {

@@ -119,11 +119,15 @@ __device__ __forceinline__ uint2 even_odd8(uint32_t w0, uint32_t w1) {
 }
 
 // A fragment of one 32-code block: lane (m, g) holds codes 8g..8g+7 of row m
-// -- int4: as 16 x code, even codes first (from 4 bytes); int8: the 8 bytes.
+// -- int4: as 16 x code, even codes first (from 4 bytes); MXFP4: as 2 x the
+// FP4 value, even codes first; int8: the 8 bytes.
 template <int WB>
 __device__ __forceinline__ long a_frag(const uint8_t *row, int b, int g) {
   if constexpr (WB == 8) {
     return *reinterpret_cast<const long *>(row + b * 32 + g * 8);
+  } else if constexpr (WB == WB_MX) {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(row + b * 16 + g * 4);
+    return (long)(uint32_t)mx_lanes(w, 0) | ((long)(uint32_t)mx_lanes(w, 4) << 32);
   } else {
     const uint32_t w = *reinterpret_cast<const uint32_t *>(row + b * 16 + g * 4);
     return (long)(uint32_t)lo16(w) | ((long)(uint32_t)hi16(w) << 32);
@@ -131,8 +135,8 @@ __device__ __forceinline__ long a_frag(const uint8_t *row, int b, int g) {
 }
 
 // Stage one K chunk of activations: rows = tokens (64), CB blocks of 32
-// int8 and their scales (for int4 weights: reordered per 8 like the nibble
-// split, and the scales / 16).
+// int8 and their scales (for int4 and MXFP4 weights: reordered per 8 like
+// the nibble split, and the scales / 16 or / 2).
 struct ActChunk {
   uint4 v[4];  // 4 x 16 bytes per thread (64 tokens x 16 pieces)
   float d[2];  // 64 tokens x 8 block scales
@@ -157,7 +161,8 @@ __device__ __forceinline__ void load_act_chunk(const int8_t *q, const float *d, 
     const int i = tid + 256 * u, tok_i = i >> 3, b = i & 7;
     const int blk = c * mf::CB + b;
     r.d[u] = (tok_i < n && blk < nblk)
-                 ? d[(size_t)tokl[tok_i] * (row_len / 32) + blk] * (WB == 8 ? 1.0f : 0.0625f)
+                 ? d[(size_t)tokl[tok_i] * (row_len / 32) + blk] *
+                       (WB == 8 ? 1.0f : WB == WB_MX ? 0.5f : 0.0625f)
                  : 0.0f;
   }
 }
@@ -183,39 +188,51 @@ __device__ __forceinline__ void store_act_chunk(const ActChunk &r, uint8_t *bs, 
   }
 }
 
-// Stage one K chunk of NM weight matrices: 64 rows x CB blocks x (4 WB)
-// bytes, as 16-byte pieces (PPR per row).
+// Stage one K chunk of NM weight matrices: 64 rows x CB blocks x (4 bits)
+// bytes, as 16-byte pieces (PPR per row); MXFP4 also the 64 x CB scale bytes
+// (two per thread).
 template <int NM, int WB>
 struct WChunk {
-  static constexpr int PPR = mf::CB * WB / 4;  // pieces per row: int4 8, int8 16
-  uint4 v[NM * PPR / 4];                       // 64 rows x PPR pieces / 256 threads
+  static constexpr int PPR = mf::CB * code_bits<WB>() / 4;  // pieces per row: 4-bit 8, int8 16
+  uint4 v[NM * PPR / 4];                                     // 64 rows x PPR pieces / 256 threads
+  uint32_t sc[NM];                                           // MXFP4: 2 scale bytes
 };
 
 template <int NM, int WB>
-__device__ __forceinline__ void load_w_chunk(const uint8_t *const *mat, size_t row_b, int r0,
+__device__ __forceinline__ void load_w_chunk(const uint8_t *const *mat,
+                                             const uint8_t *const *scl, size_t row_b, int r0,
                                              int c, int nblk, WChunk<NM, WB> &r) {
-  constexpr int PPR = WChunk<NM, WB>::PPR, PER = PPR / 4;
+  constexpr int PPR = WChunk<NM, WB>::PPR, PER = PPR / 4, CW = code_bits<WB>();
   const int tid = threadIdx.x;
 #pragma unroll
   for (int m = 0; m < NM; m++) {
 #pragma unroll
     for (int u = 0; u < PER; u++) {
       const int i = tid + 256 * u, row = i / PPR, pc = i % PPR;
-      const int blk = c * mf::CB + pc * 16 / (4 * WB);
-      r.v[m * PER + u] =
-          blk < nblk ? *reinterpret_cast<const uint4 *>(mat[m] + (size_t)(r0 + row) * row_b +
-                                                        (size_t)c * mf::CB * 4 * WB + pc * 16)
-                     : make_uint4(0, 0, 0, 0);
+      const int blk = c * mf::CB + pc * 16 / (4 * CW);
+      r.v[m * PER + u] = blk < nblk ? gload<uint4>(mat[m], (size_t)(r0 + row) * row_b +
+                                                              (size_t)c * mf::CB * 4 * CW + pc * 16)
+                                    : make_uint4(0, 0, 0, 0);
+    }
+    if constexpr (WB == WB_MX) {  // row tid / 4, blocks 2 (tid % 4), +1 of the chunk
+      const int row = tid >> 2, blk = c * mf::CB + 2 * (tid & 3);
+      r.sc[m] = blk < nblk ? gload<uint16_t>(scl[m], (size_t)(r0 + row) * nblk + blk) : 0u;
     }
   }
 }
 
+// wsl (MXFP4): the chunk's block scales as floats, [NM][CB][64 rows].
 template <int NM, int WB>
-__device__ __forceinline__ void store_w_chunk(const WChunk<NM, WB> &r, uint8_t *as) {
+__device__ __forceinline__ void store_w_chunk(const WChunk<NM, WB> &r, uint8_t *as, float *wsl) {
   constexpr int PPR = WChunk<NM, WB>::PPR, PER = PPR / 4, AS = mf::astr<WB>();
   const int tid = threadIdx.x;
 #pragma unroll
   for (int m = 0; m < NM; m++) {
+    if constexpr (WB == WB_MX) {
+      const int row = tid >> 2, b = 2 * (tid & 3);
+      wsl[(m * mf::CB + b) * mf::RT + row] = e8m0_float(r.sc[m] & 0xFFu);
+      wsl[(m * mf::CB + b + 1) * mf::RT + row] = e8m0_float(r.sc[m] >> 8);
+    }
 #pragma unroll
     for (int u = 0; u < PER; u++) {
       const int i = tid + 256 * u, row = i / PPR, pc = i % PPR;
@@ -241,10 +258,10 @@ __device__ __forceinline__ void store_w_chunk(const WChunk<NM, WB> &r, uint8_t *
 // per workgroup so the loop body has no branches), row 16 wv + 4 g + i.  DBG: raw block dots of
 // matrix m go to dots[m] at ((pair * R + row) * nblk + block).
 template <int NM, bool DBG, int NS, int WB>
-__device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, const int8_t *q,
-                           const float *d, int row_len, const int *tokl, const int *pairl, int n,
-                           int nblk, uint8_t *bs, float *ds, uint8_t *as, float (&acc)[NM][4][4],
-                           int32_t *const *dots, int R) {
+__device__ void mfma_kloop(const uint8_t *const *mat, const uint8_t *const *scl, size_t row_b,
+                           int r0, const int8_t *q, const float *d, int row_len, const int *tokl,
+                           const int *pairl, int n, int nblk, uint8_t *bs, float *ds, uint8_t *as,
+                           float *wsl, float (&acc)[NM][4][4], int32_t *const *dots, int R) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int m16 = lane & 15, g = lane >> 4;
 #pragma unroll
@@ -258,15 +275,15 @@ __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, cons
   ActChunk ac;
   WChunk<NM, WB> wc;
   load_act_chunk<WB>(q, d, row_len, tokl, n, 0, nblk, ac);
-  load_w_chunk<NM, WB>(mat, row_b, r0, 0, nblk, wc);
+  load_w_chunk<NM, WB>(mat, scl, row_b, r0, 0, nblk, wc);
   for (int c = 0; c < nchunk; c++) {
     __syncthreads();  // the previous chunk is consumed
     store_act_chunk<WB>(ac, bs, ds);
-    store_w_chunk<NM, WB>(wc, as);
+    store_w_chunk<NM, WB>(wc, as, wsl);
     __syncthreads();
     if (c + 1 < nchunk) {  // next chunk in flight during this one's MFMAs
       load_act_chunk<WB>(q, d, row_len, tokl, n, c + 1, nblk, ac);
-      load_w_chunk<NM, WB>(mat, row_b, r0, c + 1, nblk, wc);
+      load_w_chunk<NM, WB>(mat, scl, row_b, r0, c + 1, nblk, wc);
     }
     const int nb = min(mf::CB, nblk - c * mf::CB);
     for (int b = 0; b < nb; b++) {
@@ -274,6 +291,12 @@ __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, cons
 #pragma unroll
       for (int m = 0; m < NM; m++)
         af[m] = a_frag<WB>(as + (size_t)m * mf::RT * AS + (wv * 16 + m16) * AS, b, g);
+      float4 wsv[NM];  // MXFP4: block scales of this lane's 4 rows
+#pragma unroll
+      for (int m = 0; m < NM; m++)
+        wsv[m] = WB == WB_MX ? *reinterpret_cast<const float4 *>(
+                                   wsl + (m * mf::CB + b) * mf::RT + wv * 16 + g * 4)
+                             : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
 #pragma unroll
       for (int s = 0; s < NS; s++) {  // only the sub-tiles that hold tokens
         const int col = s * 16 + m16;
@@ -283,14 +306,21 @@ __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, cons
         for (int m = 0; m < NM; m++) {
           const v4i z = {0, 0, 0, 0};
           const v4i p = __builtin_amdgcn_mfma_i32_16x16x32_i8(af[m], bf, z, 0, 0, 0);
+          if constexpr (WB == WB_MX) {
+            acc[m][s][0] = fmaf(dd * wsv[m].x, (float)p[0], acc[m][s][0]);
+            acc[m][s][1] = fmaf(dd * wsv[m].y, (float)p[1], acc[m][s][1]);
+            acc[m][s][2] = fmaf(dd * wsv[m].z, (float)p[2], acc[m][s][2]);
+            acc[m][s][3] = fmaf(dd * wsv[m].w, (float)p[3], acc[m][s][3]);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; i++) acc[m][s][i] = fmaf(dd, (float)p[i], acc[m][s][i]);
+            for (int i = 0; i < 4; i++) acc[m][s][i] = fmaf(dd, (float)p[i], acc[m][s][i]);
+          }
           if (DBG && dots[m] && col < n) {
             const int blk = c * mf::CB + b;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
               const int row = r0 + wv * 16 + g * 4 + i;
-              dots[m][((size_t)pairl[col] * R + row) * nblk + blk] = WB == 8 ? p[i] : p[i] >> 4;
+              dots[m][((size_t)pairl[col] * R + row) * nblk + blk] = WB == 4 ? p[i] >> 4 : p[i];
             }
           }
         }
@@ -301,26 +331,27 @@ __device__ void mfma_kloop(const uint8_t *const *mat, size_t row_b, int r0, cons
 
 // mfma_kloop with the sub-tile count of n tokens chosen once.
 template <int NM, bool DBG, int WB>
-__device__ void mfma_kloop_n(const uint8_t *const *mat, size_t row_b, int r0, const int8_t *q,
-                             const float *d, int row_len, const int *tokl, const int *pairl,
-                             int n, int nblk, uint8_t *bs, float *ds, uint8_t *as,
-                             float (&acc)[NM][4][4], int32_t *const *dots, int R) {
+__device__ void mfma_kloop_n(const uint8_t *const *mat, const uint8_t *const *scl, size_t row_b,
+                             int r0, const int8_t *q, const float *d, int row_len,
+                             const int *tokl, const int *pairl, int n, int nblk, uint8_t *bs,
+                             float *ds, uint8_t *as, float *wsl, float (&acc)[NM][4][4],
+                             int32_t *const *dots, int R) {
   switch ((n + 15) / 16) {
     case 1:
-      mfma_kloop<NM, DBG, 1, WB>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
-                                 as, acc, dots, R);
+      mfma_kloop<NM, DBG, 1, WB>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+                                 as, wsl, acc, dots, R);
       break;
     case 2:
-      mfma_kloop<NM, DBG, 2, WB>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
-                                 as, acc, dots, R);
+      mfma_kloop<NM, DBG, 2, WB>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+                                 as, wsl, acc, dots, R);
       break;
     case 3:
-      mfma_kloop<NM, DBG, 3, WB>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
-                                 as, acc, dots, R);
+      mfma_kloop<NM, DBG, 3, WB>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+                                 as, wsl, acc, dots, R);
       break;
     default:
-      mfma_kloop<NM, DBG, 4, WB>(mat, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
-                                 as, acc, dots, R);
+      mfma_kloop<NM, DBG, 4, WB>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+                                 as, wsl, acc, dots, R);
   }
 }
 
@@ -339,6 +370,7 @@ __global__ void __launch_bounds__(256, 3) k_gate_up_mfma(FfnArgs a, const int4 *
   __shared__ __align__(16) uint8_t bs[MF_LDS_B];
   __shared__ float ds[mf::NT * mf::CB];
   __shared__ __align__(16) uint8_t as[2 * mf::RT * mf::astr<WB>()];
+  __shared__ __align__(16) float wsl[WB == WB_MX ? 2 * mf::CB * mf::RT : 4];
   __shared__ int tokl[mf::NT], pairl[mf::NT];
   if ((int)blockIdx.y >= *n_tiles) return;
   const int4 t = tiles[blockIdx.y];
@@ -352,21 +384,24 @@ __global__ void __launch_bounds__(256, 3) k_gate_up_mfma(FfnArgs a, const int4 *
     pairl[tid] = pair;
   }
   __syncthreads();
-  const size_t row_b = (size_t)H * WB / 8;
+  const size_t row_b = (size_t)H * code_bits<WB>() / 8;
   const uint8_t *mats[2] = {ti.blob, ti.blob + (size_t)I * row_b};
+  const uint8_t *tail = ti.blob + 3 * (size_t)I * row_b;  // row scales, or MXFP4 block scales
+  const uint8_t *scl[2] = {tail, tail + (size_t)I * (H / 32)};
   float acc[2][4][4];
   int32_t *dots[2] = {a.dbg.gate_dots, a.dbg.up_dots};
-  mfma_kloop_n<2, DBG, WB>(mats, row_b, r0, a.q, a.d, H, tokl, pairl, ti.n, H / 32, bs, ds, as,
-                           acc, dots, I);
+  mfma_kloop_n<2, DBG, WB>(mats, scl, row_b, r0, a.q, a.d, H, tokl, pairl, ti.n, H / 32, bs, ds,
+                           as, wsl, acc, dots, I);
   // epilogue: h into LDS as [token][64 rows] fp32 (reuses the activation tile)
-  const float *scales = reinterpret_cast<const float *>(ti.blob + 3 * (size_t)I * row_b);
+  const float *scales = reinterpret_cast<const float *>(tail);
   __syncthreads();
   float *hs = reinterpret_cast<float *>(bs);  // 64 x 64 floats = 16 KB <= sizeof(bs)
   const int m16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int rl = wv * 16 + g * 4 + i;
-    const float sg = scales[r0 + rl], su = scales[I + r0 + rl];
+    const float sg = WB == WB_MX ? 1.0f : scales[r0 + rl];
+    const float su = WB == WB_MX ? 1.0f : scales[I + r0 + rl];
 #pragma unroll
     for (int s = 0; s < 4; s++) {
       const float gv = sg * acc[0][s][i], uv = su * acc[1][s][i];
@@ -415,6 +450,7 @@ __global__ void __launch_bounds__(256) k_down_mfma(FfnArgs a, const int4 *tiles,
   __shared__ __align__(16) uint8_t bs[MF_LDS_B];
   __shared__ float ds[mf::NT * mf::CB];
   __shared__ __align__(16) uint8_t as[mf::RT * mf::astr<WB>()];
+  __shared__ __align__(16) float wsl[WB == WB_MX ? mf::CB * mf::RT : 4];
   __shared__ int tokl[mf::NT], pairl[mf::NT];
   if ((int)blockIdx.y >= *n_tiles) return;
   const int4 t = tiles[blockIdx.y];
@@ -428,17 +464,19 @@ __global__ void __launch_bounds__(256) k_down_mfma(FfnArgs a, const int4 *tiles,
     pairl[tid] = pair;
   }
   __syncthreads();
-  const size_t row_b = (size_t)I * WB / 8;
-  const size_t gate_b = (size_t)I * ((size_t)H * WB / 8);  // bytes of one gate/up matrix
+  const size_t row_b = (size_t)I * code_bits<WB>() / 8;
+  const size_t gate_b = (size_t)I * ((size_t)H * code_bits<WB>() / 8);  // one gate/up matrix
   const uint8_t *mats[1] = {ti.blob + 2 * gate_b};
+  const uint8_t *scl[1] = {ti.blob + 3 * gate_b + 2 * (size_t)I * (H / 32)};  // MXFP4
   float acc[1][4][4];
   int32_t *dots[1] = {a.dbg.down_dots};
-  mfma_kloop_n<1, DBG, WB>(mats, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs, ds, as,
-                           acc, dots, H);
+  mfma_kloop_n<1, DBG, WB>(mats, scl, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs, ds,
+                           as, wsl, acc, dots, H);
   const float *sd = reinterpret_cast<const float *>(ti.blob + 3 * gate_b) + 2 * I;
   const int m16 = lane & 15, g = lane >> 4;
   const int row = r0 + wv * 16 + g * 4;  // 4 consecutive rows per lane
-  const float4 s4 = *reinterpret_cast<const float4 *>(sd + row);
+  const float4 s4 = WB == WB_MX ? make_float4(1.0f, 1.0f, 1.0f, 1.0f)
+                                : *reinterpret_cast<const float4 *>(sd + row);
 #pragma unroll
   for (int s = 0; s < 4; s++) {
     const int col = s * 16 + m16;
@@ -481,7 +519,10 @@ void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_
                      tiles, n_tiles);
   const bool dbg = a.dbg.gate_dots || a.dbg.up_dots || a.dbg.h || a.dbg.q_h || a.dbg.d_h ||
                    a.dbg.down_dots;
-  if (a.wbits == 8) {
+  if (a.wfmt == 1) {
+    if (dbg) launch_mfma_wb<true, WB_MX>(a, max_tiles, tiles, n_tiles, q_h, d_h, st, ev);
+    else launch_mfma_wb<false, WB_MX>(a, max_tiles, tiles, n_tiles, q_h, d_h, st, ev);
+  } else if (a.wbits == 8) {
     if (dbg) launch_mfma_wb<true, 8>(a, max_tiles, tiles, n_tiles, q_h, d_h, st, ev);
     else launch_mfma_wb<false, 8>(a, max_tiles, tiles, n_tiles, q_h, d_h, st, ev);
   } else {

@@ -54,6 +54,7 @@ void launch_group(int n_slots, int E, const int32_t *idx, int32_t *counts, int32
 // Expert FFN over grouped tokens (dot-product GEMV path).
 struct FfnArgs {
   int H, I, E, K, T, n_shared, wbits;
+  int wfmt;  // 0: integer codes with row scales; 1: MXFP4
   size_t blob_bytes;
   const int8_t *q;
   const float *d;
@@ -79,6 +80,7 @@ void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_
 // Whole layer for 1..16 tokens in three kernels (decode.hip).
 struct LayerArgs {
   int H, I, E, G, TG, K, T, n_shared, wbits;
+  int wfmt;  // 0: integer codes with row scales; 1: MXFP4
   float scale, eps;
   float top_p;  // adaptive expert top-p; 0 or 1 = off
   size_t blob_bytes;

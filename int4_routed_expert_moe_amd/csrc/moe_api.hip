@@ -68,6 +68,9 @@ int check_cfg(const moe_cfg *c) {
     return fail(MOE_EINVAL, "routed_scaling must be finite and > 0");
   if (!(c->top_p >= 0.0f && c->top_p <= 1.0f))
     return fail(MOE_EINVAL, "top_p must be 0 (off) or in (0, 1]");
+  if (c->wfmt != 0 && c->wfmt != 1) return fail(MOE_EINVAL, "wfmt=%d not in {0,1}", c->wfmt);
+  if (c->wfmt == 1 && c->wbits != 4)
+    return fail(MOE_EINVAL, "MXFP4 experts (wfmt 1) need wbits 4 (4-bit codes)");
   return MOE_OK;
 }
 
@@ -89,8 +92,9 @@ int launched(const char *what) {
 }
 
 size_t blob_bytes(const moe_cfg &c) {
-  return ((size_t)2 * c.inter * c.hidden + (size_t)c.hidden * c.inter) * (size_t)c.wbits / 8 +
-         sizeof(float) * ((size_t)2 * c.inter + c.hidden);
+  const size_t elems = (size_t)2 * c.inter * c.hidden + (size_t)c.hidden * c.inter;
+  if (c.wfmt == 1) return elems / 2 + elems / 32;  // FP4 codes + one E8M0 byte per 32
+  return elems * (size_t)c.wbits / 8 + sizeof(float) * ((size_t)2 * c.inter + c.hidden);
 }
 
 // workspace carving --------------------------------------------------------
@@ -195,6 +199,7 @@ int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32
   a.T = T;
   a.n_shared = c.n_shared;
   a.wbits = c.wbits;
+  a.wfmt = c.wfmt;
   a.blob_bytes = blob_bytes(c);
   a.q = q;
   a.d = d;
@@ -211,9 +216,10 @@ int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32
   if (dbg) a.dbg = *dbg;
   else memset(&a.dbg, 0, sizeof(a.dbg));
   const bool mfma = moe::mfma_supported(a);
-  if (c.wbits == 8 && !mfma)  // the vector-dot kernels take packed int4 / int2 only
-    return fail(MOE_EINVAL, "int8 experts need the matrix-core path (H %% 256, I %% 64)");
-  if ((T >= MOE_MFMA_MIN_T || c.wbits == 8) && mfma) {  // grouped GEMMs, matrix cores
+  const bool mfma_only = c.wbits == 8 || c.wfmt == 1;  // the vector-dot kernels take int4/int2
+  if (mfma_only && !mfma)
+    return fail(MOE_EINVAL, "int8 / MXFP4 experts need the matrix-core path (H %% 256, I %% 64)");
+  if ((T >= MOE_MFMA_MIN_T || mfma_only) && mfma) {  // grouped GEMMs, matrix cores
     const size_t pairs = (size_t)T * c.top_k + (size_t)T * c.n_shared;
     int8_t *q_h = reinterpret_cast<int8_t *>(ws.h);
     float *d_h = reinterpret_cast<float *>(q_h + ((pairs * c.inter + 255) & ~(size_t)255));
@@ -431,6 +437,7 @@ int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rou
     a.T = T;
     a.n_shared = c.n_shared;
     a.wbits = c.wbits;
+    a.wfmt = c.wfmt;
     a.scale = c.routed_scaling;
     a.top_p = c.top_p;
     a.eps = eps;

@@ -53,7 +53,8 @@ def h(t):
 # ------------------------------------------------------------------ generator
 
 def test_gpu_generator_matches_host(dev):
-    for shape in (synth.TINY, synth.REAL, synth.REAL.with_bits(2), synth.REAL.with_bits(8)):
+    for shape in (synth.TINY, synth.REAL, synth.REAL.with_bits(2), synth.REAL.with_bits(8),
+                  synth.REAL.with_bits(synth.MXFP4), synth.TINY.with_bits(synth.MXFP4)):
         bb = synth.blob_bytes(shape)
         ids = [0, 3, synth.SHARED_ID]
         out = torch.empty(len(ids) * bb, dtype=torch.uint8, device=dev)
@@ -269,6 +270,29 @@ def real8(dev):
     return DeviceLayer(synth.REAL.with_bits(8), synth.SEEDS["decode"])
 
 
+# MXFP4 experts (FP4 E2M1 codes, E8M0 scale per 32): the dumped block dots
+# are sum 2 fp4(c) q, exact integers.
+
+@pytest.fixture(scope="module")
+def real_mx(dev):
+    return DeviceLayer(synth.REAL.with_bits(synth.MXFP4), synth.SEEDS["decode"])
+
+
+@pytest.mark.parametrize("T", [1, 4, 40])
+def test_ffn_tiny_mxfp4(dev, T):
+    lay = DeviceLayer(synth.TINY.with_bits(synth.MXFP4), synth.SEEDS["tiny"])
+    _ffn_check(lay, synth.tokens(synth.TINY, synth.SEEDS["tiny"], T, start=6), dev)
+
+
+def test_ffn_decode_mxfp4(dev, real_mx):
+    _ffn_check(real_mx, synth.tokens(synth.REAL, synth.SEEDS["decode"], 1, start=3), dev)
+
+
+def test_ffn_prefill_mxfp4(dev, real_mx):
+    _ffn_check(real_mx, synth.tokens(synth.REAL, synth.SEEDS["prefill"], 24), dev,
+               check_chain=False)
+
+
 @pytest.mark.parametrize("T", [1, 4, 40])
 def test_ffn_tiny_int8(dev, T):
     lay = DeviceLayer(synth.TINY.with_bits(8), synth.SEEDS["tiny"])
@@ -389,6 +413,19 @@ def test_combine_skips_dropped_rows(dev):
     out = h(moe.combine(to_d(eo, dev), to_d(w, dev), None, None))
     eo[:, 5:] = 0.0
     assert_close_rms(out, oracle.combine(eo, w), 1e-5, "y")
+
+
+def test_layer_tiny_mxfp4(dev):
+    lay = DeviceLayer(synth.TINY.with_bits(synth.MXFP4), synth.SEEDS["tiny"])
+    for T in (1, 4, 9, 33):
+        _layer_check(lay, synth.tokens(synth.TINY, 80, T), dev)
+
+
+@pytest.mark.parametrize("T,start", [(1, 0), (1, 1), (4, 0), (16, 0), (40, 0)])
+def test_layer_mxfp4(dev, real_mx, T, start):
+    x = synth.tokens(synth.REAL, synth.SEEDS["decode"], T, start=start) if T == 1 else \
+        synth.tokens_perturbed(synth.REAL, synth.SEEDS["verify"], T)
+    _layer_check(real_mx, x, dev)
 
 
 def test_layer_tiny_int8(dev):
