@@ -59,8 +59,8 @@ WORKLOADS = {
 def describe(name, shape, T, ring, layers=1, top_p=0.0, cache_slots=0):
     tp = (f", adaptive expert top-p {top_p:g} (shortest rank-order prefix holding that share of "
           f"the selected scores, weights renormalised)" if 0 < top_p < 1 else "")
-    wfmt = ("MXFP4 (FP4 E2M1 codes + E8M0 scale per 32)" if shape.wbits == -4
-            else f"int{shape.wbits} codes + fp32 row scales")
+    wfmt = ("MXFP4 (FP4 E2M1 codes + an E8M0 scale per 32)" if shape.wbits == -4
+            else f"int{shape.wbits} (codes + fp32 row scales)")
     if cache_slots:
         tp += (f"; routed experts in pinned host memory, {cache_slots} of {shape.n_experts} per "
                f"layer cached in HBM (LRU + hot store pinned from recorded usage), misses "
