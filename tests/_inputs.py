@@ -68,7 +68,8 @@ class DeviceLayer:
     def oracle_layer(self, x, residual=None, want_norm=False, top_p=0.0):
         import oracle
         s = self.shape
-        return oracle.layer(x, self.wr, self.bias, self.blob, self.blob(synth.SHARED_ID),
+        shared = self.blob(synth.SHARED_ID) if s.n_shared else None
+        return oracle.layer(x, self.wr, self.bias, self.blob, shared,
                             H=s.hidden, I=s.inter, n_experts=s.n_experts, n_group=s.n_group,
                             topk_group=s.topk_group, top_k=s.top_k, scale=s.routed_scaling,
                             wbits=s.wbits, residual=residual, want_norm=want_norm,
