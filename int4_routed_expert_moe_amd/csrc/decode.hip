@@ -48,6 +48,15 @@ namespace moe {
 #ifndef MOE_TT_INT4
 #define MOE_TT_INT4 2
 #endif
+// shared expert rows per wave for batches of several tokens (1 or 2; 2 at T = 1)
+#ifndef MOE_SHARED_RPW
+#define MOE_SHARED_RPW 1
+#endif
+constexpr int shared_rpw(int TT) { return TT == 1 ? 2 : MOE_SHARED_RPW; }
+// tokens per chunk of the shared expert's gate/up for batches of several tokens
+#ifndef MOE_SHARED_TT
+#define MOE_SHARED_TT 2
+#endif
 // largest batch the four-kernel path takes (at most 16)
 #ifndef MOE_SMALL_T_MAX
 #define MOE_SMALL_T_MAX 16
@@ -618,12 +627,13 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
 
 // ============================================================ K1b: selection + shared gate/up
 
-// The shared expert's gate/up (it needs no routing), in workgroups of 8
-// rows so that its bytes spread over every CU: wave wv holds rows 8 blk +
-// 2 wv, +1 (a gate and an up row each) and runs every token through them;
+// The shared expert's gate/up (it needs no routing), in workgroups of 4 SRW
+// rows so that its bytes spread over every CU: wave wv holds rows
+// 4 SRW blk + SRW wv .. (a gate and an up row each) and runs every token
+// through them;
 // h goes out in fp32 (its Q8_0 blocks span four workgroups; the gate/up
 // kernel quantises them).
-template <int WB, int TT, int NPL>
+template <int WB, int TT, int NPL, int SRW>
 __device__ void shared_rows_block(const LayerArgs &a, int blk) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, I = a.I, T = a.T;
@@ -635,10 +645,10 @@ __device__ void shared_rows_block(const LayerArgs &a, int blk) {
   const float *scales = reinterpret_cast<const float *>(tail);
   const int nblk = H / 32;
   const uint8_t *gsc = tail, *usc = tail + (size_t)I * nblk;  // MXFP4
-  const int r0 = blk * 8 + wv * 2;
-  WP<WB> wb[2][2][NPL];
+  const int r0 = blk * 4 * SRW + wv * SRW;
+  WP<WB> wb[SRW][2][NPL];
 #pragma unroll
-  for (int rr = 0; rr < 2; rr++) {
+  for (int rr = 0; rr < SRW; rr++) {
 #pragma unroll
     for (int i = 0; i < NPL; i++) {
       const int p = lane + 64 * i;
@@ -649,8 +659,12 @@ __device__ void shared_rows_block(const LayerArgs &a, int blk) {
     }
   }
   const bool mx = WB == WB_MX;  // no row scales
-  const float sg0 = mx ? 1.0f : scales[r0], sg1 = mx ? 1.0f : scales[r0 + 1];
-  const float su0 = mx ? 1.0f : scales[I + r0], su1 = mx ? 1.0f : scales[I + r0 + 1];
+  float sg[SRW], su[SRW];
+#pragma unroll
+  for (int rr = 0; rr < SRW; rr++) {
+    sg[rr] = mx ? 1.0f : scales[r0 + rr];
+    su[rr] = mx ? 1.0f : scales[I + r0 + rr];
+  }
   for (int c0 = 0; c0 < T; c0 += TT) {
     Act<WB> act[NPL][TT];
 #pragma unroll
@@ -665,7 +679,7 @@ __device__ void shared_rows_block(const LayerArgs &a, int blk) {
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < 2; rr++) {
+    for (int rr = 0; rr < SRW; rr++) {
       float g[TT], u[TT];
 #pragma unroll
       for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
@@ -679,8 +693,8 @@ __device__ void shared_rows_block(const LayerArgs &a, int blk) {
       }
 #pragma unroll
       for (int t = 0; t < TT; t++) {
-        const float gv = (rr ? sg1 : sg0) * wave_sum(g[t]);
-        const float uv = (rr ? su1 : su0) * wave_sum(u[t]);
+        const float gv = sg[rr] * wave_sum(g[t]);
+        const float uv = su[rr] * wave_sum(u[t]);
         if (lane == 0 && c0 + t < T) a.hs[(size_t)(c0 + t) * I + r0 + rr] = silu(gv) * uv;
       }
     }
@@ -692,7 +706,10 @@ template <int WB, int TT, int NPL>
 __global__ void __launch_bounds__(256) k_select_small(LayerArgs a) {
   __shared__ SelLds sm;
   if ((int)blockIdx.x >= a.T) {
-    shared_rows_block<WB, TT, NPL>(a, blockIdx.x - a.T);
+    // tokens per chunk of the shared rows (their weights stay in registers,
+    // so only the chain of activation round trips grows with T)
+    constexpr int STT = TT == 1 ? 1 : (WB == 4 || WB == WB_MX) ? MOE_SHARED_TT : TT;
+    shared_rows_block<WB, STT, NPL, shared_rpw(TT)>(a, blockIdx.x - a.T);
     return;
   }
   select_token(a, sm, blockIdx.x);
@@ -1068,7 +1085,7 @@ bool small_batch_supported(const moe_cfg &c, int T) {
 
 template <int WB, int TT, int NPG, int NPD>
 static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
-  const int n_sh = a.n_shared ? a.I / 8 : 0;
+  const int n_sh = a.n_shared ? a.I / (4 * shared_rpw(TT)) : 0;
   launch_k(k_route_small, dim3(a.E), dim3(256), 0, st, stage_ev(ev, MOE_STAGE_ROUTER_SCORES), a);
   launch_k(k_select_small<WB, TT, NPG>, dim3(a.T + n_sh), dim3(256), 0, st,
            stage_ev(ev, MOE_STAGE_ROUTER_SELECT), a);
