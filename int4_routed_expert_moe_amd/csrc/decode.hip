@@ -28,6 +28,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <string.h>
+
 #include <algorithm>
 
 namespace moe {
@@ -56,6 +58,10 @@ constexpr int shared_rpw(int TT) { return TT == 1 ? 2 : MOE_SHARED_RPW; }
 // tokens per chunk of the shared expert's gate/up for batches of several tokens
 #ifndef MOE_SHARED_TT
 #define MOE_SHARED_TT 2
+#endif
+// smallest batch whose down projection runs on the matrix cores (17: never)
+#ifndef MOE_DOWN_MFMA_MIN_T
+#define MOE_DOWN_MFMA_MIN_T 12
 #endif
 // largest batch the four-kernel path takes (at most 16)
 #ifndef MOE_SMALL_T_MAX
@@ -1042,6 +1048,31 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   if (comb && (v % sbk::RT) == 0) a.ssq[(size_t)(v / sbk::RT) * gridDim.x + tile] = ss;
 }
 
+// y[t] = residual[t] + shared[t] + sum_k w[t,k] expert_k[t] in rank order
+// (w = 0: dropped by top-p, skipped) from the MFMA down's per-pair rows, one
+// thread per (t, j) over T x H/256 workgroups; with y_norm, the per-8-row
+// sums of squares for k_norm_small as the down kernel above writes them.
+__global__ void __launch_bounds__(256) k_combine_small(LayerArgs a) {
+  const int t = blockIdx.x, j = blockIdx.y * 256 + threadIdx.x;
+  const int H = a.H, K = a.K;
+  float acc = 0.0f, ss = 0.0f;
+  if (j < H) {
+    acc = a.residual ? a.residual[(size_t)t * H + j] : 0.0f;
+    if (a.n_shared) acc += a.eo_s[(size_t)t * H + j];
+    for (int k = 0; k < K; k++) {
+      const float wk = a.w[t * K + k];
+      if (wk != 0.0f) acc = fmaf(wk, a.eo_r[((size_t)t * K + k) * H + j], acc);
+    }
+    a.y[(size_t)t * H + j] = acc;
+    ss = acc * acc;
+  }
+  if (!a.y_norm) return;
+  ss += __shfl_xor(ss, 1, 8);
+  ss += __shfl_xor(ss, 2, 8);
+  ss += __shfl_xor(ss, 4, 8);
+  if (j < H && (j % sbk::RT) == 0) a.ssq[(size_t)t * (H / sbk::RT) + j / sbk::RT] = ss;
+}
+
 // ============================================================ K4: RMSNorm
 
 // y_norm[t] = y[t] / sqrt(sum(y[t]^2) / H + eps) for the next layer of a
@@ -1098,12 +1129,40 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
   constexpr int SB = TT == 1 ? (WB == 2 ? 2 * MOE_K3_SLOTS : MOE_K3_SLOTS) : 2;
   constexpr int TT3 = TT == 1 ? 1 : MOE_K3_TT;  // tokens per chunk in the down kernel
   const int quarter = (a.I / (128 / code_bits<WB>()) + 3) / 4;
-  if (quarter <= 8)
+  if (WB != 2 && a.T >= MOE_DOWN_MFMA_MIN_T && a.H % 64 == 0 && a.I % 64 == 0) {
+    // many tokens per expert: the down projection as MFMA tiles of 64 rows
+    // x the slot's tokens (activations staged once per 64 rows, not once
+    // per 8), then the rank-order combine
+    FfnArgs f;
+    f.H = a.H;
+    f.I = a.I;
+    f.E = a.E;
+    f.K = a.K;
+    f.T = a.T;
+    f.n_shared = a.n_shared;
+    f.wbits = a.wbits;
+    f.wfmt = a.wfmt;
+    f.blob_bytes = a.blob_bytes;
+    f.q = nullptr;
+    f.d = nullptr;
+    f.experts = a.experts;
+    f.expert_ptrs = a.expert_ptrs;
+    f.shared = a.shared;
+    f.offsets = f.perm = f.active = f.n_active = nullptr;
+    f.h = nullptr;
+    f.expert_out = a.eo_r;
+    f.shared_out = a.eo_s;
+    memset(&f.dbg, 0, sizeof(f.dbg));
+    launch_down_mfma_slots(f, a.slots, a.n_slots_ub, SLOT_W, SLOT_PTR, a.qh, a.dh, st, ev);
+    launch_k(k_combine_small, dim3(a.T, (a.H + 255) / 256), dim3(256), 0, st,
+             stage_ev(ev, MOE_STAGE_COMBINE), a);
+  } else if (quarter <= 8) {
     launch_k(k_down_small<WB, TT3, 1, SB, 8>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
              st, stage_ev(ev, MOE_STAGE_DOWN), a);
-  else
+  } else {
     launch_k(k_down_small<WB, TT3, NPD, SB, 16>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
              st, stage_ev(ev, MOE_STAGE_DOWN), a);
+  }
   if (a.y_norm)
     launch_k(k_norm_small, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, st,
              stage_ev(ev, MOE_STAGE_NORM), a, a.H / sbk::RT);

@@ -443,27 +443,74 @@ __global__ void __launch_bounds__(256, 3) k_gate_up_mfma(FfnArgs a, const int4 *
 // Workgroup (row tile, work item): output rows 64 x .. of the down matrix
 // for the work item's pairs, from Q8_0(h); routed rows go to expert_out of
 // the slot, shared rows to shared_out of the token.
+struct DownLds {
+  uint8_t bs[MF_LDS_B];
+  float ds[mf::NT * mf::CB];
+  int tokl[mf::NT], pairl[mf::NT];
+};
+
+template <bool DBG, int WB>
+__device__ void down_mfma_tile(const FfnArgs &a, const TileInfo &ti, const int8_t *q_h,
+                               const float *d_h, DownLds &L, uint8_t *as, float *wsl);
+
 template <bool DBG, int WB>
 __global__ void __launch_bounds__(256) k_down_mfma(FfnArgs a, const int4 *tiles,
                                                    const int32_t *n_tiles, const int8_t *q_h,
                                                    const float *d_h) {
-  __shared__ __align__(16) uint8_t bs[MF_LDS_B];
-  __shared__ float ds[mf::NT * mf::CB];
+  __shared__ __align__(16) DownLds L;
   __shared__ __align__(16) uint8_t as[mf::RT * mf::astr<WB>()];
   __shared__ __align__(16) float wsl[WB == WB_MX ? mf::CB * mf::RT : 4];
-  __shared__ int tokl[mf::NT], pairl[mf::NT];
   if ((int)blockIdx.y >= *n_tiles) return;
   const int4 t = tiles[blockIdx.y];
   const TileInfo ti = tile_info(a, t);
-  const int H = a.H, I = a.I, r0 = blockIdx.x * mf::RT;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x;
   if (tid < mf::NT) {
     int tok = 0, pair = 0;
     if (tid < ti.n) tile_tok(a, t, ti.shared, tid, tok, pair);
-    tokl[tid] = pair;  // activations of the down projection are indexed by pair
-    pairl[tid] = pair;
+    L.tokl[tid] = pair;  // activations of the down projection are indexed by pair
+    L.pairl[tid] = pair;
   }
   __syncthreads();
+  down_mfma_tile<DBG, WB>(a, ti, q_h, d_h, L, as, wsl);
+}
+
+// Down projection of the small-batch layer path for batches of several
+// tokens: workgroup (row tile, slot) straight from the batch union's slot
+// table (entry: expert, token count, pair ids, record address); empty slots
+// exit at once.
+template <int WB>
+__global__ void __launch_bounds__(256) k_down_mfma_slots(FfnArgs a, const int32_t *slots,
+                                                         int slot_w, int slot_ptr,
+                                                         const int8_t *q_h, const float *d_h) {
+  __shared__ __align__(16) DownLds L;
+  __shared__ __align__(16) uint8_t as[mf::RT * mf::astr<WB>()];
+  __shared__ __align__(16) float wsl[WB == WB_MX ? mf::CB * mf::RT : 4];
+  const int32_t *ent = slots + (size_t)blockIdx.y * slot_w;
+  const int n = ent[1];
+  if (n <= 0) return;
+  TileInfo ti;
+  ti.shared = ent[0] < 0;
+  ti.blob = *reinterpret_cast<const uint8_t *const *>(ent + slot_ptr);
+  ti.n = min(n, min(a.T, mf::NT));
+  const int tid = threadIdx.x;
+  const int P = a.T * (a.K + a.n_shared);
+  if (tid < mf::NT) {
+    const int pair = tid < ti.n ? min(max(ent[2 + tid], 0), P - 1) : 0;
+    L.tokl[tid] = pair;
+    L.pairl[tid] = pair;
+  }
+  __syncthreads();
+  down_mfma_tile<false, WB>(a, ti, q_h, d_h, L, as, wsl);
+}
+
+template <bool DBG, int WB>
+__device__ void down_mfma_tile(const FfnArgs &a, const TileInfo &ti, const int8_t *q_h,
+                               const float *d_h, DownLds &L, uint8_t *as, float *wsl) {
+  const int H = a.H, I = a.I, r0 = blockIdx.x * mf::RT;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint8_t *bs = L.bs;
+  float *ds = L.ds;
+  const int *tokl = L.tokl, *pairl = L.pairl;
   const size_t row_b = (size_t)I * code_bits<WB>() / 8;
   const size_t gate_b = (size_t)I * ((size_t)H * code_bits<WB>() / 8);  // one gate/up matrix
   const uint8_t *mats[1] = {ti.blob + 2 * gate_b};
@@ -510,6 +557,20 @@ static void launch_mfma_wb(const FfnArgs &a, int max_tiles, int4 *tiles, int32_t
   launch_k(k_down_mfma<DBG, WB>, g2, dim3(256), 0, st, stage_ev(ev, MOE_STAGE_DOWN), a,
            (const int4 *)tiles, (const int32_t *)n_tiles, (const int8_t *)q_h,
            (const float *)d_h);
+}
+
+void launch_down_mfma_slots(const FfnArgs &a, const int32_t *slots, int n_slots_ub, int slot_w,
+                            int slot_ptr, const int8_t *q_h, const float *d_h, hipStream_t st,
+                            const moe_events *ev) {
+  const dim3 g(a.H / mf::RT, n_slots_ub);
+  const Ev ed = stage_ev(ev, MOE_STAGE_DOWN);
+  if (a.wfmt == 1)
+    launch_k(k_down_mfma_slots<WB_MX>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr, q_h,
+             d_h);
+  else if (a.wbits == 8)
+    launch_k(k_down_mfma_slots<8>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr, q_h, d_h);
+  else
+    launch_k(k_down_mfma_slots<4>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr, q_h, d_h);
 }
 
 void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_h, float *d_h,

@@ -76,6 +76,11 @@ size_t mfma_tiles_max(int T, int K, int E, int n_shared);
 bool mfma_supported(const FfnArgs &a);
 void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_h, float *d_h,
                      hipStream_t st, const moe_events *ev = nullptr);
+// The down projection of the small-batch path from its slot table (int8,
+// int4, MXFP4), rows to expert_out / shared_out.
+void launch_down_mfma_slots(const FfnArgs &a, const int32_t *slots, int n_slots_ub, int slot_w,
+                            int slot_ptr, const int8_t *q_h, const float *d_h, hipStream_t st,
+                            const moe_events *ev);
 
 // Whole layer for 1..16 tokens in three kernels (decode.hip).
 struct LayerArgs {
@@ -98,6 +103,7 @@ struct LayerArgs {
   int8_t *qh;                    // [P][I] Q8_0 of h
   float *dh;                     // [P][I/32]
   float *ssq;                    // [T][H/8] partial sums of squares
+  float *eo_r, *eo_s;            // expert_out [T*K][H] / shared_out [T][H] (MFMA down)
   uint32_t *sync;                // zero-initialised counters
   int n_slots_ub;
 };

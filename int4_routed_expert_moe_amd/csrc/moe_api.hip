@@ -462,6 +462,8 @@ int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rou
     a.qh = ws.qh;
     a.dh = ws.dh;
     a.ssq = ws.ssq;
+    a.eo_r = ws.expert_out;
+    a.eo_s = c.n_shared ? ws.shared_out : nullptr;
     a.sync = ws.sync;
     moe::launch_small_batch(a, st, ev);
     return launched("moe_layer (small batch)");

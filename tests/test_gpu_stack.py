@@ -5,13 +5,15 @@ on the GPU, checked against the CPU oracle.
 - teacher-forced: each layer's own GPU input (RMSNorm'd x and residual h) is
   fed to the oracle layer; indices bit-exact, outputs within 2e-3 * RMS;
 - free-running: the oracle runs the whole chain from the same tokens.  Layer
-  inputs then differ by rounding, and the layer has two discontinuities: the
-  top-k selection and the Q8_0 rounding of its input.  A token may take a
-  different discrete path only where the oracle sits at one of them: a
-  selection margin (K-th vs (K+1)-th biased score, or TG-th vs (TG+1)-th
-  group score, fp64) below 1e-5, or a differing Q8_0 code whose unrounded
-  value x/d is within 1e-3 code units of a rounding boundary.  Such tokens are
-  dropped from later comparisons; every other token must match.
+  inputs then differ by the per-layer error (teacher-forced bound: 2e-3 *
+  RMS, which the chain can add up layer after layer), and the layer has two
+  discontinuities: the top-k selection and the Q8_0 rounding of its input.
+  A token may take a different discrete path only where the oracle sits at
+  one of them: a selection margin (K-th vs (K+1)-th biased score, or TG-th
+  vs (TG+1)-th group score, fp64) below 1e-5, or a differing Q8_0 code whose
+  unrounded value x/d is within (layers so far + 1) * 2e-3 * RMS(x) / d code
+  units of a rounding boundary.  Such tokens are dropped from later
+  comparisons; every other token must match.
 """
 import numpy as np
 import pytest
@@ -79,13 +81,17 @@ def free_running(layers, x, idxs, last, gpu_ins):
         q_o, d_o = oracle.q8_0(xn)
         q_g, _ = oracle.q8_0(gpu_ins[l][1])  # the GPU chain's layer input
         dist = q8_boundary_distance(xn, d_o)
+        # how far the chains' inputs may be apart here, in code units of each block
+        slack = (l + 1) * 2e-3 * np.sqrt(np.mean(np.asarray(xn, np.float64) ** 2, axis=1))
+        reach = slack[:, None] / np.repeat(np.where(d_o > 0, d_o, np.inf), 32, axis=-1)
         ref = lay.oracle_layer(xn, residual=hh, want_norm=True)
         for t in range(x.shape[0]):
             if t in flipped:
                 continue
             diff = q_o[t] != q_g[t]
             if diff.any():
-                assert dist[t][diff].max() < 1e-3, (l, t, "Q8_0 code away from a boundary")
+                assert np.all(dist[t][diff] <= reach[t][diff]), \
+                    (l, t, "Q8_0 code away from a boundary", dist[t][diff], reach[t][diff])
                 flipped.add(t)
                 continue
             if not np.array_equal(ref["idx"][t], idxs[l][t]):
