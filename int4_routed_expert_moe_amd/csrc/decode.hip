@@ -63,6 +63,10 @@ constexpr int shared_rpw(int TT) { return TT == 1 ? 2 : MOE_SHARED_RPW; }
 #ifndef MOE_DOWN_MFMA_MIN_T
 #define MOE_DOWN_MFMA_MIN_T 12
 #endif
+// tokens per chunk of the MXFP4 gate/up kernel for batches of several tokens
+#ifndef MOE_TT_MX
+#define MOE_TT_MX 2
+#endif
 // largest batch the four-kernel path takes (at most 16)
 #ifndef MOE_SMALL_T_MAX
 #define MOE_SMALL_T_MAX 16
@@ -485,6 +489,49 @@ __device__ __forceinline__ float piece_dot<2>(const WP<2> &p, const Act<2> &a) {
   return fmaf((float)x, a.da, (float)y * a.db);
 }
 
+// A weight piece made ready for several tokens: MXFP4 codes turned into
+// int8 lanes once (the lookup costs more than the dots); other formats as
+// loaded.
+template <int WB>
+struct WReady {
+  WP<WB> p;
+};
+template <>
+struct WReady<WB_MX> {
+  int l[8];  // even / odd lanes of words 0..3: 2 x the FP4 values
+  float s;
+};
+template <int WB>
+__device__ __forceinline__ WReady<WB> ready(const WP<WB> &p) {
+  return WReady<WB>{p};
+}
+template <>
+__device__ __forceinline__ WReady<WB_MX> ready<WB_MX>(const WP<WB_MX> &p) {
+  WReady<WB_MX> r;
+  const uint32_t w[4] = {p.w.x, p.w.y, p.w.z, p.w.w};
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    r.l[2 * j] = mx_lanes(w[j], 0);
+    r.l[2 * j + 1] = mx_lanes(w[j], 4);
+  }
+  r.s = p.s;
+  return r;
+}
+template <int WB>
+__device__ __forceinline__ float ready_dot(const WReady<WB> &w, const Act<WB> &a) {
+  return piece_dot<WB>(w.p, a);
+}
+template <>
+__device__ __forceinline__ float ready_dot<WB_MX>(const WReady<WB_MX> &w, const Act<WB_MX> &a) {
+  int acc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    acc = sdot4(w.l[2 * j], a.q.ev[j], acc);
+    acc = sdot4(w.l[2 * j + 1], a.q.od[j], acc);
+  }
+  return (float)acc * (a.d * w.s);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // 32 rows of h (rows 32 blk ..) for one expert and n_tok tokens.  KS = 1:
@@ -583,10 +630,12 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
         for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
 #pragma unroll
         for (int i = 0; i < NPL; i++) {
+          const WReady<WB> rg = ready<WB>(wb[bt & 1][rr][0][i]);
+          const WReady<WB> ru = ready<WB>(wb[bt & 1][rr][1][i]);
 #pragma unroll
           for (int t = 0; t < TT; t++) {
-            g[t] += piece_dot<WB>(wb[bt & 1][rr][0][i], act[i][t]);
-            u[t] += piece_dot<WB>(wb[bt & 1][rr][1][i], act[i][t]);
+            g[t] += ready_dot<WB>(rg, act[i][t]);
+            u[t] += ready_dot<WB>(ru, act[i][t]);
           }
         }
         const float sg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), rl));
@@ -691,10 +740,12 @@ __device__ void shared_rows_block(const LayerArgs &a, int blk) {
       for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
 #pragma unroll
       for (int i = 0; i < NPL; i++) {
+        const WReady<WB> rg = ready<WB>(wb[rr][0][i]);
+        const WReady<WB> ru = ready<WB>(wb[rr][1][i]);
 #pragma unroll
         for (int t = 0; t < TT; t++) {
-          g[t] += piece_dot<WB>(wb[rr][0][i], act[i][t]);
-          u[t] += piece_dot<WB>(wb[rr][1][i], act[i][t]);
+          g[t] += ready_dot<WB>(rg, act[i][t]);
+          u[t] += ready_dot<WB>(ru, act[i][t]);
         }
       }
 #pragma unroll
@@ -883,8 +934,9 @@ __device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, in
     for (int t = 0; t < TT; t++) acc[t] = 0.0f;
 #pragma unroll
     for (int i = 0; i < NPQ; i++) {
+      const WReady<WB> rw = ready<WB>(w[rr][i]);
 #pragma unroll
-      for (int t = 0; t < TT; t++) acc[t] += piece_dot<WB>(w[rr][i], act[i][t]);
+      for (int t = 0; t < TT; t++) acc[t] += ready_dot<WB>(rw, act[i][t]);
     }
 #pragma unroll
     for (int t = 0; t < TT; t++) {
@@ -1189,7 +1241,7 @@ void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev) {
   a.n_slots_ub = a.n_shared + (a.T * a.K < a.E ? a.T * a.K : a.E);
   if (a.wfmt == 1) {  // MXFP4: int4 layout of the codes, a scale per piece
     if (a.T == 1) launch3_np<WB_MX, 1>(a, st, ev);
-    else launch3_np<WB_MX, MOE_TT_INT4>(a, st, ev);
+    else launch3_np<WB_MX, MOE_TT_MX>(a, st, ev);
   } else if (a.wbits == 8) {  // a piece carries 16 codes: two tokens per chunk
     if (a.T == 1) launch3_np<8, 1>(a, st, ev);
     else launch3_np<8, 2>(a, st, ev);
