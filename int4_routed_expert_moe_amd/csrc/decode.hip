@@ -830,7 +830,7 @@ __device__ const uint8_t *union_slot(const LayerArgs &a, int j, int *ent) {
 // workgroups with blk == 0 also publish their slot's table entry (and the
 // shared expert's) for the down kernel.
 template <int WB, int TT, int NPL>
-__global__ void __launch_bounds__(256) k_gate_up_small(LayerArgs a) {
+__global__ void __launch_bounds__(256, WB == WB_MX && TT > 1 ? 2 : 1) k_gate_up_small(LayerArgs a) {
   __shared__ float hb[TT][32];
   __shared__ int ent[SLOT_W];
   const int j = blockIdx.y, blk = blockIdx.x;
