@@ -34,9 +34,22 @@
 
 namespace moe {
 
-// expert slots whose down rows a K3 wave loads together (rows in flight)
+// Down-kernel slot batches: a double-buffered batch (the next is requested
+// while one is reduced) holds MOE_K3_SLOTS expert slots (int2 at one token:
+// MOE_K3_SLOTS_INT2, its rows are half as long); formats whose registers do
+// not allow two batches (bit f of MOE_K3_PIPE clear: 1 int4, 2 int2, 4 int8,
+// 8 MXFP4) take MOE_K3_SLOTS_NOPIPE slots at a time.
 #ifndef MOE_K3_SLOTS
-#define MOE_K3_SLOTS 2
+#define MOE_K3_SLOTS 1
+#endif
+#ifndef MOE_K3_SLOTS_INT2
+#define MOE_K3_SLOTS_INT2 2
+#endif
+#ifndef MOE_K3_SLOTS_NOPIPE
+#define MOE_K3_SLOTS_NOPIPE 2
+#endif
+#ifndef MOE_K3_PIPE
+#define MOE_K3_PIPE 0xB
 #endif
 // tokens per chunk of the down kernel for batches of more than one token
 #ifndef MOE_K3_TT
@@ -382,77 +395,117 @@ __device__ __forceinline__ WP<WB> load_wp(const uint8_t *row, const uint8_t *scl
   return r;
 }
 
+// A weight piece as loaded, for kernels that keep several loads in flight:
+// read unconditionally from a valid address and masked where it is used, so
+// that no branch holds the load (a branch around a load makes the compiler
+// wait for every load issued before it).
 template <int WB>
-__device__ __forceinline__ void load_act(const int8_t *q, const float *d, int p, bool ok,
-                                         Act<WB> &o);
+struct WRaw {
+  uint4 w;
+};
 template <>
-__device__ __forceinline__ void load_act<8>(const int8_t *q, const float *d, int p, bool ok,
-                                            Act<8> &o) {
-  uint4 x = make_uint4(0, 0, 0, 0);
-  float dd = 0.0f;
-  if (ok) {
-    x = reinterpret_cast<const uint4 *>(q)[p];
-    dd = d[p >> 1];
-  }
-  o.q[0] = (int)x.x;
-  o.q[1] = (int)x.y;
-  o.q[2] = (int)x.z;
-  o.q[3] = (int)x.w;
-  o.d = dd;
+struct WRaw<WB_MX> {
+  uint4 w;
+  uint32_t sb;  // the block's E8M0 byte
+};
+template <int WB, bool SCALE = true>
+__device__ __forceinline__ WRaw<WB> load_wraw(const uint8_t *row, const uint8_t *scl, int p) {
+  WRaw<WB> r;
+  r.w = gload<uint4>(row, (size_t)p * 16);
+  if constexpr (WB == WB_MX) r.sb = SCALE ? gload<uint8_t>(scl, p) : 0u;
+  return r;
 }
-template <>
-__device__ __forceinline__ void load_act<4>(const int8_t *q, const float *d, int p, bool ok,
-                                            Act<4> &o) {
-  uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-  float dd = 0.0f;
-  if (ok) {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(q + 32 * p);
-    x0 = qp[0];
-    x1 = qp[1];
-    dd = d[p] * (1.0f / 16.0f);
-  }
-  o.q = split_block(x0, x1);
-  o.d = dd;
+// The piece, or zeros when !ok.
+template <int WB>
+__device__ __forceinline__ WP<WB> cook_wp(const WRaw<WB> &r, bool ok) {
+  WP<WB> o;
+  o.w = ok ? r.w : make_uint4(0, 0, 0, 0);
+  if constexpr (WB == WB_MX) o.s = ok ? e8m0_float(r.sb) : 0.0f;
+  return o;
 }
-template <>
-__device__ __forceinline__ void load_act<WB_MX>(const int8_t *q, const float *d, int p, bool ok,
-                                                Act<WB_MX> &o) {
-  uint4 x0 = make_uint4(0, 0, 0, 0), x1 = make_uint4(0, 0, 0, 0);
-  float dd = 0.0f;
-  if (ok) {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(q + 32 * p);
-    x0 = qp[0];
-    x1 = qp[1];
-    dd = d[p] * 0.5f;
-  }
-  o.q = split_block(x0, x1);
-  o.d = dd;
-}
-template <>
-__device__ __forceinline__ void load_act<2>(const int8_t *q, const float *d, int p, bool ok,
-                                            Act<2> &o) {
-  uint4 z[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
-                make_uint4(0, 0, 0, 0)};
-  float d0 = 0.0f, d1 = 0.0f;
-  if (ok) {
-    const uint4 *qp = reinterpret_cast<const uint4 *>(q + 64 * p);
+
+// An activation piece as loaded: its bytes and block scale(s), not yet
+// rearranged, so that a load can stay in flight until the piece is used.
+template <int WB>
+struct ActRaw {
+  uint4 x[WB == 8 ? 1 : WB == 2 ? 4 : 2];
+  float d0, d1;
+};
+
+// Piece p of a Q8_0 row (q, d); zeros when !ok.
+template <int WB>
+__device__ __forceinline__ ActRaw<WB> load_act_raw(const int8_t *q, const float *d, int p,
+                                                   bool ok) {
+  constexpr int NX = WB == 8 ? 1 : WB == 2 ? 4 : 2;
+  ActRaw<WB> r;
 #pragma unroll
-    for (int j = 0; j < 4; j++) z[j] = qp[j];
-    d0 = d[2 * p] * (1.0f / 64.0f);
-    d1 = d[2 * p + 1] * (1.0f / 64.0f);
+  for (int j = 0; j < NX; j++) r.x[j] = make_uint4(0, 0, 0, 0);
+  r.d0 = r.d1 = 0.0f;
+  if (ok) {
+    const uint4 *qp = reinterpret_cast<const uint4 *>(q + 16 * NX * p);
+#pragma unroll
+    for (int j = 0; j < NX; j++) r.x[j] = qp[j];
+    if constexpr (WB == 8) {
+      r.d0 = d[p >> 1];
+    } else if constexpr (WB == 2) {
+      r.d0 = d[2 * p];
+      r.d1 = d[2 * p + 1];
+    } else {
+      r.d0 = d[p];
+    }
   }
+  return r;
+}
+
+// The loaded piece in the layout the dot products take.
+template <int WB>
+__device__ __forceinline__ Act<WB> cook_act(const ActRaw<WB> &r);
+template <>
+__device__ __forceinline__ Act<8> cook_act<8>(const ActRaw<8> &r) {
+  Act<8> o;
+  o.q[0] = (int)r.x[0].x;
+  o.q[1] = (int)r.x[0].y;
+  o.q[2] = (int)r.x[0].z;
+  o.q[3] = (int)r.x[0].w;
+  o.d = r.d0;
+  return o;
+}
+template <>
+__device__ __forceinline__ Act<4> cook_act<4>(const ActRaw<4> &r) {
+  Act<4> o;
+  o.q = split_block(r.x[0], r.x[1]);
+  o.d = r.d0 * (1.0f / 16.0f);
+  return o;
+}
+template <>
+__device__ __forceinline__ Act<WB_MX> cook_act<WB_MX>(const ActRaw<WB_MX> &r) {
+  Act<WB_MX> o;
+  o.q = split_block(r.x[0], r.x[1]);
+  o.d = r.d0 * 0.5f;
+  return o;
+}
+template <>
+__device__ __forceinline__ Act<2> cook_act<2>(const ActRaw<2> &r) {
+  Act<2> o;
 #pragma unroll
   for (int j = 0; j < 4; j++) {
 #pragma unroll
     for (int fi = 0; fi < 4; fi++) {
       const uint32_t sel = (uint32_t)(fi | ((4 + fi) << 8)) | 0x0C0C0000u;
-      const uint32_t a01 = __builtin_amdgcn_perm(z[j].y, z[j].x, sel);
-      const uint32_t a23 = __builtin_amdgcn_perm(z[j].w, z[j].z, sel);
+      const uint32_t a01 = __builtin_amdgcn_perm(r.x[j].y, r.x[j].x, sel);
+      const uint32_t a23 = __builtin_amdgcn_perm(r.x[j].w, r.x[j].z, sel);
       o.f[fi][j] = (int)__builtin_amdgcn_perm(a23, a01, 0x05040100u);
     }
   }
-  o.da = d0;
-  o.db = d1;
+  o.da = r.d0 * (1.0f / 64.0f);
+  o.db = r.d1 * (1.0f / 64.0f);
+  return o;
+}
+
+template <int WB>
+__device__ __forceinline__ void load_act(const int8_t *q, const float *d, int p, bool ok,
+                                         Act<WB> &o) {
+  o = cook_act<WB>(load_act_raw<WB>(q, d, p, ok));
 }
 
 // sum_b d_b * P_b of one 16-byte weight piece against one token
@@ -562,43 +615,47 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
   const uint8_t *gate = blob;
   const uint8_t *up = blob + (size_t)I * row_b;
   const uint8_t *tail = blob + 3 * (size_t)I * row_b;  // row scales, or MXFP4 block scales
-  const float *scales = reinterpret_cast<const float *>(tail);
   const int nblk = H / 32;
   const uint8_t *gsc = tail, *usc = tail + (size_t)I * nblk;  // MXFP4
   const int rbase = blk * 32 + wr * RW;
   // row scales of the wave's rows: lane l < RW gate row l, RW <= l < 2 RW up row l - RW
   const float sc = lane >= 2 * RW ? 0.0f
                    : WB == WB_MX ? 1.0f
-                                 : scales[(lane < RW ? 0 : I) + rbase + lane % RW];
+                                 : gload<float>(tail, 4 * (size_t)((lane < RW ? 0 : I) + rbase +
+                                                                   lane % RW));
   constexpr int NB = RW / RB;
   for (int c0 = 0; c0 < n_tok; c0 += TT) {
-    // two buffers: batch bt+1 is in flight while batch bt is computed
-    WP<WB> wb[2][RB][2][NPL];  // [buffer][row of batch][gate, up][piece]
-    auto load_batch = [&](WP<WB> (&dst)[RB][2][NPL], int bt) {
+    // two buffers: batch bt+1 is in flight while batch bt is computed.  Every
+    // load is unconditional (lanes past the row read its first piece and are
+    // masked where the piece is used), so that the compiler can wait for one
+    // batch while the next stays in flight.
+    WRaw<WB> wb[2][RB][2][NPL];  // [buffer][row of batch][gate, up][piece]
+    auto load_batch = [&](WRaw<WB> (&dst)[RB][2][NPL], int bt) {
 #pragma unroll
       for (int rr = 0; rr < RB; rr++) {
         const int r = rbase + bt * RB + rr;
 #pragma unroll
         for (int i = 0; i < NPL; i++) {
           const int p = p0 + lane + 64 * i;
-          const bool ok = p < npieces;
-          dst[rr][0][i] = load_wp<WB, false>(gate + (size_t)r * row_b, nullptr, p, ok);
-          dst[rr][1][i] = load_wp<WB, false>(up + (size_t)r * row_b, nullptr, p, ok);
+          const int pc = p < npieces ? p : p0;
+          dst[rr][0][i] = load_wraw<WB, false>(gate + (size_t)r * row_b, nullptr, pc);
+          dst[rr][1][i] = load_wraw<WB, false>(up + (size_t)r * row_b, nullptr, pc);
         }
       }
     };
-    load_batch(wb[0], 0);
-    Act<WB> act[NPL][TT];
+    // the activations first (cache hits), then the first batch: the
+    // activations are rearranged while that batch is in flight
+    ActRaw<WB> araw[NPL][TT];
 #pragma unroll
     for (int t = 0; t < TT; t++) {
-      const bool live = c0 + t < n_tok;
+      const int tok = c0 + t < n_tok ? c0 + t : c0;
 #pragma unroll
       for (int i = 0; i < NPL; i++) {
         const int p = p0 + lane + 64 * i;
-        load_act<WB>(qrow(live ? c0 + t : c0), drow(live ? c0 + t : c0), p, live && p < npieces,
-                     act[i][t]);
+        araw[i][t] = load_act_raw<WB>(qrow(tok), drow(tok), p < npieces ? p : p0, true);
       }
     }
+    load_batch(wb[0], 0);
     if constexpr (WB == WB_MX) {
       if (c0 == 0) {  // rows blk*32 .. +31 of each matrix: 32 * nblk contiguous bytes
         const int n16 = 32 * nblk / 16;
@@ -610,19 +667,33 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
         __syncthreads();
       }
     }
+    // lanes past the row: zero activations (their weight pieces, read from
+    // the row's first piece, then add exact zeros)
+    Act<WB> act[NPL][TT];
+#pragma unroll
+    for (int i = 0; i < NPL; i++) {
+      const bool ok = p0 + lane + 64 * i < npieces;
+#pragma unroll
+      for (int t = 0; t < TT; t++) act[i][t] = cook_act<WB>(ok ? araw[i][t] : ActRaw<WB>{});
+    }
 #pragma unroll
     for (int bt = 0; bt < NB; bt++) {
       if (bt + 1 < NB) load_batch(wb[(bt + 1) & 1], bt + 1);
+      // the next batch's loads go out before this batch is reduced
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int rr = 0; rr < RB; rr++) {
         const int rl = bt * RB + rr;  // row within the wave's RW
-        if constexpr (WB == WB_MX) {
+        WP<WB> wg[NPL], wu[NPL];
 #pragma unroll
-          for (int i = 0; i < NPL; i++) {
-            const int p = lane + 64 * i;
-            const int o = (wr * RW + rl) * nblk + p;
-            wb[bt & 1][rr][0][i].s = p < npieces ? e8m0_float(msc[o]) : 0.0f;
-            wb[bt & 1][rr][1][i].s = p < npieces ? e8m0_float(msc[MSC + o]) : 0.0f;
+        for (int i = 0; i < NPL; i++) {
+          const bool ok = p0 + lane + 64 * i < npieces;
+          wg[i] = cook_wp<WB>(wb[bt & 1][rr][0][i], true);
+          wu[i] = cook_wp<WB>(wb[bt & 1][rr][1][i], true);
+          if constexpr (WB == WB_MX) {
+            const int o = (wr * RW + rl) * nblk + lane + 64 * i;
+            wg[i].s = ok ? e8m0_float(msc[o]) : 0.0f;
+            wu[i].s = ok ? e8m0_float(msc[MSC + o]) : 0.0f;
           }
         }
         float g[TT], u[TT];
@@ -630,8 +701,8 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
         for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
 #pragma unroll
         for (int i = 0; i < NPL; i++) {
-          const WReady<WB> rg = ready<WB>(wb[bt & 1][rr][0][i]);
-          const WReady<WB> ru = ready<WB>(wb[bt & 1][rr][1][i]);
+          const WReady<WB> rg = ready<WB>(wg[i]);
+          const WReady<WB> ru = ready<WB>(wu[i]);
 #pragma unroll
           for (int t = 0; t < TT; t++) {
             g[t] += ready_dot<WB>(rg, act[i][t]);
@@ -904,7 +975,8 @@ constexpr int TAB_W = 2 + sbk::TMAX;  // expert, count, pairs: what the down ker
 // for the pieces qb + pl + LPR i of a quarter of nq pieces.
 template <int WB, int TT, int NPQ, int LPR>
 __device__ __forceinline__ void down_act(const LayerArgs &a, const int *prs, int n_tok, int c0,
-                                         int P, int qb, int nq, int pl, Act<WB> (&act)[NPQ][TT],
+                                         int P, int qb, int nq, int pl,
+                                         ActRaw<WB> (&act)[NPQ][TT],
                                          int (&pair)[TT]) {
   const int I = a.I;
 #pragma unroll
@@ -914,8 +986,12 @@ __device__ __forceinline__ void down_act(const LayerArgs &a, const int *prs, int
 #pragma unroll
     for (int i = 0; i < NPQ; i++) {
       const int q = pl + LPR * i;
-      load_act<WB>(a.qh + (size_t)pp * I, a.dh + (size_t)pp * (I / 32), qb + q,
-                   pair[t] >= 0 && q < nq, act[i][t]);
+      // always a valid piece (piece 0 of the row, pair 0 for a missing
+      // pair), so that no branch holds the load: lanes past the quarter
+      // have zero weights, and missing pairs are never stored
+      const bool ok = pair[t] >= 0 && q < nq;
+      act[i][t] = load_act_raw<WB>(a.qh + (size_t)pp * I, a.dh + (size_t)pp * (I / 32),
+                                   ok ? qb + q : 0, true);
     }
   }
 }
@@ -923,10 +999,16 @@ __device__ __forceinline__ void down_act(const LayerArgs &a, const int *prs, int
 // The RPL = LPR/8 rows of lane row rl (rl, rl + 64/LPR) of one slot for TT
 // pairs: quarter partials into part[wv][pair][row].
 template <int WB, int TT, int NPQ, int LPR>
-__device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, int pl,
-                                          const WP<WB> (&w)[LPR / 8][NPQ],
+__device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, int pl, int nq,
+                                          const WRaw<WB> (&w)[LPR / 8][NPQ],
                                           const float (&sd)[LPR / 8],
-                                          const Act<WB> (&act)[NPQ][TT], const int (&pair)[TT]) {
+                                          const ActRaw<WB> (&raw)[NPQ][TT],
+                                          const int (&pair)[TT]) {
+  Act<WB> act[NPQ][TT];  // rearranged here, where the loads are first needed
+#pragma unroll
+  for (int i = 0; i < NPQ; i++)
+#pragma unroll
+    for (int t = 0; t < TT; t++) act[i][t] = cook_act<WB>(raw[i][t]);
 #pragma unroll
   for (int rr = 0; rr < LPR / 8; rr++) {
     float acc[TT];
@@ -934,7 +1016,7 @@ __device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, in
     for (int t = 0; t < TT; t++) acc[t] = 0.0f;
 #pragma unroll
     for (int i = 0; i < NPQ; i++) {
-      const WReady<WB> rw = ready<WB>(w[rr][i]);
+      const WReady<WB> rw = ready<WB>(cook_wp<WB>(w[rr][i], pl + LPR * i < nq));
 #pragma unroll
       for (int t = 0; t < TT; t++) acc[t] += ready_dot<WB>(rw, act[i][t]);
     }
@@ -957,7 +1039,7 @@ __device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, in
 // quarters land in LDS and are added in quarter order in the combine, which
 // runs in rank order:
 //   y[t] = residual[t] + shared[t] + sum_k w[t,k] * expert_k[t]
-template <int WB, int TT, int NPQ, int SB, int LPR>
+template <int WB, int TT, int NPQ, int SB, int LPR, bool PIPE>
 __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   constexpr int RPL = LPR / 8;  // rows per lane
   extern __shared__ __align__(16) uint8_t dyn[];
@@ -986,23 +1068,22 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
 #pragma unroll
   for (int t = 0; t < sbk::TMAX; t++) shp[t] = T * K + t;
   const int S0 = a.n_shared;
-  WP<WB> ws0[RPL][NPQ];
+  WRaw<WB> ws0[RPL][NPQ];
   float sd0[RPL];
-  Act<WB> act_s[NPQ][TT];
+  ActRaw<WB> act_s[NPQ][TT];
   int pair_s[TT];
   if (S0) {
     const uint8_t *down = a.shared + down_off;
-    const float *sdp = reinterpret_cast<const float *>(a.shared + tail_off) + 2 * I;
 #pragma unroll
     for (int rr = 0; rr < RPL; rr++) {
       const int row = j0 + rl + (64 / LPR) * rr;
 #pragma unroll
       for (int i = 0; i < NPQ; i++) {
         const int q = pl + LPR * i;
-        ws0[rr][i] = load_wp<WB>(down + (size_t)row * row_b,
-                                 a.shared + dsc_off + (size_t)row * nblk, qb + q, q < nq);
+        ws0[rr][i] = load_wraw<WB>(down + (size_t)row * row_b,
+                                   a.shared + dsc_off + (size_t)row * nblk, q < nq ? qb + q : qb);
       }
-      sd0[rr] = WB == WB_MX ? 1.0f : sdp[row];
+      sd0[rr] = WB == WB_MX ? 1.0f : gload<float>(a.shared, tail_off + 4 * ((size_t)2 * I + row));
     }
     down_act<WB, TT, NPQ, LPR>(a, shp, T, 0, P, qb, nq, pl, act_s, pair_s);
   }
@@ -1019,56 +1100,78 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   int n_slots = 0;
   while (n_slots < a.n_slots_ub && tab[n_slots * TAB_W + 1] > 0) n_slots++;
 
-  if (S0) {  // the shared slot, from the registers filled above
-    down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, ws0, sd0, act_s, pair_s);
-    for (int c0 = TT; c0 < T; c0 += TT) {
-      Act<WB> act[NPQ][TT];
-      int pair[TT];
-      down_act<WB, TT, NPQ, LPR>(a, shp, T, c0, P, qb, nq, pl, act, pair);
-      down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, ws0, sd0, act, pair);
-    }
-  }
-  for (int s0 = S0; s0 < n_slots; s0 += SB) {
-    WP<WB> wd[SB][RPL][NPQ];
+  // Routed slots SB at a time, double-buffered: the rows and first pairs of
+  // the next SB slots are in flight while these are reduced.  A slot past
+  // the last reads the shared expert's rows (any valid record; nothing of
+  // it is stored), so every load is unconditional.
+  struct Batch {
+    WRaw<WB> wd[SB][RPL][NPQ];
     float sd[SB][RPL];
+    ActRaw<WB> act0[SB][NPQ][TT];
+    int pair0[SB][TT];
+  };
+  const uint8_t *fallback = S0 ? a.shared : recs[0];
+  auto load_batch = [&](Batch &bt, int s0) {
 #pragma unroll
     for (int b = 0; b < SB; b++) {
-      const bool ok_s = s0 + b < n_slots;
-      const uint8_t *blob = ok_s ? recs[s0 + b] : a.shared;
+      const int sl = min(s0 + b, a.n_slots_ub - 1);
+      const uint8_t *blob = s0 + b < n_slots ? recs[sl] : fallback;
       const uint8_t *down = blob + down_off;
-      const float *sdp = reinterpret_cast<const float *>(blob + tail_off) + 2 * I;
 #pragma unroll
       for (int rr = 0; rr < RPL; rr++) {
         const int row = j0 + rl + (64 / LPR) * rr;
 #pragma unroll
         for (int i = 0; i < NPQ; i++) {
           const int q = pl + LPR * i;
-          wd[b][rr][i] = load_wp<WB>(down + (size_t)row * row_b,
-                                     blob + dsc_off + (size_t)row * nblk, qb + q, ok_s && q < nq);
+          bt.wd[b][rr][i] = load_wraw<WB>(down + (size_t)row * row_b,
+                                          blob + dsc_off + (size_t)row * nblk,
+                                          q < nq ? qb + q : qb);
         }
-        sd[b][rr] = !ok_s ? 0.0f : WB == WB_MX ? 1.0f : sdp[row];
+        bt.sd[b][rr] = WB == WB_MX ? 1.0f : gload<float>(blob, tail_off + 4 * ((size_t)2 * I + row));
       }
+      const int n_tok = s0 + b < n_slots ? min(tab[sl * TAB_W + 1], T) : 0;
+      down_act<WB, TT, NPQ, LPR>(a, tab + sl * TAB_W + 2, n_tok, 0, P, qb, nq, pl, bt.act0[b],
+                                 bt.pair0[b]);
     }
-    // the first TT pairs of every slot of the batch: one round trip for all
-    Act<WB> act0[SB][NPQ][TT];
-    int pair0[SB][TT];
+  };
+  auto run_batch = [&](const Batch &bt, int s0) {
 #pragma unroll
     for (int b = 0; b < SB; b++) {
-      const int n_tok = (s0 + b < n_slots) ? min(tab[(s0 + b) * TAB_W + 1], T) : 0;
-      down_act<WB, TT, NPQ, LPR>(a, tab + (s0 + b) * TAB_W + 2, n_tok, 0, P, qb, nq, pl,
-                                 act0[b], pair0[b]);
-    }
-#pragma unroll
-    for (int b = 0; b < SB; b++) {
-      const int n_tok = (s0 + b < n_slots) ? min(tab[(s0 + b) * TAB_W + 1], T) : 0;
-      down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, wd[b], sd[b], act0[b], pair0[b]);
+      const int sl = min(s0 + b, a.n_slots_ub - 1);
+      const int n_tok = s0 + b < n_slots ? min(tab[sl * TAB_W + 1], T) : 0;
+      down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, nq, bt.wd[b], bt.sd[b], bt.act0[b],
+                                  bt.pair0[b]);
       for (int c0 = TT; c0 < n_tok; c0 += TT) {
-        Act<WB> act[NPQ][TT];
+        ActRaw<WB> act[NPQ][TT];
         int pair[TT];
-        down_act<WB, TT, NPQ, LPR>(a, tab + (s0 + b) * TAB_W + 2, n_tok, c0, P, qb, nq, pl, act,
-                                   pair);
-        down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, wd[b], sd[b], act, pair);
+        down_act<WB, TT, NPQ, LPR>(a, tab + sl * TAB_W + 2, n_tok, c0, P, qb, nq, pl, act, pair);
+        down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, nq, bt.wd[b], bt.sd[b], act, pair);
       }
+    }
+  };
+  Batch ba, bb;
+  if constexpr (PIPE) load_batch(ba, S0);  // requested before the shared slot is reduced
+  if (S0) {  // the shared slot, from the registers filled above
+    down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, nq, ws0, sd0, act_s, pair_s);
+    for (int c0 = TT; c0 < T; c0 += TT) {
+      ActRaw<WB> act[NPQ][TT];
+      int pair[TT];
+      down_act<WB, TT, NPQ, LPR>(a, shp, T, c0, P, qb, nq, pl, act, pair);
+      down_rows<WB, TT, NPQ, LPR>(part, P, wv, rl, pl, nq, ws0, sd0, act, pair);
+    }
+  }
+  if constexpr (PIPE) {
+    for (int s0 = S0; s0 < n_slots; s0 += 2 * SB) {
+      load_batch(bb, s0 + SB);
+      run_batch(ba, s0);
+      if (s0 + SB >= n_slots) break;
+      load_batch(ba, s0 + 2 * SB);
+      run_batch(bb, s0 + SB);
+    }
+  } else {  // one batch at a time (fewer registers)
+    for (int s0 = S0; s0 < n_slots; s0 += SB) {
+      load_batch(ba, s0);
+      run_batch(ba, s0);
     }
   }
   __syncthreads();
@@ -1178,7 +1281,11 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
   const size_t lds3 = (size_t)4 * P * sbk::RT * sizeof(float) +
                       (((size_t)a.n_slots_ub * TAB_W * 4 + 7) & ~(size_t)7) +
                       (size_t)a.n_slots_ub * sizeof(void *);
-  constexpr int SB = TT == 1 ? (WB == 2 ? 2 * MOE_K3_SLOTS : MOE_K3_SLOTS) : 2;
+  constexpr int fbit = WB == 4 ? 1 : WB == 2 ? 2 : WB == 8 ? 4 : 8;
+  constexpr bool PIPE = (MOE_K3_PIPE & fbit) != 0;
+  constexpr int SB = !PIPE ? MOE_K3_SLOTS_NOPIPE
+                    : TT == 1 && WB == 2 ? MOE_K3_SLOTS_INT2
+                                         : MOE_K3_SLOTS;
   constexpr int TT3 = TT == 1 ? 1 : MOE_K3_TT;  // tokens per chunk in the down kernel
   const int quarter = (a.I / (128 / code_bits<WB>()) + 3) / 4;
   if (WB != 2 && a.T >= MOE_DOWN_MFMA_MIN_T && a.H % 64 == 0 && a.I % 64 == 0) {
@@ -1209,10 +1316,10 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
     launch_k(k_combine_small, dim3(a.T, (a.H + 255) / 256), dim3(256), 0, st,
              stage_ev(ev, MOE_STAGE_COMBINE), a);
   } else if (quarter <= 8) {
-    launch_k(k_down_small<WB, TT3, 1, SB, 8>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
+    launch_k(k_down_small<WB, TT3, 1, SB, 8, PIPE>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
              st, stage_ev(ev, MOE_STAGE_DOWN), a);
   } else {
-    launch_k(k_down_small<WB, TT3, NPD, SB, 16>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
+    launch_k(k_down_small<WB, TT3, NPD, SB, 16, PIPE>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
              st, stage_ev(ev, MOE_STAGE_DOWN), a);
   }
   if (a.y_norm)
