@@ -149,6 +149,21 @@ __global__ void __launch_bounds__(256) k_route_small(LayerArgs a) {
   __shared__ float part[sbk::TMAX][128];
   const int e = blockIdx.x, tid = threadIdx.x;
   const int H = a.H, E = a.E, T = a.T;
+  const int half = tid >> 7, l = tid & 127;
+  const int nch = H / 64;
+  const bool dot = half < T && l < nch;
+  const float bias_e = a.bias[e];
+  // this lane's 64 router weights and its first token's 64 inputs, requested
+  // before the Q8_0 work below so that both share one memory round trip
+  float4 wv[16], xv[16];
+  if (dot) {
+    const float4 *w4 = reinterpret_cast<const float4 *>(a.wr + (size_t)e * H + l * 64);
+    const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)half * H + l * 64);
+#pragma unroll
+    for (int k = 0; k < 16; k++) wv[k] = w4[k];
+#pragma unroll
+    for (int k = 0; k < 16; k++) xv[k] = x4[k];
+  }
   {  // Q8_0 of a slice of x, 8 lanes per block of 32
     const int nbx = T * (H / 32);
     const int per = (nbx + E - 1) / E;
@@ -166,20 +181,15 @@ __global__ void __launch_bounds__(256) k_route_small(LayerArgs a) {
       }
     }
   }
-  const int half = tid >> 7, l = tid & 127;
-  const int nch = H / 64;
-  if (half < T && l < nch) {
-    const float4 *w4 = reinterpret_cast<const float4 *>(a.wr + (size_t)e * H + l * 64);
-    float4 wv[16];
-#pragma unroll
-    for (int k = 0; k < 16; k++) wv[k] = w4[k];
+  if (dot) {
     for (int t = half; t < T; t += 2) {
-      const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * H + l * 64);
-      float4 xv[16];
+      if (t > half) {
+        const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * H + l * 64);
 #pragma unroll
-      for (int k = 0; k < 16; k++) xv[k] = x4[k];
-      // keep every load of W and x ahead of the chain (one memory latency,
-      // not sixteen): nothing is scheduled across this point
+        for (int k = 0; k < 16; k++) xv[k] = x4[k];
+      }
+      // keep every load of x ahead of the chain (one memory latency, not
+      // sixteen): nothing is scheduled across this point
       __builtin_amdgcn_sched_barrier(0);
       float acc = 0.0f;
 #pragma unroll
@@ -198,7 +208,7 @@ __global__ void __launch_bounds__(256) k_route_small(LayerArgs a) {
     for (int c = 1; c < nch; c++) tot = tot + part[tid][c];
     const float sv = 1.0f / (1.0f + exp_fixed_sb(-tot));
     a.s[(size_t)tid * E + e] = sv;
-    a.sb[(size_t)tid * E + e] = sv + a.bias[e];
+    a.sb[(size_t)tid * E + e] = sv + bias_e;
   }
 }
 
@@ -768,41 +778,53 @@ __device__ void shared_rows_block(const LayerArgs &a, int blk) {
   const uint8_t *gate = a.shared;
   const uint8_t *up = a.shared + (size_t)I * row_b;
   const uint8_t *tail = a.shared + 3 * (size_t)I * row_b;
-  const float *scales = reinterpret_cast<const float *>(tail);
   const int nblk = H / 32;
   const uint8_t *gsc = tail, *usc = tail + (size_t)I * nblk;  // MXFP4
   const int r0 = blk * 4 * SRW + wv * SRW;
-  WP<WB> wb[SRW][2][NPL];
+  // Everything unconditional (lanes past the row read its first piece and
+  // get zero activations), the first tokens' activations (cache hits) ahead
+  // of the weights: one round trip for all.
+  auto load_acts = [&](ActRaw<WB> (&dst)[NPL][TT], int c0) {
+#pragma unroll
+    for (int t = 0; t < TT; t++) {
+      const int tok = c0 + t < T ? c0 + t : c0;
+#pragma unroll
+      for (int i = 0; i < NPL; i++) {
+        const int p = lane + 64 * i;
+        dst[i][t] = load_act_raw<WB>(a.q + (size_t)tok * H, a.d + (size_t)tok * (H / 32),
+                                     p < npieces ? p : 0, true);
+      }
+    }
+  };
+  ActRaw<WB> araw[NPL][TT];
+  load_acts(araw, 0);
+  WRaw<WB> wb[SRW][2][NPL];
 #pragma unroll
   for (int rr = 0; rr < SRW; rr++) {
 #pragma unroll
     for (int i = 0; i < NPL; i++) {
       const int p = lane + 64 * i;
-      const bool ok = p < npieces;
+      const int pc = p < npieces ? p : 0;
       const size_t r = (size_t)(r0 + rr);
-      wb[rr][0][i] = load_wp<WB>(gate + r * row_b, gsc + r * nblk, p, ok);
-      wb[rr][1][i] = load_wp<WB>(up + r * row_b, usc + r * nblk, p, ok);
+      wb[rr][0][i] = load_wraw<WB>(gate + r * row_b, gsc + r * nblk, pc);
+      wb[rr][1][i] = load_wraw<WB>(up + r * row_b, usc + r * nblk, pc);
     }
   }
   const bool mx = WB == WB_MX;  // no row scales
   float sg[SRW], su[SRW];
 #pragma unroll
   for (int rr = 0; rr < SRW; rr++) {
-    sg[rr] = mx ? 1.0f : scales[r0 + rr];
-    su[rr] = mx ? 1.0f : scales[I + r0 + rr];
+    sg[rr] = mx ? 1.0f : gload<float>(tail, 4 * (size_t)(r0 + rr));
+    su[rr] = mx ? 1.0f : gload<float>(tail, 4 * ((size_t)I + r0 + rr));
   }
   for (int c0 = 0; c0 < T; c0 += TT) {
+    if (c0 > 0) load_acts(araw, c0);
     Act<WB> act[NPL][TT];
 #pragma unroll
-    for (int t = 0; t < TT; t++) {
-      const bool live = c0 + t < T;
-      const int tok = live ? c0 + t : c0;
+    for (int i = 0; i < NPL; i++) {
+      const bool ok = lane + 64 * i < npieces;
 #pragma unroll
-      for (int i = 0; i < NPL; i++) {
-        const int p = lane + 64 * i;
-        load_act<WB>(a.q + (size_t)tok * H, a.d + (size_t)tok * (H / 32), p, live && p < npieces,
-                     act[i][t]);
-      }
+      for (int t = 0; t < TT; t++) act[i][t] = cook_act<WB>(ok ? araw[i][t] : ActRaw<WB>{});
     }
 #pragma unroll
     for (int rr = 0; rr < SRW; rr++) {
@@ -811,8 +833,8 @@ __device__ void shared_rows_block(const LayerArgs &a, int blk) {
       for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
 #pragma unroll
       for (int i = 0; i < NPL; i++) {
-        const WReady<WB> rg = ready<WB>(wb[rr][0][i]);
-        const WReady<WB> ru = ready<WB>(wb[rr][1][i]);
+        const WReady<WB> rg = ready<WB>(cook_wp<WB>(wb[rr][0][i], true));
+        const WReady<WB> ru = ready<WB>(cook_wp<WB>(wb[rr][1][i], true));
 #pragma unroll
         for (int t = 0; t < TT; t++) {
           g[t] += ready_dot<WB>(rg, act[i][t]);

@@ -136,10 +136,15 @@ __device__ __forceinline__ long a_frag(const uint8_t *row, int b, int g) {
 
 // Stage one K chunk of activations: rows = tokens (64), CB blocks of 32
 // int8 and their scales (for int4 and MXFP4 weights: reordered per 8 like
-// the nibble split, and the scales / 16 or / 2).
+// the nibble split, and the scales / 16 or / 2).  The loads are
+// unconditional (a block past the row reads the row's last block, a token
+// past n the list's entry, which always names a valid row) and a position
+// outside the tile gets a zero scale when the chunk is stored: a load inside
+// a branch would make the compiler wait for it (and for every load before
+// it) on the spot, ahead of the MFMAs it is meant to overlap.
 struct ActChunk {
   uint4 v[4];  // 4 x 16 bytes per thread (64 tokens x 16 pieces)
-  float d[2];  // 64 tokens x 8 block scales
+  float d[2];  // 64 tokens x 8 block scales, as loaded
 };
 
 template <int WB>
@@ -150,25 +155,22 @@ __device__ __forceinline__ void load_act_chunk(const int8_t *q, const float *d, 
 #pragma unroll
   for (int u = 0; u < 4; u++) {
     const int i = tid + 256 * u, tok_i = i >> 4, piece = i & 15;  // 16-byte piece
-    const int blk = c * mf::CB + (piece >> 1);
-    const bool ok = tok_i < n && blk < nblk;
-    r.v[u] = ok ? *reinterpret_cast<const uint4 *>(q + (size_t)tokl[tok_i] * row_len +
-                                                    (size_t)blk * 32 + (piece & 1) * 16)
-                : make_uint4(0, 0, 0, 0);
+    const int blk = min(c * mf::CB + (piece >> 1), nblk - 1);
+    r.v[u] = gload<uint4>(reinterpret_cast<const uint8_t *>(q),
+                          (size_t)tokl[tok_i] * row_len + (size_t)blk * 32 + (piece & 1) * 16);
   }
 #pragma unroll
   for (int u = 0; u < 2; u++) {
     const int i = tid + 256 * u, tok_i = i >> 3, b = i & 7;
-    const int blk = c * mf::CB + b;
-    r.d[u] = (tok_i < n && blk < nblk)
-                 ? d[(size_t)tokl[tok_i] * (row_len / 32) + blk] *
-                       (WB == 8 ? 1.0f : WB == WB_MX ? 0.5f : 0.0625f)
-                 : 0.0f;
+    const int blk = min(c * mf::CB + b, nblk - 1);
+    r.d[u] = gload<float>(reinterpret_cast<const uint8_t *>(d),
+                          4 * ((size_t)tokl[tok_i] * (row_len / 32) + blk));
   }
 }
 
 template <int WB>
-__device__ __forceinline__ void store_act_chunk(const ActChunk &r, uint8_t *bs, float *ds) {
+__device__ __forceinline__ void store_act_chunk(const ActChunk &r, uint8_t *bs, float *ds, int n,
+                                                int c, int nblk) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int u = 0; u < 4; u++) {
@@ -183,8 +185,10 @@ __device__ __forceinline__ void store_act_chunk(const ActChunk &r, uint8_t *bs, 
   }
 #pragma unroll
   for (int u = 0; u < 2; u++) {
-    const int i = tid + 256 * u;
-    ds[(i >> 3) * mf::CB + (i & 7)] = r.d[u];
+    const int i = tid + 256 * u, tok_i = i >> 3, b = i & 7;
+    const bool ok = tok_i < n && c * mf::CB + b < nblk;
+    ds[tok_i * mf::CB + b] =
+        ok ? r.d[u] * (WB == 8 ? 1.0f : WB == WB_MX ? 0.5f : 0.0625f) : 0.0f;
   }
 }
 
@@ -209,14 +213,15 @@ __device__ __forceinline__ void load_w_chunk(const uint8_t *const *mat,
 #pragma unroll
     for (int u = 0; u < PER; u++) {
       const int i = tid + 256 * u, row = i / PPR, pc = i % PPR;
+      // a block past the row: the row's last 16 bytes (its activations have
+      // zero scales), so that the load is unconditional
       const int blk = c * mf::CB + pc * 16 / (4 * CW);
-      r.v[m * PER + u] = blk < nblk ? gload<uint4>(mat[m], (size_t)(r0 + row) * row_b +
-                                                              (size_t)c * mf::CB * 4 * CW + pc * 16)
-                                    : make_uint4(0, 0, 0, 0);
+      const size_t off = blk < nblk ? (size_t)c * mf::CB * 4 * CW + pc * 16 : row_b - 16;
+      r.v[m * PER + u] = gload<uint4>(mat[m], (size_t)(r0 + row) * row_b + off);
     }
     if constexpr (WB == WB_MX) {  // row tid / 4, blocks 2 (tid % 4), +1 of the chunk
-      const int row = tid >> 2, blk = c * mf::CB + 2 * (tid & 3);
-      r.sc[m] = blk < nblk ? gload<uint16_t>(scl[m], (size_t)(r0 + row) * nblk + blk) : 0u;
+      const int row = tid >> 2, blk = min(c * mf::CB + 2 * (tid & 3), nblk - 2);
+      r.sc[m] = gload<uint16_t>(scl[m], (size_t)(r0 + row) * nblk + blk);
     }
   }
 }
@@ -278,7 +283,7 @@ __device__ void mfma_kloop(const uint8_t *const *mat, const uint8_t *const *scl,
   load_w_chunk<NM, WB>(mat, scl, row_b, r0, 0, nblk, wc);
   for (int c = 0; c < nchunk; c++) {
     __syncthreads();  // the previous chunk is consumed
-    store_act_chunk<WB>(ac, bs, ds);
+    store_act_chunk<WB>(ac, bs, ds, n, c, nblk);
     store_w_chunk<NM, WB>(wc, as, wsl);
     __syncthreads();
     if (c + 1 < nchunk) {  // next chunk in flight during this one's MFMAs
@@ -390,18 +395,25 @@ __global__ void __launch_bounds__(256, 3) k_gate_up_mfma(FfnArgs a, const int4 *
   const uint8_t *scl[2] = {tail, tail + (size_t)I * (H / 32)};
   float acc[2][4][4];
   int32_t *dots[2] = {a.dbg.gate_dots, a.dbg.up_dots};
-  mfma_kloop_n<2, DBG, WB>(mats, scl, row_b, r0, a.q, a.d, H, tokl, pairl, ti.n, H / 32, bs, ds,
-                           as, wsl, acc, dots, I);
-  // epilogue: h into LDS as [token][64 rows] fp32 (reuses the activation tile)
-  const float *scales = reinterpret_cast<const float *>(tail);
-  __syncthreads();
-  float *hs = reinterpret_cast<float *>(bs);  // 64 x 64 floats = 16 KB <= sizeof(bs)
   const int m16 = lane & 15, g = lane >> 4;
+  // the row scales of this lane's 4 rows, requested with the first chunk
+  float sgv[4], suv[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int rl = wv * 16 + g * 4 + i;
-    const float sg = WB == WB_MX ? 1.0f : scales[r0 + rl];
-    const float su = WB == WB_MX ? 1.0f : scales[I + r0 + rl];
+    sgv[i] = WB == WB_MX ? 1.0f : gload<float>(tail, 4 * (size_t)(r0 + rl));
+    suv[i] = WB == WB_MX ? 1.0f : gload<float>(tail, 4 * ((size_t)I + r0 + rl));
+  }
+  mfma_kloop_n<2, DBG, WB>(mats, scl, row_b, r0, a.q, a.d, H, tokl, pairl, ti.n, H / 32, bs, ds,
+                           as, wsl, acc, dots, I);
+  // epilogue: h into LDS as [token][64 rows] fp32 (reuses the activation tile)
+  __syncthreads();
+  float *hs = reinterpret_cast<float *>(bs);  // 64 x 64 floats = 16 KB <= sizeof(bs)
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int rl = wv * 16 + g * 4 + i;
+    const float sg = sgv[i];
+    const float su = suv[i];
 #pragma unroll
     for (int s = 0; s < 4; s++) {
       const float gv = sg * acc[0][s][i], uv = su * acc[1][s][i];
@@ -519,11 +531,14 @@ __device__ void down_mfma_tile(const FfnArgs &a, const TileInfo &ti, const int8_
   int32_t *dots[1] = {a.dbg.down_dots};
   mfma_kloop_n<1, DBG, WB>(mats, scl, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs, ds,
                            as, wsl, acc, dots, H);
-  const float *sd = reinterpret_cast<const float *>(ti.blob + 3 * gate_b) + 2 * I;
   const int m16 = lane & 15, g = lane >> 4;
   const int row = r0 + wv * 16 + g * 4;  // 4 consecutive rows per lane
-  const float4 s4 = WB == WB_MX ? make_float4(1.0f, 1.0f, 1.0f, 1.0f)
-                                : *reinterpret_cast<const float4 *>(sd + row);
+  float4 s4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);  // their row scales
+  if constexpr (WB != WB_MX) {
+    const uint4 u = gload<uint4>(ti.blob, 3 * gate_b + 4 * ((size_t)2 * I + row));
+    s4 = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                     __uint_as_float(u.w));
+  }
 #pragma unroll
   for (int s = 0; s < 4; s++) {
     const int col = s * 16 + m16;
