@@ -57,17 +57,21 @@ namespace moe {
 #endif
 // gate/up rows (each a gate and an up row) a K2 wave loads together: 1, 2, 4, 8
 #ifndef MOE_K2_ROWS
-#define MOE_K2_ROWS 2
+#define MOE_K2_ROWS 1
 #endif
 // tokens per chunk of the int4 gate/up kernel for batches of more than one token
 #ifndef MOE_TT_INT4
 #define MOE_TT_INT4 2
 #endif
-// shared expert rows per wave for batches of several tokens (1 or 2; 2 at T = 1)
+// shared expert rows per wave at one token (RPW1) and for batches of
+// several tokens (RPW)
+#ifndef MOE_SHARED_RPW1
+#define MOE_SHARED_RPW1 1
+#endif
 #ifndef MOE_SHARED_RPW
 #define MOE_SHARED_RPW 1
 #endif
-constexpr int shared_rpw(int TT) { return TT == 1 ? 2 : MOE_SHARED_RPW; }
+constexpr int shared_rpw(int TT) { return TT == 1 ? MOE_SHARED_RPW1 : MOE_SHARED_RPW; }
 // tokens per chunk of the shared expert's gate/up for batches of several tokens
 #ifndef MOE_SHARED_TT
 #define MOE_SHARED_TT 2
@@ -1124,20 +1128,20 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
 
   // Routed slots SB at a time, double-buffered: the rows and first pairs of
   // the next SB slots are in flight while these are reduced.  A slot past
-  // the last reads the shared expert's rows (any valid record; nothing of
-  // it is stored), so every load is unconditional.
+  // the last (the prefetch after the final batch) reads the last slot's
+  // rows again, which the cache still holds, and nothing of it is stored:
+  // every load is unconditional.
   struct Batch {
     WRaw<WB> wd[SB][RPL][NPQ];
     float sd[SB][RPL];
     ActRaw<WB> act0[SB][NPQ][TT];
     int pair0[SB][TT];
   };
-  const uint8_t *fallback = S0 ? a.shared : recs[0];
   auto load_batch = [&](Batch &bt, int s0) {
 #pragma unroll
     for (int b = 0; b < SB; b++) {
-      const int sl = min(s0 + b, a.n_slots_ub - 1);
-      const uint8_t *blob = s0 + b < n_slots ? recs[sl] : fallback;
+      const int sl = min(s0 + b, n_slots - 1);  // n_slots >= 1: every token has a routed expert
+      const uint8_t *blob = recs[sl];
       const uint8_t *down = blob + down_off;
 #pragma unroll
       for (int rr = 0; rr < RPL; rr++) {
