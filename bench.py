@@ -239,7 +239,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--wbits", default="4", choices=("8", "4", "2", "mxfp4"),
                     help="expert weights: int8/int4/int2 codes with row scales, or MXFP4")
-    ap.add_argument("--ring", type=int, default=0, help="layer instances to cycle (0 = default)")
+    ap.add_argument("--ring", type=int, default=0,
+                    help="layer instances to cycle (0 = the workload's ring; 1 with --cache-slots)")
     ap.add_argument("--topp", type=float, default=0.0,
                     help="adaptive expert top-p in (0, 1); 0 = off (plain top-k)")
     ap.add_argument("--cache-slots", type=int, default=0,
@@ -270,7 +271,9 @@ def main():
     shape = synth.REAL.with_bits(synth.MXFP4 if args.wbits == "mxfp4" else int(args.wbits))
     T = wl["T"]
     NL = wl.get("layers", 1)
-    R = wl["ring"] if NL > 1 else (args.ring or wl["ring"])
+    # with the expert cache one layer instance by default: its steady state needs many calls
+    # per layer, and eight interleaved caches each see an eighth of them
+    R = wl["ring"] if NL > 1 else (args.ring or (1 if args.cache_slots else wl["ring"]))
     seed = synth.SEEDS[wl["seed"]]
     K, W = args.steps, args.warmup
     dev = torch.device("cuda:0")

@@ -315,15 +315,18 @@ int moe_layer_ptrs(const moe_cfg *cfg, int32_t T, const float *x, const float *w
  * adds it to the usage counts, and promotes up to max_promote missed
  * experts per call into LRU slots (an empty slot, else the least recently
  * hit).  A victim's table entry is pointed back at host memory on `stream`
- * first; the record copy then runs on the cache's own copy stream after an
- * event on `stream` (so no earlier kernel still reads the slot), and the new
+ * first; the record copy then runs on the device's copy stream (one per
+ * device, shared by every cache on it, created by the first cache and kept
+ * until the process ends) after an event on `stream` (so no earlier kernel
+ * still reads the slot), and the new
  * entry is written on `stream` once the copy has landed (at a later call, or
  * within this call when wait != 0).  `stream` never waits for a copy; with
  * wait == 0 the host waits only when 32 read-backs are outstanding.
  * Results of moe_layer_ptrs do not depend on the cache state (same bytes
- * either way).  Not thread-safe; not capturable in a HIP graph.  create
- * allocates host memory (the handle, a pinned read-back ring) and a stream;
- * destroy waits for the copy stream and frees them.
+ * either way).  A cache is not thread-safe (caches used from different
+ * threads are independent); not capturable in a HIP graph.  create
+ * allocates host memory (the handle, a pinned read-back ring); destroy waits
+ * for this cache's copies and frees them.
  * Errors: MOE_EINVAL, MOE_EALIGN (slots 256-byte, table 8-byte, every host
  * record 256-byte aligned), MOE_EHIP.
  * ------------------------------------------------------------------------- */

@@ -16,7 +16,7 @@
 //     counts hits and misses against the table as that call saw it, and
 //     promotes missed experts into LRU slots: the victim's entry is turned
 //     back to host memory on the caller's stream first, the record copy runs
-//     on the cache's own copy stream after that, and the new entry is
+//     on the device's copy stream after that, and the new entry is
 //     written on the caller's stream once the copy has completed.  So no
 //     kernel ever reads a slot that is being overwritten, and the caller's
 //     stream never waits for a copy.
@@ -30,6 +30,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -186,7 +188,7 @@ struct moe_cache {
   std::vector<const void *> host;  // [E] device-readable records in host memory
   uint8_t *slots = nullptr;        // [S][blob_bytes] in HBM
   const void **table = nullptr;    // [E] device table of record pointers
-  hipStream_t copy = nullptr;
+  hipStream_t copy = nullptr;  // the device's copy stream (shared, not owned)
   // idx read-back ring
   static constexpr int R = 32;
   int32_t *ring = nullptr;  // pinned [R][max_pairs]
@@ -276,16 +278,38 @@ int drain(moe_cache *c, bool force, bool wait, hipStream_t st) {
   return MOE_OK;
 }
 
+// One copy stream per device, shared by every cache on it and kept until the
+// process ends: promotions of all layers go out in order over the one host
+// link, and the process stays within a few hardware queues (with a stream
+// per cache, eight layers' caches shared the compute stream's queue, and
+// their copies waited behind every layer call already queued).
+hipError_t device_copy_stream(hipStream_t *out) {
+  static std::mutex mu;
+  static std::map<int, hipStream_t> streams;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = streams.find(dev);
+  if (it == streams.end()) {
+    hipStream_t s = nullptr;
+    if ((e = hipStreamCreate(&s)) != hipSuccess) return e;
+    it = streams.emplace(dev, s).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+
+// Every copy of this cache has landed (its slots may be freed after this).
 void release(moe_cache *c) {
-  if (c->copy) hipStreamSynchronize(c->copy);
   for (auto &cp : c->copies) {
+    hipEventSynchronize(cp.done);
     hipEventDestroy(cp.after_table);
     hipEventDestroy(cp.done);
   }
   for (int r = 0; r < moe_cache::R; r++)
     if (c->ring_ev[r]) hipEventDestroy(c->ring_ev[r]);
   if (c->ring) hipHostFree(c->ring);
-  if (c->copy) hipStreamDestroy(c->copy);
   delete c;
 }
 
@@ -329,9 +353,9 @@ int moe_cache_create(const moe_cfg *cfg, int32_t n_slots, int32_t n_pinned, int3
   c->slots = static_cast<uint8_t *>(slots);
   c->table = static_cast<const void **>(table);
   hipError_t e;
-  if ((e = hipStreamCreate(&c->copy)) != hipSuccess) {
+  if ((e = device_copy_stream(&c->copy)) != hipSuccess) {
     release(c);
-    return hip_fail("moe_cache_create (stream)", e);
+    return hip_fail("moe_cache_create (copy stream)", e);
   }
   if ((e = hipHostMalloc((void **)&c->ring, sizeof(int32_t) * moe_cache::R * max_pairs)) !=
       hipSuccess) {
