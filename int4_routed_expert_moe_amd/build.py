@@ -3,7 +3,10 @@
 Flags: correctly rounded fp32 division and square root and no fp contraction
 (the router's fixed-order arithmetic relies on both), and packed-fp32 code
 generation disabled (the compiler would otherwise pair scalar fp32 ops into
-v_pk_* instructions).
+v_pk_* instructions).  The grouped MFMA GEMMs take the VGPR form of the matrix
+instructions: each block dot's result is converted and scaled at once, and
+results left in accumulation registers cost a copy per element (four more
+VALU instructions per MFMA in the down projection).
 """
 from __future__ import annotations
 
@@ -26,9 +29,15 @@ HIP_FLAGS = [
 ]
 
 
+# extra flags per source file
+FILE_FLAGS = {
+    "ffn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = ["hipcc", *HIP_FLAGS, "-c", src, "-o", obj]
+    cmd = ["hipcc", *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
