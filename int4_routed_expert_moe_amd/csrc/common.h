@@ -143,6 +143,22 @@ __device__ __forceinline__ uint4 gload<uint4>(const uint8_t *base, size_t off) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// A 16-byte weight piece read once per step: a non-temporal load, which
+// streams past the caches instead of filling them (measured on a plain
+// streaming read: ~6.9 TB/s against ~6.2 TB/s with ordinary loads).
+#ifndef MOE_NT_WEIGHTS
+#define MOE_NT_WEIGHTS 1
+#endif
+__device__ __forceinline__ uint4 gload_stream(const uint8_t *base, size_t off) {
+  const MOE_GLOBAL uint8_t *g = (const MOE_GLOBAL uint8_t *)base;
+#if MOE_NT_WEIGHTS
+  const moe_u32x4 v = __builtin_nontemporal_load((const MOE_GLOBAL moe_u32x4 *)(g + off));
+#else
+  const moe_u32x4 v = *(const MOE_GLOBAL moe_u32x4 *)(g + off);
+#endif
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Weight-format tags of the kernels: 8, 4, 2 = integer codes of that many
 // bits with one fp32 scale per row; WB_MX = MXFP4 ("Comment exécuter un
 // réseau de neurones de 744 milliards de paramètres…", section "Modèles

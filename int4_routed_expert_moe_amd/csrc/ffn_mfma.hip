@@ -202,7 +202,10 @@ struct WChunk {
   uint32_t sc[NM];                                           // MXFP4: 2 scale bytes
 };
 
-template <int NM, int WB>
+// NT: non-temporal loads, for weights read once per launch (the slot-table
+// down kernel of the small-batch path); prefill tiles of one expert re-read
+// its rows, which ordinary loads keep in the caches.
+template <int NM, int WB, bool NT>
 __device__ __forceinline__ void load_w_chunk(const uint8_t *const *mat,
                                              const uint8_t *const *scl, size_t row_b, int r0,
                                              int c, int nblk, WChunk<NM, WB> &r) {
@@ -217,7 +220,8 @@ __device__ __forceinline__ void load_w_chunk(const uint8_t *const *mat,
       // zero scales), so that the load is unconditional
       const int blk = c * mf::CB + pc * 16 / (4 * CW);
       const size_t off = blk < nblk ? (size_t)c * mf::CB * 4 * CW + pc * 16 : row_b - 16;
-      r.v[m * PER + u] = gload<uint4>(mat[m], (size_t)(r0 + row) * row_b + off);
+      r.v[m * PER + u] = NT ? gload_stream(mat[m], (size_t)(r0 + row) * row_b + off)
+                            : gload<uint4>(mat[m], (size_t)(r0 + row) * row_b + off);
     }
     if constexpr (WB == WB_MX) {  // row tid / 4, blocks 2 (tid % 4), +1 of the chunk
       const int row = tid >> 2, blk = min(c * mf::CB + 2 * (tid & 3), nblk - 2);
@@ -262,7 +266,7 @@ __device__ __forceinline__ void store_w_chunk(const WChunk<NM, WB> &r, uint8_t *
 // token sub-tile s (16 tokens, s < NS: the sub-tiles that hold tokens, fixed
 // per workgroup so the loop body has no branches), row 16 wv + 4 g + i.  DBG: raw block dots of
 // matrix m go to dots[m] at ((pair * R + row) * nblk + block).
-template <int NM, bool DBG, int NS, int WB>
+template <int NM, bool DBG, int NS, int WB, bool NT>
 __device__ void mfma_kloop(const uint8_t *const *mat, const uint8_t *const *scl, size_t row_b,
                            int r0, const int8_t *q, const float *d, int row_len, const int *tokl,
                            const int *pairl, int n, int nblk, uint8_t *bs, float *ds, uint8_t *as,
@@ -280,7 +284,7 @@ __device__ void mfma_kloop(const uint8_t *const *mat, const uint8_t *const *scl,
   ActChunk ac;
   WChunk<NM, WB> wc;
   load_act_chunk<WB>(q, d, row_len, tokl, n, 0, nblk, ac);
-  load_w_chunk<NM, WB>(mat, scl, row_b, r0, 0, nblk, wc);
+  load_w_chunk<NM, WB, NT>(mat, scl, row_b, r0, 0, nblk, wc);
   for (int c = 0; c < nchunk; c++) {
     __syncthreads();  // the previous chunk is consumed
     store_act_chunk<WB>(ac, bs, ds, n, c, nblk);
@@ -288,7 +292,7 @@ __device__ void mfma_kloop(const uint8_t *const *mat, const uint8_t *const *scl,
     __syncthreads();
     if (c + 1 < nchunk) {  // next chunk in flight during this one's MFMAs
       load_act_chunk<WB>(q, d, row_len, tokl, n, c + 1, nblk, ac);
-      load_w_chunk<NM, WB>(mat, scl, row_b, r0, c + 1, nblk, wc);
+      load_w_chunk<NM, WB, NT>(mat, scl, row_b, r0, c + 1, nblk, wc);
     }
     const int nb = min(mf::CB, nblk - c * mf::CB);
     for (int b = 0; b < nb; b++) {
@@ -335,7 +339,7 @@ __device__ void mfma_kloop(const uint8_t *const *mat, const uint8_t *const *scl,
 }
 
 // mfma_kloop with the sub-tile count of n tokens chosen once.
-template <int NM, bool DBG, int WB>
+template <int NM, bool DBG, int WB, bool NT = false>
 __device__ void mfma_kloop_n(const uint8_t *const *mat, const uint8_t *const *scl, size_t row_b,
                              int r0, const int8_t *q, const float *d, int row_len,
                              const int *tokl, const int *pairl, int n, int nblk, uint8_t *bs,
@@ -343,19 +347,19 @@ __device__ void mfma_kloop_n(const uint8_t *const *mat, const uint8_t *const *sc
                              int32_t *const *dots, int R) {
   switch ((n + 15) / 16) {
     case 1:
-      mfma_kloop<NM, DBG, 1, WB>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+      mfma_kloop<NM, DBG, 1, WB, NT>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
                                  as, wsl, acc, dots, R);
       break;
     case 2:
-      mfma_kloop<NM, DBG, 2, WB>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+      mfma_kloop<NM, DBG, 2, WB, NT>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
                                  as, wsl, acc, dots, R);
       break;
     case 3:
-      mfma_kloop<NM, DBG, 3, WB>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+      mfma_kloop<NM, DBG, 3, WB, NT>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
                                  as, wsl, acc, dots, R);
       break;
     default:
-      mfma_kloop<NM, DBG, 4, WB>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
+      mfma_kloop<NM, DBG, 4, WB, NT>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
                                  as, wsl, acc, dots, R);
   }
 }
@@ -461,7 +465,7 @@ struct DownLds {
   int tokl[mf::NT], pairl[mf::NT];
 };
 
-template <bool DBG, int WB>
+template <bool DBG, int WB, bool NT = false>
 __device__ void down_mfma_tile(const FfnArgs &a, const TileInfo &ti, const int8_t *q_h,
                                const float *d_h, DownLds &L, uint8_t *as, float *wsl);
 
@@ -512,10 +516,10 @@ __global__ void __launch_bounds__(256) k_down_mfma_slots(FfnArgs a, const int32_
     L.pairl[tid] = pair;
   }
   __syncthreads();
-  down_mfma_tile<false, WB>(a, ti, q_h, d_h, L, as, wsl);
+  down_mfma_tile<false, WB, true>(a, ti, q_h, d_h, L, as, wsl);
 }
 
-template <bool DBG, int WB>
+template <bool DBG, int WB, bool NT>
 __device__ void down_mfma_tile(const FfnArgs &a, const TileInfo &ti, const int8_t *q_h,
                                const float *d_h, DownLds &L, uint8_t *as, float *wsl) {
   const int H = a.H, I = a.I, r0 = blockIdx.x * mf::RT;
@@ -529,8 +533,8 @@ __device__ void down_mfma_tile(const FfnArgs &a, const TileInfo &ti, const int8_
   const uint8_t *scl[1] = {ti.blob + 3 * gate_b + 2 * (size_t)I * (H / 32)};  // MXFP4
   float acc[1][4][4];
   int32_t *dots[1] = {a.dbg.down_dots};
-  mfma_kloop_n<1, DBG, WB>(mats, scl, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs, ds,
-                           as, wsl, acc, dots, H);
+  mfma_kloop_n<1, DBG, WB, NT>(mats, scl, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs,
+                               ds, as, wsl, acc, dots, H);
   const int m16 = lane & 15, g = lane >> 4;
   const int row = r0 + wv * 16 + g * 4;  // 4 consecutive rows per lane
   float4 s4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);  // their row scales
