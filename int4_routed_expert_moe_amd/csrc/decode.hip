@@ -1067,7 +1067,7 @@ __device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, in
 // quarters land in LDS and are added in quarter order in the combine, which
 // runs in rank order:
 //   y[t] = residual[t] + shared[t] + sum_k w[t,k] * expert_k[t]
-template <int WB, int TT, int NPQ, int SB, int LPR, bool PIPE>
+template <int WB, int TT, int NPQ, int SB, int LPR, bool PIPE, bool SH>
 __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   constexpr int RPL = LPR / 8;  // rows per lane
   extern __shared__ __align__(16) uint8_t dyn[];
@@ -1090,17 +1090,34 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   const int nblk = I / 32;
   const int rl = lane / LPR, pl = lane % LPR;
   const int j0 = tile * sbk::RT;
-  // The shared expert (slot 0 when present) needs nothing from the slot
-  // table: its rows and its first TT pairs are requested before the table.
-  int shp[sbk::TMAX];  // its pair ids T*K + t
+  // The slot table (its first 256 entries, one per thread), the combine
+  // weights and the residual are requested first, then the shared expert's
+  // rows and first TT pairs (they need nothing from the table): the table
+  // arrives after one plain round trip, and the routed rows are requested
+  // while the shared ones are still in flight.  Every load is unconditional
+  // (clamped indices; the residual falls back to x, same shape), so that
+  // storing the table waits for the table alone.
+  const int ntab = a.n_slots_ub * TAB_W;
+  const int tab_i = min(tid, ntab - 1);
+  const int tab_v = a.slots[(size_t)(tab_i / TAB_W) * SLOT_W + tab_i % TAB_W];
+  const int rec_i = min(tid, a.n_slots_ub - 1);
+  const uint8_t *rec_v =
+      *reinterpret_cast<const uint8_t *const *>(a.slots + (size_t)rec_i * SLOT_W + SLOT_PTR);
+  const float w_v = a.w[min(tid, T * K - 1)];
+  const int v = tid;  // combine: one thread per (token, row), T * RT <= 128
+  const bool comb = v < T * sbk::RT;
+  const int vc = min(v, T * sbk::RT - 1);
+  const float *res_p = a.residual ? a.residual : a.x;
+  const float res_v = res_p[(size_t)(vc / sbk::RT) * H + j0 + vc % sbk::RT];
+  int shp[sbk::TMAX];  // the shared expert's pair ids T*K + t
 #pragma unroll
   for (int t = 0; t < sbk::TMAX; t++) shp[t] = T * K + t;
-  const int S0 = a.n_shared;
+  constexpr int S0 = SH ? 1 : 0;
   WRaw<WB> ws0[RPL][NPQ];
   float sd0[RPL];
   ActRaw<WB> act_s[NPQ][TT];
   int pair_s[TT];
-  if (S0) {
+  if constexpr (SH) {
     const uint8_t *down = a.shared + down_off;
 #pragma unroll
     for (int rr = 0; rr < RPL; rr++) {
@@ -1115,15 +1132,16 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
     }
     down_act<WB, TT, NPQ, LPR>(a, shp, T, 0, P, qb, nq, pl, act_s, pair_s);
   }
-  for (int i = tid; i < a.n_slots_ub * TAB_W; i += 256)
+  // (threads past the end store their clamped entry again, the same value:
+  // a store behind a branch would draw its load into the branch)
+  tab[tab_i] = tab_v;
+  for (int i = tid + 256; i < ntab; i += 256)  // batches of many tokens
     tab[i] = a.slots[(size_t)(i / TAB_W) * SLOT_W + i % TAB_W];
-  for (int i = tid; i < a.n_slots_ub; i += 256)
+  recs[rec_i] = rec_v;
+  for (int i = tid + 256; i < a.n_slots_ub; i += 256)
     recs[i] = *reinterpret_cast<const uint8_t *const *>(a.slots + (size_t)i * SLOT_W + SLOT_PTR);
-  if (tid < T * K) wsh[tid] = a.w[tid];
-  const int v = tid;  // combine: one thread per (token, row), T * RT <= 128
-  const bool comb = v < T * sbk::RT;
-  const float resid =
-      (comb && a.residual) ? a.residual[(size_t)(v / sbk::RT) * H + j0 + v % sbk::RT] : 0.0f;
+  wsh[min(tid, T * K - 1)] = w_v;
+  const float resid = (comb && a.residual) ? res_v : 0.0f;
   __syncthreads();
   int n_slots = 0;
   while (n_slots < a.n_slots_ub && tab[n_slots * TAB_W + 1] > 0) n_slots++;
@@ -1343,12 +1361,14 @@ static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
     launch_down_mfma_slots(f, a.slots, a.n_slots_ub, SLOT_W, SLOT_PTR, a.qh, a.dh, st, ev);
     launch_k(k_combine_small, dim3(a.T, (a.H + 255) / 256), dim3(256), 0, st,
              stage_ev(ev, MOE_STAGE_COMBINE), a);
-  } else if (quarter <= 8) {
-    launch_k(k_down_small<WB, TT3, 1, SB, 8, PIPE>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
-             st, stage_ev(ev, MOE_STAGE_DOWN), a);
   } else {
-    launch_k(k_down_small<WB, TT3, NPD, SB, 16, PIPE>, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3,
-             st, stage_ev(ev, MOE_STAGE_DOWN), a);
+    // with or without a shared expert (its rows are requested unconditionally)
+    auto kd = quarter <= 8 ? (a.n_shared ? k_down_small<WB, TT3, 1, SB, 8, PIPE, true>
+                                         : k_down_small<WB, TT3, 1, SB, 8, PIPE, false>)
+                           : (a.n_shared ? k_down_small<WB, TT3, NPD, SB, 16, PIPE, true>
+                                         : k_down_small<WB, TT3, NPD, SB, 16, PIPE, false>);
+    launch_k(kd, dim3(a.H / sbk::RT), dim3(256), (uint32_t)lds3, st,
+             stage_ev(ev, MOE_STAGE_DOWN), a);
   }
   if (a.y_norm)
     launch_k(k_norm_small, dim3(a.T, (a.H + 1023) / 1024), dim3(256), 0, st,
