@@ -121,3 +121,40 @@ def test_cache_async_real_decode(dev):
     assert st["completed"] <= st["promotions"] and st["resident"] <= 32
     assert st["hits"] > 0 and st["misses"] > 0
     cache.close()
+
+
+def test_two_layers_share_the_copy_stream(dev):
+    """Two layers' caches used alternately (their promotions share the
+    device's copy stream): outputs bit-identical every step; with copies
+    completed within each call, each cache's counts and placement equal the
+    host policy on its own routing; with copies in flight across calls, the
+    counts stay consistent."""
+    shape = synth.TINY
+    lays = [DeviceLayer(shape, synth.SEEDS["tiny"], layer, bias="zipf") for layer in (0, 1)]
+    cfg = moe.Config.of(shape)
+    caches = [moe.ExpertCache(cfg, pinned_records(lay), n_slots=3, n_pinned=1, max_promote=1,
+                              max_pairs=8, usage=np.array([0, 1, 0, 0, 0, 0, 2, 0], np.uint64))
+              for lay in lays]
+    idxs = [[], []]
+    for step in range(24):
+        l = step % 2
+        idx = run_both(lays[l], synth.tokens(shape, 700 + step, 2), caches[l].table, dev).ravel()
+        idxs[l].append(idx)
+        caches[l].step(torch.from_numpy(idx).to(dev), wait=True)
+    for l in (0, 1):
+        st = caches[l].stats()
+        hits, misses, slot_of = moe.cache_simulate(8, 3, 1, 1, np.stack(idxs[l]),
+                                                   usage=np.array([0, 1, 0, 0, 0, 0, 2, 0],
+                                                                  np.uint64))
+        assert st["hits"] == hits.sum() and st["misses"] == misses.sum()
+        assert np.array_equal(caches[l].slot_of(), slot_of)
+    for step in range(24, 48):
+        l = step % 2
+        idx = run_both(lays[l], synth.tokens(shape, 700 + step, 2), caches[l].table, dev).ravel()
+        caches[l].step(torch.from_numpy(idx).to(dev))
+    torch.cuda.synchronize()
+    for c in caches:
+        st = c.stats()
+        assert st["hits"] + st["misses"] == st["routed"]
+        assert st["completed"] <= st["promotions"] and st["resident"] <= 3
+        c.close()
