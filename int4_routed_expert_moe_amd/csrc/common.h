@@ -184,13 +184,15 @@ __device__ __forceinline__ float e8m0_float(uint32_t s) {
 // each sign bit is the top bit of one of those bytes, one v_perm yields
 // 0xFF or 0x00 per lane.
 __device__ __forceinline__ int mx_lanes(uint32_t w, int shift) {
-  const uint32_t c = (w >> shift) & 0x0F0F0F0Fu;
-  const uint32_t sel = c & 0x07070707u;
+  const uint32_t sel = (w >> shift) & 0x07070707u;
   const uint32_t pos = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, sel);
   const uint32_t neg = __builtin_amdgcn_perm(0xF4F8FAFCu, 0xFDFEFF00u, sel);
-  // input bytes 1, 3 = (c << 12) bytes 1, 3 hold the signs of code bytes 0, 2;
-  // bytes 5, 7 = (c << 4) bytes 1, 3 hold those of code bytes 1, 3
-  const uint32_t m = __builtin_amdgcn_perm(c << 4, c << 12, 0x0B090A08u);
+  // the top bit of each byte of x is its code's sign bit (x = w << 4 for the
+  // low nibbles, w for the high ones; the other bits do not matter): input
+  // bytes 1, 3 = (x << 8) bytes 1, 3 hold the signs of code bytes 0, 2,
+  // bytes 5, 7 = x bytes 1, 3 those of code bytes 1, 3
+  const uint32_t x = w << (4 - shift);
+  const uint32_t m = __builtin_amdgcn_perm(x, x << 8, 0x0B090A08u);
   return (int)((neg & m) | (pos & ~m));
 }
 
