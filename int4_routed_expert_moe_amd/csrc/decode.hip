@@ -1,5 +1,5 @@
 // The routed-MoE layer step for small batches (decode and multi-token
-// verify, 1..16 tokens) in three kernels.
+// verify, 1..16 tokens) in four kernels (five with the RMSNorm of stacked layers).
 //
 // Same method and arithmetic as the separate calls ("Show HN: 遅いコンピュータ
 // で GLM 5.2 を実行する", section 実装済みの主な機能: sigmoid router with
@@ -18,13 +18,14 @@
 //                      slot's workgroups also quantise the shared expert's h.
 //  K3  k_down_small    (H/8 workgroups) 8 output rows for every expert slot
 //                      and token, combined in LDS in rank order into y
-//                      (+ residual); with y_norm, the last workgroup applies
-//                      the unit-gain RMSNorm to whole rows.
+//                      (+ residual), with per-tile sums of squares when the
+//                      RMSNorm is wanted; from 12 tokens on the down rows run
+//                      as MFMA tiles from the slot table instead, followed by
+//                      a combine kernel.
+//  K4  k_norm_small    (with y_norm) the unit-gain RMSNorm of whole rows.
 // Every kernel spreads its weight bytes over all CUs: one CU streams only a
 // few tens of GB/s, so a phase confined to a few CUs is slow however small.
-// Kernel boundaries carry every dependency except the RMSNorm's "last
-// workgroup" step, whose counter sits in a zero-initialised workspace region
-// that each call leaves at zero.
+// Kernel boundaries carry every dependency; no workgroup waits for another.
 #include "common.h"
 #include "kernels.h"
 
