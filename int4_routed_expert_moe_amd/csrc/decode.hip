@@ -144,6 +144,27 @@ __device__ __forceinline__ uint32_t q8_quad(float4 v, float *dd_out) {
   return cv(v.x) | (cv(v.y) << 8) | (cv(v.z) << 16) | (cv(v.w) << 24);
 }
 
+// Q8_0 of h as the down kernel reads it.  Lane jj (0..7) of a block's 8
+// quantises the values k0, k0 + ks, k0 + 2 ks, k0 + 3 ks of the block and
+// stores them as one word at byte `off` of the pair's row.  Natural order
+// (codes 4 jj .. 4 jj + 3) for every format but int2, whose down kernel dots
+// a 64-code piece field by field: there word 4 fi + j of a piece holds codes
+// 16 j + fi + 4 i (i = 0..3), the bytes the dots take, so no lane has to
+// rearrange them.  Codes and block scales are those of the natural order.
+template <int WB>
+__device__ __forceinline__ void h_word(int blk, int jj, int &k0, int &ks, int &off) {
+  if constexpr (WB == 2) {
+    const int fi = jj & 3, jp = jj >> 2;
+    k0 = 16 * jp + fi;
+    ks = 4;
+    off = (blk >> 1) * 64 + (4 * fi + 2 * (blk & 1) + jp) * 4;
+  } else {
+    k0 = 4 * jj;
+    ks = 1;
+    off = blk * 32 + 4 * jj;
+  }
+}
+
 // ============================================================ K1: router
 
 // Router workgroup e (one per expert): Q8_0 of a slice of x for the expert
@@ -519,6 +540,27 @@ __device__ __forceinline__ Act<2> cook_act<2>(const ActRaw<2> &r) {
   return o;
 }
 
+// A piece of Q8_0(h) as the down kernel loads it (laid out by h_word): int2
+// pieces are already in field order, the others as cook_act takes them.
+template <int WB>
+__device__ __forceinline__ Act<WB> cook_act_h(const ActRaw<WB> &r) {
+  if constexpr (WB == 2) {
+    Act<2> o;
+#pragma unroll
+    for (int fi = 0; fi < 4; fi++) {
+      o.f[fi][0] = (int)r.x[fi].x;
+      o.f[fi][1] = (int)r.x[fi].y;
+      o.f[fi][2] = (int)r.x[fi].z;
+      o.f[fi][3] = (int)r.x[fi].w;
+    }
+    o.da = r.d0 * (1.0f / 64.0f);
+    o.db = r.d1 * (1.0f / 64.0f);
+    return o;
+  } else {
+    return cook_act<WB>(r);
+  }
+}
+
 template <int WB>
 __device__ __forceinline__ void load_act(const int8_t *q, const float *d, int p, bool ok,
                                          Act<WB> &o) {
@@ -754,13 +796,15 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
     __syncthreads();
     if (threadIdx.x < TT * 8) {  // Q8_0 of each token's 32 h values
       const int t = threadIdx.x >> 3, j = threadIdx.x & 7;
-      const float4 v = make_float4(hb[t][4 * j], hb[t][4 * j + 1], hb[t][4 * j + 2],
-                                   hb[t][4 * j + 3]);
+      int k0, ks, off;
+      h_word<WB>(blk, j, k0, ks, off);
+      const float4 v = make_float4(hb[t][k0], hb[t][k0 + ks], hb[t][k0 + 2 * ks],
+                                   hb[t][k0 + 3 * ks]);
       float dd;
       const uint32_t packed = q8_quad(v, &dd);
       if (c0 + t < n_tok) {
         const int pair = min(max(pairs[c0 + t], 0), a.T * (a.K + a.n_shared) - 1);
-        reinterpret_cast<uint32_t *>(a.qh + (size_t)pair * I + blk * 32)[j] = packed;
+        *reinterpret_cast<uint32_t *>(a.qh + (size_t)pair * I + off) = packed;
         if (j == 0) a.dh[(size_t)pair * (I / 32) + blk] = dd;
       }
     }
@@ -937,11 +981,14 @@ __global__ void __launch_bounds__(256, WB == WB_MX && TT > 1 ? 2 : 1) k_gate_up_
   if (j == 0 && a.n_shared && (int)threadIdx.x < a.T * 8) {
     // Q8_0 of the shared expert's h, block blk of every token
     const int t = threadIdx.x >> 3, q = threadIdx.x & 7;
-    const float4 v = reinterpret_cast<const float4 *>(a.hs + (size_t)t * a.I + blk * 32)[q];
+    int k0, ks, off;
+    h_word<WB>(blk, q, k0, ks, off);
+    const float *hrow = a.hs + (size_t)t * a.I + blk * 32;
+    const float4 v = make_float4(hrow[k0], hrow[k0 + ks], hrow[k0 + 2 * ks], hrow[k0 + 3 * ks]);
     float dd;
     const uint32_t packed = q8_quad(v, &dd);
     const int pair = a.T * a.K + t;
-    reinterpret_cast<uint32_t *>(a.qh + (size_t)pair * a.I + blk * 32)[q] = packed;
+    *reinterpret_cast<uint32_t *>(a.qh + (size_t)pair * a.I + off) = packed;
     if (q == 0) a.dh[(size_t)pair * (a.I / 32) + blk] = dd;
   }
   const uint8_t *rec = union_slot(a, j, ent);
@@ -1037,7 +1084,7 @@ __device__ __forceinline__ void down_rows(float *part, int P, int wv, int rl, in
 #pragma unroll
   for (int i = 0; i < NPQ; i++)
 #pragma unroll
-    for (int t = 0; t < TT; t++) act[i][t] = cook_act<WB>(raw[i][t]);
+    for (int t = 0; t < TT; t++) act[i][t] = cook_act_h<WB>(raw[i][t]);
 #pragma unroll
   for (int rr = 0; rr < LPR / 8; rr++) {
     float acc[TT];
