@@ -7,7 +7,8 @@
 // packed int4/int2 weights with per-row scales, batch-union MoE).
 //
 //  K1  k_route_small   (E workgroups) Q8_0 of a slice of x; the fixed-order
-//                      fp32 logit and sigmoid score of one expert per token.
+//                      fp32 logit and sigmoid score of one expert for every
+//                      token (from 8 tokens: two experts, half the tokens).
 //  K1b k_select_small  (T + I/8 workgroups) group-limited top-k of one token
 //                      per workgroup; the rest run the shared expert's gate/up
 //                      (it needs no routing), 8 rows each, h in fp32.
@@ -51,6 +52,10 @@ namespace moe {
 #endif
 #ifndef MOE_K3_PIPE
 #define MOE_K3_PIPE 0xB
+#endif
+// smallest batch whose router workgroups take two experts each
+#ifndef MOE_ROUTE_EB2_T
+#define MOE_ROUTE_EB2_T 8
 #endif
 // tokens per chunk of the down kernel for batches of more than one token
 #ifndef MOE_K3_TT
@@ -171,31 +176,42 @@ __device__ __forceinline__ void h_word(int blk, int jj, int &k0, int &ks, int &o
 // kernels, then the fixed-order fp32 logit and the sigmoid score of expert e
 // for every token.  Thread l < H/64 of half h owns chunk l (an fma chain
 // over its 64 elements in index order) of the tokens t = h, h+2, ...
+// Workgroup (x, g): experts EB x .. EB x + EB - 1 for the tokens g, g + G,
+// ... (G = gridDim.y).  One CU streams only a few tens of GB/s, so with
+// several tokens a workgroup's time follows the bytes it reads: all its
+// tokens' inputs and its experts' weights.  EB = 2 and G = 2 halve the input
+// bytes for twice the weight bytes, with the same number of workgroups.
+template <int EB>
 __global__ void __launch_bounds__(256) k_route_small(LayerArgs a) {
-  __shared__ float part[sbk::TMAX][128];
-  const int e = blockIdx.x, tid = threadIdx.x;
+  __shared__ float part[EB][sbk::TMAX][128];
+  const int e0 = blockIdx.x * EB, g = blockIdx.y, G = gridDim.y, tid = threadIdx.x;
   const int H = a.H, E = a.E, T = a.T;
+  const int nt = (T - g + G - 1) / G;  // this workgroup's tokens: g + G j, j < nt
   const int half = tid >> 7, l = tid & 127;
   const int nch = H / 64;
-  const bool dot = half < T && l < nch;
-  const float bias_e = a.bias[e];
-  // this lane's 64 router weights and its first token's 64 inputs, requested
-  // before the Q8_0 work below so that both share one memory round trip
-  float4 wv[16], xv[16];
+  const bool dot = half < nt && l < nch;
+  // this lane's 64 router weights of each expert and its first token's 64
+  // inputs, requested before the Q8_0 work below so that all share one memory
+  // round trip
+  float4 wv[EB][16], xv[16];
   if (dot) {
     // ordinary loads: this one round trip is latency-bound, and non-temporal
     // loads made it slower (5.3 -> 7.7 us per decode step)
-    const float4 *w4 = reinterpret_cast<const float4 *>(a.wr + (size_t)e * H + l * 64);
-    const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)half * H + l * 64);
 #pragma unroll
-    for (int k = 0; k < 16; k++) wv[k] = w4[k];
+    for (int b = 0; b < EB; b++) {
+      const float4 *w4 = reinterpret_cast<const float4 *>(a.wr + (size_t)(e0 + b) * H + l * 64);
+#pragma unroll
+      for (int k = 0; k < 16; k++) wv[b][k] = w4[k];
+    }
+    const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)(g + G * half) * H + l * 64);
 #pragma unroll
     for (int k = 0; k < 16; k++) xv[k] = x4[k];
   }
   {  // Q8_0 of a slice of x, 8 lanes per block of 32
+    const int nwg = gridDim.x * G, wg = blockIdx.x * G + g;
     const int nbx = T * (H / 32);
-    const int per = (nbx + E - 1) / E;
-    const int b0 = e * per, b1 = min(nbx, b0 + per);
+    const int per = (nbx + nwg - 1) / nwg;
+    const int b0 = wg * per, b1 = min(nbx, b0 + per);
     for (int base = b0; base < b1; base += 32) {
       const int blk = base + (tid >> 3), sub = tid & 7;
       const bool ok = blk < b1;
@@ -210,33 +226,38 @@ __global__ void __launch_bounds__(256) k_route_small(LayerArgs a) {
     }
   }
   if (dot) {
-    for (int t = half; t < T; t += 2) {
-      if (t > half) {
-        const float4 *x4 = reinterpret_cast<const float4 *>(a.x + (size_t)t * H + l * 64);
+    for (int j = half; j < nt; j += 2) {
+      if (j > half) {
+        const float4 *x4 =
+            reinterpret_cast<const float4 *>(a.x + (size_t)(g + G * j) * H + l * 64);
 #pragma unroll
         for (int k = 0; k < 16; k++) xv[k] = x4[k];
       }
-      // keep every load of x ahead of the chain (one memory latency, not
+      // keep every load of x ahead of the chains (one memory latency, not
       // sixteen): nothing is scheduled across this point
       __builtin_amdgcn_sched_barrier(0);
-      float acc = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 16; k++) {
-        acc = __builtin_fmaf(xv[k].x, wv[k].x, acc);
-        acc = __builtin_fmaf(xv[k].y, wv[k].y, acc);
-        acc = __builtin_fmaf(xv[k].z, wv[k].z, acc);
-        acc = __builtin_fmaf(xv[k].w, wv[k].w, acc);
+      for (int b = 0; b < EB; b++) {
+        float acc = 0.0f;  // an fma chain in index order
+#pragma unroll
+        for (int k = 0; k < 16; k++) {
+          acc = __builtin_fmaf(xv[k].x, wv[b][k].x, acc);
+          acc = __builtin_fmaf(xv[k].y, wv[b][k].y, acc);
+          acc = __builtin_fmaf(xv[k].z, wv[b][k].z, acc);
+          acc = __builtin_fmaf(xv[k].w, wv[b][k].w, acc);
+        }
+        part[b][j][l] = acc;
       }
-      part[t][l] = acc;
     }
   }
   __syncthreads();
-  if (tid < T) {  // chunk partials added left to right
-    float tot = part[tid][0];
-    for (int c = 1; c < nch; c++) tot = tot + part[tid][c];
+  if (tid < EB * nt) {  // chunk partials added left to right
+    const int b = tid / nt, j = tid % nt, t = g + G * j, e = e0 + b;
+    float tot = part[b][j][0];
+    for (int c = 1; c < nch; c++) tot = tot + part[b][j][c];
     const float sv = 1.0f / (1.0f + exp_fixed_sb(-tot));
-    a.s[(size_t)tid * E + e] = sv;
-    a.sb[(size_t)tid * E + e] = sv + bias_e;
+    a.s[(size_t)t * E + e] = sv;
+    a.sb[(size_t)t * E + e] = sv + a.bias[e];
   }
 }
 
@@ -1366,7 +1387,12 @@ bool small_batch_supported(const moe_cfg &c, int T) {
 template <int WB, int TT, int NPG, int NPD>
 static void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
   const int n_sh = a.n_shared ? a.I / (4 * shared_rpw(TT)) : 0;
-  launch_k(k_route_small, dim3(a.E), dim3(256), 0, st, stage_ev(ev, MOE_STAGE_ROUTER_SCORES), a);
+  if (a.T >= MOE_ROUTE_EB2_T && a.E % 2 == 0)
+    launch_k(k_route_small<2>, dim3(a.E / 2, 2), dim3(256), 0, st,
+             stage_ev(ev, MOE_STAGE_ROUTER_SCORES), a);
+  else
+    launch_k(k_route_small<1>, dim3(a.E, 1), dim3(256), 0, st,
+             stage_ev(ev, MOE_STAGE_ROUTER_SCORES), a);
   launch_k(k_select_small<WB, TT, NPG>, dim3(a.T + n_sh), dim3(256), 0, st,
            stage_ev(ev, MOE_STAGE_ROUTER_SELECT), a);
   launch_k(k_gate_up_small<WB, TT, NPG>, dim3(a.I / 32, a.n_slots_ub - a.n_shared), dim3(256), 0,
