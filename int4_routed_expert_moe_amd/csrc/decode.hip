@@ -66,6 +66,11 @@ namespace moe {
 #define MOE_K2_ROWS 1
 #endif
 // tokens per chunk of the int4 gate/up kernel for batches of more than one token
+// slots with more tokens than one chunk: activations staged in LDS, rows
+// streamed once
+#ifndef MOE_GU_LDS
+#define MOE_GU_LDS 1
+#endif
 #ifndef MOE_TT_INT4
 #define MOE_TT_INT4 2
 #endif
@@ -674,17 +679,19 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // gate and an up row each), double-buffered.  Activations of token i: Q8_0
 // codes/scales at qrow(i)/drow(i).  h goes to LDS; each token's 32 values
 // become one Q8_0 block of q_h.
+// MXFP4: the block scales of the workgroup's 32 gate and 32 up rows, staged
+// once with 16-byte loads (one byte load per piece would double the load
+// instructions of the weight stream): msc[gate, up][32 rows][H/32 <= 256]
+constexpr int GU_MSC = 32 * 256;
+
 template <int WB, int TT, int NPL, int RB, int KS, class QRow, class DRow>
-__device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t *blob, int blk,
-                             int n_tok, const int *pairs, QRow qrow, DRow drow) {
+__device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], uint8_t *msc,
+                             const uint8_t *blob, int blk, int n_tok, const int *pairs, QRow qrow,
+                             DRow drow) {
   static_assert(KS == 1 || KS == 2, "K split");
   static_assert(WB != WB_MX || KS == 1, "MXFP4 rows fit one wave");
   __shared__ float part[KS][TT][32][2];  // KS = 2: scaled half sums (gate, up)
-  // MXFP4: the block scales of the workgroup's 32 gate and 32 up rows, staged
-  // once with 16-byte loads (one byte load per piece would double the load
-  // instructions of the weight stream): [gate, up][32 rows][H/32 <= 256]
-  constexpr int MSC = 32 * 256;
-  __shared__ __align__(16) uint8_t msc[WB == WB_MX ? 2 * MSC : 16];
+  constexpr int MSC = GU_MSC;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = a.H, I = a.I;
   constexpr int RW = 8 * KS;  // rows per wave
@@ -830,6 +837,181 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], const uint8_t 
       }
     }
     __syncthreads();
+  }
+}
+
+// A cooked activation piece as words: NQ 16-byte quads of codes, then NS
+// scales (the member order of every Act<WB>).
+template <int WB>
+struct ActWords {
+  static constexpr int N = sizeof(Act<WB>) / 4;
+  static constexpr int NQ = WB == 8 ? 1 : WB == 2 ? 4 : 2;
+  static constexpr int NS = N - 4 * NQ;
+};
+
+// Tokens staged at a time by gate_up_rows_lds: up to 8, in at most 48 KB
+constexpr int GU_ACT_LDS = 48 * 1024;
+template <int WB, int TT, int NPL>
+constexpr int gu_stage_tokens() {
+  const int fit = GU_ACT_LDS / (NPL * 64 * (int)sizeof(Act<WB>));
+  return (fit < 8 ? fit : 8) / TT * TT;
+}
+
+// gate_up_rows (KS = 1) for a slot with more tokens than one chunk: the
+// slot's activations, cooked, are staged in LDS up to SG tokens at a time
+// and every row is streamed once for all of them, its chunks of TT tokens
+// read from LDS (from registers, each chunk would stream the rows again).
+// Sums per token are those of gate_up_rows, in the same order.
+template <int WB, int TT, int NPL, class QRow, class DRow>
+__device__ void gate_up_rows_lds(const LayerArgs &a, uint8_t *msc, const uint8_t *blob, int blk,
+                                 int n_tok, const int *pairs, QRow qrow, DRow drow) {
+  using AW = ActWords<WB>;
+  constexpr int P = NPL * 64;  // pieces per staged token (zeros past the row)
+  constexpr int SG = gu_stage_tokens<WB, TT, NPL>();
+  static_assert(SG >= 2 * TT, "at least two chunks staged");
+  static_assert(sizeof(Act<WB>) == 4 * (4 * AW::NQ + AW::NS), "Act<WB> as words");
+  __shared__ __align__(16) uint4 aq[SG * AW::NQ * P];  // [token][quad][piece]
+  __shared__ float as[SG * AW::NS * P];                // [token][scale][piece]
+  __shared__ float hbs[SG][32];
+  constexpr int MSC = GU_MSC;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = a.H, I = a.I;
+  constexpr int RW = 8;  // rows per wave, one per batch
+  const int npieces = H / (128 / code_bits<WB>());
+  const size_t row_b = (size_t)H * code_bits<WB>() / 8;
+  const uint8_t *gate = blob;
+  const uint8_t *up = blob + (size_t)I * row_b;
+  const uint8_t *tail = blob + 3 * (size_t)I * row_b;
+  const int nblk = H / 32;
+  const uint8_t *gsc = tail, *usc = tail + (size_t)I * nblk;  // MXFP4
+  const int rbase = blk * 32 + wv * RW;
+  const float sc = lane >= 2 * RW ? 0.0f
+                   : WB == WB_MX ? 1.0f
+                                 : gload<float>(tail, 4 * (size_t)((lane < RW ? 0 : I) + rbase +
+                                                                   lane % RW));
+  auto load_row = [&](WRaw<WB> (&dst)[2][NPL], int rl) {
+    const int r = rbase + rl;
+#pragma unroll
+    for (int i = 0; i < NPL; i++) {
+      const int p = lane + 64 * i;
+      const int pc = p < npieces ? p : 0;
+      dst[0][i] = load_wraw<WB, false>(gate + (size_t)r * row_b, nullptr, pc);
+      dst[1][i] = load_wraw<WB, false>(up + (size_t)r * row_b, nullptr, pc);
+    }
+  };
+  if constexpr (WB == WB_MX) {  // block scales of the 32 gate and up rows
+    const int n16 = 32 * nblk / 16;
+    for (int i = tid; i < 2 * n16; i += 256) {
+      const int m = i / n16, o = (i % n16) * 16;
+      *reinterpret_cast<uint4 *>(msc + m * MSC + o) =
+          gload<uint4>(m ? usc : gsc, (size_t)blk * 32 * nblk + o);
+    }
+  }
+  for (int g0 = 0; g0 < n_tok; g0 += SG) {
+    const int ng = min(SG, n_tok - g0);
+    WRaw<WB> wb[2][2][NPL];  // [buffer][gate, up][piece]
+    load_row(wb[0], 0);
+    // the group's activations: every load unconditional (clamped items
+    // repeat the last one and store the same values again)
+    constexpr int MI = (SG * P + 255) / 256;
+    const int nit = ng * P;
+    ActRaw<WB> raw[MI];
+#pragma unroll
+    for (int k = 0; k < MI; k++) {
+      const int it = min(tid + 256 * k, nit - 1);
+      const int tok = it / P, p = it % P;
+      raw[k] = load_act_raw<WB>(qrow(g0 + tok), drow(g0 + tok), p < npieces ? p : 0, true);
+    }
+    __syncthreads();  // the previous group is done with the staging
+#pragma unroll
+    for (int k = 0; k < MI; k++) {
+      const int it = min(tid + 256 * k, nit - 1);
+      const int tok = it / P, p = it % P;
+      const Act<WB> c = cook_act<WB>(p < npieces ? raw[k] : ActRaw<WB>{});
+      uint32_t w[AW::N];
+      __builtin_memcpy(w, &c, sizeof(c));
+#pragma unroll
+      for (int q = 0; q < AW::NQ; q++)
+        aq[(tok * AW::NQ + q) * P + p] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+#pragma unroll
+      for (int j = 0; j < AW::NS; j++) as[(tok * AW::NS + j) * P + p] = __uint_as_float(w[4 * AW::NQ + j]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rl = 0; rl < RW; rl++) {
+      if (rl + 1 < RW) load_row(wb[(rl + 1) & 1], rl + 1);
+      // the next row's loads go out before this one is reduced
+      __builtin_amdgcn_sched_barrier(0);
+      WReady<WB> rg[NPL], ru[NPL];
+#pragma unroll
+      for (int i = 0; i < NPL; i++) {
+        WP<WB> wg = cook_wp<WB>(wb[rl & 1][0][i], true);
+        WP<WB> wu = cook_wp<WB>(wb[rl & 1][1][i], true);
+        if constexpr (WB == WB_MX) {
+          const bool ok = lane + 64 * i < npieces;
+          const int o = (wv * RW + rl) * nblk + lane + 64 * i;
+          wg.s = ok ? e8m0_float(msc[o]) : 0.0f;
+          wu.s = ok ? e8m0_float(msc[MSC + o]) : 0.0f;
+        }
+        rg[i] = ready<WB>(wg);
+        ru[i] = ready<WB>(wu);
+      }
+      const float sg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), rl));
+      const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), RW + rl));
+      for (int c0 = 0; c0 < ng; c0 += TT) {
+        Act<WB> act[NPL][TT];
+#pragma unroll
+        for (int t = 0; t < TT; t++) {
+          const int tok = c0 + t < ng ? c0 + t : c0;
+#pragma unroll
+          for (int i = 0; i < NPL; i++) {
+            const int p = lane + 64 * i;
+            uint32_t w[AW::N];
+#pragma unroll
+            for (int q = 0; q < AW::NQ; q++) {
+              const uint4 v = aq[(tok * AW::NQ + q) * P + p];
+              w[4 * q] = v.x;
+              w[4 * q + 1] = v.y;
+              w[4 * q + 2] = v.z;
+              w[4 * q + 3] = v.w;
+            }
+#pragma unroll
+            for (int j = 0; j < AW::NS; j++) w[4 * AW::NQ + j] = __float_as_uint(as[(tok * AW::NS + j) * P + p]);
+            __builtin_memcpy(&act[i][t], w, sizeof(w));
+          }
+        }
+        float g[TT], u[TT];
+#pragma unroll
+        for (int t = 0; t < TT; t++) g[t] = u[t] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NPL; i++) {
+#pragma unroll
+          for (int t = 0; t < TT; t++) {
+            g[t] += ready_dot<WB>(rg[i], act[i][t]);
+            u[t] += ready_dot<WB>(ru[i], act[i][t]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < TT; t++) {
+          const float gv = sg * wave_sum(g[t]);
+          const float uv = su * wave_sum(u[t]);
+          if (lane == 0 && c0 + t < ng) hbs[c0 + t][wv * 8 + rl] = silu(gv) * uv;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < ng * 8) {  // Q8_0 of each token's 32 h values
+      const int t = tid >> 3, j = tid & 7;
+      int k0, ks, off;
+      h_word<WB>(blk, j, k0, ks, off);
+      const float4 v = make_float4(hbs[t][k0], hbs[t][k0 + ks], hbs[t][k0 + 2 * ks],
+                                   hbs[t][k0 + 3 * ks]);
+      float dd;
+      const uint32_t packed = q8_quad(v, &dd);
+      const int pair = min(max(pairs[g0 + t], 0), a.T * (a.K + a.n_shared) - 1);
+      *reinterpret_cast<uint32_t *>(a.qh + (size_t)pair * I + off) = packed;
+      if (j == 0) a.dh[(size_t)pair * (I / 32) + blk] = dd;
+    }
   }
 }
 
@@ -998,6 +1180,7 @@ template <int WB, int TT, int NPL>
 __global__ void __launch_bounds__(256, WB == WB_MX && TT > 1 ? 2 : 1) k_gate_up_small(LayerArgs a) {
   __shared__ float hb[TT][32];
   __shared__ int ent[SLOT_W];
+  __shared__ __align__(16) uint8_t msc[WB == WB_MX ? 2 * GU_MSC : 16];
   const int j = blockIdx.y, blk = blockIdx.x;
   if (j == 0 && a.n_shared && (int)threadIdx.x < a.T * 8) {
     // Q8_0 of the shared expert's h, block blk of every token
@@ -1032,14 +1215,24 @@ __global__ void __launch_bounds__(256, WB == WB_MX && TT > 1 ? 2 : 1) k_gate_up_
   const int *pairs = ent + 2, *toks = ent + 2 + sbk::TMAX;
   // int8 rows longer than 4 pieces per lane are split over two waves
   constexpr int KS = WB == 8 && NPL > 4 ? 2 : 1;
+  auto qrow = [&](int i) {
+    return (const int8_t *)(a.q + (size_t)min(max(toks[i], 0), a.T - 1) * a.H);
+  };
+  auto drow = [&](int i) {
+    return (const float *)(a.d + (size_t)min(max(toks[i], 0), a.T - 1) * (a.H / 32));
+  };
+  if constexpr (TT > 1 && KS == 1 && MOE_GU_LDS) {
+    if constexpr (gu_stage_tokens<WB, TT, NPL>() >= 2 * TT) {
+      if (n_tok > TT) {  // several chunks: rows streamed once for all of them
+        gate_up_rows_lds<WB, TT, NPL>(a, msc, rec, blk, n_tok, pairs, qrow, drow);
+        return;
+      }
+    }
+  }
   gate_up_rows<WB, TT, KS == 2 ? 4 : NPL,
                (TT == 1 ? (WB == 2 ? 2 * MOE_K2_ROWS : WB == 8 || WB == WB_MX ? 1 : MOE_K2_ROWS) : 1),
                KS>(
-      a, hb, rec, blk, n_tok, pairs,
-      [&](int i) { return (const int8_t *)(a.q + (size_t)min(max(toks[i], 0), a.T - 1) * a.H); },
-      [&](int i) {
-        return (const float *)(a.d + (size_t)min(max(toks[i], 0), a.T - 1) * (a.H / 32));
-      });
+      a, hb, msc, rec, blk, n_tok, pairs, qrow, drow);
 }
 
 // ============================================================ K3: down + combine
