@@ -535,3 +535,35 @@ def test_layer_prefill_full_size_sampled(dev):
         ref = lay.oracle_layer(x[t:t + 1])
         assert np.array_equal(ref["idx"][0], idx[t])
         assert_close_rms(y[t], ref["y"][0], 2e-3, f"y token {t}")
+
+
+# Every token the same: every routed slot carries all T tokens, so the gate/up
+# kernel streams each row once for many chunks of tokens whose activations it
+# stages in LDS, over several staging rounds when the slot holds more tokens
+# than one round takes (int4 at this width: 6), the last round ragged.
+
+def _same_tokens(shape, T):
+    return np.repeat(synth.tokens(shape, 11, 1), T, axis=0)
+
+
+@pytest.mark.parametrize("T", [3, 7, 13, 16])
+def test_layer_identical_tokens(dev, real, T):
+    _layer_check(real, _same_tokens(synth.REAL, T), dev)
+
+
+@pytest.mark.parametrize("T", [5, 16])
+def test_layer_identical_tokens_mxfp4(dev, real_mx, T):
+    _layer_check(real_mx, _same_tokens(synth.REAL, T), dev)
+
+
+def test_layer_identical_tokens_int2(dev):
+    lay = DeviceLayer(synth.REAL.with_bits(2), synth.SEEDS["stack"])
+    for T in (5, 13):
+        _layer_check(lay, _same_tokens(synth.REAL, T), dev)
+
+
+def test_layer_identical_tokens_tiny(dev, tiny):
+    for bits in (4, 2, synth.MXFP4, 8):
+        lay = tiny if bits == 4 else DeviceLayer(synth.TINY.with_bits(bits), synth.SEEDS["tiny"])
+        for T in (3, 9, 16):
+            _layer_check(lay, _same_tokens(synth.TINY, T), dev)
