@@ -850,41 +850,49 @@ struct ActWords {
 };
 
 // Tokens staged at a time by gate_up_rows_lds: up to 8, in at most 48 KB
+// (a staged token holds KS NPL 64 pieces: the whole row)
 constexpr int GU_ACT_LDS = 48 * 1024;
-template <int WB, int TT, int NPL>
+template <int WB, int TT, int NPL, int KS>
 constexpr int gu_stage_tokens() {
-  const int fit = GU_ACT_LDS / (NPL * 64 * (int)sizeof(Act<WB>));
+  const int fit = GU_ACT_LDS / (KS * NPL * 64 * (int)sizeof(Act<WB>));
   return (fit < 8 ? fit : 8) / TT * TT;
 }
 
-// gate_up_rows (KS = 1) for a slot with more tokens than one chunk: the
-// slot's activations, cooked, are staged in LDS up to SG tokens at a time
-// and every row is streamed once for all of them, its chunks of TT tokens
-// read from LDS (from registers, each chunk would stream the rows again).
-// Sums per token are those of gate_up_rows, in the same order.
-template <int WB, int TT, int NPL, class QRow, class DRow>
+// gate_up_rows for a slot with more tokens than one chunk: the slot's
+// activations, cooked, are staged in LDS up to SG tokens at a time and every
+// row is streamed once for all of them, its chunks of TT tokens read from LDS
+// (from registers, each chunk would stream the rows again).  With KS = 2 a
+// wave takes its half of each staged row, and the pieces past its half get
+// zero weights.  Sums per token are those of gate_up_rows, in the same order.
+template <int WB, int TT, int NPL, int KS, class QRow, class DRow>
 __device__ void gate_up_rows_lds(const LayerArgs &a, uint8_t *msc, const uint8_t *blob, int blk,
                                  int n_tok, const int *pairs, QRow qrow, DRow drow) {
+  static_assert(KS == 1 || KS == 2, "K split");
+  static_assert(WB != WB_MX || KS == 1, "MXFP4 rows fit one wave");
   using AW = ActWords<WB>;
-  constexpr int P = NPL * 64;  // pieces per staged token (zeros past the row)
-  constexpr int SG = gu_stage_tokens<WB, TT, NPL>();
+  constexpr int P = KS * NPL * 64;  // pieces per staged token (zeros past the row)
+  constexpr int SG = gu_stage_tokens<WB, TT, NPL, KS>();
   static_assert(SG >= 2 * TT, "at least two chunks staged");
   static_assert(sizeof(Act<WB>) == 4 * (4 * AW::NQ + AW::NS), "Act<WB> as words");
   __shared__ __align__(16) uint4 aq[SG * AW::NQ * P];  // [token][quad][piece]
   __shared__ float as[SG * AW::NS * P];                // [token][scale][piece]
   __shared__ float hbs[SG][32];
+  __shared__ float part[KS == 2 ? 2 : 1][KS == 2 ? SG : 1][32][2];  // KS = 2: half sums
   constexpr int MSC = GU_MSC;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.H, I = a.I;
-  constexpr int RW = 8;  // rows per wave, one per batch
+  constexpr int RW = 8 * KS;  // rows per wave, one per batch
+  const int khalf = wv / (4 / KS), wr = wv % (4 / KS);
   const int npieces = H / (128 / code_bits<WB>());
+  const int np_half = (npieces + KS - 1) / KS;
+  const int p0 = khalf * np_half, pend = min(npieces, p0 + np_half);
   const size_t row_b = (size_t)H * code_bits<WB>() / 8;
   const uint8_t *gate = blob;
   const uint8_t *up = blob + (size_t)I * row_b;
   const uint8_t *tail = blob + 3 * (size_t)I * row_b;
   const int nblk = H / 32;
   const uint8_t *gsc = tail, *usc = tail + (size_t)I * nblk;  // MXFP4
-  const int rbase = blk * 32 + wv * RW;
+  const int rbase = blk * 32 + wr * RW;
   const float sc = lane >= 2 * RW ? 0.0f
                    : WB == WB_MX ? 1.0f
                                  : gload<float>(tail, 4 * (size_t)((lane < RW ? 0 : I) + rbase +
@@ -893,8 +901,8 @@ __device__ void gate_up_rows_lds(const LayerArgs &a, uint8_t *msc, const uint8_t
     const int r = rbase + rl;
 #pragma unroll
     for (int i = 0; i < NPL; i++) {
-      const int p = lane + 64 * i;
-      const int pc = p < npieces ? p : 0;
+      const int p = p0 + lane + 64 * i;
+      const int pc = p < pend ? p : p0;
       dst[0][i] = load_wraw<WB, false>(gate + (size_t)r * row_b, nullptr, pc);
       dst[1][i] = load_wraw<WB, false>(up + (size_t)r * row_b, nullptr, pc);
     }
@@ -945,11 +953,13 @@ __device__ void gate_up_rows_lds(const LayerArgs &a, uint8_t *msc, const uint8_t
       WReady<WB> rg[NPL], ru[NPL];
 #pragma unroll
       for (int i = 0; i < NPL; i++) {
-        WP<WB> wg = cook_wp<WB>(wb[rl & 1][0][i], true);
-        WP<WB> wu = cook_wp<WB>(wb[rl & 1][1][i], true);
+        // past the wave's pieces: the staged activations are zeros past the
+        // row; with KS = 2 the other half's, so the weights are zeroed there
+        const bool ok = p0 + lane + 64 * i < pend;
+        WP<WB> wg = cook_wp<WB>(wb[rl & 1][0][i], KS == 1 || ok);
+        WP<WB> wu = cook_wp<WB>(wb[rl & 1][1][i], KS == 1 || ok);
         if constexpr (WB == WB_MX) {
-          const bool ok = lane + 64 * i < npieces;
-          const int o = (wv * RW + rl) * nblk + lane + 64 * i;
+          const int o = (wr * RW + rl) * nblk + lane + 64 * i;
           wg.s = ok ? e8m0_float(msc[o]) : 0.0f;
           wu.s = ok ? e8m0_float(msc[MSC + o]) : 0.0f;
         }
@@ -965,7 +975,7 @@ __device__ void gate_up_rows_lds(const LayerArgs &a, uint8_t *msc, const uint8_t
           const int tok = c0 + t < ng ? c0 + t : c0;
 #pragma unroll
           for (int i = 0; i < NPL; i++) {
-            const int p = lane + 64 * i;
+            const int p = p0 + lane + 64 * i;  // < KS NPL 64 = P
             uint32_t w[AW::N];
 #pragma unroll
             for (int q = 0; q < AW::NQ; q++) {
@@ -995,8 +1005,23 @@ __device__ void gate_up_rows_lds(const LayerArgs &a, uint8_t *msc, const uint8_t
         for (int t = 0; t < TT; t++) {
           const float gv = sg * wave_sum(g[t]);
           const float uv = su * wave_sum(u[t]);
-          if (lane == 0 && c0 + t < ng) hbs[c0 + t][wv * 8 + rl] = silu(gv) * uv;
+          if (lane == 0 && c0 + t < ng) {
+            if constexpr (KS == 1) {
+              hbs[c0 + t][wv * 8 + rl] = silu(gv) * uv;
+            } else {
+              part[khalf][c0 + t][wr * RW + rl][0] = gv;
+              part[khalf][c0 + t][wr * RW + rl][1] = uv;
+            }
+          }
         }
+      }
+    }
+    if constexpr (KS == 2) {  // the halves added, as gate_up_rows does
+      __syncthreads();
+      if (tid < ng * 32) {
+        const int t = tid >> 5, r = tid & 31;
+        hbs[t][r] = silu(part[0][t][r][0] + part[1][t][r][0]) *
+                    (part[0][t][r][1] + part[1][t][r][1]);
       }
     }
     __syncthreads();
@@ -1221,10 +1246,11 @@ __global__ void __launch_bounds__(256, WB == WB_MX && TT > 1 ? 2 : 1) k_gate_up_
   auto drow = [&](int i) {
     return (const float *)(a.d + (size_t)min(max(toks[i], 0), a.T - 1) * (a.H / 32));
   };
-  if constexpr (TT > 1 && KS == 1 && MOE_GU_LDS) {
-    if constexpr (gu_stage_tokens<WB, TT, NPL>() >= 2 * TT) {
+  constexpr int NPLK = KS == 2 ? 4 : NPL;  // pieces per lane of a wave's share of a row
+  if constexpr (TT > 1 && MOE_GU_LDS) {
+    if constexpr (gu_stage_tokens<WB, TT, NPLK, KS>() >= 2 * TT) {
       if (n_tok > TT) {  // several chunks: rows streamed once for all of them
-        gate_up_rows_lds<WB, TT, NPL>(a, msc, rec, blk, n_tok, pairs, qrow, drow);
+        gate_up_rows_lds<WB, TT, NPLK, KS>(a, msc, rec, blk, n_tok, pairs, qrow, drow);
         return;
       }
     }
