@@ -15,8 +15,10 @@
 //  K2  k_gate_up_small (I/32 x routed slots) each workgroup finds its expert
 //                      slot of the batch union from the T*K selections, then
 //                      32 rows of h = silu(gate x) * (up x) for that expert and
-//                      its tokens, written directly as Q8_0 blocks; the first
-//                      slot's workgroups also quantise the shared expert's h.
+//                      its tokens, written directly as Q8_0 blocks (each row
+//                      streamed once: a slot with more tokens than one chunk
+//                      takes them from LDS); the first slot's workgroups also
+//                      quantise the shared expert's h.
 //  K3  k_down_small    (H/8 workgroups) 8 output rows for every expert slot
 //                      and token, combined in LDS in rank order into y
 //                      (+ residual), with per-tile sums of squares when the
