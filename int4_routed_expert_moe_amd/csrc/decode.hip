@@ -40,14 +40,14 @@ namespace moe {
 
 // Down-kernel slot batches: a double-buffered batch (the next is requested
 // while one is reduced) holds MOE_K3_SLOTS expert slots (int2 at one token:
-// MOE_K3_SLOTS_INT2, its rows are half as long); formats whose registers do
+// MOE_K3_SLOTS_INT2, measured apart for its half-length rows); formats whose registers do
 // not allow two batches (bit f of MOE_K3_PIPE clear: 1 int4, 2 int2, 4 int8,
 // 8 MXFP4) take MOE_K3_SLOTS_NOPIPE slots at a time.
 #ifndef MOE_K3_SLOTS
 #define MOE_K3_SLOTS 1
 #endif
 #ifndef MOE_K3_SLOTS_INT2
-#define MOE_K3_SLOTS_INT2 2
+#define MOE_K3_SLOTS_INT2 1
 #endif
 #ifndef MOE_K3_SLOTS_NOPIPE
 #define MOE_K3_SLOTS_NOPIPE 2
