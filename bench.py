@@ -258,8 +258,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the multi-GPU sharding is a design, see DESIGN.md)"}))
+        print(json.dumps({"error": "the layer step runs on one GPU; --gpus must be 1 "
+                                   "(sharding it across GPUs is designed, not built)"}))
         sys.exit(2)
 
     import torch

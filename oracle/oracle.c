@@ -29,7 +29,7 @@
  *        "Comment fonctionne le moteur": requests for the same expert are
  *        merged; an expert's three matrices are read together.
  *
- * Readings where the pages are silent (each one is listed in the design doc):
+ * Readings where the pages are silent, one per point:
  *  R1 noaux_tc: the per-expert correction bias enters expert *selection*
  *     only; routing weights use the unbiased sigmoid score.
  *  R2 group score = sum of the two largest biased scores in the group; the
