@@ -9,9 +9,10 @@
 //  K1  k_route_small   (E workgroups) Q8_0 of a slice of x; the fixed-order
 //                      fp32 logit and sigmoid score of one expert for every
 //                      token (from 8 tokens: two experts, half the tokens).
-//  K1b k_select_small  (T + I/8 workgroups) group-limited top-k of one token
+//  K1b k_select_small  (T + I/4 workgroups) group-limited top-k of one token
 //                      per workgroup; the rest run the shared expert's gate/up
-//                      (it needs no routing), 8 rows each, h in fp32.
+//                      (it needs no routing), 4 rows each (one per wave), h in
+//                      fp32.
 //  K2  k_gate_up_small (I/32 x routed slots) each workgroup finds its expert
 //                      slot of the batch union from the T*K selections, then
 //                      32 rows of h = silu(gate x) * (up x) for that expert and
