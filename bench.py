@@ -333,7 +333,7 @@ def main():
             rc = L.moe_layer_ptrs(ctypes.byref(c_cfg), T, x_ptr, r["wr"].data_ptr(),
                                   r["bias"].data_ptr(), r["cache"].table.data_ptr(),
                                   r["sh"].data_ptr(), res_ptr, y_ptr, yn_ptr, 1e-5, idx_ptr, None,
-                                  ws.data_ptr(), ws.numel(), events, stream.cuda_stream)
+                                  ws.data_ptr(), ws.numel(), events, None, stream.cuda_stream)
             if rc == 0:
                 rc = L.moe_cache_step(r["cache"]._h, idx_ptr, T * shape.top_k, 0,
                                       stream.cuda_stream)
@@ -341,7 +341,7 @@ def main():
             rc = L.moe_layer(ctypes.byref(c_cfg), T, x_ptr, r["wr"].data_ptr(),
                              r["bias"].data_ptr(), r["ex"].data_ptr(), r["sh"].data_ptr(),
                              res_ptr, y_ptr, yn_ptr, 1e-5, idx_ptr, None, ws.data_ptr(),
-                             ws.numel(), events, stream.cuda_stream)
+                             ws.numel(), events, None, stream.cuda_stream)
         if rc != 0:
             raise RuntimeError(f"moe_layer failed: {L.moe_last_error().decode()}")
 

@@ -16,7 +16,8 @@
  *   5. the weighted sum of the routed experts plus the shared expert.
  *
  * Conventions for every call:
- *   - cfg (and any moe_ffn_debug) is a host pointer; every other pointer is a
+ *   - cfg (and any moe_ffn_debug / moe_layer_debug struct) is a host
+ *     pointer; every other pointer is a
  *     DEVICE pointer to caller-owned memory, at least 16-byte aligned.
  *   - The library never allocates or frees device memory and never copies
  *     between host and device.  Scratch memory comes from a caller-provided
@@ -244,6 +245,28 @@ typedef struct moe_events {
   void *stop[MOE_N_STAGES];
 } moe_events;
 
+/* Optional device buffers moe_layer / moe_layer_ptrs fill with the step's
+ * intermediates, for tests that check the integer work bit for bit (pass
+ * NULL in production).  They are written by the kernels that compute the
+ * step, as they compute it (for 1..16 tokens a build of the same kernels
+ * with these stores added; the result y is bit-identical to a call without
+ * dumps).  Any member may be NULL, except that the six union arrays are
+ * given together or not at all.
+ *   q, d        int8 [T][H], fp32 [T][H/32]   Q8_0 of x ("Show HN…",
+ *               実装済みの主な機能, integer-dot item)
+ *   counts .. n_active   the batch union in moe_group's format ("Show
+ *               HN…", 実装済みの主な機能, batch-union item): the experts the
+ *               step reads, each once, and the (token, rank) slots of each
+ *   ffn         as for moe_expert_ffn: gate/up/down block dots, h, Q8_0 of h
+ *               (pair p < T*K = slot p, pair T*K + t = the shared expert on
+ *               token t). */
+typedef struct moe_layer_debug {
+  int8_t *q;
+  float *d;
+  int32_t *counts, *offsets, *perm, *inv, *active, *n_active;
+  moe_ffn_debug ffn;
+} moe_layer_debug;
+
 /* ---------------------------------------------------------------------------
  * moe_layer — the whole step: routing, Q8_0 of x, grouping, expert FFNs and
  * combine on one stream, with all intermediates in the workspace.  For 1..16
@@ -256,25 +279,21 @@ typedef struct moe_events {
  * moe_combine (MOE_STAGE_COMBINE, which includes the RMSNorm).  Both give the same
  * arithmetic as the separate calls (bit-identical idx and int32 block dots;
  * float outputs within rounding of the summation order).
- * Workspace precondition: the workspace must be zero-filled before its first
- * use by moe_layer (it begins with a reserved line that every call leaves at
- * zero); between moe_layer calls it must not be handed to other calls.  Calls
- * that overlap on the same workspace race.
+ * Workspace: any contents on entry (every byte a call reads was written
+ * earlier in the same call); calls that overlap on the same workspace race.
  * x [T][H] is the (already normalised) layer input; y [T][H] the output
  * (plus residual when given); y_norm optional as in moe_combine.  idx_out and
  * w_out ([T][K], nullable) receive the routing decision.  ev: optional
- * kernel timestamps (see moe_events), NULL in production.
+ * kernel timestamps (see moe_events), dbg: optional dumps (see
+ * moe_layer_debug); both NULL in production.
  * Errors: as the calls it makes.
  * ------------------------------------------------------------------------- */
 size_t moe_layer_workspace(const moe_cfg *cfg, int32_t T);
-/* Bytes at the start of a moe_layer workspace that must be zero before its
- * first use (every moe_layer call leaves them zero). */
-size_t moe_layer_sync_bytes(void);
 int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
               const float *bias, const void *experts, const void *shared,
               const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
               float *w_out, void *workspace, size_t ws_bytes, const moe_events *ev,
-              void *stream);
+              const moe_layer_debug *dbg, void *stream);
 
 /* ---------------------------------------------------------------------------
  * moe_layer_ptrs — moe_layer with the routed expert records addressed one by
@@ -293,7 +312,7 @@ int moe_layer_ptrs(const moe_cfg *cfg, int32_t T, const float *x, const float *w
                    const float *bias, const void *const *expert_ptrs, const void *shared,
                    const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
                    float *w_out, void *workspace, size_t ws_bytes, const moe_events *ev,
-                   void *stream);
+                   const moe_layer_debug *dbg, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Expert cache (host runtime around moe_layer_ptrs) — "Show HN…", section

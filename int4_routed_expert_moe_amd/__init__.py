@@ -23,7 +23,7 @@ MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 EXPORTS = (
     "moe_expert_blob_bytes", "moe_route_workspace", "moe_route", "moe_quant_act", "moe_group",
     "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_combine", "moe_rmsnorm",
-    "moe_layer_workspace", "moe_layer_sync_bytes", "moe_layer", "moe_layer_ptrs",
+    "moe_layer_workspace", "moe_layer", "moe_layer_ptrs",
     "moe_host_device_ptr", "moe_cache_create", "moe_cache_step", "moe_cache_get_stats",
     "moe_cache_usage", "moe_cache_slot_of", "moe_cache_destroy", "moe_cache_simulate",
     "moe_strerror", "moe_last_error",
@@ -58,6 +58,14 @@ class MoeFfnDebug(ctypes.Structure):
     _fields_ = [("gate_dots", ctypes.c_void_p), ("up_dots", ctypes.c_void_p),
                 ("h", ctypes.c_void_p), ("q_h", ctypes.c_void_p), ("d_h", ctypes.c_void_p),
                 ("down_dots", ctypes.c_void_p)]
+
+
+class MoeLayerDebug(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("d", ctypes.c_void_p),
+                ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("perm", ctypes.c_void_p), ("inv", ctypes.c_void_p),
+                ("active", ctypes.c_void_p), ("n_active", ctypes.c_void_p),
+                ("ffn", MoeFfnDebug)]
 
 
 class MoeCacheStats(ctypes.Structure):
@@ -106,10 +114,8 @@ def lib():
     L.moe_rmsnorm.restype = ctypes.c_int
     L.moe_layer_workspace.argtypes = [pc, i32]
     L.moe_layer_workspace.restype = sz
-    L.moe_layer_sync_bytes.argtypes = []
-    L.moe_layer_sync_bytes.restype = sz
     L.moe_layer.argtypes = [pc, i32, v, v, v, v, v, v, v, v, f32, v, v, v, sz,
-                            ctypes.POINTER(MoeEvents), v]
+                            ctypes.POINTER(MoeEvents), ctypes.POINTER(MoeLayerDebug), v]
     L.moe_layer.restype = ctypes.c_int
     L.moe_layer_ptrs.argtypes = L.moe_layer.argtypes
     L.moe_layer_ptrs.restype = ctypes.c_int
@@ -207,18 +213,12 @@ def layer_workspace(cfg: Config, T: int) -> int:
     return int(lib().moe_layer_workspace(ctypes.byref(cfg.c()), T))
 
 
-def layer_sync_bytes() -> int:
-    """Leading bytes of a layer workspace holding its (zero-between-calls) counters."""
-    return int(lib().moe_layer_sync_bytes())
-
-
-
 def _workspace(nbytes, device, ws=None):
-    """Caller's workspace, or a new zero-filled one (moe_layer needs zeros)."""
+    """Caller's workspace, or a new one (its contents do not matter)."""
     torch = _torch()
     if ws is not None:
         return ws
-    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def route(cfg: Config, x, w_router, bias, idx=None, w=None, workspace=None):
@@ -265,7 +265,8 @@ def group(cfg: Config, idx):
 
 
 def debug_buffers(cfg: Config, T: int, device):
-    """Device buffers for every intermediate moe_expert_ffn can report."""
+    """Device buffers for every intermediate moe_expert_ffn can report
+    (moe_layer's dumps add q, d and the union: ``layer_debug_buffers``)."""
     torch = _torch()
     P = T * cfg.top_k + T * cfg.n_shared
     H, I = cfg.hidden, cfg.inter
@@ -275,6 +276,32 @@ def debug_buffers(cfg: Config, T: int, device):
                 q_h=torch.zeros((P, I), dtype=torch.int8, device=device),
                 d_h=torch.zeros((P, I // 32), dtype=torch.float32, device=device),
                 down_dots=torch.zeros((P, H, I // 32), dtype=torch.int32, device=device))
+
+
+def layer_debug_buffers(cfg: Config, T: int, device):
+    """Device buffers for every intermediate moe_layer can report."""
+    torch = _torch()
+    H, E, S = cfg.hidden, cfg.n_experts, T * cfg.top_k
+    out = debug_buffers(cfg, T, device)
+    i32 = dict(dtype=torch.int32, device=device)
+    out.update(q=torch.zeros((T, H), dtype=torch.int8, device=device),
+               d=torch.zeros((T, H // 32), dtype=torch.float32, device=device),
+               counts=torch.zeros(E, **i32), offsets=torch.zeros(E + 1, **i32),
+               perm=torch.zeros(S, **i32), inv=torch.zeros(S, **i32),
+               active=torch.zeros(E, **i32), n_active=torch.zeros(1, **i32))
+    return out
+
+
+_FFN_DUMPS = ("gate_dots", "up_dots", "h", "q_h", "d_h", "down_dots")
+_UNION_DUMPS = ("counts", "offsets", "perm", "inv", "active", "n_active")
+
+
+def _layer_debug(debug):
+    if debug is None:
+        return None
+    p = lambda k: _ptr(debug[k]) if debug.get(k) is not None else None  # noqa: E731
+    return MoeLayerDebug(p("q"), p("d"), *[p(k) for k in _UNION_DUMPS],
+                         MoeFfnDebug(*[p(k) for k in _FFN_DUMPS]))
 
 
 def expert_ffn(cfg: Config, q, d, idx, experts, shared=None, expert_out=None, shared_out=None,
@@ -292,7 +319,7 @@ def expert_ffn(cfg: Config, q, d, idx, experts, shared=None, expert_out=None, sh
     dbg = None
     if debug is not None:
         dbg = MoeFfnDebug(*[(_ptr(debug[k]) if debug.get(k) is not None else None)
-                            for k in ("gate_dots", "up_dots", "h", "q_h", "d_h", "down_dots")])
+                            for k in _FFN_DUMPS])
     _check(lib().moe_expert_ffn(ctypes.byref(cfg.c()), T, _ptr(q), _ptr(d), _ptr(idx),
                                 _ptr(experts), _ptr(shared), _ptr(expert_out), _ptr(shared_out),
                                 _ptr(ws), ws.numel(), ctypes.byref(dbg) if dbg else None,
@@ -323,27 +350,30 @@ def rmsnorm(x, y=None, eps=1e-5):
 
 def layer(cfg: Config, x, w_router, bias, experts, shared=None, residual=None, y=None,
           y_norm=None, eps=1e-5, want_norm=False, idx_out=None, w_out=None, workspace=None,
-          events=None):
+          events=None, debug=None):
     """moe_layer (whole step): returns y (and y_norm when want_norm).
 
     events: optional MoeEvents (hipEvent_t handles per stage) to receive the
-    kernels' own start/stop timestamps."""
+    kernels' own start/stop timestamps; debug: optional dict of device
+    buffers (``layer_debug_buffers``, any subset) for the intermediates."""
     torch = _torch()
     T, H = x.shape
     y = y if y is not None else torch.empty((T, H), dtype=torch.float32, device=x.device)
     if want_norm and y_norm is None:
         y_norm = torch.empty_like(y)
     ws = _workspace(layer_workspace(cfg, T), x.device, workspace)
+    dbg = _layer_debug(debug)
     _check(lib().moe_layer(ctypes.byref(cfg.c()), T, _ptr(x), _ptr(w_router), _ptr(bias),
                            _ptr(experts), _ptr(shared), _ptr(residual), _ptr(y), _ptr(y_norm),
                            eps, _ptr(idx_out), _ptr(w_out), _ptr(ws), ws.numel(),
-                           ctypes.byref(events) if events is not None else None, _stream()))
+                           ctypes.byref(events) if events is not None else None,
+                           ctypes.byref(dbg) if dbg is not None else None, _stream()))
     return (y, y_norm) if want_norm else y
 
 
 def layer_ptrs(cfg: Config, x, w_router, bias, expert_ptrs, shared=None, residual=None, y=None,
                y_norm=None, eps=1e-5, want_norm=False, idx_out=None, w_out=None,
-               workspace=None, events=None):
+               workspace=None, events=None, debug=None):
     """moe_layer_ptrs: as layer(), the routed records given by a device int64
     tensor of E record addresses (HBM or device-readable pinned host memory)."""
     torch = _torch()
@@ -352,11 +382,12 @@ def layer_ptrs(cfg: Config, x, w_router, bias, expert_ptrs, shared=None, residua
     if want_norm and y_norm is None:
         y_norm = torch.empty_like(y)
     ws = _workspace(layer_workspace(cfg, T), x.device, workspace)
+    dbg = _layer_debug(debug)
     _check(lib().moe_layer_ptrs(ctypes.byref(cfg.c()), T, _ptr(x), _ptr(w_router), _ptr(bias),
                                 _ptr(expert_ptrs), _ptr(shared), _ptr(residual), _ptr(y),
                                 _ptr(y_norm), eps, _ptr(idx_out), _ptr(w_out), _ptr(ws),
                                 ws.numel(), ctypes.byref(events) if events is not None else None,
-                                _stream()))
+                                ctypes.byref(dbg) if dbg is not None else None, _stream()))
     return (y, y_norm) if want_norm else y
 
 

@@ -46,6 +46,34 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
   return v;
 }
 
+// --- the router's fixed-order sigmoid -------------------------------------
+// e^y in fp32 from basic operations only, so that every kernel and a CPU
+// following the same steps get the same bits: y clamped to [-87, 87];
+// Cody–Waite reduction n = rint(y log2 e), r = (y - n LN2_HI) - n LN2_LO with
+// ln 2 split into a 16-bit-exact high part and the fp32 remainder; the
+// degree-7 Taylor polynomial of e^r (coefficients fp32(1/k!)) in Horner form
+// with fma; then the scaling by 2^n.  Files using it are compiled with
+// -ffp-contract=off and correctly rounded fp32 division.
+__device__ __forceinline__ float exp_fixed(float y) {
+  y = y > 87.0f ? 87.0f : y;
+  y = y < -87.0f ? -87.0f : y;
+  const float n = __builtin_rintf(y * 1.44269502f);
+  float r = __builtin_fmaf(-n, 0.693145751953125f, y);
+  r = __builtin_fmaf(-n, 1.42860677e-06f, r);
+  float p = 1.98412701e-04f;                  // 1/7!
+  p = __builtin_fmaf(p, r, 1.38888892e-03f);  // 1/6!
+  p = __builtin_fmaf(p, r, 8.33333377e-03f);  // 1/5!
+  p = __builtin_fmaf(p, r, 4.16666679e-02f);  // 1/4!
+  p = __builtin_fmaf(p, r, 1.66666672e-01f);  // 1/3!
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  return __builtin_ldexpf(p, (int)n);
+}
+
+// sigmoid(l) = 1 / (1 + e^-l), correctly rounded division.
+__device__ __forceinline__ float sigmoid_fixed(float l) { return 1.0f / (1.0f + exp_fixed(-l)); }
+
 // --- order-preserving key of a float (no NaN); -0 is folded onto +0 -------
 __device__ __forceinline__ uint32_t float_key(float f) {
   f = f + 0.0f;

@@ -494,7 +494,7 @@ __global__ void __launch_bounds__(256) k_down_mfma(FfnArgs a, const int4 *tiles,
 // tokens: workgroup (row tile, slot) straight from the batch union's slot
 // table (entry: expert, token count, pair ids, record address); empty slots
 // exit at once.
-template <int WB>
+template <int WB, bool DBG>
 __global__ void __launch_bounds__(256) k_down_mfma_slots(FfnArgs a, const int32_t *slots,
                                                          int slot_w, int slot_ptr,
                                                          const int8_t *q_h, const float *d_h) {
@@ -516,7 +516,7 @@ __global__ void __launch_bounds__(256) k_down_mfma_slots(FfnArgs a, const int32_
     L.pairl[tid] = pair;
   }
   __syncthreads();
-  down_mfma_tile<false, WB, true>(a, ti, q_h, d_h, L, as, wsl);
+  down_mfma_tile<DBG, WB, true>(a, ti, q_h, d_h, L, as, wsl);
 }
 
 template <bool DBG, int WB, bool NT>
@@ -578,18 +578,28 @@ static void launch_mfma_wb(const FfnArgs &a, int max_tiles, int4 *tiles, int32_t
            (const float *)d_h);
 }
 
-void launch_down_mfma_slots(const FfnArgs &a, const int32_t *slots, int n_slots_ub, int slot_w,
-                            int slot_ptr, const int8_t *q_h, const float *d_h, hipStream_t st,
-                            const moe_events *ev) {
+template <bool DBG>
+static void launch_down_slots_dbg(const FfnArgs &a, const int32_t *slots, int n_slots_ub,
+                                  int slot_w, int slot_ptr, const int8_t *q_h, const float *d_h,
+                                  hipStream_t st, const moe_events *ev) {
   const dim3 g(a.H / mf::RT, n_slots_ub);
   const Ev ed = stage_ev(ev, MOE_STAGE_DOWN);
   if (a.wfmt == 1)
-    launch_k(k_down_mfma_slots<WB_MX>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr, q_h,
-             d_h);
+    launch_k(k_down_mfma_slots<WB_MX, DBG>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr,
+             q_h, d_h);
   else if (a.wbits == 8)
-    launch_k(k_down_mfma_slots<8>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr, q_h, d_h);
+    launch_k(k_down_mfma_slots<8, DBG>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr, q_h,
+             d_h);
   else
-    launch_k(k_down_mfma_slots<4>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr, q_h, d_h);
+    launch_k(k_down_mfma_slots<4, DBG>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr, q_h,
+             d_h);
+}
+
+void launch_down_mfma_slots(const FfnArgs &a, const int32_t *slots, int n_slots_ub, int slot_w,
+                            int slot_ptr, const int8_t *q_h, const float *d_h, bool dbg,
+                            hipStream_t st, const moe_events *ev) {
+  if (dbg) launch_down_slots_dbg<true>(a, slots, n_slots_ub, slot_w, slot_ptr, q_h, d_h, st, ev);
+  else launch_down_slots_dbg<false>(a, slots, n_slots_ub, slot_w, slot_ptr, q_h, d_h, st, ev);
 }
 
 void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_h, float *d_h,

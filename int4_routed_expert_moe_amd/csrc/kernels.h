@@ -78,11 +78,12 @@ void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_
                      hipStream_t st, const moe_events *ev = nullptr);
 // The down projection of the small-batch path from its slot table (int8,
 // int4, MXFP4), rows to expert_out / shared_out.
+// dbg: the kernel that also writes a.dbg.down_dots.
 void launch_down_mfma_slots(const FfnArgs &a, const int32_t *slots, int n_slots_ub, int slot_w,
-                            int slot_ptr, const int8_t *q_h, const float *d_h, hipStream_t st,
-                            const moe_events *ev);
+                            int slot_ptr, const int8_t *q_h, const float *d_h, bool dbg,
+                            hipStream_t st, const moe_events *ev);
 
-// Whole layer for 1..16 tokens in three kernels (decode.hip).
+// Whole layer for 1..16 tokens in four kernels (decode.h).
 struct LayerArgs {
   int H, I, E, G, TG, K, T, n_shared, wbits;
   int wfmt;  // 0: integer codes with row scales; 1: MXFP4
@@ -104,12 +105,13 @@ struct LayerArgs {
   float *dh;                     // [P][I/32]
   float *ssq;                    // [T][H/8] partial sums of squares
   float *eo_r, *eo_s;            // expert_out [T*K][H] / shared_out [T][H] (MFMA down)
-  uint32_t *sync;                // zero-initialised counters
   int n_slots_ub;
+  moe_layer_debug dbg;           // dumps (launch_small_batch_dbg only)
 };
-size_t small_batch_sync_bytes();
 size_t small_batch_slot_ints(int T, int K, int n_shared);
 bool small_batch_supported(const moe_cfg &c, int T);
 void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev);
+// The same with a.dbg's dumps written (decode_dbg.hip).
+void launch_small_batch_dbg(LayerArgs a, hipStream_t st, const moe_events *ev);
 
 }  // namespace moe

@@ -142,7 +142,6 @@ FfnWs carve_ffn(Carve &cv, const moe_cfg &c, int T) {
 }
 
 struct LayerWs {
-  uint32_t *sync;  // first in the workspace: counters of the fused kernel
   float *ssq;
   int32_t *slots;
   float *hs;
@@ -158,7 +157,6 @@ struct LayerWs {
 };
 LayerWs carve_layer(Carve &cv, const moe_cfg &c, int T) {
   LayerWs l;
-  l.sync = cv.take<uint32_t>(moe::small_batch_sync_bytes() / sizeof(uint32_t));
   l.ssq = cv.take<float>((size_t)T * (c.hidden / 8));
   l.slots = cv.take<int32_t>(moe::small_batch_slot_ints(T, c.top_k, c.n_shared));
   l.hs = cv.take<float>((size_t)T * c.inter * c.n_shared);
@@ -380,19 +378,44 @@ size_t moe_layer_workspace(const moe_cfg *cfg, int32_t T) {
   return cv.off;
 }
 
-size_t moe_layer_sync_bytes(void) { return moe::small_batch_sync_bytes(); }
-
 }  // extern "C"
 
 namespace {
 
 // moe_layer with the routed records either contiguous (experts) or given one
 // pointer each (expert_ptrs, a device array of E pointers); exactly one is set.
+bool any_ffn_dump(const moe_ffn_debug &f) {
+  return f.gate_dots || f.up_dots || f.h || f.q_h || f.d_h || f.down_dots;
+}
+
+int check_layer_debug(const moe_layer_debug *g) {
+  if (!g) return MOE_OK;
+  OPTIONAL(g->q, "dbg->q");
+  OPTIONAL(g->d, "dbg->d");
+  const int32_t *u[6] = {g->counts, g->offsets, g->perm, g->inv, g->active, g->n_active};
+  const char *un[6] = {"dbg->counts", "dbg->offsets", "dbg->perm", "dbg->inv", "dbg->active",
+                       "dbg->n_active"};
+  int given = 0;
+  for (int i = 0; i < 6; i++) {
+    OPTIONAL(u[i], un[i]);
+    given += u[i] != nullptr;
+  }
+  if (given != 0 && given != 6)
+    return fail(MOE_EINVAL, "dbg: the six union arrays are given together or not at all");
+  OPTIONAL(g->ffn.gate_dots, "dbg->ffn.gate_dots");
+  OPTIONAL(g->ffn.up_dots, "dbg->ffn.up_dots");
+  OPTIONAL(g->ffn.h, "dbg->ffn.h");
+  OPTIONAL(g->ffn.q_h, "dbg->ffn.q_h");
+  OPTIONAL(g->ffn.d_h, "dbg->ffn.d_h");
+  OPTIONAL(g->ffn.down_dots, "dbg->ffn.down_dots");
+  return MOE_OK;
+}
+
 int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
                const float *bias, const void *experts, const void *const *expert_ptrs,
                const void *shared, const float *residual, float *y, float *y_norm, float eps,
                int32_t *idx_out, float *w_out, void *workspace, size_t ws_bytes,
-               const moe_events *ev, void *stream) {
+               const moe_events *ev, const moe_layer_debug *dbg, void *stream) {
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
@@ -416,6 +439,11 @@ int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rou
     REQUIRE(shared, "shared");
     if (!aligned(shared, 256)) return fail(MOE_EALIGN, "shared is not 256-byte aligned");
   }
+  if ((rc = check_layer_debug(dbg))) return rc;
+  moe_layer_debug g;
+  if (dbg) g = *dbg;
+  else memset(&g, 0, sizeof(g));
+  const bool dump_union = g.counts != nullptr, dump_ffn = any_ffn_dump(g.ffn);
   const size_t need = moe_layer_workspace(cfg, T);
   if (!workspace || ws_bytes < need)
     return fail(MOE_EWORKSPACE, "layer workspace %zu < %zu bytes", ws_bytes, need);
@@ -426,6 +454,8 @@ int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rou
   LayerWs ws = carve_layer(cv, c, T);
   int32_t *idx = idx_out ? idx_out : ws.idx;
   float *w = w_out ? w_out : ws.w;
+  int8_t *q = g.q ? g.q : ws.q;  // the kernels write Q8_0 of x straight into a dump
+  float *d = g.d ? g.d : ws.d;
   if (moe::small_batch_supported(c, T)) {
     moe::LayerArgs a;
     a.H = c.hidden;
@@ -455,8 +485,8 @@ int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rou
     a.w = w;
     a.s = ws.route.s;
     a.sb = ws.route.sb;
-    a.q = ws.q;
-    a.d = ws.d;
+    a.q = q;
+    a.d = d;
     a.slots = ws.slots;
     a.hs = ws.hs;
     a.qh = ws.qh;
@@ -464,15 +494,26 @@ int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rou
     a.ssq = ws.ssq;
     a.eo_r = ws.expert_out;
     a.eo_s = c.n_shared ? ws.shared_out : nullptr;
-    a.sync = ws.sync;
-    moe::launch_small_batch(a, st, ev);
+    a.dbg = g;
+    if (dump_union || dump_ffn) moe::launch_small_batch_dbg(a, st, ev);
+    else moe::launch_small_batch(a, st, ev);
     return launched("moe_layer (small batch)");
   }
   if ((rc = do_route(c, T, x, w_router, bias, idx, w, ws.route, st, ev))) return rc;
-  moe::launch_quant_act(x, ws.q, ws.d, (int64_t)T * c.hidden, st, ev);
+  moe::launch_quant_act(x, q, d, (int64_t)T * c.hidden, st, ev);
   if ((rc = launched("moe_layer quant"))) return rc;
-  if ((rc = do_ffn(c, T, ws.q, ws.d, idx, experts, c.n_shared ? shared : nullptr, ws.expert_out,
-                   c.n_shared ? ws.shared_out : nullptr, ws.ffn, nullptr, st, ev, expert_ptrs)))
+  FfnWs fws = ws.ffn;
+  if (dump_union) {  // the grouping kernel writes the union straight into the dump
+    fws.counts = g.counts;
+    fws.offsets = g.offsets;
+    fws.perm = g.perm;
+    fws.inv = g.inv;
+    fws.active = g.active;
+    fws.n_active = g.n_active;
+  }
+  if ((rc = do_ffn(c, T, q, d, idx, experts, c.n_shared ? shared : nullptr, ws.expert_out,
+                   c.n_shared ? ws.shared_out : nullptr, fws, dump_ffn ? &g.ffn : nullptr, st,
+                   ev, expert_ptrs)))
     return rc;
   moe::launch_combine(T, c.hidden, c.top_k, ws.expert_out, w,
                       c.n_shared ? ws.shared_out : nullptr, residual, y, y_norm, eps, st, ev);
@@ -487,20 +528,20 @@ int moe_layer(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
               const float *bias, const void *experts, const void *shared,
               const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
               float *w_out, void *workspace, size_t ws_bytes, const moe_events *ev,
-              void *stream) {
+              const moe_layer_debug *dbg, void *stream) {
   if (!experts) return fail(MOE_EINVAL, "experts is NULL");
   return layer_impl(cfg, T, x, w_router, bias, experts, nullptr, shared, residual, y, y_norm,
-                    eps, idx_out, w_out, workspace, ws_bytes, ev, stream);
+                    eps, idx_out, w_out, workspace, ws_bytes, ev, dbg, stream);
 }
 
 int moe_layer_ptrs(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
                    const float *bias, const void *const *expert_ptrs, const void *shared,
                    const float *residual, float *y, float *y_norm, float eps, int32_t *idx_out,
                    float *w_out, void *workspace, size_t ws_bytes, const moe_events *ev,
-                   void *stream) {
+                   const moe_layer_debug *dbg, void *stream) {
   if (!expert_ptrs) return fail(MOE_EINVAL, "expert_ptrs is NULL");
   return layer_impl(cfg, T, x, w_router, bias, nullptr, expert_ptrs, shared, residual, y, y_norm,
-                    eps, idx_out, w_out, workspace, ws_bytes, ev, stream);
+                    eps, idx_out, w_out, workspace, ws_bytes, ev, dbg, stream);
 }
 
 const char *moe_strerror(int code) {

@@ -19,25 +19,6 @@
 
 namespace moe {
 
-__device__ __forceinline__ float exp_fixed(float y) {
-  y = y > 87.0f ? 87.0f : y;
-  y = y < -87.0f ? -87.0f : y;
-  const float n = __builtin_rintf(y * 1.44269502f);
-  float r = __builtin_fmaf(-n, 0.693145751953125f, y);
-  r = __builtin_fmaf(-n, 1.42860677e-06f, r);
-  float p = 1.98412701e-04f;            // 1/7!
-  p = __builtin_fmaf(p, r, 1.38888892e-03f);  // 1/6!
-  p = __builtin_fmaf(p, r, 8.33333377e-03f);  // 1/5!
-  p = __builtin_fmaf(p, r, 4.16666679e-02f);  // 1/4!
-  p = __builtin_fmaf(p, r, 1.66666672e-01f);  // 1/3!
-  p = __builtin_fmaf(p, r, 0.5f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  p = __builtin_fmaf(p, r, 1.0f);
-  return __builtin_ldexpf(p, (int)n);
-}
-
-__device__ __forceinline__ float sigmoid_fixed(float l) { return 1.0f / (1.0f + exp_fixed(-l)); }
-
 // One wave per (expert, chunk of TT tokens).  Lane l owns the 64-element
 // chunks l, l+64, ...; each chunk is an fma chain over its 64 elements; the
 // chunk partials go to LDS and one lane per token adds them left to right.

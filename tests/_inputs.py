@@ -27,7 +27,11 @@ class DeviceLayer:
 
     Router weights and bias are drawn on the host; expert records are drawn on
     the host for small shapes and by the GPU copy of the generator for the
-    real shape (identical bytes either way)."""
+    real shape (identical bytes either way: the generator test checks it, and
+    each such layer re-checks one record against the host generator).  Host
+    copies of GPU-drawn records are read back from device memory (no kernel
+    of the library writes a record), since drawing 19 MB on the host takes
+    ~0.2 s per record."""
 
     def __init__(self, shape, seed, layer=0, bias="uniform", device="cuda:0", gpu_gen=None):
         import torch
@@ -48,6 +52,7 @@ class DeviceLayer:
         self.experts_d = torch.empty(E * bb, dtype=torch.uint8, device=self.dev)
         self.shared_d = torch.empty(bb, dtype=torch.uint8, device=self.dev)
         self._cache = {}
+        self.gpu_gen = gpu_gen
         if gpu_gen:
             stream = torch.cuda.current_stream().cuda_stream
             synth.expert_blobs_gpu(shape, seed, layer, list(range(E)), self.experts_d.data_ptr(),
@@ -55,15 +60,34 @@ class DeviceLayer:
             synth.expert_blobs_gpu(shape, seed, layer, [synth.SHARED_ID], self.shared_d.data_ptr(),
                                    bb, stream)
             torch.cuda.synchronize()
+            probe = (layer * 37 + 5) % E
+            assert np.array_equal(self.blob(probe),
+                                  synth.expert_blob(shape, seed, layer, probe)), "generator"
         else:
             host = np.concatenate([self.blob(e) for e in range(E)])
             self.experts_d.copy_(torch.from_numpy(host))
             self.shared_d.copy_(torch.from_numpy(self.blob(synth.SHARED_ID)))
 
+    def _dev_record(self, e: int):
+        bb = self.blob_bytes
+        return self.shared_d if e == synth.SHARED_ID else self.experts_d[e * bb:(e + 1) * bb]
+
     def blob(self, e: int) -> np.ndarray:
+        if self.gpu_gen:
+            return self._dev_record(e).cpu().numpy()
         if e not in self._cache:
             self._cache[e] = synth.expert_blob(self.shape, self.seed, self.layer, e)
         return self._cache[e]
+
+    def set_record(self, e: int, rec: np.ndarray) -> None:
+        """Replace expert e's record (or the shared one) on the device and in
+        the host copies."""
+        import torch
+        assert rec.dtype == np.uint8 and rec.size == self.blob_bytes
+        self._dev_record(e).copy_(torch.from_numpy(np.ascontiguousarray(rec)))
+        torch.cuda.synchronize()
+        if not self.gpu_gen:
+            self._cache[e] = rec.copy()
 
     def oracle_layer(self, x, residual=None, want_norm=False, top_p=0.0):
         import oracle

@@ -153,11 +153,18 @@ def test_combine_and_layer_errors(L):
     ws = moe.layer_workspace(REAL, 1)
     lay = L.moe_layer
     assert lay(ctypes.byref(c), 1, A, A, A, A, A, None, A, None, 1e-5, None, None, A, ws - 1,
-               None, None) == moe.MOE_EWORKSPACE
+               None, None, None) == moe.MOE_EWORKSPACE
     assert lay(ctypes.byref(c), 1, A, A, A, A, None, None, A, None, 1e-5, None, None, A, ws,
-               None, None) == moe.MOE_EINVAL
+               None, None, None) == moe.MOE_EINVAL
     assert lay(ctypes.byref(c), 1, A, A, A, A + 64, A, None, A, None, 1e-5, None, None, A, ws,
-               None, None) == moe.MOE_EALIGN
+               None, None, None) == moe.MOE_EALIGN
+    # the union dumps come as a set of six
+    part = moe.MoeLayerDebug(None, None, A, A, None, None, None, None)
+    assert lay(ctypes.byref(c), 1, A, A, A, A, A, None, A, None, 1e-5, None, None, A, ws,
+               None, ctypes.byref(part), None) == moe.MOE_EINVAL
+    mis = moe.MoeLayerDebug(A + 4)
+    assert lay(ctypes.byref(c), 1, A, A, A, A, A, None, A, None, 1e-5, None, None, A, ws,
+               None, ctypes.byref(mis), None) == moe.MOE_EALIGN
 
 
 def test_strerror(L):
@@ -190,5 +197,5 @@ def test_cache_create_rejects_bad_arguments(L):
 def test_layer_ptrs_rejects_null_table(L):
     c = TINY.c()
     rc = L.moe_layer_ptrs(ctypes.byref(c), 1, A, A, A, None, A, None, A, None, 1e-5, None, None,
-                          A, 1 << 30, None, None)
+                          A, 1 << 30, None, None, None)
     assert rc == moe.MOE_EINVAL

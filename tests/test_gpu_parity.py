@@ -495,46 +495,71 @@ def test_layer_graph_replays_match_eager(dev, real):
             assert np.all(np.isfinite(h(other)))
 
 
-@pytest.mark.parametrize("T", [1, 2, 5, 16])
-def test_layer_counters_return_to_zero(dev, real, T):
-    """The single-launch path leaves its counter region zero and records no
-    timed-out wait, call after call (same workspace)."""
-    cfg = moe.Config.of(synth.REAL)
-    ws = torch.zeros(moe.layer_workspace(cfg, T), dtype=torch.uint8, device=dev)
-    nsync = moe.layer_sync_bytes()
-    outs = []
-    for rep in range(3):
-        x = to_d(synth.tokens(synth.REAL, 300 + rep, T), dev)
-        outs.append(h(moe.layer(cfg, x, real.wr_d, real.bias_d, real.experts_d, real.shared_d,
-                                workspace=ws, want_norm=True)[1]))
-        sync = h(ws[:nsync])
-        assert np.count_nonzero(sync) == 0, f"call {rep}: counters not cleared"
-    assert all(np.all(np.isfinite(o)) for o in outs)
+_prefill = {}
 
 
-def test_layer_prefill_full_size_sampled(dev):
-    """Prefill at full size (2048 tokens, Zipf-skewed bias): every index
-    bit-exact; the layer output of sampled tokens against the oracle run on
-    those tokens alone (tokens are independent once routed)."""
-    lay = DeviceLayer(synth.REAL, synth.SEEDS["prefill"], bias="zipf")
-    s = lay.shape
-    cfg = moe.Config.of(s)
-    T = 2048
-    x = synth.tokens(s, synth.SEEDS["prefill"], T)
-    idx_d = torch.empty((T, s.top_k), dtype=torch.int32, device=dev)
-    w_d = torch.empty((T, s.top_k), dtype=torch.float32, device=dev)
-    y = h(moe.layer(cfg, to_d(x, dev), lay.wr_d, lay.bias_d, lay.experts_d, lay.shared_d,
-                    idx_out=idx_d, w_out=w_d))
-    idx, w, _ = oracle.route(x, lay.wr, lay.bias, s.n_group, s.topk_group, s.top_k,
-                             s.routed_scaling)
-    assert np.array_equal(h(idx_d), idx)
-    assert np.array_equal(h(w_d), w)
+def teardown_module(module):
+    _prefill.clear()
+
+
+def prefill_run(dev):
+    """Prefill at full size (2048 tokens, Zipf-skewed bias) through moe_layer,
+    run once for the module: (layer, x, idx, w, y)."""
+    if not _prefill:
+        lay = DeviceLayer(synth.REAL, synth.SEEDS["prefill"], bias="zipf")
+        s = lay.shape
+        T = 2048
+        x = synth.tokens(s, synth.SEEDS["prefill"], T)
+        idx_d = torch.empty((T, s.top_k), dtype=torch.int32, device=dev)
+        w_d = torch.empty((T, s.top_k), dtype=torch.float32, device=dev)
+        y = h(moe.layer(moe.Config.of(s), to_d(x, dev), lay.wr_d, lay.bias_d, lay.experts_d,
+                        lay.shared_d, idx_out=idx_d, w_out=w_d))
+        _prefill.update(lay=lay, x=x, idx=h(idx_d), w=h(w_d), y=y)
+    return _prefill
+
+
+def test_layer_prefill_full_size_routing(dev):
+    """Every index and weight of the 2048 tokens bit-exact."""
+    r = prefill_run(dev)
+    s = r["lay"].shape
+    idx, w, _ = oracle.route(r["x"], r["lay"].wr, r["lay"].bias, s.n_group, s.topk_group,
+                             s.top_k, s.routed_scaling)
+    assert np.array_equal(r["idx"], idx)
+    assert np.array_equal(r["w"], w)
     counts = np.bincount(idx.ravel(), minlength=s.n_experts)
     assert counts.max() > 64  # several token tiles for the hot experts
-    for t in (0, 1, 777, 1500, 2047):
-        ref = lay.oracle_layer(x[t:t + 1])
-        assert np.array_equal(ref["idx"][0], idx[t])
-        assert_close_rms(y[t], ref["y"][0], 2e-3, f"y token {t}")
+
+
+def _prefill_sample(r, chunk):
+    """Token chunk `chunk` of the 256 checked: 0 = the hottest expert's first
+    64-token tile, 1 = its last tile (with the tokens after it to fill 64),
+    2-3 = tokens spread over the batch."""
+    s = r["lay"].shape
+    idx = r["idx"]
+    hot = int(np.argmax(np.bincount(idx.ravel(), minlength=s.n_experts)))
+    toks = np.flatnonzero((idx == hot).any(axis=1))  # the hot expert's list, in order
+    if chunk == 0:
+        return toks[:64]
+    if chunk == 1:
+        last = toks[(len(toks) - 1) // 64 * 64:]
+        rest = np.setdiff1d(np.arange(2048), np.concatenate([toks[:64], last]))
+        return np.concatenate([last, rest[-(64 - len(last)):]]) if len(last) < 64 else last
+    rng = np.random.default_rng(chunk)
+    return np.sort(rng.choice(2048, 64, replace=False))
+
+
+@pytest.mark.parametrize("chunk", [0, 1, 2, 3])
+def test_layer_prefill_full_size_outputs(dev, chunk):
+    """The layer output of 256 of the 2048 tokens (every token of the hottest
+    expert's first and last tiles among them) against the oracle run on
+    those tokens alone (tokens are independent once routed)."""
+    r = prefill_run(dev)
+    sel = _prefill_sample(r, chunk)
+    assert len(sel) == 64
+    ref = r["lay"].oracle_layer(r["x"][sel])
+    assert np.array_equal(ref["idx"], r["idx"][sel])
+    for i, t in enumerate(sel):
+        assert_close_rms(r["y"][t], ref["y"][i], 2e-3, f"y token {t}")
 
 
 # Every token the same: every routed slot carries all T tokens, so the gate/up

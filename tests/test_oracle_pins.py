@@ -213,9 +213,44 @@ def test_select_hand_cases():
     for c in _load("router_cases.json")["cases"]:
         s = np.array([c["s"]], np.float32)
         sb = np.array([c["sb"]], np.float32)
-        idx, w, _ = oracle.select(s, sb, c["G"], c["TG"], c["K"], c["scale"])
+        idx, w, margin = oracle.select(s, sb, c["G"], c["TG"], c["K"], c["scale"])
         assert idx[0].tolist() == c["idx"], c["name"]
         assert np.allclose(w[0], np.array(c["w"], np.float32), rtol=0, atol=1e-7), c["name"]
+        if "margin" in c:  # dyadic cases: exact
+            want = [math.inf if m == "inf" else m for m in c["margin"]]
+            assert margin[0].tolist() == want, c["name"]
+
+
+@pytest.mark.parametrize("E,G,TG,K", [(8, 2, 1, 2), (16, 4, 2, 3), (256, 8, 4, 8), (12, 3, 3, 4)])
+def test_select_margins_vs_sorted_scores(E, G, TG, K):
+    """The selection margins against their definition, from sorted lists: the
+    K-th largest biased score of the kept groups minus the (K+1)-th, and the
+    TG-th largest group score (sum of the group's two largest, fp32) minus
+    the (TG+1)-th; +inf when nothing is left out.  Also on grid values with
+    many exact ties (margins 0)."""
+    rng = np.random.default_rng(E + 7 * K)
+    gs = E // G
+    for trial in range(100):
+        if trial % 2:
+            sb = (rng.integers(0, 8, (1, E)) / 8.0).astype(np.float32)
+        else:
+            sb = rng.uniform(-0.1, 1.1, (1, E)).astype(np.float32)
+        s = np.full((1, E), 0.5, np.float32)
+        idx, _, margin = oracle.select(s, sb, G, TG, K, 1.0)
+        v = sb[0]
+        gsc = [np.float32(np.sort(v[g * gs:(g + 1) * gs])[-1] + np.sort(v[g * gs:(g + 1) * gs])[-2])
+               for g in range(G)]
+        order = sorted(range(G), key=lambda g: (-float(gsc[g]), g))
+        kept = order[:TG]
+        mg = float(gsc[order[TG - 1]]) - float(gsc[order[TG]]) if TG < G else math.inf
+        cand = np.sort(np.concatenate([v[g * gs:(g + 1) * gs] for g in kept]).astype(np.float64))[::-1]
+        mp = cand[K - 1] - cand[K] if K < cand.size else math.inf
+        assert margin[0, 0] == mp and margin[0, 1] == mg, (trial, margin[0], mp, mg)
+        assert margin[0, 0] >= 0 and margin[0, 1] >= 0
+        # a zero pick margin means the K-th pick ties a left-out candidate
+        if mp == 0:
+            assert any(v[e] == v[idx[0, K - 1]] for e in range(E)
+                       if e // gs in kept and e not in idx[0])
 
 
 @pytest.mark.parametrize("E,G,TG,K", [(8, 2, 1, 2), (8, 4, 2, 3), (16, 4, 2, 3), (12, 3, 2, 4)])
@@ -556,6 +591,45 @@ def test_layer_zero_routed_experts_gives_shared_only():
     out = _tiny_layer(lambda e: zero, shared)
     assert np.all(out["expert_out"] == 0)
     assert np.array_equal(out["y"], out["shared_out"])
+
+
+def test_layer_places_each_expert_output_at_its_slot():
+    """Distinct routed experts: expert e is expert 0 with its down-row scales
+    times 2^e (so its output is exactly 2^e E0(x)).  Then, whatever the
+    grouping does, y[t] = S(x_t) + E0(x_t) * sum_k w[t,k] 2^idx[t,k]: an output
+    written to another rank's or token's slot breaks the sum.  Also every
+    expert_out row is the expert of its (t, k) slot applied to token t."""
+    shape = synth.TINY
+    H, I, E = shape.hidden, shape.inter, shape.n_experts
+    base = synth.expert_blob(shape, 100, 0, 0)
+    ds_off = 3 * I * H // 2 + 2 * I * 4  # the down-row scales of an int4 record
+
+    def blob_of(e):
+        b = base.copy()
+        b[ds_off:].view(np.float32)[:] *= np.float32(2.0 ** e)
+        return b
+
+    shared = synth.expert_blob(shape, 100, 0, synth.SHARED_ID)
+    x = synth.tokens(shape, 55, 16)
+    wr = synth.router_weights(shape, 55)
+    bias = synth.router_bias_uniform(shape, 55)
+    for p in (0.0, 0.6):
+        out = oracle.layer(x, wr, bias, blob_of, shared, H=H, I=I, n_experts=E,
+                           n_group=shape.n_group, topk_group=shape.topk_group, top_k=shape.top_k,
+                           scale=shape.routed_scaling, top_p_value=p)
+        idx, w = out["idx"], out["w"]
+        assert len({tuple(r) for r in idx.tolist()}) > 3  # varied placements
+        for t in range(16):
+            e0 = oracle.expert(base, H, I, 4, out["q"][t], out["d"][t])["y"].astype(np.float64)
+            mult = sum(float(w[t, k]) * 2.0 ** idx[t, k] for k in range(shape.top_k) if idx[t, k] >= 0)
+            ref = out["shared_out"][t].astype(np.float64) + mult * e0
+            assert np.max(np.abs(out["y"][t] - ref)) <= 1e-6 * np.sqrt(np.mean(ref ** 2))
+            for k in range(shape.top_k):
+                if idx[t, k] < 0:
+                    assert np.all(out["expert_out"][t, k] == 0)
+                    continue
+                assert np.array_equal(out["expert_out"][t, k],
+                                      (e0 * 2.0 ** idx[t, k]).astype(np.float32)), (t, k)
 
 
 def test_layer_groups_cover_every_slot_once():
