@@ -6,6 +6,16 @@ import numpy as np
 import synth
 
 
+def pairs_of(idx, n_shared):
+    """(pair, expert, token) of every routed slot kept and of the shared expert
+    (pair t*K + k: slot (t, k); pair T*K + t: the shared expert on token t)."""
+    T, K = idx.shape
+    out = [(t * K + k, int(idx[t, k]), t) for t in range(T) for k in range(K) if idx[t, k] >= 0]
+    if n_shared:
+        out += [(T * K + t, synth.SHARED_ID, t) for t in range(T)]
+    return out
+
+
 def rms(a) -> float:
     a = np.asarray(a, np.float64)
     return float(np.sqrt(np.mean(a * a))) if a.size else 0.0
@@ -88,6 +98,53 @@ class DeviceLayer:
         torch.cuda.synchronize()
         if not self.gpu_gen:
             self._cache[e] = rec.copy()
+
+    def oracle_layer_on_gpu_qh(self, x, dumps, residual=None, want_norm=False, top_p=0.0,
+                               tokens=None):
+        """The oracle layer with each down projection taken on the GPU's own
+        Q8_0(h) -- after checking that decision: the dumped q_h / d_h
+        (moe_layer_debug) are exactly Q8_0 of the dumped h, and h is within the
+        fp32 summation bound of the oracle's fp64 h.  Q8_0 of h is an fp32
+        decision on a value whose last bits depend on the summation order, so
+        where h sits within rounding of a code boundary both codes are
+        correct; the down projection of the GPU's codes is then the unique
+        comparand.  tokens: row of each x row in the dumps' batch (default
+        0..len(x)-1), when x is a sample of a larger batch.  Returns
+        oracle.layer's dict plus 'qh_flips', the pairs whose codes differ
+        from the oracle's own Q8_0(h)."""
+        import oracle
+        s = self.shape
+        H, I, K, wb = s.hidden, s.inter, s.top_k, s.wbits
+        tol_h = max(1e-5, 8 * (H // 32) * 2.0 ** -24)
+        x = np.ascontiguousarray(x, np.float32)
+        T = x.shape[0]
+        rows = np.arange(T) if tokens is None else np.asarray(tokens)
+        n_batch = int(dumps["h"].shape[0]) // (K + s.n_shared)
+        idx, w, margin = oracle.route(x, self.wr, self.bias, s.n_group, s.topk_group, K,
+                                      s.routed_scaling, top_p)
+        q, d = oracle.q8_0(x)
+        eo = np.zeros((T, K, H), np.float32)
+        so = np.zeros((T, H), np.float32) if s.n_shared else None
+        flips = 0
+        blobs = {}
+        for p, e, t in pairs_of(idx, s.n_shared):
+            gp = rows[t] * K + p % K if p < T * K else n_batch * K + rows[t]  # in the dumps
+            if e not in blobs:
+                blobs[e] = self.blob(e)
+            hr = oracle.gate_up(blobs[e], H, I, wb, q[t], d[t])["h"]
+            hg, qg, dg = dumps["h"][gp], dumps["q_h"][gp], dumps["d_h"][gp]
+            assert_close_rms(hg, hr, tol_h, f"h of pair {gp}")
+            qc, dc = oracle.q8_0(hg)
+            assert np.array_equal(qg, qc) and np.array_equal(dg, dc), f"Q8_0(h) of pair {gp}"
+            flips += not np.array_equal(oracle.q8_0(hr)[0], qg)
+            y, _ = oracle.down(blobs[e], H, I, wb, qg, dg)
+            if p < T * K:
+                eo[t, p % K] = y
+            else:
+                so[t] = y
+        res = oracle.combine(eo, w, so, residual, 1e-5, want_norm)
+        y, yn = res if want_norm else (res, None)
+        return dict(idx=idx, w=w, margin=margin, y=y, y_norm=yn, qh_flips=flips)
 
     def oracle_layer(self, x, residual=None, want_norm=False, top_p=0.0):
         import oracle

@@ -30,7 +30,7 @@ import torch
 import int4_routed_expert_moe_amd as moe
 import oracle
 import synth
-from _inputs import DeviceLayer, assert_close_rms
+from _inputs import DeviceLayer, assert_close_rms, pairs_of
 
 pytestmark = pytest.mark.gpu
 
@@ -74,15 +74,6 @@ def batch(shape, T, seed):
     if T == 1:
         return synth.tokens(shape, seed, 1, start=3)
     return synth.tokens_perturbed(shape, seed, T)
-
-
-def pairs_of(idx, n_shared):
-    """(pair, expert, token) of every routed slot kept and of the shared expert."""
-    T, K = idx.shape
-    out = [(t * K + k, int(idx[t, k]), t) for t in range(T) for k in range(K) if idx[t, k] >= 0]
-    if n_shared:
-        out += [(T * K + t, synth.SHARED_ID, t) for t in range(T)]
-    return out
 
 
 def check_dots(lay, q, d, idx, dbg, what=""):

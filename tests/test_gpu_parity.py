@@ -504,17 +504,27 @@ def teardown_module(module):
 
 def prefill_run(dev):
     """Prefill at full size (2048 tokens, Zipf-skewed bias) through moe_layer,
-    run once for the module: (layer, x, idx, w, y)."""
+    run once for the module, with h and Q8_0(h) of every pair dumped:
+    (layer, x, idx, w, y, dumps)."""
     if not _prefill:
         lay = DeviceLayer(synth.REAL, synth.SEEDS["prefill"], bias="zipf")
         s = lay.shape
         T = 2048
+        cfg = moe.Config.of(s)
         x = synth.tokens(s, synth.SEEDS["prefill"], T)
         idx_d = torch.empty((T, s.top_k), dtype=torch.int32, device=dev)
         w_d = torch.empty((T, s.top_k), dtype=torch.float32, device=dev)
-        y = h(moe.layer(moe.Config.of(s), to_d(x, dev), lay.wr_d, lay.bias_d, lay.experts_d,
-                        lay.shared_d, idx_out=idx_d, w_out=w_d))
-        _prefill.update(lay=lay, x=x, idx=h(idx_d), w=h(w_d), y=y)
+        full = moe.layer_debug_buffers(cfg, 1, dev)  # shapes only
+        P = T * (s.top_k + s.n_shared)
+        dumps = {k: torch.zeros((P,) + tuple(full[k].shape[1:]), dtype=full[k].dtype, device=dev)
+                 for k in ("h", "q_h", "d_h")}
+        y = h(moe.layer(cfg, to_d(x, dev), lay.wr_d, lay.bias_d, lay.experts_d, lay.shared_d,
+                        idx_out=idx_d, w_out=w_d, debug=dumps))
+        y_plain = h(moe.layer(cfg, to_d(x, dev), lay.wr_d, lay.bias_d, lay.experts_d,
+                              lay.shared_d))
+        assert np.array_equal(y, y_plain)
+        _prefill.update(lay=lay, x=x, idx=h(idx_d), w=h(w_d), y=y,
+                        dumps={k: h(v) for k, v in dumps.items()})
     return _prefill
 
 
@@ -552,14 +562,21 @@ def _prefill_sample(r, chunk):
 def test_layer_prefill_full_size_outputs(dev, chunk):
     """The layer output of 256 of the 2048 tokens (every token of the hottest
     expert's first and last tiles among them) against the oracle run on
-    those tokens alone (tokens are independent once routed)."""
+    those tokens alone (tokens are independent once routed), its down
+    projections taken on the GPU's own Q8_0(h) once that decision is checked
+    (DeviceLayer.oracle_layer_on_gpu_qh).  Tokens whose every Q8_0(h) code
+    equals the oracle's own also match the plain oracle layer."""
     r = prefill_run(dev)
     sel = _prefill_sample(r, chunk)
     assert len(sel) == 64
-    ref = r["lay"].oracle_layer(r["x"][sel])
+    lay = r["lay"]
+    ref = lay.oracle_layer_on_gpu_qh(r["x"][sel], r["dumps"], tokens=sel)
     assert np.array_equal(ref["idx"], r["idx"][sel])
     for i, t in enumerate(sel):
         assert_close_rms(r["y"][t], ref["y"][i], 2e-3, f"y token {t}")
+    if ref["qh_flips"] == 0:
+        plain = lay.oracle_layer(r["x"][sel])
+        assert_close_rms(r["y"][sel], plain["y"], 2e-3, "y (plain oracle)")
 
 
 # Every token the same: every routed slot carries all T tokens, so the gate/up
