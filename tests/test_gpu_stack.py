@@ -24,7 +24,9 @@ on the GPU, checked against the CPU oracle.
   the level of independent Q8_0 rounding noise, where it stays (measured on
   these stacks: at most 1.6% RMS and 5.6% max-norm of the normalised input;
   it does not grow with depth), and selections with margins of that order
-  then flip, each one excused by the score movement measured above.  So on
+  then flip, each one excused by the score movement measured above (two
+  adjacent ranks within that movement may also trade places, the same
+  experts in another order, which changes only the order of the sum).  So on
   the tokens still compared the inputs stay within 3x that noise floor
   (5% RMS, 20% max-norm) at every layer, and so do the final outputs.  (A
   check that the chains do not run away and that every flip is justified;
@@ -119,6 +121,16 @@ def free_running(layers, x, idxs, last, gpu_ins):
                 continue
             delta = float(np.max(np.abs(sb_g[t].astype(np.float64) - sb_o[t])))
             slack = 2.0 ** -22  # fp32 rounding of the scores
+            io, ig = ref["idx"][t], idxs[l][t]
+            if sorted(io.tolist()) == sorted(ig.tolist()):
+                # the same experts, two adjacent ranks swapped: their scores are
+                # within the movement; the output changes only by the order
+                # of the weighted sum, so the token stays in
+                sbo = sb_o[t].astype(np.float64)[io]
+                for k in np.flatnonzero(io != ig):
+                    near = [abs(sbo[k] - sbo[j]) for j in (k - 1, k + 1) if 0 <= j < len(io)]
+                    assert min(near) <= 2 * delta + slack, (l, t, "rank swap", io, ig, delta)
+                continue
             m = ref["margin"][t]
             assert m[0] <= 2 * delta + slack or m[1] <= 4 * delta + slack, \
                 (l, t, "selection flip with margins", m, "score moves", delta)
