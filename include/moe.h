@@ -315,6 +315,26 @@ int moe_layer_ptrs(const moe_cfg *cfg, int32_t T, const float *x, const float *w
                    const moe_layer_debug *dbg, void *stream);
 
 /* ---------------------------------------------------------------------------
+ * moe_layer_noalloc — moe_layer for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the workspace is a static device array inside the
+ * library, MOE_NOALLOC_SCRATCH_BYTES per device, held by each device that
+ * runs the library until the process ends; the call itself allocates
+ * nothing.  Same arguments as moe_layer without the workspace (and without
+ * debug dumps), same results bit for bit.  Every call on one device shares
+ * that device's array: calls that overlap on one device (two streams, two
+ * threads) race.  The first call on a device also looks up the array's
+ * device address there (once per device).
+ * Errors: as moe_layer; MOE_EWORKSPACE when moe_layer_workspace(cfg, T)
+ * exceeds MOE_NOALLOC_SCRATCH_BYTES (at the real shape, T <= 96 fits).
+ * ------------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int moe_layer_noalloc(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
+                      const float *bias, const void *experts, const void *shared,
+                      const float *residual, float *y, float *y_norm, float eps,
+                      int32_t *idx_out, float *w_out, const moe_events *ev, void *stream);
+
+/* ---------------------------------------------------------------------------
  * Expert cache (host runtime around moe_layer_ptrs) — "Show HN…", section
  * ディスクストリーミングベースの MoE 実行方式 (per-layer LRU cache and pinned hot
  * store for experts loaded on demand) and section Learning cache (usage of

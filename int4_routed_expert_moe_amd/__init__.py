@@ -23,7 +23,7 @@ MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 EXPORTS = (
     "moe_expert_blob_bytes", "moe_route_workspace", "moe_route", "moe_quant_act", "moe_group",
     "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_combine", "moe_rmsnorm",
-    "moe_layer_workspace", "moe_layer", "moe_layer_ptrs",
+    "moe_layer_workspace", "moe_layer", "moe_layer_ptrs", "moe_layer_noalloc",
     "moe_host_device_ptr", "moe_cache_create", "moe_cache_step", "moe_cache_get_stats",
     "moe_cache_usage", "moe_cache_slot_of", "moe_cache_destroy", "moe_cache_simulate",
     "moe_strerror", "moe_last_error",
@@ -119,6 +119,9 @@ def lib():
     L.moe_layer.restype = ctypes.c_int
     L.moe_layer_ptrs.argtypes = L.moe_layer.argtypes
     L.moe_layer_ptrs.restype = ctypes.c_int
+    L.moe_layer_noalloc.argtypes = [pc, i32, v, v, v, v, v, v, v, v, f32, v, v,
+                                    ctypes.POINTER(MoeEvents), v]
+    L.moe_layer_noalloc.restype = ctypes.c_int
     u64p, i32p = ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(ctypes.c_int32)
     L.moe_host_device_ptr.argtypes = [v, ctypes.POINTER(v)]
     L.moe_host_device_ptr.restype = ctypes.c_int
@@ -388,6 +391,27 @@ def layer_ptrs(cfg: Config, x, w_router, bias, expert_ptrs, shared=None, residua
                                 _ptr(y_norm), eps, _ptr(idx_out), _ptr(w_out), _ptr(ws),
                                 ws.numel(), ctypes.byref(events) if events is not None else None,
                                 ctypes.byref(dbg) if dbg is not None else None, _stream()))
+    return (y, y_norm) if want_norm else y
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def layer_noalloc(cfg: Config, x, w_router, bias, experts, shared=None, residual=None, y=None,
+                  y_norm=None, eps=1e-5, want_norm=False, idx_out=None, w_out=None, events=None):
+    """moe_layer_noalloc: as layer(), with the library's static device scratch
+    instead of a workspace (nothing is allocated by the call; y / y_norm are
+    created here only when not given)."""
+    torch = _torch()
+    T, H = x.shape
+    y = y if y is not None else torch.empty((T, H), dtype=torch.float32, device=x.device)
+    if want_norm and y_norm is None:
+        y_norm = torch.empty_like(y)
+    _check(lib().moe_layer_noalloc(ctypes.byref(cfg.c()), T, _ptr(x), _ptr(w_router),
+                                   _ptr(bias), _ptr(experts), _ptr(shared), _ptr(residual),
+                                   _ptr(y), _ptr(y_norm), eps, _ptr(idx_out), _ptr(w_out),
+                                   ctypes.byref(events) if events is not None else None,
+                                   _stream()))
     return (y, y_norm) if want_norm else y
 
 

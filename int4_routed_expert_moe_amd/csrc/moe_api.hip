@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
@@ -542,6 +544,76 @@ int moe_layer_ptrs(const moe_cfg *cfg, int32_t T, const float *x, const float *w
   if (!expert_ptrs) return fail(MOE_EINVAL, "expert_ptrs is NULL");
   return layer_impl(cfg, T, x, w_router, bias, nullptr, expert_ptrs, shared, residual, y, y_norm,
                     eps, idx_out, w_out, workspace, ws_bytes, ev, dbg, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- moe_layer_noalloc
+
+// The workspace of moe_layer_noalloc: one copy per device (each device that
+// runs the library holds its own until the process ends), shared by every
+// call on that device.  In host code `scratch` names a host-side stand-in,
+// not device memory: the device address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that address is
+// handed to kernels.  No call needs any of it zeroed (every byte a call
+// reads it wrote earlier in the same call).
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of the scratch array on the device of `st` (the current
+// device for the null stream).
+int scratch_of(hipStream_t st, void **out) {
+  int dev = -1;
+  hipError_t e = st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_EHIP, "device of the stream: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EINVAL, "device %d out of range", dev);
+  std::call_once(g_scratch_once[dev], [dev] {
+    int cur = -1;
+    hipError_t r = hipGetDevice(&cur);
+    if (r == hipSuccess && cur != dev) r = hipSetDevice(dev);
+    void *p = nullptr;
+    if (r == hipSuccess) r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+    g_scratch_ptr[dev] = p;
+    g_scratch_err[dev] = r;
+  });
+  if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev])
+    return fail(MOE_EHIP, "scratch of device %d: %s", dev,
+                hipGetErrorString(g_scratch_err[dev] != hipSuccess ? g_scratch_err[dev]
+                                                                    : hipErrorInvalidSymbol));
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_layer_noalloc(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
+                      const float *bias, const void *experts, const void *shared,
+                      const float *residual, float *y, float *y_norm, float eps,
+                      int32_t *idx_out, float *w_out, const moe_events *ev, void *stream) {
+  int rc = check_cfg(cfg);
+  if (rc) return rc;
+  if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
+  if (T == 0) return MOE_OK;
+  const size_t need = moe_layer_workspace(cfg, T);
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_EWORKSPACE,
+                "moe_layer_noalloc: %d tokens need %zu bytes of workspace, more than its %u-byte "
+                "scratch (use moe_layer with a workspace)",
+                T, need, (unsigned)MOE_NOALLOC_SCRATCH_BYTES);
+  if (!experts) return fail(MOE_EINVAL, "experts is NULL");
+  void *ws = nullptr;
+  if ((rc = scratch_of((hipStream_t)stream, &ws))) return rc;
+  return layer_impl(cfg, T, x, w_router, bias, experts, nullptr, shared, residual, y, y_norm, eps,
+                    idx_out, w_out, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, ev, nullptr, stream);
 }
 
 const char *moe_strerror(int code) {

@@ -167,6 +167,22 @@ def test_combine_and_layer_errors(L):
                None, ctypes.byref(mis), None) == moe.MOE_EALIGN
 
 
+def test_layer_noalloc_rejects_batches_beyond_its_scratch(L):
+    """The static scratch holds moe_layer's workspace up to its size; a larger
+    batch fails with MOE_EWORKSPACE before anything touches a device."""
+    c = REAL.c()
+    assert moe.layer_workspace(REAL, 96) <= moe.NOALLOC_SCRATCH_BYTES
+    big = 4096
+    assert moe.layer_workspace(REAL, big) > moe.NOALLOC_SCRATCH_BYTES
+    assert L.moe_layer_noalloc(ctypes.byref(c), big, A, A, A, A, A, None, A, None, 1e-5, None,
+                               None, None, None) == moe.MOE_EWORKSPACE
+    assert b"scratch" in L.moe_last_error()
+    assert L.moe_layer_noalloc(ctypes.byref(c), -1, A, A, A, A, A, None, A, None, 1e-5, None,
+                               None, None, None) == moe.MOE_EINVAL
+    assert L.moe_layer_noalloc(ctypes.byref(c), 0, None, None, None, None, None, None, None,
+                               None, 1e-5, None, None, None, None) == moe.MOE_OK
+
+
 def test_strerror(L):
     for code in (0, -1, -2, -3, -4):
         assert L.moe_strerror(code)
