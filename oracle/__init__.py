@@ -27,6 +27,7 @@ _lib = None
 
 
 MXFP4 = -4  # weight-format code of MXFP4 experts (reading R16)
+ACT_Q8_0, ACT_ROW = 32, -1  # activation formats: Q8_0 blocks of 32 (R6), one scale per row (R17)
 
 def build() -> str:
     """Compile oracle.c into liboracle.so (gcc, plain C11, no fp contraction)."""
@@ -59,6 +60,16 @@ def lib():
     L.oracle_pack.restype = c_i
     L.oracle_q8_0.argtypes = [c_v, ctypes.c_int64, c_i, c_v, c_v]
     L.oracle_q8_0.restype = c_i
+    L.oracle_quant_act.argtypes = [c_v, ctypes.c_int64, c_i, c_i, c_v, c_v]
+    L.oracle_quant_act.restype = c_i
+    L.oracle_act_dots.argtypes = [c_v, c_i, c_v, c_i, c_i, c_v]
+    L.oracle_act_dots.restype = c_i
+    L.oracle_gate_up_act.argtypes = [c_v, c_i, c_i, c_i, c_i, c_v, c_v, c_v, c_v, c_v, c_v, c_v]
+    L.oracle_gate_up_act.restype = c_i
+    L.oracle_down_act.argtypes = [c_v, c_i, c_i, c_i, c_i, c_v, c_v, c_v, c_v]
+    L.oracle_down_act.restype = c_i
+    L.oracle_expert_act.argtypes = [c_v, c_i, c_i, c_i, c_i, c_v, c_v, c_v, c_v, c_v, c_v]
+    L.oracle_expert_act.restype = c_i
     L.oracle_dot_canon.argtypes = [c_v, c_v, c_i]
     L.oracle_dot_canon.restype = c_f
     L.oracle_exp_canon.argtypes = [c_f]
@@ -152,6 +163,22 @@ def q8_0(x: np.ndarray):
     q = np.empty(x.shape, np.int8)
     d = np.empty(x.shape[:-1] + (n // QBLK,), np.float32)
     _check(lib().oracle_q8_0(_ptr(x), rows, n, _ptr(q), _ptr(d)), "q8_0")
+    return q, d
+
+
+def act_len(act_block: int, n: int) -> int:
+    """Activation block length of a format on rows of n values."""
+    return n if act_block == ACT_ROW else act_block
+
+
+def quant_act(x: np.ndarray, act_block: int = ACT_Q8_0):
+    """Activations of each row in format act_block (R6 Q8_0 or R17 one scale
+    per row): (int8 codes, fp32 scales [..., n / block])."""
+    x = _c(x, np.float32)
+    rows, n = (1, x.size) if x.ndim == 1 else (int(np.prod(x.shape[:-1])), x.shape[-1])
+    q = np.empty(x.shape, np.int8)
+    d = np.empty(x.shape[:-1] + (n // act_len(act_block, n),), np.float32)
+    _check(lib().oracle_quant_act(_ptr(x), rows, n, act_block, _ptr(q), _ptr(d)), "quant_act")
     return q, d
 
 
@@ -287,38 +314,50 @@ def block_dots(row, wbits, q):
     return out
 
 
-def gate_up(blob, H, I, wbits, q, d, want_dots=False):
-    """One token through gate/up + SwiGLU: dict(h fp32 [I], g, u fp64 [I], dots)."""
+def act_dots(row, wbits, q, act_block=ACT_Q8_0):
+    """Exact int32 dots of a packed weight row with int8 activations, one per
+    activation block of the format."""
+    row, q = _c(row, np.uint8), _c(q, np.int8)
+    out = np.empty(q.size // act_len(act_block, q.size), np.int32)
+    _check(lib().oracle_act_dots(_ptr(row), wbits, _ptr(q), q.size, act_block, _ptr(out)),
+           "act_dots")
+    return out
+
+
+def gate_up(blob, H, I, wbits, q, d, want_dots=False, act_block=ACT_Q8_0):
+    """One token through gate/up + SwiGLU: dict(h fp32 [I], g, u fp64 [I], dots
+    [I][H / block])."""
     blob, q, d = _c(blob, np.uint8), _c(q, np.int8), _c(d, np.float32)
+    nb = H // act_len(act_block, H)
     h = np.empty(I, np.float32)
     g = np.empty(I, np.float64)
     u = np.empty(I, np.float64)
-    gd = np.empty((I, H // QBLK), np.int32) if want_dots else None
-    ud = np.empty((I, H // QBLK), np.int32) if want_dots else None
-    _check(lib().oracle_gate_up(_ptr(blob), H, I, wbits, _ptr(q), _ptr(d), _ptr(gd), _ptr(ud),
-                                _ptr(g), _ptr(u), _ptr(h)), "gate_up")
+    gd = np.empty((I, nb), np.int32) if want_dots else None
+    ud = np.empty((I, nb), np.int32) if want_dots else None
+    _check(lib().oracle_gate_up_act(_ptr(blob), H, I, wbits, act_block, _ptr(q), _ptr(d),
+                                    _ptr(gd), _ptr(ud), _ptr(g), _ptr(u), _ptr(h)), "gate_up")
     return dict(h=h, g=g, u=u, gate_dots=gd, up_dots=ud)
 
 
-def down(blob, H, I, wbits, qh, dh, want_dots=False):
-    """One token through the down matrix: (y fp32 [H], dots [H][I/32] or None)."""
+def down(blob, H, I, wbits, qh, dh, want_dots=False, act_block=ACT_Q8_0):
+    """One token through the down matrix: (y fp32 [H], dots [H][I / block] or None)."""
     blob, qh, dh = _c(blob, np.uint8), _c(qh, np.int8), _c(dh, np.float32)
     y = np.empty(H, np.float32)
-    dd = np.empty((H, I // QBLK), np.int32) if want_dots else None
-    _check(lib().oracle_down(_ptr(blob), H, I, wbits, _ptr(qh), _ptr(dh), _ptr(dd), _ptr(y)),
-           "down")
+    dd = np.empty((H, I // act_len(act_block, I)), np.int32) if want_dots else None
+    _check(lib().oracle_down_act(_ptr(blob), H, I, wbits, act_block, _ptr(qh), _ptr(dh),
+                                 _ptr(dd), _ptr(y)), "down")
     return y, dd
 
 
-def expert(blob, H, I, wbits, q, d):
+def expert(blob, H, I, wbits, q, d, act_block=ACT_Q8_0):
     """One token through a whole expert: dict(h, qh, dh, y)."""
     blob, q, d = _c(blob, np.uint8), _c(q, np.int8), _c(d, np.float32)
     h = np.empty(I, np.float32)
     qh = np.empty(I, np.int8)
-    dh = np.empty(I // QBLK, np.float32)
+    dh = np.empty(I // act_len(act_block, I), np.float32)
     y = np.empty(H, np.float32)
-    _check(lib().oracle_expert(_ptr(blob), H, I, wbits, _ptr(q), _ptr(d), _ptr(h), _ptr(qh),
-                               _ptr(dh), _ptr(y)), "expert")
+    _check(lib().oracle_expert_act(_ptr(blob), H, I, wbits, act_block, _ptr(q), _ptr(d), _ptr(h),
+                                   _ptr(qh), _ptr(dh), _ptr(y)), "expert")
     return dict(h=h, qh=qh, dh=dh, y=y)
 
 
@@ -347,8 +386,10 @@ def rmsnorm(x, eps=1e-5):
 # ------------------------------------------------------------------ whole layer
 
 def layer(x, router_w, bias, blob_of, shared_blob, *, H, I, n_experts, n_group, topk_group,
-          top_k, scale, wbits=4, residual=None, want_norm=False, eps=1e-5, top_p_value=0.0):
-    """One routed-MoE layer for T tokens, step by step.
+          top_k, scale, wbits=4, residual=None, want_norm=False, eps=1e-5, top_p_value=0.0,
+          act_block=ACT_Q8_0):
+    """One routed-MoE layer for T tokens, step by step (activations of x and h
+    in format act_block: Q8_0, or one scale per row, R17).
 
     ``blob_of(e)`` returns the packed record of routed expert ``e`` (only the
     experts the router selects are requested); ``shared_blob`` may be None.
@@ -358,7 +399,7 @@ def layer(x, router_w, bias, blob_of, shared_blob, *, H, I, n_experts, n_group, 
     x = _c(x, np.float32)
     T = x.shape[0]
     idx, w, margin = route(x, router_w, bias, n_group, topk_group, top_k, scale, top_p_value)
-    q, d = q8_0(x)
+    q, d = quant_act(x, act_block)
     groups = group(idx, n_experts)
     expert_out = np.zeros((T, top_k, H), np.float32)
     for e in groups["active"][: groups["n_active"]]:
@@ -366,10 +407,10 @@ def layer(x, router_w, bias, blob_of, shared_blob, *, H, I, n_experts, n_group, 
         lo, hi = groups["offsets"][e], groups["offsets"][e + 1]
         for slot in groups["perm"][lo:hi]:
             t, k = divmod(int(slot), top_k)
-            expert_out[t, k] = expert(blob, H, I, wbits, q[t], d[t])["y"]
+            expert_out[t, k] = expert(blob, H, I, wbits, q[t], d[t], act_block)["y"]
     shared_out = None
     if shared_blob is not None:
-        shared_out = np.stack([expert(shared_blob, H, I, wbits, q[t], d[t])["y"]
+        shared_out = np.stack([expert(shared_blob, H, I, wbits, q[t], d[t], act_block)["y"]
                                for t in range(T)])
     res = combine(expert_out, w, shared_out, residual, eps, want_norm)
     y, yn = res if want_norm else (res, None)

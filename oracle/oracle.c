@@ -65,6 +65,16 @@
  *     w_k = (s_k / S_kept) * routed_scaling; a dropped rank has idx -1 and
  *     w 0 and is read by no later step.
  *
+ *  R17 per-row activation scales (declared format beside Q8_0; activation
+ *     block "row", ablk = -1 below): the pages' integer kernels take Q8_0
+ *     blocks of 32; this second format applies the R6 rule to a whole
+ *     activation row at once -- one fp32 scale d = amax(row)/127 per token
+ *     row of x (H values) and per (token, expert) row of h (I values),
+ *     q = clamp(roundf(x * (1/d)), -127, 127) -- so that an output row is
+ *     scale_r * d * P with P the exact integer dot over the whole row
+ *     (|P| <= 6144 * 128 * 127 < 2^31 at the real shape).  Integer codes
+ *     only (MXFP4 keeps its per-32 weight scales, hence Q8_0 blocks).
+ *
  * Precision: router fp32 (R5); Q8_0 decisions fp32; block dots exact in
  * int64 (checked to fit int32); the float epilogues in fp64, rounded to fp32.
  */
@@ -146,28 +156,39 @@ int oracle_pack(const int8_t *codes, int n, int wbits, uint8_t *out) {
 
 /* ---------------------------------------------------------------- Q8_0 */
 
-/* R6, [HN] integer-dot item: rows x rows of n floats -> int8 codes and one
- * fp32 scale per block of 32. */
-int oracle_q8_0(const float *x, int64_t rows, int n, int8_t *q, float *d) {
-  if (n % QBLK) return -1;
-  const int nb = n / QBLK;
+/* Activation block length of format ablk on a row of n values: Q8_0 (32)
+ * or the whole row (R17, ablk = -1); 0 if ablk is neither. */
+static int act_len(int ablk, int n) { return ablk == -1 ? n : ablk == QBLK ? QBLK : 0; }
+
+/* R6 (and R17 with ablk = -1), [HN] integer-dot item: rows x rows of n
+ * floats -> int8 codes and one fp32 scale per block of the format:
+ * d = amax/127, q = clamp(roundf(x * (1/d)), -127, 127). */
+int oracle_quant_act(const float *x, int64_t rows, int n, int ablk, int8_t *q, float *d) {
+  const int B = act_len(ablk, n);
+  if (B <= 0 || n % B) return -1;
+  const int nb = n / B;
   for (int64_t r = 0; r < rows; r++) {
     for (int b = 0; b < nb; b++) {
-      const float *xb = x + r * n + b * QBLK;
+      const float *xb = x + r * n + (int64_t)b * B;
       float amax = 0.0f;
-      for (int k = 0; k < QBLK; k++) amax = fmaxf(amax, fabsf(xb[k]));
+      for (int k = 0; k < B; k++) amax = fmaxf(amax, fabsf(xb[k]));
       float dd = amax / 127.0f;
       float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
       d[r * nb + b] = dd;
-      for (int k = 0; k < QBLK; k++) {
+      for (int k = 0; k < B; k++) {
         float v = roundf(xb[k] * id);
         if (v > 127.0f) v = 127.0f;
         if (v < -127.0f) v = -127.0f;
-        q[r * n + b * QBLK + k] = (int8_t)v;
+        q[r * n + (int64_t)b * B + k] = (int8_t)v;
       }
     }
   }
   return 0;
+}
+
+/* R6: Q8_0, blocks of 32. */
+int oracle_q8_0(const float *x, int64_t rows, int n, int8_t *q, float *d) {
+  return oracle_quant_act(x, rows, n, QBLK, q, d);
 }
 
 /* ---------------------------------------------------------------- router */
@@ -390,12 +411,16 @@ int oracle_group(int T, int K, int E, const int32_t *idx, int32_t *counts,
 
 /* ---------------------------------------------------------------- expert FFN */
 
-/* Exact integer dot of each 32-block of a packed weight row with int8
- * activations ([HN] integer-dot and quantisation items). */
-int oracle_block_dots(const uint8_t *row, int wbits, const int8_t *q, int n, int32_t *out) {
-  for (int b = 0; b < n / QBLK; b++) {
+/* Exact integer dot of each activation block (32 values, or the whole row
+ * for R17) of a packed weight row with int8 activations ([HN] integer-dot
+ * and quantisation items). */
+int oracle_act_dots(const uint8_t *row, int wbits, const int8_t *q, int n, int ablk,
+                    int32_t *out) {
+  const int B = act_len(ablk, n);
+  if (B <= 0 || n % B || (wbits == ORACLE_MXFP4 && B != QBLK)) return -1;
+  for (int b = 0; b < n / B; b++) {
     int64_t acc = 0;
-    for (int k = b * QBLK; k < (b + 1) * QBLK; k++) {
+    for (int k = b * B; k < (b + 1) * B; k++) {
       const int c = oracle_code(row, wbits, k);
       const int64_t wv = wbits == ORACLE_MXFP4 ? (int64_t)(2.0 * oracle_fp4_value(c)) : c;
       acc += wv * (int64_t)q[k];
@@ -404,6 +429,10 @@ int oracle_block_dots(const uint8_t *row, int wbits, const int8_t *q, int n, int
     out[b] = (int32_t)acc;
   }
   return 0;
+}
+
+int oracle_block_dots(const uint8_t *row, int wbits, const int8_t *q, int n, int32_t *out) {
+  return oracle_act_dots(row, wbits, q, n, QBLK, out);
 }
 
 size_t oracle_blob_bytes(int H, int I, int wbits) {
@@ -444,50 +473,61 @@ static blob_view view_of(const uint8_t *blob, int H, int I, int wbits) {
   return v;
 }
 
-/* fp64 value of one output row (dequantise on use): integer codes
- * scale_r * sum_b d_b * P_b; MXFP4 (bsc: the row's block scales)
+/* fp64 value of one output row (dequantise on use), activation blocks of
+ * the format ablk (nb = n / block length of them): integer codes
+ * scale_r * sum_b d_b * P_b; MXFP4 (bsc: the row's block scales, Q8_0 only)
  * sum_b 2^(s_b-127) * d_b * P2_b / 2. */
-static double row_value(const uint8_t *row, int wbits, float scale, const uint8_t *bsc,
-                        const int8_t *q, const float *d, int n, int32_t *dots_out, int *err) {
+static double row_value(const uint8_t *row, int wbits, int ablk, float scale,
+                        const uint8_t *bsc, const int8_t *q, const float *d, int n,
+                        int32_t *dots_out, int *err) {
+  const int B = act_len(ablk, n);
+  if (B <= 0) {
+    *err = 1;
+    return 0.0;
+  }
+  const int nb = n / B;
   int32_t P[QBLK * 16];
   int32_t *dots = dots_out;
   int32_t *tmp = NULL;
   if (!dots) {
-    if (n / QBLK <= (int)(sizeof(P) / sizeof(P[0]))) dots = P;
-    else dots = tmp = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n / QBLK));
+    if (nb <= (int)(sizeof(P) / sizeof(P[0]))) dots = P;
+    else dots = tmp = (int32_t *)malloc(sizeof(int32_t) * (size_t)nb);
   }
-  if (oracle_block_dots(row, wbits, q, n, dots)) *err = 1;
+  if (oracle_act_dots(row, wbits, q, n, ablk, dots)) *err = 1;
   double acc = 0.0;
   if (bsc) {
-    for (int b = 0; b < n / QBLK; b++)
+    for (int b = 0; b < nb; b++)
       acc += oracle_e8m0_value(bsc[b]) * (double)d[b] * (0.5 * (double)dots[b]);
     free(tmp);
     return acc;
   }
-  for (int b = 0; b < n / QBLK; b++) acc += (double)d[b] * (double)dots[b];
+  for (int b = 0; b < nb; b++) acc += (double)d[b] * (double)dots[b];
   free(tmp);
   return (double)scale * acc;
 }
 
-/* Gate and up projections plus SwiGLU for one token (R8).  q, d: Q8_0 of the
- * token's hidden state (H values).  Outputs (each nullable): gate_dots and
- * up_dots [I][H/32] int32, g and u [I] fp64, h [I] fp32 = fp32(silu(g) * u). */
-int oracle_gate_up(const uint8_t *blob, int H, int I, int wbits, const int8_t *q,
-                   const float *d, int32_t *gate_dots, int32_t *up_dots, double *g_out,
-                   double *u_out, float *h) {
-  if (H % QBLK || I % QBLK) return -1;
+/* Gate and up projections plus SwiGLU for one token (R8), activations in
+ * format ablk (Q8_0: 32; R17 rows: -1).  q, d: the token's activations (H
+ * values; d one scale per block).  Outputs (each nullable): gate_dots and
+ * up_dots [I][H/block] int32, g and u [I] fp64, h [I] fp32 =
+ * fp32(silu(g) * u). */
+int oracle_gate_up_act(const uint8_t *blob, int H, int I, int wbits, int ablk, const int8_t *q,
+                       const float *d, int32_t *gate_dots, int32_t *up_dots, double *g_out,
+                       double *u_out, float *h) {
+  const int B = act_len(ablk, H);
+  if (H % QBLK || I % QBLK || B <= 0) return -1;
   blob_view v = view_of(blob, H, I, wbits);
   int err = 0;
 #pragma omp parallel for schedule(static) reduction(| : err)
   for (int r = 0; r < I; r++) {
     int e1 = 0;
     const int mx = wbits == ORACLE_MXFP4;
-    double g = row_value(v.gate + r * v.gate_row, wbits, mx ? 1.0f : v.sg[r],
+    double g = row_value(v.gate + r * v.gate_row, wbits, ablk, mx ? 1.0f : v.sg[r],
                          mx ? v.bg + (size_t)r * (H / QBLK) : NULL, q, d, H,
-                         gate_dots ? gate_dots + (size_t)r * (H / QBLK) : NULL, &e1);
-    double u = row_value(v.up + r * v.gate_row, wbits, mx ? 1.0f : v.su[r],
+                         gate_dots ? gate_dots + (size_t)r * (H / B) : NULL, &e1);
+    double u = row_value(v.up + r * v.gate_row, wbits, ablk, mx ? 1.0f : v.su[r],
                          mx ? v.bu + (size_t)r * (H / QBLK) : NULL, q, d, H,
-                         up_dots ? up_dots + (size_t)r * (H / QBLK) : NULL, &e1);
+                         up_dots ? up_dots + (size_t)r * (H / B) : NULL, &e1);
     double silu = g / (1.0 + exp(-g));
     if (g_out) g_out[r] = g;
     if (u_out) u_out[r] = u;
@@ -497,43 +537,64 @@ int oracle_gate_up(const uint8_t *blob, int H, int I, int wbits, const int8_t *q
   return err ? -1 : 0;
 }
 
-/* Down projection for one token: qh, dh = Q8_0 of h (I values).  Outputs
- * (nullable): down_dots [H][I/32] int32, y [H] fp32. */
-int oracle_down(const uint8_t *blob, int H, int I, int wbits, const int8_t *qh,
-                const float *dh, int32_t *down_dots, float *y) {
-  if (H % QBLK || I % QBLK) return -1;
+int oracle_gate_up(const uint8_t *blob, int H, int I, int wbits, const int8_t *q,
+                   const float *d, int32_t *gate_dots, int32_t *up_dots, double *g_out,
+                   double *u_out, float *h) {
+  return oracle_gate_up_act(blob, H, I, wbits, QBLK, q, d, gate_dots, up_dots, g_out, u_out, h);
+}
+
+/* Down projection for one token, activations (qh, dh: h of I values) in
+ * format ablk.  Outputs (nullable): down_dots [H][I/block] int32, y [H]
+ * fp32. */
+int oracle_down_act(const uint8_t *blob, int H, int I, int wbits, int ablk, const int8_t *qh,
+                    const float *dh, int32_t *down_dots, float *y) {
+  const int B = act_len(ablk, I);
+  if (H % QBLK || I % QBLK || B <= 0) return -1;
   blob_view v = view_of(blob, H, I, wbits);
   int err = 0;
 #pragma omp parallel for schedule(static) reduction(| : err)
   for (int j = 0; j < H; j++) {
     int e1 = 0;
     const int mx = wbits == ORACLE_MXFP4;
-    double val = row_value(v.down + j * v.down_row, wbits, mx ? 1.0f : v.sd[j],
+    double val = row_value(v.down + j * v.down_row, wbits, ablk, mx ? 1.0f : v.sd[j],
                            mx ? v.bd + (size_t)j * (I / QBLK) : NULL, qh, dh, I,
-                           down_dots ? down_dots + (size_t)j * (I / QBLK) : NULL, &e1);
+                           down_dots ? down_dots + (size_t)j * (I / B) : NULL, &e1);
     if (y) y[j] = (float)val;
     err |= e1;
   }
   return err ? -1 : 0;
 }
 
-/* Whole expert for one token: gate/up, SwiGLU, Q8_0 of h (R7), down.
- * h, qh, dh nullable (intermediates for inspection); y [H] required. */
-int oracle_expert(const uint8_t *blob, int H, int I, int wbits, const int8_t *q,
-                  const float *d, float *h_out, int8_t *qh_out, float *dh_out, float *y) {
+int oracle_down(const uint8_t *blob, int H, int I, int wbits, const int8_t *qh,
+                const float *dh, int32_t *down_dots, float *y) {
+  return oracle_down_act(blob, H, I, wbits, QBLK, qh, dh, down_dots, y);
+}
+
+/* Whole expert for one token: gate/up, SwiGLU, quantisation of h in the same
+ * activation format (R7, R17), down.  h, qh, dh nullable (intermediates for
+ * inspection; dh has I/block entries); y [H] required. */
+int oracle_expert_act(const uint8_t *blob, int H, int I, int wbits, int ablk, const int8_t *q,
+                      const float *d, float *h_out, int8_t *qh_out, float *dh_out, float *y) {
+  const int B = act_len(ablk, I);
+  if (B <= 0) return -1;
   float *h = (float *)malloc(sizeof(float) * I);
   int8_t *qh = (int8_t *)malloc((size_t)I);
-  float *dh = (float *)malloc(sizeof(float) * (I / QBLK));
-  int rc = oracle_gate_up(blob, H, I, wbits, q, d, NULL, NULL, NULL, NULL, h);
-  if (!rc) rc = oracle_q8_0(h, 1, I, qh, dh);
-  if (!rc) rc = oracle_down(blob, H, I, wbits, qh, dh, NULL, y);
+  float *dh = (float *)malloc(sizeof(float) * (I / B));
+  int rc = oracle_gate_up_act(blob, H, I, wbits, ablk, q, d, NULL, NULL, NULL, NULL, h);
+  if (!rc) rc = oracle_quant_act(h, 1, I, ablk, qh, dh);
+  if (!rc) rc = oracle_down_act(blob, H, I, wbits, ablk, qh, dh, NULL, y);
   if (h_out) memcpy(h_out, h, sizeof(float) * I);
   if (qh_out) memcpy(qh_out, qh, (size_t)I);
-  if (dh_out) memcpy(dh_out, dh, sizeof(float) * (I / QBLK));
+  if (dh_out) memcpy(dh_out, dh, sizeof(float) * (I / B));
   free(h);
   free(qh);
   free(dh);
   return rc;
+}
+
+int oracle_expert(const uint8_t *blob, int H, int I, int wbits, const int8_t *q,
+                  const float *d, float *h_out, int8_t *qh_out, float *dh_out, float *y) {
+  return oracle_expert_act(blob, H, I, wbits, QBLK, q, d, h_out, qh_out, dh_out, y);
 }
 
 /* ---------------------------------------------------------------- combine */

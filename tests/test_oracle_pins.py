@@ -748,3 +748,141 @@ def test_mx_grid_exact_dots():
     ref = oracle.gate_up(blob, H, I, MX, q[0], d[0], want_dots=True)
     fp4 = np.array([oracle.fp4_value(c) for c in range(16)])
     assert np.array_equal(ref["g"], fp4[codes] @ x[0].astype(np.float64))
+
+
+# ------------------------------------------------------------------ per-row activations (R17)
+
+ROW = oracle.ACT_ROW
+
+
+def test_quant_rows_hand_case():
+    """Worked by hand: a row of 64 whose amax is 254 has d = 254/127 = 2 and
+    id = 0.5; codes are roundf(x/2), halves away from zero, clamped."""
+    x = np.zeros(64, np.float32)
+    x[:8] = [254.0, -254.0, 1.0, -1.0, 3.0, -5.0, 0.99, 100.5]
+    q, d = oracle.quant_act(x, ROW)
+    assert d.tolist() == [2.0]
+    assert q[:8].tolist() == [127, -127, 1, -1, 2, -3, 0, 50]
+    assert not q[8:].any()
+
+
+def test_quant_rows_invariants():
+    rng = np.random.default_rng(21)
+    for n in (64, 2048, 6144):
+        x = (rng.standard_normal((8, n)) * np.exp2(rng.integers(-20, 20, (8, 1)))).astype(np.float32)
+        x[3] = 0.0
+        q, d = oracle.quant_act(x, ROW)
+        assert d.shape == (8, 1)
+        assert np.all(np.abs(q.astype(np.int32)) <= 127)
+        for r in range(8):
+            if r == 3:
+                assert d[r, 0] == 0 and not q[r].any()
+                continue
+            assert np.abs(q[r].astype(np.int32)).max() == 127
+            err = np.abs(x[r].astype(np.float64) - q[r] * np.float64(d[r, 0]))
+            assert err.max() <= d[r, 0] / 2 * (1 + 2.0 ** -22)
+
+
+def test_quant_rows_integer_grid_is_exact():
+    rng = np.random.default_rng(22)
+    x = rng.integers(-127, 128, (4, 2048)).astype(np.float32)
+    x[:, 5] = 127.0
+    q, d = oracle.quant_act(x, ROW)
+    assert np.all(d == 1.0) and np.array_equal(q, x.astype(np.int8))
+
+
+def test_quant_rows_of_32_is_q8_0():
+    """A row of 32 values is one Q8_0 block: both formats give the same bits."""
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((50, 32)) * 3).astype(np.float32)
+    assert all(np.array_equal(a, b) for a, b in zip(oracle.quant_act(x, ROW), oracle.q8_0(x)))
+
+
+@pytest.mark.parametrize("wbits", [4, 8, 2])
+def test_row_dots_are_sums_of_block_dots(wbits):
+    """The whole-row integer dot is the sum of the pinned 32-block dots and the
+    int64 brute force (no int32 overflow at the real width, extreme codes)."""
+    rng = np.random.default_rng(24 + wbits)
+    lo, hi = -(1 << (wbits - 1)), (1 << (wbits - 1)) - 1
+    for n in (256, 6144):
+        codes = rng.integers(lo, hi + 1, n).astype(np.int8)
+        codes[:n // 2] = lo  # the largest magnitude
+        q = rng.integers(-127, 128, n).astype(np.int8)
+        q[:n // 2] = -127
+        row = oracle.pack(codes, wbits)
+        p_row = oracle.act_dots(row, wbits, q, ROW)
+        assert p_row.shape == (1,)
+        assert int(p_row[0]) == int(oracle.block_dots(row, wbits, q).astype(np.int64).sum())
+        assert int(p_row[0]) == int(codes.astype(np.int64) @ q.astype(np.int64))
+
+
+@pytest.mark.parametrize("wbits", [4, 8])
+def test_row_format_gate_up_and_down_equal_dequantised_matmul(wbits):
+    """g = s_r * d * P_row equals the fp64 product of the dequantised weights
+    and activations (algebraic identity), as does the down projection."""
+    shape = synth.TINY.with_bits(wbits)
+    H, I = shape.hidden, shape.inter
+    blob = synth.expert_blob(shape, 31, 0, 2)
+    gate, up, down, sg, su, sd = oracle.blob_view(blob, H, I, wbits)
+    x = synth.tokens(shape, 31, 1)[0]
+    q, d = oracle.quant_act(x, ROW)
+    xv = q.astype(np.float64) * np.float64(d[0])
+    r = oracle.gate_up(blob, H, I, wbits, q, d, want_dots=True, act_block=ROW)
+    Wg = np.stack([oracle.unpack(gate[i], wbits, H) for i in range(I)]).astype(np.float64)
+    Wu = np.stack([oracle.unpack(up[i], wbits, H) for i in range(I)]).astype(np.float64)
+    g_ref = (Wg * sg[:, None].astype(np.float64)) @ xv
+    u_ref = (Wu * su[:, None].astype(np.float64)) @ xv
+    assert np.allclose(r["g"], g_ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(r["u"], u_ref, rtol=1e-12, atol=1e-12)
+    assert r["gate_dots"].shape == (I, 1)
+    assert np.array_equal(r["gate_dots"][:, 0], (Wg @ q.astype(np.float64)).astype(np.int64))
+    qh, dh = oracle.quant_act(r["h"], ROW)
+    y, dd = oracle.down(blob, H, I, wbits, qh, dh, want_dots=True, act_block=ROW)
+    Wd = np.stack([oracle.unpack(down[j], wbits, I) for j in range(H)]).astype(np.float64)
+    y_ref = (Wd * sd[:, None].astype(np.float64)) @ (qh.astype(np.float64) * np.float64(dh[0]))
+    assert np.allclose(y, y_ref.astype(np.float32), rtol=1e-6, atol=1e-7)
+    assert np.array_equal(dd[:, 0], (Wd @ qh.astype(np.float64)).astype(np.int64))
+
+
+def test_formats_agree_when_every_block_holds_the_row_max():
+    """If every 32-block of a row reaches the row's amax, Q8_0 and the per-row
+    format give the same codes and scales, and the same gate/up values."""
+    shape = synth.TINY
+    H, I = shape.hidden, shape.inter
+    rng = np.random.default_rng(25)
+    x = (rng.standard_normal(H) * 0.3).astype(np.float32)
+    x[::32] = np.where(rng.integers(0, 2, H // 32) == 1, 1.75, -1.75)
+    qb, db = oracle.q8_0(x)
+    qr, dr = oracle.quant_act(x, ROW)
+    assert np.array_equal(qb, qr) and np.all(db == dr[0])
+    blob = synth.expert_blob(shape, 32, 0, 1)
+    a = oracle.gate_up(blob, H, I, 4, qb, db)
+    b = oracle.gate_up(blob, H, I, 4, qr, dr, act_block=ROW)
+    assert np.allclose(a["g"], b["g"], rtol=1e-13, atol=1e-13)
+    assert np.allclose(a["u"], b["u"], rtol=1e-13, atol=1e-13)
+
+
+def test_layer_row_format_identical_experts_closed_form():
+    """All routed experts identical -> y = shared(x) + 2.5 * expert(x), in the
+    per-row format too."""
+    shape = synth.TINY
+    blob = synth.expert_blob(shape, 100, 0, 0)
+    shared = synth.expert_blob(shape, 100, 0, synth.SHARED_ID)
+    x = synth.tokens(shape, 100, 4)
+    out = oracle.layer(x, synth.router_weights(shape, 100), synth.router_bias_uniform(shape, 100),
+                       lambda e: blob, shared, H=256, I=128, n_experts=8, n_group=2,
+                       topk_group=1, top_k=2, scale=2.5, act_block=ROW)
+    assert out["d"].shape == (4, 1)
+    for t in range(4):
+        e_y = oracle.expert(blob, 256, 128, 4, out["q"][t], out["d"][t], ROW)["y"]
+        ref = out["shared_out"][t].astype(np.float64) + 2.5 * e_y.astype(np.float64)
+        assert np.max(np.abs(out["y"][t] - ref)) <= 1e-6 * np.sqrt(np.mean(ref ** 2)) + 1e-7
+
+
+def test_row_format_rejects_mxfp4():
+    """MXFP4 keeps per-32 weight scales: only Q8_0 activations pair with it."""
+    shape = synth.TINY.with_bits(synth.MXFP4)
+    blob = synth.expert_blob(shape, 3, 0, 0)
+    q, d = oracle.quant_act(synth.tokens(shape, 3, 1)[0], ROW)
+    with pytest.raises(ValueError):
+        oracle.gate_up(blob, 256, 128, oracle.MXFP4, q, d, act_block=ROW)
