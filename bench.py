@@ -144,6 +144,17 @@ def gate_up_bytes(shape, T, U, small):
     return (U + S) * per_expert + x_in + (T * K + T * S) * I * 4
 
 
+# the sources of the small-batch kernels whose counters profiles/ records
+TRAFFIC_SOURCES = ("decode.h", "decode.hip", "common.h", "kernels.h")
+
+
+def sources_sha256():
+    import hashlib
+    csrc = os.path.join(ROOT, "int4_routed_expert_moe_amd", "csrc")
+    return hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read()
+                                   for f in TRAFFIC_SOURCES)).hexdigest()
+
+
 def measured_traffic(workload):
     """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, calibrated), or None when the
@@ -157,10 +168,7 @@ def measured_traffic(workload):
                   r"bytes_per_launch=(\d+) -->", open(path).read())
     if not m or m.group(1) != workload:
         return None
-    csrc = os.path.join(ROOT, "int4_routed_expert_moe_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, f), "rb").read()
-                   for f in ("decode.hip", "common.h", "kernels.h"))
-    if hashlib.sha256(src).hexdigest() != m.group(2):
+    if sources_sha256() != m.group(2):
         return None
     return float(m.group(3))
 

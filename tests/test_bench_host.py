@@ -32,8 +32,9 @@ def test_traffic_lookup_follows_the_source_hash():
     m = re.search(r"src_sha256=([0-9a-f]+) bytes_per_launch=(\d+)", open(path).read())
     assert m, "the decode summary carries its machine-readable line"
     csrc = os.path.join(ROOT, "int4_routed_expert_moe_amd", "csrc")
-    src = b"".join(open(os.path.join(csrc, f), "rb").read()
-                   for f in ("decode.hip", "common.h", "kernels.h"))
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in bench.TRAFFIC_SOURCES)
+    assert hashlib.sha256(src).hexdigest() == bench.sources_sha256()
+    assert "decode.h" in bench.TRAFFIC_SOURCES  # the kernels themselves
     got = bench.measured_traffic("decode")
     if hashlib.sha256(src).hexdigest() == m.group(1):
         # counters of these very sources: within 1 % above the algorithmic
