@@ -85,7 +85,18 @@ extern "C" {
  * (448 for int8) along hidden and 128 along inter, i.e. hidden <= 8192 and
  * inter <= 4096 for int4 (16384 / 8192 for int2, 7168 / 2048 for int8);
  * top_p = 0 (off), or in (0, 1] (1 is off as well); wfmt 0, or 1 with
- * wbits 4 (MXFP4). */
+ * wbits 4 (MXFP4); act_block 0 or 32 (Q8_0), or MOE_ACT_ROW with int4 or
+ * int8 codes (wfmt 0). */
+/* Activation format act_block = MOE_ACT_ROW: one fp32 scale per activation
+ * row instead of one per 32 values -- per token row of x (H values) and per
+ * (token, expert) row of h (I values) -- with the Q8_0 rule over the whole
+ * row: d = amax/127, q = clamp(roundf(x * (1/d)), -127, 127).  An output
+ * row is then scale_r * d * P with P the exact int32 dot over the whole row
+ * (a second format beside the pages' Q8_0 blocks, "Show HN…", 実装済みの主な
+ * 機能, integer-dot item; with one integer accumulator per row the matrix
+ * cores run without per-block scaling).  q and d of x are then int8 [T][H]
+ * and fp32 [T]. */
+#define MOE_ACT_ROW (-1)
 typedef struct moe_cfg {
   int32_t hidden;       /* H */
   int32_t inter;        /* I, intermediate width of every expert (shared too) */
@@ -98,6 +109,7 @@ typedef struct moe_cfg {
   float routed_scaling; /* routed_scaling_factor applied to routed weights */
   float top_p;          /* adaptive expert top-p (see moe_route); 0 = off */
   int32_t wfmt;         /* 0: integer codes, fp32 row scales; 1: MXFP4 (wbits 4) */
+  int32_t act_block;    /* activations: 0 or 32 = Q8_0 blocks; MOE_ACT_ROW = one scale per row */
 } moe_cfg;
 
 /* Bytes of one packed expert record for cfg (0 if cfg is unsupported). */
@@ -135,13 +147,17 @@ int moe_route(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
 
 /* ---------------------------------------------------------------------------
  * moe_quant_act — Q8_0-style int8 activations ("Show HN…", 実装済みの主な機能,
- * integer-dot item).  For each of `rows` rows of n floats and each block of 32:
+ * integer-dot item).  For each of `rows` rows of n floats and each block of
+ * `block` values (32: Q8_0; n: one scale per row, the MOE_ACT_ROW format):
  *   d = amax / 127 (fp32, correctly rounded), id = d != 0 ? 1/d : 0,
  *   q = clamp(roundf(x * id), -127, 127)  (round half away from zero).
+ * q int8 [rows][n], d fp32 [rows][n/block].
  * Bit-identical to the same steps on a CPU.  n % 32 == 0.
- * Errors: MOE_EINVAL (rows < 0, n <= 0 or n % 32, null pointer), MOE_EALIGN.
+ * Errors: MOE_EINVAL (rows < 0, n <= 0 or n % 32, block not 32 or n, null
+ * pointer), MOE_EALIGN.
  * ------------------------------------------------------------------------- */
-int moe_quant_act(int32_t rows, int32_t n, const float *x, int8_t *q, float *d, void *stream);
+int moe_quant_act(int32_t rows, int32_t n, int32_t block, const float *x, int8_t *q, float *d,
+                  void *stream);
 
 /* ---------------------------------------------------------------------------
  * moe_group — batch-union grouping ("Show HN…", 実装済みの主な機能, batch-union
@@ -167,10 +183,12 @@ int moe_group(const moe_cfg *cfg, int32_t T, const int32_t *idx, int32_t *counts
  * intermediate results (any member may be NULL; pass NULL for the struct in
  * production).  Pair p < T*K is slot p (token p / K, rank p % K); pair
  * T*K + t is the shared expert applied to token t.  P = T*K + T*n_shared.
- *   gate_dots, up_dots  int32 [P][I][H/32]  exact block dots of code . q
- *   h                   fp32  [P][I]        silu(gate) * up
- *   q_h, d_h            int8 [P][I], fp32 [P][I/32]   Q8_0 of h
- *   down_dots           int32 [P][H][I/32]  exact block dots of code . q_h   */
+ * B = 32 for Q8_0 activations, the row length for MOE_ACT_ROW (one dot per
+ * output row):
+ *   gate_dots, up_dots  int32 [P][I][H/B]  exact block dots of code . q
+ *   h                   fp32  [P][I]       silu(gate) * up
+ *   q_h, d_h            int8 [P][I], fp32 [P][I/B]   activations of h
+ *   down_dots           int32 [P][H][I/B]  exact block dots of code . q_h   */
 typedef struct moe_ffn_debug {
   int32_t *gate_dots;
   int32_t *up_dots;
@@ -185,7 +203,8 @@ typedef struct moe_ffn_debug {
  * 実装済みの主な機能: quantisation-kernel item, packed int4/int2 with per-row
  * scales, dequantised on use; integer-dot item; batch-union item).
  * For each selected (token t, expert e) and for the shared expert on every
- * token, with q, d the Q8_0 activations of x (moe_quant_act):
+ * token, with q, d the activations of x (moe_quant_act; with MOE_ACT_ROW one
+ * scale per token, d [T], and one block spanning the row below):
  *   g[r] = sg[r] * sum_b d[t,b] * P_gate[r,b],  P = exact int32 block dots
  *   u[r] = su[r] * sum_b d[t,b] * P_up[r,b]
  *   h[r] = silu(g[r]) * u[r],  silu(z) = z / (1 + e^-z)

@@ -42,7 +42,10 @@ class MoeCfg(ctypes.Structure):
                 ("topk_group", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("wbits", ctypes.c_int32),
                 ("routed_scaling", ctypes.c_float), ("top_p", ctypes.c_float),
-                ("wfmt", ctypes.c_int32)]
+                ("wfmt", ctypes.c_int32), ("act_block", ctypes.c_int32)]
+
+
+ACT_Q8_0, ACT_ROW = 32, -1  # moe_cfg.act_block: Q8_0 blocks, one scale per row (MOE_ACT_ROW)
 
 
 MOE_N_STAGES = 8
@@ -99,7 +102,7 @@ def lib():
     L.moe_route_workspace.restype = sz
     L.moe_route.argtypes = [pc, i32, v, v, v, v, v, v, sz, v]
     L.moe_route.restype = ctypes.c_int
-    L.moe_quant_act.argtypes = [i32, i32, v, v, v, v]
+    L.moe_quant_act.argtypes = [i32, i32, i32, v, v, v, v]
     L.moe_quant_act.restype = ctypes.c_int
     L.moe_group.argtypes = [pc, i32, v, v, v, v, v, v, v, v]
     L.moe_group.restype = ctypes.c_int
@@ -167,18 +170,23 @@ class Config:
     routed_scaling: float = 2.5
     top_p: float = 0.0  # adaptive expert top-p; 0 = off
     wfmt: int = 0  # 0: integer codes with fp32 row scales; 1: MXFP4 (wbits 4)
+    act_block: int = ACT_Q8_0  # activations: Q8_0 blocks of 32, or ACT_ROW (one scale per row)
 
     @classmethod
-    def of(cls, shape, top_p: float = 0.0) -> "Config":
+    def of(cls, shape, top_p: float = 0.0, act_block: int = ACT_Q8_0) -> "Config":
         mx = shape.wbits == -4  # the synthetic shapes' code for MXFP4 experts
         return cls(shape.hidden, shape.inter, shape.n_experts, shape.n_group, shape.topk_group,
                    shape.top_k, shape.n_shared, 4 if mx else shape.wbits, shape.routed_scaling,
-                   top_p, 1 if mx else 0)
+                   top_p, 1 if mx else 0, act_block)
+
+    def act_len(self, n: int) -> int:
+        """Activation block length on rows of n values."""
+        return n if self.act_block == ACT_ROW else 32
 
     def c(self) -> MoeCfg:
         return MoeCfg(self.hidden, self.inter, self.n_experts, self.n_group, self.topk_group,
                       self.top_k, self.n_shared, self.wbits, self.routed_scaling, self.top_p,
-                      self.wfmt)
+                      self.wfmt, self.act_block)
 
 
 def _torch():
@@ -237,15 +245,16 @@ def route(cfg: Config, x, w_router, bias, idx=None, w=None, workspace=None):
     return idx, w
 
 
-def quant_act(x, q=None, d=None):
-    """moe_quant_act on the rows of x: returns (q int8, d fp32 [..., n/32])."""
+def quant_act(x, q=None, d=None, block=32):
+    """moe_quant_act on the rows of x, blocks of `block` values (32 = Q8_0, or
+    the row length = one scale per row): returns (q int8, d fp32 [..., n/block])."""
     torch = _torch()
     n = x.shape[-1]
     rows = x.numel() // n if n else 0
     q = q if q is not None else torch.empty(x.shape, dtype=torch.int8, device=x.device)
-    d = d if d is not None else torch.empty(x.shape[:-1] + (n // 32,), dtype=torch.float32,
+    d = d if d is not None else torch.empty(x.shape[:-1] + (n // block,), dtype=torch.float32,
                                             device=x.device)
-    _check(lib().moe_quant_act(rows, n, _ptr(x), _ptr(q), _ptr(d), _stream()))
+    _check(lib().moe_quant_act(rows, n, block, _ptr(x), _ptr(q), _ptr(d), _stream()))
     return q, d
 
 
@@ -273,12 +282,13 @@ def debug_buffers(cfg: Config, T: int, device):
     torch = _torch()
     P = T * cfg.top_k + T * cfg.n_shared
     H, I = cfg.hidden, cfg.inter
-    return dict(gate_dots=torch.zeros((P, I, H // 32), dtype=torch.int32, device=device),
-                up_dots=torch.zeros((P, I, H // 32), dtype=torch.int32, device=device),
+    nh, ni = H // cfg.act_len(H), I // cfg.act_len(I)
+    return dict(gate_dots=torch.zeros((P, I, nh), dtype=torch.int32, device=device),
+                up_dots=torch.zeros((P, I, nh), dtype=torch.int32, device=device),
                 h=torch.zeros((P, I), dtype=torch.float32, device=device),
                 q_h=torch.zeros((P, I), dtype=torch.int8, device=device),
-                d_h=torch.zeros((P, I // 32), dtype=torch.float32, device=device),
-                down_dots=torch.zeros((P, H, I // 32), dtype=torch.int32, device=device))
+                d_h=torch.zeros((P, ni), dtype=torch.float32, device=device),
+                down_dots=torch.zeros((P, H, ni), dtype=torch.int32, device=device))
 
 
 def layer_debug_buffers(cfg: Config, T: int, device):
@@ -288,7 +298,7 @@ def layer_debug_buffers(cfg: Config, T: int, device):
     out = debug_buffers(cfg, T, device)
     i32 = dict(dtype=torch.int32, device=device)
     out.update(q=torch.zeros((T, H), dtype=torch.int8, device=device),
-               d=torch.zeros((T, H // 32), dtype=torch.float32, device=device),
+               d=torch.zeros((T, H // cfg.act_len(H)), dtype=torch.float32, device=device),
                counts=torch.zeros(E, **i32), offsets=torch.zeros(E + 1, **i32),
                perm=torch.zeros(S, **i32), inv=torch.zeros(S, **i32),
                active=torch.zeros(E, **i32), n_active=torch.zeros(1, **i32))

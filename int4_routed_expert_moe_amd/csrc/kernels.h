@@ -35,6 +35,11 @@ inline void launch_k(F kernel, dim3 g, dim3 b, uint32_t lds, hipStream_t st, Ev 
 
 void launch_quant_act(const float *x, int8_t *q, float *d, int64_t n_elems, hipStream_t st,
                       const moe_events *ev = nullptr);
+// The per-row activation format: one scale per row of n floats (rows r <
+// n_skip with skip[r] < 0 are not written; skip may be NULL).
+void launch_quant_rows(const float *x, int8_t *q, float *d, int64_t rows, int n,
+                       const int32_t *skip, int n_skip, hipStream_t st,
+                       const moe_events *ev = nullptr);
 void launch_combine(int T, int H, int K, const float *eo, const float *w, const float *shared,
                     const float *residual, float *y, float *yn, float eps, hipStream_t st,
                     const moe_events *ev = nullptr);
@@ -76,6 +81,15 @@ size_t mfma_tiles_max(int T, int K, int E, int n_shared);
 bool mfma_supported(const FfnArgs &a);
 void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_h, float *d_h,
                      hipStream_t st, const moe_events *ev = nullptr);
+// The same with one activation scale per row (the per-row format): q, d of
+// x per token row; gate/up writes fp32 h [P][I], which is quantised per
+// (token, expert) row into q_h [P][I] / d_h [P] (pairs of slots dropped by
+// top-p, idx[p] < 0, skipped), then the down projection.  Int4 and int8
+// codes.  Dumps: one int32 dot per row ([P][I][1], [P][H][1]) and h.
+bool mfma_rows_supported(const FfnArgs &a);
+void launch_ffn_mfma_rows(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, float *h, int8_t *q_h,
+                          float *d_h, const int32_t *idx, hipStream_t st,
+                          const moe_events *ev = nullptr);
 // The down projection of the small-batch path from its slot table (int8,
 // int4, MXFP4), rows to expert_out / shared_out.
 // dbg: the kernel that also writes a.dbg.down_dots.

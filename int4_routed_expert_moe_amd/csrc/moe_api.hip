@@ -73,8 +73,14 @@ int check_cfg(const moe_cfg *c) {
   if (c->wfmt != 0 && c->wfmt != 1) return fail(MOE_EINVAL, "wfmt=%d not in {0,1}", c->wfmt);
   if (c->wfmt == 1 && c->wbits != 4)
     return fail(MOE_EINVAL, "MXFP4 experts (wfmt 1) need wbits 4 (4-bit codes)");
+  if (c->act_block != 0 && c->act_block != 32 && c->act_block != MOE_ACT_ROW)
+    return fail(MOE_EINVAL, "act_block=%d not in {0, 32, MOE_ACT_ROW}", c->act_block);
+  if (c->act_block == MOE_ACT_ROW && (c->wfmt != 0 || (c->wbits != 4 && c->wbits != 8)))
+    return fail(MOE_EINVAL, "per-row activation scales need int4 or int8 codes (wfmt 0)");
   return MOE_OK;
 }
+
+bool act_rows(const moe_cfg &c) { return c.act_block == MOE_ACT_ROW; }
 
 #define REQUIRE(p, name)                                                       \
   do {                                                                         \
@@ -126,6 +132,8 @@ struct FfnWs {
   int32_t *n_tiles;
   int4 *tiles;
   float *h;  // fp32 h [P][I] (GEMV path); the MFMA path keeps Q8_0(h) here
+  int8_t *qh_rows;  // per-row activations: q_h [P][I] and d_h [P] (h stays fp32)
+  float *dh_rows;
 };
 FfnWs carve_ffn(Carve &cv, const moe_cfg &c, int T) {
   FfnWs f;
@@ -140,6 +148,8 @@ FfnWs carve_ffn(Carve &cv, const moe_cfg &c, int T) {
   f.n_tiles = cv.take<int32_t>(1);
   f.tiles = cv.take<int4>(moe::mfma_tiles_max(T, c.top_k, c.n_experts, c.n_shared));
   f.h = cv.take<float>(pairs * c.inter);
+  f.qh_rows = cv.take<int8_t>(act_rows(c) ? pairs * c.inter : 0);
+  f.dh_rows = cv.take<float>(act_rows(c) ? pairs : 0);
   return f;
 }
 
@@ -215,6 +225,14 @@ int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32
   a.shared_out = shared_out;
   if (dbg) a.dbg = *dbg;
   else memset(&a.dbg, 0, sizeof(a.dbg));
+  if (act_rows(c)) {  // per-row activation scales: the row-dot MFMA kernels at every T
+    if (!moe::mfma_rows_supported(a))
+      return fail(MOE_EINVAL, "per-row activations need hidden and inter multiples of 128");
+    int8_t *q_h = a.dbg.q_h ? a.dbg.q_h : ws.qh_rows;  // written straight into a dump
+    float *d_h = a.dbg.d_h ? a.dbg.d_h : ws.dh_rows;
+    moe::launch_ffn_mfma_rows(a, ws.tiles, ws.n_tiles, ws.h, q_h, d_h, idx, st, ev);
+    return launched("moe_expert_ffn");
+  }
   const bool mfma = moe::mfma_supported(a);
   const bool mfma_only = c.wbits == 8 || c.wfmt == 1;  // the vector-dot kernels take int4/int2
   if (mfma_only && !mfma)
@@ -267,14 +285,18 @@ int moe_route(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
   return do_route(*cfg, T, x, w_router, bias, idx, w, ws, (hipStream_t)stream);
 }
 
-int moe_quant_act(int32_t rows, int32_t n, const float *x, int8_t *q, float *d, void *stream) {
+int moe_quant_act(int32_t rows, int32_t n, int32_t block, const float *x, int8_t *q, float *d,
+                  void *stream) {
   if (rows < 0) return fail(MOE_EINVAL, "rows=%d < 0", rows);
   if (n <= 0 || n % 32) return fail(MOE_EINVAL, "n=%d must be a positive multiple of 32", n);
+  if (block != 32 && block != n)
+    return fail(MOE_EINVAL, "block=%d must be 32 (Q8_0) or n=%d (one scale per row)", block, n);
   if (rows == 0) return MOE_OK;
   REQUIRE(x, "x");
   REQUIRE(q, "q");
   REQUIRE(d, "d");
-  moe::launch_quant_act(x, q, d, (int64_t)rows * n, (hipStream_t)stream);
+  if (block == 32) moe::launch_quant_act(x, q, d, (int64_t)rows * n, (hipStream_t)stream);
+  else moe::launch_quant_rows(x, q, d, rows, n, nullptr, 0, (hipStream_t)stream);
   return launched("moe_quant_act");
 }
 
@@ -458,7 +480,7 @@ int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rou
   float *w = w_out ? w_out : ws.w;
   int8_t *q = g.q ? g.q : ws.q;  // the kernels write Q8_0 of x straight into a dump
   float *d = g.d ? g.d : ws.d;
-  if (moe::small_batch_supported(c, T)) {
+  if (!act_rows(c) && moe::small_batch_supported(c, T)) {
     moe::LayerArgs a;
     a.H = c.hidden;
     a.I = c.inter;
@@ -502,7 +524,8 @@ int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rou
     return launched("moe_layer (small batch)");
   }
   if ((rc = do_route(c, T, x, w_router, bias, idx, w, ws.route, st, ev))) return rc;
-  moe::launch_quant_act(x, q, d, (int64_t)T * c.hidden, st, ev);
+  if (act_rows(c)) moe::launch_quant_rows(x, q, d, T, c.hidden, nullptr, 0, st, ev);
+  else moe::launch_quant_act(x, q, d, (int64_t)T * c.hidden, st, ev);
   if ((rc = launched("moe_layer quant"))) return rc;
   FfnWs fws = ws.ffn;
   if (dump_union) {  // the grouping kernel writes the union straight into the dump

@@ -43,6 +43,52 @@ void launch_quant_act(const float *x, int8_t *q, float *d, int64_t n_elems, hipS
            q, d, quads);
 }
 
+// The per-row activation format (one scale per row, the Q8_0 rule over the
+// whole row): one workgroup per row of n floats (n % 4 == 0).  The row's
+// amax (a maximum, so exact in any order), then d = amax/127,
+// id = d != 0 ? 1/d : 0, q = clamp(roundf(x * id), -127, 127).  Rows
+// r < n_skip whose skip[r] < 0 (slots dropped by top-p) are left alone.
+__global__ void __launch_bounds__(256) k_quant_rows(const float *__restrict__ x,
+                                                    int8_t *__restrict__ q,
+                                                    float *__restrict__ d, int n,
+                                                    const int32_t *__restrict__ skip,
+                                                    int n_skip) {
+  __shared__ float wm[4];
+  const size_t row = blockIdx.x;
+  if (skip && (int)row < n_skip && skip[row] < 0) return;
+  const float4 *x4 = reinterpret_cast<const float4 *>(x + row * n);
+  uint32_t *q4 = reinterpret_cast<uint32_t *>(q + row * n);
+  const int n4 = n / 4;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const float4 v = x4[i];
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  const float amax = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  const float dd = amax / 127.0f;
+  const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
+  auto cv = [&](float f) -> uint32_t {
+    float r = roundf(f * id);
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (uint32_t)(uint8_t)(int8_t)(int)r;
+  };
+  for (int i = threadIdx.x; i < n4; i += 256) {
+    const float4 v = x4[i];
+    q4[i] = cv(v.x) | (cv(v.y) << 8) | (cv(v.z) << 16) | (cv(v.w) << 24);
+  }
+  if (threadIdx.x == 0) d[row] = dd;
+}
+
+void launch_quant_rows(const float *x, int8_t *q, float *d, int64_t rows, int n,
+                       const int32_t *skip, int n_skip, hipStream_t st, const moe_events *ev) {
+  if (rows <= 0) return;
+  launch_k(k_quant_rows, dim3((unsigned)rows), dim3(256), 0, st, stage_ev(ev, MOE_STAGE_QUANT), x, q,
+           d, n, skip, n_skip);
+}
+
 // One block per token row; 256 threads stride over H in float4.
 // y = residual + shared + sum_k w_k * expert_k (fp32, rank order); optional
 // unit-gain RMSNorm of y.

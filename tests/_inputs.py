@@ -100,7 +100,7 @@ class DeviceLayer:
             self._cache[e] = rec.copy()
 
     def oracle_layer_on_gpu_qh(self, x, dumps, residual=None, want_norm=False, top_p=0.0,
-                               tokens=None):
+                               tokens=None, act_block=32):
         """The oracle layer with each down projection taken on the GPU's own
         Q8_0(h) -- after checking that decision: the dumped q_h / d_h
         (moe_layer_debug) are exactly Q8_0 of the dumped h, and h is within the
@@ -109,9 +109,10 @@ class DeviceLayer:
         where h sits within rounding of a code boundary both codes are
         correct; the down projection of the GPU's codes is then the unique
         comparand.  tokens: row of each x row in the dumps' batch (default
-        0..len(x)-1), when x is a sample of a larger batch.  Returns
-        oracle.layer's dict plus 'qh_flips', the pairs whose codes differ
-        from the oracle's own Q8_0(h)."""
+        0..len(x)-1), when x is a sample of a larger batch.  act_block: the
+        activation format (Q8_0, or oracle.ACT_ROW: one scale per row, the
+        same argument for that row's codes).  Returns oracle.layer's dict plus
+        'qh_flips', the pairs whose codes differ from the oracle's own."""
         import oracle
         s = self.shape
         H, I, K, wb = s.hidden, s.inter, s.top_k, s.wbits
@@ -122,7 +123,7 @@ class DeviceLayer:
         n_batch = int(dumps["h"].shape[0]) // (K + s.n_shared)
         idx, w, margin = oracle.route(x, self.wr, self.bias, s.n_group, s.topk_group, K,
                                       s.routed_scaling, top_p)
-        q, d = oracle.q8_0(x)
+        q, d = oracle.quant_act(x, act_block)
         eo = np.zeros((T, K, H), np.float32)
         so = np.zeros((T, H), np.float32) if s.n_shared else None
         flips = 0
@@ -131,13 +132,13 @@ class DeviceLayer:
             gp = rows[t] * K + p % K if p < T * K else n_batch * K + rows[t]  # in the dumps
             if e not in blobs:
                 blobs[e] = self.blob(e)
-            hr = oracle.gate_up(blobs[e], H, I, wb, q[t], d[t])["h"]
+            hr = oracle.gate_up(blobs[e], H, I, wb, q[t], d[t], act_block=act_block)["h"]
             hg, qg, dg = dumps["h"][gp], dumps["q_h"][gp], dumps["d_h"][gp]
             assert_close_rms(hg, hr, tol_h, f"h of pair {gp}")
-            qc, dc = oracle.q8_0(hg)
-            assert np.array_equal(qg, qc) and np.array_equal(dg, dc), f"Q8_0(h) of pair {gp}"
-            flips += not np.array_equal(oracle.q8_0(hr)[0], qg)
-            y, _ = oracle.down(blobs[e], H, I, wb, qg, dg)
+            qc, dc = oracle.quant_act(hg, act_block)
+            assert np.array_equal(qg, qc) and np.array_equal(dg, dc), f"codes of h, pair {gp}"
+            flips += not np.array_equal(oracle.quant_act(hr, act_block)[0], qg)
+            y, _ = oracle.down(blobs[e], H, I, wb, qg, dg, act_block=act_block)
             if p < T * K:
                 eo[t, p % K] = y
             else:
@@ -146,7 +147,7 @@ class DeviceLayer:
         y, yn = res if want_norm else (res, None)
         return dict(idx=idx, w=w, margin=margin, y=y, y_norm=yn, qh_flips=flips)
 
-    def oracle_layer(self, x, residual=None, want_norm=False, top_p=0.0):
+    def oracle_layer(self, x, residual=None, want_norm=False, top_p=0.0, act_block=32):
         import oracle
         s = self.shape
         shared = self.blob(synth.SHARED_ID) if s.n_shared else None
@@ -154,4 +155,4 @@ class DeviceLayer:
                             H=s.hidden, I=s.inter, n_experts=s.n_experts, n_group=s.n_group,
                             topk_group=s.topk_group, top_k=s.top_k, scale=s.routed_scaling,
                             wbits=s.wbits, residual=residual, want_norm=want_norm,
-                            top_p_value=top_p)
+                            top_p_value=top_p, act_block=act_block)

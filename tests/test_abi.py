@@ -110,12 +110,15 @@ def test_route_errors(L):
 
 
 def test_quant_act_errors(L):
-    assert L.moe_quant_act(-1, 32, A, A, A, None) == moe.MOE_EINVAL
-    assert L.moe_quant_act(2, 48, A, A, A, None) == moe.MOE_EINVAL
-    assert L.moe_quant_act(2, 0, A, A, A, None) == moe.MOE_EINVAL
-    assert L.moe_quant_act(2, 64, A, None, A, None) == moe.MOE_EINVAL
-    assert L.moe_quant_act(2, 64, A, A + 8, A, None) == moe.MOE_EALIGN
-    assert L.moe_quant_act(0, 64, None, None, None, None) == 0
+    assert L.moe_quant_act(-1, 32, 32, A, A, A, None) == moe.MOE_EINVAL
+    assert L.moe_quant_act(2, 48, 32, A, A, A, None) == moe.MOE_EINVAL
+    assert L.moe_quant_act(2, 0, 32, A, A, A, None) == moe.MOE_EINVAL
+    assert L.moe_quant_act(2, 64, 32, A, None, A, None) == moe.MOE_EINVAL
+    assert L.moe_quant_act(2, 64, 32, A, A + 8, A, None) == moe.MOE_EALIGN
+    assert L.moe_quant_act(0, 64, 32, None, None, None, None) == 0
+    # the block is 32 (Q8_0) or the whole row
+    assert L.moe_quant_act(2, 128, 64, A, A, A, None) == moe.MOE_EINVAL
+    assert L.moe_quant_act(0, 128, 128, None, None, None, None) == 0
 
 
 def test_group_errors(L):
@@ -181,6 +184,17 @@ def test_layer_noalloc_rejects_batches_beyond_its_scratch(L):
                                None, None, None) == moe.MOE_EINVAL
     assert L.moe_layer_noalloc(ctypes.byref(c), 0, None, None, None, None, None, None, None,
                                None, 1e-5, None, None, None, None) == moe.MOE_OK
+
+
+def test_per_row_activations_take_int4_or_int8_codes(L):
+    for shape in (synth.REAL.with_bits(2), synth.REAL.with_bits(synth.MXFP4)):
+        c = moe.Config.of(shape, act_block=moe.ACT_ROW).c()
+        assert L.moe_expert_blob_bytes(ctypes.byref(c)) == 0  # rejected
+    for bits in (4, 8):
+        c = moe.Config.of(synth.REAL.with_bits(bits), act_block=moe.ACT_ROW).c()
+        assert L.moe_expert_blob_bytes(ctypes.byref(c)) > 0
+    bad = moe.Config.of(synth.REAL, act_block=64).c()
+    assert L.moe_expert_blob_bytes(ctypes.byref(bad)) == 0
 
 
 def test_strerror(L):
