@@ -50,13 +50,20 @@ WORKLOADS = {
     "verify4": dict(T=4, tokens="perturbed", bias="uniform", seed="verify", ring=8),
     "verify16": dict(T=16, tokens="perturbed", bias="uniform", seed="verify", ring=4),
     "prefill": dict(T=2048, tokens="normal", bias="zipf", seed="prefill", ring=2),
+    # every token routed to the same 8 experts (their bias raised by 2.0): nine dense
+    # GEMMs of 2048 tokens (8 routed + shared), the layer's matrix-core-bound sub-problem
+    "prefill_dense": dict(T=2048, tokens="normal", bias="dense", seed="prefill", ring=2),
     # 16 consecutive layers per step (pre-norm residual between them), all resident
     "stack1": dict(T=1, tokens="normal", bias="zipf", seed="stack", ring=16, layers=16),
     "stack8": dict(T=8, tokens="normal", bias="zipf", seed="stack", ring=16, layers=16),
 }
 
 
-def describe(name, shape, T, ring, layers=1, top_p=0.0, cache_slots=0):
+ACT_TEXT = {"q8_0": "Q8_0 activations",
+            "row": "activations with one scale per row (per token, per token and expert)"}
+
+
+def describe(name, shape, T, ring, layers=1, top_p=0.0, cache_slots=0, act="q8_0"):
     tp = (f", adaptive expert top-p {top_p:g} (shortest rank-order prefix holding that share of "
           f"the selected scores, weights renormalised)" if 0 < top_p < 1 else "")
     wfmt = ("MXFP4 (FP4 E2M1 codes + an E8M0 scale per 32)" if shape.wbits == -4
@@ -71,12 +78,12 @@ def describe(name, shape, T, ring, layers=1, top_p=0.0, cache_slots=0):
                 f"layers; hidden {shape.hidden}, expert intermediate {shape.inter}, "
                 f"{shape.n_experts} experts in {shape.n_group} groups, top-{shape.topk_group} "
                 f"groups, top-{shape.top_k}, {shape.n_shared} shared expert, {wfmt} "
-                f"experts, Q8_0 activations{tp})" +
+                f"experts, {ACT_TEXT[act]}{tp})" +
                 ("" if cache_slots else ", all layers resident in HBM"))
     return (f"{name}: {T} token(s) per step through one routed-MoE layer (hidden {shape.hidden}, "
             f"expert intermediate {shape.inter}, {shape.n_experts} experts in {shape.n_group} "
             f"groups, top-{shape.topk_group} groups, top-{shape.top_k}, {shape.n_shared} shared "
-            f"expert, {wfmt} experts, Q8_0 activations{tp}); weights "
+            f"expert, {wfmt} experts, {ACT_TEXT[act]}{tp}); weights "
             f"cycled over {ring} seeded layer instances" + ("" if cache_slots else " in HBM"))
 
 
@@ -206,8 +213,19 @@ def cpu_baseline_stack(shape, seed, layers, tokens_fn, T, n_steps, top_p=0.0):
                        f"over output rows; expert records drawn outside the timed region)")
 
 
-def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s, top_p=0.0):
-    """Oracle (plain C + OpenMP) on the first steps of the same workload."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s, top_p=0.0, act_block=32):
+    """Oracle (plain C + OpenMP) on the first steps of the same workload: with
+    all its threads, then (a third of the budget) on one thread."""
     import oracle
     import synth
     cache = {}
@@ -220,23 +238,34 @@ def cpu_baseline(shape, seed, wr, bias, tokens_fn, T, budget_s, top_p=0.0):
     shared = synth.expert_blob(shape, seed, 0, synth.SHARED_ID)
     kw = dict(H=shape.hidden, I=shape.inter, n_experts=shape.n_experts, n_group=shape.n_group,
               topk_group=shape.topk_group, top_k=shape.top_k, scale=shape.routed_scaling,
-              wbits=shape.wbits, top_p_value=top_p)
-    done_tok, spent, steps = 0, 0.0, 0
-    while spent < budget_s and steps < 1024:
-        x = tokens_fn(steps)
-        idx, _, _ = oracle.route(x, wr, bias, shape.n_group, shape.topk_group, shape.top_k,
-                                 shape.routed_scaling, top_p)
-        for e in np.unique(idx[idx >= 0]):
-            blob_of(int(e))  # drawn outside the timed region
-        t0 = time.perf_counter()
-        oracle.layer(x, wr, bias, blob_of, shared, **kw)
-        spent += time.perf_counter() - t0
-        done_tok += x.shape[0]
-        steps += 1
-    return dict(value=done_tok / spent, unit="tokens/s", cores=oracle.threads(), kind="oracle",
+              wbits=shape.wbits, top_p_value=top_p, act_block=act_block)
+
+    def timed(budget):
+        done_tok, spent, steps = 0, 0.0, 0
+        while spent < budget and steps < 1024:
+            x = tokens_fn(steps)
+            idx, _, _ = oracle.route(x, wr, bias, shape.n_group, shape.topk_group, shape.top_k,
+                                     shape.routed_scaling, top_p)
+            for e in np.unique(idx[idx >= 0]):
+                blob_of(int(e))  # drawn outside the timed region
+            t0 = time.perf_counter()
+            oracle.layer(x, wr, bias, blob_of, shared, **kw)
+            spent += time.perf_counter() - t0
+            done_tok += x.shape[0]
+            steps += 1
+        return done_tok, spent, steps
+
+    threads = oracle.threads()
+    done_tok, spent, steps = timed(budget_s)
+    oracle.set_threads(1)
+    d1, s1, n1 = timed(budget_s / 3)
+    oracle.set_threads(threads)
+    return dict(value=done_tok / spent, unit="tokens/s", cores=threads, kind="oracle",
+                value_single_thread=d1 / s1, cpu_model=cpu_model(), host_cpus=os.cpu_count(),
                 sample=f"first {steps} step(s) ({done_tok} tokens) of the same workload on layer "
-                       f"instance 0, {spent:.1f} s of oracle time (plain C, OpenMP over output "
-                       f"rows; expert records drawn outside the timed region)")
+                       f"instance 0, {spent:.1f} s of oracle time on {threads} threads; then the "
+                       f"first {n1} step(s) on one thread ({s1:.1f} s) (plain C, OpenMP over "
+                       f"output rows; expert records drawn outside the timed region)")
 
 
 def main():
@@ -249,6 +278,8 @@ def main():
                     help="expert weights: int8/int4/int2 codes with row scales, or MXFP4")
     ap.add_argument("--ring", type=int, default=0,
                     help="layer instances to cycle (0 = the workload's ring; 1 with --cache-slots)")
+    ap.add_argument("--act", default="q8_0", choices=("q8_0", "row"),
+                    help="activation format: Q8_0 blocks of 32, or one scale per row")
     ap.add_argument("--topp", type=float, default=0.0,
                     help="adaptive expert top-p in (0, 1); 0 = off (plain top-k)")
     ap.add_argument("--cache-slots", type=int, default=0,
@@ -288,7 +319,8 @@ def main():
     torch.cuda.set_device(dev)
     moe.lib()
     hip = Hip()
-    cfg = moe.Config.of(shape, args.topp)
+    act = moe.ACT_ROW if args.act == "row" else moe.ACT_Q8_0
+    cfg = moe.Config.of(shape, args.topp, act)
     bb = moe.blob_bytes(cfg)
     stream = torch.cuda.Stream(device=dev)  # default priority; graphs cannot capture stream 0
     torch.cuda.set_stream(stream)
@@ -299,6 +331,8 @@ def main():
         wr = synth.router_weights(shape, seed, l)
         bias = (synth.router_bias_zipf(shape, seed, l) if wl["bias"] == "zipf"
                 else synth.router_bias_uniform(shape, seed, l))
+        if wl["bias"] == "dense":
+            bias[:shape.top_k] += np.float32(2.0)
         ex = torch.empty(shape.n_experts * bb, dtype=torch.uint8, device=dev)
         sh = torch.empty(bb, dtype=torch.uint8, device=dev)
         synth.expert_blobs_gpu(shape, seed, l, list(range(shape.n_experts)), ex.data_ptr(), bb,
@@ -504,7 +538,8 @@ def main():
                            if args.wbits == "4" and not args.topp else None)
         roof.update(bytes_per_launch=dom_bytes, launch_us=dom_sec * 1e6)
     else:  # grouped GEMM on the matrix cores: int8 operations (2 per MAC) of the launch
-        dom = f"gate_up (grouped {shape.label} x int8 MFMA GEMM + SwiGLU + Q8_0 of h)"
+        fmt = "per-row activation scales" if args.act == "row" else "Q8_0 activations"
+        dom = f"gate_up (grouped {shape.label} x int8 MFMA GEMM, {fmt}, + SwiGLU)"
         ops = 2.0 * (pairs + T * shape.n_shared) * 2 * shape.inter * shape.hidden
         roof = {"bound": "mfma", "kernel": dom, "achieved": ops / dom_sec / 1e12,
                 "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s", "traffic": None,
@@ -512,6 +547,11 @@ def main():
                 "note": "int8 operations (2 per multiply-accumulate) against the dense "
                         "int8 MFMA peak"}
         roof["frac"] = roof["achieved"] / INT8_PEAK_TOPS
+        if "down" in stage_ms:  # the down projection: half the operations of gate/up
+            roof["down_frac"] = ops / 2 / (stage_ms["down"] * 1e-3) / 1e12 / INT8_PEAK_TOPS
+        # whole step against the larger of its HBM and matrix-core bounds
+        bound_s = max(step_bytes / (HBM_PEAK_GBPS * 1e9), 1.5 * ops / (INT8_PEAK_TOPS * 1e12))
+        roof["step_frac_of_bound"] = bound_s / (sec / K)
 
     out = {
         "metric": METRIC,
@@ -524,10 +564,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4e2m1xi8->i32" if shape.wbits == -4 else f"i{shape.wbits}xi8->i32",
+        "dtype": ("fp4e2m1xi8->i32" if shape.wbits == -4 else f"i{shape.wbits}xi8->i32")
+                 + ("" if args.act == "q8_0" else " (per-row activation scales)"),
         "data": "synthetic",
         "config": {"workload": describe(args.workload, shape, T, R, NL, args.topp,
-                                        min(args.cache_slots, shape.n_experts)),
+                                        min(args.cache_slots, shape.n_experts), args.act),
                    "tokens_per_step": T, "layers_per_step": NL, "layer_instances": R,
                    "hip_graph": use_graph, "top_p": args.topp or None,
                    "distinct_routed_experts_per_step": U,
@@ -548,7 +589,7 @@ def main():
         else:
             r0 = ring[0]
             out["cpu_baseline"] = cpu_baseline(shape, seed, r0["wr_h"], r0["bias_h"], tokens_for,
-                                               T, args.cpu_budget, args.topp)
+                                               T, args.cpu_budget, args.topp, act)
     print(json.dumps(out), flush=True)
 
 

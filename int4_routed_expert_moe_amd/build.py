@@ -32,6 +32,7 @@ HIP_FLAGS = [
 # extra flags per source file
 FILE_FLAGS = {
     "ffn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "ffn_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

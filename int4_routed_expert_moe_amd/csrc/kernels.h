@@ -79,6 +79,9 @@ void launch_ffn_gemv(const FfnArgs &a, hipStream_t st, const moe_events *ev = nu
 // [P][I] and [P][I/32]) and grouped down into expert_out / shared_out.
 size_t mfma_tiles_max(int T, int K, int E, int n_shared);
 bool mfma_supported(const FfnArgs &a);
+// The tile list alone (one workgroup): work items (expert, first list
+// position, token count) of TILE_T tokens from the grouping offsets.
+void launch_mfma_tiles(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, hipStream_t st);
 void launch_ffn_mfma(const FfnArgs &a, int4 *tiles, int32_t *n_tiles, int8_t *q_h, float *d_h,
                      hipStream_t st, const moe_events *ev = nullptr);
 // The same with one activation scale per row (the per-row format): q, d of

@@ -106,6 +106,8 @@ def lib():
     L.oracle_rmsnorm.restype = None
     L.oracle_threads.argtypes = []
     L.oracle_threads.restype = c_i
+    L.oracle_set_threads.argtypes = [c_i]
+    L.oracle_set_threads.restype = None
     _lib = L
     return L
 
@@ -126,6 +128,12 @@ def _check(rc, what):
 def threads() -> int:
     """OpenMP threads used by the oracle's parallel loops."""
     return int(lib().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for the oracle's parallel loops from now on (results do not
+    depend on it: each output row is computed by one thread)."""
+    lib().oracle_set_threads(int(n))
 
 
 # ------------------------------------------------------------------ codes

@@ -640,6 +640,8 @@ void oracle_rmsnorm(int T, int H, const float *x, float *y, float eps) {
 #ifdef _OPENMP
 #include <omp.h>
 int oracle_threads(void) { return omp_get_max_threads(); }
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int oracle_threads(void) { return 1; }
+void oracle_set_threads(int n) { (void)n; }
 #endif
