@@ -28,6 +28,10 @@
  *     synchronisation, as for any HIP call.
  *   - On a non-zero return nothing has been enqueued.  moe_strerror() names
  *     the code; moe_last_error() gives a per-thread message with details.
+ *     A call that launches work first clears HIP's per-thread last-error
+ *     state (hipGetLastError), so MOE_EHIP always describes a failure of
+ *     that call's own launches, never an earlier failed HIP call of the
+ *     caller's.
  *   - T = 0 tokens is a valid no-op.
  *   - Results are bit-identical from run to run for fixed inputs and device
  *     (no floating-point atomics).
@@ -418,6 +422,18 @@ int moe_cache_destroy(moe_cache *c);
 int moe_cache_simulate(int32_t n_experts, int32_t n_slots, int32_t n_pinned, int32_t max_promote,
                        const uint64_t *usage, const int32_t *idx, int32_t n_steps, int32_t n,
                        int32_t *hits, int32_t *misses, int32_t *slot_of);
+
+/* ---------------------------------------------------------------------------
+ * moe_mfma_peak — measurement helper, not part of the layer: n_wg workgroups
+ * of 4 waves, each wave running iters x 8 independent int8 MFMAs
+ * (v_mfma_i32_16x16x64_i8, 32768 operations each) and nothing else, so that
+ * n_wg * 4 * iters * 8 * 32768 int8 operations divided by the launch's time
+ * is the matrix-core rate the chip reaches in practice.  out [n_wg * 256]
+ * int32 (device, caller-owned) receives a checksum per thread so that no
+ * work is elided.  Errors: MOE_EINVAL for n_wg outside [1, 2^20], iters
+ * outside [1, 2^21) or a NULL out.
+ */
+int moe_mfma_peak(int32_t n_wg, int32_t iters, int32_t *out, void *stream);
 
 /* Name of a return code, and the calling thread's last detailed message. */
 const char *moe_strerror(int code);

@@ -26,7 +26,7 @@ EXPORTS = (
     "moe_layer_workspace", "moe_layer", "moe_layer_ptrs", "moe_layer_noalloc",
     "moe_host_device_ptr", "moe_cache_create", "moe_cache_step", "moe_cache_get_stats",
     "moe_cache_usage", "moe_cache_slot_of", "moe_cache_destroy", "moe_cache_simulate",
-    "moe_strerror", "moe_last_error",
+    "moe_mfma_peak", "moe_strerror", "moe_last_error",
 )
 
 
@@ -115,6 +115,8 @@ def lib():
     L.moe_combine.restype = ctypes.c_int
     L.moe_rmsnorm.argtypes = [i32, i32, v, v, f32, v]
     L.moe_rmsnorm.restype = ctypes.c_int
+    L.moe_mfma_peak.argtypes = [i32, i32, v, v]
+    L.moe_mfma_peak.restype = ctypes.c_int
     L.moe_layer_workspace.argtypes = [pc, i32]
     L.moe_layer_workspace.restype = sz
     L.moe_layer.argtypes = [pc, i32, v, v, v, v, v, v, v, v, f32, v, v, v, sz,
@@ -359,6 +361,13 @@ def rmsnorm(x, y=None, eps=1e-5):
     y = y if y is not None else torch.empty_like(x)
     _check(lib().moe_rmsnorm(T, H, _ptr(x), _ptr(y), eps, _stream()))
     return y
+
+
+def mfma_peak(n_wg, iters, out):
+    """moe_mfma_peak: matrix cores alone; out int32 [n_wg * 256] on the device.
+    Returns the int8 operations launched (n_wg * 4 * iters * 8 * 32768)."""
+    _check(lib().moe_mfma_peak(n_wg, iters, _ptr(out), _stream()))
+    return n_wg * 4 * iters * 8 * 32768
 
 
 def layer(cfg: Config, x, w_router, bias, experts, shared=None, residual=None, y=None,

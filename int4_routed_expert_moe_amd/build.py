@@ -33,6 +33,7 @@ HIP_FLAGS = [
 FILE_FLAGS = {
     "ffn_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "ffn_rows.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "peak.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -327,6 +327,7 @@ int moe_host_device_ptr(const void *host, void **dev) {
 int moe_cache_create(const moe_cfg *cfg, int32_t n_slots, int32_t n_pinned, int32_t max_promote,
                      int32_t max_pairs, const void *const *host_records, void *slots,
                      void *table, const uint64_t *usage, void *stream, moe_cache **out) {
+  (void)hipGetLastError();  // a failure reported below is then this call's own
   if (!out) return moe::set_error(MOE_EINVAL, "moe_cache_create: out is NULL");
   *out = nullptr;
   const size_t bb = moe_expert_blob_bytes(cfg);
@@ -393,6 +394,7 @@ int moe_cache_create(const moe_cfg *cfg, int32_t n_slots, int32_t n_pinned, int3
 }
 
 int moe_cache_step(moe_cache *c, const int32_t *idx, int32_t n, int32_t wait, void *stream) {
+  (void)hipGetLastError();  // a failure reported below is then this call's own
   if (!c || !idx) return moe::set_error(MOE_EINVAL, "moe_cache_step: NULL argument");
   if (n < 0 || n > c->max_pairs)
     return moe::set_error(MOE_EINVAL, "moe_cache_step: n outside [0, max_pairs]");

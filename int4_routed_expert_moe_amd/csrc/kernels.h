@@ -126,6 +126,10 @@ struct LayerArgs {
   moe_layer_debug dbg;           // dumps (launch_small_batch_dbg only)
 };
 size_t small_batch_slot_ints(int T, int K, int n_shared);
+// Matrix cores alone (peak.hip): n_wg workgroups of 4 waves, each wave
+// iters x 8 int8 MFMAs (16x16x64); out [n_wg * 256] takes a checksum.
+void launch_mfma_peak(int n_wg, int iters, int32_t *out, hipStream_t st);
+
 bool small_batch_supported(const moe_cfg &c, int T);
 void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev);
 // The same with a.dbg's dumps written (decode_dbg.hip).

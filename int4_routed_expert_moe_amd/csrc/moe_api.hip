@@ -93,6 +93,11 @@ bool act_rows(const moe_cfg &c) { return c.act_block == MOE_ACT_ROW; }
     if ((p) && !aligned((p), 16)) return fail(MOE_EALIGN, "%s is not 16-byte aligned", name); \
   } while (0)
 
+// HIP's per-thread last-error state is cleared on entry to every call that
+// launches work, so that launched() sees only this call's own launches (an
+// earlier failed HIP call of the caller would otherwise be reported here).
+void clear_hip_error() { (void)hipGetLastError(); }
+
 int launched(const char *what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -267,6 +272,7 @@ size_t moe_route_workspace(const moe_cfg *cfg, int32_t T) {
 int moe_route(const moe_cfg *cfg, int32_t T, const float *x, const float *w_router,
               const float *bias, int32_t *idx, float *w, void *workspace, size_t ws_bytes,
               void *stream) {
+  clear_hip_error();  // MOE_EHIP then names this call's own launches
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
@@ -287,6 +293,7 @@ int moe_route(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rout
 
 int moe_quant_act(int32_t rows, int32_t n, int32_t block, const float *x, int8_t *q, float *d,
                   void *stream) {
+  clear_hip_error();  // MOE_EHIP then names this call's own launches
   if (rows < 0) return fail(MOE_EINVAL, "rows=%d < 0", rows);
   if (n <= 0 || n % 32) return fail(MOE_EINVAL, "n=%d must be a positive multiple of 32", n);
   if (block != 32 && block != n)
@@ -303,6 +310,7 @@ int moe_quant_act(int32_t rows, int32_t n, int32_t block, const float *x, int8_t
 int moe_group(const moe_cfg *cfg, int32_t T, const int32_t *idx, int32_t *counts,
               int32_t *offsets, int32_t *perm, int32_t *inv, int32_t *active,
               int32_t *n_active, void *stream) {
+  clear_hip_error();  // MOE_EHIP then names this call's own launches
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
@@ -330,6 +338,7 @@ int moe_expert_ffn(const moe_cfg *cfg, int32_t T, const int8_t *q, const float *
                    const int32_t *idx, const void *experts, const void *shared,
                    float *expert_out, float *shared_out, void *workspace, size_t ws_bytes,
                    const moe_ffn_debug *dbg, void *stream) {
+  clear_hip_error();  // MOE_EHIP then names this call's own launches
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
@@ -366,6 +375,7 @@ int moe_expert_ffn(const moe_cfg *cfg, int32_t T, const int8_t *q, const float *
 int moe_combine(int32_t T, int32_t H, int32_t K, const float *expert_out, const float *w,
                 const float *shared_out, const float *residual, float *y, float *y_norm,
                 float eps, void *stream) {
+  clear_hip_error();  // MOE_EHIP then names this call's own launches
   if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
   if (H <= 0 || H % 4) return fail(MOE_EINVAL, "H=%d must be a positive multiple of 4", H);
   if (K < 0 || K > 16) return fail(MOE_EINVAL, "K=%d not in [0,16]", K);
@@ -384,7 +394,17 @@ int moe_combine(int32_t T, int32_t H, int32_t K, const float *expert_out, const 
   return launched("moe_combine");
 }
 
+int moe_mfma_peak(int32_t n_wg, int32_t iters, int32_t *out, void *stream) {
+  clear_hip_error();  // MOE_EHIP then names this call's own launches
+  if (n_wg <= 0 || n_wg > (1 << 20)) return fail(MOE_EINVAL, "n_wg=%d not in [1, 2^20]", n_wg);
+  if (iters <= 0 || iters >= (1 << 21)) return fail(MOE_EINVAL, "iters=%d not in [1, 2^21)", iters);
+  REQUIRE(out, "out");
+  moe::launch_mfma_peak(n_wg, iters, out, (hipStream_t)stream);
+  return launched("moe_mfma_peak");
+}
+
 int moe_rmsnorm(int32_t T, int32_t H, const float *x, float *y, float eps, void *stream) {
+  clear_hip_error();  // MOE_EHIP then names this call's own launches
   if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);
   if (H <= 0 || H % 4) return fail(MOE_EINVAL, "H=%d must be a positive multiple of 4", H);
   if (!(eps >= 0.0f)) return fail(MOE_EINVAL, "eps must be >= 0");
@@ -440,6 +460,7 @@ int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rou
                const void *shared, const float *residual, float *y, float *y_norm, float eps,
                int32_t *idx_out, float *w_out, void *workspace, size_t ws_bytes,
                const moe_events *ev, const moe_layer_debug *dbg, void *stream) {
+  clear_hip_error();  // MOE_EHIP then names this call's own launches
   int rc = check_cfg(cfg);
   if (rc) return rc;
   if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);

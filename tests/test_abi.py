@@ -152,6 +152,10 @@ def test_combine_and_layer_errors(L):
     assert L.moe_combine(2, 6144, 8, A, A, A + 4, None, A, None, 1e-5, None) == moe.MOE_EALIGN
     assert L.moe_combine(2, 6144, 8, A, A, None, None, A, None, -1.0, None) == moe.MOE_EINVAL
     assert L.moe_rmsnorm(2, 6144, None, A, 1e-5, None) == moe.MOE_EINVAL
+    assert L.moe_mfma_peak(0, 10, A, None) == moe.MOE_EINVAL
+    assert L.moe_mfma_peak(4, 0, A, None) == moe.MOE_EINVAL
+    assert L.moe_mfma_peak(4, 1 << 21, A, None) == moe.MOE_EINVAL
+    assert L.moe_mfma_peak(4, 10, None, None) == moe.MOE_EINVAL
     c = REAL.c()
     ws = moe.layer_workspace(REAL, 1)
     lay = L.moe_layer
