@@ -304,6 +304,14 @@ def main():
     ap.add_argument("--cache-pinned", type=int, default=-1,
                     help="slots pinned from the warm-up's recorded usage (-1 = half)")
     ap.add_argument("--cache-promote", type=int, default=2, help="promotions per layer call")
+    ap.add_argument("--cache-wait", action="store_true",
+                    help="with --cache-slots: each moe_cache_step waits for its read-back and "
+                         "copies (the synchronous cache)")
+    ap.add_argument("--lookahead", action="store_true",
+                    help="stacks with --cache-slots: route layer l+1 from layer l's input and "
+                         "prefetch its predicted experts before layer l runs")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layers of a stack workload (0 = the workload's)")
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly")
     ap.add_argument("--graph-block", type=int, default=64, help="steps per captured graph")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time")
@@ -326,9 +334,14 @@ def main():
     shape = synth.REAL.with_bits(synth.MXFP4 if args.wbits == "mxfp4" else int(args.wbits))
     T = wl["T"]
     NL = wl.get("layers", 1)
+    if NL > 1 and args.layers:
+        NL = args.layers
+    if args.lookahead and (NL < 2 or not args.cache_slots):
+        print(json.dumps({"error": "--lookahead needs a stack workload and --cache-slots"}))
+        sys.exit(2)
     # with the expert cache one layer instance by default: its steady state needs many calls
     # per layer, and eight interleaved caches each see an eighth of them
-    R = wl["ring"] if NL > 1 else (args.ring or (1 if args.cache_slots else wl["ring"]))
+    R = NL if NL > 1 else (args.ring or (1 if args.cache_slots else wl["ring"]))
     seed = synth.SEEDS[wl["seed"]]
     K, W = args.steps, args.warmup
     dev = torch.device("cuda:0")
@@ -381,6 +394,10 @@ def main():
     hbuf = [torch.empty((T, shape.hidden), dtype=torch.float32, device=dev) for _ in range(2)]
     xnbuf = [torch.empty((T, shape.hidden), dtype=torch.float32, device=dev) for _ in range(2)]
     ws = torch.zeros(moe.layer_workspace(cfg, T), dtype=torch.uint8, device=dev)
+    ws_route = torch.zeros(moe.route_workspace(cfg, T), dtype=torch.uint8, device=dev)
+    # predictions of layer l+1's routing (lookahead), kept per step for their accuracy
+    pred_all = torch.full((n_tok_steps, NL, T, shape.top_k), -1, dtype=torch.int32, device=dev)
+    pred_w = torch.empty((T, shape.top_k), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
     L = moe.lib()
@@ -393,8 +410,8 @@ def main():
                                   r["sh"].data_ptr(), res_ptr, y_ptr, yn_ptr, 1e-5, idx_ptr, None,
                                   ws.data_ptr(), ws.numel(), events, None, stream.cuda_stream)
             if rc == 0:
-                rc = L.moe_cache_step(r["cache"]._h, idx_ptr, T * shape.top_k, 0,
-                                      stream.cuda_stream)
+                rc = L.moe_cache_step(r["cache"]._h, idx_ptr, T * shape.top_k,
+                                      int(args.cache_wait), stream.cuda_stream)
         else:
             rc = L.moe_layer(ctypes.byref(c_cfg), T, x_ptr, r["wr"].data_ptr(),
                              r["bias"].data_ptr(), r["ex"].data_ptr(), r["sh"].data_ptr(),
@@ -419,6 +436,22 @@ def main():
         h_ptr = x_all[i].data_ptr()
         for l in range(NL):
             a, b = l % 2, (l + 1) % 2
+            if args.lookahead:
+                if l + 1 < NL:  # layer l+1 routed from layer l's input, its experts prefetched
+                    nxt = ring[l + 1]
+                    pred_idx = pred_all[i, l + 1]
+                    rc = L.moe_route(ctypes.byref(c_cfg), T, xnbuf[a].data_ptr(),
+                                     nxt["wr"].data_ptr(), nxt["bias"].data_ptr(),
+                                     pred_idx.data_ptr(), pred_w.data_ptr(), ws_route.data_ptr(),
+                                     ws_route.numel(), stream.cuda_stream)
+                    if rc == 0:
+                        rc = L.moe_cache_prefetch(nxt["cache"]._h, pred_idx.data_ptr(),
+                                                  T * shape.top_k, stream.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"lookahead failed: {L.moe_last_error().decode()}")
+                rc = L.moe_cache_publish(ring[l]["cache"]._h, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"moe_cache_publish failed: {L.moe_last_error().decode()}")
             call_layer(ring[l], xnbuf[a].data_ptr(), h_ptr, hbuf[b].data_ptr(),
                        xnbuf[b].data_ptr(), idx_all[i, l].data_ptr(), ev(l))
             h_ptr = hbuf[b].data_ptr()
@@ -540,6 +573,22 @@ def main():
 
     # --- work accounting ------------------------------------------------------
     idx_h = idx_all.cpu().numpy()
+
+    def lookahead_accuracy():
+        """Share of layer l+1's routed experts (l >= 0) that the prediction
+        from layer l's input named, over the timed steps."""
+        if not args.lookahead:
+            return None
+        pr = pred_all.cpu().numpy()
+        got = tot = 0
+        for i in range(W, W + K):
+            for l in range(1, NL):
+                for t in range(T):
+                    real = set(idx_h[i, l, t][idx_h[i, l, t] >= 0].tolist())
+                    got += len(real & set(pr[i, l, t].tolist()))
+                    tot += len(real)
+        return got / max(tot, 1)
+
     def distinct(v):  # routed experts of one step (-1: ranks dropped by top-p)
         return np.unique(v[v >= 0]).size
 
@@ -552,7 +601,8 @@ def main():
     cache_info = None
     if args.cache_slots:
         d = {k: sum(c1[k] - c0[k] for c0, c1 in zip(cache0, cache1))
-             for k in ("steps", "routed", "hits", "misses", "promotions", "bytes_copied")}
+             for k in ("steps", "routed", "hits", "misses", "promotions", "bytes_copied",
+                       "prefetched")}
         calls = max(d["steps"], 1)  # layer calls accounted in the timed region
         miss_bytes = d["misses"] * bb  # a missed record is streamed once over the host link
         link = (miss_bytes + d["bytes_copied"]) / calls * (K * NL) / sec / 1e9
@@ -564,6 +614,10 @@ def main():
                       "hit_rate": d["hits"] / max(d["routed"], 1),
                       "misses_per_layer_call": d["misses"] / calls,
                       "promotions_per_layer_call": d["promotions"] / calls,
+                      "prefetches_per_layer_call": d["prefetched"] / calls,
+                      "lookahead": bool(args.lookahead),
+                      "prediction_accuracy": lookahead_accuracy(),
+                      "synchronous_steps": bool(args.cache_wait),
                       "host_link_gbps": link}
     if args.cache_slots:  # bound by the host link: missed records + promotion copies
         roof = {"bound": "host-link", "kernel": "whole step (misses stream over the host link)",

@@ -384,11 +384,34 @@ int moe_layer_noalloc(const moe_cfg *cfg, int32_t T, const float *x, const float
  * entry is written on `stream` once the copy has landed (at a later call, or
  * within this call when wait != 0).  `stream` never waits for a copy; with
  * wait == 0 the host waits only when 32 read-backs are outstanding.
+ *
+ * moe_cache_prefetch — routing one layer ahead ("Comment exécuter un réseau
+ * de neurones de 744 milliards de paramètres…", section "Comment fonctionne
+ * le moteur", step 1: the next layer is routed early on a prefetch thread, a
+ * prediction right about 71 % of the time, so that expert reads overlap
+ * compute).  idx (device, n <= max_pairs entries, -1 skipped) is a predicted
+ * routing of this cache's layer, typically moe_route with this layer's
+ * router and bias on the previous layer's input, enqueued before the
+ * previous layer.  The call reads idx back (the host waits for `stream` to
+ * reach it), then starts promotions of the predicted experts that are
+ * neither resident nor being copied, at most max_promote, into LRU victims
+ * exactly as moe_cache_step does (predicted experts already resident are
+ * marked used first, so the prefetch does not evict them), and returns: the
+ * copies run on the copy stream while the caller enqueues the previous
+ * layer.  No hit, miss or usage counts change (the call has not happened);
+ * stats.prefetched counts the promotions it started.
+ * moe_cache_publish, called just before this layer's moe_layer_ptrs on the
+ * same stream, makes `stream` wait for every copy of this cache still in
+ * flight and then points their table entries at the slots (on `stream`), so
+ * the call reads them from HBM and counts them as hits.  Without it, copies
+ * are published by moe_cache_step once the host sees them landed, and
+ * `stream` never waits.
  * Results of moe_layer_ptrs do not depend on the cache state (same bytes
  * either way).  A cache is not thread-safe (caches used from different
  * threads are independent); not capturable in a HIP graph.  create
  * allocates host memory (the handle, a pinned read-back ring); destroy waits
- * for this cache's copies and frees them.
+ * for this cache's copies and frees them (create also allocates a pinned
+ * buffer of max_pairs entries for predictions).
  * Errors: MOE_EINVAL, MOE_EALIGN (slots 256-byte, table 8-byte, every host
  * record 256-byte aligned), MOE_EHIP.
  * ------------------------------------------------------------------------- */
@@ -402,6 +425,7 @@ typedef struct moe_cache_stats {
   uint64_t completed;    /* record copies landed and published */
   uint64_t bytes_copied; /* host -> HBM bytes of the promotions */
   int32_t resident;      /* experts whose entry points at HBM now */
+  uint64_t prefetched;   /* of the promotions, those moe_cache_prefetch started */
 } moe_cache_stats;
 
 /* Device-readable address of pinned host memory (hipHostGetDevicePointer). */
@@ -410,6 +434,8 @@ int moe_cache_create(const moe_cfg *cfg, int32_t n_slots, int32_t n_pinned, int3
                      int32_t max_pairs, const void *const *host_records, void *slots,
                      void *table, const uint64_t *usage, void *stream, moe_cache **out);
 int moe_cache_step(moe_cache *c, const int32_t *idx, int32_t n, int32_t wait, void *stream);
+int moe_cache_prefetch(moe_cache *c, const int32_t *idx, int32_t n, void *stream);
+int moe_cache_publish(moe_cache *c, void *stream);
 int moe_cache_get_stats(const moe_cache *c, moe_cache_stats *s);
 /* usage [E]: the recorded counts (start-up counts included), for the next
  * run's pinning; slot_of [E]: slot of each expert, -1 when read from host. */
@@ -418,10 +444,13 @@ int moe_cache_slot_of(const moe_cache *c, int32_t *slot_of);
 int moe_cache_destroy(moe_cache *c);
 /* The cache policy alone on the host, for tests: n_steps calls of n idx
  * entries each, copies landing before the next call (as with wait != 0);
- * hits/misses per call [n_steps], final slot_of [n_experts]. */
+ * pred (nullable, [n_steps][n]): a prediction prefetched before each call,
+ * its copies landed before the call; hits/misses per call [n_steps], final
+ * slot_of [n_experts]. */
 int moe_cache_simulate(int32_t n_experts, int32_t n_slots, int32_t n_pinned, int32_t max_promote,
-                       const uint64_t *usage, const int32_t *idx, int32_t n_steps, int32_t n,
-                       int32_t *hits, int32_t *misses, int32_t *slot_of);
+                       const uint64_t *usage, const int32_t *idx, const int32_t *pred,
+                       int32_t n_steps, int32_t n, int32_t *hits, int32_t *misses,
+                       int32_t *slot_of);
 
 /* ---------------------------------------------------------------------------
  * moe_mfma_peak — measurement helper, not part of the layer: n_wg workgroups

@@ -25,7 +25,8 @@ EXPORTS = (
     "moe_expert_ffn_workspace", "moe_expert_ffn", "moe_combine", "moe_rmsnorm",
     "moe_layer_workspace", "moe_layer", "moe_layer_ptrs", "moe_layer_noalloc",
     "moe_host_device_ptr", "moe_cache_create", "moe_cache_step", "moe_cache_get_stats",
-    "moe_cache_usage", "moe_cache_slot_of", "moe_cache_destroy", "moe_cache_simulate",
+    "moe_cache_prefetch", "moe_cache_publish", "moe_cache_usage", "moe_cache_slot_of", "moe_cache_destroy",
+    "moe_cache_simulate",
     "moe_mfma_peak", "moe_strerror", "moe_last_error",
 )
 
@@ -75,7 +76,8 @@ class MoeCacheStats(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_uint64), ("routed", ctypes.c_uint64),
                 ("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64),
                 ("promotions", ctypes.c_uint64), ("completed", ctypes.c_uint64),
-                ("bytes_copied", ctypes.c_uint64), ("resident", ctypes.c_int32)]
+                ("bytes_copied", ctypes.c_uint64), ("resident", ctypes.c_int32),
+                ("prefetched", ctypes.c_uint64)]
 
 
 _lib = None
@@ -135,6 +137,10 @@ def lib():
     L.moe_cache_create.restype = ctypes.c_int
     L.moe_cache_step.argtypes = [v, v, i32, i32, v]
     L.moe_cache_step.restype = ctypes.c_int
+    L.moe_cache_prefetch.argtypes = [v, v, i32, v]
+    L.moe_cache_prefetch.restype = ctypes.c_int
+    L.moe_cache_publish.argtypes = [v, v]
+    L.moe_cache_publish.restype = ctypes.c_int
     L.moe_cache_get_stats.argtypes = [v, ctypes.POINTER(MoeCacheStats)]
     L.moe_cache_get_stats.restype = ctypes.c_int
     L.moe_cache_usage.argtypes = [v, u64p]
@@ -143,7 +149,8 @@ def lib():
     L.moe_cache_slot_of.restype = ctypes.c_int
     L.moe_cache_destroy.argtypes = [v]
     L.moe_cache_destroy.restype = ctypes.c_int
-    L.moe_cache_simulate.argtypes = [i32, i32, i32, i32, u64p, i32p, i32, i32, i32p, i32p, i32p]
+    L.moe_cache_simulate.argtypes = [i32, i32, i32, i32, u64p, i32p, i32p, i32, i32, i32p, i32p,
+                                     i32p]
     L.moe_cache_simulate.restype = ctypes.c_int
     L.moe_strerror.argtypes = [ctypes.c_int]
     L.moe_strerror.restype = ctypes.c_char_p
@@ -474,6 +481,15 @@ class ExpertCache:
     def step(self, idx, wait=False):
         _check(lib().moe_cache_step(self._h, _ptr(idx), idx.numel(), int(bool(wait)), _stream()))
 
+    def prefetch(self, idx):
+        """moe_cache_prefetch: start promotions of a predicted idx (device)."""
+        _check(lib().moe_cache_prefetch(self._h, _ptr(idx), idx.numel(), _stream()))
+
+    def publish(self):
+        """moe_cache_publish: the stream waits for this cache's copies in flight
+        and their entries point at the slots."""
+        _check(lib().moe_cache_publish(self._h, _stream()))
+
     def stats(self) -> dict:
         s = MoeCacheStats()
         _check(lib().moe_cache_get_stats(self._h, ctypes.byref(s)))
@@ -503,10 +519,16 @@ class ExpertCache:
             pass
 
 
-def cache_simulate(n_experts, n_slots, n_pinned, max_promote, idx, usage=None):
-    """The cache policy alone (host): per-step hits and misses, final slot_of."""
+def cache_simulate(n_experts, n_slots, n_pinned, max_promote, idx, usage=None, pred=None):
+    """The cache policy alone (host): per-step hits and misses, final slot_of;
+    pred: optional per-step predictions prefetched before each step."""
     import numpy as np
     idx = np.ascontiguousarray(idx, dtype=np.int32)
+    pp = None
+    if pred is not None:
+        pred = np.ascontiguousarray(pred, dtype=np.int32)
+        assert pred.shape == idx.shape
+        pp = pred.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     n_steps = idx.shape[0]
     n = idx[0].size if n_steps else 0
     hits = np.zeros(n_steps, np.int32)
@@ -518,7 +540,7 @@ def cache_simulate(n_experts, n_slots, n_pinned, max_promote, idx, usage=None):
         u = usage.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))
     i32p = ctypes.POINTER(ctypes.c_int32)
     _check(lib().moe_cache_simulate(n_experts, n_slots, n_pinned, max_promote, u,
-                                    idx.ctypes.data_as(i32p), n_steps, n,
+                                    idx.ctypes.data_as(i32p), pp, n_steps, n,
                                     hits.ctypes.data_as(i32p), misses.ctypes.data_as(i32p),
                                     slot_of.ctypes.data_as(i32p)))
     return hits, misses, slot_of

@@ -22,6 +22,18 @@
 //     stream never waits for a copy.
 //   - Slots [0, n_pinned) hold the experts with the largest recorded usage
 //     (the learning cache's pinning), loaded at creation; the others are LRU.
+//   - Routing one layer ahead ("Comment exécuter un réseau de neurones de 744
+//     milliards de paramètres...", section "Comment fonctionne le moteur",
+//     step 1: a prefetch thread routes the next layer early, a prediction
+//     right about 71 % of the time, so that its reads overlap compute):
+//     moe_cache_prefetch takes a predicted idx for this cache's layer (the
+//     caller routes it with this layer's router on the previous layer's
+//     input) and starts promotions of the predicted experts at once, so their
+//     copies run while the previous layer computes; moe_cache_publish, just
+//     before this layer's call, makes the caller's stream wait for the
+//     copies still in flight and points their entries at the slots.  A
+//     wrong prediction costs a copy and an LRU slot, never a result: the
+//     layer reads whatever the table points at.
 //
 // The policy (Policy below) is plain host code, also run by
 // moe_cache_simulate for tests without a GPU.
@@ -83,12 +95,13 @@ struct Policy {
     expert_in[s] = e;
   }
 
-  // LRU victim among the unpinned slots that are not being copied: an empty
-  // one first (lowest index), else the least recently used (ties: lower).
-  int victim() const {
+  // LRU victim among the unpinned slots that are not being copied (nor
+  // marked in keep): an empty one first (lowest index), else the least
+  // recently used (ties: lower).
+  int victim(const std::vector<char> *keep = nullptr) const {
     int best = -1;
     for (int s = P; s < S; s++) {
-      if (pending[s]) continue;
+      if (pending[s] || (keep && (*keep)[s])) continue;
       if (expert_in[s] < 0) return s;
       if (best < 0 || last_use[s] < last_use[best]) best = s;
     }
@@ -135,6 +148,42 @@ struct Policy {
       out.push_back(Promotion{e, v, old});
       promoted++;
       st.promotions++;
+    }
+  }
+
+  // Predicted experts of the layer's next call (any order, -1 skipped):
+  // resident ones are marked used now and are no victims of this prefetch;
+  // the others that are not being copied take LRU victims, at most
+  // max_promote.  No usage or hit counts: the call has not happened.
+  void prefetch(const int32_t *idx, int n, std::vector<Promotion> &out) {
+    std::vector<int> U;
+    for (int i = 0; i < n; i++)
+      if (idx[i] >= 0 && idx[i] < E) U.push_back(idx[i]);
+    std::sort(U.begin(), U.end());
+    U.erase(std::unique(U.begin(), U.end()), U.end());
+    std::vector<char> keep(S, 0);
+    for (int e : U)
+      if (slot_of[e] >= 0) {
+        last_use[slot_of[e]] = step;
+        keep[slot_of[e]] = 1;
+      }
+    int promoted = 0;
+    for (int e : U) {
+      if (slot_of[e] >= 0) continue;
+      bool in_flight = false;
+      for (int t = 0; t < S; t++) in_flight |= (pending[t] && expert_in[t] == e);
+      if (in_flight || promoted >= max_promote) continue;
+      const int v = victim(&keep);
+      if (v < 0) continue;
+      const int old = expert_in[v];
+      if (old >= 0) slot_of[old] = -1;
+      expert_in[v] = e;
+      pending[v] = 1;
+      last_use[v] = step;
+      out.push_back(Promotion{e, v, old});
+      promoted++;
+      st.promotions++;
+      st.prefetched++;
     }
   }
 
@@ -196,9 +245,12 @@ struct moe_cache {
   int ring_n[R] = {};
   std::vector<char> ring_res[R];
   uint64_t head = 0, tail = 0;  // entries [tail, head) are in flight
+  int32_t *pred = nullptr;      // pinned [max_pairs]: a predicted idx read back
+  hipEvent_t pred_ev = nullptr;
   struct Copy {
     int slot;
     hipEvent_t after_table, done;
+    bool published;  // entry already written on a stream that waited for the copy
   };
   std::vector<Copy> copies;
 };
@@ -222,7 +274,7 @@ int start_promotions(moe_cache *c, const std::vector<moe::Promotion> &pr, hipStr
   hipError_t e = moe::set_ptrs(c->table, back, st);
   if (e != hipSuccess) return hip_fail("moe_cache_step (table)", e);
   for (const auto &p : pr) {
-    moe_cache::Copy cp{p.slot, nullptr, nullptr};
+    moe_cache::Copy cp{p.slot, nullptr, nullptr, false};
     if ((e = hipEventCreateWithFlags(&cp.after_table, hipEventDisableTiming)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&cp.done, hipEventDisableTiming)) != hipSuccess ||
         (e = hipEventRecord(cp.after_table, st)) != hipSuccess ||
@@ -249,8 +301,10 @@ int finish_copies(moe_cache *c, bool wait, hipStream_t st) {
       continue;
     }
     if (e != hipSuccess) return hip_fail("moe_cache_step (copy event)", e);
-    c->pol.complete(cp.slot);
-    upd.push_back({c->pol.expert_in[cp.slot], c->slots + (size_t)cp.slot * c->blob_bytes});
+    if (!cp.published) {
+      c->pol.complete(cp.slot);
+      upd.push_back({c->pol.expert_in[cp.slot], c->slots + (size_t)cp.slot * c->blob_bytes});
+    }
     hipEventDestroy(cp.after_table);
     hipEventDestroy(cp.done);
   }
@@ -310,6 +364,8 @@ void release(moe_cache *c) {
   for (int r = 0; r < moe_cache::R; r++)
     if (c->ring_ev[r]) hipEventDestroy(c->ring_ev[r]);
   if (c->ring) hipHostFree(c->ring);
+  if (c->pred_ev) hipEventDestroy(c->pred_ev);
+  if (c->pred) hipHostFree(c->pred);
   delete c;
 }
 
@@ -369,6 +425,16 @@ int moe_cache_create(const moe_cfg *cfg, int32_t n_slots, int32_t n_pinned, int3
       release(c);
       return hip_fail("moe_cache_create (events)", e);
     }
+  if ((e = hipHostMalloc((void **)&c->pred, sizeof(int32_t) * max_pairs)) != hipSuccess) {
+    c->pred = nullptr;
+    release(c);
+    return hip_fail("moe_cache_create (pinned prediction buffer)", e);
+  }
+  if ((e = hipEventCreateWithFlags(&c->pred_ev, hipEventDisableTiming)) != hipSuccess) {
+    c->pred_ev = nullptr;
+    release(c);
+    return hip_fail("moe_cache_create (events)", e);
+  }
   // every entry to host memory, then the pinned hot store
   std::vector<std::pair<int, const void *>> init;
   for (int x = 0; x < E; x++) init.push_back({x, c->host[x]});
@@ -416,6 +482,43 @@ int moe_cache_step(moe_cache *c, const int32_t *idx, int32_t n, int32_t wait, vo
   return MOE_OK;
 }
 
+int moe_cache_prefetch(moe_cache *c, const int32_t *idx, int32_t n, void *stream) {
+  (void)hipGetLastError();  // a failure reported below is then this call's own
+  if (!c || (n > 0 && !idx)) return moe::set_error(MOE_EINVAL, "moe_cache_prefetch: NULL argument");
+  if (n < 0 || n > c->max_pairs)
+    return moe::set_error(MOE_EINVAL, "moe_cache_prefetch: n outside [0, max_pairs]");
+  if (n == 0) return MOE_OK;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = hipMemcpyAsync(c->pred, idx, sizeof(int32_t) * n, hipMemcpyDeviceToHost, st)) !=
+          hipSuccess ||
+      (e = hipEventRecord(c->pred_ev, st)) != hipSuccess ||
+      (e = hipEventSynchronize(c->pred_ev)) != hipSuccess)
+    return hip_fail("moe_cache_prefetch (idx read-back)", e);
+  int rc = finish_copies(c, false, st);  // landed copies free their slots' pending state
+  if (rc) return rc;
+  std::vector<moe::Promotion> pr;
+  c->pol.prefetch(c->pred, n, pr);
+  return start_promotions(c, pr, st);
+}
+
+int moe_cache_publish(moe_cache *c, void *stream) {
+  (void)hipGetLastError();  // a failure reported below is then this call's own
+  if (!c) return moe::set_error(MOE_EINVAL, "moe_cache_publish: NULL argument");
+  hipStream_t st = (hipStream_t)stream;
+  std::vector<std::pair<int, const void *>> upd;
+  for (auto &cp : c->copies) {
+    if (cp.published) continue;
+    hipError_t e = hipStreamWaitEvent(st, cp.done, 0);
+    if (e != hipSuccess) return hip_fail("moe_cache_publish (wait)", e);
+    cp.published = true;
+    c->pol.complete(cp.slot);
+    upd.push_back({c->pol.expert_in[cp.slot], c->slots + (size_t)cp.slot * c->blob_bytes});
+  }
+  hipError_t e = moe::set_ptrs(c->table, upd, st);
+  return e == hipSuccess ? MOE_OK : hip_fail("moe_cache_publish (table)", e);
+}
+
 int moe_cache_get_stats(const moe_cache *c, moe_cache_stats *s) {
   if (!c || !s) return moe::set_error(MOE_EINVAL, "moe_cache_get_stats: NULL argument");
   *s = c->pol.st;
@@ -443,8 +546,9 @@ int moe_cache_destroy(moe_cache *c) {
 }
 
 int moe_cache_simulate(int32_t n_experts, int32_t n_slots, int32_t n_pinned, int32_t max_promote,
-                       const uint64_t *usage, const int32_t *idx, int32_t n_steps, int32_t n,
-                       int32_t *hits, int32_t *misses, int32_t *slot_of) {
+                       const uint64_t *usage, const int32_t *idx, const int32_t *pred,
+                       int32_t n_steps, int32_t n, int32_t *hits, int32_t *misses,
+                       int32_t *slot_of) {
   if (n_experts < 1 || n_slots < 0 || n_pinned < 0 || n_pinned > n_slots || max_promote < 0 ||
       n_steps < 0 || n < 0 || (n_steps > 0 && !idx) || !hits || !misses || !slot_of)
     return moe::set_error(MOE_EINVAL, "moe_cache_simulate: bad argument");
@@ -454,6 +558,11 @@ int moe_cache_simulate(int32_t n_experts, int32_t n_slots, int32_t n_pinned, int
   for (size_t i = 0; i < pin.size(); i++) p.place(pin[i], (int)i);
   if (usage) p.usage.assign(usage, usage + n_experts);
   for (int t = 0; t < n_steps; t++) {
+    if (pred) {  // the step's prediction, its copies landed before the step
+      std::vector<moe::Promotion> pp;
+      p.prefetch(pred + (size_t)t * n, n, pp);
+      for (const auto &x : pp) p.complete(x.slot);
+    }
     const moe_cache_stats before = p.st;
     std::vector<moe::Promotion> pr;
     p.account(idx + (size_t)t * n, n, p.residency(), pr);

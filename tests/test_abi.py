@@ -226,6 +226,8 @@ def test_cache_create_rejects_bad_arguments(L):
                               ctypes.c_void_p(A), None, None, ctypes.byref(out)) == moe.MOE_EALIGN
     assert not out.value
     assert L.moe_cache_step(None, ctypes.c_void_p(A), 8, 0, None) == moe.MOE_EINVAL
+    assert L.moe_cache_prefetch(None, ctypes.c_void_p(A), 8, None) == moe.MOE_EINVAL
+    assert L.moe_cache_publish(None, None) == moe.MOE_EINVAL
 
 
 def test_layer_ptrs_rejects_null_table(L):

@@ -7,12 +7,16 @@ import pytest
 import int4_routed_expert_moe_amd as moe
 
 
-def model(E, S, P, max_promote, idx_steps, usage=None):
+def model(E, S, P, max_promote, idx_steps, usage=None, pred_steps=None):
     """Slots [0, P) pinned with the most used experts; on each step the
     distinct routed experts hit if resident when the step starts (and are
     marked used); then up to max_promote misses (ascending) take an unpinned
     slot: an empty one (lowest), else the one used or filled longest ago
-    (lowest on ties)."""
+    (lowest on ties).  With predictions, before step t the distinct
+    predicted experts are handled the same way, stamped with the previous
+    step (resident ones refreshed first and kept, then up to max_promote
+    others placed in slots neither kept nor filled by this prefetch), their
+    copies landed before the step."""
     occupant = [None] * S
     stamp = [0] * S
     if usage is not None:
@@ -20,7 +24,35 @@ def model(E, S, P, max_promote, idx_steps, usage=None):
         for s, e in enumerate(ranked[:P]):
             occupant[s] = e
     hits, misses = [], []
+
+    def place(wanted, t_stamp):
+        resident = {occupant[s]: s for s in range(S) if occupant[s] is not None}
+        for e in wanted:  # every resident expert of the step is fresh first
+            if e in resident:
+                stamp[resident[e]] = t_stamp
+        promoted = 0
+        # slots of predicted experts, and those filled by this batch (their
+        # copies are in flight), are no victims
+        busy = {resident[e] for e in wanted if e in resident}
+        for e in wanted:
+            if e in resident or promoted == max_promote:
+                continue
+            free = [s for s in range(P, S) if occupant[s] is None and s not in busy]
+            cand = [k for k in range(P, S) if k not in busy]
+            if free:
+                s = free[0]
+            elif cand:
+                s = min(cand, key=lambda k: (stamp[k], k))
+            else:
+                continue
+            busy.add(s)
+            occupant[s] = e
+            stamp[s] = t_stamp
+            promoted += 1
+
     for t, row in enumerate(idx_steps, start=1):
+        if pred_steps is not None:
+            place(sorted({int(e) for e in pred_steps[t - 1] if e >= 0}), t - 1)
         routed = sorted({int(e) for e in row if e >= 0})
         resident = {occupant[s]: s for s in range(S) if occupant[s] is not None}
         h = sum(e in resident for e in routed)
@@ -109,3 +141,77 @@ def test_pinned_experts_stay_and_always_hit():
     assert [slot_of[e] for e in hot] == list(range(6))
     total = np.array([np.unique(r).size for r in steps])
     assert np.all(hits >= 1) and np.array_equal(hits + misses, total)
+
+
+def predictions(rng, steps, E, right=0.7):
+    """Each entry of the true routing kept with probability `right`, else a
+    random expert (or -1)."""
+    pred = steps.copy()
+    wrong = rng.random(steps.shape) >= right
+    pred[wrong] = rng.integers(-1, E, size=int(wrong.sum()))
+    return pred
+
+
+@pytest.mark.parametrize("E,S,P,K,mp", [(8, 3, 1, 2, 2), (64, 16, 4, 8, 2), (256, 64, 16, 8, 1),
+                                        (256, 128, 0, 8, 8), (32, 32, 8, 4, 4)])
+def test_simulator_with_prefetch_matches_model(E, S, P, K, mp):
+    rng = np.random.default_rng(7 * E + S + P)
+    steps = zipf_steps(rng, E, K, 300)
+    steps[rng.random(steps.shape) < 0.1] = -1
+    pred = predictions(rng, steps, E)
+    usage = np.bincount(zipf_steps(rng, E, K, 50).ravel(), minlength=E).astype(np.uint64)
+    for u in (None, usage):
+        got = moe.cache_simulate(E, S, P, mp, steps, usage=u, pred=pred)
+        want = model(E, S, P, mp, steps, usage=u, pred_steps=pred)
+        for g, w in zip(got, want):
+            assert np.array_equal(g, w)
+
+
+def test_exact_prediction_never_misses():
+    """Predictions equal to the routing, room for a step's experts and a
+    promotion budget that covers them: every routed expert is resident when
+    its step runs, however the routing moves."""
+    rng = np.random.default_rng(3)
+    E, K = 64, 8
+    steps = np.stack([rng.choice(E, K, replace=False) for _ in range(100)]).astype(np.int32)
+    hits, misses, _ = moe.cache_simulate(E, K, 0, K, steps, pred=steps)
+    assert misses.sum() == 0 and hits.sum() == steps.size
+    # without the prediction the same cache misses nearly every time
+    hits0, misses0, _ = moe.cache_simulate(E, K, 0, K, steps)
+    assert misses0.sum() > steps.size // 2
+
+
+def test_prefetch_keeps_predicted_residents():
+    """Two LRU slots hold experts 1 and 2; a prediction of {1, 3} brings 3
+    into the slot of 2 (the only one not predicted), never into 1's, even
+    though both slots were last used at the same step."""
+    steps = np.array([[1, 2], [1, 3]], np.int32)
+    pred = np.array([[1, 2], [1, 3]], np.int32)
+    hits, misses, slot_of = moe.cache_simulate(8, 2, 0, 2, steps, pred=pred)
+    assert hits.tolist() == [2, 2] and misses.tolist() == [0, 0]
+    assert slot_of[1] == 0 and slot_of[3] == 1 and slot_of[2] == -1
+
+
+def test_wrong_prediction_changes_only_residency():
+    """Predictions of experts never routed: they take LRU slots (so later
+    steps can lose hits) but hits + misses still count each routed expert
+    once per step."""
+    rng = np.random.default_rng(4)
+    E, K = 32, 4
+    steps = zipf_steps(rng, E, K, 200)
+    pred = (steps + 16) % E  # a different expert for every entry
+    hits, misses, _ = moe.cache_simulate(E, 12, 2, 2, steps, pred=pred)
+    routed = np.array([len(set(r.tolist())) for r in steps])
+    assert np.array_equal(hits + misses, routed)
+
+
+def test_prefetch_helps_a_near_prediction():
+    """A prediction right most of the time (70 %, as the pages report for
+    routing one layer ahead) raises the hit count of the same cache."""
+    rng = np.random.default_rng(5)
+    E, K, S = 256, 8, 64
+    steps = zipf_steps(rng, E, K, 400)
+    pred = predictions(rng, steps, E, right=0.7)
+    h0, _, _ = moe.cache_simulate(E, S, 0, 2, steps)
+    h1, _, _ = moe.cache_simulate(E, S, 0, 2, steps, pred=pred)
+    assert h1.sum() > h0.sum()

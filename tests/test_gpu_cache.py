@@ -8,7 +8,7 @@ import torch
 
 import int4_routed_expert_moe_amd as moe
 import synth
-from _inputs import DeviceLayer
+from _inputs import DeviceLayer, assert_close_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +158,67 @@ def test_two_layers_share_the_copy_stream(dev):
         assert st["hits"] + st["misses"] == st["routed"]
         assert st["completed"] <= st["promotions"] and st["resident"] <= 3
         c.close()
+
+
+def test_routing_one_layer_ahead(dev):
+    """Three tiny layers in a pre-norm stack, each with a 3-slot cache (no
+    pinning): before layer l runs, layer l+1's routing is predicted from
+    layer l's input (moe_route with layer l+1's router) and prefetched into
+    layer l+1's cache.  The prediction is bit-exact against the oracle's
+    routing of that input; every layer output is bit-identical to moe_layer
+    on the HBM records, and the first step's against the oracle; the cache
+    with prefetch counts its prefetches, and its counts stay consistent."""
+    import oracle
+    shape = synth.TINY
+    L = 3
+    lays = [DeviceLayer(shape, synth.SEEDS["tiny"], layer, bias="zipf") for layer in range(L)]
+    cfg = moe.Config.of(shape)
+    K = shape.top_k
+
+    def run(prefetch):
+        caches = [moe.ExpertCache(cfg, pinned_records(lay), n_slots=3, n_pinned=0,
+                                  max_promote=2, max_pairs=8) for lay in lays]
+        outs = []
+        for step in range(16):
+            hcur = torch.from_numpy(synth.tokens(shape, 900 + step, 2)).to(dev)
+            xn = moe.rmsnorm(hcur)
+            for l in range(L):
+                lay = lays[l]
+                if prefetch and l + 1 < L:
+                    nxt = lays[l + 1]
+                    pi, _ = moe.route(cfg, xn, nxt.wr_d, nxt.bias_d)
+                    ri, _, _ = oracle.route(h(xn), nxt.wr, nxt.bias, shape.n_group,
+                                            shape.topk_group, K, shape.routed_scaling)
+                    assert np.array_equal(h(pi), ri), (step, l)
+                    caches[l + 1].prefetch(pi.view(-1))
+                if prefetch:
+                    caches[l].publish()
+                i1 = torch.empty((2, K), dtype=torch.int32, device=dev)
+                y1, yn1 = moe.layer_ptrs(cfg, xn, lay.wr_d, lay.bias_d, caches[l].table,
+                                         lay.shared_d, residual=hcur, want_norm=True,
+                                         idx_out=i1)
+                y2, yn2 = moe.layer(cfg, xn, lay.wr_d, lay.bias_d, lay.experts_d, lay.shared_d,
+                                    residual=hcur, want_norm=True)
+                assert np.array_equal(h(y1).view(np.uint32), h(y2).view(np.uint32))
+                assert np.array_equal(h(yn1).view(np.uint32), h(yn2).view(np.uint32))
+                if step == 0:
+                    ref = lay.oracle_layer(h(xn), residual=h(hcur), want_norm=True)
+                    assert np.array_equal(h(i1), ref["idx"])
+                    assert_close_rms(h(y1), ref["y"], 2e-3, f"layer {l}")
+                caches[l].step(i1.view(-1), wait=not prefetch)
+                outs.append(h(y1))
+                hcur, xn = y1, yn1
+        stats = [c.stats() for c in caches]
+        for c in caches:
+            c.close()
+        return outs, stats
+
+    outs0, st0 = run(False)
+    outs1, st1 = run(True)
+    for a, b in zip(outs0, outs1):  # the cache state never changes a result
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    for l in range(L):
+        assert st1[l]["hits"] + st1[l]["misses"] == st1[l]["routed"]
+        assert st0[l]["prefetched"] == 0
+    assert st1[0]["prefetched"] == 0  # nothing routes layer 0 ahead
+    assert sum(s["prefetched"] for s in st1[1:]) > 0
