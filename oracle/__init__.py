@@ -27,6 +27,8 @@ _lib = None
 
 
 MXFP4 = -4  # weight-format code of MXFP4 experts (reading R16)
+FP8 = -8  # weight-format code of FP8 E4M3 experts with 128x128 block scales (reading R18)
+F8BLK = 128
 ACT_Q8_0, ACT_ROW = 32, -1  # activation formats: Q8_0 blocks of 32 (R6), one scale per row (R17)
 
 def build() -> str:
@@ -86,6 +88,8 @@ def lib():
     L.oracle_fp4_value.restype = ctypes.c_double
     L.oracle_e8m0_value.argtypes = [c_i]
     L.oracle_e8m0_value.restype = ctypes.c_double
+    L.oracle_fp8_value.argtypes = [c_i]
+    L.oracle_fp8_value.restype = ctypes.c_double
     L.oracle_top_p.argtypes = [c_i, c_i, c_i, c_f, c_f, c_v, c_v, c_v, c_v]
     L.oracle_top_p.restype = c_i
     L.oracle_group.argtypes = [c_i, c_i, c_i, c_v, c_v, c_v, c_v, c_v, c_v, c_v]
@@ -144,7 +148,7 @@ def code(row: np.ndarray, wbits: int, k: int) -> int:
 
 
 def _bits(wbits: int) -> int:
-    return 4 if wbits == MXFP4 else wbits
+    return 4 if wbits == MXFP4 else 8 if wbits == FP8 else wbits
 
 
 def unpack(row: np.ndarray, wbits: int, n: int) -> np.ndarray:
@@ -291,13 +295,28 @@ def e8m0_value(s: int) -> float:
     return float(lib().oracle_e8m0_value(s))
 
 
+def fp8_value(code: int) -> float:
+    """R18: value of an FP8 E4M3 code byte (NaN for 0x7F, 0xFF)."""
+    return float(lib().oracle_fp8_value(code))
+
+
 def blob_bytes(H, I, wbits=4) -> int:
     return int(lib().oracle_blob_bytes(H, I, wbits))
 
 
 def blob_view(blob: np.ndarray, H: int, I: int, wbits: int = 4):
     """Split a packed expert record into (gate, up, down code rows, scales);
-    MXFP4: the scales are the per-block E8M0 bytes [rows][n/32]."""
+    MXFP4: the scales are the per-block E8M0 bytes [rows][n/32]; FP8: the
+    fp32 128x128 block scales [rows/128][n/128]."""
+    if wbits == FP8:
+        gate = blob[: I * H].reshape(I, H)
+        up = blob[I * H: 2 * I * H].reshape(I, H)
+        down = blob[2 * I * H: 3 * I * H].reshape(H, I)
+        sc = blob[3 * I * H:].view(np.float32)
+        nb = (I // F8BLK) * (H // F8BLK)
+        return (gate, up, down, sc[:nb].reshape(I // F8BLK, H // F8BLK),
+                sc[nb:2 * nb].reshape(I // F8BLK, H // F8BLK),
+                sc[2 * nb:3 * nb].reshape(H // F8BLK, I // F8BLK))
     if wbits == MXFP4:
         gr, dr = H // 2, I // 2
         gate = blob[: I * gr].reshape(I, gr)

@@ -58,6 +58,20 @@
  *     Activations stay Q8_0 (the engine's integer kernels take them), so a
  *     row is sum_b 2^(s_b-127) * d_b * sum_k fp4(c_k) q_k; the integer block
  *     dot reported for it is P2 = sum_k (2 fp4(c_k)) q_k (2 fp4 is an integer).
+ *  R18 FP8 experts (wbits code ORACLE_FP8 below): one page says a supported
+ *     model runs on fp4/fp8 weights, another that the engine's converter
+ *     dequantises FP8 checkpoints with one scale per 128x128 block.  The
+ *     format is therefore OCP FP8 E4M3 ("FN": sign bit, 4-bit exponent with
+ *     bias 7, 3-bit mantissa, no infinities; codes 0x7F and 0xFF are NaN and
+ *     not valid weights; normal value (1 + m/8) 2^(e-7), subnormal (e = 0)
+ *     m 2^-9, largest 448), one byte per element, and one fp32 scale per
+ *     128x128 block of each matrix.  Record: gate codes [I][H], up [I][H],
+ *     down [H][I], then the fp32 block scales gate [I/128][H/128], up
+ *     [I/128][H/128], down [H/128][I/128].  Activations stay Q8_0, so a row r
+ *     is sum_b S[r/128][b/4] * d_b * sum_k fp8(c_k) q_k over the 32-blocks
+ *     b; since 512 fp8 is an integer (|512 fp8| <= 229376), the block dot
+ *     P9 = sum_k (512 fp8(c_k)) q_k is exact in int32 and is what the debug
+ *     dumps report (the row is then sum_b S * d_b * P9_b / 512).
  *  R15 adaptive expert top-p (p in (0,1); 0 or 1 = off): after the top-K
  *     selection, keep the shortest prefix of the rank order whose unbiased
  *     scores, summed left to right in fp32, reach p * S (fp32 product; S as
@@ -88,6 +102,8 @@
 /* ---------------------------------------------------------------- codes */
 
 #define ORACLE_MXFP4 (-4)
+#define ORACLE_FP8 (-8)
+#define F8BLK 128
 
 /* R16: value of an FP4 E2M1 code (0..15) and of an E8M0 scale byte. */
 double oracle_fp4_value(int code) {
@@ -97,8 +113,19 @@ double oracle_fp4_value(int code) {
 }
 double oracle_e8m0_value(int s) { return ldexp(1.0, s - 127); }
 
+/* R18: value of an FP8 E4M3 code (0..255); NaN for 0x7F and 0xFF. */
+double oracle_fp8_value(int code) {
+  const int e = (code >> 3) & 15, m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(1.0 + m / 8.0, e - 7);
+  return (code & 0x80) ? -v : v;
+}
+
 /* Element k of a packed weight row (R10; MXFP4: the raw 4-bit code, R16). */
 int oracle_code(const uint8_t *row, int wbits, int k) {
+  if (wbits == ORACLE_FP8) return row[k];  /* the raw byte, R18 */
   if (wbits == ORACLE_MXFP4) {
     int b = row[k / 2];
     return (k % 2 == 0) ? (b & 0xF) : ((b >> 4) & 0xF);
@@ -133,7 +160,7 @@ int oracle_pack(const int8_t *codes, int n, int wbits, uint8_t *out) {
     }
     return 0;
   }
-  if (wbits == 8) {  /* one two's-complement byte per code */
+  if (wbits == 8 || wbits == ORACLE_FP8) {  /* one byte per code (FP8: the raw byte) */
     for (int k = 0; k < n; k++) out[k] = (uint8_t)codes[k];
     return 0;
   }
@@ -417,12 +444,15 @@ int oracle_group(int T, int K, int E, const int32_t *idx, int32_t *counts,
 int oracle_act_dots(const uint8_t *row, int wbits, const int8_t *q, int n, int ablk,
                     int32_t *out) {
   const int B = act_len(ablk, n);
-  if (B <= 0 || n % B || (wbits == ORACLE_MXFP4 && B != QBLK)) return -1;
+  if (B <= 0 || n % B || ((wbits == ORACLE_MXFP4 || wbits == ORACLE_FP8) && B != QBLK)) return -1;
   for (int b = 0; b < n / B; b++) {
     int64_t acc = 0;
     for (int k = b * B; k < (b + 1) * B; k++) {
       const int c = oracle_code(row, wbits, k);
-      const int64_t wv = wbits == ORACLE_MXFP4 ? (int64_t)(2.0 * oracle_fp4_value(c)) : c;
+      if (wbits == ORACLE_FP8 && isnan(oracle_fp8_value(c))) return -1;
+      const int64_t wv = wbits == ORACLE_MXFP4 ? (int64_t)(2.0 * oracle_fp4_value(c))
+                         : wbits == ORACLE_FP8 ? (int64_t)(512.0 * oracle_fp8_value(c))
+                                               : c;
       acc += wv * (int64_t)q[k];
     }
     if (acc > INT32_MAX || acc < INT32_MIN) return -1;
@@ -436,6 +466,8 @@ int oracle_block_dots(const uint8_t *row, int wbits, const int8_t *q, int n, int
 }
 
 size_t oracle_blob_bytes(int H, int I, int wbits) {
+  if (wbits == ORACLE_FP8)  /* R18: byte codes, one fp32 scale per 128x128 block */
+    return (size_t)3 * I * H + sizeof(float) * 3 * (size_t)(I / F8BLK) * (H / F8BLK);
   if (wbits == ORACLE_MXFP4)  /* R16: 4-bit codes, one scale byte per 32 */
     return ((size_t)2 * I * H + (size_t)H * I) / 2 + ((size_t)2 * I * H + (size_t)H * I) / QBLK;
   return ((size_t)2 * I * H + (size_t)H * I) * (size_t)wbits / 8 +
@@ -446,12 +478,13 @@ typedef struct {
   const uint8_t *gate, *up, *down;
   const float *sg, *su, *sd;        /* per-row scales (integer codes) */
   const uint8_t *bg, *bu, *bd;      /* per-block E8M0 scales (MXFP4) */
+  const float *fg, *fu, *fd;        /* 128x128 block scales (FP8) */
   size_t gate_row, down_row;
 } blob_view;
 
 static blob_view view_of(const uint8_t *blob, int H, int I, int wbits) {
   blob_view v;
-  const int bits = wbits == ORACLE_MXFP4 ? 4 : wbits;
+  const int bits = wbits == ORACLE_MXFP4 ? 4 : wbits == ORACLE_FP8 ? 8 : wbits;
   v.gate_row = (size_t)H * bits / 8;
   v.down_row = (size_t)I * bits / 8;
   v.gate = blob;
@@ -460,7 +493,14 @@ static blob_view view_of(const uint8_t *blob, int H, int I, int wbits) {
   const uint8_t *tail = v.down + (size_t)H * v.down_row;
   v.sg = v.su = v.sd = NULL;
   v.bg = v.bu = v.bd = NULL;
-  if (wbits == ORACLE_MXFP4) {
+  v.fg = v.fu = v.fd = NULL;
+  if (wbits == ORACLE_FP8) {
+    const float *sc = (const float *)tail;
+    const size_t nb = (size_t)(I / F8BLK) * (H / F8BLK);
+    v.fg = sc;
+    v.fu = sc + nb;
+    v.fd = sc + 2 * nb;
+  } else if (wbits == ORACLE_MXFP4) {
     v.bg = tail;
     v.bu = tail + (size_t)I * (H / QBLK);
     v.bd = tail + 2 * (size_t)I * (H / QBLK);
@@ -478,8 +518,8 @@ static blob_view view_of(const uint8_t *blob, int H, int I, int wbits) {
  * scale_r * sum_b d_b * P_b; MXFP4 (bsc: the row's block scales, Q8_0 only)
  * sum_b 2^(s_b-127) * d_b * P2_b / 2. */
 static double row_value(const uint8_t *row, int wbits, int ablk, float scale,
-                        const uint8_t *bsc, const int8_t *q, const float *d, int n,
-                        int32_t *dots_out, int *err) {
+                        const uint8_t *bsc, const float *fsc, const int8_t *q, const float *d,
+                        int n, int32_t *dots_out, int *err) {
   const int B = act_len(ablk, n);
   if (B <= 0) {
     *err = 1;
@@ -501,6 +541,12 @@ static double row_value(const uint8_t *row, int wbits, int ablk, float scale,
     free(tmp);
     return acc;
   }
+  if (fsc) {  /* R18: the 128-block scale of each group of four 32-blocks */
+    for (int b = 0; b < nb; b++)
+      acc += (double)fsc[b / (F8BLK / QBLK)] * (double)d[b] * ((double)dots[b] / 512.0);
+    free(tmp);
+    return acc;
+  }
   for (int b = 0; b < nb; b++) acc += (double)d[b] * (double)dots[b];
   free(tmp);
   return (double)scale * acc;
@@ -516,18 +562,20 @@ int oracle_gate_up_act(const uint8_t *blob, int H, int I, int wbits, int ablk, c
                        double *u_out, float *h) {
   const int B = act_len(ablk, H);
   if (H % QBLK || I % QBLK || B <= 0) return -1;
+  if (wbits == ORACLE_FP8 && (H % F8BLK || I % F8BLK)) return -1;
   blob_view v = view_of(blob, H, I, wbits);
   int err = 0;
 #pragma omp parallel for schedule(static) reduction(| : err)
   for (int r = 0; r < I; r++) {
     int e1 = 0;
-    const int mx = wbits == ORACLE_MXFP4;
-    double g = row_value(v.gate + r * v.gate_row, wbits, ablk, mx ? 1.0f : v.sg[r],
-                         mx ? v.bg + (size_t)r * (H / QBLK) : NULL, q, d, H,
-                         gate_dots ? gate_dots + (size_t)r * (H / B) : NULL, &e1);
-    double u = row_value(v.up + r * v.gate_row, wbits, ablk, mx ? 1.0f : v.su[r],
-                         mx ? v.bu + (size_t)r * (H / QBLK) : NULL, q, d, H,
-                         up_dots ? up_dots + (size_t)r * (H / B) : NULL, &e1);
+    const int mx = wbits == ORACLE_MXFP4, f8 = wbits == ORACLE_FP8;
+    const size_t fo = (size_t)(r / F8BLK) * (H / F8BLK);  /* the row's 128-block scales */
+    double g = row_value(v.gate + r * v.gate_row, wbits, ablk, mx || f8 ? 1.0f : v.sg[r],
+                         mx ? v.bg + (size_t)r * (H / QBLK) : NULL, f8 ? v.fg + fo : NULL, q,
+                         d, H, gate_dots ? gate_dots + (size_t)r * (H / B) : NULL, &e1);
+    double u = row_value(v.up + r * v.gate_row, wbits, ablk, mx || f8 ? 1.0f : v.su[r],
+                         mx ? v.bu + (size_t)r * (H / QBLK) : NULL, f8 ? v.fu + fo : NULL, q,
+                         d, H, up_dots ? up_dots + (size_t)r * (H / B) : NULL, &e1);
     double silu = g / (1.0 + exp(-g));
     if (g_out) g_out[r] = g;
     if (u_out) u_out[r] = u;
@@ -550,15 +598,17 @@ int oracle_down_act(const uint8_t *blob, int H, int I, int wbits, int ablk, cons
                     const float *dh, int32_t *down_dots, float *y) {
   const int B = act_len(ablk, I);
   if (H % QBLK || I % QBLK || B <= 0) return -1;
+  if (wbits == ORACLE_FP8 && (H % F8BLK || I % F8BLK)) return -1;
   blob_view v = view_of(blob, H, I, wbits);
   int err = 0;
 #pragma omp parallel for schedule(static) reduction(| : err)
   for (int j = 0; j < H; j++) {
     int e1 = 0;
-    const int mx = wbits == ORACLE_MXFP4;
-    double val = row_value(v.down + j * v.down_row, wbits, ablk, mx ? 1.0f : v.sd[j],
-                           mx ? v.bd + (size_t)j * (I / QBLK) : NULL, qh, dh, I,
-                           down_dots ? down_dots + (size_t)j * (I / B) : NULL, &e1);
+    const int mx = wbits == ORACLE_MXFP4, f8 = wbits == ORACLE_FP8;
+    const size_t fo = (size_t)(j / F8BLK) * (I / F8BLK);
+    double val = row_value(v.down + j * v.down_row, wbits, ablk, mx || f8 ? 1.0f : v.sd[j],
+                           mx ? v.bd + (size_t)j * (I / QBLK) : NULL, f8 ? v.fd + fo : NULL, qh,
+                           dh, I, down_dots ? down_dots + (size_t)j * (I / B) : NULL, &e1);
     if (y) y[j] = (float)val;
     err |= e1;
   }

@@ -44,6 +44,7 @@ _glib = None
 
 
 MXFP4 = -4  # weight-format code: MXFP4 experts (FP4 E2M1 codes, E8M0 scale per 32)
+FP8 = -8  # weight-format code: FP8 E4M3 experts (one fp32 scale per 128x128 block)
 
 
 @dataclass(frozen=True)
@@ -56,11 +57,11 @@ class LayerShape:
     top_k: int
     n_shared: int = 1
     routed_scaling: float = 2.5
-    wbits: int = 4  # 8, 4, 2 (integer codes, fp32 row scales) or MXFP4
+    wbits: int = 4  # 8, 4, 2 (integer codes, fp32 row scales), MXFP4 or FP8
 
     @property
     def label(self) -> str:
-        return "mxfp4" if self.wbits == MXFP4 else f"int{self.wbits}"
+        return {MXFP4: "mxfp4", FP8: "fp8"}.get(self.wbits, f"int{self.wbits}")
 
     def with_bits(self, wbits: int) -> "LayerShape":
         return LayerShape(self.hidden, self.inter, self.n_experts, self.n_group,

@@ -42,6 +42,15 @@
  * FP4 magnitude {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even mantissa,
  * saturating at 6, sign in bit 3 (zero magnitude -> code 0).
  *
+ * FP8 record (wbits code -8; the fp8 weights one of the pages' supported
+ * models ships, with the 128x128 block scales its converter reads): one
+ * OCP E4M3 byte per element for the three matrices in the same order, then
+ * fp32 scales per 128x128 block: gate [I/128][H/128], up [I/128][H/128],
+ * down [H/128][I/128].  Block quantiser: amax = max|w| over the block,
+ * s = amax / 448 (s = 0 -> codes 0); each v = w / s (correctly rounded) goes
+ * to the nearest E4M3 value, ties to the even mantissa, saturating at 448;
+ * a zero magnitude is code 0.
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC
  */
 #include <math.h>
@@ -99,10 +108,12 @@ void synth_uniform_fill(uint64_t key, uint64_t start, int64_t n, float lo,
 }
 
 #define SYN_MXFP4 (-4)
+#define SYN_FP8 (-8)
 
 size_t synth_blob_bytes(int H, int I, int wbits) {
   const size_t elems = (size_t)2 * I * H + (size_t)H * I;
   if (wbits == SYN_MXFP4) return elems / 2 + elems / 32;
+  if (wbits == SYN_FP8) return elems + sizeof(float) * 3 * (size_t)(I / 128) * (H / 128);
   return elems * (size_t)wbits / 8 + sizeof(float) * ((size_t)2 * I + H);
 }
 
@@ -119,6 +130,69 @@ static unsigned fp4_code(float w, int X) {
   else if (v <= 5.0f) m = 6;
   else m = 7;
   return m == 0 ? 0u : (m | (w < 0.0f ? 8u : 0u));
+}
+
+/* E4M3 code of v = w / s (see the header): exact steps only (frexpf,
+ * ldexpf, rintf in round-to-nearest-even). */
+static unsigned fp8_code(float v) {
+  const unsigned sign = v < 0.0f ? 0x80u : 0u;
+  const float a = fabsf(v);
+  unsigned code;
+  if (a >= 448.0f) {
+    code = 0x7E;
+  } else {
+    int ex;
+    frexpf(a, &ex); /* a = f 2^ex, f in [0.5, 1): floor(log2 a) = ex - 1 */
+    const int E = ex - 1;
+    if (a == 0.0f) {
+      code = 0;
+    } else if (E < -6) { /* subnormal: units of 2^-9; 8 units = 2^-6 = code 0x08 */
+      code = (unsigned)rintf(ldexpf(a, 9));
+    } else {
+      int q = (int)rintf(ldexpf(a, 3 - E)); /* in [8, 16] */
+      int EE = E;
+      if (q == 16) {
+        q = 8;
+        EE++;
+      }
+      code = ((unsigned)(EE + 7) << 3) | (unsigned)(q - 8);
+      if (code > 0x7E) code = 0x7E;
+    }
+  }
+  return code == 0 ? 0u : (sign | code);
+}
+
+/* FP8 record for (seed, layer, expert): each 128x128 block of a matrix is
+ * drawn twice (its amax first, then its codes), so no block is held. */
+static int fp8_expert_blob(uint64_t seed, uint32_t layer, uint32_t expert, int H, int I,
+                           float sigma, uint8_t *blob) {
+  if (H <= 0 || I <= 0 || H % 128 || I % 128) return -1;
+  const size_t gate_b = (size_t)I * H;
+  uint8_t *codes[3] = {blob, blob + gate_b, blob + 2 * gate_b};
+  float *sc = (float *)(blob + 3 * gate_b);
+  const size_t nb = (size_t)(I / 128) * (H / 128);
+  float *scl[3] = {sc, sc + nb, sc + 2 * nb};
+  const int rows[3] = {I, I, H}, cols[3] = {H, H, I};
+  for (int m = 0; m < 3; m++) {
+    const uint64_t key = synth_key(seed, layer, 4u + (uint32_t)m, expert, (uint32_t)m);
+    const int n = cols[m], rb = rows[m] / 128, cb = n / 128;
+#pragma omp parallel for schedule(static)
+    for (int blk = 0; blk < rb * cb; blk++) {
+      const int br = blk / cb, bc = blk % cb;
+      float amax = 0.0f;
+      for (int r = br * 128; r < br * 128 + 128; r++)
+        for (int c = bc * 128; c < bc * 128 + 128; c++)
+          amax = fmaxf(amax, fabsf(normal_at(key, (uint64_t)r * (uint64_t)n + (uint64_t)c) * sigma));
+      const float s = amax / 448.0f;
+      scl[m][blk] = s;
+      for (int r = br * 128; r < br * 128 + 128; r++)
+        for (int c = bc * 128; c < bc * 128 + 128; c++) {
+          const float w = normal_at(key, (uint64_t)r * (uint64_t)n + (uint64_t)c) * sigma;
+          codes[m][(size_t)r * n + c] = (uint8_t)(s != 0.0f ? fp8_code(w / s) : 0u);
+        }
+    }
+  }
+  return 0;
 }
 
 /* One MXFP4 block: 32 floats -> 16 code bytes and the E8M0 scale byte. */
@@ -209,6 +283,7 @@ static int mx_expert_blob(uint64_t seed, uint32_t layer, uint32_t expert, int H,
 int synth_expert_blob(uint64_t seed, uint32_t layer, uint32_t expert, int H,
                       int I, int wbits, float sigma, uint8_t *blob) {
   if (wbits == SYN_MXFP4) return mx_expert_blob(seed, layer, expert, H, I, sigma, blob);
+  if (wbits == SYN_FP8) return fp8_expert_blob(seed, layer, expert, H, I, sigma, blob);
   if ((wbits != 8 && wbits != 4 && wbits != 2) || H <= 0 || I <= 0 || H % 8 || I % 8) return -1;
   const size_t gate_b = (size_t)I * H * wbits / 8;
   const size_t down_b = (size_t)H * I * wbits / 8;

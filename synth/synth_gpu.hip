@@ -137,6 +137,95 @@ __global__ void __launch_bounds__(256) k_synth_rows_mx(MxJob job, int n, float s
   }
 }
 
+// FP8 records (wbits code -8): the 128x128 block quantiser of synth.c, one
+// workgroup per block: the block's amax from a first pass over its draws,
+// then the codes from a second.
+__device__ static unsigned fp8_code(float v) {
+  const unsigned sign = v < 0.0f ? 0x80u : 0u;
+  const float a = fabsf(v);
+  unsigned code;
+  if (a >= 448.0f) {
+    code = 0x7E;
+  } else {
+    int ex;
+    frexpf(a, &ex);
+    const int E = ex - 1;
+    if (a == 0.0f) {
+      code = 0;
+    } else if (E < -6) {
+      code = (unsigned)rintf(ldexpf(a, 9));
+    } else {
+      int q = (int)rintf(ldexpf(a, 3 - E));
+      int EE = E;
+      if (q == 16) {
+        q = 8;
+        EE++;
+      }
+      code = ((unsigned)(EE + 7) << 3) | (unsigned)(q - 8);
+      if (code > 0x7E) code = 0x7E;
+    }
+  }
+  return code == 0 ? 0u : (sign | code);
+}
+
+struct F8Job {
+  uint64_t key[8];
+  uint8_t *codes[8];  // first code row of this matrix in each record
+  float *scales[8];   // first block scale of this matrix in each record
+};
+
+__global__ void __launch_bounds__(256) k_synth_blocks_f8(F8Job job, int n, float sigma) {
+  __shared__ float red[256];
+  const int cb = n / 128, blk = blockIdx.x, ex = blockIdx.y, tid = threadIdx.x;
+  const int br = blk / cb, bc = blk % cb;
+  const uint64_t key = job.key[ex];
+  float amax = 0.0f;
+  for (int i = tid; i < 128 * 128; i += 256) {
+    const int r = br * 128 + i / 128, c = bc * 128 + i % 128;
+    amax = fmaxf(amax, fabsf(normal_at(key, (uint64_t)r * (uint64_t)n + (uint64_t)c) * sigma));
+  }
+  red[tid] = amax;
+  __syncthreads();
+  for (int k = 128; k > 0; k >>= 1) {
+    if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
+    __syncthreads();
+  }
+  const float s = red[0] / 448.0f;
+  if (tid == 0) job.scales[ex][blk] = s;
+  for (int i = tid; i < 128 * 128; i += 256) {
+    const int r = br * 128 + i / 128, c = bc * 128 + i % 128;
+    const float w = normal_at(key, (uint64_t)r * (uint64_t)n + (uint64_t)c) * sigma;
+    job.codes[ex][(size_t)r * n + c] = (uint8_t)(s != 0.0f ? fp8_code(w / s) : 0u);
+  }
+}
+
+static int f8_blobs(uint64_t seed, uint32_t layer, const uint32_t *expert_ids, int n_experts,
+                    int H, int I, float sigma, void *out, size_t stride, hipStream_t st) {
+  if (H % 128 || I % 128) return -1;
+  const size_t gate_b = (size_t)I * H;
+  const size_t nb = (size_t)(I / 128) * (H / 128);
+  const int rows[3] = {I, I, H}, cols[3] = {H, H, I};
+  for (int e0 = 0; e0 < n_experts; e0 += 8) {
+    const int ne = (n_experts - e0) < 8 ? (n_experts - e0) : 8;
+    for (int m = 0; m < 3; m++) {
+      F8Job job;
+      for (int i = 0; i < 8; i++) {
+        const int ei = e0 + (i < ne ? i : 0);
+        uint8_t *base = (uint8_t *)out + (size_t)ei * stride;
+        float *sc = (float *)(base + 3 * gate_b);
+        job.key[i] = host_key(seed, layer, 4u + (uint32_t)m, expert_ids[ei], (uint32_t)m);
+        job.codes[i] = base + (size_t)m * gate_b;
+        job.scales[i] = sc + (size_t)m * nb;
+      }
+      hipLaunchKernelGGL(k_synth_blocks_f8, dim3((rows[m] / 128) * (cols[m] / 128), ne),
+                         dim3(256), 0, st, job, cols[m], sigma);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return (int)err;
+    }
+  }
+  return 0;
+}
+
 static int mx_blobs(uint64_t seed, uint32_t layer, const uint32_t *expert_ids, int n_experts,
                     int H, int I, float sigma, void *out, size_t stride, hipStream_t st) {
   const size_t gate_b = (size_t)I * H / 2, down_b = (size_t)H * I / 2;
@@ -171,11 +260,13 @@ extern "C" {
 int synth_gpu_expert_blobs(uint64_t seed, uint32_t layer, const uint32_t *expert_ids,
                            int n_experts, int H, int I, int wbits, float sigma,
                            void *out, size_t stride, void *stream) {
-  if ((wbits != 8 && wbits != 4 && wbits != 2 && wbits != -4) || H <= 0 || I <= 0 || H % 32 ||
+  if ((wbits != 8 && wbits != 4 && wbits != 2 && wbits != -4 && wbits != -8) || H <= 0 ||
+      I <= 0 || H % 32 ||
       I % 32 || n_experts < 0 || !out || H > 16384 || I > 16384)
     return -1;
   hipStream_t st = (hipStream_t)stream;
   if (wbits == -4) return mx_blobs(seed, layer, expert_ids, n_experts, H, I, sigma, out, stride, st);
+  if (wbits == -8) return f8_blobs(seed, layer, expert_ids, n_experts, H, I, sigma, out, stride, st);
   const size_t gate_b = (size_t)I * H * wbits / 8;
   const size_t down_b = (size_t)H * I * wbits / 8;
   const int rows[3] = {I, I, H}, cols[3] = {H, H, I};

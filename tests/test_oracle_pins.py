@@ -886,3 +886,120 @@ def test_row_format_rejects_mxfp4():
     q, d = oracle.quant_act(synth.tokens(shape, 3, 1)[0], ROW)
     with pytest.raises(ValueError):
         oracle.gate_up(blob, 256, 128, oracle.MXFP4, q, d, act_block=ROW)
+
+
+# ---------------------------------------------------------------- R18: FP8 experts
+
+def _torch_e4m3fn(codes):
+    import torch
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(
+        torch.float64).numpy()
+
+
+def test_fp8_values_match_an_independent_decoder():
+    """Every E4M3 code against PyTorch's float8_e4m3fn (OCP E4M3), an
+    implementation that shares nothing with the oracle: same values, same
+    signs of zero, NaN exactly at 0x7F and 0xFF."""
+    ref = _torch_e4m3fn(np.arange(256))
+    got = np.array([oracle.fp8_value(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and np.flatnonzero(nan).tolist() == [0x7F, 0xFF]
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_fp8_hand_values():
+    """Values worked out by hand from the format (bias 7, 3 mantissa bits):
+    smallest subnormal 2^-9, smallest normal 2^-6, largest 448; the
+    positive codes increase strictly."""
+    hand = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5,
+            0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x77: 240.0, 0x78: 256.0, 0x7E: 448.0,
+            0xB8: -1.0, 0xFE: -448.0}
+    for c, v in hand.items():
+        assert oracle.fp8_value(c) == v, hex(c)
+    pos = [oracle.fp8_value(c) for c in range(0x7F)]
+    assert all(b > a for a, b in zip(pos, pos[1:]))
+
+
+def test_fp8_block_dot_hand_cases():
+    """P9 = sum 512 fp8(c) q: ones against 1..32; the largest magnitude
+    against 127 everywhere (932,184,064, inside int32); the smallest
+    subnormal is 1 unit; a NaN code is refused."""
+    q = np.arange(1, 33, dtype=np.int8)
+    assert oracle.act_dots(np.full(32, 0x38, np.uint8), oracle.FP8, q).tolist() == [512 * 528]
+    big = oracle.act_dots(np.full(32, 0x7E, np.uint8), oracle.FP8, np.full(32, 127, np.int8))
+    assert big.tolist() == [448 * 512 * 127 * 32]
+    neg = oracle.act_dots(np.full(32, 0xFE, np.uint8), oracle.FP8, np.full(32, 127, np.int8))
+    assert neg.tolist() == [-448 * 512 * 127 * 32]
+    assert oracle.act_dots(np.full(32, 0x01, np.uint8), oracle.FP8, q).tolist() == [528]
+    bad = np.full(32, 0x38, np.uint8)
+    bad[5] = 0x7F
+    with pytest.raises(ValueError):
+        oracle.act_dots(bad, oracle.FP8, q)
+
+
+def _fp8_record(rng, H, I):
+    """Random valid codes (no NaN) and a distinct fp32 scale per 128x128 block."""
+    codes = rng.integers(0, 256, size=3 * I * H).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    nb = (I // 128) * (H // 128)
+    sc = (rng.uniform(0.5, 2.0, 3 * nb) * 1e-3).astype(np.float32)
+    return np.concatenate([codes, sc.view(np.uint8)])
+
+
+def _dequant(codes, scales, rows, cols):
+    vals = _torch_e4m3fn(codes).reshape(rows, cols)
+    return vals * np.kron(scales.astype(np.float64), np.ones((128, 128)))
+
+
+def test_fp8_rows_equal_dequantised_matmul():
+    """gate/up/down of an FP8 record against the textbook fp64 product of the
+    dequantised matrices (PyTorch's decoding, each 128x128 block times its
+    own scale) with the dequantised Q8_0 activations: a transposed or
+    misplaced block scale, or a wrong 1/512, fails here."""
+    rng = np.random.default_rng(18)
+    H, I = 256, 384
+    blob = _fp8_record(rng, H, I)
+    gate, up, down, sg, su, sd = oracle.blob_view(blob, H, I, oracle.FP8)
+    assert sg.shape == (I // 128, H // 128) and sd.shape == (H // 128, I // 128)
+    x = rng.standard_normal(H).astype(np.float32)
+    q, d = oracle.q8_0(x[None])
+    xd = q[0].astype(np.float64) * np.repeat(d[0].astype(np.float64), 32)
+    ref = oracle.gate_up(blob, H, I, oracle.FP8, q[0], d[0])
+    Wg, Wu = _dequant(gate, sg, I, H), _dequant(up, su, I, H)
+    assert np.allclose(ref["g"], Wg @ xd, rtol=1e-12, atol=1e-12)
+    assert np.allclose(ref["u"], Wu @ xd, rtol=1e-12, atol=1e-12)
+    h = rng.standard_normal(I).astype(np.float32)
+    qh, dh = oracle.q8_0(h[None])
+    y, dots = oracle.down(blob, H, I, oracle.FP8, qh[0], dh[0], want_dots=True)
+    hd = qh[0].astype(np.float64) * np.repeat(dh[0].astype(np.float64), 32)
+    Wd = _dequant(down, sd, H, I)
+    assert np.allclose(y, (Wd @ hd).astype(np.float32), rtol=1e-6, atol=1e-9)
+    # and the reported dots are the exact integer sums
+    w512 = (_torch_e4m3fn(down) * 512).astype(np.int64).reshape(H, I // 32, 32)
+    assert np.array_equal(dots, (w512 * qh[0].astype(np.int64).reshape(I // 32, 32)).sum(-1))
+
+
+def test_fp8_generated_record_is_the_e4m3_rounding_of_the_weights():
+    """The generator's FP8 record (tiny shape): each 128x128 block's scale is
+    amax/448 of its float weights, and every code is PyTorch's
+    round-to-nearest-even E4M3 conversion of weight / scale (zero as code
+    0)."""
+    import torch
+    shape = synth.TINY.with_bits(synth.FP8)
+    H, I = shape.hidden, shape.inter
+    blob = synth.expert_blob(shape, 5, 0, 3)
+    assert blob.size == oracle.blob_bytes(H, I, oracle.FP8)
+    mats = oracle.blob_view(blob, H, I, oracle.FP8)
+    for m, (rows, cols) in enumerate(((I, H), (I, H), (H, I))):
+        W = np.stack([synth.weight_row(5, 0, 3, m, cols, r) for r in range(rows)])
+        codes, sc = mats[m], mats[3 + m]
+        for br in range(rows // 128):
+            for bc in range(cols // 128):
+                blk = W[br * 128:(br + 1) * 128, bc * 128:(bc + 1) * 128]
+                s = np.float32(np.abs(blk).max()) / np.float32(448.0)
+                assert sc[br, bc] == s
+                want = torch.from_numpy(blk / s).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+                want = np.where(want == 0x80, 0, want)
+                got = codes[br * 128:(br + 1) * 128, bc * 128:(bc + 1) * 128]
+                assert np.array_equal(got, want), (m, br, bc)
