@@ -67,6 +67,7 @@ def describe(name, shape, T, ring, layers=1, top_p=0.0, cache_slots=0, act="q8_0
     tp = (f", adaptive expert top-p {top_p:g} (shortest rank-order prefix holding that share of "
           f"the selected scores, weights renormalised)" if 0 < top_p < 1 else "")
     wfmt = ("MXFP4 (FP4 E2M1 codes + an E8M0 scale per 32)" if shape.wbits == -4
+            else "FP8 E4M3 (+ an fp32 scale per 128x128 block)" if shape.wbits == -8
             else f"int{shape.wbits} (codes + fp32 row scales)")
     if cache_slots:
         tp += (f"; routed experts in pinned host memory, {cache_slots} of {shape.n_experts} per "
@@ -146,6 +147,8 @@ def gate_up_bytes(shape, T, U, small):
     H, I, K, S = shape.hidden, shape.inter, shape.top_k, shape.n_shared
     if shape.wbits == -4:  # MXFP4: 4-bit codes and one scale byte per 32
         per_expert = 2 * I * H // 2 + 2 * I * H // 32
+    elif shape.wbits == -8:  # FP8: byte codes and one fp32 scale per 128x128 block
+        per_expert = 2 * I * H + 2 * (I // 128) * (H // 128) * 4
     else:
         per_expert = 2 * I * H * shape.wbits // 8 + 2 * I * 4
     q8 = 1 + 4 / 32  # bytes per element of a Q8_0 vector (codes + fp32 block scales)
@@ -290,8 +293,9 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--wbits", default="4", choices=("8", "4", "2", "mxfp4"),
-                    help="expert weights: int8/int4/int2 codes with row scales, or MXFP4")
+    ap.add_argument("--wbits", default="4", choices=("8", "4", "2", "mxfp4", "fp8"),
+                    help="expert weights: int8/int4/int2 codes with row scales, MXFP4, or FP8 "
+                         "E4M3 with 128x128 block scales")
     ap.add_argument("--ring", type=int, default=0,
                     help="layer instances to cycle (0 = the workload's ring; 1 with --cache-slots)")
     ap.add_argument("--act", default="q8_0", choices=("q8_0", "row"),
@@ -331,7 +335,8 @@ def main():
     import synth
 
     wl = WORKLOADS[args.workload]
-    shape = synth.REAL.with_bits(synth.MXFP4 if args.wbits == "mxfp4" else int(args.wbits))
+    shape = synth.REAL.with_bits({"mxfp4": synth.MXFP4, "fp8": synth.FP8}.get(args.wbits)
+                                 or int(args.wbits))
     T = wl["T"]
     NL = wl.get("layers", 1)
     if NL > 1 and args.layers:
@@ -596,7 +601,8 @@ def main():
     pairs = float(np.mean([(idx_h[i] >= 0).sum() for i in range(W, W + K)])) / NL
     U = float(np.mean(U_l))
     step_bytes = sum(layer_bytes(shape, T, u, bb) for u in U_l)
-    small = T <= 16  # the layer's small-batch path (four kernels)
+    fp8 = shape.wbits == synth.FP8  # chained path with vector kernels at every batch size
+    small = T <= 16 and not fp8  # the layer's small-batch path (four kernels)
     dom_sec = stage_ms["gate_up"] * 1e-3
     cache_info = None
     if args.cache_slots:
@@ -624,8 +630,9 @@ def main():
                 "achieved": cache_info["host_link_gbps"], "peak": HOST_LINK_PEAK_GBPS,
                 "unit": "GB/s", "frac": cache_info["host_link_gbps"] / HOST_LINK_PEAK_GBPS,
                 "traffic": None}
-    elif small:  # HBM-bound GEMV: algorithmic bytes of the gate/up launch
-        dom = "gate_up (routed expert gate/up + SwiGLU + Q8_0 of h)"
+    elif small or fp8:  # HBM-bound GEMV: algorithmic bytes of the gate/up launch
+        dom = ("gate_up (FP8 expert gate/up + SwiGLU, exact block dots)" if fp8 else
+               "gate_up (routed expert gate/up + SwiGLU + Q8_0 of h)")
         dom_bytes = float(np.mean([gate_up_bytes(shape, T, u, small) for u in U_l]))
         roof = {"bound": "hbm", "kernel": dom, "achieved": dom_bytes / dom_sec / 1e9,
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s"}
@@ -666,7 +673,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp4e2m1xi8->i32" if shape.wbits == -4 else f"i{shape.wbits}xi8->i32")
+        "dtype": ("fp4e2m1xi8->i32" if shape.wbits == -4 else "fp8e4m3xi8->i32"
+                  if shape.wbits == -8 else f"i{shape.wbits}xi8->i32")
                  + ("" if args.act == "q8_0" else " (per-row activation scales)"),
         "data": "synthetic",
         "config": {"workload": describe(args.workload, shape, T, R, NL, args.topp,

@@ -56,6 +56,18 @@
  *     row scales: gate [I][H/32] | up [I][H/32] | down [H][I/32]; a row is
  *     sum_b 2^(s_b-127) d_b sum_k fp4(c_k) q_k, and the int32 block dot
  *     reported for it (moe_ffn_debug) is sum_k 2 fp4(c_k) q_k.
+ *     FP8 records (wfmt = 2, wbits 8; "Comment exécuter…", section "Modèles
+ *     supportés": a supported model runs on fp4/fp8 weights, and "Show
+ *     HN…", converter item: FP8 checkpoints with 128x128 block scales): one
+ *     OCP FP8 E4M3 byte per element (bias 7, 3 mantissa bits, largest 448;
+ *     codes 0x7F and 0xFF are NaN and not valid weights) for gate [I][H],
+ *     up [I][H], down [H][I], then one fp32 scale per 128x128 block: gate
+ *     [I/128][H/128] | up [I/128][H/128] | down [H/128][I/128]; a row r is
+ *     sum_b S[r/128][b/4] d_b sum_k fp8(c_k) q_k over its 32-blocks b, and
+ *     the int32 block dot reported for it is sum_k 512 fp8(c_k) q_k (exact:
+ *     512 fp8 is an integer).  hidden and inter multiples of 128; every
+ *     batch size runs the vector kernels (no matrix-core path), and
+ *     moe_layer takes the chained kernels.
  *     int8: element j in byte j, codes in [-127, 127] (-128 is not
  *     produced by the quantiser but is accepted);
  *     int4: element 2j in the low nibble of byte j, 2j+1 in the high nibble;
@@ -88,9 +100,9 @@ extern "C" {
  * wbits in {8, 4, 2}; a weight row holds at most 256 16-byte pieces of codes
  * (448 for int8) along hidden and 128 along inter, i.e. hidden <= 8192 and
  * inter <= 4096 for int4 (16384 / 8192 for int2, 7168 / 2048 for int8);
- * top_p = 0 (off), or in (0, 1] (1 is off as well); wfmt 0, or 1 with
- * wbits 4 (MXFP4); act_block 0 or 32 (Q8_0), or MOE_ACT_ROW with int4 or
- * int8 codes (wfmt 0). */
+ * top_p = 0 (off), or in (0, 1] (1 is off as well); wfmt 0, 1 with
+ * wbits 4 (MXFP4), or 2 with wbits 8 (FP8); act_block 0 or 32 (Q8_0), or
+ * MOE_ACT_ROW with int4 or int8 codes (wfmt 0). */
 /* Activation format act_block = MOE_ACT_ROW: one fp32 scale per activation
  * row instead of one per 32 values -- per token row of x (H values) and per
  * (token, expert) row of h (I values) -- with the Q8_0 rule over the whole
@@ -112,7 +124,8 @@ typedef struct moe_cfg {
   int32_t wbits;        /* 8 (int8), 4 (packed int4) or 2 (packed int2) */
   float routed_scaling; /* routed_scaling_factor applied to routed weights */
   float top_p;          /* adaptive expert top-p (see moe_route); 0 = off */
-  int32_t wfmt;         /* 0: integer codes, fp32 row scales; 1: MXFP4 (wbits 4) */
+  int32_t wfmt;         /* 0: integer codes, fp32 row scales; 1: MXFP4 (wbits 4);
+                           2: FP8 E4M3 with 128x128 block scales (wbits 8) */
   int32_t act_block;    /* activations: 0 or 32 = Q8_0 blocks; MOE_ACT_ROW = one scale per row */
 } moe_cfg;
 
@@ -236,14 +249,16 @@ int moe_expert_ffn(const moe_cfg *cfg, int32_t T, const int8_t *q, const float *
  * residual and shared_out may be NULL (treated as 0).  A term with
  * w[t,k] == 0 is skipped and its expert_out row not read (top-p drops).  If y_norm is not NULL
  * it receives y[t] / sqrt(mean(y[t]^2) + eps) (unit-gain RMSNorm, the input
- * of the next layer in a pre-norm stack).
- * Errors: MOE_EINVAL, MOE_EALIGN.
+ * of the next layer in a pre-norm stack); y_norm must not overlap y.  y may
+ * be residual itself (each element is read before it is written).
+ * Errors: MOE_EINVAL (also for overlapping y and y_norm), MOE_EALIGN.
  * ------------------------------------------------------------------------- */
 int moe_combine(int32_t T, int32_t H, int32_t K, const float *expert_out, const float *w,
                 const float *shared_out, const float *residual, float *y, float *y_norm,
                 float eps, void *stream);
 
-/* Unit-gain RMSNorm of T rows of H floats: y = x / sqrt(mean(x^2) + eps). */
+/* Unit-gain RMSNorm of T rows of H floats: y = x / sqrt(mean(x^2) + eps);
+ * y must not overlap x (MOE_EINVAL). */
 int moe_rmsnorm(int32_t T, int32_t H, const float *x, float *y, float eps, void *stream);
 
 /* Optional kernel timestamps for moe_layer (pass NULL in production).  For

@@ -178,15 +178,16 @@ class Config:
     wbits: int = 4
     routed_scaling: float = 2.5
     top_p: float = 0.0  # adaptive expert top-p; 0 = off
-    wfmt: int = 0  # 0: integer codes with fp32 row scales; 1: MXFP4 (wbits 4)
+    wfmt: int = 0  # 0: integer codes with fp32 row scales; 1: MXFP4 (wbits 4); 2: FP8 (wbits 8)
     act_block: int = ACT_Q8_0  # activations: Q8_0 blocks of 32, or ACT_ROW (one scale per row)
 
     @classmethod
     def of(cls, shape, top_p: float = 0.0, act_block: int = ACT_Q8_0) -> "Config":
-        mx = shape.wbits == -4  # the synthetic shapes' code for MXFP4 experts
+        # the synthetic shapes' codes: -4 MXFP4 experts, -8 FP8 experts
+        wbits, wfmt = {-4: (4, 1), -8: (8, 2)}.get(shape.wbits, (shape.wbits, 0))
         return cls(shape.hidden, shape.inter, shape.n_experts, shape.n_group, shape.topk_group,
-                   shape.top_k, shape.n_shared, 4 if mx else shape.wbits, shape.routed_scaling,
-                   top_p, 1 if mx else 0, act_block)
+                   shape.top_k, shape.n_shared, wbits, shape.routed_scaling, top_p, wfmt,
+                   act_block)
 
     def act_len(self, n: int) -> int:
         """Activation block length on rows of n values."""

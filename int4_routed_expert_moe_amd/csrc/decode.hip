@@ -10,6 +10,7 @@ size_t small_batch_slot_ints(int T, int K, int n_shared) {
 
 bool small_batch_supported(const moe_cfg &c, int T) {
   if (T < 1 || T > MOE_SMALL_T_MAX) return false;
+  if (c.wfmt == 2) return false;  // FP8 experts take the chained path
   if (T * c.top_k > 256) return false;
   if (c.hidden / 64 > 128 || c.hidden % sbk::RT) return false;
   const int per = 128 / c.wbits;  // codes per 16-byte piece

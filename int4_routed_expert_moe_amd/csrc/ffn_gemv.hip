@@ -74,6 +74,41 @@ __device__ __forceinline__ void token_of(const FfnArgs &a, const SlotInfo &si, i
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+// Q8_0 of h for the TT pairs of a down chunk (pair -1: zeros) into LDS:
+// codes lq [TT][I], scales ld [TT][I/32]; 8 threads per block of 32, 4
+// values each, the rule of the activation quantiser.  Workgroup-wide, with
+// a barrier before (the previous chunk is consumed) and after.
+template <int TT, bool DBG>
+__device__ __forceinline__ void stage_qh(const FfnArgs &a, const int (&pair)[TT], int8_t *lq,
+                                         float *ld) {
+  const int I = a.I, nblk = I / 32;
+  __syncthreads();
+  for (int v = threadIdx.x; v < TT * (I / 4); v += 256) {
+    const int t = v / (I / 4), k4 = v % (I / 4);
+    float4 hv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (pair[t] >= 0) hv = reinterpret_cast<const float4 *>(a.h + (size_t)pair[t] * I)[k4];
+    float m = fmaxf(fmaxf(fabsf(hv.x), fabsf(hv.y)), fmaxf(fabsf(hv.z), fabsf(hv.w)));
+    m = fmaxf(m, __shfl_xor(m, 1, 8));
+    m = fmaxf(m, __shfl_xor(m, 2, 8));
+    m = fmaxf(m, __shfl_xor(m, 4, 8));
+    const float dd = m / 127.0f;
+    const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
+    auto cv = [&](float f) -> uint32_t {
+      float r = roundf(f * id);
+      r = fminf(fmaxf(r, -127.0f), 127.0f);
+      return (uint32_t)(uint8_t)(int8_t)(int)r;
+    };
+    const uint32_t packed = cv(hv.x) | (cv(hv.y) << 8) | (cv(hv.z) << 16) | (cv(hv.w) << 24);
+    reinterpret_cast<uint32_t *>(lq + (size_t)t * I)[k4] = packed;
+    if ((k4 & 7) == 0) ld[t * nblk + (k4 >> 3)] = dd;
+    if (DBG && blockIdx.x == 0 && pair[t] >= 0) {
+      if (a.dbg.q_h) reinterpret_cast<uint32_t *>(a.dbg.q_h + (size_t)pair[t] * I)[k4] = packed;
+      if (a.dbg.d_h && (k4 & 7) == 0) a.dbg.d_h[(size_t)pair[t] * nblk + (k4 >> 3)] = dd;
+    }
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------------ int4
 
 // Gate/up: each wave owns GU_RPW row indices; lane l owns pieces l + 64 i.
@@ -195,32 +230,7 @@ __global__ void __launch_bounds__(256) k_down_i4(FfnArgs a) {
       tok[t] = 0;
       if (c0 + t < si.n_tok) token_of(a, si, c0 + t, tok[t], pair[t]);
     }
-    // Q8_0 of h: 8 threads per block of 32, 4 values each
-    __syncthreads();
-    for (int v = threadIdx.x; v < TT * (I / 4); v += 256) {
-      const int t = v / (I / 4), k4 = v % (I / 4);
-      float4 hv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (pair[t] >= 0) hv = reinterpret_cast<const float4 *>(a.h + (size_t)pair[t] * I)[k4];
-      float m = fmaxf(fmaxf(fabsf(hv.x), fabsf(hv.y)), fmaxf(fabsf(hv.z), fabsf(hv.w)));
-      m = fmaxf(m, __shfl_xor(m, 1, 8));
-      m = fmaxf(m, __shfl_xor(m, 2, 8));
-      m = fmaxf(m, __shfl_xor(m, 4, 8));
-      const float dd = m / 127.0f;
-      const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
-      auto cv = [&](float f) -> uint32_t {
-        float r = roundf(f * id);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        return (uint32_t)(uint8_t)(int8_t)(int)r;
-      };
-      const uint32_t packed = cv(hv.x) | (cv(hv.y) << 8) | (cv(hv.z) << 16) | (cv(hv.w) << 24);
-      reinterpret_cast<uint32_t *>(lq + (size_t)t * I)[k4] = packed;
-      if ((k4 & 7) == 0) ld[t * (I / 32) + (k4 >> 3)] = dd;
-      if (DBG && blockIdx.x == 0 && pair[t] >= 0) {
-        if (a.dbg.q_h) reinterpret_cast<uint32_t *>(a.dbg.q_h + (size_t)pair[t] * I)[k4] = packed;
-        if (a.dbg.d_h && (k4 & 7) == 0) a.dbg.d_h[(size_t)pair[t] * (I / 32) + (k4 >> 3)] = dd;
-      }
-    }
-    __syncthreads();
+    stage_qh<TT, DBG>(a, pair, lq, ld);  // Q8_0 of h
     QBlock act[NPL][TT];
     float dq[NPL][TT];
 #pragma unroll
@@ -448,31 +458,7 @@ __global__ void __launch_bounds__(256) k_down_i2(FfnArgs a) {
       tok[t] = 0;
       if (c0 + t < si.n_tok) token_of(a, si, c0 + t, tok[t], pair[t]);
     }
-    __syncthreads();
-    for (int v = threadIdx.x; v < TT * (I / 4); v += 256) {
-      const int t = v / (I / 4), k4 = v % (I / 4);
-      float4 hv = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (pair[t] >= 0) hv = reinterpret_cast<const float4 *>(a.h + (size_t)pair[t] * I)[k4];
-      float m = fmaxf(fmaxf(fabsf(hv.x), fabsf(hv.y)), fmaxf(fabsf(hv.z), fabsf(hv.w)));
-      m = fmaxf(m, __shfl_xor(m, 1, 8));
-      m = fmaxf(m, __shfl_xor(m, 2, 8));
-      m = fmaxf(m, __shfl_xor(m, 4, 8));
-      const float dd = m / 127.0f;
-      const float id = (dd != 0.0f) ? 1.0f / dd : 0.0f;
-      auto cv = [&](float f) -> uint32_t {
-        float r = roundf(f * id);
-        r = fminf(fmaxf(r, -127.0f), 127.0f);
-        return (uint32_t)(uint8_t)(int8_t)(int)r;
-      };
-      const uint32_t packed = cv(hv.x) | (cv(hv.y) << 8) | (cv(hv.z) << 16) | (cv(hv.w) << 24);
-      reinterpret_cast<uint32_t *>(lq + (size_t)t * I)[k4] = packed;
-      if ((k4 & 7) == 0) ld[t * nblk + (k4 >> 3)] = dd;
-      if (DBG && blockIdx.x == 0 && pair[t] >= 0) {
-        if (a.dbg.q_h) reinterpret_cast<uint32_t *>(a.dbg.q_h + (size_t)pair[t] * I)[k4] = packed;
-        if (a.dbg.d_h && (k4 & 7) == 0) a.dbg.d_h[(size_t)pair[t] * nblk + (k4 >> 3)] = dd;
-      }
-    }
-    __syncthreads();
+    stage_qh<TT, DBG>(a, pair, lq, ld);  // Q8_0 of h
     QPiece2 act[NPL][TT];
     float da[NPL][TT], db[NPL][TT];
 #pragma unroll
@@ -542,6 +528,238 @@ __global__ void __launch_bounds__(256) k_down_i2(FfnArgs a) {
         }
       }
     }
+  }
+}
+
+// ------------------------------------------------------------------ FP8
+
+// FP8 E4M3 experts with one fp32 scale per 128x128 block ("Comment exécuter
+// un réseau de neurones de 744 milliards de paramètres…", section "Modèles
+// supportés": a supported model runs on fp4/fp8 weights; "Show HN…",
+// converter item: its FP8 checkpoints carry 128x128 block scales).  A lane
+// takes whole 32-code blocks (32 bytes); the codes become the exact integers
+// 512 x value (gfx950's OCP E4M3 conversion, scaled by 512: at most 18
+// bits) and meet the block's int8 activations in 24-bit integer
+// multiply-adds, so each block dot P9 = sum 512 fp8(c) q is exact; the
+// float epilogue per block is acc += P9 * (d * S) with S the block's
+// 128x128 scale, and the row is scaled by 1/512 at the end.
+
+typedef float f8v2 __attribute__((ext_vector_type(2)));
+
+// P9 of one block: codes w0, w1 (32 bytes) against the block's activation
+// bytes x0, x1 (kept packed; each byte is sign-extended where it is used, so
+// a lane holds 8 activation words per block rather than 32).
+__device__ __forceinline__ int dot_fp8_block(const uint4 w0, const uint4 w1, const uint4 x0,
+                                             const uint4 x1) {
+  const uint32_t w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  const uint32_t x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  int acc = 0;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const f8v2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 512.0f, false);
+    const f8v2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 512.0f, true);
+    acc = __mul24((int)lo.x, (int)(int8_t)x[j]) + acc;
+    acc = __mul24((int)lo.y, (int)(int8_t)(x[j] >> 8)) + acc;
+    acc = __mul24((int)hi.x, (int)(int8_t)(x[j] >> 16)) + acc;
+    acc = __mul24((int)hi.y, (int)(int8_t)(x[j] >> 24)) + acc;
+  }
+  return acc;
+}
+
+// Marks a weight piece as changed (an empty asm, registers only), so the
+// compiler converts the codes where they are used instead of hoisting every
+// converted value out of the token loop (192 live registers at NPL = 3).
+__device__ __forceinline__ void opaque(uint4 &v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+// Gate/up: one gate/up row pair per wave, lane l takes blocks l + 64 i; the
+// weights stay in registers while the slot's tokens go through them.
+template <int NPL, bool DBG>
+__global__ void __launch_bounds__(256) k_gate_up_f8(FfnArgs a) {
+  SlotInfo si;
+  if (!slot_info(a, blockIdx.y, si)) return;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int H = a.H, I = a.I, nblk = H / 32, nsb = H / 128;
+  const uint8_t *gate = si.blob, *up = si.blob + (size_t)I * H;
+  const float *bs = reinterpret_cast<const float *>(si.blob + 3 * (size_t)I * H);
+  const size_t nbs = (size_t)(I / 128) * nsb;
+  const int r = blockIdx.x * 4 + wv;
+  const float *sgr = bs + (size_t)(r / 128) * nsb, *sur = bs + nbs + (size_t)(r / 128) * nsb;
+  uint4 wg[NPL][2], wu[NPL][2];
+  float sg[NPL], su[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; i++) {
+    const int p = lane + 64 * i;
+    const bool ok = p < nblk;
+    const uint4 *gp = reinterpret_cast<const uint4 *>(gate + (size_t)r * H + 32 * (ok ? p : 0));
+    const uint4 *upp = reinterpret_cast<const uint4 *>(up + (size_t)r * H + 32 * (ok ? p : 0));
+    wg[i][0] = gp[0];
+    wg[i][1] = gp[1];
+    wu[i][0] = upp[0];
+    wu[i][1] = upp[1];
+    sg[i] = ok ? sgr[p / 4] : 0.0f;
+    su[i] = ok ? sur[p / 4] : 0.0f;
+  }
+  for (int c = 0; c < si.n_tok; c++) {
+    int tok, pair;
+    token_of(a, si, c, tok, pair);
+#pragma unroll
+    for (int i = 0; i < NPL; i++) {
+      opaque(wg[i][0]);
+      opaque(wg[i][1]);
+      opaque(wu[i][0]);
+      opaque(wu[i][1]);
+    }
+    float gacc = 0.0f, uacc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NPL; i++) {
+      const int p = lane + 64 * i;
+      const bool ok = p < nblk;
+      const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (size_t)tok * H + 32 * (ok ? p : 0));
+      const uint4 x0 = qp[0], x1 = qp[1];
+      const float dd = ok ? a.d[(size_t)tok * nblk + p] : 0.0f;
+      const int pg = dot_fp8_block(wg[i][0], wg[i][1], x0, x1);
+      const int pu = dot_fp8_block(wu[i][0], wu[i][1], x0, x1);
+      gacc = fmaf((float)pg, dd * sg[i], gacc);
+      uacc = fmaf((float)pu, dd * su[i], uacc);
+      if (DBG && ok) {
+        const size_t o = ((size_t)pair * I + r) * nblk + p;
+        if (a.dbg.gate_dots) a.dbg.gate_dots[o] = pg;
+        if (a.dbg.up_dots) a.dbg.up_dots[o] = pu;
+      }
+    }
+    const float g = wave_sum(gacc) * (1.0f / 512.0f);
+    const float u = wave_sum(uacc) * (1.0f / 512.0f);
+    if (lane == 0) {
+      const float hv = silu(g) * u;
+      a.h[(size_t)pair * I + r] = hv;
+      if (DBG && a.dbg.h) a.dbg.h[(size_t)pair * I + r] = hv;
+    }
+  }
+}
+
+// Down: Q8_0 of h for TT pairs into LDS (stage_qh), then DN_RPW rows per
+// wave, lane l taking blocks l + 64 i of each row.
+template <int TT, int NPL, bool DBG>
+__global__ void __launch_bounds__(256) k_down_f8(FfnArgs a) {
+  SlotInfo si;
+  if (!slot_info(a, blockIdx.y, si)) return;
+  extern __shared__ uint8_t smem[];
+  const int I = a.I, H = a.H, nblk = I / 32, nsb = I / 128;
+  int8_t *lq = reinterpret_cast<int8_t *>(smem);                // [TT][I]
+  float *ld = reinterpret_cast<float *>(smem + (size_t)TT * I);  // [TT][I/32]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const uint8_t *down = si.blob + 2 * (size_t)I * H;
+  const float *bs = reinterpret_cast<const float *>(si.blob + 3 * (size_t)I * H) +
+                    2 * (size_t)(I / 128) * (H / 128);
+  const int j0 = (blockIdx.x * 4 + wv) * DN_RPW;
+  uint4 wd[DN_RPW][NPL][2];
+  float sd[DN_RPW][NPL];
+#pragma unroll
+  for (int rr = 0; rr < DN_RPW; rr++)
+#pragma unroll
+    for (int i = 0; i < NPL; i++) {
+      const int p = lane + 64 * i, j = j0 + rr;
+      const bool ok = p < nblk;
+      const uint4 *dp = reinterpret_cast<const uint4 *>(down + (size_t)j * I + 32 * (ok ? p : 0));
+      wd[rr][i][0] = dp[0];
+      wd[rr][i][1] = dp[1];
+      sd[rr][i] = ok ? bs[(size_t)(j / 128) * nsb + p / 4] : 0.0f;
+    }
+  for (int c0 = 0; c0 < si.n_tok; c0 += TT) {
+    int pair[TT], tok[TT];
+#pragma unroll
+    for (int t = 0; t < TT; t++) {
+      pair[t] = -1;
+      tok[t] = 0;
+      if (c0 + t < si.n_tok) token_of(a, si, c0 + t, tok[t], pair[t]);
+    }
+    stage_qh<TT, DBG>(a, pair, lq, ld);  // Q8_0 of h
+    float acc[DN_RPW][TT];
+#pragma unroll
+    for (int rr = 0; rr < DN_RPW; rr++) {
+#pragma unroll
+      for (int t = 0; t < TT; t++) acc[rr][t] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < NPL; i++) {
+        opaque(wd[rr][i][0]);
+        opaque(wd[rr][i][1]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TT; t++) {
+#pragma unroll
+      for (int i = 0; i < NPL; i++) {
+        const int p = lane + 64 * i;
+        const bool ok = p < nblk;
+        const uint4 *qp = reinterpret_cast<const uint4 *>(lq + (size_t)t * I + 32 * (ok ? p : 0));
+        const uint4 x0 = qp[0], x1 = qp[1];
+        const float dd = ok ? ld[t * nblk + p] : 0.0f;
+#pragma unroll
+        for (int rr = 0; rr < DN_RPW; rr++) {
+          const int pd = dot_fp8_block(wd[rr][i][0], wd[rr][i][1], x0, x1);
+          acc[rr][t] = fmaf((float)pd, dd * sd[rr][i], acc[rr][t]);
+          if (DBG && a.dbg.down_dots && pair[t] >= 0 && ok)
+            a.dbg.down_dots[((size_t)pair[t] * H + j0 + rr) * nblk + p] = pd;
+        }
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < DN_RPW; rr++) {
+      const int j = j0 + rr;
+#pragma unroll
+      for (int t = 0; t < TT; t++) {
+        const float y = wave_sum(acc[rr][t]) * (1.0f / 512.0f);
+        if (lane == 0 && pair[t] >= 0) {
+          if (si.shared)
+            a.shared_out[(size_t)tok[t] * H + j] = y;
+          else
+            a.expert_out[(size_t)pair[t] * H + j] = y;
+        }
+      }
+    }
+  }
+}
+
+template <int TT, int NG, int ND, bool DBG>
+static void launch_f8_tt(const FfnArgs &a, int n_slots, hipStream_t st, const moe_events *ev) {
+  const size_t lds = (size_t)TT * a.I + sizeof(float) * (size_t)TT * (a.I / 32);
+  launch_k(k_gate_up_f8<NG, DBG>, dim3(a.I / 4, n_slots), dim3(256), 0, st,
+           stage_ev(ev, MOE_STAGE_GATE_UP), a);
+  launch_k(k_down_f8<TT, ND, DBG>, dim3(a.H / (4 * DN_RPW), n_slots), dim3(256), (uint32_t)lds,
+           st, stage_ev(ev, MOE_STAGE_DOWN), a);
+}
+
+template <int TT, bool DBG>
+static void launch_f8_shape(const FfnArgs &a, int n_slots, hipStream_t st,
+                            const moe_events *ev) {
+  const int ng = (a.H / 32 + 63) / 64, nd = (a.I / 32 + 63) / 64;
+  if (ng <= 1 && nd <= 1) launch_f8_tt<TT, 1, 1, DBG>(a, n_slots, st, ev);
+  else if (ng <= 2 && nd <= 1) launch_f8_tt<TT, 2, 1, DBG>(a, n_slots, st, ev);
+  else if (ng <= 3 && nd <= 1) launch_f8_tt<TT, 3, 1, DBG>(a, n_slots, st, ev);
+  else if (ng <= 4 && nd <= 1) launch_f8_tt<TT, 4, 1, DBG>(a, n_slots, st, ev);
+  else launch_f8_tt<TT, 4, 2, DBG>(a, n_slots, st, ev);
+}
+
+bool f8_supported(const FfnArgs &a) {
+  return a.H % 128 == 0 && a.I % 128 == 0 && a.H / 32 <= 256 && a.I / 32 <= 128 &&
+         a.H % (4 * DN_RPW) == 0;
+}
+
+void launch_ffn_f8(const FfnArgs &a, hipStream_t st, const moe_events *ev) {
+  const int n_slots = a.n_shared + (a.T * a.K < a.E ? a.T * a.K : a.E);
+  const bool dbg = a.dbg.gate_dots || a.dbg.up_dots || a.dbg.h || a.dbg.q_h || a.dbg.d_h ||
+                   a.dbg.down_dots;
+  const int tt = a.T <= 1 ? 1 : (a.T <= 2 ? 2 : 4);
+  if (dbg) {
+    if (tt == 1) launch_f8_shape<1, true>(a, n_slots, st, ev);
+    else if (tt == 2) launch_f8_shape<2, true>(a, n_slots, st, ev);
+    else launch_f8_shape<4, true>(a, n_slots, st, ev);
+  } else {
+    if (tt == 1) launch_f8_shape<1, false>(a, n_slots, st, ev);
+    else if (tt == 2) launch_f8_shape<2, false>(a, n_slots, st, ev);
+    else launch_f8_shape<4, false>(a, n_slots, st, ev);
   }
 }
 

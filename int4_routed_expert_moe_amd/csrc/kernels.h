@@ -59,7 +59,7 @@ void launch_group(int n_slots, int E, const int32_t *idx, int32_t *counts, int32
 // Expert FFN over grouped tokens (dot-product GEMV path).
 struct FfnArgs {
   int H, I, E, K, T, n_shared, wbits;
-  int wfmt;  // 0: integer codes with row scales; 1: MXFP4
+  int wfmt;  // 0: integer codes with row scales; 1: MXFP4; 2: FP8 with 128x128 block scales
   size_t blob_bytes;
   const int8_t *q;
   const float *d;
@@ -73,6 +73,10 @@ struct FfnArgs {
   moe_ffn_debug dbg;
 };
 void launch_ffn_gemv(const FfnArgs &a, hipStream_t st, const moe_events *ev = nullptr);
+// FP8 E4M3 experts with 128x128 block scales (wfmt 2), every batch size:
+// vector gate/up and down with exact int32 block dots (ffn_gemv.hip).
+bool f8_supported(const FfnArgs &a);
+void launch_ffn_f8(const FfnArgs &a, hipStream_t st, const moe_events *ev = nullptr);
 
 // Expert FFN over grouped tokens on the matrix cores (ffn_mfma.hip): tile list
 // from the grouping offsets, then grouped gate/up (Q8_0 of h into q_h/d_h,
@@ -103,7 +107,7 @@ void launch_down_mfma_slots(const FfnArgs &a, const int32_t *slots, int n_slots_
 // Whole layer for 1..16 tokens in four kernels (decode.h).
 struct LayerArgs {
   int H, I, E, G, TG, K, T, n_shared, wbits;
-  int wfmt;  // 0: integer codes with row scales; 1: MXFP4
+  int wfmt;  // 0: integer codes with row scales; 1: MXFP4; 2: FP8 with 128x128 block scales
   float scale, eps;
   float top_p;  // adaptive expert top-p; 0 or 1 = off
   size_t blob_bytes;

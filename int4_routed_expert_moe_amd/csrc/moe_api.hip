@@ -70,9 +70,11 @@ int check_cfg(const moe_cfg *c) {
     return fail(MOE_EINVAL, "routed_scaling must be finite and > 0");
   if (!(c->top_p >= 0.0f && c->top_p <= 1.0f))
     return fail(MOE_EINVAL, "top_p must be 0 (off) or in (0, 1]");
-  if (c->wfmt != 0 && c->wfmt != 1) return fail(MOE_EINVAL, "wfmt=%d not in {0,1}", c->wfmt);
+  if (c->wfmt < 0 || c->wfmt > 2) return fail(MOE_EINVAL, "wfmt=%d not in {0,1,2}", c->wfmt);
   if (c->wfmt == 1 && c->wbits != 4)
     return fail(MOE_EINVAL, "MXFP4 experts (wfmt 1) need wbits 4 (4-bit codes)");
+  if (c->wfmt == 2 && c->wbits != 8)
+    return fail(MOE_EINVAL, "FP8 experts (wfmt 2) need wbits 8 (byte codes)");
   if (c->act_block != 0 && c->act_block != 32 && c->act_block != MOE_ACT_ROW)
     return fail(MOE_EINVAL, "act_block=%d not in {0, 32, MOE_ACT_ROW}", c->act_block);
   if (c->act_block == MOE_ACT_ROW && (c->wfmt != 0 || (c->wbits != 4 && c->wbits != 8)))
@@ -81,6 +83,12 @@ int check_cfg(const moe_cfg *c) {
 }
 
 bool act_rows(const moe_cfg &c) { return c.act_block == MOE_ACT_ROW; }
+
+// Byte ranges [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return a && b && x < y + nb && y < x + na;
+}
 
 #define REQUIRE(p, name)                                                       \
   do {                                                                         \
@@ -107,6 +115,8 @@ int launched(const char *what) {
 size_t blob_bytes(const moe_cfg &c) {
   const size_t elems = (size_t)2 * c.inter * c.hidden + (size_t)c.hidden * c.inter;
   if (c.wfmt == 1) return elems / 2 + elems / 32;  // FP4 codes + one E8M0 byte per 32
+  if (c.wfmt == 2)  // E4M3 bytes + one fp32 scale per 128x128 block of each matrix
+    return elems + sizeof(float) * 3 * (size_t)(c.inter / 128) * (c.hidden / 128);
   return elems * (size_t)c.wbits / 8 + sizeof(float) * ((size_t)2 * c.inter + c.hidden);
 }
 
@@ -236,6 +246,12 @@ int do_ffn(const moe_cfg &c, int T, const int8_t *q, const float *d, const int32
     int8_t *q_h = a.dbg.q_h ? a.dbg.q_h : ws.qh_rows;  // written straight into a dump
     float *d_h = a.dbg.d_h ? a.dbg.d_h : ws.dh_rows;
     moe::launch_ffn_mfma_rows(a, ws.tiles, ws.n_tiles, ws.h, q_h, d_h, idx, st, ev);
+    return launched("moe_expert_ffn");
+  }
+  if (c.wfmt == 2) {  // FP8: the vector kernels with exact block dots, every T
+    if (!moe::f8_supported(a))
+      return fail(MOE_EINVAL, "FP8 experts need hidden <= 8192 and inter <= 4096");
+    moe::launch_ffn_f8(a, st, ev);
     return launched("moe_expert_ffn");
   }
   const bool mfma = moe::mfma_supported(a);
@@ -389,6 +405,9 @@ int moe_combine(int32_t T, int32_t H, int32_t K, const float *expert_out, const 
   OPTIONAL(residual, "residual");
   REQUIRE(y, "y");
   OPTIONAL(y_norm, "y_norm");
+  const size_t row_bytes = sizeof(float) * (size_t)T * H;
+  if (overlap(y, row_bytes, y_norm, row_bytes))
+    return fail(MOE_EINVAL, "y_norm overlaps y");
   moe::launch_combine(T, H, K, expert_out, w, shared_out, residual, y, y_norm, eps,
                       (hipStream_t)stream);
   return launched("moe_combine");
@@ -411,6 +430,8 @@ int moe_rmsnorm(int32_t T, int32_t H, const float *x, float *y, float eps, void 
   if (T == 0) return MOE_OK;
   REQUIRE(x, "x");
   REQUIRE(y, "y");
+  const size_t row_bytes = sizeof(float) * (size_t)T * H;
+  if (overlap(x, row_bytes, y, row_bytes)) return fail(MOE_EINVAL, "y overlaps x");
   moe::launch_rmsnorm(T, H, x, y, eps, (hipStream_t)stream);
   return launched("moe_rmsnorm");
 }
@@ -474,6 +495,9 @@ int layer_impl(const moe_cfg *cfg, int32_t T, const float *x, const float *w_rou
   OPTIONAL(y_norm, "y_norm");
   OPTIONAL(idx_out, "idx_out");
   OPTIONAL(w_out, "w_out");
+  if (overlap(y, sizeof(float) * (size_t)T * cfg->hidden, y_norm,
+              sizeof(float) * (size_t)T * cfg->hidden))
+    return fail(MOE_EINVAL, "y_norm overlaps y");
   if (expert_ptrs) {
     if (!aligned(expert_ptrs, 8)) return fail(MOE_EALIGN, "expert_ptrs is not 8-byte aligned");
   } else {

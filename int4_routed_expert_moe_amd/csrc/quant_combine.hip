@@ -89,86 +89,83 @@ void launch_quant_rows(const float *x, int8_t *q, float *d, int64_t rows, int n,
            d, n, skip, n_skip);
 }
 
-// One block per token row; 256 threads stride over H in float4.
-// y = residual + shared + sum_k w_k * expert_k (fp32, rank order); optional
-// unit-gain RMSNorm of y.
+// y = residual + shared + sum_k w_k * expert_k (fp32, rank order); the
+// optional unit-gain RMSNorm of y is a second kernel (k_rmsnorm).
+// Workgroup (t, c): values 1024 c .. 1024 c + 1023 of token t's output (one
+// float4 per thread), so that a few tokens still spread over many CUs.
 __global__ void __launch_bounds__(256) k_combine(int H, int K, const float *__restrict__ eo,
                                                  const float *__restrict__ w,
                                                  const float *__restrict__ shared,
                                                  const float *__restrict__ residual,
-                                                 float *__restrict__ y, float *__restrict__ yn,
-                                                 float eps) {
-  const int t = blockIdx.x;
+                                                 float *__restrict__ y) {
+  const int t = blockIdx.x, j = blockIdx.y * 256 + threadIdx.x;
   const int H4 = H / 4;
   __shared__ float wk[16];
-  __shared__ float red[4];
   if (threadIdx.x < K) wk[threadIdx.x] = w[(size_t)t * K + threadIdx.x];
   __syncthreads();
-  float ss = 0.0f;
+  if (j >= H4) return;
   const float4 *eo4 = reinterpret_cast<const float4 *>(eo) + (size_t)t * K * H4;
-  for (int j = threadIdx.x; j < H4; j += 256) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (residual) acc = reinterpret_cast<const float4 *>(residual)[(size_t)t * H4 + j];
-    if (shared) {
-      float4 s = reinterpret_cast<const float4 *>(shared)[(size_t)t * H4 + j];
-      acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
-    }
-    for (int k = 0; k < K; k++) {
-      const float c = wk[k];
-      if (c == 0.0f) continue;  // a rank dropped by top-p: its row is not read
-      float4 e = eo4[(size_t)k * H4 + j];
-      acc.x = fmaf(c, e.x, acc.x);
-      acc.y = fmaf(c, e.y, acc.y);
-      acc.z = fmaf(c, e.z, acc.z);
-      acc.w = fmaf(c, e.w, acc.w);
-    }
-    reinterpret_cast<float4 *>(y)[(size_t)t * H4 + j] = acc;
-    ss += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (residual) acc = reinterpret_cast<const float4 *>(residual)[(size_t)t * H4 + j];
+  if (shared) {
+    float4 s = reinterpret_cast<const float4 *>(shared)[(size_t)t * H4 + j];
+    acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
   }
-  if (!yn) return;
+  for (int k = 0; k < K; k++) {
+    const float c = wk[k];
+    if (c == 0.0f) continue;  // a rank dropped by top-p: its row is not read
+    float4 e = eo4[(size_t)k * H4 + j];
+    acc.x = fmaf(c, e.x, acc.x);
+    acc.y = fmaf(c, e.y, acc.y);
+    acc.z = fmaf(c, e.z, acc.z);
+    acc.w = fmaf(c, e.w, acc.w);
+  }
+  reinterpret_cast<float4 *>(y)[(size_t)t * H4 + j] = acc;
+}
+
+// RMSNorm, workgroup (t, c): the sum of squares of token t's whole row (read
+// by every workgroup of the row, four loads in flight per thread), then
+// values 1024 c .. 1024 c + 1023 scaled.
+__global__ void __launch_bounds__(256) k_rmsnorm(int H, const float *__restrict__ x,
+                                                 float *__restrict__ y, float eps) {
+  const int t = blockIdx.x, jc = blockIdx.y * 256 + threadIdx.x;
+  const int H4 = H / 4;
+  __shared__ float red[4];
+  const float4 *x4 = reinterpret_cast<const float4 *>(x) + (size_t)t * H4;
+  float ss = 0.0f;
+  for (int j0 = 0; j0 < H4; j0 += 1024) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int j = j0 + u * 256 + threadIdx.x;
+      v[u] = j < H4 ? x4[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) ss += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
+  }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float tot = red[0] + red[1] + red[2] + red[3];
-  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
-  for (int j = threadIdx.x; j < H4; j += 256) {
-    float4 v = reinterpret_cast<const float4 *>(y)[(size_t)t * H4 + j];
+  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+  if (jc < H4) {
+    float4 v = x4[jc];
     v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
-    reinterpret_cast<float4 *>(yn)[(size_t)t * H4 + j] = v;
+    reinterpret_cast<float4 *>(y)[(size_t)t * H4 + jc] = v;
   }
 }
 
 void launch_combine(int T, int H, int K, const float *eo, const float *w, const float *shared,
                     const float *residual, float *y, float *yn, float eps, hipStream_t st,
                     const moe_events *ev) {
-  launch_k(k_combine, dim3(T), dim3(256), 0, st, stage_ev(ev, MOE_STAGE_COMBINE), H, K, eo, w,
-           shared, residual, y, yn, eps);
-}
-
-__global__ void __launch_bounds__(256) k_rmsnorm(int H, const float *__restrict__ x,
-                                                 float *__restrict__ y, float eps) {
-  const int t = blockIdx.x;
-  const int H4 = H / 4;
-  __shared__ float red[4];
-  const float4 *x4 = reinterpret_cast<const float4 *>(x) + (size_t)t * H4;
-  float ss = 0.0f;
-  for (int j = threadIdx.x; j < H4; j += 256) {
-    float4 v = x4[j];
-    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-  }
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
-  for (int j = threadIdx.x; j < H4; j += 256) {
-    float4 v = x4[j];
-    v.x *= inv; v.y *= inv; v.z *= inv; v.w *= inv;
-    reinterpret_cast<float4 *>(y)[(size_t)t * H4 + j] = v;
-  }
+  const Ev e = stage_ev(ev, MOE_STAGE_COMBINE);
+  const dim3 g(T, (H / 4 + 255) / 256);
+  launch_k(k_combine, g, dim3(256), 0, st, Ev{e.start, yn ? nullptr : e.stop}, H, K, eo, w,
+           shared, residual, y);
+  if (yn) launch_k(k_rmsnorm, g, dim3(256), 0, st, Ev{nullptr, e.stop}, H, (const float *)y, yn, eps);
 }
 
 void launch_rmsnorm(int T, int H, const float *x, float *y, float eps, hipStream_t st) {
-  hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(256), 0, st, H, x, y, eps);
+  hipLaunchKernelGGL(k_rmsnorm, dim3(T, (H / 4 + 255) / 256), dim3(256), 0, st, H, x, y, eps);
 }
 
 }  // namespace moe

@@ -152,6 +152,10 @@ def test_combine_and_layer_errors(L):
     assert L.moe_combine(2, 6144, 8, A, A, A + 4, None, A, None, 1e-5, None) == moe.MOE_EALIGN
     assert L.moe_combine(2, 6144, 8, A, A, None, None, A, None, -1.0, None) == moe.MOE_EINVAL
     assert L.moe_rmsnorm(2, 6144, None, A, 1e-5, None) == moe.MOE_EINVAL
+    # outputs may not overlap the row they are computed from (several workgroups per row)
+    assert L.moe_rmsnorm(2, 64, A, A + 256, 1e-5, None) == moe.MOE_EINVAL
+    assert b"overlaps" in L.moe_last_error()
+    assert L.moe_combine(2, 64, 0, None, None, None, None, A, A + 16, 1e-5, None) == moe.MOE_EINVAL
     assert L.moe_mfma_peak(0, 10, A, None) == moe.MOE_EINVAL
     assert L.moe_mfma_peak(4, 0, A, None) == moe.MOE_EINVAL
     assert L.moe_mfma_peak(4, 1 << 21, A, None) == moe.MOE_EINVAL
@@ -188,6 +192,23 @@ def test_layer_noalloc_rejects_batches_beyond_its_scratch(L):
                                None, None, None) == moe.MOE_EINVAL
     assert L.moe_layer_noalloc(ctypes.byref(c), 0, None, None, None, None, None, None, None,
                                None, 1e-5, None, None, None, None) == moe.MOE_OK
+
+
+def test_fp8_records(L):
+    """FP8 experts (wfmt 2) need byte codes (wbits 8), Q8_0 activations and
+    multiples of 128; the record size agrees with the generator's and the
+    oracle's layout."""
+    import oracle
+    f8 = moe.Config.of(synth.REAL.with_bits(synth.FP8))
+    assert (f8.wbits, f8.wfmt) == (8, 2)
+    H, I = synth.REAL.hidden, synth.REAL.inter
+    assert moe.blob_bytes(f8) == 3 * I * H + 3 * (I // 128) * (H // 128) * 4 == 37_757_952
+    assert moe.blob_bytes(f8) == synth.blob_bytes(synth.REAL.with_bits(synth.FP8))
+    assert moe.blob_bytes(f8) == oracle.blob_bytes(H, I, oracle.FP8)
+    for field, value in (("wbits", 4), ("wfmt", 3), ("act_block", moe.ACT_ROW)):
+        c = f8.c()
+        setattr(c, field, value)
+        assert L.moe_expert_blob_bytes(ctypes.byref(c)) == 0, field
 
 
 def test_per_row_activations_take_int4_or_int8_codes(L):

@@ -34,7 +34,7 @@ from _inputs import DeviceLayer, assert_close_rms, pairs_of
 
 pytestmark = pytest.mark.gpu
 
-FORMATS = {"int4": 4, "int2": 2, "int8": 8, "mxfp4": synth.MXFP4}
+FORMATS = {"int4": 4, "int2": 2, "int8": 8, "mxfp4": synth.MXFP4, "fp8": synth.FP8}
 UNION = ("counts", "offsets", "perm", "inv", "active")
 
 
@@ -168,7 +168,7 @@ def test_layer_dumps_top_p_and_residual(dev):
     check_layer_dumps(lay, x[:4], dev, top_p=0.5)
 
 
-@pytest.mark.parametrize("fmt", ["int4", "int8"])
+@pytest.mark.parametrize("fmt", ["int4", "int8", "fp8"])
 def test_layer_dumps_chained_path(dev, fmt):
     """Above 16 tokens the same dumps come from the chained kernels."""
     lay = real_layer(fmt)
@@ -243,10 +243,14 @@ def test_ties_duplicated_router_rows(dev, T):
 def pattern_codes(rng, rows, n, fmt, variant):
     """Code matrices that use every code: per row, cycling over families --
     all lowest code, lowest/highest alternating, every code in turn, uniform
-    random, and for MXFP4 blocks of +0/-0 only."""
+    random, and for MXFP4 blocks of +0/-0 only.  FP8: raw E4M3 bytes (as
+    int8), every code but the two NaN ones (0x7F, 0xFF)."""
     wb = FORMATS[fmt]
     if wb == synth.MXFP4:
         lo, hi, allc = 15, 7, np.arange(16)  # raw E2M1 codes: 15 = -6, 7 = +6, 8 = -0
+    elif wb == synth.FP8:
+        allc = np.array([c for c in range(256) if c & 0x7F != 0x7F]).astype(np.uint8).view(np.int8)
+        lo, hi = np.int8(np.uint8(0xFE).view(np.int8)), np.int8(0x7E)  # -448, +448
     else:
         lo, hi = -(1 << (wb - 1)), (1 << (wb - 1)) - 1
         allc = np.arange(lo, hi + 1)
@@ -279,7 +283,11 @@ def pattern_record(shape, fmt, variant):
     mats = [pattern_codes(rng, I, H, fmt, variant), pattern_codes(rng, I, H, fmt, variant + 1),
             pattern_codes(rng, H, I, fmt, variant + 2)]
     packed = [oracle.pack(m.ravel(), wb) for m in mats]
-    if wb == synth.MXFP4:
+    if wb == synth.FP8:  # one fp32 scale per 128x128 block
+        sc = [(rng.uniform(0.5, 1.5, (m.shape[0] // 128) * (m.shape[1] // 128)) * 0.02 / 448)
+              .astype(np.float32) for m in mats]
+        rec = np.concatenate(packed + [v.view(np.uint8) for v in sc])
+    elif wb == synth.MXFP4:
         scales = []
         for m in mats:
             rows, n = m.shape

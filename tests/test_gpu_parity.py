@@ -293,6 +293,34 @@ def test_ffn_prefill_mxfp4(dev, real_mx):
                check_chain=False)
 
 
+# FP8 E4M3 experts with 128x128 block scales: the vector kernels at every
+# batch size; the dumped block dots are sum 512 fp8(c) q, exact integers.
+
+@pytest.fixture(scope="module")
+def real_f8(dev):
+    return DeviceLayer(synth.REAL.with_bits(synth.FP8), synth.SEEDS["decode"])
+
+
+@pytest.mark.parametrize("T", [1, 4, 40])
+def test_ffn_tiny_fp8(dev, T):
+    lay = DeviceLayer(synth.TINY.with_bits(synth.FP8), synth.SEEDS["tiny"])
+    _ffn_check(lay, synth.tokens(synth.TINY, synth.SEEDS["tiny"], T, start=4), dev)
+
+
+def test_ffn_decode_fp8(dev, real_f8):
+    _ffn_check(real_f8, synth.tokens(synth.REAL, synth.SEEDS["decode"], 1, start=3), dev)
+
+
+def test_ffn_verify_fp8(dev, real_f8):
+    _ffn_check(real_f8, synth.tokens_perturbed(synth.REAL, synth.SEEDS["verify"], 4), dev,
+               check_chain=False)
+
+
+def test_ffn_prefill_fp8(dev, real_f8):
+    _ffn_check(real_f8, synth.tokens(synth.REAL, synth.SEEDS["prefill"], 24), dev,
+               check_chain=False)
+
+
 @pytest.mark.parametrize("T", [1, 4, 40])
 def test_ffn_tiny_int8(dev, T):
     lay = DeviceLayer(synth.TINY.with_bits(8), synth.SEEDS["tiny"])
