@@ -20,6 +20,7 @@
 namespace moe {
 
 constexpr int GW = 16;  // waves per group workgroup
+constexpr int PB = 8;   // slots per lane loaded together
 
 // Exclusive prefix sum over the 1024 threads of the block; *total receives
 // the sum of all v.  Every thread must call it (contains barriers).
@@ -63,9 +64,17 @@ __global__ void __launch_bounds__(GW * 64) k_group(int n_slots, int E,
 
   for (int i = tid; i < GW * E; i += GW * 64) hist[i] = 0;
   __syncthreads();
-  for (int s = s_lo + lane; s < s_hi; s += 64) {
-    const int e = idx[s];
-    if (e >= 0 && e < E) atomicAdd(&hist[wv * E + e], 1);
+  // idx in batches of PB slots per lane, each batch's loads in one round trip
+  for (int base = s_lo; base < s_hi; base += 64 * PB) {
+    int ev[PB];
+#pragma unroll
+    for (int u = 0; u < PB; u++) {
+      const int s = base + 64 * u + lane;
+      ev[u] = s < s_hi ? idx[s] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < PB; u++)
+      if (ev[u] >= 0 && ev[u] < E) atomicAdd(&hist[wv * E + ev[u]], 1);
   }
   __syncthreads();
   int c = 0;
@@ -96,27 +105,40 @@ __global__ void __launch_bounds__(GW * 64) k_group(int n_slots, int E,
   // Stable placement, 64 slots at a time in slot order.  Only wave wv touches
   // its cursors hist[wv][*], and a wave's LDS accesses are performed in
   // program order, so no barrier is needed inside this (wave-divergent) loop.
-  for (int base = s_lo; base < s_hi; base += 64) {
-    const int s = base + lane;
-    int e = (s < s_hi) ? idx[s] : -1;
-    if (e >= E || e < 0) e = -1;
-    int rank = 0, same = 0;
-    for (int j = 0; j < 64; j++) {
-      const int ej = __shfl(e, j, 64);
-      rank += (j < lane && ej == e) ? 1 : 0;
-      same += (ej == e) ? 1 : 0;
+  for (int base = s_lo; base < s_hi; base += 64 * PB) {
+    int ev[PB];
+#pragma unroll
+    for (int u = 0; u < PB; u++) {
+      const int s = base + 64 * u + lane;
+      ev[u] = s < s_hi ? idx[s] : -1;
     }
-    int pos = 0;
-    if (e >= 0) pos = off[e] + hist[wv * E + e] + rank;
-    __builtin_amdgcn_wave_barrier();
-    if (e >= 0) {
-      perm[pos] = s;
-      inv[s] = pos;
-      if (rank == 0) hist[wv * E + e] += same;  // the first lane holding e advances
-    } else if (s < s_hi) {
-      inv[s] = -1;  // not routed (top-p drop)
+#pragma unroll
+    for (int u = 0; u < PB; u++) {
+      const int s = base + 64 * u + lane;
+      const int e = (ev[u] >= 0 && ev[u] < E) ? ev[u] : -1;
+      // lanes holding the same expert: the valid lanes that agree with e on
+      // each of its 10 bits (E <= 1024)
+      unsigned long long m = __ballot(e >= 0);
+#pragma unroll
+      for (int b = 0; b < 10; b++) {
+        const bool bit = (e >> b) & 1;
+        const unsigned long long bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      const int rank = __popcll(m & ((1ull << lane) - 1ull));  // same expert, earlier lanes
+      const int same = __popcll(m);
+      int pos = 0;
+      if (e >= 0) pos = off[e] + hist[wv * E + e] + rank;
+      __builtin_amdgcn_wave_barrier();
+      if (e >= 0) {
+        perm[pos] = s;
+        inv[s] = pos;
+        if (rank == 0) hist[wv * E + e] += same;  // the first lane holding e advances
+      } else if (s < s_hi) {
+        inv[s] = -1;  // not routed (top-p drop)
+      }
+      __builtin_amdgcn_wave_barrier();
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 

@@ -208,7 +208,8 @@ __global__ void __launch_bounds__(64) k_router_select(int E, int G, int TG, int 
                                                       const float *__restrict__ sb,
                                                       int32_t *__restrict__ idx,
                                                       float *__restrict__ w) {
-  __shared__ float lsb[1024];
+  __shared__ __align__(16) float lsb[1024];  // the token's biased scores
+  __shared__ float ls[1024];                 // and its unbiased ones
   __shared__ float gscore[64];
   __shared__ float ssel[16];
   __shared__ int isel[16];
@@ -216,18 +217,33 @@ __global__ void __launch_bounds__(64) k_router_select(int E, int G, int TG, int 
   const int gs = E / G;
   const float *srow = s + (size_t)t * E;
   const float *sbrow = sb + (size_t)t * E;
-  for (int e = lane; e < E; e += 64) lsb[e] = sbrow[e];
+  // both rows in one round trip (a pick's unbiased score read from memory
+  // inside the selection loop put one round trip per pick in series)
+  for (int e = lane; e < E; e += 64) {
+    lsb[e] = sbrow[e];
+    ls[e] = srow[e];
+  }
   __syncthreads();
-  if (lane < G) {
+  if (lane < G) {  // the two largest of the group (a multiset), in index order
     float m1 = -INFINITY, m2 = -INFINITY;
-    for (int e = lane * gs; e < (lane + 1) * gs; e++) {
-      const float v = lsb[e];
+    auto take = [&](float v) {
       if (v > m1) {
         m2 = m1;
         m1 = v;
       } else if (v > m2) {
         m2 = v;
       }
+    };
+    if ((gs & 3) == 0) {  // 16-byte LDS reads, four values per read
+      for (int e = lane * gs; e < (lane + 1) * gs; e += 4) {
+        const float4 v = *reinterpret_cast<const float4 *>(lsb + e);
+        take(v.x);
+        take(v.y);
+        take(v.z);
+        take(v.w);
+      }
+    } else {
+      for (int e = lane * gs; e < (lane + 1) * gs; e++) take(lsb[e]);
     }
     gscore[lane] = m1 + m2;
   }
@@ -260,7 +276,7 @@ __global__ void __launch_bounds__(64) k_router_select(int E, int G, int TG, int 
     if ((e & 63) == lane) taken |= 1u << (e >> 6);
     if (lane == 0) {
       isel[k] = e;
-      ssel[k] = srow[e];
+      ssel[k] = ls[e];
     }
   }
   __syncthreads();
