@@ -12,8 +12,12 @@
 // int8 MFMA of gfx950 (v_mfma_i32_16x16x64_i8, twice the work per
 // instruction of the K = 32 one) with no fix-up arithmetic in the inner loop.
 //
-// A workgroup computes 128 rows x 64 tokens of one work item (expert, token
-// tile), 4 waves of 32 rows, gate and up together in the gate/up kernel.  K
+// A workgroup computes 4 x 16 RS rows x 64 tokens of one work item (expert,
+// token tile), 4 waves of 16 RS rows, gate and up together in the gate/up
+// kernel; RS = 2 (32 rows per wave): with RS = 1 three workgroups fit on a
+// CU instead of two, but every MFMA then needs twice the activation bytes
+// from LDS, and both GEMMs ran slower (dense 2048-token int4 gate/up 0.349
+// against 0.369 of the int8 peak, down 0.245 against 0.280).  K
 // runs in chunks staged in LDS (weights as packed codes, activations
 // reordered like the nibble split for int4), the next chunk in registers
 // meanwhile.  Row strides in LDS are padded so that the 8-byte (int4
@@ -25,9 +29,16 @@
 
 namespace moe {
 
+// row sub-tiles of 16 per wave (2: 32 rows per wave, 128 per workgroup)
+#ifndef MOE_ROWS_RS
+#define MOE_ROWS_RS 2
+#endif
+
 namespace mr {
-constexpr int NT = TILE_T;  // tokens per work item
-constexpr int RT = 128;  // rows per workgroup, 32 per wave
+constexpr int NT = TILE_T;       // tokens per work item
+constexpr int RS = MOE_ROWS_RS;  // 16-row sub-tiles per wave
+constexpr int RW = 16 * RS;      // rows per wave
+constexpr int RT = 4 * RW;       // rows per workgroup
 template <int WB>
 constexpr int KC() { return WB == 8 ? 128 : 256; }  // K (codes) per chunk: 128 bytes of a row
 template <int WB>
@@ -36,7 +47,7 @@ template <int WB>
 constexpr int BSTR() { return KC<WB>() + 16; }  // LDS bytes per activation row
 }  // namespace mr
 
-// One K chunk in registers: NM weight matrices x 128 rows x 128 bytes, and
+// One K chunk in registers: NM weight matrices x RT rows x 128 bytes, and
 // 64 activation rows x KC bytes, as 16-byte pieces per thread.
 template <int NM, int WB>
 struct RChunk {
@@ -111,14 +122,14 @@ __device__ __forceinline__ void rstore(const RChunk<NM, WB> &r, uint8_t *as, uin
 template <int NM, int NS, int WB>
 __device__ void rkloop(const uint8_t *const *mat, size_t row_b, int r0, const int8_t *q,
                        const int *tokl, int K, uint8_t *as, uint8_t *bs,
-                       v4i (&acc)[NM][2][4]) {
+                       v4i (&acc)[NM][mr::RS][4]) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int m16 = lane & 15, g = lane >> 4;
   constexpr int KC = mr::KC<WB>(), AS = mr::ASTR<WB>(), BS = mr::BSTR<WB>();
 #pragma unroll
   for (int m = 0; m < NM; m++)
 #pragma unroll
-    for (int rs = 0; rs < 2; rs++)
+    for (int rs = 0; rs < mr::RS; rs++)
 #pragma unroll
       for (int s = 0; s < 4; s++) acc[m][rs][s] = v4i{0, 0, 0, 0};
   const int nchunk = (K + KC - 1) / KC;
@@ -133,12 +144,12 @@ __device__ void rkloop(const uint8_t *const *mat, size_t row_b, int r0, const in
 #pragma unroll
     for (int st = 0; st < KC / 64; st++) {
       if (st < steps) {
-        v4i af[NM][2];
+        v4i af[NM][mr::RS];
 #pragma unroll
         for (int m = 0; m < NM; m++)
 #pragma unroll
-          for (int rs = 0; rs < 2; rs++) {
-            const uint8_t *ar = as + (size_t)(m * mr::RT + wv * 32 + rs * 16 + m16) * AS;
+          for (int rs = 0; rs < mr::RS; rs++) {
+            const uint8_t *ar = as + (size_t)(m * mr::RT + wv * mr::RW + rs * 16 + m16) * AS;
             if constexpr (WB == 8) {
               const uint4 w = *reinterpret_cast<const uint4 *>(ar + st * 64 + g * 16);
               af[m][rs] = v4i{(int)w.x, (int)w.y, (int)w.z, (int)w.w};
@@ -155,7 +166,7 @@ __device__ void rkloop(const uint8_t *const *mat, size_t row_b, int r0, const in
 #pragma unroll
           for (int m = 0; m < NM; m++)
 #pragma unroll
-            for (int rs = 0; rs < 2; rs++)
+            for (int rs = 0; rs < mr::RS; rs++)
               acc[m][rs][s] =
                   __builtin_amdgcn_mfma_i32_16x16x64_i8(af[m][rs], bf, acc[m][rs][s], 0, 0, 0);
         }
@@ -167,7 +178,7 @@ __device__ void rkloop(const uint8_t *const *mat, size_t row_b, int r0, const in
 template <int NM, int WB>
 __device__ void rkloop_n(const uint8_t *const *mat, size_t row_b, int r0, const int8_t *q,
                          const int *tokl, int K, int n, uint8_t *as, uint8_t *bs,
-                         v4i (&acc)[NM][2][4]) {
+                         v4i (&acc)[NM][mr::RS][4]) {
   switch ((n + 15) / 16) {
     case 1: rkloop<NM, 1, WB>(mat, row_b, r0, q, tokl, K, as, bs, acc); break;
     case 2: rkloop<NM, 2, WB>(mat, row_b, r0, q, tokl, K, as, bs, acc); break;
@@ -176,7 +187,7 @@ __device__ void rkloop_n(const uint8_t *const *mat, size_t row_b, int r0, const 
   }
 }
 
-// Workgroup (row tile, work item): rows 128 x .. of gate and up for the work
+// Workgroup (row tile, work item): rows RT x .. of gate and up for the work
 // item's tokens; h = silu(g) * u (fp32) to hbuf [P][I], quantised per row by
 // the next kernel once every row tile of the pair is written.
 template <bool DBG, int WB>
@@ -205,20 +216,20 @@ __global__ void __launch_bounds__(256) k_gate_up_rows(FfnArgs a, const int4 *til
   const size_t row_b = (size_t)H * code_bits<WB>() / 8;
   const uint8_t *mats[2] = {ti.blob, ti.blob + (size_t)I * row_b};
   const uint8_t *tail = ti.blob + 3 * (size_t)I * row_b;
-  float4 sc[2][2];  // row scales of this lane's 4 rows: [gate, up][rs]
+  float4 sc[2][mr::RS];  // row scales of this lane's 4 rows: [gate, up][rs]
 #pragma unroll
   for (int m = 0; m < 2; m++)
 #pragma unroll
-    for (int rs = 0; rs < 2; rs++) {
-      const uint4 u = gload<uint4>(tail, 4 * ((size_t)m * I + r0 + wv * 32 + rs * 16 + g * 4));
+    for (int rs = 0; rs < mr::RS; rs++) {
+      const uint4 u = gload<uint4>(tail, 4 * ((size_t)m * I + r0 + wv * mr::RW + rs * 16 + g * 4));
       sc[m][rs] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
                               __uint_as_float(u.w));
     }
-  v4i acc[2][2][4];
+  v4i acc[2][mr::RS][4];
   rkloop_n<2, WB>(mats, row_b, r0, a.q, tokl, H, ti.n, as, bs, acc);
 #pragma unroll
-  for (int rs = 0; rs < 2; rs++) {
-    const int row = r0 + wv * 32 + rs * 16 + g * 4;  // 4 consecutive rows per lane
+  for (int rs = 0; rs < mr::RS; rs++) {
+    const int row = r0 + wv * mr::RW + rs * 16 + g * 4;  // 4 consecutive rows per lane
 #pragma unroll
     for (int s = 0; s < 4; s++) {
       const int col = s * 16 + m16;
@@ -247,7 +258,7 @@ __global__ void __launch_bounds__(256) k_gate_up_rows(FfnArgs a, const int4 *til
   }
 }
 
-// Workgroup (row tile, work item): output rows 128 x .. of the down matrix
+// Workgroup (row tile, work item): output rows RT x .. of the down matrix
 // for the work item's pairs, from their per-row quantised h; routed rows to
 // expert_out of the slot, shared rows to shared_out of the token.
 template <bool DBG, int WB>
@@ -275,19 +286,19 @@ __global__ void __launch_bounds__(256) k_down_rows(FfnArgs a, const int4 *tiles,
   const size_t row_b = (size_t)I * code_bits<WB>() / 8;
   const size_t gate_b = (size_t)I * ((size_t)H * code_bits<WB>() / 8);  // one gate/up matrix
   const uint8_t *mats[1] = {ti.blob + 2 * gate_b};
-  float4 sd[2];
+  float4 sd[mr::RS];
 #pragma unroll
-  for (int rs = 0; rs < 2; rs++) {
+  for (int rs = 0; rs < mr::RS; rs++) {
     const uint4 u =
-        gload<uint4>(ti.blob, 3 * gate_b + 4 * ((size_t)2 * I + r0 + wv * 32 + rs * 16 + g * 4));
+        gload<uint4>(ti.blob, 3 * gate_b + 4 * ((size_t)2 * I + r0 + wv * mr::RW + rs * 16 + g * 4));
     sd[rs] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
                          __uint_as_float(u.w));
   }
-  v4i acc[1][2][4];
+  v4i acc[1][mr::RS][4];
   rkloop_n<1, WB>(mats, row_b, r0, q_h, pairl, I, ti.n, as, bs, acc);
 #pragma unroll
-  for (int rs = 0; rs < 2; rs++) {
-    const int row = r0 + wv * 32 + rs * 16 + g * 4;
+  for (int rs = 0; rs < mr::RS; rs++) {
+    const int row = r0 + wv * mr::RW + rs * 16 + g * 4;
 #pragma unroll
     for (int s = 0; s < 4; s++) {
       const int col = s * 16 + m16;
