@@ -202,6 +202,13 @@ void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *
 //     the experts in rank order;
 //  4. w_k = (s_k / S) * scale, S summed in rank order; with top-p, only the
 //     kept ranks, renormalised over their own sum.
+// running top-2 (a multiset: equal values fill both) of a sequence
+__device__ __forceinline__ void top2_add(float v, float &m1, float &m2) {
+  const float hi = fmaxf(m1, v), lo = fminf(m1, v);
+  m1 = hi;
+  m2 = fmaxf(m2, lo);
+}
+
 __global__ void __launch_bounds__(64) k_router_select(int E, int G, int TG, int K, float scale,
                                                       float top_p,
                                                       const float *__restrict__ s,
@@ -217,33 +224,39 @@ __global__ void __launch_bounds__(64) k_router_select(int E, int G, int TG, int 
   const int gs = E / G;
   const float *srow = s + (size_t)t * E;
   const float *sbrow = sb + (size_t)t * E;
-  // both rows in one round trip (a pick's unbiased score read from memory
-  // inside the selection loop put one round trip per pick in series)
-  for (int e = lane; e < E; e += 64) {
-    lsb[e] = sbrow[e];
-    ls[e] = srow[e];
+  // both rows, every load issued before any is stored (a pick's unbiased
+  // score read from memory inside the selection loop put one round trip per
+  // pick in series); indices past E read element 0 and are not stored
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    float vb[4], vs[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int e = e0 + 64 * u + lane;
+      vb[u] = sbrow[e < E ? e : 0];
+      vs[u] = srow[e < E ? e : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const int e = e0 + 64 * u + lane;
+      if (e < E) {
+        lsb[e] = vb[u];
+        ls[e] = vs[u];
+      }
+    }
   }
   __syncthreads();
-  if (lane < G) {  // the two largest of the group (a multiset), in index order
+  if (lane < G) {  // the two largest of the group (a multiset)
     float m1 = -INFINITY, m2 = -INFINITY;
-    auto take = [&](float v) {
-      if (v > m1) {
-        m2 = m1;
-        m1 = v;
-      } else if (v > m2) {
-        m2 = v;
-      }
-    };
     if ((gs & 3) == 0) {  // 16-byte LDS reads, four values per read
       for (int e = lane * gs; e < (lane + 1) * gs; e += 4) {
         const float4 v = *reinterpret_cast<const float4 *>(lsb + e);
-        take(v.x);
-        take(v.y);
-        take(v.z);
-        take(v.w);
+        top2_add(v.x, m1, m2);
+        top2_add(v.y, m1, m2);
+        top2_add(v.z, m1, m2);
+        top2_add(v.w, m1, m2);
       }
     } else {
-      for (int e = lane * gs; e < (lane + 1) * gs; e++) take(lsb[e]);
+      for (int e = lane * gs; e < (lane + 1) * gs; e++) top2_add(lsb[e], m1, m2);
     }
     gscore[lane] = m1 + m2;
   }
