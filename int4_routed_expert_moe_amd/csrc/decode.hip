@@ -21,4 +21,29 @@ void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev) {
   launch_small_batch_t<false>(a, st, ev);
 }
 
+// Group-limited top-k of token blockIdx.x by the whole workgroup (ranks in
+// LDS), the selection the small-batch path runs: the chained path's
+// selection at every batch size.
+__global__ void __launch_bounds__(256) k_select_tokens(LayerArgs a) {
+  __shared__ SelLds sm;
+  select_token(a, sm, blockIdx.x);
+}
+
+void launch_router_select(const moe_cfg &c, int T, const float *s, const float *sb,
+                          int32_t *idx, float *w, hipStream_t st, const moe_events *ev) {
+  LayerArgs a{};
+  a.E = c.n_experts;
+  a.G = c.n_group;
+  a.TG = c.topk_group;
+  a.K = c.top_k;
+  a.T = T;
+  a.scale = c.routed_scaling;
+  a.top_p = c.top_p;
+  a.s = const_cast<float *>(s);  // read only
+  a.sb = const_cast<float *>(sb);
+  a.idx = idx;
+  a.w = w;
+  launch_k(k_select_tokens, dim3(T), dim3(256), 0, st, stage_ev(ev, MOE_STAGE_ROUTER_SELECT), a);
+}
+
 }  // namespace moe

@@ -45,7 +45,8 @@ void launch_combine(int T, int H, int K, const float *eo, const float *w, const 
                     const moe_events *ev = nullptr);
 void launch_rmsnorm(int T, int H, const float *x, float *y, float eps, hipStream_t st);
 
-// Router: scores into s/sb [T][E] (workspace), then selection into idx/w.
+// Router: scores into s/sb [T][E] (workspace, route.hip), then selection
+// into idx/w (one workgroup per token, decode.hip).
 void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *wr,
                           const float *bias, float *s, float *sb, hipStream_t st,
                           const moe_events *ev = nullptr);

@@ -195,124 +195,7 @@ void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *
   }
 }
 
-// One wave per token.  Lane l holds experts l, l+64, ... (at most 16).
-//  1. group score = sum of the two largest sb of each group (lane g < G);
-//  2. TG rounds of a wave-wide max over (score, -group) keep the groups;
-//  3. K rounds of a wave-wide max over (sb, -expert) among kept groups pick
-//     the experts in rank order;
-//  4. w_k = (s_k / S) * scale, S summed in rank order; with top-p, only the
-//     kept ranks, renormalised over their own sum.
-// running top-2 (a multiset: equal values fill both) of a sequence
-__device__ __forceinline__ void top2_add(float v, float &m1, float &m2) {
-  const float hi = fmaxf(m1, v), lo = fminf(m1, v);
-  m1 = hi;
-  m2 = fmaxf(m2, lo);
-}
-
-__global__ void __launch_bounds__(64) k_router_select(int E, int G, int TG, int K, float scale,
-                                                      float top_p,
-                                                      const float *__restrict__ s,
-                                                      const float *__restrict__ sb,
-                                                      int32_t *__restrict__ idx,
-                                                      float *__restrict__ w) {
-  __shared__ __align__(16) float lsb[1024];  // the token's biased scores
-  __shared__ float ls[1024];                 // and its unbiased ones
-  __shared__ float gscore[64];
-  __shared__ float ssel[16];
-  __shared__ int isel[16];
-  const int t = blockIdx.x, lane = threadIdx.x;
-  const int gs = E / G;
-  const float *srow = s + (size_t)t * E;
-  const float *sbrow = sb + (size_t)t * E;
-  // both rows, every load issued before any is stored (a pick's unbiased
-  // score read from memory inside the selection loop put one round trip per
-  // pick in series); indices past E read element 0 and are not stored
-  for (int e0 = 0; e0 < E; e0 += 256) {
-    float vb[4], vs[4];
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int e = e0 + 64 * u + lane;
-      vb[u] = sbrow[e < E ? e : 0];
-      vs[u] = srow[e < E ? e : 0];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int e = e0 + 64 * u + lane;
-      if (e < E) {
-        lsb[e] = vb[u];
-        ls[e] = vs[u];
-      }
-    }
-  }
-  __syncthreads();
-  if (lane < G) {  // the two largest of the group (a multiset)
-    float m1 = -INFINITY, m2 = -INFINITY;
-    if ((gs & 3) == 0) {  // 16-byte LDS reads, four values per read
-      for (int e = lane * gs; e < (lane + 1) * gs; e += 4) {
-        const float4 v = *reinterpret_cast<const float4 *>(lsb + e);
-        top2_add(v.x, m1, m2);
-        top2_add(v.y, m1, m2);
-        top2_add(v.z, m1, m2);
-        top2_add(v.w, m1, m2);
-      }
-    } else {
-      for (int e = lane * gs; e < (lane + 1) * gs; e++) top2_add(lsb[e], m1, m2);
-    }
-    gscore[lane] = m1 + m2;
-  }
-  __syncthreads();
-  bool kept = false;  // lane g < G: is group g kept
-  for (int j = 0; j < TG; j++) {
-    unsigned long long key = 0;
-    if (lane < G && !kept)
-      key = ((unsigned long long)float_key(gscore[lane]) << 32) | (0xFFFFFFFFu - (uint32_t)lane);
-    key = wave_max_u64(key);
-    int g = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
-    g = (g >= 0 && g < G) ? g : 0;  // key 0 (no candidate) cannot occur for a valid cfg
-    if (lane == g) kept = true;
-  }
-  const unsigned long long kept_mask = __ballot(kept);
-  uint32_t taken = 0;  // bit j: expert lane + 64 j taken
-  for (int k = 0; k < K; k++) {
-    unsigned long long best = 0;
-    for (int j = 0; j * 64 + lane < E; j++) {
-      const int e = j * 64 + lane;
-      if (((kept_mask >> (e / gs)) & 1ull) && !((taken >> j) & 1u)) {
-        const unsigned long long key =
-            ((unsigned long long)float_key(lsb[e]) << 32) | (0xFFFFFFFFu - (uint32_t)e);
-        best = key > best ? key : best;
-      }
-    }
-    best = wave_max_u64(best);
-    int e = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-    e = (e >= 0 && e < E) ? e : 0;  // as above: K <= candidates is validated on the host
-    if ((e & 63) == lane) taken |= 1u << (e >> 6);
-    if (lane == 0) {
-      isel[k] = e;
-      ssel[k] = ls[e];
-    }
-  }
-  __syncthreads();
-  if (lane < K) {
-    float sv[16];
-#pragma unroll
-    for (int k = 0; k < 16; k++) sv[k] = k < K ? ssel[k] : 0.0f;
-    float S = sv[0];
-#pragma unroll
-    for (int k = 1; k < 16; k++) S = (k < K) ? S + sv[k] : S;
-    float Sk;
-    const int n = top_p_keep(sv, K, S, top_p, &Sk);  // n = K unless top-p cuts
-    const bool keep = lane < n;
-    idx[(size_t)t * K + lane] = keep ? isel[lane] : -1;
-    w[(size_t)t * K + lane] = keep ? (ssel[lane] / Sk) * scale : 0.0f;
-  }
-}
-
-void launch_router_select(const moe_cfg &c, int T, const float *s, const float *sb,
-                          int32_t *idx, float *w, hipStream_t st, const moe_events *ev) {
-  launch_k(k_router_select, dim3(T), dim3(64), 0, st, stage_ev(ev, MOE_STAGE_ROUTER_SELECT),
-           c.n_experts, c.n_group, c.topk_group, c.top_k, c.routed_scaling, c.top_p, s, sb, idx,
-           w);
-}
-
+// The selection (group-limited top-k, weights, top-p) is the small-batch
+// path's per-token selection, one workgroup per token (decode.hip,
+// launch_router_select).
 }  // namespace moe
