@@ -398,7 +398,8 @@ int moe_layer_noalloc(const moe_cfg *cfg, int32_t T, const float *x, const float
  * still reads the slot), and the new
  * entry is written on `stream` once the copy has landed (at a later call, or
  * within this call when wait != 0).  `stream` never waits for a copy; with
- * wait == 0 the host waits only when 32 read-backs are outstanding.
+ * wait == 0 the host waits only when 4 read-backs are outstanding (so that
+ * promotions are not queued behind many layer calls).
  *
  * moe_cache_prefetch — routing one layer ahead ("Comment exécuter un réseau
  * de neurones de 744 milliards de paramètres…", section "Comment fonctionne

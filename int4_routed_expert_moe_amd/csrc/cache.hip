@@ -48,6 +48,15 @@
 
 #include "kernels.h"
 
+// read-backs outstanding before moe_cache_step waits: promotions are decided
+// when a read-back lands and their copies queue behind the layer calls
+// already enqueued, so a host far ahead of the GPU promotes too late (a
+// 4-layer stack at 192 of 256 slots: 15 % hits with 32, 63 % with 4; 2 is
+// no better than 4, which still keeps several calls queued)
+#ifndef MOE_CACHE_RING
+#define MOE_CACHE_RING 4
+#endif
+
 namespace moe {
 
 // ------------------------------------------------------------------ policy
@@ -238,8 +247,8 @@ struct moe_cache {
   uint8_t *slots = nullptr;        // [S][blob_bytes] in HBM
   const void **table = nullptr;    // [E] device table of record pointers
   hipStream_t copy = nullptr;  // the device's copy stream (shared, not owned)
-  // idx read-back ring
-  static constexpr int R = 32;
+  // idx read-back ring: the host waits once R read-backs are outstanding
+  static constexpr int R = MOE_CACHE_RING;
   int32_t *ring = nullptr;  // pinned [R][max_pairs]
   hipEvent_t ring_ev[R] = {};
   int ring_n[R] = {};

@@ -37,15 +37,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    unsigned long long u = __shfl_xor(v, o, WAVE);
-    v = u > v ? u : v;
-  }
-  return v;
-}
-
 // --- the router's fixed-order sigmoid -------------------------------------
 // e^y in fp32 from basic operations only, so that every kernel and a CPU
 // following the same steps get the same bits: y clamped to [-87, 87];
