@@ -43,6 +43,9 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / int8 MFMA % (prefill)"
 HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
+# 32-bit vector lane operations per second: 256 CUs x 4 SIMDs x 16 lanes per
+# clock at 2.4 GHz (a wave64 VALU instruction issues over 4 clocks)
+VALU_LANE_OPS = 256 * 4 * 16 * 2.4e9
 HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction (host to GPU)
 
 WORKLOADS = {
@@ -657,9 +660,21 @@ def main():
         roof["frac_of_achievable"] = roof["achieved"] / pk
         if "down" in stage_ms:  # the down projection: half the operations of gate/up
             roof["down_frac"] = ops / 2 / (stage_ms["down"] * 1e-3) / 1e12 / INT8_PEAK_TOPS
-        # whole step against the larger of its HBM and matrix-core bounds
-        bound_s = max(step_bytes / (HBM_PEAK_GBPS * 1e9), 1.5 * ops / (INT8_PEAK_TOPS * 1e12))
-        roof["step_frac_of_bound"] = bound_s / (sec / K)
+        # Q8_0: every (pair, output row, 32-block) of gate, up and down takes a
+        # convert and a multiply-add after its block dot (the activation scale
+        # changes every 32 codes); with one scale per row there is no fix-up
+        n_pairs = pairs + T * shape.n_shared
+        fix = (0.0 if args.act == "row" else
+               n_pairs * 3 * shape.inter * shape.hidden / 32)
+        valu_s = 2.0 * fix / VALU_LANE_OPS
+        roof["valu_fixup"] = {"fixups": fix, "lane_ops": 2.0 * fix,
+                              "peak_lane_ops_per_s": VALU_LANE_OPS, "bound_us": valu_s * 1e6}
+        # whole step against the largest of its HBM, matrix-core and fix-up bounds
+        bounds = {"hbm": step_bytes / (HBM_PEAK_GBPS * 1e9),
+                  "mfma": 1.5 * ops / (INT8_PEAK_TOPS * 1e12), "valu_fixup": valu_s}
+        roof["step_bound"] = max(bounds, key=bounds.get)
+        roof["step_bounds_us"] = {k: v * 1e6 for k, v in bounds.items()}
+        roof["step_frac_of_bound"] = max(bounds.values()) / (sec / K)
 
     out = {
         "metric": METRIC,
