@@ -604,8 +604,9 @@ def main():
     pairs = float(np.mean([(idx_h[i] >= 0).sum() for i in range(W, W + K)])) / NL
     U = float(np.mean(U_l))
     step_bytes = sum(layer_bytes(shape, T, u, bb) for u in U_l)
-    fp8 = shape.wbits == synth.FP8  # chained path with vector kernels at every batch size
-    small = T <= 16 and not fp8  # the layer's small-batch path (four kernels)
+    fp8 = shape.wbits == synth.FP8  # otherwise vector kernels (no matrix-core path)
+    # the layer's small-batch path (four kernels) records no separate Q8_0 stage
+    small = T <= 16 and "quant" not in stage_ms
     dom_sec = stage_ms["gate_up"] * 1e-3
     cache_info = None
     if args.cache_slots:
@@ -634,7 +635,9 @@ def main():
                 "unit": "GB/s", "frac": cache_info["host_link_gbps"] / HOST_LINK_PEAK_GBPS,
                 "traffic": None}
     elif small or fp8:  # HBM-bound GEMV: algorithmic bytes of the gate/up launch
-        dom = ("gate_up (FP8 expert gate/up + SwiGLU, exact block dots)" if fp8 else
+        dom = ("gate_up (routed FP8 expert gate/up + SwiGLU + Q8_0 of h, exact block dots)"
+               if fp8 and small else
+               "gate_up (FP8 expert gate/up + SwiGLU, exact block dots)" if fp8 else
                "gate_up (routed expert gate/up + SwiGLU + Q8_0 of h)")
         dom_bytes = float(np.mean([gate_up_bytes(shape, T, u, small) for u in U_l]))
         roof = {"bound": "hbm", "kernel": dom, "achieved": dom_bytes / dom_sec / 1e9,

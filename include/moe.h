@@ -65,9 +65,10 @@
  *     [I/128][H/128] | up [I/128][H/128] | down [H/128][I/128]; a row r is
  *     sum_b S[r/128][b/4] d_b sum_k fp8(c_k) q_k over its 32-blocks b, and
  *     the int32 block dot reported for it is sum_k 512 fp8(c_k) q_k (exact:
- *     512 fp8 is an integer).  hidden and inter multiples of 128; every
- *     batch size runs the vector kernels (no matrix-core path), and
- *     moe_layer takes the chained kernels.
+ *     512 fp8 is an integer).  hidden and inter multiples of 128;
+ *     moe_expert_ffn runs vector kernels at every batch size (no
+ *     matrix-core path); moe_layer takes the small-batch kernels up to 4
+ *     tokens and the chained kernels above.
  *     int8: element j in byte j, codes in [-127, 127] (-128 is not
  *     produced by the quantiser but is accepted);
  *     int4: element 2j in the low nibble of byte j, 2j+1 in the high nibble;
@@ -308,8 +309,8 @@ typedef struct moe_layer_debug {
 /* ---------------------------------------------------------------------------
  * moe_layer — the whole step: routing, Q8_0 of x, grouping, expert FFNs and
  * combine on one stream, with all intermediates in the workspace.  For 1..16
- * tokens (with T*top_k <= 256) it runs as four kernels: router scores
- * (MOE_STAGE_ROUTER_SCORES); per-token selection beside the shared expert's
+ * tokens (FP8 experts: 1..4; with T*top_k <= 256) it runs as four kernels:
+ * router scores (MOE_STAGE_ROUTER_SCORES); per-token selection beside the shared expert's
  * gate/up (MOE_STAGE_ROUTER_SELECT); batch union and routed gate/up with the
  * Q8_0 of h (MOE_STAGE_GATE_UP); down with the combine (MOE_STAGE_DOWN);
  * then, when y_norm is given, the RMSNorm (MOE_STAGE_NORM).  Otherwise it

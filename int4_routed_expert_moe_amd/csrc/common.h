@@ -184,9 +184,38 @@ __device__ __forceinline__ uint4 gload_stream(const uint8_t *base, size_t off) {
 // supportés": native MXFP4 weights) -- FP4 E2M1 codes packed like int4, one
 // E8M0 scale byte per 32 codes of a row, no row scale.
 constexpr int WB_MX = 5;
+// WB_F8 = FP8 E4M3 codes, one byte per element, one fp32 scale per 128x128
+// block, no row scale ("Comment exécuter…", section "Modèles supportés":
+// fp4/fp8 weights; "Show HN…", converter item: 128x128 block scales).
+constexpr int WB_F8 = 9;
 template <int WB>
 __host__ __device__ constexpr int code_bits() {
-  return WB == WB_MX ? 4 : WB;
+  return WB == WB_MX ? 4 : WB == WB_F8 ? 8 : WB;
+}
+// Byte-wide codes: activation pieces of 16 codes (half a Q8_0 block).
+__host__ __device__ constexpr bool byte_codes(int WB) { return WB == 8 || WB == WB_F8; }
+
+typedef float f8v2 __attribute__((ext_vector_type(2)));
+
+// Marks a weight piece as changed (an empty asm, registers only), so the
+// compiler converts FP8 codes where they are used instead of hoisting every
+// converted value out of a token loop (16 live registers per piece).
+__device__ __forceinline__ void opaque_words(uint4 &v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+// acc + sum over the 4 bytes of w (FP8 E4M3 codes) and of x (int8) of
+// 512 fp8(c) q: gfx950's OCP E4M3 conversion scaled by 512 gives exact
+// integers of at most 18 bits, multiplied in 24-bit integer multiply-adds
+// (|512 fp8| <= 229376, so 16 such products stay below 2^31).
+__device__ __forceinline__ int dot_fp8_word(uint32_t w, uint32_t x, int acc) {
+  const f8v2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 512.0f, false);
+  const f8v2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 512.0f, true);
+  acc = __mul24((int)lo.x, (int)(int8_t)x) + acc;
+  acc = __mul24((int)lo.y, (int)(int8_t)(x >> 8)) + acc;
+  acc = __mul24((int)hi.x, (int)(int8_t)(x >> 16)) + acc;
+  acc = __mul24((int)hi.y, (int)(int8_t)(x >> 24)) + acc;
+  return acc;
 }
 
 // E8M0 scale byte -> 2^(s-127) as fp32 (s = 0 gives the subnormal 2^-127).

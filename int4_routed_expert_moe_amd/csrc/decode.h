@@ -428,6 +428,11 @@ struct Act<WB_MX> {
   QBlock q;
   float d;  // block scale / 2 (the MXFP4 dot returns 2 x the block dot)
 };
+template <>
+struct Act<WB_F8> {  // as int8: 16 activations (half a Q8_0 block)
+  int q[4];
+  float d;
+};
 
 // One 16-byte weight piece; for MXFP4 also its block's scale.
 template <int WB>
@@ -439,8 +444,14 @@ struct WP<WB_MX> {
   uint4 w;
   float s;
 };
+template <>
+struct WP<WB_F8> {
+  uint4 w;
+  float s;  // the 128x128 block's scale
+};
 
-// Piece p of a weight row (scl: the row's E8M0 bytes, MXFP4 only; with
+// Piece p of a weight row (scl: the row's E8M0 bytes for MXFP4, the fp32
+// scales of the row's 128-row block for FP8 (8 pieces per scale); with
 // SCALE false the scale is filled in later).
 template <int WB, bool SCALE = true>
 __device__ __forceinline__ WP<WB> load_wp(const uint8_t *row, const uint8_t *scl, int p,
@@ -448,6 +459,7 @@ __device__ __forceinline__ WP<WB> load_wp(const uint8_t *row, const uint8_t *scl
   WP<WB> r;
   r.w = ok ? gload<uint4>(row, (size_t)p * 16) : make_uint4(0, 0, 0, 0);
   if constexpr (WB == WB_MX) r.s = (SCALE && ok) ? e8m0_float(gload<uint8_t>(scl, p)) : 0.0f;
+  if constexpr (WB == WB_F8) r.s = (SCALE && ok) ? gload<float>(scl, 4 * (size_t)(p >> 3)) : 0.0f;
   return r;
 }
 
@@ -464,11 +476,17 @@ struct WRaw<WB_MX> {
   uint4 w;
   uint32_t sb;  // the block's E8M0 byte
 };
+template <>
+struct WRaw<WB_F8> {
+  uint4 w;
+  float s;
+};
 template <int WB, bool SCALE = true>
 __device__ __forceinline__ WRaw<WB> load_wraw(const uint8_t *row, const uint8_t *scl, int p) {
   WRaw<WB> r;
   r.w = gload_stream(row, (size_t)p * 16);
   if constexpr (WB == WB_MX) r.sb = SCALE ? gload<uint8_t>(scl, p) : 0u;
+  if constexpr (WB == WB_F8) r.s = SCALE ? gload<float>(scl, 4 * (size_t)(p >> 3)) : 0.0f;
   return r;
 }
 // The piece, or zeros when !ok.
@@ -477,6 +495,7 @@ __device__ __forceinline__ WP<WB> cook_wp(const WRaw<WB> &r, bool ok) {
   WP<WB> o;
   o.w = ok ? r.w : make_uint4(0, 0, 0, 0);
   if constexpr (WB == WB_MX) o.s = ok ? e8m0_float(r.sb) : 0.0f;
+  if constexpr (WB == WB_F8) o.s = ok ? r.s : 0.0f;
   return o;
 }
 
@@ -484,7 +503,7 @@ __device__ __forceinline__ WP<WB> cook_wp(const WRaw<WB> &r, bool ok) {
 // rearranged, so that a load can stay in flight until the piece is used.
 template <int WB>
 struct ActRaw {
-  uint4 x[WB == 8 ? 1 : WB == 2 ? 4 : 2];
+  uint4 x[byte_codes(WB) ? 1 : WB == 2 ? 4 : 2];
   float d0, d1;
 };
 
@@ -492,7 +511,7 @@ struct ActRaw {
 template <int WB>
 __device__ __forceinline__ ActRaw<WB> load_act_raw(const int8_t *q, const float *d, int p,
                                                    bool ok) {
-  constexpr int NX = WB == 8 ? 1 : WB == 2 ? 4 : 2;
+  constexpr int NX = byte_codes(WB) ? 1 : WB == 2 ? 4 : 2;
   ActRaw<WB> r;
 #pragma unroll
   for (int j = 0; j < NX; j++) r.x[j] = make_uint4(0, 0, 0, 0);
@@ -501,7 +520,7 @@ __device__ __forceinline__ ActRaw<WB> load_act_raw(const int8_t *q, const float 
     const uint4 *qp = reinterpret_cast<const uint4 *>(q + 16 * NX * p);
 #pragma unroll
     for (int j = 0; j < NX; j++) r.x[j] = qp[j];
-    if constexpr (WB == 8) {
+    if constexpr (byte_codes(WB)) {
       r.d0 = d[p >> 1];
     } else if constexpr (WB == 2) {
       r.d0 = d[2 * p];
@@ -519,6 +538,16 @@ __device__ __forceinline__ Act<WB> cook_act(const ActRaw<WB> &r);
 template <>
 __device__ __forceinline__ Act<8> cook_act<8>(const ActRaw<8> &r) {
   Act<8> o;
+  o.q[0] = (int)r.x[0].x;
+  o.q[1] = (int)r.x[0].y;
+  o.q[2] = (int)r.x[0].z;
+  o.q[3] = (int)r.x[0].w;
+  o.d = r.d0;
+  return o;
+}
+template <>
+__device__ __forceinline__ Act<WB_F8> cook_act<WB_F8>(const ActRaw<WB_F8> &r) {
+  Act<WB_F8> o;
   o.q[0] = (int)r.x[0].x;
   o.q[1] = (int)r.x[0].y;
   o.q[2] = (int)r.x[0].z;
@@ -589,7 +618,8 @@ __device__ __forceinline__ void load_act(const int8_t *q, const float *d, int p,
 // activations, as the lanes compute them: int4 gives 16 x the block dot (its
 // codes enter as 16 x code), int2 64 x the dots of its two 32-code blocks,
 // int8 the dot of half a block (16 codes), MXFP4 the block dot of the doubled
-// FP4 values.  Every float sum below is built from these.
+// FP4 values, FP8 the dot of half a block with the codes as 512 x value.
+// Every float sum below is built from these.
 template <int WB>
 struct PDots {
   int v[WB == 2 ? 2 : 1];
@@ -611,6 +641,15 @@ __device__ __forceinline__ PDots<8> piece_idot<8>(const WP<8> &p, const Act<8> &
   return PDots<8>{{acc}};
 }
 template <>
+__device__ __forceinline__ PDots<WB_F8> piece_idot<WB_F8>(const WP<WB_F8> &p,
+                                                          const Act<WB_F8> &a) {
+  int acc = dot_fp8_word(p.w.x, (uint32_t)a.q[0], 0);
+  acc = dot_fp8_word(p.w.y, (uint32_t)a.q[1], acc);
+  acc = dot_fp8_word(p.w.z, (uint32_t)a.q[2], acc);
+  acc = dot_fp8_word(p.w.w, (uint32_t)a.q[3], acc);
+  return PDots<WB_F8>{{acc}};
+}
+template <>
 __device__ __forceinline__ PDots<4> piece_idot<4>(const WP<4> &p, const Act<4> &a) {
   return PDots<4>{{dot_int4_block16(p.w, a.q)}};
 }
@@ -628,12 +667,12 @@ __device__ __forceinline__ PDots<2> piece_idot<2>(const WP<2> &p, const Act<2> &
   return PDots<2>{{x, y}};
 }
 
-// sum_b d_b * P_b of the piece from its integer dot(s); ws is the MXFP4
-// block scale (unused by the other formats).
+// sum_b d_b * P_b of the piece from its integer dot(s); ws is the MXFP4 or
+// FP8 block scale (unused by the other formats).
 template <int WB>
 __device__ __forceinline__ float pdots_value(const PDots<WB> &r, const Act<WB> &a, float ws) {
   if constexpr (WB == 2) return fmaf((float)r.v[0], a.da, (float)r.v[1] * a.db);
-  else if constexpr (WB == WB_MX) return (float)r.v[0] * (a.d * ws);
+  else if constexpr (WB == WB_MX || WB == WB_F8) return (float)r.v[0] * (a.d * ws);
   else return (float)r.v[0] * a.d;
 }
 
@@ -641,7 +680,7 @@ __device__ __forceinline__ float pdots_value(const PDots<WB> &r, const Act<WB> &
 template <int WB>
 __device__ __forceinline__ float piece_dot(const WP<WB> &p, const Act<WB> &a) {
   float ws = 1.0f;
-  if constexpr (WB == WB_MX) ws = p.s;
+  if constexpr (WB == WB_MX || WB == WB_F8) ws = p.s;
   return pdots_value<WB>(piece_idot<WB>(p, a), a, ws);
 }
 
@@ -690,8 +729,18 @@ __device__ __forceinline__ PDots<WB> ready_idot(const WReady<WB> &w, const Act<W
 template <int WB>
 __device__ __forceinline__ float ready_scale(const WReady<WB> &w) {
   if constexpr (WB == WB_MX) return w.s;
+  else if constexpr (WB == WB_F8) return w.p.s;
   else return 1.0f;
 }
+// At the top of a token loop over weights held in registers: FP8 codes are
+// marked changed, so that they are converted where each token uses them
+// rather than all at once before the loop (16 integers per piece: 256
+// registers, then spills).
+template <int WB>
+__device__ __forceinline__ void fresh_codes(uint4 &w) {
+  if constexpr (WB == WB_F8) opaque_words(w);
+}
+
 template <int WB>
 __device__ __forceinline__ float ready_dot(const WReady<WB> &w, const Act<WB> &a) {
   return pdots_value<WB>(ready_idot<WB>(w, a), a, ready_scale<WB>(w));
@@ -700,14 +749,14 @@ __device__ __forceinline__ float ready_dot(const WReady<WB> &w, const Act<WB> &a
 // Debug dumps (moe_layer_debug): the block dot(s) of piece p of a row (p
 // counted along the whole row) into dots [pair][R rows][nblk blocks], as
 // reported: int4 >> 4, int2 >> 6 (two blocks), MXFP4 as is, and for int8
-// the sum of the two half-block dots, which sit in adjacent lanes (pieces
-// 2b and 2b + 1; the even lane stores).  Every lane of the wave calls it
+// and FP8 the sum of the two half-block dots, which sit in adjacent lanes
+// (pieces 2b and 2b + 1; the even lane stores).  Every lane of the wave calls it
 // (the int8 exchange is a wave operation); ok masks the store.
 template <int WB>
 __device__ __forceinline__ void dump_pdots(int32_t *dots, const PDots<WB> &r, int pair, int row,
                                            int R, int nblk, int p, bool ok) {
   const size_t base = ((size_t)pair * R + row) * nblk;
-  if constexpr (WB == 8) {
+  if constexpr (byte_codes(WB)) {
     const int s = r.v[0] + __shfl_xor(r.v[0], 1);
     if (ok && (p & 1) == 0) dots[base + (p >> 1)] = s;
   } else if constexpr (WB == 2) {
@@ -748,6 +797,23 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 // once with 16-byte loads (one byte load per piece would double the load
 // instructions of the weight stream): msc[gate, up][32 rows][H/32 <= 256]
 constexpr int GU_MSC = 32 * 256;
+// FP8: the 32 rows lie in one 128-row block, whose H/128 <= 64 fp32 scales
+// of gate and of up are staged: msc as float [gate, up][F8_MSC]
+constexpr int F8_MSC = 64;
+template <int WB>
+constexpr int gu_msc_bytes() {
+  return WB == WB_MX ? 2 * GU_MSC : WB == WB_F8 ? 2 * F8_MSC * 4 : 16;
+}
+// Stage the FP8 scales of rows blk*32.. (every thread calls it).
+__device__ __forceinline__ void stage_f8_scales(uint8_t *msc, const uint8_t *tail, int H, int I,
+                                                int blk) {
+  float *fs = reinterpret_cast<float *>(msc);
+  const int nsb = H / 128;
+  const size_t gs = 4 * (size_t)((blk * 32) / 128) * nsb;
+  const size_t us = 4 * (size_t)(I / 128) * nsb + gs;
+  for (int i = threadIdx.x; i < 2 * nsb; i += 256)
+    fs[i < nsb ? i : F8_MSC + i - nsb] = gload<float>(tail, i < nsb ? gs + 4 * i : us + 4 * (i - nsb));
+}
 
 template <int WB, int TT, int NPL, int RB, int KS, bool DBG, class QRow, class DRow>
 __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], uint8_t *msc,
@@ -773,6 +839,7 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], uint8_t *msc,
   // row scales of the wave's rows: lane l < RW gate row l, RW <= l < 2 RW up row l - RW
   const float sc = lane >= 2 * RW ? 0.0f
                    : WB == WB_MX ? 1.0f
+                   : WB == WB_F8 ? 1.0f / 512.0f  // the codes enter as 512 x value
                                  : gload<float>(tail, 4 * (size_t)((lane < RW ? 0 : I) + rbase +
                                                                    lane % RW));
   constexpr int NB = RW / RB;
@@ -819,6 +886,12 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], uint8_t *msc,
         __syncthreads();
       }
     }
+    if constexpr (WB == WB_F8) {
+      if (c0 == 0) {
+        stage_f8_scales(msc, tail, H, I, blk);
+        __syncthreads();
+      }
+    }
     // lanes past the row: zero activations (their weight pieces, read from
     // the row's first piece, then add exact zeros)
     Act<WB> act[NPL][TT];
@@ -846,6 +919,12 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], uint8_t *msc,
             const int o = (wr * RW + rl) * nblk + lane + 64 * i;
             wg[i].s = ok ? e8m0_float(msc[o]) : 0.0f;
             wu[i].s = ok ? e8m0_float(msc[MSC + o]) : 0.0f;
+          }
+          if constexpr (WB == WB_F8) {  // 8 pieces per 128-column block
+            const int o = (ok ? p0 + lane + 64 * i : p0) >> 3;
+            const float *fs = reinterpret_cast<const float *>(msc);
+            wg[i].s = ok ? fs[o] : 0.0f;
+            wu[i].s = ok ? fs[F8_MSC + o] : 0.0f;
           }
         }
         float g[TT], u[TT];
@@ -926,7 +1005,7 @@ __device__ void gate_up_rows(const LayerArgs &a, float (*hb)[32], uint8_t *msc,
 template <int WB>
 struct ActWords {
   static constexpr int N = sizeof(Act<WB>) / 4;
-  static constexpr int NQ = WB == 8 ? 1 : WB == 2 ? 4 : 2;
+  static constexpr int NQ = byte_codes(WB) ? 1 : WB == 2 ? 4 : 2;
   static constexpr int NS = N - 4 * NQ;
 };
 
@@ -976,6 +1055,7 @@ __device__ void gate_up_rows_lds(const LayerArgs &a, uint8_t *msc, const uint8_t
   const int rbase = blk * 32 + wr * RW;
   const float sc = lane >= 2 * RW ? 0.0f
                    : WB == WB_MX ? 1.0f
+                   : WB == WB_F8 ? 1.0f / 512.0f  // the codes enter as 512 x value
                                  : gload<float>(tail, 4 * (size_t)((lane < RW ? 0 : I) + rbase +
                                                                    lane % RW));
   auto load_row = [&](WRaw<WB> (&dst)[2][NPL], int rl) {
@@ -996,6 +1076,7 @@ __device__ void gate_up_rows_lds(const LayerArgs &a, uint8_t *msc, const uint8_t
           gload<uint4>(m ? usc : gsc, (size_t)blk * 32 * nblk + o);
     }
   }
+  if constexpr (WB == WB_F8) stage_f8_scales(msc, tail, H, I, blk);  // read after a barrier below
   for (int g0 = 0; g0 < n_tok; g0 += SG) {
     const int ng = min(SG, n_tok - g0);
     WRaw<WB> wb[2][2][NPL];  // [buffer][gate, up][piece]
@@ -1044,12 +1125,25 @@ __device__ void gate_up_rows_lds(const LayerArgs &a, uint8_t *msc, const uint8_t
           wg.s = ok ? e8m0_float(msc[o]) : 0.0f;
           wu.s = ok ? e8m0_float(msc[MSC + o]) : 0.0f;
         }
+        if constexpr (WB == WB_F8) {
+          const int o = (ok ? p0 + lane + 64 * i : p0) >> 3;
+          const float *fs = reinterpret_cast<const float *>(msc);
+          wg.s = ok ? fs[o] : 0.0f;
+          wu.s = ok ? fs[F8_MSC + o] : 0.0f;
+        }
         rg[i] = ready<WB>(wg);
         ru[i] = ready<WB>(wu);
       }
       const float sg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), rl));
       const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), RW + rl));
       for (int c0 = 0; c0 < ng; c0 += TT) {
+        if constexpr (WB == WB_F8) {
+#pragma unroll
+          for (int i = 0; i < NPL; i++) {
+            fresh_codes<WB>(rg[i].p.w);
+            fresh_codes<WB>(ru[i].p.w);
+          }
+        }
         Act<WB> act[NPL][TT];
 #pragma unroll
         for (int t = 0; t < TT; t++) {
@@ -1155,7 +1249,14 @@ __device__ void shared_rows_block(const LayerArgs &a, int blk) {
   const uint8_t *up = a.shared + (size_t)I * row_b;
   const uint8_t *tail = a.shared + 3 * (size_t)I * row_b;
   const int nblk = H / 32;
-  const uint8_t *gsc = tail, *usc = tail + (size_t)I * nblk;  // MXFP4
+  // the scales the piece loads take for row r of gate (m = 0) or up: MXFP4
+  // the row's E8M0 bytes, FP8 its 128-row block's fp32 scales
+  auto scl = [&](int m, size_t r) -> const uint8_t * {
+    if constexpr (WB == WB_F8)
+      return tail + 4 * ((size_t)m * (I / 128) * (H / 128) + (r >> 7) * (H / 128));
+    else
+      return tail + ((size_t)m * I + r) * nblk;
+  };
   const int r0 = blk * 4 * SRW + wv * SRW;
   // Everything unconditional (lanes past the row read its first piece and
   // get zero activations), the first tokens' activations (cache hits) ahead
@@ -1182,18 +1283,26 @@ __device__ void shared_rows_block(const LayerArgs &a, int blk) {
       const int p = lane + 64 * i;
       const int pc = p < npieces ? p : 0;
       const size_t r = (size_t)(r0 + rr);
-      wb[rr][0][i] = load_wraw<WB>(gate + r * row_b, gsc + r * nblk, pc);
-      wb[rr][1][i] = load_wraw<WB>(up + r * row_b, usc + r * nblk, pc);
+      wb[rr][0][i] = load_wraw<WB>(gate + r * row_b, scl(0, r), pc);
+      wb[rr][1][i] = load_wraw<WB>(up + r * row_b, scl(1, r), pc);
     }
   }
-  const bool mx = WB == WB_MX;  // no row scales
+  // no row scales: MXFP4 1, FP8 1/512 (its codes enter as 512 x value)
+  constexpr bool blk_scaled = WB == WB_MX || WB == WB_F8;
+  constexpr float unit = WB == WB_F8 ? 1.0f / 512.0f : 1.0f;
   float sg[SRW], su[SRW];
 #pragma unroll
   for (int rr = 0; rr < SRW; rr++) {
-    sg[rr] = mx ? 1.0f : gload<float>(tail, 4 * (size_t)(r0 + rr));
-    su[rr] = mx ? 1.0f : gload<float>(tail, 4 * ((size_t)I + r0 + rr));
+    sg[rr] = blk_scaled ? unit : gload<float>(tail, 4 * (size_t)(r0 + rr));
+    su[rr] = blk_scaled ? unit : gload<float>(tail, 4 * ((size_t)I + r0 + rr));
   }
   for (int c0 = 0; c0 < T; c0 += TT) {
+#pragma unroll
+    for (int rr = 0; rr < SRW; rr++)
+#pragma unroll
+      for (int m = 0; m < 2; m++)
+#pragma unroll
+        for (int i = 0; i < NPL; i++) fresh_codes<WB>(wb[rr][m][i].w);
     if (c0 > 0) load_acts(araw, c0);
     Act<WB> act[NPL][TT];
 #pragma unroll
@@ -1373,7 +1482,7 @@ template <int WB, int TT, int NPL, bool DBG>
 __global__ void __launch_bounds__(256, WB == WB_MX && TT > 1 ? 2 : 1) k_gate_up_small(LayerArgs a) {
   __shared__ float hb[TT][32];
   __shared__ int ent[SLOT_W];
-  __shared__ __align__(16) uint8_t msc[WB == WB_MX ? 2 * GU_MSC : 16];
+  __shared__ __align__(16) uint8_t msc[gu_msc_bytes<WB>()];
   const int j = blockIdx.y, blk = blockIdx.x;
   if (j == 0 && a.n_shared && (int)threadIdx.x < a.T * 8) {
     // Q8_0 of the shared expert's h, block blk of every token
@@ -1409,14 +1518,14 @@ __global__ void __launch_bounds__(256, WB == WB_MX && TT > 1 ? 2 : 1) k_gate_up_
   if (n_tok == 0) return;
   const int *pairs = ent + 2, *toks = ent + 2 + sbk::TMAX;
   // int8 rows longer than 4 pieces per lane are split over two waves
-  constexpr int KS = WB == 8 && NPL > 4 ? 2 : 1;
+  constexpr int KS = byte_codes(WB) && NPL > 4 ? 2 : 1;
   auto qrow = [&](int i) {
     return (const int8_t *)(a.q + (size_t)min(max(toks[i], 0), a.T - 1) * a.H);
   };
   auto drow = [&](int i) {
     return (const float *)(a.d + (size_t)min(max(toks[i], 0), a.T - 1) * (a.H / 32));
   };
-  constexpr int NPLK = KS == 2 ? 4 : NPL;  // pieces per lane of a wave's share of a row
+  constexpr int NPLK = KS == 2 ? (NPL + 1) / 2 : NPL;  // pieces per lane of a wave's share of a row
   if constexpr (TT > 1 && MOE_GU_LDS) {
     if constexpr (gu_stage_tokens<WB, TT, NPLK, KS>() >= 2 * TT) {
       if (n_tok > TT) {  // several chunks: rows streamed once for all of them
@@ -1425,8 +1534,8 @@ __global__ void __launch_bounds__(256, WB == WB_MX && TT > 1 ? 2 : 1) k_gate_up_
       }
     }
   }
-  gate_up_rows<WB, TT, KS == 2 ? 4 : NPL,
-               (TT == 1 ? (WB == 2 ? 2 * MOE_K2_ROWS : WB == 8 || WB == WB_MX ? 1 : MOE_K2_ROWS) : 1),
+  gate_up_rows<WB, TT, NPLK,
+               (TT == 1 ? (WB == 2 ? 2 * MOE_K2_ROWS : byte_codes(WB) || WB == WB_MX ? 1 : MOE_K2_ROWS) : 1),
                KS, DBG>(
       a, hb, msc, rec, blk, n_tok, pairs, qrow, drow);
 }
@@ -1561,6 +1670,21 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
   const size_t tail_off = 3 * (size_t)I * ((size_t)H * CB / 8);  // scales after the codes
   const size_t dsc_off = tail_off + 2 * (size_t)I * (H / 32);    // MXFP4 down block scales
   const int nblk = I / 32;
+  // the scales the piece loads take for down row `row` of a record: MXFP4
+  // the row's E8M0 bytes, FP8 its 128-row block's fp32 scales; the row
+  // scale (MXFP4 none, FP8 1/512: its codes enter as 512 x value)
+  auto dscl = [&](const uint8_t *blob, int row) -> const uint8_t * {
+    if constexpr (WB == WB_F8)
+      return blob + tail_off +
+             4 * ((size_t)2 * (I / 128) * (H / 128) + (size_t)(row >> 7) * (I / 128));
+    else
+      return blob + dsc_off + (size_t)row * nblk;
+  };
+  auto drow_scale = [&](const uint8_t *blob, int row) -> float {
+    if constexpr (WB == WB_MX) return 1.0f;
+    else if constexpr (WB == WB_F8) return 1.0f / 512.0f;
+    else return gload<float>(blob, tail_off + 4 * ((size_t)2 * I + row));
+  };
   const int rl = lane / LPR, pl = lane % LPR;
   const int j0 = tile * sbk::RT;
   const DownDump ddump{DBG ? a.dbg.ffn.down_dots : nullptr, H, I / 32, j0, qb};
@@ -1599,10 +1723,10 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
 #pragma unroll
       for (int i = 0; i < NPQ; i++) {
         const int q = pl + LPR * i;
-        ws0[rr][i] = load_wraw<WB>(down + (size_t)row * row_b,
-                                   a.shared + dsc_off + (size_t)row * nblk, q < nq ? qb + q : qb);
+        ws0[rr][i] = load_wraw<WB>(down + (size_t)row * row_b, dscl(a.shared, row),
+                                   q < nq ? qb + q : qb);
       }
-      sd0[rr] = WB == WB_MX ? 1.0f : gload<float>(a.shared, tail_off + 4 * ((size_t)2 * I + row));
+      sd0[rr] = drow_scale(a.shared, row);
     }
     down_act<WB, TT, NPQ, LPR>(a, shp, T, 0, P, qb, nq, pl, act_s, pair_s);
   }
@@ -1643,11 +1767,10 @@ __global__ void __launch_bounds__(256) k_down_small(LayerArgs a) {
 #pragma unroll
         for (int i = 0; i < NPQ; i++) {
           const int q = pl + LPR * i;
-          bt.wd[b][rr][i] = load_wraw<WB>(down + (size_t)row * row_b,
-                                          blob + dsc_off + (size_t)row * nblk,
+          bt.wd[b][rr][i] = load_wraw<WB>(down + (size_t)row * row_b, dscl(blob, row),
                                           q < nq ? qb + q : qb);
         }
-        bt.sd[b][rr] = WB == WB_MX ? 1.0f : gload<float>(blob, tail_off + 4 * ((size_t)2 * I + row));
+        bt.sd[b][rr] = drow_scale(blob, row);
       }
       const int n_tok = s0 + b < n_slots ? min(tab[sl * TAB_W + 1], T) : 0;
       down_act<WB, TT, NPQ, LPR>(a, tab + sl * TAB_W + 2, n_tok, 0, P, qb, nq, pl, bt.act0[b],
@@ -1795,14 +1918,15 @@ void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
   const size_t lds3 = (size_t)4 * P * sbk::RT * sizeof(float) +
                       (((size_t)a.n_slots_ub * TAB_W * 4 + 7) & ~(size_t)7) +
                       (size_t)a.n_slots_ub * sizeof(void *);
-  constexpr int fbit = WB == 4 ? 1 : WB == 2 ? 2 : WB == 8 ? 4 : 8;
+  constexpr int fbit = WB == 4 ? 1 : WB == 2 ? 2 : byte_codes(WB) ? 4 : 8;
   constexpr bool PIPE = (MOE_K3_PIPE & fbit) != 0;
   constexpr int SB = !PIPE ? MOE_K3_SLOTS_NOPIPE
                     : TT == 1 && WB == 2 ? MOE_K3_SLOTS_INT2
                                          : MOE_K3_SLOTS;
   constexpr int TT3 = TT == 1 ? 1 : MOE_K3_TT;  // tokens per chunk in the down kernel
   const int quarter = (a.I / (128 / code_bits<WB>()) + 3) / 4;
-  if (WB != 2 && a.T >= MOE_DOWN_MFMA_MIN_T && a.H % 64 == 0 && a.I % 64 == 0) {
+  if (WB != 2 && WB != WB_F8 && a.T >= MOE_DOWN_MFMA_MIN_T && a.H % 64 == 0 &&
+      a.I % 64 == 0) {
     // many tokens per expert: the down projection as MFMA tiles of 64 rows
     // x the slot's tokens (activations staged once per 64 rows, not once
     // per 8), then the rank-order combine
@@ -1847,9 +1971,10 @@ template <int WB, int TT, bool DBG>
 void launch3_np(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
   const int per = 128 / code_bits<WB>();
   const int ng = (a.H / per + 63) / 64, nd = (a.I / per + 63) / 64;
-  if constexpr (WB == 8) {  // 16 codes per piece: up to 7 pieces per lane
+  if constexpr (byte_codes(WB)) {  // 16 codes per piece: up to 7 pieces per lane
     if (ng <= 2 && nd <= 1) launch3<WB, TT, 2, 1, DBG>(a, st, ev);
     else if (ng <= 4 && nd <= 2) launch3<WB, TT, 4, 2, DBG>(a, st, ev);
+    else if (ng <= 6 && nd <= 2) launch3<WB, TT, 6, 2, DBG>(a, st, ev);  // H = 6144: 3 per half
     else launch3<WB, TT, 7, 2, DBG>(a, st, ev);
   } else {
     if (ng <= 1 && nd <= 1) launch3<WB, TT, 1, 1, DBG>(a, st, ev);
@@ -1868,6 +1993,11 @@ void launch_small_batch_t(LayerArgs a, hipStream_t st, const moe_events *ev) {
   if (a.wfmt == 1) {  // MXFP4: int4 layout of the codes, a scale per piece
     if (a.T == 1) launch3_np<WB_MX, 1, DBG>(a, st, ev);
     else launch3_np<WB_MX, MOE_TT_MX, DBG>(a, st, ev);
+  } else if (a.wfmt == 2) {
+    // FP8: pieces as int8, one token per chunk at every batch size (a slot's
+    // further tokens are staged in LDS, rows still streamed once): two
+    // tokens' converted codes do not fit the registers of the long rows
+    launch3_np<WB_F8, 1, DBG>(a, st, ev);
   } else if (a.wbits == 8) {  // a piece carries 16 codes: two tokens per chunk
     if (a.T == 1) launch3_np<8, 1, DBG>(a, st, ev);
     else launch3_np<8, 2, DBG>(a, st, ev);

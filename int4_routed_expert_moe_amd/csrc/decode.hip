@@ -8,9 +8,20 @@ size_t small_batch_slot_ints(int T, int K, int n_shared) {
   return (size_t)(n_shared + T * K) * SLOT_W;
 }
 
+// largest FP8 batch on the small-batch kernels: they take one token per
+// chunk, so every token converts the codes again and larger batches turn
+// VALU-bound (measured at 4 tokens: 251 against 254 us per step on the vector
+// kernels; at 16: 886 against 791 us), where the vector kernels win
+#ifndef MOE_F8_SMALL_T_MAX
+#define MOE_F8_SMALL_T_MAX 4
+#endif
+
 bool small_batch_supported(const moe_cfg &c, int T) {
   if (T < 1 || T > MOE_SMALL_T_MAX) return false;
-  if (c.wfmt == 2) return false;  // FP8 experts take the chained path
+  // FP8: its 128x128 block scales of one 128-row block staged per gate/up
+  // workgroup (at most 64 of them per matrix)
+  if (c.wfmt == 2 && (c.hidden % 128 || c.inter % 128 || c.hidden / 128 > 64)) return false;
+  if (c.wfmt == 2 && T > MOE_F8_SMALL_T_MAX) return false;
   if (T * c.top_k > 256) return false;
   if (c.hidden / 64 > 128 || c.hidden % sbk::RT) return false;
   const int per = 128 / c.wbits;  // codes per 16-byte piece

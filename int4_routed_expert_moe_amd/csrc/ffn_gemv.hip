@@ -544,8 +544,6 @@ __global__ void __launch_bounds__(256) k_down_i2(FfnArgs a) {
 // float epilogue per block is acc += P9 * (d * S) with S the block's
 // 128x128 scale, and the row is scaled by 1/512 at the end.
 
-typedef float f8v2 __attribute__((ext_vector_type(2)));
-
 // P9 of one block: codes w0, w1 (32 bytes) against the block's activation
 // bytes x0, x1 (kept packed; each byte is sign-extended where it is used, so
 // a lane holds 8 activation words per block rather than 32).
@@ -555,23 +553,10 @@ __device__ __forceinline__ int dot_fp8_block(const uint4 w0, const uint4 w1, con
   const uint32_t x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
   int acc = 0;
 #pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const f8v2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 512.0f, false);
-    const f8v2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[j], 512.0f, true);
-    acc = __mul24((int)lo.x, (int)(int8_t)x[j]) + acc;
-    acc = __mul24((int)lo.y, (int)(int8_t)(x[j] >> 8)) + acc;
-    acc = __mul24((int)hi.x, (int)(int8_t)(x[j] >> 16)) + acc;
-    acc = __mul24((int)hi.y, (int)(int8_t)(x[j] >> 24)) + acc;
-  }
+  for (int j = 0; j < 8; j++) acc = dot_fp8_word(w[j], x[j], acc);
   return acc;
 }
 
-// Marks a weight piece as changed (an empty asm, registers only), so the
-// compiler converts the codes where they are used instead of hoisting every
-// converted value out of the token loop (192 live registers at NPL = 3).
-__device__ __forceinline__ void opaque(uint4 &v) {
-  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
-}
 
 // Gate/up: one gate/up row pair per wave, lane l takes blocks l + 64 i; the
 // weights stay in registers while the slot's tokens go through them.
@@ -606,10 +591,10 @@ __global__ void __launch_bounds__(256) k_gate_up_f8(FfnArgs a) {
     token_of(a, si, c, tok, pair);
 #pragma unroll
     for (int i = 0; i < NPL; i++) {
-      opaque(wg[i][0]);
-      opaque(wg[i][1]);
-      opaque(wu[i][0]);
-      opaque(wu[i][1]);
+      opaque_words(wg[i][0]);
+      opaque_words(wg[i][1]);
+      opaque_words(wu[i][0]);
+      opaque_words(wu[i][1]);
     }
     float gacc = 0.0f, uacc = 0.0f;
 #pragma unroll
@@ -683,8 +668,8 @@ __global__ void __launch_bounds__(256) k_down_f8(FfnArgs a) {
       for (int t = 0; t < TT; t++) acc[rr][t] = 0.0f;
 #pragma unroll
       for (int i = 0; i < NPL; i++) {
-        opaque(wd[rr][i][0]);
-        opaque(wd[rr][i][1]);
+        opaque_words(wd[rr][i][0]);
+        opaque_words(wd[rr][i][1]);
       }
     }
 #pragma unroll
