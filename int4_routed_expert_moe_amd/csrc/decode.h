@@ -4,7 +4,10 @@
 // Same method and arithmetic as the separate calls ("Show HN: 遅いコンピュータ
 // で GLM 5.2 を実行する", section 実装済みの主な機能: sigmoid router with
 // noaux_tc and routed_scaling_factor, shared expert, Q8_0 int8 activations,
-// packed int4/int2 weights with per-row scales, batch-union MoE).
+// packed int4/int2 weights with per-row scales, batch-union MoE), for every
+// weight format: int4, int2 and int8 codes with row scales, MXFP4, and FP8
+// E4M3 with 128x128 block scales (up to 4 tokens; "Comment exécuter…",
+// section "Modèles supportés").
 //
 //  K1  k_route_small   (E workgroups) Q8_0 of a slice of x; the fixed-order
 //                      fp32 logit and sigmoid score of one expert for every
