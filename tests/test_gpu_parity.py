@@ -472,6 +472,32 @@ def test_layer_int8_verify(dev, real8, T):
     _layer_check(real8, synth.tokens_perturbed(synth.REAL, synth.SEEDS["verify"], T), dev)
 
 
+# FP8 layers: the small-batch kernels up to 4 tokens, the chained vector
+# kernels above.
+
+def test_layer_tiny_fp8(dev):
+    lay = DeviceLayer(synth.TINY.with_bits(synth.FP8), synth.SEEDS["tiny"])
+    for T in (1, 2, 3, 4, 5, 9, 33):
+        _layer_check(lay, synth.tokens(synth.TINY, 76, T), dev)
+
+
+@pytest.mark.parametrize("T,start", [(1, 0), (1, 1), (1, 2), (3, 0), (4, 0), (16, 0)])
+def test_layer_fp8(dev, real_f8, T, start):
+    # perturbed pairs of tokens (even T) share most experts
+    x = synth.tokens(synth.REAL, synth.SEEDS["decode"], T, start=start) if T % 2 else \
+        synth.tokens_perturbed(synth.REAL, synth.SEEDS["verify"], T)
+    _layer_check(real_f8, x, dev)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_layer_fp8_residual_norm_top_p(dev, real_f8, T):
+    """The small-batch FP8 kernels with the residual, the RMSNorm kernel and
+    top-p 0.7 together."""
+    x = synth.tokens(synth.REAL, 12, T)
+    res = synth.tokens(synth.REAL, 13, T)
+    _layer_check(real_f8, x, dev, residual=res, want_norm=True, top_p=0.7)
+
+
 def test_layer_int8_residual_norm(dev, real8):
     x = synth.tokens(synth.REAL, 9, 2)
     res = synth.tokens(synth.REAL, 10, 2)
@@ -632,8 +658,15 @@ def test_layer_identical_tokens_int2(dev):
         _layer_check(lay, _same_tokens(synth.REAL, T), dev)
 
 
+@pytest.mark.parametrize("T", [2, 4, 16])
+def test_layer_identical_tokens_fp8(dev, real_f8, T):
+    """Every token on the same experts: at 2 and 4 tokens the small-batch
+    kernels' slots hold all of them (staged in LDS, rows streamed once)."""
+    _layer_check(real_f8, _same_tokens(synth.REAL, T), dev)
+
+
 def test_layer_identical_tokens_tiny(dev, tiny):
-    for bits in (4, 2, synth.MXFP4, 8):
+    for bits in (4, 2, synth.MXFP4, 8, synth.FP8):
         lay = tiny if bits == 4 else DeviceLayer(synth.TINY.with_bits(bits), synth.SEEDS["tiny"])
         for T in (3, 9, 16):
             _layer_check(lay, _same_tokens(synth.TINY, T), dev)
