@@ -170,8 +170,14 @@ __global__ void __launch_bounds__(256) k_router_gemm(int T, int H, int E,
   }
 }
 
+// tile (16 TM tokens x 16 TN experts): 2 x 2 gives 512 workgroups at 2048
+// tokens (two per CU); 2 x 4 (256 workgroups) took 197-201 us against 168,
+// and 1 x 4, 1 x 2 and 4 x 2 took 194-204 us
 #ifndef ROUTER_TM
 #define ROUTER_TM 2
+#endif
+#ifndef ROUTER_TN
+#define ROUTER_TN 2
 #endif
 
 void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *wr,
@@ -189,8 +195,9 @@ void launch_router_scores(const moe_cfg &c, int T, const float *x, const float *
     launch_k(k_router_scores<8>, dim3(E, (T + 7) / 8), dim3(64), 8 * lds, st, e0, T, H, E, x, wr,
              bias, s, sb);
   } else {
-    launch_k(k_router_gemm<ROUTER_TM, 4>, dim3((T + 16 * ROUTER_TM - 1) / (16 * ROUTER_TM),
-                                               (E + 63) / 64),
+    launch_k(k_router_gemm<ROUTER_TM, ROUTER_TN>,
+             dim3((T + 16 * ROUTER_TM - 1) / (16 * ROUTER_TM),
+                  (E + 16 * ROUTER_TN - 1) / (16 * ROUTER_TN)),
              dim3(256), 0, st, e0, T, H, E, x, wr, bias, s, sb);
   }
 }
