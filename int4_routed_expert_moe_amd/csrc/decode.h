@@ -1997,7 +1997,7 @@ void launch_small_batch_t(LayerArgs a, hipStream_t st, const moe_events *ev) {
     if (a.T == 1) launch3_np<WB_MX, 1, DBG>(a, st, ev);
     else launch3_np<WB_MX, MOE_TT_MX, DBG>(a, st, ev);
   } else if (a.wfmt == 2) {
-    // FP8: pieces as int8, one token per chunk at every batch size (a slot's
+    // FP8 (1..4 tokens): pieces as int8, one token per chunk (a slot's
     // further tokens are staged in LDS, rows still streamed once): two
     // tokens' converted codes do not fit the registers of the long rows
     launch3_np<WB_F8, 1, DBG>(a, st, ev);
