@@ -161,6 +161,22 @@ def gate_up_bytes(shape, T, U, small):
     return (U + S) * per_expert + x_in + (T * K + T * S) * I * 4
 
 
+def gate_up_bounds(shape, T, U, pairs, act_row):
+    """The prefill gate/up launch at each peak, in seconds: its int8 operations
+    (2 per multiply-accumulate) at the MFMA peak, its algorithmic bytes at the
+    HBM peak, and for Q8_0 activations its fix-ups (a convert and a
+    multiply-add per pair, gate or up row and 32-block) at the VALU rate.
+    pairs: routed (token, expert) pairs; the shared expert adds T.  Returns
+    (bounds, ops, bytes, fixups)."""
+    n_pairs = pairs + T * shape.n_shared
+    ops = 2.0 * n_pairs * 2 * shape.inter * shape.hidden
+    nbytes = gate_up_bytes(shape, T, U, False)
+    fix = 0.0 if act_row else n_pairs * 2 * shape.inter * shape.hidden / 32
+    bounds = {"mfma": ops / (INT8_PEAK_TOPS * 1e12), "hbm": nbytes / (HBM_PEAK_GBPS * 1e9),
+              "alu": 2.0 * fix / VALU_LANE_OPS}
+    return bounds, ops, nbytes, fix
+
+
 # the sources of the small-batch kernels whose counters profiles/ records
 TRAFFIC_SOURCES = ("decode.h", "decode.hip", "common.h", "kernels.h")
 
@@ -650,16 +666,9 @@ def main():
     else:  # grouped GEMMs: the gate/up launch against its matrix-core, HBM and fix-up bounds
         fmt = "per-row activation scales" if args.act == "row" else "Q8_0 activations"
         dom = f"gate_up (grouped {shape.label} x int8 MFMA GEMM, {fmt}, + SwiGLU)"
-        ops = 2.0 * (pairs + T * shape.n_shared) * 2 * shape.inter * shape.hidden
-        mfma_tops = ops / dom_sec / 1e12
         # algorithmic bytes: every used expert's gate and up once, activations in, h out
-        gu_bytes = float(np.mean([gate_up_bytes(shape, T, u, False) for u in U_l]))
-        # Q8_0: a convert and a multiply-add per (pair, row, 32-block) of gate and up
-        gu_fix = (0.0 if args.act == "row" else
-                  (pairs + T * shape.n_shared) * 2 * shape.inter * shape.hidden / 32)
-        gu_bounds = {"mfma": ops / (INT8_PEAK_TOPS * 1e12),
-                     "hbm": gu_bytes / (HBM_PEAK_GBPS * 1e9),
-                     "alu": 2.0 * gu_fix / VALU_LANE_OPS}
+        gu_bounds, ops, gu_bytes, gu_fix = gate_up_bounds(shape, T, U, pairs, args.act == "row")
+        mfma_tops = ops / dom_sec / 1e12
         bound = max(gu_bounds, key=gu_bounds.get)
         if bound == "mfma":
             roof = {"bound": "mfma", "kernel": dom, "achieved": mfma_tops,

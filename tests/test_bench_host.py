@@ -1,5 +1,5 @@
-"""Host-side checks of bench.py (no GPU): the one-GPU guard and the lookup of
-the committed HBM-traffic counters."""
+"""Host-side checks of bench.py (no GPU): the one-GPU guard, the lookup of
+the committed HBM-traffic counters, and the bounds a prefill line reports."""
 import hashlib
 import importlib.util
 import json
@@ -43,3 +43,31 @@ def test_traffic_lookup_follows_the_source_hash():
         assert 100.8e6 <= got <= 1.01 * 100.83e6
     else:
         assert got is None  # stale counters are never reported
+
+
+def test_prefill_gate_up_bounds():
+    """The 2048-token layer: with Zipf routing nearly every expert is used and
+    the weights (one read of each used expert's gate and up) outweigh the
+    matrix-core work; on 8 experts the MFMA bound rules; Q8_0 activations add
+    one convert and one multiply-add per (pair, gate or up row, 32-block)."""
+    bench = _bench()
+    sys.path.insert(0, ROOT)
+    import synth
+    s = synth.REAL
+    T, pairs = 2048, 2048 * s.top_k
+    n_pairs = pairs + T * s.n_shared  # 18,432 with the shared expert
+    # Zipf: 256 experts used
+    b, ops, nbytes, fix = bench.gate_up_bounds(s, T, 256, pairs, True)
+    assert ops == 2 * n_pairs * 2 * 2048 * 6144 and fix == 0
+    per_expert = 2 * 2048 * 6144 // 2 + 2 * 2048 * 4  # codes + row scales of gate and up
+    assert nbytes >= (256 + 1) * per_expert
+    assert max(b, key=b.get) == "hbm"
+    assert abs(b["mfma"] - ops / 5e15) < 1e-12
+    # dense: the same pairs on 8 experts
+    b, _, nbytes, _ = bench.gate_up_bounds(s, T, 8, pairs, True)
+    assert max(b, key=b.get) == "mfma" and b["hbm"] < b["mfma"] / 4
+    # Q8_0: 2 rows (gate, up) x 2048 x 192 blocks per pair
+    b, _, _, fix = bench.gate_up_bounds(s, T, 8, pairs, False)
+    assert fix == n_pairs * 2 * 2048 * (6144 // 32)
+    assert max(b, key=b.get) == "alu"
+    assert abs(b["alu"] - 2 * fix / (256 * 4 * 16 * 2.4e9)) < 1e-12
