@@ -411,12 +411,13 @@ def test_layer_workspace_contents_do_not_matter(dev, T):
 
 # ------------------------------------------------------------------ records through pointers
 
-@pytest.mark.parametrize("T", [1, 8, 24])
-def test_layer_ptrs_host_records_against_oracle(dev, T):
+@pytest.mark.parametrize("fmt,T", [("int4", 1), ("int4", 8), ("int4", 24), ("fp8", 1),
+                                   ("fp8", 4)])
+def test_layer_ptrs_host_records_against_oracle(dev, fmt, T):
     """moe_layer_ptrs with the selected experts' records in pinned host memory
     (read over the host link) and the rest in HBM, against the oracle, with
     every dump."""
-    lay = real_layer("int4")
+    lay = real_layer(fmt)
     s = lay.shape
     bb = lay.blob_bytes
     x = batch(s, T, 700 + T)

@@ -59,6 +59,14 @@ def test_noalloc_matches_layer_twice(dev, real, Ts):
         _both(real, x, dev, norm=(i == 1))
 
 
+def test_noalloc_fp8_small_batches(dev):
+    """FP8 experts on the small-batch kernels: 4 tokens, then 1."""
+    lay = DeviceLayer(synth.REAL.with_bits(synth.FP8), synth.SEEDS["decode"])
+    _both(lay, synth.tokens_perturbed(synth.REAL, 804, 4), dev, norm=True)
+    _both(lay, synth.tokens(synth.REAL, 801, 1, start=3), dev, norm=False)
+    del lay
+
+
 def test_noalloc_tiny_ragged(dev):
     lay = DeviceLayer(synth.TINY, synth.SEEDS["tiny"])
     for T in (33, 5, 1):
