@@ -306,6 +306,30 @@ def measured_mfma_peak(torch, moe, dev, n_wg=1024, iters=4000):
     return ops / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
+def measured_read_peak(torch, moe, hip, dev, bufs, nbytes, grids=(2048, 8192, 16384), reps=16):
+    """GB/s of moe_read_peak reading nbytes from each of bufs in turn (the
+    layer instances' expert records: not in the last-level cache, like the
+    step's weights), timed by the kernel's own dispatch as the stages are:
+    for each grid size the mean over reps launches after one pass over bufs,
+    and the best of the grid sizes (no single one is best at every size)."""
+    nbytes = nbytes // 16 * 16
+    out = torch.empty(max(grids) * 4, dtype=torch.int32, device=dev)
+    best = 0.0
+    for n_wg in grids:
+        for b in bufs:
+            moe.read_peak(b, nbytes, n_wg, out)
+        evs = [(hip.event(), hip.event()) for _ in range(reps)]
+        for k, (a, z) in enumerate(evs):
+            moe.read_peak(bufs[k % len(bufs)], nbytes, n_wg, out, a, z)
+        torch.cuda.synchronize()
+        ms = [hip.elapsed_ms(a, z) for a, z in evs]
+        for a, z in evs:
+            hip.destroy(a)
+            hip.destroy(z)
+        best = max(best, nbytes / (float(np.mean(ms)) * 1e-3) / 1e9)
+    return best
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -663,6 +687,11 @@ def main():
         roof["traffic"] = (measured_traffic(args.workload)
                            if args.wbits == "4" and not args.topp else None)
         roof.update(bytes_per_launch=dom_bytes, launch_us=dom_sec * 1e6)
+        # the same byte count read plainly (moe_read_peak): the HBM rate this
+        # chip reaches for a read of that size
+        pk = measured_read_peak(torch, moe, hip, dev, [r["ex"] for r in ring], int(dom_bytes))
+        roof["achievable_peak"] = pk
+        roof["frac_of_achievable"] = roof["achieved"] / pk
     else:  # grouped GEMMs: the gate/up launch against its matrix-core, HBM and fix-up bounds
         fmt = "per-row activation scales" if args.act == "row" else "Q8_0 activations"
         dom = f"gate_up (grouped {shape.label} x int8 MFMA GEMM, {fmt}, + SwiGLU)"

@@ -481,6 +481,23 @@ int moe_cache_simulate(int32_t n_experts, int32_t n_slots, int32_t n_pinned, int
  */
 int moe_mfma_peak(int32_t n_wg, int32_t iters, int32_t *out, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * moe_read_peak — measurement helper, not part of the layer: n_wg
+ * workgroups of 256 threads read buf [bytes] (device, 16-byte aligned,
+ * bytes a positive multiple of 16) once, 16 bytes per load with the expert
+ * kernels' non-temporal loads, four in flight per thread, grid-stride, so
+ * that bytes divided by the launch's time is the HBM read rate the chip
+ * reaches for that many bytes.  out [n_wg * 4] uint32 (device,
+ * caller-owned) receives the XOR of every 32-bit word each wave read (their
+ * XOR over all of out is the XOR of the whole buffer).  ev_start / ev_stop:
+ * optional hipEvent_t handles (NULL: none) stamped by the kernel's own
+ * dispatch, as moe_events are for the layer's stages.  Errors: MOE_EINVAL
+ * for bytes not a positive multiple of 16, n_wg outside [1, 2^20], or a
+ * NULL buf or out; MOE_EALIGN for a buf or out not 16-byte aligned.
+ */
+int moe_read_peak(const void *buf, int64_t bytes, int32_t n_wg, uint32_t *out, void *ev_start,
+                  void *ev_stop, void *stream);
+
 /* Name of a return code, and the calling thread's last detailed message. */
 const char *moe_strerror(int code);
 const char *moe_last_error(void);

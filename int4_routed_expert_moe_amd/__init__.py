@@ -27,7 +27,7 @@ EXPORTS = (
     "moe_host_device_ptr", "moe_cache_create", "moe_cache_step", "moe_cache_get_stats",
     "moe_cache_prefetch", "moe_cache_publish", "moe_cache_usage", "moe_cache_slot_of", "moe_cache_destroy",
     "moe_cache_simulate",
-    "moe_mfma_peak", "moe_strerror", "moe_last_error",
+    "moe_mfma_peak", "moe_read_peak", "moe_strerror", "moe_last_error",
 )
 
 
@@ -119,6 +119,8 @@ def lib():
     L.moe_rmsnorm.restype = ctypes.c_int
     L.moe_mfma_peak.argtypes = [i32, i32, v, v]
     L.moe_mfma_peak.restype = ctypes.c_int
+    L.moe_read_peak.argtypes = [v, ctypes.c_int64, i32, v, v, v, v]
+    L.moe_read_peak.restype = ctypes.c_int
     L.moe_layer_workspace.argtypes = [pc, i32]
     L.moe_layer_workspace.restype = sz
     L.moe_layer.argtypes = [pc, i32, v, v, v, v, v, v, v, v, f32, v, v, v, sz,
@@ -376,6 +378,19 @@ def mfma_peak(n_wg, iters, out):
     Returns the int8 operations launched (n_wg * 4 * iters * 8 * 32768)."""
     _check(lib().moe_mfma_peak(n_wg, iters, _ptr(out), _stream()))
     return n_wg * 4 * iters * 8 * 32768
+
+
+def read_peak(buf, nbytes, n_wg, out, ev_start=None, ev_stop=None):
+    """moe_read_peak: a plain streaming read of the first nbytes of the device
+    tensor buf; out uint32 (int32 tensor) [n_wg * 4] on the device receives
+    one XOR checksum per wave; ev_start / ev_stop: optional hipEvent_t
+    handles stamped by the kernel's dispatch."""
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    if out.numel() < 4 * n_wg:
+        raise ValueError("out needs n_wg * 4 words")
+    _check(lib().moe_read_peak(_ptr(buf), nbytes, n_wg, _ptr(out), ev_start, ev_stop,
+                               _stream()))
 
 
 def layer(cfg: Config, x, w_router, bias, experts, shared=None, residual=None, y=None,

@@ -134,6 +134,11 @@ size_t small_batch_slot_ints(int T, int K, int n_shared);
 // Matrix cores alone (peak.hip): n_wg workgroups of 4 waves, each wave
 // iters x 8 int8 MFMAs (16x16x64); out [n_wg * 256] takes a checksum.
 void launch_mfma_peak(int n_wg, int iters, int32_t *out, hipStream_t st);
+// A plain streaming read of bytes (a multiple of 16) for the HBM read rate
+// (peak.hip); one checksum word per wave into out [n_wg * 4]; ev: optional
+// timestamps of the kernel's own dispatch.
+void launch_read_peak(const void *buf, int64_t bytes, int n_wg, uint32_t *out, hipStream_t st,
+                      Ev ev);
 
 bool small_batch_supported(const moe_cfg &c, int T);
 void launch_small_batch(LayerArgs a, hipStream_t st, const moe_events *ev);

@@ -422,6 +422,21 @@ int moe_mfma_peak(int32_t n_wg, int32_t iters, int32_t *out, void *stream) {
   return launched("moe_mfma_peak");
 }
 
+int moe_read_peak(const void *buf, int64_t bytes, int32_t n_wg, uint32_t *out, void *ev_start,
+                  void *ev_stop, void *stream) {
+  clear_hip_error();  // MOE_EHIP then names this call's own launches
+  if (bytes <= 0 || bytes % 16)
+    return fail(MOE_EINVAL, "bytes=%lld must be a positive multiple of 16", (long long)bytes);
+  if (n_wg <= 0 || n_wg > (1 << 20)) return fail(MOE_EINVAL, "n_wg=%d not in [1, 2^20]", n_wg);
+  REQUIRE(buf, "buf");
+  REQUIRE(out, "out");
+  moe::Ev ev;
+  ev.start = (hipEvent_t)ev_start;
+  ev.stop = (hipEvent_t)ev_stop;
+  moe::launch_read_peak(buf, bytes, n_wg, out, (hipStream_t)stream, ev);
+  return launched("moe_read_peak");
+}
+
 int moe_rmsnorm(int32_t T, int32_t H, const float *x, float *y, float eps, void *stream) {
   clear_hip_error();  // MOE_EHIP then names this call's own launches
   if (T < 0) return fail(MOE_EINVAL, "T=%d < 0", T);

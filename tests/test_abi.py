@@ -160,6 +160,14 @@ def test_combine_and_layer_errors(L):
     assert L.moe_mfma_peak(4, 0, A, None) == moe.MOE_EINVAL
     assert L.moe_mfma_peak(4, 1 << 21, A, None) == moe.MOE_EINVAL
     assert L.moe_mfma_peak(4, 10, None, None) == moe.MOE_EINVAL
+    rp = L.moe_read_peak
+    assert rp(A, 0, 4, A, None, None, None) == moe.MOE_EINVAL
+    assert rp(A, 17, 4, A, None, None, None) == moe.MOE_EINVAL
+    assert rp(A, 256, 0, A, None, None, None) == moe.MOE_EINVAL
+    assert rp(A, 256, 1 << 21, A, None, None, None) == moe.MOE_EINVAL
+    assert rp(None, 256, 4, A, None, None, None) == moe.MOE_EINVAL
+    assert rp(A, 256, 4, None, None, None, None) == moe.MOE_EINVAL
+    assert rp(A + 4, 256, 4, A, None, None, None) == moe.MOE_EALIGN
     c = REAL.c()
     ws = moe.layer_workspace(REAL, 1)
     lay = L.moe_layer

@@ -1,7 +1,10 @@
-"""moe_mfma_peak (the matrix-core-only loop bench.py reports beside the
-published int8 peak) does the work it is counted for: every thread's
-checksum equals the CPU's value of 8 chains x iters int8 16x16x64 products
-of the kernel's operands, i.e. no MFMA was elided or misread."""
+"""The measurement loops do the work they are counted for: moe_mfma_peak
+(the matrix-core-only loop bench.py reports beside the published int8
+peak) -- every thread's checksum equals the CPU's value of 8 chains x iters
+int8 16x16x64 products of the kernel's operands, i.e. no MFMA was elided or
+misread; moe_read_peak (the plain streaming read reported beside the HBM
+peak) -- the XOR of its per-wave checksums is the XOR of every word of the
+buffer, for sizes that end inside the unrolled loop and in its tail."""
 import numpy as np
 import pytest
 import torch
@@ -43,6 +46,21 @@ def test_mfma_peak_checksums():
     want = expected_checksums(iters)
     for w in range(n_wg):
         assert np.array_equal(got[w], want), w
+
+
+@pytest.mark.parametrize("nbytes,n_wg", [(16, 1), (16 * 1000, 3), (1 << 20, 7), (96 << 20, 2048)])
+def test_read_peak_reads_every_word(nbytes, n_wg):
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(nbytes + n_wg)
+    host = torch.randint(-2**31, 2**31 - 1, (nbytes // 4 + 8,), generator=g, dtype=torch.int32)
+    buf = host.to(dev)  # 8 words past nbytes that must not be read
+    out = torch.full((n_wg * 4,), 0x5A5A5A5A, dtype=torch.int32, device=dev)
+    moe.read_peak(buf, nbytes, n_wg, out)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(host.numpy()[:nbytes // 4].view(np.uint32))
+    assert got == want
 
 
 def test_stale_hip_error_is_not_reported():
