@@ -139,6 +139,16 @@ def layer_bytes(shape, T, U, bb):
     return E * H * 4 + E * 4 + (U + shape.n_shared) * bb + 2 * T * H * 4
 
 
+def gate_up_record_bytes(shape):
+    """Bytes of an expert record's gate and up parts (codes and their scales)."""
+    H, I = shape.hidden, shape.inter
+    if shape.wbits == -4:  # MXFP4: 4-bit codes and one scale byte per 32
+        return 2 * I * H // 2 + 2 * I * H // 32
+    if shape.wbits == -8:  # FP8: byte codes and one fp32 scale per 128x128 block
+        return 2 * I * H + 2 * (I // 128) * (H // 128) * 4
+    return 2 * I * H * shape.wbits // 8 + 2 * I * 4
+
+
 def gate_up_bytes(shape, T, U, small):
     """Algorithmic bytes of one gate/up launch.
 
@@ -148,12 +158,7 @@ def gate_up_bytes(shape, T, U, small):
     selection).  Larger batches: the same for U + shared experts with fp32 h
     out."""
     H, I, K, S = shape.hidden, shape.inter, shape.top_k, shape.n_shared
-    if shape.wbits == -4:  # MXFP4: 4-bit codes and one scale byte per 32
-        per_expert = 2 * I * H // 2 + 2 * I * H // 32
-    elif shape.wbits == -8:  # FP8: byte codes and one fp32 scale per 128x128 block
-        per_expert = 2 * I * H + 2 * (I // 128) * (H // 128) * 4
-    else:
-        per_expert = 2 * I * H * shape.wbits // 8 + 2 * I * 4
+    per_expert = gate_up_record_bytes(shape)
     q8 = 1 + 4 / 32  # bytes per element of a Q8_0 vector (codes + fp32 block scales)
     x_in = T * H * q8
     if small:
@@ -327,6 +332,48 @@ def measured_read_peak(torch, moe, hip, dev, bufs, nbytes, grids=(2048, 8192, 16
             hip.destroy(a)
             hip.destroy(z)
         best = max(best, nbytes / (float(np.mean(ms)) * 1e-3) / 1e9)
+    return best
+
+
+def small_phase_bytes(shape, U, bb):
+    """Weight bytes each dependent launch of the small-batch step streams: the
+    router matrix, the shared expert's gate/up (beside the selection), the U
+    routed experts' gate/up, and the down rows of the U routed and the shared
+    experts."""
+    E, H, S = shape.n_experts, shape.hidden, shape.n_shared
+    gu = gate_up_record_bytes(shape)
+    down = bb - gu  # the record's down codes and scales
+    return [E * H * 4, S * gu, U * gu, (U + S) * down]
+
+
+def measured_step_floor(torch, moe, stream, dev, bufs, phase_bytes, n_steps=64, reps=8,
+                        grids=(2048, 8192)):
+    """Microseconds per step of plain streaming reads (moe_read_peak), one
+    dependent launch per phase of the step reading that phase's bytes, step i
+    from layer instance i mod len(bufs) (phases at disjoint offsets), replayed
+    from a HIP graph like the timed steps: the time any design pays whose
+    phases are separate launches streaming those bytes at the plain-read rate
+    (best of the grid sizes)."""
+    out = torch.empty(max(grids) * 4, dtype=torch.int32, device=dev)
+    offs = np.concatenate([[0], np.cumsum([(b + 255) // 256 * 256 for b in phase_bytes])])
+    best = None
+    for n_wg in grids:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n_steps):
+                buf = bufs[i % len(bufs)]
+                for p, nb in enumerate(phase_bytes):
+                    if nb >= 16:
+                        moe.read_peak(buf[int(offs[p]):], int(nb) // 16 * 16, n_wg, out)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) / (reps * n_steps) * 1e6
+        best = us if best is None else min(best, us)
+        del g
     return best
 
 
@@ -649,6 +696,7 @@ def main():
     small = T <= 16 and "quant" not in stage_ms
     dom_sec = stage_ms["gate_up"] * 1e-3
     cache_info = None
+    step_floor = None
     if args.cache_slots:
         d = {k: sum(c1[k] - c0[k] for c0, c1 in zip(cache0, cache1))
              for k in ("steps", "routed", "hits", "misses", "promotions", "bytes_copied",
@@ -692,6 +740,13 @@ def main():
         pk = measured_read_peak(torch, moe, hip, dev, [r["ex"] for r in ring], int(dom_bytes))
         roof["achievable_peak"] = pk
         roof["frac_of_achievable"] = roof["achieved"] / pk
+        if small and NL == 1 and not fp8:
+            # the step's dependent launches as plain reads of their bytes
+            phases = small_phase_bytes(shape, U, bb)
+            floor_us = measured_step_floor(torch, moe, stream, dev, [r["ex"] for r in ring],
+                                           phases)
+            step_floor = {"phase_bytes": phases, "floor_us": floor_us,
+                          "step_us": sec / K * 1e6, "frac": floor_us / (sec / K * 1e6)}
     else:  # grouped GEMMs: the gate/up launch against its matrix-core, HBM and fix-up bounds
         fmt = "per-row activation scales" if args.act == "row" else "Q8_0 activations"
         dom = f"gate_up (grouped {shape.label} x int8 MFMA GEMM, {fmt}, + SwiGLU)"
@@ -771,6 +826,8 @@ def main():
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "roofline": roof,
     }
+    if step_floor:
+        out["step_floor"] = step_floor
     if cache_info:
         out["cache"] = cache_info
     if not args.no_cpu:

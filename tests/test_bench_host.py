@@ -71,3 +71,21 @@ def test_prefill_gate_up_bounds():
     assert fix == n_pairs * 2 * 2048 * (6144 // 32)
     assert max(b, key=b.get) == "alu"
     assert abs(b["alu"] - 2 * fix / (256 * 4 * 16 * 2.4e9)) < 1e-12
+
+
+def test_small_phase_bytes_cover_the_step():
+    """The step-floor chain reads, per launch of the small-batch step, the
+    router matrix, the shared expert's gate/up, the routed experts' gate/up
+    and every used expert's down rows: together every weight byte of the
+    step once (the records of U routed experts and the shared one, the
+    router matrix), and the split at the record's down part."""
+    bench = _bench()
+    sys.path.insert(0, ROOT)
+    import synth
+    s = synth.REAL
+    bb = 18_915_328  # int4 record at the real shape
+    phases = bench.small_phase_bytes(s, 8, bb)
+    assert phases == [6144 * 256 * 4, 12_599_296, 8 * 12_599_296, 9 * 6_316_032]
+    assert sum(phases) == s.n_experts * s.hidden * 4 + 9 * bb
+    # gate/up codes (two I x H/2 matrices) and their 2 I row scales
+    assert bench.gate_up_record_bytes(s) == 2 * 2048 * 6144 // 2 + 2 * 2048 * 4
