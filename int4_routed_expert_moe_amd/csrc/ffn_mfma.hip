@@ -113,38 +113,41 @@ __device__ __forceinline__ long a_frag(const uint8_t *row, int b, int g) {
 // outside the tile gets a zero scale when the chunk is stored: a load inside
 // a branch would make the compiler wait for it (and for every load before
 // it) on the spot, ahead of the MFMAs it is meant to overlap.
+template <int TR>
 struct ActChunk {
-  uint4 v[4];  // 4 x 16 bytes per thread (64 tokens x 16 pieces)
-  float d[2];  // 64 tokens x 8 block scales, as loaded
+  static constexpr int NV = TR * 16 / 256;          // 16-byte pieces per thread
+  static constexpr int ND = (TR * mf::CB + 255) / 256;  // block scales per thread
+  uint4 v[NV];  // TR tokens x 16 pieces
+  float d[ND];  // TR tokens x 8 block scales, as loaded
 };
 
-template <int WB>
+template <int WB, int TR>
 __device__ __forceinline__ void load_act_chunk(const int8_t *q, const float *d, int row_len,
                                                const int *tokl, int n, int c, int nblk,
-                                               ActChunk &r) {
+                                               ActChunk<TR> &r) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 4; u++) {
+  for (int u = 0; u < ActChunk<TR>::NV; u++) {
     const int i = tid + 256 * u, tok_i = i >> 4, piece = i & 15;  // 16-byte piece
     const int blk = min(c * mf::CB + (piece >> 1), nblk - 1);
     r.v[u] = gload<uint4>(reinterpret_cast<const uint8_t *>(q),
                           (size_t)tokl[tok_i] * row_len + (size_t)blk * 32 + (piece & 1) * 16);
   }
 #pragma unroll
-  for (int u = 0; u < 2; u++) {
-    const int i = tid + 256 * u, tok_i = i >> 3, b = i & 7;
+  for (int u = 0; u < ActChunk<TR>::ND; u++) {
+    const int i = min(tid + 256 * u, TR * mf::CB - 1), tok_i = i >> 3, b = i & 7;
     const int blk = min(c * mf::CB + b, nblk - 1);
     r.d[u] = gload<float>(reinterpret_cast<const uint8_t *>(d),
                           4 * ((size_t)tokl[tok_i] * (row_len / 32) + blk));
   }
 }
 
-template <int WB>
-__device__ __forceinline__ void store_act_chunk(const ActChunk &r, uint8_t *bs, float *ds, int n,
-                                                int c, int nblk) {
+template <int WB, int TR>
+__device__ __forceinline__ void store_act_chunk(const ActChunk<TR> &r, uint8_t *bs, float *ds,
+                                                int n, int c, int nblk) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int u = 0; u < 4; u++) {
+  for (int u = 0; u < ActChunk<TR>::NV; u++) {
     const int i = tid + 256 * u, tok_i = i >> 4, piece = i & 15;
     if constexpr (WB == 8) {
       *reinterpret_cast<uint4 *>(bs + tok_i * mf::BSTR + piece * 16) = r.v[u];
@@ -155,11 +158,12 @@ __device__ __forceinline__ void store_act_chunk(const ActChunk &r, uint8_t *bs, 
     }
   }
 #pragma unroll
-  for (int u = 0; u < 2; u++) {
+  for (int u = 0; u < ActChunk<TR>::ND; u++) {
     const int i = tid + 256 * u, tok_i = i >> 3, b = i & 7;
     const bool ok = tok_i < n && c * mf::CB + b < nblk;
-    ds[tok_i * mf::CB + b] =
-        ok ? r.d[u] * (WB == 8 ? 1.0f : WB == WB_MX ? 0.5f : 0.0625f) : 0.0f;
+    if (i < TR * mf::CB)
+      ds[tok_i * mf::CB + b] =
+          ok ? r.d[u] * (WB == 8 ? 1.0f : WB == WB_MX ? 0.5f : 0.0625f) : 0.0f;
   }
 }
 
@@ -237,7 +241,7 @@ __device__ __forceinline__ void store_w_chunk(const WChunk<NM, WB> &r, uint8_t *
 // token sub-tile s (16 tokens, s < NS: the sub-tiles that hold tokens, fixed
 // per workgroup so the loop body has no branches), row 16 wv + 4 g + i.  DBG: raw block dots of
 // matrix m go to dots[m] at ((pair * R + row) * nblk + block).
-template <int NM, bool DBG, int NS, int WB, bool NT>
+template <int NM, bool DBG, int NS, int WB, bool NT, int TR>
 __device__ void mfma_kloop(const uint8_t *const *mat, const uint8_t *const *scl, size_t row_b,
                            int r0, const int8_t *q, const float *d, int row_len, const int *tokl,
                            const int *pairl, int n, int nblk, uint8_t *bs, float *ds, uint8_t *as,
@@ -252,17 +256,18 @@ __device__ void mfma_kloop(const uint8_t *const *mat, const uint8_t *const *scl,
       for (int i = 0; i < 4; i++) acc[m][s][i] = 0.0f;
   const int nchunk = (nblk + mf::CB - 1) / mf::CB;
   constexpr int AS = mf::astr<WB>();
-  ActChunk ac;
+  static_assert(16 * NS <= TR, "token sub-tiles within the staged rows");
+  ActChunk<TR> ac;
   WChunk<NM, WB> wc;
-  load_act_chunk<WB>(q, d, row_len, tokl, n, 0, nblk, ac);
+  load_act_chunk<WB, TR>(q, d, row_len, tokl, n, 0, nblk, ac);
   load_w_chunk<NM, WB, NT>(mat, scl, row_b, r0, 0, nblk, wc);
   for (int c = 0; c < nchunk; c++) {
     __syncthreads();  // the previous chunk is consumed
-    store_act_chunk<WB>(ac, bs, ds, n, c, nblk);
+    store_act_chunk<WB, TR>(ac, bs, ds, n, c, nblk);
     store_w_chunk<NM, WB>(wc, as, wsl);
     __syncthreads();
     if (c + 1 < nchunk) {  // next chunk in flight during this one's MFMAs
-      load_act_chunk<WB>(q, d, row_len, tokl, n, c + 1, nblk, ac);
+      load_act_chunk<WB, TR>(q, d, row_len, tokl, n, c + 1, nblk, ac);
       load_w_chunk<NM, WB, NT>(mat, scl, row_b, r0, c + 1, nblk, wc);
     }
     const int nb = min(mf::CB, nblk - c * mf::CB);
@@ -309,29 +314,35 @@ __device__ void mfma_kloop(const uint8_t *const *mat, const uint8_t *const *scl,
   }
 }
 
-// mfma_kloop with the sub-tile count of n tokens chosen once.
-template <int NM, bool DBG, int WB, bool NT = false>
+// mfma_kloop with the sub-tile count of n tokens chosen once; TR token rows
+// are staged per chunk (16 when the work item never holds more tokens).
+template <int NM, bool DBG, int WB, bool NT = false, int TR = mf::NT>
 __device__ void mfma_kloop_n(const uint8_t *const *mat, const uint8_t *const *scl, size_t row_b,
                              int r0, const int8_t *q, const float *d, int row_len,
                              const int *tokl, const int *pairl, int n, int nblk, uint8_t *bs,
                              float *ds, uint8_t *as, float *wsl, float (&acc)[NM][4][4],
                              int32_t *const *dots, int R) {
-  switch ((n + 15) / 16) {
-    case 1:
-      mfma_kloop<NM, DBG, 1, WB, NT>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
-                                 as, wsl, acc, dots, R);
-      break;
-    case 2:
-      mfma_kloop<NM, DBG, 2, WB, NT>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
-                                 as, wsl, acc, dots, R);
-      break;
-    case 3:
-      mfma_kloop<NM, DBG, 3, WB, NT>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
-                                 as, wsl, acc, dots, R);
-      break;
-    default:
-      mfma_kloop<NM, DBG, 4, WB, NT>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk, bs, ds,
-                                 as, wsl, acc, dots, R);
+  if constexpr (TR == 16) {
+    mfma_kloop<NM, DBG, 1, WB, NT, TR>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n, nblk,
+                                       bs, ds, as, wsl, acc, dots, R);
+  } else {
+    switch ((n + 15) / 16) {
+      case 1:
+        mfma_kloop<NM, DBG, 1, WB, NT, TR>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n,
+                                           nblk, bs, ds, as, wsl, acc, dots, R);
+        break;
+      case 2:
+        mfma_kloop<NM, DBG, 2, WB, NT, TR>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n,
+                                           nblk, bs, ds, as, wsl, acc, dots, R);
+        break;
+      case 3:
+        mfma_kloop<NM, DBG, 3, WB, NT, TR>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n,
+                                           nblk, bs, ds, as, wsl, acc, dots, R);
+        break;
+      default:
+        mfma_kloop<NM, DBG, 4, WB, NT, TR>(mat, scl, row_b, r0, q, d, row_len, tokl, pairl, n,
+                                           nblk, bs, ds, as, wsl, acc, dots, R);
+    }
   }
 }
 
@@ -431,21 +442,22 @@ __global__ void __launch_bounds__(256, 3) k_gate_up_mfma(FfnArgs a, const int4 *
 // Workgroup (row tile, work item): output rows 64 x .. of the down matrix
 // for the work item's pairs, from Q8_0(h); routed rows go to expert_out of
 // the slot, shared rows to shared_out of the token.
+template <int TR>
 struct DownLds {
-  uint8_t bs[MF_LDS_B];
-  float ds[mf::NT * mf::CB];
-  int tokl[mf::NT], pairl[mf::NT];
+  uint8_t bs[TR * mf::BSTR];
+  float ds[TR * mf::CB];
+  int tokl[TR], pairl[TR];
 };
 
-template <bool DBG, int WB, bool NT = false>
+template <bool DBG, int WB, bool NT = false, int TR = mf::NT>
 __device__ void down_mfma_tile(const FfnArgs &a, const TileInfo &ti, int rt, const int8_t *q_h,
-                               const float *d_h, DownLds &L, uint8_t *as, float *wsl);
+                               const float *d_h, DownLds<TR> &L, uint8_t *as, float *wsl);
 
 template <bool DBG, int WB>
 __global__ void __launch_bounds__(256) k_down_mfma(FfnArgs a, const int4 *tiles,
                                                    const int32_t *n_tiles, const int8_t *q_h,
                                                    const float *d_h) {
-  __shared__ __align__(16) DownLds L;
+  __shared__ __align__(16) DownLds<mf::NT> L;
   __shared__ __align__(16) uint8_t as[mf::RT * mf::astr<WB>()];
   __shared__ __align__(16) float wsl[WB == WB_MX ? mf::CB * mf::RT : 4];
   const int rt = blockIdx.x;
@@ -466,12 +478,14 @@ __global__ void __launch_bounds__(256) k_down_mfma(FfnArgs a, const int4 *tiles,
 // Down projection of the small-batch layer path for batches of several
 // tokens: workgroup (row tile, slot) straight from the batch union's slot
 // table (entry: expert, token count, pair ids, record address); empty slots
-// exit at once.
+// exit at once.  A slot holds at most 16 tokens, so 16 activation rows are
+// staged per chunk (a quarter of the prefill tiles' LDS and loads).
 template <int WB, bool DBG>
 __global__ void __launch_bounds__(256) k_down_mfma_slots(FfnArgs a, const int32_t *slots,
                                                          int slot_w, int slot_ptr,
                                                          const int8_t *q_h, const float *d_h) {
-  __shared__ __align__(16) DownLds L;
+  constexpr int TR = 16;
+  __shared__ __align__(16) DownLds<TR> L;
   __shared__ __align__(16) uint8_t as[mf::RT * mf::astr<WB>()];
   __shared__ __align__(16) float wsl[WB == WB_MX ? mf::CB * mf::RT : 4];
   const int32_t *ent = slots + (size_t)blockIdx.y * slot_w;
@@ -480,21 +494,21 @@ __global__ void __launch_bounds__(256) k_down_mfma_slots(FfnArgs a, const int32_
   TileInfo ti;
   ti.shared = ent[0] < 0;
   ti.blob = *reinterpret_cast<const uint8_t *const *>(ent + slot_ptr);
-  ti.n = min(n, min(a.T, mf::NT));
+  ti.n = min(n, min(a.T, TR));
   const int tid = threadIdx.x;
   const int P = a.T * (a.K + a.n_shared);
-  if (tid < mf::NT) {
+  if (tid < TR) {
     const int pair = tid < ti.n ? min(max(ent[2 + tid], 0), P - 1) : 0;
     L.tokl[tid] = pair;
     L.pairl[tid] = pair;
   }
   __syncthreads();
-  down_mfma_tile<DBG, WB, true>(a, ti, blockIdx.x, q_h, d_h, L, as, wsl);
+  down_mfma_tile<DBG, WB, true, TR>(a, ti, blockIdx.x, q_h, d_h, L, as, wsl);
 }
 
-template <bool DBG, int WB, bool NT>
+template <bool DBG, int WB, bool NT, int TR>
 __device__ void down_mfma_tile(const FfnArgs &a, const TileInfo &ti, int rt, const int8_t *q_h,
-                               const float *d_h, DownLds &L, uint8_t *as, float *wsl) {
+                               const float *d_h, DownLds<TR> &L, uint8_t *as, float *wsl) {
   const int H = a.H, I = a.I, r0 = rt * mf::RT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   uint8_t *bs = L.bs;
@@ -506,7 +520,7 @@ __device__ void down_mfma_tile(const FfnArgs &a, const TileInfo &ti, int rt, con
   const uint8_t *scl[1] = {ti.blob + 3 * gate_b + 2 * (size_t)I * (H / 32)};  // MXFP4
   float acc[1][4][4];
   int32_t *dots[1] = {a.dbg.down_dots};
-  mfma_kloop_n<1, DBG, WB, NT>(mats, scl, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs,
+  mfma_kloop_n<1, DBG, WB, NT, TR>(mats, scl, row_b, r0, q_h, d_h, I, tokl, pairl, ti.n, I / 32, bs,
                                ds, as, wsl, acc, dots, H);
   const int m16 = lane & 15, g = lane >> 4;
   const int row = r0 + wv * 16 + g * 4;  // 4 consecutive rows per lane
@@ -517,7 +531,7 @@ __device__ void down_mfma_tile(const FfnArgs &a, const TileInfo &ti, int rt, con
                      __uint_as_float(u.w));
   }
 #pragma unroll
-  for (int s = 0; s < 4; s++) {
+  for (int s = 0; s < TR / 16; s++) {
     const int col = s * 16 + m16;
     if (col >= ti.n) continue;
     const float4 y = make_float4(s4.x * acc[0][s][0], s4.y * acc[0][s][1], s4.z * acc[0][s][2],
