@@ -740,7 +740,7 @@ def main():
         pk = measured_read_peak(torch, moe, hip, dev, [r["ex"] for r in ring], int(dom_bytes))
         roof["achievable_peak"] = pk
         roof["frac_of_achievable"] = roof["achieved"] / pk
-        if small and NL == 1 and not fp8:
+        if small and NL == 1 and not fp8 and use_graph:
             # the step's dependent launches as plain reads of their bytes
             phases = small_phase_bytes(shape, U, bb)
             floor_us = measured_step_floor(torch, moe, stream, dev, [r["ex"] for r in ring],
