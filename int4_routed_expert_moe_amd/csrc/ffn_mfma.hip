@@ -30,9 +30,10 @@ constexpr int NT = TILE_T;          // tokens per tile
 constexpr int RT = 64;              // rows per workgroup
 constexpr int CB = 8;               // Q8_0 blocks per K chunk (256 k)
 constexpr int BSTR = CB * 32 + 16;  // LDS bytes per activation row (padded)
-// LDS bytes per weight row of a chunk (padded): int4 16 B per block, int8 32 B
+// LDS bytes per weight row of a chunk (padded): int4 16 B per block, int8 32
+// B, int2 8 B
 template <int WB>
-constexpr int astr() { return WB == 8 ? CB * 32 + 8 : CB * 16 + 4; }
+constexpr int astr() { return WB == 8 ? CB * 32 + 8 : WB == 2 ? CB * 8 + 4 : CB * 16 + 4; }
 }  // namespace mf
 
 
@@ -91,11 +92,19 @@ __global__ void __launch_bounds__(256) k_mfma_tiles(int E, int T, int n_shared,
 
 // A fragment of one 32-code block: lane (m, g) holds codes 8g..8g+7 of row m
 // -- int4: as 16 x code, even codes first (from 4 bytes); MXFP4: as 2 x the
-// FP4 value, even codes first; int8: the 8 bytes.
+// FP4 value, even codes first; int8: the 8 bytes; int2: codes g + 4 i
+// (i = 0..7, field g of each of the block's 8 bytes) as 64 x code, the order
+// in which the small-batch gate/up kernel writes Q8_0(h) for int2 (bytes
+// 16 g + 8 (b & 1) .. + 7 of each 64-code piece).
 template <int WB>
 __device__ __forceinline__ long a_frag(const uint8_t *row, int b, int g) {
   if constexpr (WB == 8) {
     return *reinterpret_cast<const long *>(row + b * 32 + g * 8);
+  } else if constexpr (WB == 2) {
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(row + b * 8);
+    const uint32_t lo = ((w[0] >> (2 * g)) & 0x03030303u) << 6;
+    const uint32_t hi = ((w[1] >> (2 * g)) & 0x03030303u) << 6;
+    return (long)lo | ((long)hi << 32);
   } else if constexpr (WB == WB_MX) {
     const uint32_t w = *reinterpret_cast<const uint32_t *>(row + b * 16 + g * 4);
     return (long)(uint32_t)mx_lanes(w, 0) | ((long)(uint32_t)mx_lanes(w, 4) << 32);
@@ -149,7 +158,7 @@ __device__ __forceinline__ void store_act_chunk(const ActChunk<TR> &r, uint8_t *
 #pragma unroll
   for (int u = 0; u < ActChunk<TR>::NV; u++) {
     const int i = tid + 256 * u, tok_i = i >> 4, piece = i & 15;
-    if constexpr (WB == 8) {
+    if constexpr (WB == 8 || WB == 2) {  // int2: already in its fragment order
       *reinterpret_cast<uint4 *>(bs + tok_i * mf::BSTR + piece * 16) = r.v[u];
     } else {
       uint2 *dst = reinterpret_cast<uint2 *>(bs + tok_i * mf::BSTR + piece * 16);
@@ -163,7 +172,8 @@ __device__ __forceinline__ void store_act_chunk(const ActChunk<TR> &r, uint8_t *
     const bool ok = tok_i < n && c * mf::CB + b < nblk;
     if (i < TR * mf::CB)
       ds[tok_i * mf::CB + b] =
-          ok ? r.d[u] * (WB == 8 ? 1.0f : WB == WB_MX ? 0.5f : 0.0625f) : 0.0f;
+          ok ? r.d[u] * (WB == 8 ? 1.0f : WB == WB_MX ? 0.5f : WB == 2 ? 0.015625f : 0.0625f)
+             : 0.0f;
   }
 }
 
@@ -285,7 +295,8 @@ __device__ void mfma_kloop(const uint8_t *const *mat, const uint8_t *const *scl,
 #pragma unroll
       for (int s = 0; s < NS; s++) {  // only the sub-tiles that hold tokens
         const int col = s * 16 + m16;
-        const long bf = *reinterpret_cast<const long *>(bs + col * mf::BSTR + b * 32 + g * 8);
+        const int bo = WB == 2 ? (b >> 1) * 64 + g * 16 + (b & 1) * 8 : b * 32 + g * 8;
+        const long bf = *reinterpret_cast<const long *>(bs + col * mf::BSTR + bo);
         const float dd = ds[col * mf::CB + b];
 #pragma unroll
         for (int m = 0; m < NM; m++) {
@@ -305,7 +316,8 @@ __device__ void mfma_kloop(const uint8_t *const *mat, const uint8_t *const *scl,
 #pragma unroll
             for (int i = 0; i < 4; i++) {
               const int row = r0 + wv * 16 + g * 4 + i;
-              dots[m][((size_t)pairl[col] * R + row) * nblk + blk] = WB == 4 ? p[i] >> 4 : p[i];
+              dots[m][((size_t)pairl[col] * R + row) * nblk + blk] =
+                  WB == 4 ? p[i] >> 4 : WB == 2 ? p[i] >> 6 : p[i];
             }
           }
         }
@@ -576,6 +588,9 @@ static void launch_down_slots_dbg(const FfnArgs &a, const int32_t *slots, int n_
              q_h, d_h);
   else if (a.wbits == 8)
     launch_k(k_down_mfma_slots<8, DBG>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr, q_h,
+             d_h);
+  else if (a.wbits == 2)
+    launch_k(k_down_mfma_slots<2, DBG>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr, q_h,
              d_h);
   else
     launch_k(k_down_mfma_slots<4, DBG>, g, dim3(256), 0, st, ed, a, slots, slot_w, slot_ptr, q_h,
