@@ -27,9 +27,9 @@
 //                      and token, combined in LDS in rank order into y
 //                      (+ residual), with per-tile sums of squares when the
 //                      RMSNorm is wanted; from 4 tokens on (int4 and int2;
-//                      int8 and MXFP4 from 12) the down rows run as MFMA tiles
-//                      from the slot table instead, followed by a combine
-//                      kernel.
+//                      MXFP4 from 8, int8 from 12) the down rows run as MFMA
+//                      tiles from the slot table instead, followed by a
+//                      combine kernel.
 //  K4  k_norm_small    (with y_norm) the unit-gain RMSNorm of whole rows.
 // Every kernel spreads its weight bytes over all CUs: one CU streams only a
 // few tens of GB/s, so a phase confined to a few CUs is slow however small.
@@ -100,9 +100,13 @@ constexpr int shared_rpw(int TT) { return TT == 1 ? MOE_SHARED_RPW1 : MOE_SHARED
 #define MOE_SHARED_TT 2
 #endif
 // smallest batch whose down projection runs on the matrix cores (17: never):
-// int4 and int2, and int8 / MXFP4 (their vector down kernels hold out longer)
+// int4 and int2, MXFP4, and int8 (the vector down kernels of the last two
+// hold out longer)
 #ifndef MOE_DOWN_MFMA_MIN_T
 #define MOE_DOWN_MFMA_MIN_T 4
+#endif
+#ifndef MOE_DOWN_MFMA_MIN_T_MX
+#define MOE_DOWN_MFMA_MIN_T_MX 8
 #endif
 #ifndef MOE_DOWN_MFMA_MIN_T_WIDE
 #define MOE_DOWN_MFMA_MIN_T_WIDE 12
@@ -1933,7 +1937,9 @@ void launch3(const LayerArgs &a, hipStream_t st, const moe_events *ev) {
                                          : MOE_K3_SLOTS;
   constexpr int TT3 = TT == 1 ? 1 : MOE_K3_TT;  // tokens per chunk in the down kernel
   const int quarter = (a.I / (128 / code_bits<WB>()) + 3) / 4;
-  const int mfma_min_t = WB == 4 || WB == 2 ? MOE_DOWN_MFMA_MIN_T : MOE_DOWN_MFMA_MIN_T_WIDE;
+  const int mfma_min_t = WB == 4 || WB == 2 ? MOE_DOWN_MFMA_MIN_T
+                         : WB == WB_MX        ? MOE_DOWN_MFMA_MIN_T_MX
+                                              : MOE_DOWN_MFMA_MIN_T_WIDE;
   if (WB != WB_F8 && a.T >= mfma_min_t && a.H % 64 == 0 && a.I % 64 == 0) {
     // many tokens per expert: the down projection as MFMA tiles of 64 rows
     // x the slot's tokens (activations staged once per 64 rows, not once

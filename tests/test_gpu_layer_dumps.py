@@ -2,9 +2,9 @@
 
 For 1..16 tokens moe_layer runs the fused small-batch kernels (router,
 selection beside the shared expert's gate/up, batch union + routed gate/up +
-Q8_0 of h, down + combine; from 4 tokens (int4; int8 and MXFP4 from 12) the
-down projection as MFMA tiles from the slot table); above that it chains the
-separate kernels.  With a
+Q8_0 of h, down + combine; from 4 tokens (int4 and int2; MXFP4 from 8, int8
+from 12) the down projection as MFMA tiles from the slot table); above that
+it chains the separate kernels.  With a
 moe_layer_debug those kernels also write what they compute: Q8_0 of x, the
 batch union, the exact int32 block dots of gate/up and down, h and its Q8_0.
 Each is compared with the CPU oracle on the same seeded inputs:
