@@ -14,11 +14,16 @@
 // the MFMA as 16 x code (the low/high nibble split), with the 1/16 folded
 // into the activation scale; the split reorders k inside each group of 8,
 // and the activations staged in LDS are reordered the same way.  int8 codes
-// (the same format with 8-bit codes) enter as they are.
+// (the same format with 8-bit codes) enter as they are; int2 codes (the small-
+// batch down tiles only) as 64 x code, in the field order of the activations
+// the small-batch gate/up kernel writes, with 1/64 folded into the scale.
 //
 // Work items are (expert, 64-token tile) pairs from a tile list; a
 // workgroup computes 64 rows x 64 tokens of one work item (gate and up
-// together, so SwiGLU and the Q8_0 of h happen in its epilogue).
+// together, so SwiGLU and the Q8_0 of h happen in its epilogue).  The
+// small-batch path's down projection (4..16 tokens) uses the same K loop on
+// (64-row tile, expert slot) workgroups read from its slot table, staging 16
+// token rows.
 #include "common.h"
 #include "kernels.h"
 #include "tiles.h"
