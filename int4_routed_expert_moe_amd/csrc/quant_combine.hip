@@ -111,14 +111,22 @@ __global__ void __launch_bounds__(256) k_combine(int H, int K, const float *__re
     float4 s = reinterpret_cast<const float4 *>(shared)[(size_t)t * H4 + j];
     acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
   }
-  for (int k = 0; k < K; k++) {
-    const float c = wk[k];
-    if (c == 0.0f) continue;  // a rank dropped by top-p: its row is not read
-    float4 e = eo4[(size_t)k * H4 + j];
-    acc.x = fmaf(c, e.x, acc.x);
-    acc.y = fmaf(c, e.y, acc.y);
-    acc.z = fmaf(c, e.z, acc.z);
-    acc.w = fmaf(c, e.w, acc.w);
+  for (int k0 = 0; k0 < K; k0 += 8) {
+    // 8 ranks' rows requested at once (one memory round trip, not 8); a rank
+    // dropped by top-p (weight 0, its row never written) is read and skipped
+    float4 e[8];
+#pragma unroll
+    for (int u = 0; u < 8; u++) e[u] = eo4[(size_t)min(k0 + u, K - 1) * H4 + j];
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+      const float c = k0 + u < K ? wk[k0 + u] : 0.0f;
+      if (c != 0.0f) {
+        acc.x = fmaf(c, e[u].x, acc.x);
+        acc.y = fmaf(c, e[u].y, acc.y);
+        acc.z = fmaf(c, e[u].z, acc.z);
+        acc.w = fmaf(c, e[u].w, acc.w);
+      }
+    }
   }
   reinterpret_cast<float4 *>(y)[(size_t)t * H4 + j] = acc;
 }
